@@ -1,0 +1,264 @@
+"""Python binding of ``libmoe.so``, the gfx950 MoE-layer share.
+
+Argument marshalling only: each function checks tensor placement, shape and
+dtype, allocates any output the caller did not pass (PyTorch device memory),
+and calls the C entry point of the same name on the current HIP stream. Every
+step of the computation runs in the library's HIP kernels; there is no other
+implementation to fall back to, and a missing library raises
+``MoeLibraryMissing``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "COMPACT", "PADDED", "GG_FULL", "GG_UP", "GG_DOWN", "STATUS_OVERFLOW", "MoeError", "MoeLibraryMissing",
+    "lib", "lib_path", "moe_route_topk", "moe_dispatch_layout", "moe_layout_rows", "moe_dispatch",
+    "moe_grouped_gemm", "moe_combine", "moe_abi_version",
+]
+
+COMPACT, PADDED = 0, 1
+GG_FULL, GG_UP, GG_DOWN = 0, 1, 2
+STATUS_OVERFLOW = 1
+_F32, _BF16, _FP8 = 0, 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_FILE = os.path.join(_HERE, "libmoe.so")
+_lib = None
+
+
+class MoeError(RuntimeError):
+    pass
+
+
+class MoeLibraryMissing(ImportError):
+    pass
+
+
+class LayoutDesc(ctypes.Structure):
+    _fields_ = [("n_tokens", ctypes.c_int), ("top_k", ctypes.c_int), ("n_experts", ctypes.c_int),
+                ("n_src", ctypes.c_int), ("expert_lo", ctypes.c_int), ("n_local", ctypes.c_int),
+                ("layout", ctypes.c_int), ("capacity", ctypes.c_int)]
+
+
+class GGemmDesc(ctypes.Structure):
+    _fields_ = [("n_groups", ctypes.c_int), ("hidden", ctypes.c_int), ("inter", ctypes.c_int),
+                ("act_dt", ctypes.c_int), ("w_dt", ctypes.c_int), ("layout", ctypes.c_int),
+                ("n_src", ctypes.c_int), ("capacity", ctypes.c_int), ("rows", ctypes.c_int64),
+                ("stage", ctypes.c_int)]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+
+_SIGNATURES = {
+    "moe_abi_version": (_I, []),
+    "moe_status_string": (ctypes.c_char_p, [_I]),
+    "moe_route_topk": (_I, [_P, _I, _I, _I, _I, _P, _P, _P]),
+    "moe_layout_rows": (_I64, [ctypes.POINTER(LayoutDesc)]),
+    "moe_dispatch_layout_workspace": (_SZ, [ctypes.POINTER(LayoutDesc)]),
+    "moe_dispatch_layout": (_I, [ctypes.POINTER(LayoutDesc), _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_dispatch": (_I, [_P, _I, _I, _I, _I, _P, _I64, _P, _P]),
+    "moe_grouped_gemm_workspace": (_SZ, [ctypes.POINTER(GGemmDesc)]),
+    "moe_grouped_gemm": (_I, [ctypes.POINTER(GGemmDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_combine": (_I, [_P, _I, _I64, _P, _P, _I, _I, _I, _P, _I, _I, _P, _P]),
+}
+
+
+def lib_path() -> str:
+    return _LIB_FILE
+
+
+def lib():
+    """The loaded library (ctypes), loading it on first use."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_FILE):
+            raise MoeLibraryMissing(
+                f"{_LIB_FILE} is not built; run `python combine_router_softmax_amd/build.py` "
+                "(there is no CPU fallback)")
+        l = ctypes.CDLL(_LIB_FILE)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(l, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = l
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = lib().moe_status_string(status).decode()
+        raise MoeError(f"{what}: {msg} (status {status})")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return t
+
+
+def _act_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return _F32
+    if dt == torch.bfloat16:
+        return _BF16
+    raise ValueError(f"unsupported activation dtype {dt}")
+
+
+def moe_abi_version() -> int:
+    return int(lib().moe_abi_version())
+
+
+# --------------------------------------------------------------------------- route
+def moe_route_topk(logits: torch.Tensor, top_k: int, renormalize: bool = True,
+                   topk_idx: Optional[torch.Tensor] = None, topk_w: Optional[torch.Tensor] = None):
+    """Top-K experts per token and their (renormalised) softmax weights."""
+    _dev(logits, "logits", torch.float32)
+    N, E = logits.shape
+    if topk_idx is None:
+        topk_idx = torch.empty((N, top_k), dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty((N, top_k), dtype=torch.float32, device=logits.device)
+    _dev(topk_idx, "topk_idx", torch.int32)
+    _dev(topk_w, "topk_w", torch.float32)
+    _check(lib().moe_route_topk(_ptr(logits), N, E, top_k, int(bool(renormalize)), _ptr(topk_idx), _ptr(topk_w),
+                                _stream()), "moe_route_topk")
+    return topk_idx, topk_w
+
+
+# --------------------------------------------------------------------------- layout
+def _layout_desc(n_tokens, top_k, n_experts, n_src, expert_lo, n_local, layout, capacity) -> LayoutDesc:
+    return LayoutDesc(n_tokens, top_k, n_experts, n_src, expert_lo, n_local, layout, capacity)
+
+
+def moe_layout_rows(n_tokens, top_k, n_experts, n_src, expert_lo, n_local, layout, capacity) -> int:
+    d = _layout_desc(n_tokens, top_k, n_experts, n_src, expert_lo, n_local, layout, capacity)
+    r = int(lib().moe_layout_rows(ctypes.byref(d)))
+    if r < 0:
+        raise MoeError("moe_layout_rows: invalid descriptor")
+    return r
+
+
+def moe_dispatch_layout(topk_idx: torch.Tensor, src_offsets: torch.Tensor, n_experts: int, expert_lo: int,
+                        n_local: int, layout: int, capacity: int, out: Optional[dict] = None) -> dict:
+    """Counts, offsets and a slot per (token, k). ``out`` may hold preallocated
+    ``counts, expert_off, row_of, row_token, status, ws`` tensors."""
+    _dev(topk_idx, "topk_idx", torch.int32)
+    _dev(src_offsets, "src_offsets", torch.int32)
+    N, K = topk_idx.shape
+    S = src_offsets.numel() - 1
+    d = _layout_desc(N, K, n_experts, S, expert_lo, n_local, layout, capacity)
+    R = int(lib().moe_layout_rows(ctypes.byref(d)))
+    if R < 0:
+        raise MoeError("moe_dispatch_layout: invalid descriptor")
+    wsb = int(lib().moe_dispatch_layout_workspace(ctypes.byref(d)))
+    dev = topk_idx.device
+    o = dict(out) if out else {}
+    o.setdefault("counts", torch.empty((n_local, S), dtype=torch.int32, device=dev))
+    o.setdefault("expert_off", torch.empty(n_local + 1, dtype=torch.int32, device=dev))
+    o.setdefault("row_of", torch.empty(N * K, dtype=torch.int32, device=dev))
+    o.setdefault("row_token", torch.empty(max(R, 1), dtype=torch.int32, device=dev))
+    o.setdefault("status", torch.empty(1, dtype=torch.int32, device=dev))
+    o.setdefault("ws", torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev))
+    for k in ("counts", "expert_off", "row_of", "row_token", "status"):
+        _dev(o[k], k, torch.int32)
+    _check(lib().moe_dispatch_layout(ctypes.byref(d), _ptr(topk_idx), _ptr(src_offsets), _ptr(o["counts"]),
+                                     _ptr(o["expert_off"]), _ptr(o["row_of"]), _ptr(o["row_token"]),
+                                     _ptr(o["status"]), _ptr(o["ws"]), o["ws"].numel(), _stream()),
+           "moe_dispatch_layout")
+    o["rows"] = R
+    return o
+
+
+# --------------------------------------------------------------------------- dispatch
+def moe_dispatch(x: torch.Tensor, row_of: torch.Tensor, top_k: int, n_rows: int,
+                 xe: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Copy token rows into their expert-grouped slots (unused rows untouched)."""
+    _dev(x, "x", (torch.float32, torch.bfloat16))
+    _dev(row_of, "row_of", torch.int32)
+    N, H = x.shape
+    if xe is None:
+        xe = torch.empty((n_rows, H), dtype=x.dtype, device=x.device)
+    _dev(xe, "xe", x.dtype)
+    _check(lib().moe_dispatch(_ptr(x), _act_code(x.dtype), N, H, top_k, _ptr(row_of), n_rows, _ptr(xe), _stream()),
+           "moe_dispatch")
+    return xe
+
+
+# --------------------------------------------------------------------------- grouped GEMM
+def gemm_desc(n_groups, hidden, inter, act_dtype, w_dtype, layout, n_src, capacity, rows, stage=GG_FULL):
+    w_code = {torch.float32: _F32, torch.bfloat16: _BF16, torch.uint8: _FP8, torch.float8_e4m3fn: _FP8}[w_dtype]
+    return GGemmDesc(n_groups, hidden, inter, _act_code(act_dtype), w_code, layout, n_src, capacity, rows, stage)
+
+
+def moe_grouped_gemm_workspace(desc: GGemmDesc) -> int:
+    return int(lib().moe_grouped_gemm_workspace(ctypes.byref(desc)))
+
+
+def moe_grouped_gemm(a: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, *, group_off=None, counts=None,
+                     s13=None, s2=None, layout: int = COMPACT, n_src: int = 1, capacity: int = 0,
+                     stage: int = GG_FULL, y: Optional[torch.Tensor] = None,
+                     ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """SwiGLU FFN per expert over the rows each expert holds (see moe.h)."""
+    _dev(a, "a", (torch.float32, torch.bfloat16))
+    _dev(w13, "w13")
+    _dev(w2, "w2")
+    R, H = a.shape
+    G, I2, H2 = w13.shape
+    if H2 != H or I2 % 2:
+        raise ValueError("w13 must be [G, 2I, H]")
+    I = I2 // 2
+    desc = gemm_desc(G, H, I, a.dtype, w13.dtype, layout, n_src, capacity, R, stage)
+    wsb = moe_grouped_gemm_workspace(desc)
+    if wsb == 0:
+        raise MoeError("moe_grouped_gemm: invalid descriptor")
+    if ws is None:
+        ws = torch.empty(wsb, dtype=torch.uint8, device=a.device)
+    if y is None and stage != GG_UP:
+        y = torch.empty((R, H), dtype=a.dtype, device=a.device)
+    for name, t in (("group_off", group_off), ("counts", counts)):
+        if t is not None:
+            _dev(t, name, torch.int32)
+    for name, t in (("s13", s13), ("s2", s2)):
+        if t is not None:
+            _dev(t, name, torch.float32)
+    _check(lib().moe_grouped_gemm(ctypes.byref(desc), _ptr(a), _ptr(counts), _ptr(group_off), _ptr(w13), _ptr(w2),
+                                  _ptr(s13), _ptr(s2), _ptr(y), _ptr(ws), ws.numel(), _stream()),
+           "moe_grouped_gemm")
+    return y
+
+
+# --------------------------------------------------------------------------- combine
+def moe_combine(ye: torch.Tensor, row_of: torch.Tensor, topk_w: torch.Tensor, out: torch.Tensor,
+                shared_y: Optional[torch.Tensor] = None, self_lo: int = 0, self_hi: int = 0) -> torch.Tensor:
+    """Router-weighted sum of each token's expert rows (+ shared expert) into ``out``."""
+    _dev(ye, "ye", (torch.float32, torch.bfloat16))
+    _dev(row_of, "row_of", torch.int32)
+    _dev(topk_w, "topk_w", torch.float32)
+    _dev(out, "out", ye.dtype)
+    N, H = out.shape
+    K = topk_w.shape[-1] if topk_w.dim() == 2 else (topk_w.numel() // N if N else 1)
+    if shared_y is not None:
+        _dev(shared_y, "shared_y", ye.dtype)
+    _check(lib().moe_combine(_ptr(ye), _act_code(ye.dtype), ye.shape[0], _ptr(row_of), _ptr(topk_w), N, K, H,
+                             _ptr(shared_y), self_lo, self_hi, _ptr(out), _stream()), "moe_combine")
+    return out

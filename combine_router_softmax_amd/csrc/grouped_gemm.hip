@@ -1,0 +1,542 @@
+// Grouped SwiGLU expert FFN (Perplexity, "Lower latency and higher throughput
+// with multi-node DeepSeek deployment", sections GroupGEMM and Quantization).
+//
+// Two products per expert g over the rows it holds:
+//   up   : h = silu(A W_gate^T) * (A W_up^T)   A [m_g, H], W13 [2I, H]  -> h [m_g, I]
+//   down : y = h W2^T                          W2 [H, I]               -> y [m_g, H]
+// Both are "NT" products: activations and weights are contiguous along the
+// reduction dimension.
+//
+// Work decomposition (routing-aware, persistent; the page's point that kernels
+// must read the per-expert counts on the device rather than size the work from
+// the buffer bound): a fixed grid of workgroups walks a tile list built in
+// every workgroup from the device counts. A tile is (expert, 128-row block,
+// N block); row blocks are the fastest index, so workgroups that share a
+// weight block run side by side and the weight block is fetched from HBM
+// once. Empty experts produce no tiles.
+//
+// Tile (4 waves): up = 128 rows x 64 h columns, i.e. 64 gate + 64 up weight
+// rows; down = 128 rows x 128 output columns. Each wave owns 32 weight rows
+// (up: 16 gate + the 16 matching up rows, so SwiGLU pairs land in one lane)
+// and all row blocks. MFMA v_mfma_f32_32x32x16_bf16 with the weights as the
+// A operand (32 weight rows) and the activations as the B operand (32 rows);
+// 32-row blocks with no rows are skipped, so a decode expert with ~32 rows
+// costs one MFMA column block while the weights stream once.
+//
+// Data path per 128-deep K chunk: each lane loads 64 contiguous bytes of its
+// weight row straight from HBM into registers (one chunk ahead), and the
+// workgroup stages the activation chunk [128 rows x 128] in LDS (double
+// buffer, one barrier per chunk). The reduction order inside a chunk is
+// permuted identically for both operands so every weight load is a 64-byte
+// run.
+//
+// fp8 e4m3 weights: codes are decoded exactly to bf16 in registers
+// (v_cvt_scalef32_pk_bf16_fp8 with unit scale), the chunk is accumulated
+// separately, and the fp32 128x128 block scale is applied to that partial sum
+// (scale blocks align with the 128-deep chunks and the 64/128-row tiles).
+//
+// fp32 activations + fp32 weights (small parity problems) use a plain SIMT
+// kernel with the same scheduler.
+#include "moe_common.hpp"
+
+namespace moe {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kGemmThreads = 256;
+constexpr int kBM = 128;            // rows per tile
+constexpr int kMB = kBM / 32;       // 32-row MFMA blocks per tile
+constexpr int kKC = 128;            // reduction chunk
+constexpr int kLdsStride = kKC + 8; // bf16 per staged activation row (272 B, 16-B aligned)
+constexpr int kMaxGroups = 512;
+constexpr int kGemmMaxSrc = 512;
+
+enum { kUp = 0, kDown = 1 };
+
+struct GemmArgs {
+  const void* a;              // [rows, K] activations (x for up, h for down)
+  int64_t rows;               // R
+  const int32_t* counts;      // [G, S] (padded)
+  const int32_t* group_off;   // [G + 1] (compact)
+  int G, S, C, layout;
+  const void* w;              // [G, n_w_rows, K]
+  const float* s;             // fp8: [G, n_w_rows/128, K/128]
+  int n_w_rows;               // 2I (up) or H (down)
+  int K;                      // reduction length
+  void* out;                  // [rows, n_out]
+  int n_out;                  // I (up) or H (down)
+  int n_tiles_n;              // N tiles per expert
+};
+
+struct Sched {
+  int tile_start[kMaxGroups + 1];
+  int m[kMaxGroups];
+  int seg[kGemmMaxSrc + 1];
+  int rowmap[kBM];
+  int tmp[kGemmThreads];
+  int cur_seg_group;
+};
+
+// Rows per expert from the device counts (clamped so every row stays inside
+// [0, rows)), then the exclusive prefix of tiles per expert. Returns the tile
+// count. All threads must call it.
+__device__ int build_schedule(const GemmArgs& p, int bm, Sched& sh) {
+  const int tid = threadIdx.x;
+  if (p.layout == MOE_LAYOUT_COMPACT) {
+    for (int g = tid; g < p.G; g += kGemmThreads) {
+      const int64_t lo = min<int64_t>(max<int64_t>(p.group_off[g], 0), p.rows);
+      const int64_t hi = min<int64_t>(max<int64_t>(p.group_off[g + 1], lo), p.rows);
+      sh.m[g] = int(hi - lo);
+    }
+  } else {
+    for (int g = tid; g < p.G; g += kGemmThreads) sh.m[g] = 0;
+    __syncthreads();
+    for (int i = tid; i < p.G * p.S; i += kGemmThreads) {
+      const int c = min(max(p.counts[i], 0), p.C);
+      if (c) atomicAdd(&sh.m[i / p.S], c);
+    }
+  }
+  __syncthreads();
+  for (int g = tid; g < p.G; g += kGemmThreads) sh.tile_start[g] = (sh.m[g] + bm - 1) / bm * p.n_tiles_n;
+  __syncthreads();
+  const int total = block_scan_lds<false, kGemmThreads>(sh.tile_start, p.G, sh.tmp);
+  if (tid == 0) {
+    sh.tile_start[p.G] = total;
+    sh.cur_seg_group = -1;
+  }
+  __syncthreads();
+  return total;
+}
+
+struct Tile {
+  int g, nt, r0, nrows;
+};
+
+__device__ Tile decode_tile(const GemmArgs& p, int bm, const Sched& sh, int t) {
+  int lo = 0, hi = p.G;  // last g with tile_start[g] <= t
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (sh.tile_start[mid] <= t) lo = mid;
+    else hi = mid;
+  }
+  Tile tl;
+  tl.g = lo;
+  const int local = t - sh.tile_start[lo];
+  const int mtiles = (sh.m[lo] + bm - 1) / bm;
+  tl.nt = local / mtiles;
+  tl.r0 = (local % mtiles) * bm;
+  tl.nrows = min(bm, sh.m[lo] - tl.r0);
+  return tl;
+}
+
+// Physical row of each of the tile's rows (-1 past the expert's rows).
+__device__ void build_rowmap(const GemmArgs& p, const Tile& tl, int bm, Sched& sh) {
+  const int tid = threadIdx.x;
+  if (p.layout == MOE_LAYOUT_COMPACT) {
+    if (tid < bm) {
+      const int64_t base = min<int64_t>(max<int64_t>(p.group_off[tl.g], 0), p.rows);
+      sh.rowmap[tid] = tid < tl.nrows ? int(base + tl.r0 + tid) : -1;
+    }
+    __syncthreads();
+    return;
+  }
+  if (sh.cur_seg_group != tl.g) {  // uniform: every thread reads the same LDS word
+    __syncthreads();
+    for (int s = tid; s < p.S; s += kGemmThreads) sh.seg[s] = min(max(p.counts[tl.g * p.S + s], 0), p.C);
+    __syncthreads();
+    const int tot = block_scan_lds<false, kGemmThreads>(sh.seg, p.S, sh.tmp);
+    if (tid == 0) {
+      sh.seg[p.S] = tot;
+      sh.cur_seg_group = tl.g;
+    }
+    __syncthreads();
+  }
+  if (tid < bm) {
+    int phys = -1;
+    if (tid < tl.nrows) {
+      const int li = tl.r0 + tid;
+      int lo = 0, hi = p.S;  // last s with seg[s] <= li
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (sh.seg[mid] <= li) lo = mid;
+        else hi = mid;
+      }
+      phys = (tl.g * p.S + lo) * p.C + (li - sh.seg[lo]);
+    }
+    sh.rowmap[tid] = phys;
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ float silu_f(float g) { return g / (1.f + __expf(-g)); }
+
+// e4m3fn x 8 (two dwords) -> bf16 x 8, exact.
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  bf16x8_t r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+// ------------------------------------------------------------------ MFMA kernel
+template <int KIND, bool FP8>
+__global__ __launch_bounds__(kGemmThreads, 2) void ffn_mfma_kernel(GemmArgs p) {
+  __shared__ Sched sh;
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][kBM * kLdsStride];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
+  const int lr = lane & 31;   // MFMA row/column inside a 32 block
+  const int lh = lane >> 5;   // which half of the 16-deep MFMA step this lane feeds
+  const int n_tiles = build_schedule(p, kBM, sh);
+  const int nchunks = p.K / kKC;
+  const uint16_t* A = static_cast<const uint16_t*>(p.a);
+
+  for (int t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+    const Tile tl = decode_tile(p, kBM, sh, t);
+    build_rowmap(p, tl, kBM, sh);
+    const int nb = (tl.nrows + 31) / 32;  // active 32-row blocks (uniform)
+
+    // weight row of this lane
+    int wrow;
+    if (KIND == kUp) {
+      const int j = tl.nt * 64 + 16 * wv + (lr & 15);
+      wrow = lr < 16 ? j : p.n_out + j;
+    } else {
+      wrow = tl.nt * 128 + 32 * wv + lr;
+    }
+    const size_t wrow_elems = (size_t(tl.g) * p.n_w_rows + wrow) * p.K;
+
+    // fp8 block scales used by this tile's rows (uniform per workgroup)
+    int srow0 = 0, srow1 = 0;
+    if (FP8) {
+      if (KIND == kUp) {
+        srow0 = (tl.nt * 64) / 128;
+        srow1 = (p.n_out + tl.nt * 64) / 128;
+      } else {
+        srow0 = srow1 = tl.nt;
+      }
+    }
+    const float* sbase = FP8 ? p.s + size_t(tl.g) * (p.n_w_rows / 128) * nchunks : nullptr;
+
+    // activation staging: thread -> (row = tid/16 + 16*i, 16-byte column tid%16)
+    const int xr = tid >> 4, xc = (tid & 15) * 8;
+    auto load_x = [&](uint4* xv, int c) {
+#pragma unroll
+      for (int i = 0; i < kBM / 16; ++i) {
+        const int r = xr + 16 * i;
+        const int phys = sh.rowmap[r];
+        if (i * 16 < nb * 32 && phys >= 0)
+          xv[i] = *reinterpret_cast<const uint4*>(A + size_t(phys) * p.K + size_t(c) * kKC + xc);
+        else
+          xv[i] = make_uint4(0, 0, 0, 0);
+      }
+    };
+    auto store_x = [&](const uint4* xv, int buf) {
+#pragma unroll
+      for (int i = 0; i < kBM / 16; ++i)
+        if (i * 16 < nb * 32)
+          *reinterpret_cast<uint4*>(&xs[buf][(xr + 16 * i) * kLdsStride + xc]) = xv[i];
+    };
+
+    constexpr int WV = FP8 ? 4 : 8;  // 16-byte weight loads per lane per chunk
+    auto load_w = [&](uint4* wvv, int c) {
+      if (FP8) {
+        const uint8_t* wp = static_cast<const uint8_t*>(p.w) + wrow_elems + size_t(c) * kKC + 64 * lh;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wvv[j] = *reinterpret_cast<const uint4*>(wp + 16 * j);
+      } else {
+        const uint16_t* wp = static_cast<const uint16_t*>(p.w) + wrow_elems + size_t(c) * kKC + 32 * lh;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) wvv[sb * 4 + j] = *reinterpret_cast<const uint4*>(wp + 64 * sb + 8 * j);
+      }
+    };
+
+    f32x16_t acc[kMB];
+#pragma unroll
+    for (int b = 0; b < kMB; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
+
+    uint4 wcur[WV], wnxt[WV], xv[kBM / 16];
+    load_w(wcur, 0);
+    load_x(xv, 0);
+    store_x(xv, 0);
+
+    for (int c = 0; c < nchunks; ++c) {
+      const bool more = c + 1 < nchunks;
+      if (more) {
+        load_w(wnxt, c + 1);
+        load_x(xv, c + 1);
+      }
+      __syncthreads();
+      const uint16_t* xb = xs[c & 1];
+      if (FP8) {
+        f32x16_t part[kMB];
+#pragma unroll
+        for (int b = 0; b < kMB; ++b)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) part[b][v] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint4 q = wcur[j >> 1];
+          const bf16x8_t a = (j & 1) ? fp8x8_to_bf16(q.z, q.w) : fp8x8_to_bf16(q.x, q.y);
+          const int col = 64 * lh + 8 * j;
+#pragma unroll
+          for (int b = 0; b < kMB; ++b) {
+            if (b < nb) {
+              const uint4 bv = *reinterpret_cast<const uint4*>(&xb[(b * 32 + lr) * kLdsStride + col]);
+              part[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bv), part[b], 0, 0,
+                                                                 0);
+            }
+          }
+        }
+        const float s0 = sbase[srow0 * nchunks + c];
+        const float s1 = sbase[srow1 * nchunks + c];
+#pragma unroll
+        for (int b = 0; b < kMB; ++b) {
+          if (b < nb) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[b][v] = fmaf(v < 8 ? s0 : s1, part[b][v], acc[b][v]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, wcur[sb * 4 + j]);
+            const int col = 64 * sb + 32 * lh + 8 * j;
+#pragma unroll
+            for (int b = 0; b < kMB; ++b) {
+              if (b < nb) {
+                const uint4 bv = *reinterpret_cast<const uint4*>(&xb[(b * 32 + lr) * kLdsStride + col]);
+                acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bv), acc[b], 0, 0,
+                                                                  0);
+              }
+            }
+          }
+        }
+      }
+      if (more) {
+        store_x(xv, (c + 1) & 1);
+#pragma unroll
+        for (int j = 0; j < WV; ++j) wcur[j] = wnxt[j];
+      }
+    }
+
+    // epilogue: lane holds rows 8q + 4*lh + r (q = v/4, r = v%4) of the wave's
+    // 32 weight rows, for activation row lr of each block
+    uint16_t* out = static_cast<uint16_t*>(p.out);
+#pragma unroll
+    for (int b = 0; b < kMB; ++b) {
+      if (b >= nb) continue;
+      const int phys = sh.rowmap[b * 32 + lr];
+      if (phys < 0) continue;
+      uint16_t* orow = out + size_t(phys) * p.n_out;
+      if (KIND == kUp) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          float h[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) h[r] = silu_f(acc[b][4 * q + r]) * acc[b][4 * (q + 2) + r];
+          const int col = tl.nt * 64 + 16 * wv + 8 * q + 4 * lh;
+          *reinterpret_cast<uint2*>(orow + col) = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = tl.nt * 128 + 32 * wv + 8 * q + 4 * lh;
+          *reinterpret_cast<uint2*>(orow + col) =
+              make_uint2(pack_bf16x2(acc[b][4 * q], acc[b][4 * q + 1]), pack_bf16x2(acc[b][4 * q + 2], acc[b][4 * q + 3]));
+        }
+      }
+    }
+    __syncthreads();  // rowmap and staging buffers are rewritten by the next tile
+  }
+}
+
+// ------------------------------------------------------------------ fp32 SIMT kernel
+constexpr int kFBM = 32;  // rows per tile
+constexpr int kFBN = 32;  // output columns per tile
+constexpr int kFKC = 32;  // reduction chunk
+
+template <int KIND>
+__global__ __launch_bounds__(kGemmThreads) void ffn_f32_kernel(GemmArgs p) {
+  __shared__ Sched sh;
+  __shared__ float xs[kFBM][kFKC + 1];
+  __shared__ float ws[2 * kFBN][kFKC + 1];
+  const int tid = threadIdx.x;
+  const int n_tiles = build_schedule(p, kFBM, sh);
+  const float* A = static_cast<const float*>(p.a);
+  const float* W = static_cast<const float*>(p.w);
+  float* out = static_cast<float*>(p.out);
+  const int nwr = KIND == kUp ? 2 * kFBN : kFBN;  // weight rows staged per tile
+  const int row = tid / 8;                         // 0..31
+  const int cg = (tid % 8) * 4;                    // 4 output columns
+
+  for (int t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+    const Tile tl = decode_tile(p, kFBM, sh, t);
+    build_rowmap(p, tl, kFBM, sh);
+    float g[4] = {0.f, 0.f, 0.f, 0.f}, u[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < p.K; k0 += kFKC) {
+      for (int i = tid; i < kFBM * kFKC; i += kGemmThreads) {
+        const int r = i / kFKC, k = i % kFKC;
+        const int phys = sh.rowmap[r];
+        xs[r][k] = phys >= 0 ? A[size_t(phys) * p.K + k0 + k] : 0.f;
+      }
+      for (int i = tid; i < nwr * kFKC; i += kGemmThreads) {
+        const int r = i / kFKC, k = i % kFKC;
+        int wr;
+        if (KIND == kUp) wr = r < kFBN ? tl.nt * kFBN + r : p.n_out + tl.nt * kFBN + (r - kFBN);
+        else wr = tl.nt * kFBN + r;
+        ws[r][k] = W[(size_t(tl.g) * p.n_w_rows + wr) * p.K + k0 + k];
+      }
+      __syncthreads();
+#pragma unroll 4
+      for (int k = 0; k < kFKC; ++k) {
+        const float xv = xs[row][k];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          g[c] = fmaf(xv, ws[cg + c][k], g[c]);
+          if (KIND == kUp) u[c] = fmaf(xv, ws[kFBN + cg + c][k], u[c]);
+        }
+      }
+      __syncthreads();
+    }
+    const int phys = sh.rowmap[row];
+    if (phys >= 0) {
+      float* orow = out + size_t(phys) * p.n_out + tl.nt * kFBN + cg;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) orow[c] = KIND == kUp ? silu_f(g[c]) * u[c] : g[c];
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+static bool ggemm_desc_ok(const moe_ggemm_desc_t* d) {
+  if (!d) return false;
+  if (d->n_groups < 0 || d->hidden < 1 || d->inter < 1 || d->rows < 0) return false;
+  if (d->layout != MOE_LAYOUT_COMPACT && d->layout != MOE_LAYOUT_PADDED) return false;
+  if (d->stage != MOE_GG_FULL && d->stage != MOE_GG_UP && d->stage != MOE_GG_DOWN) return false;
+  if (d->layout == MOE_LAYOUT_PADDED) {
+    if (d->n_src < 1 || d->capacity < 0) return false;
+    if (int64_t(d->n_groups) * d->n_src * d->capacity > d->rows) return false;
+  }
+  return true;
+}
+
+static bool ggemm_desc_supported(const moe_ggemm_desc_t* d) {
+  const bool f32 = d->act_dt == MOE_F32 && d->w_dt == MOE_F32;
+  const bool bf16 = d->act_dt == MOE_BF16 && (d->w_dt == MOE_BF16 || d->w_dt == MOE_FP8_E4M3);
+  if (!f32 && !bf16) return false;
+  if (d->hidden % 128 || d->inter % 128) return false;
+  if (d->n_groups > kMaxGroups) return false;
+  if (d->layout == MOE_LAYOUT_PADDED && d->n_src > kGemmMaxSrc) return false;
+  if (d->rows >= (int64_t(1) << 31)) return false;
+  return true;
+}
+
+MOE_API size_t moe_grouped_gemm_workspace(const moe_ggemm_desc_t* d) {
+  if (!ggemm_desc_ok(d)) return 0;
+  const size_t el = d->act_dt == MOE_F32 ? 4 : 2;
+  return align_up(size_t(d->rows) * size_t(d->inter) * el, 256) + 256;
+}
+
+namespace moe {
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int cu = 0;
+  if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0) cu = 256;
+  if (dev < 64) cached[dev] = cu;
+  return cu;
+}
+}  // namespace moe
+
+static moe_status_t launch_stage(const GemmArgs& p, bool f32, bool fp8, int kind, hipStream_t stream) {
+  const int bm = f32 ? kFBM : kBM;
+  const int64_t upper = int64_t(p.n_tiles_n) * ((p.rows + bm - 1) / bm + p.G);
+  if (upper <= 0) return MOE_OK;
+  const int64_t resident = int64_t(device_cu_count()) * (f32 ? 4 : 2);
+  const dim3 grid(unsigned(upper < resident ? upper : resident)), block(kGemmThreads);
+  if (f32) {
+    if (kind == kUp) hipLaunchKernelGGL(ffn_f32_kernel<kUp>, grid, block, 0, stream, p);
+    else hipLaunchKernelGGL(ffn_f32_kernel<kDown>, grid, block, 0, stream, p);
+  } else if (fp8) {
+    if (kind == kUp) hipLaunchKernelGGL((ffn_mfma_kernel<kUp, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((ffn_mfma_kernel<kDown, true>), grid, block, 0, stream, p);
+  } else {
+    if (kind == kUp) hipLaunchKernelGGL((ffn_mfma_kernel<kUp, false>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((ffn_mfma_kernel<kDown, false>), grid, block, 0, stream, p);
+  }
+  return launch_status();
+}
+
+MOE_API moe_status_t moe_grouped_gemm(const moe_ggemm_desc_t* d, const void* a, const int32_t* counts,
+                                      const int32_t* group_off, const void* w13, const void* w2, const float* s13,
+                                      const float* s2, void* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!ggemm_desc_ok(d)) return MOE_ERR_INVALID_ARG;
+  if (!ggemm_desc_supported(d)) return MOE_ERR_UNSUPPORTED;
+  if (d->n_groups == 0 || d->rows == 0) return MOE_OK;
+  const bool f32 = d->act_dt == MOE_F32;
+  const bool fp8 = d->w_dt == MOE_FP8_E4M3;
+  const bool up = d->stage != MOE_GG_DOWN, down = d->stage != MOE_GG_UP;
+  if (d->layout == MOE_LAYOUT_COMPACT && !group_off) return MOE_ERR_INVALID_ARG;
+  if (d->layout == MOE_LAYOUT_PADDED && !counts) return MOE_ERR_INVALID_ARG;
+  if (up && (!a || !w13 || !aligned16(a) || !aligned16(w13))) return MOE_ERR_INVALID_ARG;
+  if (down && (!y || !w2 || !aligned16(y) || !aligned16(w2))) return MOE_ERR_INVALID_ARG;
+  if (fp8 && ((up && !s13) || (down && !s2))) return MOE_ERR_INVALID_ARG;
+  if (!ws || !aligned16(ws) || ws_bytes < moe_grouped_gemm_workspace(d)) return MOE_ERR_WORKSPACE;
+
+  GemmArgs p;
+  p.rows = d->rows;
+  p.counts = counts;
+  p.group_off = group_off;
+  p.G = d->n_groups;
+  p.S = d->layout == MOE_LAYOUT_PADDED ? d->n_src : 1;
+  p.C = d->layout == MOE_LAYOUT_PADDED ? d->capacity : 0;
+  p.layout = d->layout;
+  moe_status_t st = MOE_OK;
+  if (up) {
+    p.a = a;
+    p.w = w13;
+    p.s = s13;
+    p.n_w_rows = 2 * d->inter;
+    p.K = d->hidden;
+    p.out = ws;
+    p.n_out = d->inter;
+    p.n_tiles_n = f32 ? d->inter / kFBN : d->inter / 64;
+    st = launch_stage(p, f32, fp8, kUp, stream);
+    if (st != MOE_OK) return st;
+  }
+  if (down) {
+    p.a = ws;
+    p.w = w2;
+    p.s = s2;
+    p.n_w_rows = d->hidden;
+    p.K = d->inter;
+    p.out = y;
+    p.n_out = d->hidden;
+    p.n_tiles_n = f32 ? d->hidden / kFBN : d->hidden / 128;
+    st = launch_stage(p, f32, fp8, kDown, stream);
+  }
+  return st;
+}

@@ -1,0 +1,120 @@
+"""One step of the one-GPU MoE-layer share, as a sequence of the five C-ABI calls.
+
+Host orchestration only: buffers are allocated once (PyTorch device memory)
+and every step enqueues route -> layout -> dispatch -> grouped GEMM (routed,
+then shared expert) -> combine on the current stream. No host synchronisation
+inside a step: the expert buffer is sized for the worst case (compact) or for
+the fixed rectangle (padded), and the kernels read the real counts on the
+device.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import (COMPACT, GG_DOWN, GG_FULL, GG_UP, PADDED, gemm_desc, moe_combine, moe_dispatch, moe_dispatch_layout,
+               moe_grouped_gemm, moe_grouped_gemm_workspace, moe_layout_rows, moe_route_topk)
+
+
+class MoEShare:
+    """Buffers and weights for one GPU's share of the layer."""
+
+    def __init__(self, *, n_tokens: int, hidden: int, inter: int, n_experts: int, top_k: int, n_src: int,
+                 expert_lo: int, n_local: int, act_dtype: torch.dtype, layout: int = COMPACT,
+                 capacity: Optional[int] = None, self_range=(0, 0), device="cuda"):
+        self.N, self.H, self.I, self.E, self.K = n_tokens, hidden, inter, n_experts, top_k
+        self.S, self.lo, self.L = n_src, expert_lo, n_local
+        self.layout = layout
+        if capacity is None:
+            if layout != COMPACT:
+                raise ValueError("the padded layout needs an explicit capacity (rows per expert and source)")
+            capacity = n_tokens * min(top_k, n_local)
+        self.capacity = capacity
+        self.self_lo, self.self_hi = self_range
+        self.act_dtype = act_dtype
+        self.dev = torch.device(device)
+        self.R = moe_layout_rows(n_tokens, top_k, n_experts, n_src, expert_lo, n_local, layout, capacity)
+        d = self.dev
+        self.topk_idx = torch.empty((n_tokens, top_k), dtype=torch.int32, device=d)
+        self.topk_w = torch.empty((n_tokens, top_k), dtype=torch.float32, device=d)
+        self.lay = None
+        self.xe = torch.empty((max(self.R, 1), hidden), dtype=act_dtype, device=d)
+        self.ye = torch.empty((max(self.R, 1), hidden), dtype=act_dtype, device=d)
+        B0 = self.self_hi - self.self_lo
+        self.ys = torch.empty((max(B0, 1), hidden), dtype=act_dtype, device=d)
+        self.shared_off = torch.tensor([0, B0], dtype=torch.int32, device=d)
+        self.w = None
+        self.sw = None
+        self.ws = None
+        self.sws = None
+
+    # weights: dict with w13 [G,2I,H], w2 [G,H,I], optional s13/s2 (host or device tensors)
+    def set_weights(self, routed: dict, shared: Optional[dict] = None):
+        def todev(wd):
+            if wd is None:
+                return None
+            return {k: (v.to(self.dev).contiguous() if isinstance(v, torch.Tensor) else v)
+                    for k, v in wd.items() if k in ("w13", "w2", "s13", "s2")}
+        self.w = todev(routed)
+        self.sw = todev(shared)
+        wdt = self.w["w13"].dtype
+        desc = gemm_desc(self.L, self.H, self.I, self.act_dtype, wdt, self.layout, self.S, self.capacity, self.R)
+        self.ws = torch.empty(moe_grouped_gemm_workspace(desc), dtype=torch.uint8, device=self.dev)
+        if self.sw is not None:
+            B0 = self.self_hi - self.self_lo
+            sdesc = gemm_desc(1, self.H, self.I, self.act_dtype, self.sw["w13"].dtype, COMPACT, 1, 0, max(B0, 1))
+            self.sws = torch.empty(moe_grouped_gemm_workspace(sdesc), dtype=torch.uint8, device=self.dev)
+
+    def route(self, logits):
+        moe_route_topk(logits, self.K, True, self.topk_idx, self.topk_w)
+
+    def layout_step(self, src_offsets):
+        self.lay = moe_dispatch_layout(self.topk_idx, src_offsets, self.E, self.lo, self.L, self.layout,
+                                       self.capacity, out=self.lay)
+
+    def dispatch(self, x):
+        moe_dispatch(x, self.lay["row_of"], self.K, self.R, self.xe)
+
+    def gemm(self, stage=GG_FULL):
+        w = self.w
+        moe_grouped_gemm(self.xe[: self.R], w["w13"], w["w2"], group_off=self.lay["expert_off"],
+                         counts=self.lay["counts"], s13=w.get("s13"), s2=w.get("s2"), layout=self.layout,
+                         n_src=self.S, capacity=self.capacity, stage=stage, y=self.ye[: self.R], ws=self.ws)
+
+    def shared_gemm(self, x, stage=GG_FULL):
+        if self.sw is None or self.self_hi <= self.self_lo:
+            return
+        sw = self.sw
+        a = x[self.self_lo: self.self_hi]
+        moe_grouped_gemm(a, sw["w13"], sw["w2"], group_off=self.shared_off, s13=sw.get("s13"), s2=sw.get("s2"),
+                         layout=COMPACT, stage=stage, y=self.ys[: a.shape[0]], ws=self.sws)
+
+    def combine(self, out):
+        sy = self.ys if (self.sw is not None and self.self_hi > self.self_lo) else None
+        moe_combine(self.ye[: max(self.R, 1)] if self.R else self.ye[:0], self.lay["row_of"], self.topk_w, out, sy,
+                    self.self_lo, self.self_hi)
+
+    def step(self, logits, src_offsets, x, out, events: Optional[dict] = None):
+        """One full pass. ``events`` maps step names to (start, end) CUDA events
+        recorded around each call on the current stream."""
+        def run(name, fn):
+            if events is not None and name in events:
+                events[name][0].record()
+                fn()
+                events[name][1].record()
+            else:
+                fn()
+
+        run("route", lambda: self.route(logits))
+        run("layout", lambda: self.layout_step(src_offsets))
+        run("dispatch", lambda: self.dispatch(x))
+        run("gemm_up", lambda: self.gemm(GG_UP))
+        run("gemm_down", lambda: self.gemm(GG_DOWN))
+        run("shared_up", lambda: self.shared_gemm(x, GG_UP))
+        run("shared_down", lambda: self.shared_gemm(x, GG_DOWN))
+        run("combine", lambda: self.combine(out))
+        return out
+
+
+__all__ = ["MoEShare", "COMPACT", "PADDED"]

@@ -1,0 +1,235 @@
+/*
+ * moe.h - C ABI of the one-GPU share of an expert-parallel MoE layer on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer (Perplexity, "Lower latency and higher throughput with multi-node
+ * DeepSeek deployment", section Expert parallelism): every token is sent to
+ * its top-K routed experts, the expert outputs are summed with the router
+ * weights, and a shared expert present on every GPU adds its output. Under
+ * expert parallelism a GPU holds E/EP routed experts; here the other ranks are
+ * logical source partitions of one global batch held on this GPU.
+ *
+ * Pipeline, one call per step, all enqueued on the caller's stream:
+ *   moe_route_topk       top-K experts and weights per token
+ *   moe_dispatch_layout  per-expert counts, prefix sum, a slot per (token, k)
+ *   moe_dispatch         copy token rows into the expert-grouped buffer
+ *   moe_grouped_gemm     SwiGLU FFN per local expert (and the shared expert)
+ *   moe_combine          weighted sum back in token order
+ *
+ * Conventions for every entry point:
+ *  - Pointers are device pointers unless stated; descriptors and return values
+ *    are host memory. The caller allocates and owns every buffer; the library
+ *    allocates and frees nothing. Scratch comes in through `ws` with a size
+ *    query. Buffers must not alias unless stated.
+ *  - Row-major storage; activation rows must be 16-byte aligned
+ *    (hidden * element size % 16 == 0 and 16-byte aligned base pointers).
+ *  - Every call enqueues on `stream` (NULL = the default stream) and returns
+ *    without synchronising. Argument errors are found on the host and
+ *    returned before anything is enqueued (MOE_ERR_INVALID_ARG,
+ *    MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE); a failed launch returns
+ *    MOE_ERR_HIP. Data-dependent conditions (a count above capacity) are
+ *    reported through a device status word; kernels never write out of bounds
+ *    even when device-side inputs (indices, offsets, counts) are invalid.
+ *  - Results are deterministic: no floating-point atomics anywhere, and the
+ *    integer layout is bit-reproducible.
+ *  - No global mutable state apart from a per-device cache of the compute-unit
+ *    count; calls from several host threads are safe.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* a null pointer with a nonzero size, a size out of range, misalignment */
+  MOE_ERR_UNSUPPORTED = 2, /* a valid request this build does not implement (dtype pair, shape limit) */
+  MOE_ERR_WORKSPACE = 3,   /* ws is NULL or smaller than the size query returned */
+  MOE_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} moe_status_t;
+
+typedef enum {
+  MOE_F32 = 0,
+  MOE_BF16 = 1,
+  MOE_FP8_E4M3 = 2 /* OCP e4m3fn: bias 7, no infinities, max 448 (the gfx950 FP8 format) */
+} moe_dtype_t;
+
+typedef enum {
+  /* Count-first ragged buffer: rows packed by local expert, then by global
+   * token index (lehuy.net, "Decoding high-performance EP kernels", section
+   * Throughput: ask first, send later > Dispatch; Perplexity, "Enabling
+   * trillion-parameter models on AWS EFA", section Send and receive buffers). */
+  MOE_LAYOUT_COMPACT = 0,
+  /* Fixed rectangle: a private region of `capacity` rows per (local expert,
+   * source rank), expert-major, static address (lehuy.net page, section
+   * Latency: send without asking). */
+  MOE_LAYOUT_PADDED = 1
+} moe_layout_t;
+
+/* Bit of the device status word written by moe_dispatch_layout. */
+#define MOE_STATUS_OVERFLOW 1
+
+/* Library version and a readable name for a status code (static strings). */
+int moe_abi_version(void);
+const char* moe_status_string(moe_status_t s);
+
+/* ------------------------------------------------------------------ route
+ * Top-K routing (Perplexity DeepSeek deployment page, section MoE Router:
+ * the router yields top-K expert indices and scores per token; the softmax
+ * rule is the plain, group-free case the page calls Mixtral's).
+ *
+ * logits    [n_tokens, n_experts] float32.
+ * topk_idx  [n_tokens, top_k] int32 out: experts by descending logit, equal
+ *           logits broken by the lower expert index (+0 and -0 compare equal).
+ * topk_w    [n_tokens, top_k] float32 out: softmax(logits)[idx], divided by
+ *           its sum over the K picked when renormalize != 0.
+ * Limits: 1 <= n_experts <= 1024, 1 <= top_k <= min(16, n_experts),
+ *         n_tokens >= 0 (0 enqueues nothing). NaN logits give unspecified
+ *         but in-range indices.
+ */
+moe_status_t moe_route_topk(const float* logits, int n_tokens, int n_experts, int top_k, int renormalize,
+                            int32_t* topk_idx, float* topk_w, hipStream_t stream);
+
+/* ------------------------------------------------------------------ layout */
+typedef struct {
+  int n_tokens;     /* N = sum of B_s */
+  int top_k;        /* K */
+  int n_experts;    /* E (global) */
+  int n_src;        /* S logical source ranks, 1..4096 */
+  int expert_lo;    /* first local expert */
+  int n_local;      /* L local experts [expert_lo, expert_lo + L), 1..1024, L*S <= 65536 */
+  moe_layout_t layout;
+  int capacity;     /* COMPACT: rows available in the expert buffer (worst case N*min(K,L));
+                       PADDED: rows per (expert, source) region (max B_s never overflows) */
+} moe_layout_desc_t;
+
+/* Rows R of the expert-grouped buffer (xe, ye, h): COMPACT capacity,
+ * PADDED n_local * n_src * capacity. Returns -1 for an invalid descriptor. */
+int64_t moe_layout_rows(const moe_layout_desc_t* d);
+
+/* Bytes of scratch moe_dispatch_layout needs; 0 for an invalid descriptor. */
+size_t moe_dispatch_layout_workspace(const moe_layout_desc_t* d);
+
+/* Per-expert aggregation of the routing and a slot for every (token, k)
+ * (Perplexity DeepSeek page, section MoE Router: all-to-all dispatch needs the
+ * routing per expert; AWS EFA page, section Dispatch and combine: per-expert
+ * counts, then their prefix sum gives the offsets; lehuy.net page: the
+ * prefix sum of the counts is the layout, or a static stride times a fixed
+ * maximum in the fixed-rectangle shape).
+ *
+ * topk_idx    [N, K] int32 (any values; those outside the local range are
+ *             not local).
+ * src_offsets [S + 1] int32: source s owns tokens [src_offsets[s],
+ *             src_offsets[s+1]); must start at 0, be nondecreasing and end at
+ *             N (other values are clamped into that shape).
+ * counts      [L, S] int32 out: entries of source s routed to local expert le
+ *             (before any capacity drop), at counts[le * S + s].
+ * expert_off  [L + 1] int32 out: first row of each local expert. COMPACT:
+ *             exclusive prefix sum of the per-expert totals, clipped to
+ *             capacity (expert_off[L] = rows in use). PADDED: le * S * capacity.
+ * row_of      [N * K] int32 out: row of entry (t, k) at t*K + k, or -1 (not
+ *             local, or dropped). COMPACT rows inside one expert follow the
+ *             token order; PADDED entry j of (le, s) sits at
+ *             (le * S + s) * capacity + j.
+ * row_token   [R] int32 out: token held by each row, -1 for an unused row.
+ * status      [1] int32 out: MOE_STATUS_OVERFLOW if a row had to be dropped
+ *             (COMPACT: total above capacity; PADDED: a count above capacity).
+ * ws          scratch of moe_dispatch_layout_workspace(d) bytes.
+ */
+moe_status_t moe_dispatch_layout(const moe_layout_desc_t* d, const int32_t* topk_idx, const int32_t* src_offsets,
+                                 int32_t* counts, int32_t* expert_off, int32_t* row_of, int32_t* row_token,
+                                 int32_t* status, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------ dispatch
+ * Copy each token row into every slot the layout gave it: xe[row_of[t*K+k]] =
+ * x[t] for row_of >= 0 (lehuy.net page, section Throughput > Dispatch: gather
+ * the tokens bound for local experts into one buffer the grouped GEMM reads
+ * at once). Bit-exact copy; unused rows of xe are not written. Each token row
+ * is read once. Entries outside [0, n_rows) are skipped.
+ *
+ * x [n_tokens, hidden] of dtype dt (MOE_F32 or MOE_BF16); xe [n_rows, hidden].
+ */
+moe_status_t moe_dispatch(const void* x, moe_dtype_t dt, int n_tokens, int hidden, int top_k,
+                          const int32_t* row_of, int64_t n_rows, void* xe, hipStream_t stream);
+
+/* ------------------------------------------------------------------ grouped GEMM */
+typedef enum {
+  MOE_GG_FULL = 0, /* both products */
+  MOE_GG_UP = 1,   /* h = silu(a W_gate^T) * (a W_up^T) into the workspace only */
+  MOE_GG_DOWN = 2  /* y = h W2^T from the workspace only (after MOE_GG_UP on the same ws) */
+} moe_gg_stage_t;
+
+typedef struct {
+  int n_groups;        /* G experts in this call (1 for the shared expert) */
+  int hidden;          /* H, multiple of 128 */
+  int inter;           /* I, multiple of 128 */
+  moe_dtype_t act_dt;  /* a, y, workspace h: MOE_F32 or MOE_BF16 */
+  moe_dtype_t w_dt;    /* weights: MOE_F32 with f32 activations; MOE_BF16 or MOE_FP8_E4M3 with bf16 */
+  moe_layout_t layout; /* how rows of a/y are grouped (as moe_dispatch_layout wrote them) */
+  int n_src;           /* PADDED: S */
+  int capacity;        /* PADDED: rows per (group, source) region */
+  int64_t rows;        /* R rows of a, y and h (row indices are shared by all three) */
+  moe_gg_stage_t stage;
+} moe_ggemm_desc_t;
+
+/* Bytes of scratch moe_grouped_gemm needs (the intermediate h [R, I] in the
+ * activation dtype, 256-byte aligned); 0 for an invalid descriptor. */
+size_t moe_grouped_gemm_workspace(const moe_ggemm_desc_t* d);
+
+/* Per-expert SwiGLU FFN over the rows each expert holds (Perplexity DeepSeek
+ * page, section GroupGEMM: g groups, group i a [m_i, k] x [k, n] product;
+ * section Quantization: SiLU activation, fp8 weights with one scale per
+ * 128 x 128 tile; routing-aware kernels read per-expert counts on the device
+ * instead of sizing work from the buffer bound):
+ *   h[r] = silu(W13[g][0:I] a[r]) * (W13[g][I:2I] a[r]),   y[r] = W2[g] h[r]
+ * for every occupied row r of group g, with fp32 accumulation; h and y are
+ * rounded to the activation dtype. Unoccupied rows are not written. Empty
+ * groups cost nothing.
+ *
+ * a          [R, H] activations (act_dt).
+ * counts     [G, S] int32 (PADDED: group g's rows are, for each s,
+ *            (g*S+s)*capacity + [0, min(counts[g*S+s], capacity)) ); may be NULL
+ *            for COMPACT.
+ * group_off  [G + 1] int32 (COMPACT: group g owns rows [group_off[g],
+ *            group_off[g+1])); may be NULL for PADDED.
+ * w13        [G, 2I, H]: gate rows 0..I-1, then up rows I..2I-1 (w_dt; fp8 as raw bytes).
+ * w2         [G, H, I].
+ * s13, s2    fp8 only: float32 scales [G, 2I/128, H/128] and [G, H/128, I/128]; else NULL.
+ * y          [R, H] out (act_dt); unused with MOE_GG_UP.
+ * The shared expert is a call with n_groups = 1, COMPACT, group_off = {0, B}
+ * and a pointing at its B token rows.
+ */
+moe_status_t moe_grouped_gemm(const moe_ggemm_desc_t* d, const void* a, const int32_t* counts,
+                              const int32_t* group_off, const void* w13, const void* w2, const float* s13,
+                              const float* s2, void* y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------ combine
+ * Undo the dispatch permutation and take the router-weighted sum (lehuy.net
+ * page, section Throughput > Combine; AWS EFA page, section MoE all-to-all
+ * over EFA: the combine returns each token's weighted average), summed at the
+ * sender over this GPU's experts (AWS EFA page, section Evaluation). For a
+ * token t with a kept entry, or self_lo <= t < self_hi when shared_y is given:
+ *   out[t] = sum over k ascending with row_of[t*K+k] in [0, n_rows) of
+ *            topk_w[t*K+k] * ye[row] + [t in self] shared_y[t - self_lo]
+ * accumulated in fp32 and rounded once to dt. Other rows of out are not written.
+ *
+ * ye [n_rows, hidden] (dt), topk_w [N, K] float32, shared_y
+ * [self_hi - self_lo, hidden] (dt) or NULL, out [N, hidden] (dt).
+ */
+moe_status_t moe_combine(const void* ye, moe_dtype_t dt, int64_t n_rows, const int32_t* row_of,
+                         const float* topk_w, int n_tokens, int top_k, int hidden, const void* shared_y,
+                         int self_lo, int self_hi, void* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -10,6 +10,7 @@ from .workloads import (  # noqa: F401
     get_config,
     make_inputs,
     make_routing_inputs,
+    make_x,
     make_expert_weights,
     tiny_config,
 )

@@ -1,0 +1,138 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared
+symbol, and rejects bad arguments on the host before touching HIP."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import combine_router_softmax_amd as moe
+from combine_router_softmax_amd import GGemmDesc, LayoutDesc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = ctypes.c_void_p(0x100000)  # never dereferenced: every call below fails validation first
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(moe.lib_path()):
+        pytest.fail("libmoe.so is not built: run python combine_router_softmax_amd/build.py")
+    return moe.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert {"moe_route_topk", "moe_dispatch_layout", "moe_dispatch", "moe_grouped_gemm", "moe_combine"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert moe.moe_abi_version() == 1
+    for s, txt in [(0, b"ok"), (1, b"invalid argument"), (3, b"workspace missing or too small")]:
+        assert lib.moe_status_string(s) == txt
+
+
+def test_binding_exposes_the_same_names():
+    for n in ("moe_route_topk", "moe_dispatch_layout", "moe_dispatch", "moe_grouped_gemm", "moe_combine"):
+        assert callable(getattr(moe, n))
+
+
+def test_route_argument_errors(lib):
+    f = lib.moe_route_topk
+    assert f(FAKE, 10, 16, 17, 1, FAKE, FAKE, None) == INVALID      # top_k > E
+    assert f(FAKE, 10, 16, 0, 1, FAKE, FAKE, None) == INVALID       # top_k < 1
+    assert f(FAKE, -1, 16, 2, 1, FAKE, FAKE, None) == INVALID
+    assert f(FAKE, 10, 2048, 8, 1, FAKE, FAKE, None) == UNSUPPORTED  # E > 1024
+    assert f(FAKE, 10, 64, 20, 1, FAKE, FAKE, None) == UNSUPPORTED   # K > 16
+    assert f(None, 10, 16, 2, 1, FAKE, FAKE, None) == INVALID       # null with work to do
+    assert f(None, 0, 16, 2, 1, None, None, None) == OK             # nothing to do, nothing enqueued
+
+
+def _ld(**kw):
+    base = dict(n_tokens=100, top_k=2, n_experts=16, n_src=4, expert_lo=0, n_local=2, layout=0, capacity=200)
+    base.update(kw)
+    return LayoutDesc(**base)
+
+
+def test_layout_rows_and_workspace(lib):
+    assert lib.moe_layout_rows(ctypes.byref(_ld())) == 200
+    assert lib.moe_layout_rows(ctypes.byref(_ld(layout=1, capacity=30))) == 2 * 4 * 30
+    assert lib.moe_layout_rows(ctypes.byref(_ld(n_src=0))) == -1
+    assert lib.moe_layout_rows(ctypes.byref(_ld(layout=7))) == -1
+    ws = lib.moe_dispatch_layout_workspace(ctypes.byref(_ld()))
+    assert ws > 0 and ws % 256 == 0
+    assert lib.moe_dispatch_layout_workspace(ctypes.byref(_ld(top_k=0))) == 0
+
+
+def test_layout_argument_errors(lib):
+    f = lib.moe_dispatch_layout
+    d = _ld()
+    ws = lib.moe_dispatch_layout_workspace(ctypes.byref(d))
+    args = [FAKE] * 7
+    assert f(ctypes.byref(_ld(top_k=17)), *args, FAKE, ws, None) == INVALID
+    assert f(ctypes.byref(_ld(n_local=2000)), *args, FAKE, ws, None) == UNSUPPORTED
+    assert f(ctypes.byref(_ld(n_src=5000)), *args, FAKE, ws, None) == UNSUPPORTED
+    assert f(ctypes.byref(d), *args, None, ws, None) == WORKSPACE
+    assert f(ctypes.byref(d), *args, FAKE, ws - 4, None) == WORKSPACE
+    assert f(ctypes.byref(d), FAKE, None, *([FAKE] * 5), FAKE, ws, None) == INVALID  # src_offsets NULL
+    assert f(None, *args, FAKE, ws, None) == INVALID
+
+
+def test_dispatch_and_combine_argument_errors(lib):
+    assert lib.moe_dispatch(FAKE, 1, 10, 12, 2, FAKE, 100, FAKE, None) == INVALID     # 24-byte rows
+    assert lib.moe_dispatch(FAKE, 2, 10, 64, 2, FAKE, 100, FAKE, None) == UNSUPPORTED  # fp8 rows
+    assert lib.moe_dispatch(FAKE, 1, 10, 64, 17, FAKE, 100, FAKE, None) == UNSUPPORTED
+    assert lib.moe_dispatch(ctypes.c_void_p(0x100008), 1, 10, 64, 2, FAKE, 100, FAKE, None) == INVALID  # misaligned
+    assert lib.moe_dispatch(None, 1, 0, 64, 2, None, 100, None, None) == OK
+    c = lib.moe_combine
+    assert c(FAKE, 1, 100, FAKE, FAKE, 10, 2, 12, None, 0, 0, FAKE, None) == INVALID  # 24-byte rows
+    assert c(FAKE, 1, 100, FAKE, FAKE, 10, 2, 64, FAKE, 5, 20, FAKE, None) == INVALID  # self range past N
+    assert c(FAKE, 1, 100, FAKE, None, 10, 2, 64, None, 0, 0, FAKE, None) == INVALID   # no weights
+    assert c(None, 1, 0, None, None, 0, 2, 64, None, 0, 0, None, None) == OK
+
+
+def _gd(**kw):
+    base = dict(n_groups=4, hidden=256, inter=128, act_dt=1, w_dt=1, layout=0, n_src=1, capacity=0, rows=64, stage=0)
+    base.update(kw)
+    return GGemmDesc(**base)
+
+
+def test_grouped_gemm_workspace_and_errors(lib):
+    ws = lib.moe_grouped_gemm_workspace(ctypes.byref(_gd()))
+    assert ws >= 64 * 128 * 2
+    assert lib.moe_grouped_gemm_workspace(ctypes.byref(_gd(act_dt=0, w_dt=0))) >= 64 * 128 * 4
+    assert lib.moe_grouped_gemm_workspace(ctypes.byref(_gd(layout=1, n_src=4, capacity=8, rows=100))) == 0
+    f = lib.moe_grouped_gemm
+    ptrs = [FAKE] * 8
+    assert f(ctypes.byref(_gd(hidden=200)), *ptrs, FAKE, ws, None) == UNSUPPORTED          # H % 128
+    assert f(ctypes.byref(_gd(act_dt=0, w_dt=1)), *ptrs, FAKE, ws, None) == UNSUPPORTED    # f32 x bf16
+    assert f(ctypes.byref(_gd(act_dt=1, w_dt=0)), *ptrs, FAKE, ws, None) == UNSUPPORTED    # bf16 x f32
+    assert f(ctypes.byref(_gd(n_groups=600)), *ptrs, FAKE, ws, None) == UNSUPPORTED
+    assert f(ctypes.byref(_gd(stage=5)), *ptrs, FAKE, ws, None) == INVALID
+    assert f(ctypes.byref(_gd()), *ptrs, FAKE, ws - 1, None) == WORKSPACE
+    assert f(ctypes.byref(_gd()), *ptrs, None, ws, None) == WORKSPACE
+    # compact needs group_off, padded needs counts, fp8 needs scales
+    assert f(ctypes.byref(_gd()), FAKE, FAKE, None, *([FAKE] * 5), FAKE, ws, None) == INVALID
+    pd = _gd(layout=1, n_src=4, capacity=4, rows=64)
+    pws = lib.moe_grouped_gemm_workspace(ctypes.byref(pd))
+    assert f(ctypes.byref(pd), FAKE, None, FAKE, *([FAKE] * 5), FAKE, pws, None) == INVALID
+    fd = _gd(w_dt=2)
+    assert f(ctypes.byref(fd), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, ws, None) == INVALID
+    assert f(ctypes.byref(_gd(rows=0)), *ptrs, FAKE, ws, None) == OK   # nothing to do
+
+
+def test_product_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "combine_router_softmax_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, flags=re.M), fn
+                assert "oracle/" not in text, fn

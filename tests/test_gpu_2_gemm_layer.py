@@ -1,0 +1,255 @@
+"""GPU parity: grouped SwiGLU GEMM, combine and the whole layer step.
+
+Tolerances (relative L2 against the float64 oracle on exactly upcast inputs):
+1e-5 with fp32 activations and weights, 2e-2 with bf16, 5e-2 with fp8 e4m3
+weights. Full-size configs compare sampled rows/tokens the oracle computes one
+by one, plus exact integer results and properties that hold at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import combine_router_softmax_amd as moe
+from combine_router_softmax_amd.layer import MoEShare
+from oracle import (COMPACT, PADDED, combine, dispatch, dispatch_layout, group_rows, grouped_ffn, moe_layer,
+                    route_topk, swiglu_ffn, worst_case_rows)
+from synth import get_config, make_expert_weights, make_inputs, make_routing_inputs, tiny_config
+from util import f64, flush, i64, rel_l2, weights_f64
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8_e4m3": 5e-2}
+
+
+class _Lazy:
+    """Item g -> NumPy array (float64 values, or uint8 codes) of a stacked weight tensor."""
+
+    def __init__(self, t, codes=False):
+        self.t, self.codes = t, codes
+
+    def __getitem__(self, g):
+        return self.t[g].cpu().numpy() if self.codes else f64(self.t[g])
+
+    def __len__(self):
+        return self.t.shape[0]
+
+
+def _oracle_weights(wd):
+    fp8 = wd.get("s13") is not None
+    return (_Lazy(wd["w13"], fp8), _Lazy(wd["w2"], fp8),
+            None if not fp8 else wd["s13"].numpy(), None if not fp8 else wd["s2"].numpy())
+
+
+def _dev_weights(wd):
+    return {k: v.cuda() for k, v in wd.items() if k in ("w13", "w2", "s13", "s2") and v is not None}
+
+
+# --------------------------------------------------------------------------- grouped GEMM
+def _gemm_case(cfg, m_per_group, layout, seed=0, S=3, C=None):
+    """Random rows grouped as given; returns GPU y and oracle y on occupied rows."""
+    rng = np.random.default_rng(seed)
+    G = len(m_per_group)
+    H, I = cfg.hidden, cfg.inter
+    wd = make_expert_weights(cfg, seed, experts=range(G))
+    if layout == COMPACT:
+        off = np.concatenate([[0], np.cumsum(m_per_group)]).astype(np.int32)
+        R = int(off[-1]) + 5
+        lay = {"layout": COMPACT, "expert_off": off, "rows": R}
+        counts = None
+    else:
+        counts = np.zeros((G, S), dtype=np.int64)
+        for g, m in enumerate(m_per_group):
+            cuts = np.sort(rng.integers(0, m + 1, size=S - 1))
+            counts[g] = np.diff(np.concatenate([[0], cuts, [m]]))
+        if C is None:
+            C = int(counts.max()) + 2
+        R = G * S * C
+        lay = {"layout": PADDED, "counts": counts, "n_src": S, "capacity": C, "rows": R,
+               "expert_off": np.arange(G + 1) * S * C}
+    act = torch.float32 if cfg.act == "f32" else torch.bfloat16
+    a = torch.from_numpy(rng.standard_normal((R, H)).astype(np.float32)).to(act)
+    y = torch.full((R, H), 3.0, dtype=act, device="cuda")
+    kw = dict(layout=layout, y=y)
+    if layout == COMPACT:
+        kw["group_off"] = torch.from_numpy(lay["expert_off"].astype(np.int32)).cuda()
+    else:
+        kw["counts"] = torch.from_numpy(counts.astype(np.int32)).cuda()
+        kw.update(n_src=S, capacity=C)
+    dw = _dev_weights(wd)
+    moe.moe_grouped_gemm(a.cuda(), dw["w13"], dw["w2"], s13=dw.get("s13"), s2=dw.get("s2"), **kw)
+    ref = grouped_ffn(f64(a), lay, *_oracle_weights(wd))
+    occ = np.zeros(R, dtype=bool)
+    for g in range(G):
+        occ[group_rows(lay, g)] = True
+    got = f64(y)
+    assert np.all(got[~occ] == 3.0), "unoccupied rows must not be written"
+    return got[occ], ref[occ], (a, dw, kw)
+
+
+@pytest.mark.parametrize("layout", [COMPACT, PADDED])
+def test_gemm_f32_tiny_shapes(layout):
+    cfg = tiny_config()
+    got, ref, _ = _gemm_case(cfg, [0, 1, 31, 33, 70, 5], layout)
+    assert rel_l2(got, ref) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("layout", [COMPACT, PADDED])
+@pytest.mark.parametrize("ms", [[0, 1, 31, 32, 33, 127, 128, 129, 300], [5], [0, 0, 7]])
+def test_gemm_bf16_ragged(layout, ms):
+    cfg = get_config("dsv3_decode_ep8", hidden=512, inter=256)
+    got, ref, _ = _gemm_case(cfg, ms, layout, seed=len(ms))
+    if len(ref):
+        assert rel_l2(got, ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("layout", [COMPACT, PADDED])
+def test_gemm_fp8_ragged(layout):
+    cfg = get_config("kimi_k2_ep8", hidden=512, inter=384)
+    got, ref, _ = _gemm_case(cfg, [3, 0, 64, 129, 40], layout, seed=9)
+    assert rel_l2(got, ref) <= TOL["fp8_e4m3"]
+    # the fp8 path must be far better than the bound: it decodes codes exactly
+    assert rel_l2(got, ref) <= 1e-2
+
+
+def test_gemm_stages_match_full_and_are_deterministic():
+    cfg = get_config("dsv3_decode_ep8", hidden=512, inter=256)
+    got, ref, (a, dw, kw) = _gemm_case(cfg, [40, 3, 200], COMPACT, seed=4)
+    y_full = kw["y"].clone()
+    ws = torch.empty(1 << 24, dtype=torch.uint8, device="cuda")
+    kw2 = dict(kw)
+    kw2["y"] = torch.zeros_like(y_full)
+    moe.moe_grouped_gemm(a.cuda(), dw["w13"], dw["w2"], stage=moe.GG_UP, ws=ws, **{k: v for k, v in kw2.items()})
+    moe.moe_grouped_gemm(a.cuda(), dw["w13"], dw["w2"], stage=moe.GG_DOWN, ws=ws, **{k: v for k, v in kw2.items()})
+    occ = slice(0, 243)
+    assert torch.equal(kw2["y"][occ], y_full[occ])
+
+
+# --------------------------------------------------------------------------- whole layer (small)
+def _share_from_inputs(d, layout, cap=None):
+    cfg = d["cfg"]
+    off = d["src_offsets"]
+    N = int(off[-1])
+    act = torch.float32 if cfg.act == "f32" else torch.bfloat16
+    if cap is None and layout == PADDED:
+        cap = int(np.diff(off).max())
+    share = MoEShare(n_tokens=N, hidden=cfg.hidden, inter=cfg.inter, n_experts=cfg.n_experts, top_k=cfg.top_k,
+                     n_src=cfg.n_src, expert_lo=cfg.expert_lo, n_local=cfg.n_local, act_dtype=act, layout=layout,
+                     capacity=cap, self_range=(0, int(off[1])))
+    share.set_weights(d["routed"], d["shared"])
+    return share
+
+
+def _run(share, d, sentinel=-9.0):
+    logits = torch.from_numpy(d["logits"]).cuda()
+    off = torch.from_numpy(d["src_offsets"]).cuda()
+    x = d["x"].cuda()
+    out = torch.full_like(x, sentinel)
+    share.step(logits, off, x, out)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("shared", [False, True])
+@pytest.mark.parametrize("layout", [COMPACT, PADDED])
+@pytest.mark.parametrize("seed", range(16))
+def test_layer_tiny(seed, layout, shared):
+    cfg = tiny_config(shared=shared)
+    d = make_inputs(cfg, seed)
+    share = _share_from_inputs(d, layout)
+    out = _run(share, d)
+    w13, w2, _, _ = _oracle_weights(d["routed"])
+    sh = None
+    if shared:
+        sw = d["shared"]
+        sh = (_Lazy(sw["w13"]), _Lazy(sw["w2"]), None, None)
+    off = d["src_offsets"]
+    ref = moe_layer(f64(d["x"]), d["logits"], off, cfg.top_k, 0, cfg.n_local, w13, w2, shared=sh,
+                    self_range=(0, int(off[1])), layout=layout, capacity=share.capacity,
+                    out_init=np.full(tuple(d["x"].shape), -9.0))
+    got = f64(out)
+    np.testing.assert_array_equal(i64(share.topk_idx), ref["topk_idx"])
+    np.testing.assert_array_equal(i64(share.lay["row_of"]), ref["layout"]["row_of"])
+    touched = ref["out"] != -9.0
+    assert np.all(got[~touched] == -9.0)
+    assert rel_l2(got[touched], ref["out"][touched]) <= TOL["f32"]
+
+
+def test_layer_identity_property_bf16():
+    # combine(dispatch(x)) with identity experts: out = (sum of local weights) * x.
+    cfg = get_config("dsv3_decode_ep8")
+    d = make_routing_inputs(cfg, 1)
+    from synth import make_x
+    x = make_x(cfg, 1, d["src_offsets"]).cuda()
+    logits = torch.from_numpy(d["logits"]).cuda()
+    off = torch.from_numpy(d["src_offsets"]).cuda()
+    N = x.shape[0]
+    idx, w = moe.moe_route_topk(logits, 8)
+    lay = moe.moe_dispatch_layout(idx, off, 256, 0, 32, COMPACT, N * 8)
+    xe = moe.moe_dispatch(x, lay["row_of"], 8, lay["rows"])
+    out = torch.zeros_like(x)
+    moe.moe_combine(xe, lay["row_of"], w, out)
+    ridx, rw = route_topk(d["logits"], 8)
+    local = (ridx < 32)
+    ref = (rw * local).sum(axis=1)[:, None] * f64(x)
+    assert rel_l2(f64(out), ref) <= 4e-3  # one bf16 rounding of each output
+
+
+# --------------------------------------------------------------------------- whole layer (full size)
+FULL = ["dsv3_decode_ep8", "dsv3_decode_ep128", "kimi_k2_ep8", "dsv3_prefill_ep8"]
+
+
+@pytest.fixture(scope="module", params=FULL)
+def full_case(request):
+    cfg = get_config(request.param)
+    flush(f"generate {cfg.name}")
+    d = make_inputs(cfg, 0)
+    yield cfg, d
+    torch.cuda.empty_cache()
+
+
+def _sample_tokens(rng, N, B0, n=12):
+    a = np.sort(rng.choice(B0, size=min(n // 2, B0), replace=False))
+    b = np.sort(rng.choice(np.arange(B0, N), size=min(n - len(a), N - B0), replace=False))
+    return np.concatenate([a, b]).astype(np.int64), len(a)
+
+
+def test_layer_full_size(full_case):
+    cfg, d = full_case
+    flush(f"layer {cfg.name}")
+    off = d["src_offsets"]
+    N, B0 = int(off[-1]), int(off[1])
+    outs = {}
+    for layout in (COMPACT, PADDED):
+        share = _share_from_inputs(d, layout)
+        out = _run(share, d)
+        if layout == COMPACT:
+            ridx, rw = route_topk(d["logits"], cfg.top_k)
+            np.testing.assert_array_equal(i64(share.topk_idx), ridx)
+            assert rel_l2(f64(share.topk_w), rw) <= 1e-5
+            lay = dispatch_layout(ridx, off, cfg.expert_lo, cfg.n_local, COMPACT, share.capacity)
+            np.testing.assert_array_equal(i64(share.lay["row_of"]), lay["row_of"])
+            np.testing.assert_array_equal(i64(share.lay["counts"]).reshape(cfg.n_local, -1), lay["counts"])
+            assert int(share.lay["status"].item()) == 0
+        outs[layout] = out
+        # determinism: a second step gives the same bits
+        out2 = _run(share, d)
+        assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+        del share
+        torch.cuda.empty_cache()
+    # the two layouts compute every row the same way
+    assert torch.equal(outs[COMPACT].view(torch.int16), outs[PADDED].view(torch.int16))
+
+    # sampled tokens, end to end against the oracle on the same tokens
+    rng = np.random.default_rng(5)
+    tok, n_self = _sample_tokens(rng, N, B0, n=8 if cfg.n_local > 8 else 16)
+    w13, w2, s13, s2 = _oracle_weights(d["routed"])
+    sw = d["shared"]
+    sh = (_Lazy(sw["w13"], sw.get("s13") is not None), _Lazy(sw["w2"], sw.get("s2") is not None),
+          None if sw.get("s13") is None else sw["s13"].numpy(), None if sw.get("s2") is None else sw["s2"].numpy())
+    xs = f64(d["x"][torch.from_numpy(tok)])
+    ref = moe_layer(xs, d["logits"][tok], [0, len(tok)], cfg.top_k, cfg.expert_lo, cfg.n_local, w13, w2, s13, s2,
+                    shared=sh, self_range=(0, n_self), out_init=np.full(xs.shape, -9.0))
+    got = f64(outs[COMPACT][torch.from_numpy(tok).cuda()])
+    touched = ref["out"][:, 0] != -9.0
+    assert np.all(got[~touched] == -9.0)
+    assert rel_l2(got[touched], ref["out"][touched]) <= TOL[cfg.weight]
