@@ -33,7 +33,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
-STEP_NAMES = ("route", "layout", "dispatch", "gemm_up", "gemm_down", "shared_up", "shared_down", "combine")
+# the shared expert runs inside the gemm_up / gemm_down launches
+STEP_NAMES = ("route", "layout", "dispatch", "gemm_up", "gemm_down", "combine")
 KERNEL_OF_STEP = {"gemm_up": "ffn_mfma_kernel<up>", "gemm_down": "ffn_mfma_kernel<down>",
                   "dispatch": "dispatch_kernel", "combine": "combine_kernel", "route": "route_topk_kernel"}
 
@@ -77,22 +78,18 @@ def algorithmic_model(cfg, counts, row_of, B0):
     sh_up_w = (2 * I * H * wb + scale_bytes) if cfg.shared else 0
     sh_down_w = (H * I * wb + scale_bytes // 2) if cfg.shared else 0
     B0s = B0 if cfg.shared else 0
+    MS = M + B0s  # rows through the expert FFN: routed plus the shared expert's
     model = {
         "M": M, "U": U, "active_experts": active, "max_rows_per_expert": int(m.max(initial=0)),
         "bytes": {
             "route": N * cfg.n_experts * 4 + N * K * 8,
             "layout": 3 * N * K * 4 + M * 4,
             "dispatch": (U + M) * H * ab + N * K * 4,
-            "gemm_up": up_w + M * H * ab + M * I * ab,
-            "gemm_down": down_w + M * I * ab + M * H * ab,
-            "shared_up": sh_up_w + B0s * H * ab + B0s * I * ab,
-            "shared_down": sh_down_w + B0s * I * ab + B0s * H * ab,
+            "gemm_up": up_w + sh_up_w + MS * H * ab + MS * I * ab,
+            "gemm_down": down_w + sh_down_w + MS * I * ab + MS * H * ab,
             "combine": (M + B0s + UT) * H * ab + N * K * 8,
         },
-        "flops": {
-            "gemm_up": 2 * M * H * 2 * I, "gemm_down": 2 * M * I * H,
-            "shared_up": 2 * B0s * H * 2 * I, "shared_down": 2 * B0s * I * H,
-        },
+        "flops": {"gemm_up": 2 * MS * H * 2 * I, "gemm_down": 2 * MS * I * H},
     }
     return model
 

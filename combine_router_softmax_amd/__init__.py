@@ -18,10 +18,11 @@ import torch
 __all__ = [
     "COMPACT", "PADDED", "GG_FULL", "GG_UP", "GG_DOWN", "STATUS_OVERFLOW", "MoeError", "MoeLibraryMissing",
     "lib", "lib_path", "moe_route_topk", "moe_dispatch_layout", "moe_layout_rows", "moe_dispatch",
-    "moe_grouped_gemm", "moe_combine", "moe_abi_version",
+    "moe_grouped_gemm", "moe_combine", "moe_abi_version", "moe_pack_weights", "W_ROWMAJOR", "W_PACKED",
 ]
 
 COMPACT, PADDED = 0, 1
+W_ROWMAJOR, W_PACKED = 0, 1
 GG_FULL, GG_UP, GG_DOWN = 0, 1, 2
 STATUS_OVERFLOW = 1
 _F32, _BF16, _FP8 = 0, 1, 2
@@ -45,11 +46,16 @@ class LayoutDesc(ctypes.Structure):
                 ("layout", ctypes.c_int), ("capacity", ctypes.c_int)]
 
 
+class SharedExpert(ctypes.Structure):
+    _fields_ = [("a", ctypes.c_void_p), ("rows", ctypes.c_int), ("w13", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+                ("s13", ctypes.c_void_p), ("s2", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+
+
 class GGemmDesc(ctypes.Structure):
     _fields_ = [("n_groups", ctypes.c_int), ("hidden", ctypes.c_int), ("inter", ctypes.c_int),
                 ("act_dt", ctypes.c_int), ("w_dt", ctypes.c_int), ("layout", ctypes.c_int),
                 ("n_src", ctypes.c_int), ("capacity", ctypes.c_int), ("rows", ctypes.c_int64),
-                ("stage", ctypes.c_int)]
+                ("stage", ctypes.c_int), ("shared", ctypes.POINTER(SharedExpert)), ("w_format", ctypes.c_int)]
 
 
 _P = ctypes.c_void_p
@@ -68,6 +74,7 @@ _SIGNATURES = {
     "moe_grouped_gemm_workspace": (_SZ, [ctypes.POINTER(GGemmDesc)]),
     "moe_grouped_gemm": (_I, [ctypes.POINTER(GGemmDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_combine": (_I, [_P, _I, _I64, _P, _P, _I, _I, _I, _P, _I, _I, _P, _P]),
+    "moe_pack_weights": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P]),
 }
 
 
@@ -205,9 +212,30 @@ def moe_dispatch(x: torch.Tensor, row_of: torch.Tensor, top_k: int, n_rows: int,
 
 
 # --------------------------------------------------------------------------- grouped GEMM
-def gemm_desc(n_groups, hidden, inter, act_dtype, w_dtype, layout, n_src, capacity, rows, stage=GG_FULL):
-    w_code = {torch.float32: _F32, torch.bfloat16: _BF16, torch.uint8: _FP8, torch.float8_e4m3fn: _FP8}[w_dtype]
-    return GGemmDesc(n_groups, hidden, inter, _act_code(act_dtype), w_code, layout, n_src, capacity, rows, stage)
+_W_CODE = {torch.float32: _F32, torch.bfloat16: _BF16, torch.uint8: _FP8, torch.float8_e4m3fn: _FP8}
+
+
+def gemm_desc(n_groups, hidden, inter, act_dtype, w_dtype, layout, n_src, capacity, rows, stage=GG_FULL,
+              shared: "SharedExpert | None" = None, w_format: int = W_ROWMAJOR):
+    w_code = _W_CODE[w_dtype]
+    d = GGemmDesc(n_groups, hidden, inter, _act_code(act_dtype), w_code, layout, n_src, capacity, rows, stage)
+    d.w_format = w_format
+    if shared is not None:
+        d.shared = ctypes.pointer(shared)
+    return d
+
+
+def shared_expert(a: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, y: Optional[torch.Tensor],
+                  s13: Optional[torch.Tensor] = None, s2: Optional[torch.Tensor] = None) -> SharedExpert:
+    """Descriptor of the shared expert run inside a moe_grouped_gemm call."""
+    _dev(a, "shared a")
+    _dev(w13, "shared w13")
+    _dev(w2, "shared w2")
+    if y is not None:
+        _dev(y, "shared y", a.dtype)
+    return SharedExpert(a.data_ptr(), a.shape[0], w13.data_ptr(), w2.data_ptr(),
+                        None if s13 is None else s13.data_ptr(), None if s2 is None else s2.data_ptr(),
+                        None if y is None else y.data_ptr())
 
 
 def moe_grouped_gemm_workspace(desc: GGemmDesc) -> int:
@@ -217,8 +245,11 @@ def moe_grouped_gemm_workspace(desc: GGemmDesc) -> int:
 def moe_grouped_gemm(a: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, *, group_off=None, counts=None,
                      s13=None, s2=None, layout: int = COMPACT, n_src: int = 1, capacity: int = 0,
                      stage: int = GG_FULL, y: Optional[torch.Tensor] = None,
-                     ws: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """SwiGLU FFN per expert over the rows each expert holds (see moe.h)."""
+                     ws: Optional[torch.Tensor] = None, shared: Optional[dict] = None,
+                     w_format: int = W_ROWMAJOR) -> torch.Tensor:
+    """SwiGLU FFN per expert over the rows each expert holds (see moe.h).
+
+    ``shared`` = dict(a, w13, w2, y[, s13, s2]) runs the shared expert in the same launches."""
     _dev(a, "a", (torch.float32, torch.bfloat16))
     _dev(w13, "w13")
     _dev(w2, "w2")
@@ -227,12 +258,16 @@ def moe_grouped_gemm(a: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, *, gr
     if H2 != H or I2 % 2:
         raise ValueError("w13 must be [G, 2I, H]")
     I = I2 // 2
-    desc = gemm_desc(G, H, I, a.dtype, w13.dtype, layout, n_src, capacity, R, stage)
+    se = None
+    if shared is not None:
+        se = shared_expert(shared["a"], shared["w13"], shared["w2"], shared.get("y"), shared.get("s13"),
+                           shared.get("s2"))
+    desc = gemm_desc(G, H, I, a.dtype, w13.dtype, layout, n_src, capacity, R, stage, se, w_format)
     wsb = moe_grouped_gemm_workspace(desc)
     if wsb == 0:
         raise MoeError("moe_grouped_gemm: invalid descriptor")
     if ws is None:
-        ws = torch.empty(wsb, dtype=torch.uint8, device=a.device)
+        ws = torch.zeros(wsb, dtype=torch.uint8, device=a.device)
     if y is None and stage != GG_UP:
         y = torch.empty((R, H), dtype=a.dtype, device=a.device)
     for name, t in (("group_off", group_off), ("counts", counts)):
@@ -245,6 +280,17 @@ def moe_grouped_gemm(a: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, *, gr
                                   _ptr(s13), _ptr(s2), _ptr(y), _ptr(ws), ws.numel(), _stream()),
            "moe_grouped_gemm")
     return y
+
+
+def moe_pack_weights(w13: Optional[torch.Tensor], w2: Optional[torch.Tensor], hidden: int, inter: int):
+    """Packed copies of expert weights (w13 [G,2I,H], w2 [G,H,I]; bf16 or fp8 codes)."""
+    ref = w13 if w13 is not None else w2
+    G = ref.shape[0]
+    out13 = None if w13 is None else torch.empty_like(_dev(w13, "w13"))
+    out2 = None if w2 is None else torch.empty_like(_dev(w2, "w2"))
+    _check(lib().moe_pack_weights(G, hidden, inter, _W_CODE[ref.dtype], _ptr(w13), _ptr(w2), _ptr(out13), _ptr(out2),
+                                  _stream()), "moe_pack_weights")
+    return out13, out2
 
 
 # --------------------------------------------------------------------------- combine

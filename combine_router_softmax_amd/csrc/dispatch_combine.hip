@@ -1,9 +1,11 @@
 // Dispatch (token rows -> expert-grouped rows) and combine (expert rows ->
 // router-weighted sum in token order).
 //
-// Both are pure HBM streams: one wavefront per token, 16-byte vector loads and
-// stores, every lane moving consecutive 16-byte pieces of the row so a wave
-// instruction covers 1 KiB of contiguous memory. Dispatch reads each token row
+// Both are pure HBM streams of 16-byte vector loads and stores: a workgroup
+// covers 4 KiB of one token row (consecutive lanes, consecutive 16-byte
+// pieces, so a wave instruction covers 1 KiB of contiguous memory), and a row
+// of 7168 bf16 spreads over 4 workgroups, which gives thousands of independent
+// workgroups to hide HBM latency. Dispatch reads each token row
 // once and writes it to each of its slots (lehuy.net, "Decoding
 // high-performance EP kernels", section Throughput > Dispatch). Combine reads
 // the up-to-K expert rows of a token (and the shared-expert row), accumulates
@@ -15,42 +17,32 @@
 namespace moe {
 namespace {
 
-constexpr int kTokensPerBlock = 4;
+constexpr int kVecThreads = 256;  // one 16-byte piece per thread, 4 KiB of a row per workgroup
 constexpr int kMaxK = 16;
 
-template <int U>
-__global__ __launch_bounds__(kWave * kTokensPerBlock) void dispatch_kernel(
-    const uint4* __restrict__ x, int n_tokens, int row_vecs, int top_k, const int32_t* __restrict__ row_of,
-    int64_t n_rows, uint4* __restrict__ xe) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int t = blockIdx.x * kTokensPerBlock + threadIdx.x / kWave;
-  if (t >= n_tokens) return;
-  int my_row = -1;
-  if (lane < top_k) my_row = row_of[size_t(t) * top_k + lane];
-  const bool ok = lane < top_k && my_row >= 0 && int64_t(my_row) < n_rows;
-  const uint64_t mask = __ballot(ok);
-  if (mask == 0) return;
-  const uint4* src = x + size_t(t) * row_vecs;
-  for (int c0 = 0; c0 < row_vecs; c0 += kWave * U) {
-    uint4 v[U];
+// Workgroup b handles 16-byte pieces [chunk * 256, chunk * 256 + 256) of token
+// t = b / n_chunks: the token's slots are uniform per workgroup (scalar loads),
+// every thread loads one piece and stores it to each slot.
+template <int KMAX>
+__global__ __launch_bounds__(kVecThreads) void dispatch_kernel(const uint4* __restrict__ x, int row_vecs, int n_chunks,
+                                                                int top_k, const int32_t* __restrict__ row_of,
+                                                                int64_t n_rows, uint4* __restrict__ xe) {
+  const int t = blockIdx.x / n_chunks;
+  const int c = (blockIdx.x - t * n_chunks) * kVecThreads + threadIdx.x;
+  const int32_t* ro = row_of + size_t(t) * top_k;
+  int r[KMAX];
+  bool any = false;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = c0 + u * kWave + lane;
-      if (c < row_vecs) v[u] = src[c];
-    }
-    uint64_t m = mask;
-    while (m) {
-      const int k = __ffsll((unsigned long long)m) - 1;
-      m &= m - 1;
-      const int r = __shfl(my_row, k, kWave);
-      uint4* dst = xe + size_t(r) * row_vecs;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = c0 + u * kWave + lane;
-        if (c < row_vecs) dst[c] = v[u];
-      }
-    }
+  for (int k = 0; k < KMAX; ++k) {
+    r[k] = k < top_k ? ro[k] : -1;
+    if (r[k] >= n_rows) r[k] = -1;
+    any |= r[k] >= 0;
   }
+  if (!any || c >= row_vecs) return;
+  const uint4 v = x[size_t(t) * row_vecs + c];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k)
+    if (r[k] >= 0) xe[size_t(r[k]) * row_vecs + c] = v;
 }
 
 // 16-byte piece <-> floats
@@ -86,94 +78,54 @@ struct Vec<uint16_t> {
   }
 };
 
-template <typename T, int KMAX, int U>
-__global__ __launch_bounds__(kWave * kTokensPerBlock) void combine_kernel(
+// Same decomposition as dispatch: each thread owns one 16-byte piece of the
+// output row and sums the token's kept expert rows in k order (all K loads in
+// flight at once), plus the shared-expert row for the GPU's own tokens.
+template <typename T, int KMAX>
+__global__ __launch_bounds__(kVecThreads) void combine_kernel(
     const uint4* __restrict__ ye, int64_t n_rows, const int32_t* __restrict__ row_of, const float* __restrict__ topk_w,
-    int n_tokens, int top_k, int row_vecs, const uint4* __restrict__ shared_y, int self_lo, int self_hi,
+    int top_k, int row_vecs, int n_chunks, const uint4* __restrict__ shared_y, int self_lo, int self_hi,
     uint4* __restrict__ out) {
   constexpr int EPV = Vec<T>::N;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int t = blockIdx.x * kTokensPerBlock + threadIdx.x / kWave;
-  if (t >= n_tokens) return;
-  int my_row = -1;
-  float my_w = 0.f;
-  if (lane < top_k) {
-    my_row = row_of[size_t(t) * top_k + lane];
-    my_w = topk_w[size_t(t) * top_k + lane];
+  const int t = blockIdx.x / n_chunks;
+  const int c = (blockIdx.x - t * n_chunks) * kVecThreads + threadIdx.x;
+  const int32_t* ro = row_of + size_t(t) * top_k;
+  const float* wo = topk_w + size_t(t) * top_k;
+  int r[KMAX];
+  float w[KMAX];
+  bool any = false;
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    r[k] = k < top_k ? ro[k] : -1;
+    if (r[k] >= n_rows) r[k] = -1;
+    w[k] = r[k] >= 0 ? wo[k] : 0.f;
+    any |= r[k] >= 0;
   }
-  const bool ok = lane < top_k && my_row >= 0 && int64_t(my_row) < n_rows;
-  const uint64_t mask = __ballot(ok);
   const bool in_self = shared_y != nullptr && t >= self_lo && t < self_hi;
-  if (mask == 0 && !in_self) return;
-
-  // compact the kept (row, weight) pairs, k ascending, into uniform registers
-  int rows[KMAX];
-  float ws[KMAX];
-  int nk = 0;
-  {
-    uint64_t m = mask;
+  if ((!any && !in_self) || c >= row_vecs) return;
+  uint4 v[KMAX];
 #pragma unroll
-    for (int i = 0; i < KMAX; ++i) {
-      rows[i] = 0;
-      ws[i] = 0.f;
-      if (m) {
-        const int k = __ffsll((unsigned long long)m) - 1;
-        m &= m - 1;
-        rows[i] = __shfl(my_row, k, kWave);
-        ws[i] = __shfl(my_w, k, kWave);
-        nk = i + 1;
-      }
+  for (int k = 0; k < KMAX; ++k) v[k] = r[k] >= 0 ? ye[size_t(r[k]) * row_vecs + c] : make_uint4(0, 0, 0, 0);
+  const uint4 vs = in_self ? shared_y[size_t(t - self_lo) * row_vecs + c] : make_uint4(0, 0, 0, 0);
+  float acc[EPV];
+#pragma unroll
+  for (int e = 0; e < EPV; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    if (r[k] >= 0) {
+      float f[EPV];
+      Vec<T>::load(v[k], f);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) acc[e] = fmaf(w[k], f[e], acc[e]);
     }
   }
-  const uint4* sy = in_self ? shared_y + size_t(t - self_lo) * row_vecs : nullptr;
-  uint4* dst = out + size_t(t) * row_vecs;
-
-  for (int c0 = 0; c0 < row_vecs; c0 += kWave * U) {
-    uint4 v[KMAX][U];
-    uint4 vs[U];
+  if (in_self) {
+    float f[EPV];
+    Vec<T>::load(vs, f);
 #pragma unroll
-    for (int i = 0; i < KMAX; ++i) {
-      if (i < nk) {
-        const uint4* src = ye + size_t(rows[i]) * row_vecs;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int c = c0 + u * kWave + lane;
-          if (c < row_vecs) v[i][u] = src[c];
-        }
-      }
-    }
-    if (in_self) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = c0 + u * kWave + lane;
-        if (c < row_vecs) vs[u] = sy[c];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = c0 + u * kWave + lane;
-      if (c >= row_vecs) continue;
-      float acc[EPV];
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) acc[e] = 0.f;
-#pragma unroll
-      for (int i = 0; i < KMAX; ++i) {
-        if (i < nk) {
-          float f[EPV];
-          Vec<T>::load(v[i][u], f);
-#pragma unroll
-          for (int e = 0; e < EPV; ++e) acc[e] = fmaf(ws[i], f[e], acc[e]);
-        }
-      }
-      if (in_self) {
-        float f[EPV];
-        Vec<T>::load(vs[u], f);
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) acc[e] += f[e];
-      }
-      dst[c] = Vec<T>::store(acc);
-    }
+    for (int e = 0; e < EPV; ++e) acc[e] += f[e];
   }
+  out[size_t(t) * row_vecs + c] = Vec<T>::store(acc);
 }
 
 }  // namespace
@@ -182,6 +134,8 @@ __global__ __launch_bounds__(kWave * kTokensPerBlock) void combine_kernel(
 using namespace moe;
 
 static bool row_dtype_ok(moe_dtype_t dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+
+static int kmax_of(int top_k) { return top_k <= 2 ? 2 : top_k <= 4 ? 4 : top_k <= 8 ? 8 : 16; }
 
 MOE_API moe_status_t moe_dispatch(const void* x, moe_dtype_t dt, int n_tokens, int hidden, int top_k,
                                   const int32_t* row_of, int64_t n_rows, void* xe, hipStream_t stream) {
@@ -193,19 +147,26 @@ MOE_API moe_status_t moe_dispatch(const void* x, moe_dtype_t dt, int n_tokens, i
   if (n_tokens == 0 || n_rows == 0) return MOE_OK;
   if (!x || !row_of || !xe || !aligned16(x) || !aligned16(xe)) return MOE_ERR_INVALID_ARG;
   const int row_vecs = int(row_bytes / 16);
-  const dim3 grid((n_tokens + kTokensPerBlock - 1) / kTokensPerBlock), block(kWave * kTokensPerBlock);
-  hipLaunchKernelGGL(dispatch_kernel<8>, grid, block, 0, stream, static_cast<const uint4*>(x), n_tokens, row_vecs,
-                     top_k, row_of, n_rows, static_cast<uint4*>(xe));
+  const int n_chunks = (row_vecs + kVecThreads - 1) / kVecThreads;
+  if (int64_t(n_chunks) * n_tokens >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  const dim3 grid(unsigned(n_chunks * n_tokens)), block(kVecThreads);
+  const uint4* xv = static_cast<const uint4*>(x);
+  uint4* ov = static_cast<uint4*>(xe);
+  switch (kmax_of(top_k)) {
+    case 2: hipLaunchKernelGGL(dispatch_kernel<2>, grid, block, 0, stream, xv, row_vecs, n_chunks, top_k, row_of, n_rows, ov); break;
+    case 4: hipLaunchKernelGGL(dispatch_kernel<4>, grid, block, 0, stream, xv, row_vecs, n_chunks, top_k, row_of, n_rows, ov); break;
+    case 8: hipLaunchKernelGGL(dispatch_kernel<8>, grid, block, 0, stream, xv, row_vecs, n_chunks, top_k, row_of, n_rows, ov); break;
+    default: hipLaunchKernelGGL(dispatch_kernel<16>, grid, block, 0, stream, xv, row_vecs, n_chunks, top_k, row_of, n_rows, ov); break;
+  }
   return launch_status();
 }
 
 template <typename T, int KMAX>
-static void launch_combine(dim3 grid, dim3 block, hipStream_t stream, const void* ye, int64_t n_rows,
-                           const int32_t* row_of, const float* topk_w, int n_tokens, int top_k, int row_vecs,
-                           const void* shared_y, int self_lo, int self_hi, void* out) {
-  constexpr int U = KMAX > 8 ? 1 : 2;
-  hipLaunchKernelGGL((combine_kernel<T, KMAX, U>), grid, block, 0, stream, static_cast<const uint4*>(ye), n_rows,
-                     row_of, topk_w, n_tokens, top_k, row_vecs, static_cast<const uint4*>(shared_y), self_lo,
+static void launch_combine(dim3 grid, hipStream_t stream, const void* ye, int64_t n_rows, const int32_t* row_of,
+                           const float* topk_w, int top_k, int row_vecs, int n_chunks, const void* shared_y,
+                           int self_lo, int self_hi, void* out) {
+  hipLaunchKernelGGL((combine_kernel<T, KMAX>), grid, dim3(kVecThreads), 0, stream, static_cast<const uint4*>(ye),
+                     n_rows, row_of, topk_w, top_k, row_vecs, n_chunks, static_cast<const uint4*>(shared_y), self_lo,
                      self_hi, static_cast<uint4*>(out));
 }
 
@@ -223,11 +184,12 @@ MOE_API moe_status_t moe_combine(const void* ye, moe_dtype_t dt, int64_t n_rows,
   if (n_rows > 0 && (!ye || !aligned16(ye))) return MOE_ERR_INVALID_ARG;
   if (shared_y && !aligned16(shared_y)) return MOE_ERR_INVALID_ARG;
   const int row_vecs = int(row_bytes / 16);
-  const dim3 grid((n_tokens + kTokensPerBlock - 1) / kTokensPerBlock), block(kWave * kTokensPerBlock);
-  const int kmax = top_k <= 2 ? 2 : top_k <= 4 ? 4 : top_k <= 8 ? 8 : 16;
-#define MOE_COMBINE(T, KM)                                                                                    \
-  launch_combine<T, KM>(grid, block, stream, ye, n_rows, row_of, topk_w, n_tokens, top_k, row_vecs, shared_y, \
-                        self_lo, self_hi, out)
+  const int n_chunks = (row_vecs + kVecThreads - 1) / kVecThreads;
+  if (int64_t(n_chunks) * n_tokens >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  const dim3 grid(unsigned(n_chunks * n_tokens));
+#define MOE_COMBINE(T, KM) \
+  launch_combine<T, KM>(grid, stream, ye, n_rows, row_of, topk_w, top_k, row_vecs, n_chunks, shared_y, self_lo, self_hi, out)
+  const int kmax = kmax_of(top_k);
   if (dt == MOE_F32) {
     if (kmax == 2) MOE_COMBINE(float, 2);
     else if (kmax == 4) MOE_COMBINE(float, 4);

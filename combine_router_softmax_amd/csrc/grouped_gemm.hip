@@ -37,6 +37,8 @@
 //
 // fp32 activations + fp32 weights (small parity problems) use a plain SIMT
 // kernel with the same scheduler.
+#include <algorithm>
+
 #include "moe_common.hpp"
 
 namespace moe {
@@ -56,6 +58,7 @@ constexpr int kGemmMaxSrc = 512;
 enum { kUp = 0, kDown = 1 };
 
 struct GemmArgs {
+  // routed experts
   const void* a;              // [rows, K] activations (x for up, h for down)
   int64_t rows;               // R
   const int32_t* counts;      // [G, S] (padded)
@@ -63,47 +66,59 @@ struct GemmArgs {
   int G, S, C, layout;
   const void* w;              // [G, n_w_rows, K]
   const float* s;             // fp8: [G, n_w_rows/128, K/128]
+  void* out;                  // [rows, n_out]
+  // optional shared expert: one more group (index G) over rows [0, sh_rows) of its own buffers
+  const void* sh_a;
+  const void* sh_w;
+  const float* sh_s;
+  void* sh_out;
+  int sh_rows;                // 0 = none
   int n_w_rows;               // 2I (up) or H (down)
   int K;                      // reduction length
-  void* out;                  // [rows, n_out]
   int n_out;                  // I (up) or H (down)
   int n_tiles_n;              // N tiles per expert
+  int packed;                 // weights in the packed (load-order) layout
 };
 
 struct Sched {
-  int tile_start[kMaxGroups + 1];
-  int m[kMaxGroups];
+  int tile_start[kMaxGroups + 2];
+  int m[kMaxGroups + 1];
   int seg[kGemmMaxSrc + 1];
   int rowmap[kBM];
   int tmp[kGemmThreads];
   int cur_seg_group;
 };
 
-// Rows per expert from the device counts (clamped so every row stays inside
-// [0, rows)), then the exclusive prefix of tiles per expert. Returns the tile
-// count. All threads must call it.
+// Rows per group from the device counts (clamped so every row stays inside
+// [0, rows)), then the exclusive prefix of tiles per group. Schedule order:
+// the shared expert first (its rows are always present, so its tiles start
+// with the first wave of workgroups instead of forming a tail), then the
+// routed experts. Returns the tile count. All threads must call it.
 __device__ int build_schedule(const GemmArgs& p, int bm, Sched& sh) {
   const int tid = threadIdx.x;
+  const int nsh = p.sh_rows > 0 ? 1 : 0;
+  const int Gt = p.G + nsh;
   if (p.layout == MOE_LAYOUT_COMPACT) {
     for (int g = tid; g < p.G; g += kGemmThreads) {
       const int64_t lo = min<int64_t>(max<int64_t>(p.group_off[g], 0), p.rows);
       const int64_t hi = min<int64_t>(max<int64_t>(p.group_off[g + 1], lo), p.rows);
-      sh.m[g] = int(hi - lo);
+      sh.m[nsh + g] = int(hi - lo);
     }
   } else {
-    for (int g = tid; g < p.G; g += kGemmThreads) sh.m[g] = 0;
+    for (int g = tid; g < p.G; g += kGemmThreads) sh.m[nsh + g] = 0;
     __syncthreads();
     for (int i = tid; i < p.G * p.S; i += kGemmThreads) {
       const int c = min(max(p.counts[i], 0), p.C);
-      if (c) atomicAdd(&sh.m[i / p.S], c);
+      if (c) atomicAdd(&sh.m[nsh + i / p.S], c);
     }
   }
+  if (tid == 0 && nsh) sh.m[0] = p.sh_rows;
   __syncthreads();
-  for (int g = tid; g < p.G; g += kGemmThreads) sh.tile_start[g] = (sh.m[g] + bm - 1) / bm * p.n_tiles_n;
+  for (int g = tid; g < Gt; g += kGemmThreads) sh.tile_start[g] = (sh.m[g] + bm - 1) / bm * p.n_tiles_n;
   __syncthreads();
-  const int total = block_scan_lds<false, kGemmThreads>(sh.tile_start, p.G, sh.tmp);
+  const int total = block_scan_lds<false, kGemmThreads>(sh.tile_start, Gt, sh.tmp);
   if (tid == 0) {
-    sh.tile_start[p.G] = total;
+    sh.tile_start[Gt] = total;
     sh.cur_seg_group = -1;
   }
   __syncthreads();
@@ -111,18 +126,25 @@ __device__ int build_schedule(const GemmArgs& p, int bm, Sched& sh) {
 }
 
 struct Tile {
-  int g, nt, r0, nrows;
+  int g;        // routed expert index (unused for the shared expert)
+  int we;       // expert index inside the weight tensor of the tile's problem
+  bool shared;
+  int nt, r0, nrows;
 };
 
 __device__ Tile decode_tile(const GemmArgs& p, int bm, const Sched& sh, int t) {
-  int lo = 0, hi = p.G;  // last g with tile_start[g] <= t
+  const int nsh = p.sh_rows > 0 ? 1 : 0;
+  const int Gt = p.G + nsh;
+  int lo = 0, hi = Gt;  // last q with tile_start[q] <= t
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (sh.tile_start[mid] <= t) lo = mid;
     else hi = mid;
   }
   Tile tl;
-  tl.g = lo;
+  tl.shared = lo < nsh;
+  tl.g = tl.shared ? 0 : lo - nsh;
+  tl.we = tl.g;
   const int local = t - sh.tile_start[lo];
   const int mtiles = (sh.m[lo] + bm - 1) / bm;
   tl.nt = local / mtiles;
@@ -131,12 +153,12 @@ __device__ Tile decode_tile(const GemmArgs& p, int bm, const Sched& sh, int t) {
   return tl;
 }
 
-// Physical row of each of the tile's rows (-1 past the expert's rows).
+// Physical row of each of the tile's rows (-1 past the group's rows).
 __device__ void build_rowmap(const GemmArgs& p, const Tile& tl, int bm, Sched& sh) {
   const int tid = threadIdx.x;
-  if (p.layout == MOE_LAYOUT_COMPACT) {
+  if (tl.shared || p.layout == MOE_LAYOUT_COMPACT) {
     if (tid < bm) {
-      const int64_t base = min<int64_t>(max<int64_t>(p.group_off[tl.g], 0), p.rows);
+      const int64_t base = tl.shared ? 0 : min<int64_t>(max<int64_t>(p.group_off[tl.g], 0), p.rows);
       sh.rowmap[tid] = tid < tl.nrows ? int(base + tl.r0 + tid) : -1;
     }
     __syncthreads();
@@ -186,8 +208,60 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
 }
 
 // ------------------------------------------------------------------ MFMA kernel
+// Stream-K split of the work: the iterations (tile, 128-deep K chunk) of the
+// whole launch are cut into kSkGrid equal contiguous ranges, one per
+// workgroup, so every workgroup streams the same number of weight bytes no
+// matter how the tile count compares with the number of workgroups. A tile
+// covered by one workgroup is finished in place; a tile cut by a range
+// boundary leaves fp32 partial sums (in accumulator-register order) in the
+// workspace, and ffn_fixup_kernel adds them in workgroup order and finishes
+// the tile. No workgroup ever waits for another.
+constexpr int kSkGrid = 512;                          // 2 resident workgroups x 256 compute units
+constexpr int kPartFloats = 4 * kMB * 16 * kWave;     // one workgroup's accumulators (64 KiB)
+
+__host__ __device__ inline int64_t sk_start(int b, int64_t total) { return int64_t(b) * total / kSkGrid; }
+
+// Workgroup whose range holds iteration i (the last one, if several start there).
+__device__ inline int sk_owner(int64_t i, int64_t total) {
+  return int(((i + 1) * kSkGrid + total - 1) / total) - 1;
+}
+
+// Partial slot of workgroup b: 0 for its first tile, 1 for its last.
+__device__ inline float* sk_slot(float* parts, int b, int slot) {
+  return parts + (size_t(b) * 2 + slot) * kPartFloats;
+}
+
+template <int KIND>
+__device__ __forceinline__ void ffn_epilogue(const f32x16_t (&acc)[kMB], const Tile& tl, int nb, const Sched& sh,
+                                             uint16_t* out, int n_out, int wv, int lr, int lh) {
+#pragma unroll
+  for (int b = 0; b < kMB; ++b) {
+    if (b >= nb) continue;
+    const int phys = sh.rowmap[b * 32 + lr];
+    if (phys < 0) continue;
+    uint16_t* orow = out + size_t(phys) * n_out;
+    if (KIND == kUp) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        float h[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) h[r] = silu_f(acc[b][4 * q + r]) * acc[b][4 * (q + 2) + r];
+        const int col = tl.nt * 64 + 16 * wv + 8 * q + 4 * lh;
+        *reinterpret_cast<uint2*>(orow + col) = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = tl.nt * 128 + 32 * wv + 8 * q + 4 * lh;
+        *reinterpret_cast<uint2*>(orow + col) =
+            make_uint2(pack_bf16x2(acc[b][4 * q], acc[b][4 * q + 1]), pack_bf16x2(acc[b][4 * q + 2], acc[b][4 * q + 3]));
+      }
+    }
+  }
+}
+
 template <int KIND, bool FP8>
-__global__ __launch_bounds__(kGemmThreads, 2) void ffn_mfma_kernel(GemmArgs p) {
+__global__ __launch_bounds__(kGemmThreads, 2) void ffn_mfma_kernel(GemmArgs p, float* __restrict__ parts) {
   __shared__ Sched sh;
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][kBM * kLdsStride];
 
@@ -198,12 +272,20 @@ __global__ __launch_bounds__(kGemmThreads, 2) void ffn_mfma_kernel(GemmArgs p) {
   const int lh = lane >> 5;   // which half of the 16-deep MFMA step this lane feeds
   const int n_tiles = build_schedule(p, kBM, sh);
   const int nchunks = p.K / kKC;
-  const uint16_t* A = static_cast<const uint16_t*>(p.a);
+  const int64_t total = int64_t(n_tiles) * nchunks;
+  const int64_t i0 = sk_start(blockIdx.x, total), i1 = sk_start(blockIdx.x + 1, total);
+  if (i0 >= i1) return;  // uniform
+  const int t_first = int(i0 / nchunks), t_last = int((i1 - 1) / nchunks);
 
-  for (int t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+  for (int t = t_first; t <= t_last; ++t) {
+    const int c_begin = int(max<int64_t>(i0, int64_t(t) * nchunks) - int64_t(t) * nchunks);
+    const int c_end = int(min<int64_t>(i1, int64_t(t + 1) * nchunks) - int64_t(t) * nchunks);
     const Tile tl = decode_tile(p, kBM, sh, t);
     build_rowmap(p, tl, kBM, sh);
     const int nb = (tl.nrows + 31) / 32;  // active 32-row blocks (uniform)
+    const uint16_t* A = static_cast<const uint16_t*>(tl.shared ? p.sh_a : p.a);
+    const void* Wt = tl.shared ? p.sh_w : p.w;
+    const float* St = tl.shared ? p.sh_s : p.s;
 
     // weight row of this lane
     int wrow;
@@ -213,7 +295,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void ffn_mfma_kernel(GemmArgs p) {
     } else {
       wrow = tl.nt * 128 + 32 * wv + lr;
     }
-    const size_t wrow_elems = (size_t(tl.g) * p.n_w_rows + wrow) * p.K;
+    const size_t wrow_elems = (size_t(tl.we) * p.n_w_rows + wrow) * p.K;
 
     // fp8 block scales used by this tile's rows (uniform per workgroup)
     int srow0 = 0, srow1 = 0;
@@ -225,7 +307,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void ffn_mfma_kernel(GemmArgs p) {
         srow0 = srow1 = tl.nt;
       }
     }
-    const float* sbase = FP8 ? p.s + size_t(tl.g) * (p.n_w_rows / 128) * nchunks : nullptr;
+    const float* sbase = FP8 ? St + size_t(tl.we) * (p.n_w_rows / 128) * nchunks : nullptr;
 
     // activation staging: thread -> (row = tid/16 + 16*i, 16-byte column tid%16)
     const int xr = tid >> 4, xc = (tid & 15) * 8;
@@ -249,12 +331,18 @@ __global__ __launch_bounds__(kGemmThreads, 2) void ffn_mfma_kernel(GemmArgs p) {
 
     constexpr int WV = FP8 ? 4 : 8;  // 16-byte weight loads per lane per chunk
     auto load_w = [&](uint4* wvv, int c) {
-      if (FP8) {
-        const uint8_t* wp = static_cast<const uint8_t*>(p.w) + wrow_elems + size_t(c) * kKC + 64 * lh;
+      if (p.packed) {
+        // packed: this wave's WV x 1 KiB of chunk c, one contiguous 1 KiB per load
+        const uint4* wp = static_cast<const uint4*>(Wt) +
+                          ((((size_t(tl.we) * p.n_tiles_n + tl.nt) * nchunks + c) * 4 + wv) * WV) * kWave + lane;
+#pragma unroll
+        for (int j = 0; j < WV; ++j) wvv[j] = wp[j * kWave];
+      } else if (FP8) {
+        const uint8_t* wp = static_cast<const uint8_t*>(Wt) + wrow_elems + size_t(c) * kKC + 64 * lh;
 #pragma unroll
         for (int j = 0; j < 4; ++j) wvv[j] = *reinterpret_cast<const uint4*>(wp + 16 * j);
       } else {
-        const uint16_t* wp = static_cast<const uint16_t*>(p.w) + wrow_elems + size_t(c) * kKC + 32 * lh;
+        const uint16_t* wp = static_cast<const uint16_t*>(Wt) + wrow_elems + size_t(c) * kKC + 32 * lh;
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
@@ -268,19 +356,18 @@ __global__ __launch_bounds__(kGemmThreads, 2) void ffn_mfma_kernel(GemmArgs p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
 
-    uint4 wcur[WV], wnxt[WV], xv[kBM / 16];
-    load_w(wcur, 0);
-    load_x(xv, 0);
-    store_x(xv, 0);
-
-    for (int c = 0; c < nchunks; ++c) {
-      const bool more = c + 1 < nchunks;
-      if (more) {
-        load_w(wnxt, c + 1);
-        load_x(xv, c + 1);
-      }
+    // One K chunk: MFMAs on the weight registers `cur` and the staged activations;
+    // on entry the loads of chunk c+2 go into `nxt` (weights two chunks ahead:
+    // two chunks of every lane's weight stream are in flight while one is used)
+    // and of chunk c+1 into xv (activations, one chunk ahead, L2-resident).
+    uint4 wa[WV], wb[WV], wc[WV], xv[kBM / 16];
+    auto step = [&](int c, const uint4 (&cur)[WV], uint4 (&nxt)[WV]) {
+      const int buf = (c - c_begin) & 1;
+      const bool more = c + 1 < c_end;
+      if (c + 2 < c_end) load_w(nxt, c + 2);
+      if (more) load_x(xv, c + 1);
       __syncthreads();
-      const uint16_t* xb = xs[c & 1];
+      const uint16_t* xb = xs[buf];
       if (FP8) {
         f32x16_t part[kMB];
 #pragma unroll
@@ -289,7 +376,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void ffn_mfma_kernel(GemmArgs p) {
           for (int v = 0; v < 16; ++v) part[b][v] = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const uint4 q = wcur[j >> 1];
+          const uint4 q = cur[j >> 1];
           const bf16x8_t a = (j & 1) ? fp8x8_to_bf16(q.z, q.w) : fp8x8_to_bf16(q.x, q.y);
           const int col = 64 * lh + 8 * j;
 #pragma unroll
@@ -315,7 +402,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void ffn_mfma_kernel(GemmArgs p) {
         for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, wcur[sb * 4 + j]);
+            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, cur[sb * 4 + j]);
             const int col = 64 * sb + 32 * lh + 8 * j;
 #pragma unroll
             for (int b = 0; b < kMB; ++b) {
@@ -328,41 +415,118 @@ __global__ __launch_bounds__(kGemmThreads, 2) void ffn_mfma_kernel(GemmArgs p) {
           }
         }
       }
-      if (more) {
-        store_x(xv, (c + 1) & 1);
-#pragma unroll
-        for (int j = 0; j < WV; ++j) wcur[j] = wnxt[j];
-      }
+      if (more) store_x(xv, buf ^ 1);
+    };
+
+    load_w(wa, c_begin);
+    if (c_begin + 1 < c_end) load_w(wb, c_begin + 1);
+    load_x(xv, c_begin);
+    store_x(xv, 0);
+    for (int c = c_begin; c < c_end; c += 3) {
+      step(c, wa, wc);
+      if (c + 1 >= c_end) break;
+      step(c + 1, wb, wa);
+      if (c + 2 >= c_end) break;
+      step(c + 2, wc, wb);
     }
 
-    // epilogue: lane holds rows 8q + 4*lh + r (q = v/4, r = v%4) of the wave's
-    // 32 weight rows, for activation row lr of each block
-    uint16_t* out = static_cast<uint16_t*>(p.out);
+    if (c_begin == 0 && c_end == nchunks) {
+      uint16_t* out = static_cast<uint16_t*>(tl.shared ? p.sh_out : p.out);
+      ffn_epilogue<KIND>(acc, tl, nb, sh, out, p.n_out, wv, lr, lh);
+    } else {
+      // partial sums of a split tile, in accumulator-register order
+      float* dst = sk_slot(parts, blockIdx.x, t == t_first ? 0 : 1);
 #pragma unroll
-    for (int b = 0; b < kMB; ++b) {
-      if (b >= nb) continue;
-      const int phys = sh.rowmap[b * 32 + lr];
-      if (phys < 0) continue;
-      uint16_t* orow = out + size_t(phys) * p.n_out;
-      if (KIND == kUp) {
+      for (int b = 0; b < kMB; ++b) {
+        if (b >= nb) continue;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          float h[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) h[r] = silu_f(acc[b][4 * q + r]) * acc[b][4 * (q + 2) + r];
-          const int col = tl.nt * 64 + 16 * wv + 8 * q + 4 * lh;
-          *reinterpret_cast<uint2*>(orow + col) = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = tl.nt * 128 + 32 * wv + 8 * q + 4 * lh;
-          *reinterpret_cast<uint2*>(orow + col) =
-              make_uint2(pack_bf16x2(acc[b][4 * q], acc[b][4 * q + 1]), pack_bf16x2(acc[b][4 * q + 2], acc[b][4 * q + 3]));
-        }
+        for (int v = 0; v < 16; ++v) dst[((wv * kMB + b) * 16 + v) * kWave + lane] = acc[b][v];
       }
     }
     __syncthreads();  // rowmap and staging buffers are rewritten by the next tile
+  }
+}
+
+// Finishes the tiles cut by a stream-K range boundary: block j looks at the
+// boundary between workgroups j and j+1; the first boundary inside a tile
+// sums that tile's partials in workgroup order and runs the epilogue.
+template <int KIND>
+__global__ __launch_bounds__(kGemmThreads) void ffn_fixup_kernel(GemmArgs p, const float* __restrict__ parts) {
+  __shared__ Sched sh;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
+  const int lr = lane & 31;
+  const int lh = lane >> 5;
+  const int n_tiles = build_schedule(p, kBM, sh);
+  const int nchunks = p.K / kKC;
+  const int64_t total = int64_t(n_tiles) * nchunks;
+  const int j = blockIdx.x;
+  const int64_t ib = sk_start(j + 1, total);
+  if (ib <= 0 || ib >= total || ib % nchunks == 0) return;  // not inside a tile
+  const int t = int(ib / nchunks);
+  if (j > 0 && sk_start(j, total) > int64_t(t) * nchunks) return;  // an earlier boundary owns this tile
+  const Tile tl = decode_tile(p, kBM, sh, t);
+  build_rowmap(p, tl, kBM, sh);
+  const int nb = (tl.nrows + 31) / 32;
+  const int b_lo = sk_owner(int64_t(t) * nchunks, total);
+  const int b_hi = sk_owner(int64_t(t + 1) * nchunks - 1, total);
+  f32x16_t acc[kMB];
+#pragma unroll
+  for (int b = 0; b < kMB; ++b)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
+  for (int w = b_lo; w <= b_hi; ++w) {
+    const int64_t s0 = sk_start(w, total), s1 = sk_start(w + 1, total);
+    if (s0 >= s1) continue;  // empty range
+    const float* src = sk_slot(const_cast<float*>(parts), w, int(s0 / nchunks) == t ? 0 : 1);
+#pragma unroll
+    for (int b = 0; b < kMB; ++b) {
+      if (b >= nb) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[b][v] += src[((wv * kMB + b) * 16 + v) * kWave + lane];
+    }
+  }
+  uint16_t* out = static_cast<uint16_t*>(tl.shared ? p.sh_out : p.out);
+  ffn_epilogue<KIND>(acc, tl, nb, sh, out, p.n_out, wv, lr, lh);
+}
+
+// ------------------------------------------------------------------ weight packing
+// Packed layout: for expert g, N block nt (64 h columns = 128 rows of W13, or
+// 128 rows of W2) and 128-deep K chunk c, the 32 rows x 128 k of each of the 4
+// waves, in the order the lanes of ffn_mfma_kernel load them:
+// [g][nt][c][wave][load i][lane][16 bytes]. One load instruction of a wave then
+// reads 1 KiB of contiguous memory and a workgroup streams one sequential
+// region, instead of 128 rows in 256-byte pieces. It is a permutation of the
+// row-major bytes (same size); one thread moves one 16-byte piece.
+__global__ __launch_bounds__(256) void pack_weights_kernel(const uint8_t* __restrict__ src, uint4* __restrict__ dst,
+                                                           int64_t n_pieces, int kind, int fp8, int n_w_rows, int K,
+                                                           int n_out, int n_tiles_n) {
+  const int WV = fp8 ? 4 : 8;
+  const int eb = fp8 ? 1 : 2;
+  const int nchunks = K / kKC;
+  for (int64_t d = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; d < n_pieces;
+       d += int64_t(gridDim.x) * blockDim.x) {
+    const int l = int(d % kWave);
+    int64_t q = d / kWave;
+    const int i = int(q % WV);
+    q /= WV;
+    const int w = int(q % 4);
+    q /= 4;
+    const int c = int(q % nchunks);
+    q /= nchunks;
+    const int nt = int(q % n_tiles_n);
+    const int64_t g = q / n_tiles_n;
+    const int r = l & 31, h = l >> 5;
+    int row;
+    if (kind == kUp) {
+      const int j = nt * 64 + 16 * w + (r & 15);
+      row = r < 16 ? j : n_out + j;
+    } else {
+      row = nt * 128 + 32 * w + r;
+    }
+    const int k = fp8 ? c * kKC + 64 * h + 16 * i : c * kKC + 64 * (i >> 2) + 32 * h + 8 * (i & 3);
+    dst[d] = *reinterpret_cast<const uint4*>(src + ((g * n_w_rows + row) * int64_t(K) + k) * eb);
   }
 }
 
@@ -378,9 +542,6 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_f32_kernel(GemmArgs p) {
   __shared__ float ws[2 * kFBN][kFKC + 1];
   const int tid = threadIdx.x;
   const int n_tiles = build_schedule(p, kFBM, sh);
-  const float* A = static_cast<const float*>(p.a);
-  const float* W = static_cast<const float*>(p.w);
-  float* out = static_cast<float*>(p.out);
   const int nwr = KIND == kUp ? 2 * kFBN : kFBN;  // weight rows staged per tile
   const int row = tid / 8;                         // 0..31
   const int cg = (tid % 8) * 4;                    // 4 output columns
@@ -388,6 +549,9 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_f32_kernel(GemmArgs p) {
   for (int t = blockIdx.x; t < n_tiles; t += gridDim.x) {
     const Tile tl = decode_tile(p, kFBM, sh, t);
     build_rowmap(p, tl, kFBM, sh);
+    const float* A = static_cast<const float*>(tl.shared ? p.sh_a : p.a);
+    const float* W = static_cast<const float*>(tl.shared ? p.sh_w : p.w);
+    float* out = static_cast<float*>(tl.shared ? p.sh_out : p.out);
     float g[4] = {0.f, 0.f, 0.f, 0.f}, u[4] = {0.f, 0.f, 0.f, 0.f};
     for (int k0 = 0; k0 < p.K; k0 += kFKC) {
       for (int i = tid; i < kFBM * kFKC; i += kGemmThreads) {
@@ -400,7 +564,7 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_f32_kernel(GemmArgs p) {
         int wr;
         if (KIND == kUp) wr = r < kFBN ? tl.nt * kFBN + r : p.n_out + tl.nt * kFBN + (r - kFBN);
         else wr = tl.nt * kFBN + r;
-        ws[r][k] = W[(size_t(tl.g) * p.n_w_rows + wr) * p.K + k0 + k];
+        ws[r][k] = W[(size_t(tl.we) * p.n_w_rows + wr) * p.K + k0 + k];
       }
       __syncthreads();
 #pragma unroll 4
@@ -438,6 +602,8 @@ static bool ggemm_desc_ok(const moe_ggemm_desc_t* d) {
     if (d->n_src < 1 || d->capacity < 0) return false;
     if (int64_t(d->n_groups) * d->n_src * d->capacity > d->rows) return false;
   }
+  if (d->shared && d->shared->rows < 0) return false;
+  if (d->w_format != MOE_W_ROWMAJOR && d->w_format != MOE_W_PACKED) return false;
   return true;
 }
 
@@ -449,13 +615,24 @@ static bool ggemm_desc_supported(const moe_ggemm_desc_t* d) {
   if (d->n_groups > kMaxGroups) return false;
   if (d->layout == MOE_LAYOUT_PADDED && d->n_src > kGemmMaxSrc) return false;
   if (d->rows >= (int64_t(1) << 31)) return false;
+  if (d->shared && d->shared->rows >= (1 << 30)) return false;
+  if (f32 && d->w_format == MOE_W_PACKED) return false;
   return true;
+}
+
+static size_t h_bytes(const moe_ggemm_desc_t* d, int64_t rows) {
+  const size_t el = d->act_dt == MOE_F32 ? 4 : 2;
+  return align_up(size_t(rows) * size_t(d->inter) * el, 256);
+}
+
+static size_t parts_bytes(const moe_ggemm_desc_t* d) {
+  return d->act_dt == MOE_F32 ? 0 : size_t(2) * kSkGrid * kPartFloats * sizeof(float);
 }
 
 MOE_API size_t moe_grouped_gemm_workspace(const moe_ggemm_desc_t* d) {
   if (!ggemm_desc_ok(d)) return 0;
-  const size_t el = d->act_dt == MOE_F32 ? 4 : 2;
-  return align_up(size_t(d->rows) * size_t(d->inter) * el, 256) + 256;
+  const int64_t sh_rows = d->shared ? d->shared->rows : 0;
+  return h_bytes(d, d->rows) + h_bytes(d, sh_rows) + parts_bytes(d) + 256;
 }
 
 namespace moe {
@@ -471,22 +648,28 @@ int device_cu_count() {
 }
 }  // namespace moe
 
-static moe_status_t launch_stage(const GemmArgs& p, bool f32, bool fp8, int kind, hipStream_t stream) {
-  const int bm = f32 ? kFBM : kBM;
-  const int64_t upper = int64_t(p.n_tiles_n) * ((p.rows + bm - 1) / bm + p.G);
-  if (upper <= 0) return MOE_OK;
-  const int64_t resident = int64_t(device_cu_count()) * (f32 ? 4 : 2);
-  const dim3 grid(unsigned(upper < resident ? upper : resident)), block(kGemmThreads);
+static moe_status_t launch_stage(const GemmArgs& p, bool f32, bool fp8, int kind, float* parts,
+                                 hipStream_t stream) {
+  const dim3 block(kGemmThreads);
   if (f32) {
+    const int64_t upper = int64_t(p.n_tiles_n) * ((p.rows + kFBM - 1) / kFBM + p.G + (p.sh_rows + kFBM - 1) / kFBM + 1);
+    const int64_t resident = int64_t(device_cu_count()) * 4;
+    const dim3 grid(unsigned(upper < resident ? upper : resident));
     if (kind == kUp) hipLaunchKernelGGL(ffn_f32_kernel<kUp>, grid, block, 0, stream, p);
     else hipLaunchKernelGGL(ffn_f32_kernel<kDown>, grid, block, 0, stream, p);
-  } else if (fp8) {
-    if (kind == kUp) hipLaunchKernelGGL((ffn_mfma_kernel<kUp, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((ffn_mfma_kernel<kDown, true>), grid, block, 0, stream, p);
-  } else {
-    if (kind == kUp) hipLaunchKernelGGL((ffn_mfma_kernel<kUp, false>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((ffn_mfma_kernel<kDown, false>), grid, block, 0, stream, p);
+    return launch_status();
   }
+  const dim3 grid(kSkGrid), fix_grid(kSkGrid - 1);
+  if (fp8) {
+    if (kind == kUp) hipLaunchKernelGGL((ffn_mfma_kernel<kUp, true>), grid, block, 0, stream, p, parts);
+    else hipLaunchKernelGGL((ffn_mfma_kernel<kDown, true>), grid, block, 0, stream, p, parts);
+  } else {
+    if (kind == kUp) hipLaunchKernelGGL((ffn_mfma_kernel<kUp, false>), grid, block, 0, stream, p, parts);
+    else hipLaunchKernelGGL((ffn_mfma_kernel<kDown, false>), grid, block, 0, stream, p, parts);
+  }
+  if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
+  if (kind == kUp) hipLaunchKernelGGL(ffn_fixup_kernel<kUp>, fix_grid, block, 0, stream, p, parts);
+  else hipLaunchKernelGGL(ffn_fixup_kernel<kDown>, fix_grid, block, 0, stream, p, parts);
   return launch_status();
 }
 
@@ -495,48 +678,101 @@ MOE_API moe_status_t moe_grouped_gemm(const moe_ggemm_desc_t* d, const void* a, 
                                       const float* s2, void* y, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!ggemm_desc_ok(d)) return MOE_ERR_INVALID_ARG;
   if (!ggemm_desc_supported(d)) return MOE_ERR_UNSUPPORTED;
-  if (d->n_groups == 0 || d->rows == 0) return MOE_OK;
+  const moe_shared_expert_t* se = (d->shared && d->shared->rows > 0) ? d->shared : nullptr;
+  const bool routed = d->n_groups > 0 && d->rows > 0;
+  if (!routed && !se) return MOE_OK;
   const bool f32 = d->act_dt == MOE_F32;
   const bool fp8 = d->w_dt == MOE_FP8_E4M3;
   const bool up = d->stage != MOE_GG_DOWN, down = d->stage != MOE_GG_UP;
-  if (d->layout == MOE_LAYOUT_COMPACT && !group_off) return MOE_ERR_INVALID_ARG;
-  if (d->layout == MOE_LAYOUT_PADDED && !counts) return MOE_ERR_INVALID_ARG;
-  if (up && (!a || !w13 || !aligned16(a) || !aligned16(w13))) return MOE_ERR_INVALID_ARG;
-  if (down && (!y || !w2 || !aligned16(y) || !aligned16(w2))) return MOE_ERR_INVALID_ARG;
-  if (fp8 && ((up && !s13) || (down && !s2))) return MOE_ERR_INVALID_ARG;
+  if (routed) {
+    if (d->layout == MOE_LAYOUT_COMPACT && !group_off) return MOE_ERR_INVALID_ARG;
+    if (d->layout == MOE_LAYOUT_PADDED && !counts) return MOE_ERR_INVALID_ARG;
+    if (up && (!a || !w13 || !aligned16(a) || !aligned16(w13))) return MOE_ERR_INVALID_ARG;
+    if (down && (!y || !w2 || !aligned16(y) || !aligned16(w2))) return MOE_ERR_INVALID_ARG;
+    if (fp8 && ((up && !s13) || (down && !s2))) return MOE_ERR_INVALID_ARG;
+  }
+  if (se) {
+    if (up && (!se->a || !se->w13 || !aligned16(se->a) || !aligned16(se->w13))) return MOE_ERR_INVALID_ARG;
+    if (down && (!se->y || !se->w2 || !aligned16(se->y) || !aligned16(se->w2))) return MOE_ERR_INVALID_ARG;
+    if (fp8 && ((up && !se->s13) || (down && !se->s2))) return MOE_ERR_INVALID_ARG;
+  }
   if (!ws || !aligned16(ws) || ws_bytes < moe_grouped_gemm_workspace(d)) return MOE_ERR_WORKSPACE;
 
+  void* h = ws;
+  void* sh_h = static_cast<char*>(ws) + h_bytes(d, d->rows);
+  float* parts = reinterpret_cast<float*>(static_cast<char*>(sh_h) + h_bytes(d, d->shared ? d->shared->rows : 0));
   GemmArgs p;
-  p.rows = d->rows;
+  p.rows = routed ? d->rows : 0;
   p.counts = counts;
   p.group_off = group_off;
-  p.G = d->n_groups;
+  p.G = routed ? d->n_groups : 0;
   p.S = d->layout == MOE_LAYOUT_PADDED ? d->n_src : 1;
   p.C = d->layout == MOE_LAYOUT_PADDED ? d->capacity : 0;
   p.layout = d->layout;
+  p.sh_rows = se ? se->rows : 0;
+  p.packed = d->w_format == MOE_W_PACKED;
   moe_status_t st = MOE_OK;
   if (up) {
     p.a = a;
     p.w = w13;
     p.s = s13;
+    p.out = h;
+    p.sh_a = se ? se->a : nullptr;
+    p.sh_w = se ? se->w13 : nullptr;
+    p.sh_s = se ? se->s13 : nullptr;
+    p.sh_out = sh_h;
     p.n_w_rows = 2 * d->inter;
     p.K = d->hidden;
-    p.out = ws;
     p.n_out = d->inter;
     p.n_tiles_n = f32 ? d->inter / kFBN : d->inter / 64;
-    st = launch_stage(p, f32, fp8, kUp, stream);
+    st = launch_stage(p, f32, fp8, kUp, parts, stream);
     if (st != MOE_OK) return st;
   }
   if (down) {
-    p.a = ws;
+    p.a = h;
     p.w = w2;
     p.s = s2;
+    p.out = y;
+    p.sh_a = sh_h;
+    p.sh_w = se ? se->w2 : nullptr;
+    p.sh_s = se ? se->s2 : nullptr;
+    p.sh_out = se ? se->y : nullptr;
     p.n_w_rows = d->hidden;
     p.K = d->inter;
-    p.out = y;
     p.n_out = d->hidden;
     p.n_tiles_n = f32 ? d->hidden / kFBN : d->hidden / 128;
-    st = launch_stage(p, f32, fp8, kDown, stream);
+    st = launch_stage(p, f32, fp8, kDown, parts, stream);
   }
   return st;
+}
+
+MOE_API moe_status_t moe_pack_weights(int n_groups, int hidden, int inter, moe_dtype_t w_dt, const void* w13,
+                                      const void* w2, void* w13_packed, void* w2_packed, hipStream_t stream) {
+  if (n_groups < 0 || hidden < 1 || inter < 1) return MOE_ERR_INVALID_ARG;
+  if (w_dt != MOE_BF16 && w_dt != MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
+  if (hidden % 128 || inter % 128) return MOE_ERR_UNSUPPORTED;
+  if (n_groups == 0) return MOE_OK;
+  const bool fp8 = w_dt == MOE_FP8_E4M3;
+  const int64_t eb = fp8 ? 1 : 2;
+  const int64_t bytes13 = int64_t(n_groups) * 2 * inter * hidden * eb, bytes2 = int64_t(n_groups) * hidden * inter * eb;
+  if ((w13 == nullptr) != (w13_packed == nullptr) || (w2 == nullptr) != (w2_packed == nullptr))
+    return MOE_ERR_INVALID_ARG;
+  for (const void* q : {w13, w2, static_cast<const void*>(w13_packed), static_cast<const void*>(w2_packed)})
+    if (q && !aligned16(q)) return MOE_ERR_INVALID_ARG;
+  if ((w13 && w13 == w13_packed) || (w2 && w2 == w2_packed)) return MOE_ERR_INVALID_ARG;  // not in place
+  const dim3 block(256);
+  if (w13) {
+    const int64_t n = bytes13 / 16;
+    const dim3 grid(unsigned(std::min<int64_t>((n + 255) / 256, 65536)));
+    hipLaunchKernelGGL(pack_weights_kernel, grid, block, 0, stream, static_cast<const uint8_t*>(w13),
+                       static_cast<uint4*>(w13_packed), n, int(kUp), int(fp8), 2 * inter, hidden, inter, inter / 64);
+    if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
+  }
+  if (w2) {
+    const int64_t n = bytes2 / 16;
+    const dim3 grid(unsigned(std::min<int64_t>((n + 255) / 256, 65536)));
+    hipLaunchKernelGGL(pack_weights_kernel, grid, block, 0, stream, static_cast<const uint8_t*>(w2),
+                       static_cast<uint4*>(w2_packed), n, int(kDown), int(fp8), hidden, inter, hidden, hidden / 128);
+  }
+  return launch_status();
 }

@@ -13,8 +13,9 @@ from typing import Optional
 
 import torch
 
-from . import (COMPACT, GG_DOWN, GG_FULL, GG_UP, PADDED, gemm_desc, moe_combine, moe_dispatch, moe_dispatch_layout,
-               moe_grouped_gemm, moe_grouped_gemm_workspace, moe_layout_rows, moe_route_topk)
+from . import (COMPACT, GG_DOWN, GG_FULL, GG_UP, PADDED, W_PACKED, W_ROWMAJOR, SharedExpert, gemm_desc, moe_combine, moe_dispatch, moe_dispatch_layout,
+               moe_grouped_gemm, moe_grouped_gemm_workspace, moe_layout_rows, moe_pack_weights,
+               moe_route_topk)
 
 
 class MoEShare:
@@ -46,25 +47,42 @@ class MoEShare:
         self.shared_off = torch.tensor([0, B0], dtype=torch.int32, device=d)
         self.w = None
         self.sw = None
+        self.w_format = W_ROWMAJOR
         self.ws = None
         self.sws = None
 
     # weights: dict with w13 [G,2I,H], w2 [G,H,I], optional s13/s2 (host or device tensors)
-    def set_weights(self, routed: dict, shared: Optional[dict] = None):
+    def set_weights(self, routed: dict, shared: Optional[dict] = None, pack: bool = True):
+        """Upload weights; bf16/fp8 weights are packed once into the kernel's load order."""
         def todev(wd):
             if wd is None:
                 return None
-            return {k: (v.to(self.dev).contiguous() if isinstance(v, torch.Tensor) else v)
-                    for k, v in wd.items() if k in ("w13", "w2", "s13", "s2")}
+            out = {k: (v.to(self.dev).contiguous() if isinstance(v, torch.Tensor) else v)
+                   for k, v in wd.items() if k in ("w13", "w2", "s13", "s2")}
+            if self.w_format == W_PACKED:
+                out["w13"], out["w2"] = moe_pack_weights(out["w13"], out["w2"], self.H, self.I)
+            return out
+        self.w_format = W_PACKED if (pack and routed["w13"].dtype != torch.float32) else W_ROWMAJOR
         self.w = todev(routed)
         self.sw = todev(shared)
         wdt = self.w["w13"].dtype
-        desc = gemm_desc(self.L, self.H, self.I, self.act_dtype, wdt, self.layout, self.S, self.capacity, self.R)
-        self.ws = torch.empty(moe_grouped_gemm_workspace(desc), dtype=torch.uint8, device=self.dev)
+        B0 = self.self_hi - self.self_lo
+        se = SharedExpert(rows=B0 if self.sw is not None else 0)
+        desc = gemm_desc(self.L, self.H, self.I, self.act_dtype, wdt, self.layout, self.S, self.capacity, self.R,
+                         shared=se, w_format=self.w_format)
+        self.ws = torch.zeros(moe_grouped_gemm_workspace(desc), dtype=torch.uint8, device=self.dev)
         if self.sw is not None:
-            B0 = self.self_hi - self.self_lo
-            sdesc = gemm_desc(1, self.H, self.I, self.act_dtype, self.sw["w13"].dtype, COMPACT, 1, 0, max(B0, 1))
-            self.sws = torch.empty(moe_grouped_gemm_workspace(sdesc), dtype=torch.uint8, device=self.dev)
+            sdesc = gemm_desc(1, self.H, self.I, self.act_dtype, self.sw["w13"].dtype, COMPACT, 1, 0, max(B0, 1),
+                              w_format=self.w_format)
+            self.sws = torch.zeros(moe_grouped_gemm_workspace(sdesc), dtype=torch.uint8, device=self.dev)
+
+    def _shared_arg(self, x):
+        if self.sw is None or self.self_hi <= self.self_lo:
+            return None
+        sw = self.sw
+        a = x[self.self_lo: self.self_hi]
+        return {"a": a, "w13": sw["w13"], "w2": sw["w2"], "s13": sw.get("s13"), "s2": sw.get("s2"),
+                "y": self.ys[: a.shape[0]]}
 
     def route(self, logits):
         moe_route_topk(logits, self.K, True, self.topk_idx, self.topk_w)
@@ -76,11 +94,13 @@ class MoEShare:
     def dispatch(self, x):
         moe_dispatch(x, self.lay["row_of"], self.K, self.R, self.xe)
 
-    def gemm(self, stage=GG_FULL):
+    def gemm(self, stage=GG_FULL, x=None):
+        """Routed experts; with ``x`` the shared expert runs in the same launches."""
         w = self.w
         moe_grouped_gemm(self.xe[: self.R], w["w13"], w["w2"], group_off=self.lay["expert_off"],
                          counts=self.lay["counts"], s13=w.get("s13"), s2=w.get("s2"), layout=self.layout,
-                         n_src=self.S, capacity=self.capacity, stage=stage, y=self.ye[: self.R], ws=self.ws)
+                         n_src=self.S, capacity=self.capacity, stage=stage, y=self.ye[: self.R], ws=self.ws,
+                         shared=None if x is None else self._shared_arg(x), w_format=self.w_format)
 
     def shared_gemm(self, x, stage=GG_FULL):
         if self.sw is None or self.self_hi <= self.self_lo:
@@ -88,16 +108,18 @@ class MoEShare:
         sw = self.sw
         a = x[self.self_lo: self.self_hi]
         moe_grouped_gemm(a, sw["w13"], sw["w2"], group_off=self.shared_off, s13=sw.get("s13"), s2=sw.get("s2"),
-                         layout=COMPACT, stage=stage, y=self.ys[: a.shape[0]], ws=self.sws)
+                         layout=COMPACT, stage=stage, y=self.ys[: a.shape[0]], ws=self.sws, w_format=self.w_format)
 
     def combine(self, out):
         sy = self.ys if (self.sw is not None and self.self_hi > self.self_lo) else None
         moe_combine(self.ye[: max(self.R, 1)] if self.R else self.ye[:0], self.lay["row_of"], self.topk_w, out, sy,
                     self.self_lo, self.self_hi)
 
-    def step(self, logits, src_offsets, x, out, events: Optional[dict] = None):
+    def step(self, logits, src_offsets, x, out, events: Optional[dict] = None, fused_shared: bool = True):
         """One full pass. ``events`` maps step names to (start, end) CUDA events
-        recorded around each call on the current stream."""
+        recorded around each call on the current stream. With ``fused_shared``
+        the shared expert runs inside the routed grouped-GEMM launches; otherwise
+        as calls of its own."""
         def run(name, fn):
             if events is not None and name in events:
                 events[name][0].record()
@@ -109,10 +131,12 @@ class MoEShare:
         run("route", lambda: self.route(logits))
         run("layout", lambda: self.layout_step(src_offsets))
         run("dispatch", lambda: self.dispatch(x))
-        run("gemm_up", lambda: self.gemm(GG_UP))
-        run("gemm_down", lambda: self.gemm(GG_DOWN))
-        run("shared_up", lambda: self.shared_gemm(x, GG_UP))
-        run("shared_down", lambda: self.shared_gemm(x, GG_DOWN))
+        xs = x if fused_shared else None
+        run("gemm_up", lambda: self.gemm(GG_UP, xs))
+        run("gemm_down", lambda: self.gemm(GG_DOWN, xs))
+        if not fused_shared:
+            run("shared_up", lambda: self.shared_gemm(x, GG_UP))
+            run("shared_down", lambda: self.shared_gemm(x, GG_DOWN))
         run("combine", lambda: self.combine(out))
         return out
 

@@ -162,13 +162,33 @@ moe_status_t moe_dispatch(const void* x, moe_dtype_t dt, int n_tokens, int hidde
 
 /* ------------------------------------------------------------------ grouped GEMM */
 typedef enum {
+  MOE_W_ROWMAJOR = 0, /* w13 [G, 2I, H] and w2 [G, H, I] row-major */
+  MOE_W_PACKED = 1    /* the same bytes permuted by moe_pack_weights (bf16 and fp8 only) */
+} moe_weight_format_t;
+
+typedef enum {
   MOE_GG_FULL = 0, /* both products */
   MOE_GG_UP = 1,   /* h = silu(a W_gate^T) * (a W_up^T) into the workspace only */
   MOE_GG_DOWN = 2  /* y = h W2^T from the workspace only (after MOE_GG_UP on the same ws) */
 } moe_gg_stage_t;
 
+/* The shared expert (Perplexity DeepSeek page, section Expert parallelism:
+ * every GPU keeps a copy of it and runs it on its own tokens). When given,
+ * moe_grouped_gemm runs it as one more group inside the same launches as the
+ * routed experts, so the small problem does not run alone on a few compute
+ * units. Same dtypes and sizes as the routed experts. */
 typedef struct {
-  int n_groups;        /* G experts in this call (1 for the shared expert) */
+  const void* a;     /* [rows, H] input rows (act_dt), e.g. this GPU's own tokens */
+  int rows;          /* B (0 = no shared expert) */
+  const void* w13;   /* [1, 2I, H] */
+  const void* w2;    /* [1, H, I] */
+  const float* s13;  /* fp8 only: [1, 2I/128, H/128] */
+  const float* s2;   /* fp8 only: [1, H/128, I/128] */
+  void* y;           /* [rows, H] out (act_dt) */
+} moe_shared_expert_t;
+
+typedef struct {
+  int n_groups;        /* G routed experts in this call (may be 0 with a shared expert) */
   int hidden;          /* H, multiple of 128 */
   int inter;           /* I, multiple of 128 */
   moe_dtype_t act_dt;  /* a, y, workspace h: MOE_F32 or MOE_BF16 */
@@ -178,10 +198,13 @@ typedef struct {
   int capacity;        /* PADDED: rows per (group, source) region */
   int64_t rows;        /* R rows of a, y and h (row indices are shared by all three) */
   moe_gg_stage_t stage;
+  const moe_shared_expert_t* shared; /* host pointer, or NULL for none */
+  moe_weight_format_t w_format;      /* layout of w13/w2 (and of the shared expert's) */
 } moe_ggemm_desc_t;
 
-/* Bytes of scratch moe_grouped_gemm needs (the intermediate h [R, I] in the
- * activation dtype, 256-byte aligned); 0 for an invalid descriptor. */
+/* Bytes of scratch moe_grouped_gemm needs (the intermediates h [R, I] and, with
+ * a shared expert, [B, I], in the activation dtype, 256-byte aligned); 0 for an
+ * invalid descriptor. */
 size_t moe_grouped_gemm_workspace(const moe_ggemm_desc_t* d);
 
 /* Per-expert SwiGLU FFN over the rows each expert holds (Perplexity DeepSeek
@@ -204,12 +227,30 @@ size_t moe_grouped_gemm_workspace(const moe_ggemm_desc_t* d);
  * w2         [G, H, I].
  * s13, s2    fp8 only: float32 scales [G, 2I/128, H/128] and [G, H/128, I/128]; else NULL.
  * y          [R, H] out (act_dt); unused with MOE_GG_UP.
- * The shared expert is a call with n_groups = 1, COMPACT, group_off = {0, B}
- * and a pointing at its B token rows.
+ * The shared expert is either desc->shared (same launches) or a call of its own
+ * with n_groups = 1, COMPACT, group_off = {0, B} and a pointing at its rows.
+ * MOE_GG_UP then MOE_GG_DOWN with the same workspace equals MOE_GG_FULL.
  */
 moe_status_t moe_grouped_gemm(const moe_ggemm_desc_t* d, const void* a, const int32_t* counts,
                               const int32_t* group_off, const void* w13, const void* w2, const float* s13,
                               const float* s2, void* y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* One-time permutation of expert weights into the order the grouped-GEMM
+ * kernel streams them (weights are static, quantized and stored once;
+ * Perplexity DeepSeek page, section Quantization). For expert g, block nt of
+ * 128 weight rows (W13: the gate and up rows of 64 h columns, interleaved 16 by
+ * 16 per wave; W2: 128 output rows) and 128-deep K chunk c, the 4 waves' 32 rows
+ * each are stored as [g][nt][c][wave][load][lane][16 bytes], so each wave load
+ * reads 1 KiB of contiguous memory and each workgroup streams one sequential
+ * region (the row-major layout makes a workgroup read 128 rows in 256-byte
+ * pieces, which MI355X HBM serves at about two thirds of the rate).
+ *
+ * w13 [G, 2I, H] -> w13_packed, w2 [G, H, I] -> w2_packed, same byte sizes,
+ * w_dt MOE_BF16 or MOE_FP8_E4M3 (fp8 scales keep their layout). Either pair may
+ * be NULL to skip it. Not in place. H and I multiples of 128.
+ */
+moe_status_t moe_pack_weights(int n_groups, int hidden, int inter, moe_dtype_t w_dt, const void* w13, const void* w2,
+                              void* w13_packed, void* w2_packed, hipStream_t stream);
 
 /* ------------------------------------------------------------------ combine
  * Undo the dispatch permutation and take the router-weighted sum (lehuy.net

@@ -100,8 +100,12 @@ def test_dispatch_and_combine_argument_errors(lib):
 
 def _gd(**kw):
     base = dict(n_groups=4, hidden=256, inter=128, act_dt=1, w_dt=1, layout=0, n_src=1, capacity=0, rows=64, stage=0)
+    shared = kw.pop("shared", None)
     base.update(kw)
-    return GGemmDesc(**base)
+    d = GGemmDesc(**base)
+    if shared is not None:
+        d.shared = ctypes.pointer(shared)
+    return d
 
 
 def test_grouped_gemm_workspace_and_errors(lib):
@@ -126,6 +130,40 @@ def test_grouped_gemm_workspace_and_errors(lib):
     fd = _gd(w_dt=2)
     assert f(ctypes.byref(fd), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, ws, None) == INVALID
     assert f(ctypes.byref(_gd(rows=0)), *ptrs, FAKE, ws, None) == OK   # nothing to do
+
+
+def test_grouped_gemm_shared_expert_validation(lib):
+    from combine_router_softmax_amd import SharedExpert
+    f = lib.moe_grouped_gemm
+    base = lib.moe_grouped_gemm_workspace(ctypes.byref(_gd()))
+    se = SharedExpert(FAKE.value, 32, FAKE.value, FAKE.value, None, None, FAKE.value)
+    ws = lib.moe_grouped_gemm_workspace(ctypes.byref(_gd(shared=se)))
+    assert ws >= base + 32 * 128 * 2
+    assert lib.moe_grouped_gemm_workspace(ctypes.byref(_gd(shared=SharedExpert(None, -1)))) == 0
+    ptrs = [FAKE] * 8
+    assert f(ctypes.byref(_gd(shared=se)), *ptrs, FAKE, base, None) == WORKSPACE      # sized without it
+    bad = SharedExpert(None, 32, FAKE.value, FAKE.value, None, None, FAKE.value)
+    assert f(ctypes.byref(_gd(shared=bad)), *ptrs, FAKE, ws, None) == INVALID        # no input rows
+    fp8 = SharedExpert(FAKE.value, 32, FAKE.value, FAKE.value, None, None, FAKE.value)
+    assert f(ctypes.byref(_gd(w_dt=2, shared=fp8)), *ptrs, FAKE, ws, None) == INVALID  # fp8 without scales
+    assert f(ctypes.byref(_gd(n_groups=0, shared=SharedExpert(None, 0))), *ptrs, FAKE, ws, None) == OK
+
+
+def test_pack_weights_and_format_validation(lib):
+    f = lib.moe_pack_weights
+    assert f(4, 256, 128, 0, FAKE, FAKE, FAKE, FAKE, None) == UNSUPPORTED      # f32 weights are not packed
+    assert f(4, 200, 128, 1, FAKE, FAKE, FAKE, FAKE, None) == UNSUPPORTED      # H % 128
+    assert f(4, 256, 128, 1, FAKE, FAKE, FAKE, ctypes.c_void_p(0x200000), None) == INVALID  # in place
+    assert f(4, 256, 128, 1, FAKE, None, ctypes.c_void_p(0x300000), FAKE, None) == INVALID  # pairs mismatch
+    assert f(-1, 256, 128, 1, FAKE, FAKE, FAKE, FAKE, None) == INVALID
+    assert f(0, 256, 128, 1, None, None, None, None, None) == OK
+    bad = _gd()
+    bad.w_format = 7
+    assert lib.moe_grouped_gemm_workspace(ctypes.byref(bad)) == 0
+    f32p = _gd(act_dt=0, w_dt=0)
+    f32p.w_format = 1
+    ws = lib.moe_grouped_gemm_workspace(ctypes.byref(f32p))
+    assert lib.moe_grouped_gemm(ctypes.byref(f32p), *([FAKE] * 8), FAKE, ws, None) == UNSUPPORTED
 
 
 def test_product_never_imports_the_oracle():

@@ -115,7 +115,8 @@ def test_gemm_stages_match_full_and_are_deterministic():
     cfg = get_config("dsv3_decode_ep8", hidden=512, inter=256)
     got, ref, (a, dw, kw) = _gemm_case(cfg, [40, 3, 200], COMPACT, seed=4)
     y_full = kw["y"].clone()
-    ws = torch.empty(1 << 24, dtype=torch.uint8, device="cuda")
+    desc = moe.gemm_desc(3, 512, 256, torch.bfloat16, torch.bfloat16, COMPACT, 1, 0, a.shape[0])
+    ws = torch.zeros(moe.moe_grouped_gemm_workspace(desc), dtype=torch.uint8, device="cuda")
     kw2 = dict(kw)
     kw2["y"] = torch.zeros_like(y_full)
     moe.moe_grouped_gemm(a.cuda(), dw["w13"], dw["w2"], stage=moe.GG_UP, ws=ws, **{k: v for k, v in kw2.items()})
@@ -253,3 +254,82 @@ def test_layer_full_size(full_case):
     touched = ref["out"][:, 0] != -9.0
     assert np.all(got[~touched] == -9.0)
     assert rel_l2(got[touched], ref["out"][touched]) <= TOL[cfg.weight]
+
+
+@pytest.mark.parametrize("name", ["dsv3_decode_ep8", "kimi_k2_ep8"])
+@pytest.mark.parametrize("layout", [COMPACT, PADDED])
+def test_fused_shared_expert_matches_separate_calls(name, layout):
+    # the shared expert inside the routed launches matches a call of its own (up to
+    # the fp32 order of stream-K partial sums, which depends on the launch's tile
+    # count) and the oracle
+    cfg = get_config(name, hidden=1024, inter=512, n_experts=64, n_local=8, tokens_per_src=96)
+    d = make_inputs(cfg, 2)
+    share = _share_from_inputs(d, layout)
+    logits = torch.from_numpy(d["logits"]).cuda()
+    off = torch.from_numpy(d["src_offsets"]).cuda()
+    x = d["x"].cuda()
+    o1 = torch.full_like(x, -9.0)
+    o2 = torch.full_like(x, -9.0)
+    share.step(logits, off, x, o1, fused_shared=True)
+    ys1 = share.ys.clone()
+    share.step(logits, off, x, o2, fused_shared=False)
+    torch.cuda.synchronize()
+    assert rel_l2(f64(ys1), f64(share.ys)) <= 2e-3
+    assert rel_l2(f64(o1), f64(o2)) <= 2e-3
+    sw = d["shared"]
+    fp8 = sw.get("s13") is not None
+    B0 = int(d["src_offsets"][1])
+    ref = swiglu_ffn(f64(d["x"][:B0]), *(weights_f64(sw, 0)))
+    assert rel_l2(f64(ys1[:B0]), ref) <= TOL[cfg.weight]
+
+
+def test_shared_expert_only_call():
+    cfg = get_config("dsv3_decode_ep8", hidden=512, inter=256)
+    sw = make_expert_weights(cfg, 3, shared=True)
+    a = torch.randn(77, 512, dtype=torch.bfloat16, device="cuda")
+    y = torch.full((77, 512), 5.0, dtype=torch.bfloat16, device="cuda")
+    dummy = torch.empty((0, 512), dtype=torch.bfloat16, device="cuda")
+    w13, w2 = sw["w13"].cuda(), sw["w2"].cuda()
+    moe.moe_grouped_gemm(dummy, w13[:0], w2[:0], group_off=torch.zeros(1, dtype=torch.int32, device="cuda"),
+                         shared={"a": a, "w13": w13, "w2": w2, "y": y})
+    ref = swiglu_ffn(f64(a), *(weights_f64(sw, 0)))
+    assert rel_l2(f64(y), ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("wname", ["bf16", "fp8"])
+def test_pack_weights_is_a_permutation_and_gemm_matches(wname):
+    cfg = get_config("dsv3_decode_ep8" if wname == "bf16" else "kimi_k2_ep8", hidden=1024, inter=512)
+    G = 5
+    wd = make_expert_weights(cfg, 1, experts=range(G))
+    w13, w2 = wd["w13"].cuda(), wd["w2"].cuda()
+    p13, p2 = moe.moe_pack_weights(w13, w2, cfg.hidden, cfg.inter)
+    torch.cuda.synchronize()
+    for a, b in ((w13, p13), (w2, p2)):
+        ab = a.view(torch.uint8).reshape(-1).cpu().numpy()
+        bb = b.view(torch.uint8).reshape(-1).cpu().numpy()
+        assert not np.array_equal(ab, bb)
+        np.testing.assert_array_equal(np.sort(ab), np.sort(bb))
+    # same arithmetic from either layout: bit-identical outputs, with a shared expert in the launch
+    rng = np.random.default_rng(3)
+    ms = [40, 0, 129, 7, 64]
+    off = torch.tensor(np.concatenate([[0], np.cumsum(ms)]), dtype=torch.int32, device="cuda")
+    R = int(off[-1])
+    x = torch.from_numpy(rng.standard_normal((R, cfg.hidden)).astype(np.float32)).to(torch.bfloat16).cuda()
+    xs = torch.from_numpy(rng.standard_normal((50, cfg.hidden)).astype(np.float32)).to(torch.bfloat16).cuda()
+    sw = make_expert_weights(cfg, 2, shared=True)
+    s13, s2 = sw["w13"].cuda(), sw["w2"].cuda()
+    ps13, ps2 = moe.moe_pack_weights(s13, s2, cfg.hidden, cfg.inter)
+    outs = []
+    for fmt, (a13, a2, b13, b2) in ((moe.W_ROWMAJOR, (w13, w2, s13, s2)), (moe.W_PACKED, (p13, p2, ps13, ps2))):
+        y = torch.zeros((R, cfg.hidden), dtype=torch.bfloat16, device="cuda")
+        ys = torch.zeros((50, cfg.hidden), dtype=torch.bfloat16, device="cuda")
+        sc = {} if wname == "bf16" else {"s13": wd["s13"].cuda(), "s2": wd["s2"].cuda()}
+        ssc = {} if wname == "bf16" else {"s13": sw["s13"].cuda(), "s2": sw["s2"].cuda()}
+        moe.moe_grouped_gemm(x, a13, a2, group_off=off, y=y, w_format=fmt,
+                             shared={"a": xs, "w13": b13, "w2": b2, "y": ys, **ssc}, **sc)
+        outs.append((y, ys))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
+    assert torch.equal(outs[0][1].view(torch.int16), outs[1][1].view(torch.int16))
+    ref = grouped_ffn(f64(x), {"layout": COMPACT, "expert_off": off.cpu().numpy(), "rows": R}, *_oracle_weights(wd))
+    assert rel_l2(f64(outs[1][0]), ref) <= TOL[cfg.weight]
