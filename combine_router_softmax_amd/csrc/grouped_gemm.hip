@@ -51,7 +51,6 @@ constexpr int kGemmThreads = 256;
 constexpr int kBM = 128;            // rows per tile
 constexpr int kMB = kBM / 32;       // 32-row MFMA blocks per tile
 constexpr int kKC = 128;            // reduction chunk
-constexpr int kLdsStride = kKC + 8; // bf16 per staged activation row (272 B, 16-B aligned)
 constexpr int kMaxGroups = 512;
 constexpr int kGemmMaxSrc = 512;
 
@@ -231,11 +230,11 @@ __device__ inline float* sk_slot(float* parts, int b, int slot) {
   return parts + (size_t(b) * 2 + slot) * kPartFloats;
 }
 
-template <int KIND>
-__device__ __forceinline__ void ffn_epilogue(const f32x16_t (&acc)[kMB], const Tile& tl, int nb, const Sched& sh,
+template <int KIND, int NBMAX>
+__device__ __forceinline__ void ffn_epilogue(const f32x16_t (&acc)[NBMAX], const Tile& tl, int nb, const Sched& sh,
                                              uint16_t* out, int n_out, int wv, int lr, int lh) {
 #pragma unroll
-  for (int b = 0; b < kMB; ++b) {
+  for (int b = 0; b < NBMAX; ++b) {
     if (b >= nb) continue;
     const int phys = sh.rowmap[b * 32 + lr];
     if (phys < 0) continue;
@@ -260,17 +259,178 @@ __device__ __forceinline__ void ffn_epilogue(const f32x16_t (&acc)[kMB], const T
   }
 }
 
-template <int KIND, bool FP8>
+// Everything one workgroup does for the K chunks [c_begin, c_end) of one tile.
+struct TileRun {
+  const uint16_t* A;   // activation rows of the tile's problem
+  const void* W;       // weights of the tile's problem
+  const float* sbase;  // fp8: block scales of the tile's expert
+  size_t wrow_elems;   // row-major weights: first element of this lane's weight row
+  size_t wpack;        // packed weights: first 16-byte piece of this workgroup's (expert, N block)
+  int srow0, srow1;    // fp8: scale rows of the gate/up (or output) rows
+  int c_begin, c_end, nchunks;
+};
+
+// NB = active 32-row blocks, a compile-time constant so the K loop has no
+// branches. Loads are issued unconditionally (chunk indices clamped to the
+// range; rows past the tile read a valid row and are zeroed before staging),
+// activations for chunk c+1 before weights for chunk c+2, because vector loads
+// retire in order: staging chunk c+1 then waits only for its own loads while
+// two weight chunks stay in flight.
+template <int KIND, bool FP8, bool PACKED, int NB, int BMT>
+__device__ __forceinline__ void run_tile(const GemmArgs& p, const TileRun& tr, const Tile& tl, Sched& sh,
+                                         uint16_t (&xs)[2][BMT * kKC], float* __restrict__ parts,
+                                         bool first_tile) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
+  const int lr = lane & 31;
+  const int lh = lane >> 5;
+  constexpr int WV = FP8 ? 4 : 8;  // 16-byte weight loads per lane per chunk
+  constexpr int XV = NB * 2;       // 16-row passes of activation staging
+  const int last = tr.c_end - 1;
+
+  // Activation staging through registers into LDS: thread -> (row = tid/16 +
+  // 16*i, 16-byte column tid%16). Slot s of staged row r holds 16-byte column
+  // s ^ (r % 16) (XOR swizzle instead of padding: a column read by 16
+  // consecutive rows hits 16 different bank groups). Rows past the tile load a
+  // valid row: a token row only feeds its own MFMA output column, which the
+  // epilogue discards.
+  const int xr = tid >> 4;
+  const int xslot = ((tid & 15) ^ (xr & 15)) * 8;  // (xr + 16 i) % 16 == xr % 16
+  int xrow[XV];
+  const int phys0 = sh.rowmap[0];
+#pragma unroll
+  for (int i = 0; i < XV; ++i) {
+    const int phys = sh.rowmap[xr + 16 * i];
+    xrow[i] = phys >= 0 ? phys : phys0;
+  }
+  // (plain unrolled loops over register arrays, no closures: the arrays must
+  // stay in registers)
+  // staged activations live in one vector value (XV x 16 bytes)
+  typedef uint32_t xvec_t __attribute__((ext_vector_type(4 * XV)));
+#define MOE_LOAD_X(XV_, C_)                                                                                   \
+  _Pragma("unroll") for (int i = 0; i < XV; ++i) {                                                            \
+    const uint4 t_ =                                                                                          \
+        *reinterpret_cast<const uint4*>(tr.A + size_t(xrow[i]) * p.K + size_t(C_) * kKC + (tid & 15) * 8);    \
+    XV_[4 * i] = t_.x;                                                                                        \
+    XV_[4 * i + 1] = t_.y;                                                                                    \
+    XV_[4 * i + 2] = t_.z;                                                                                    \
+    XV_[4 * i + 3] = t_.w;                                                                                    \
+  }
+#define MOE_STORE_X(XV_, BUF_)                                                                                \
+  _Pragma("unroll") for (int i = 0; i < XV; ++i)                                                              \
+      *reinterpret_cast<uint4*>(&xs[BUF_][(xr + 16 * i) * kKC + xslot]) =                                     \
+          make_uint4(XV_[4 * i], XV_[4 * i + 1], XV_[4 * i + 2], XV_[4 * i + 3]);
+  const uint4* wpk = static_cast<const uint4*>(tr.W) + tr.wpack + size_t(wv) * WV * kWave + lane;
+  const uint8_t* wrm8 = static_cast<const uint8_t*>(tr.W) + tr.wrow_elems + 64 * lh;
+  const uint16_t* wrm16 = static_cast<const uint16_t*>(tr.W) + tr.wrow_elems + 32 * lh;
+#define MOE_LOAD_W(W_, C_)                                                                                    \
+  if constexpr (PACKED) {                                                                                     \
+    _Pragma("unroll") for (int j = 0; j < WV; ++j) W_[j] = wpk[(size_t(C_) * 4 * WV + j) * kWave];           \
+  } else if constexpr (FP8) {                                                                                 \
+    _Pragma("unroll") for (int j = 0; j < WV; ++j)                                                            \
+        W_[j] = *reinterpret_cast<const uint4*>(wrm8 + size_t(C_) * kKC + 16 * j);                            \
+  } else {                                                                                                    \
+    _Pragma("unroll") for (int j = 0; j < WV; ++j)                                                            \
+        W_[j] = *reinterpret_cast<const uint4*>(wrm16 + size_t(C_) * kKC + 64 * (j >> 2) + 8 * (j & 3));      \
+  }
+
+  f32x16_t acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
+
+  // weight register ring: DEPTH-1 chunks in flight while one is used (3 deep
+  // where the registers allow it). Per chunk, the activations of chunk c+1 are
+  // loaded before the weights of chunk c+DEPTH-1: vector loads retire in order,
+  // so staging chunk c+1 waits only for its own loads while the weight
+  // prefetch stays in flight.
+  constexpr int DEPTH = (NB == 1 || (FP8 && NB <= 2)) ? 3 : 2;
+  uint4 w[DEPTH][WV];
+  xvec_t xv;
+  MOE_LOAD_X(xv, tr.c_begin)
+#pragma unroll
+  for (int d = 0; d + 1 < DEPTH; ++d) { MOE_LOAD_W(w[d], min(tr.c_begin + d, last)) }
+  MOE_STORE_X(xv, 0)
+  for (int c0 = tr.c_begin; c0 < tr.c_end; c0 += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const int c = c0 + d;
+      if (c >= tr.c_end) break;
+      const int buf = (c - tr.c_begin) & 1;
+      MOE_LOAD_X(xv, min(c + 1, last))
+      MOE_LOAD_W(w[(d + DEPTH - 1) % DEPTH], min(c + DEPTH - 1, last))
+      __syncthreads();  // chunk c staged by every wave; nobody still reads buf ^ 1
+      const uint16_t* xb = xs[buf];
+      if constexpr (FP8) {
+        f32x16_t part[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) part[b][v] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint4 q = w[d][j >> 1];
+          const bf16x8_t a = (j & 1) ? fp8x8_to_bf16(q.z, q.w) : fp8x8_to_bf16(q.x, q.y);
+          const int cl = 8 * lh + j;  // 16-byte column: k = 64*lh + 8*j
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            const int rr = b * 32 + lr;
+            const uint4 bv = *reinterpret_cast<const uint4*>(&xb[rr * kKC + ((cl ^ (rr & 15)) * 8)]);
+            part[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bv), part[b], 0, 0, 0);
+          }
+        }
+        const float s0 = tr.sbase[tr.srow0 * tr.nchunks + c];
+        const float s1 = tr.sbase[tr.srow1 * tr.nchunks + c];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[b][v] = fmaf(v < 8 ? s0 : s1, part[b][v], acc[b][v]);
+      } else {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int cl = 8 * (j >> 2) + 4 * lh + (j & 3);  // k = 64*(j/4) + 32*lh + 8*(j%4)
+            const int rr = b * 32 + lr;
+            const uint4 bv = *reinterpret_cast<const uint4*>(&xb[rr * kKC + ((cl ^ (rr & 15)) * 8)]);
+            acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w[d][j]),
+                                                              __builtin_bit_cast(bf16x8_t, bv), acc[b], 0, 0, 0);
+          }
+        }
+      }
+      MOE_STORE_X(xv, buf ^ 1)  // chunk c+1 (a harmless repeat of the last chunk at the end)
+    }
+  }
+#undef MOE_LOAD_X
+#undef MOE_STORE_X
+#undef MOE_LOAD_W
+  if (tr.c_begin == 0 && tr.c_end == tr.nchunks) {
+    uint16_t* out = static_cast<uint16_t*>(tl.shared ? p.sh_out : p.out);
+    ffn_epilogue<KIND, NB>(acc, tl, NB, sh, out, p.n_out, wv, lr, lh);
+  } else {
+    // partial sums of a split tile, in accumulator-register order
+    float* dst = sk_slot(parts, blockIdx.x, first_tile ? 0 : 1);
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) dst[((wv * kMB + b) * 16 + v) * kWave + lane] = acc[b][v];
+  }
+}
+
+template <int KIND, bool FP8, bool PACKED>
 __global__ __launch_bounds__(kGemmThreads, 2) void ffn_mfma_kernel(GemmArgs p, float* __restrict__ parts) {
+  // rows per tile: 64 for bf16 weights (registers), 128 for fp8 weights
+  constexpr int BMT = FP8 ? kBM : kBM / 2;
   __shared__ Sched sh;
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][kBM * kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][BMT * kKC];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
-  const int lr = lane & 31;   // MFMA row/column inside a 32 block
-  const int lh = lane >> 5;   // which half of the 16-deep MFMA step this lane feeds
-  const int n_tiles = build_schedule(p, kBM, sh);
+  const int lr = lane & 31;
+  const int n_tiles = build_schedule(p, BMT, sh);
   const int nchunks = p.K / kKC;
   const int64_t total = int64_t(n_tiles) * nchunks;
   const int64_t i0 = sk_start(blockIdx.x, total), i1 = sk_start(blockIdx.x + 1, total);
@@ -278,170 +438,46 @@ __global__ __launch_bounds__(kGemmThreads, 2) void ffn_mfma_kernel(GemmArgs p, f
   const int t_first = int(i0 / nchunks), t_last = int((i1 - 1) / nchunks);
 
   for (int t = t_first; t <= t_last; ++t) {
-    const int c_begin = int(max<int64_t>(i0, int64_t(t) * nchunks) - int64_t(t) * nchunks);
-    const int c_end = int(min<int64_t>(i1, int64_t(t + 1) * nchunks) - int64_t(t) * nchunks);
-    const Tile tl = decode_tile(p, kBM, sh, t);
-    build_rowmap(p, tl, kBM, sh);
-    const int nb = (tl.nrows + 31) / 32;  // active 32-row blocks (uniform)
-    const uint16_t* A = static_cast<const uint16_t*>(tl.shared ? p.sh_a : p.a);
-    const void* Wt = tl.shared ? p.sh_w : p.w;
-    const float* St = tl.shared ? p.sh_s : p.s;
-
-    // weight row of this lane
-    int wrow;
+    const Tile tl = decode_tile(p, BMT, sh, t);
+    build_rowmap(p, tl, BMT, sh);
+    TileRun tr;
+    tr.c_begin = int(max<int64_t>(i0, int64_t(t) * nchunks) - int64_t(t) * nchunks);
+    tr.c_end = int(min<int64_t>(i1, int64_t(t + 1) * nchunks) - int64_t(t) * nchunks);
+    tr.nchunks = nchunks;
+    tr.A = static_cast<const uint16_t*>(tl.shared ? p.sh_a : p.a);
+    tr.W = tl.shared ? p.sh_w : p.w;
+    int wrow;  // weight row of this lane (row-major weights)
     if (KIND == kUp) {
       const int j = tl.nt * 64 + 16 * wv + (lr & 15);
       wrow = lr < 16 ? j : p.n_out + j;
     } else {
       wrow = tl.nt * 128 + 32 * wv + lr;
     }
-    const size_t wrow_elems = (size_t(tl.we) * p.n_w_rows + wrow) * p.K;
-
-    // fp8 block scales used by this tile's rows (uniform per workgroup)
-    int srow0 = 0, srow1 = 0;
+    tr.wrow_elems = (size_t(tl.we) * p.n_w_rows + wrow) * p.K;
+    constexpr int WV = FP8 ? 4 : 8;
+    tr.wpack = (size_t(tl.we) * p.n_tiles_n + tl.nt) * nchunks * 4 * WV * kWave;
+    tr.srow0 = tr.srow1 = 0;
+    tr.sbase = nullptr;
     if (FP8) {
       if (KIND == kUp) {
-        srow0 = (tl.nt * 64) / 128;
-        srow1 = (p.n_out + tl.nt * 64) / 128;
+        tr.srow0 = (tl.nt * 64) / 128;
+        tr.srow1 = (p.n_out + tl.nt * 64) / 128;
       } else {
-        srow0 = srow1 = tl.nt;
+        tr.srow0 = tr.srow1 = tl.nt;
       }
+      tr.sbase = (tl.shared ? p.sh_s : p.s) + size_t(tl.we) * (p.n_w_rows / 128) * nchunks;
     }
-    const float* sbase = FP8 ? St + size_t(tl.we) * (p.n_w_rows / 128) * nchunks : nullptr;
-
-    // activation staging: thread -> (row = tid/16 + 16*i, 16-byte column tid%16)
-    const int xr = tid >> 4, xc = (tid & 15) * 8;
-    auto load_x = [&](uint4* xv, int c) {
-#pragma unroll
-      for (int i = 0; i < kBM / 16; ++i) {
-        const int r = xr + 16 * i;
-        const int phys = sh.rowmap[r];
-        if (i * 16 < nb * 32 && phys >= 0)
-          xv[i] = *reinterpret_cast<const uint4*>(A + size_t(phys) * p.K + size_t(c) * kKC + xc);
-        else
-          xv[i] = make_uint4(0, 0, 0, 0);
+    const int nb = (tl.nrows + 31) / 32;  // active 32-row blocks (uniform; 3 runs as 4)
+    const bool first = t == t_first;
+    if constexpr (FP8) {
+      switch (nb) {
+        case 1: run_tile<KIND, FP8, PACKED, 1, BMT>(p, tr, tl, sh, xs, parts, first); break;
+        case 2: run_tile<KIND, FP8, PACKED, 2, BMT>(p, tr, tl, sh, xs, parts, first); break;
+        default: run_tile<KIND, FP8, PACKED, 4, BMT>(p, tr, tl, sh, xs, parts, first); break;
       }
-    };
-    auto store_x = [&](const uint4* xv, int buf) {
-#pragma unroll
-      for (int i = 0; i < kBM / 16; ++i)
-        if (i * 16 < nb * 32)
-          *reinterpret_cast<uint4*>(&xs[buf][(xr + 16 * i) * kLdsStride + xc]) = xv[i];
-    };
-
-    constexpr int WV = FP8 ? 4 : 8;  // 16-byte weight loads per lane per chunk
-    auto load_w = [&](uint4* wvv, int c) {
-      if (p.packed) {
-        // packed: this wave's WV x 1 KiB of chunk c, one contiguous 1 KiB per load
-        const uint4* wp = static_cast<const uint4*>(Wt) +
-                          ((((size_t(tl.we) * p.n_tiles_n + tl.nt) * nchunks + c) * 4 + wv) * WV) * kWave + lane;
-#pragma unroll
-        for (int j = 0; j < WV; ++j) wvv[j] = wp[j * kWave];
-      } else if (FP8) {
-        const uint8_t* wp = static_cast<const uint8_t*>(Wt) + wrow_elems + size_t(c) * kKC + 64 * lh;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) wvv[j] = *reinterpret_cast<const uint4*>(wp + 16 * j);
-      } else {
-        const uint16_t* wp = static_cast<const uint16_t*>(Wt) + wrow_elems + size_t(c) * kKC + 32 * lh;
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) wvv[sb * 4 + j] = *reinterpret_cast<const uint4*>(wp + 64 * sb + 8 * j);
-      }
-    };
-
-    f32x16_t acc[kMB];
-#pragma unroll
-    for (int b = 0; b < kMB; ++b)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
-
-    // One K chunk: MFMAs on the weight registers `cur` and the staged activations;
-    // on entry the loads of chunk c+2 go into `nxt` (weights two chunks ahead:
-    // two chunks of every lane's weight stream are in flight while one is used)
-    // and of chunk c+1 into xv (activations, one chunk ahead, L2-resident).
-    uint4 wa[WV], wb[WV], wc[WV], xv[kBM / 16];
-    auto step = [&](int c, const uint4 (&cur)[WV], uint4 (&nxt)[WV]) {
-      const int buf = (c - c_begin) & 1;
-      const bool more = c + 1 < c_end;
-      if (c + 2 < c_end) load_w(nxt, c + 2);
-      if (more) load_x(xv, c + 1);
-      __syncthreads();
-      const uint16_t* xb = xs[buf];
-      if (FP8) {
-        f32x16_t part[kMB];
-#pragma unroll
-        for (int b = 0; b < kMB; ++b)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) part[b][v] = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint4 q = cur[j >> 1];
-          const bf16x8_t a = (j & 1) ? fp8x8_to_bf16(q.z, q.w) : fp8x8_to_bf16(q.x, q.y);
-          const int col = 64 * lh + 8 * j;
-#pragma unroll
-          for (int b = 0; b < kMB; ++b) {
-            if (b < nb) {
-              const uint4 bv = *reinterpret_cast<const uint4*>(&xb[(b * 32 + lr) * kLdsStride + col]);
-              part[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bv), part[b], 0, 0,
-                                                                 0);
-            }
-          }
-        }
-        const float s0 = sbase[srow0 * nchunks + c];
-        const float s1 = sbase[srow1 * nchunks + c];
-#pragma unroll
-        for (int b = 0; b < kMB; ++b) {
-          if (b < nb) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[b][v] = fmaf(v < 8 ? s0 : s1, part[b][v], acc[b][v]);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, cur[sb * 4 + j]);
-            const int col = 64 * sb + 32 * lh + 8 * j;
-#pragma unroll
-            for (int b = 0; b < kMB; ++b) {
-              if (b < nb) {
-                const uint4 bv = *reinterpret_cast<const uint4*>(&xb[(b * 32 + lr) * kLdsStride + col]);
-                acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bv), acc[b], 0, 0,
-                                                                  0);
-              }
-            }
-          }
-        }
-      }
-      if (more) store_x(xv, buf ^ 1);
-    };
-
-    load_w(wa, c_begin);
-    if (c_begin + 1 < c_end) load_w(wb, c_begin + 1);
-    load_x(xv, c_begin);
-    store_x(xv, 0);
-    for (int c = c_begin; c < c_end; c += 3) {
-      step(c, wa, wc);
-      if (c + 1 >= c_end) break;
-      step(c + 1, wb, wa);
-      if (c + 2 >= c_end) break;
-      step(c + 2, wc, wb);
-    }
-
-    if (c_begin == 0 && c_end == nchunks) {
-      uint16_t* out = static_cast<uint16_t*>(tl.shared ? p.sh_out : p.out);
-      ffn_epilogue<KIND>(acc, tl, nb, sh, out, p.n_out, wv, lr, lh);
     } else {
-      // partial sums of a split tile, in accumulator-register order
-      float* dst = sk_slot(parts, blockIdx.x, t == t_first ? 0 : 1);
-#pragma unroll
-      for (int b = 0; b < kMB; ++b) {
-        if (b >= nb) continue;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) dst[((wv * kMB + b) * 16 + v) * kWave + lane] = acc[b][v];
-      }
+      if (nb == 1) run_tile<KIND, FP8, PACKED, 1, BMT>(p, tr, tl, sh, xs, parts, first);
+      else run_tile<KIND, FP8, PACKED, 2, BMT>(p, tr, tl, sh, xs, parts, first);
     }
     __syncthreads();  // rowmap and staging buffers are rewritten by the next tile
   }
@@ -450,7 +486,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void ffn_mfma_kernel(GemmArgs p, f
 // Finishes the tiles cut by a stream-K range boundary: block j looks at the
 // boundary between workgroups j and j+1; the first boundary inside a tile
 // sums that tile's partials in workgroup order and runs the epilogue.
-template <int KIND>
+template <int KIND, int BMT>
 __global__ __launch_bounds__(kGemmThreads) void ffn_fixup_kernel(GemmArgs p, const float* __restrict__ parts) {
   __shared__ Sched sh;
   const int tid = threadIdx.x;
@@ -458,7 +494,7 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_fixup_kernel(GemmArgs p, con
   const int wv = tid / kWave;
   const int lr = lane & 31;
   const int lh = lane >> 5;
-  const int n_tiles = build_schedule(p, kBM, sh);
+  const int n_tiles = build_schedule(p, BMT, sh);
   const int nchunks = p.K / kKC;
   const int64_t total = int64_t(n_tiles) * nchunks;
   const int j = blockIdx.x;
@@ -466,8 +502,8 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_fixup_kernel(GemmArgs p, con
   if (ib <= 0 || ib >= total || ib % nchunks == 0) return;  // not inside a tile
   const int t = int(ib / nchunks);
   if (j > 0 && sk_start(j, total) > int64_t(t) * nchunks) return;  // an earlier boundary owns this tile
-  const Tile tl = decode_tile(p, kBM, sh, t);
-  build_rowmap(p, tl, kBM, sh);
+  const Tile tl = decode_tile(p, BMT, sh, t);
+  build_rowmap(p, tl, BMT, sh);
   const int nb = (tl.nrows + 31) / 32;
   const int b_lo = sk_owner(int64_t(t) * nchunks, total);
   const int b_hi = sk_owner(int64_t(t + 1) * nchunks - 1, total);
@@ -488,7 +524,7 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_fixup_kernel(GemmArgs p, con
     }
   }
   uint16_t* out = static_cast<uint16_t*>(tl.shared ? p.sh_out : p.out);
-  ffn_epilogue<KIND>(acc, tl, nb, sh, out, p.n_out, wv, lr, lh);
+  ffn_epilogue<KIND, kMB>(acc, tl, nb, sh, out, p.n_out, wv, lr, lh);
 }
 
 // ------------------------------------------------------------------ weight packing
@@ -660,16 +696,24 @@ static moe_status_t launch_stage(const GemmArgs& p, bool f32, bool fp8, int kind
     return launch_status();
   }
   const dim3 grid(kSkGrid), fix_grid(kSkGrid - 1);
+#define MOE_FFN(K, F, P) hipLaunchKernelGGL((ffn_mfma_kernel<K, F, P>), grid, block, 0, stream, p, parts)
   if (fp8) {
-    if (kind == kUp) hipLaunchKernelGGL((ffn_mfma_kernel<kUp, true>), grid, block, 0, stream, p, parts);
-    else hipLaunchKernelGGL((ffn_mfma_kernel<kDown, true>), grid, block, 0, stream, p, parts);
+    if (kind == kUp) { if (p.packed) MOE_FFN(kUp, true, true); else MOE_FFN(kUp, true, false); }
+    else { if (p.packed) MOE_FFN(kDown, true, true); else MOE_FFN(kDown, true, false); }
   } else {
-    if (kind == kUp) hipLaunchKernelGGL((ffn_mfma_kernel<kUp, false>), grid, block, 0, stream, p, parts);
-    else hipLaunchKernelGGL((ffn_mfma_kernel<kDown, false>), grid, block, 0, stream, p, parts);
+    if (kind == kUp) { if (p.packed) MOE_FFN(kUp, false, true); else MOE_FFN(kUp, false, false); }
+    else { if (p.packed) MOE_FFN(kDown, false, true); else MOE_FFN(kDown, false, false); }
   }
+#undef MOE_FFN
   if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
-  if (kind == kUp) hipLaunchKernelGGL(ffn_fixup_kernel<kUp>, fix_grid, block, 0, stream, p, parts);
-  else hipLaunchKernelGGL(ffn_fixup_kernel<kDown>, fix_grid, block, 0, stream, p, parts);
+  const int bmt = fp8 ? kBM : kBM / 2;  // must match ffn_mfma_kernel
+  if (kind == kUp) {
+    if (bmt == kBM) hipLaunchKernelGGL((ffn_fixup_kernel<kUp, kBM>), fix_grid, block, 0, stream, p, parts);
+    else hipLaunchKernelGGL((ffn_fixup_kernel<kUp, kBM / 2>), fix_grid, block, 0, stream, p, parts);
+  } else {
+    if (bmt == kBM) hipLaunchKernelGGL((ffn_fixup_kernel<kDown, kBM>), fix_grid, block, 0, stream, p, parts);
+    else hipLaunchKernelGGL((ffn_fixup_kernel<kDown, kBM / 2>), fix_grid, block, 0, stream, p, parts);
+  }
   return launch_status();
 }
 
