@@ -179,6 +179,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="dsv3_decode_ep8")
     ap.add_argument("--layout", choices=["compact", "padded"], default="compact")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches instead of replays of a HIP graph of one step")
     ap.add_argument("--cpu-max-tokens", type=int, default=1024)
     ap.add_argument("--copy-calib", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
@@ -230,6 +232,7 @@ def main(argv=None):
         share.step(logits, offs, x, out)
     torch.cuda.synchronize()
 
+    # per-call timing: eager steps with events around each call
     ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)] for n in STEP_NAMES}
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -241,9 +244,35 @@ def main(argv=None):
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gpu_ms = e0.elapsed_time(e1)
-    ms_per_step = gpu_ms / args.steps
+    eager_ms = e0.elapsed_time(e1) / args.steps
     per_call_us = {n: 1e3 * float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n in STEP_NAMES}
+
+    # the step as one HIP graph (one graph per batch shape, as the pages do with
+    # CUDA graphs): same kernels, no host launch gaps
+    graph_ms = None
+    if not args.eager:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            share.step(logits, offs, x, out)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            share.step(logits, offs, x, out)
+        for _ in range(max(1, args.warmup)):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        g0.record()
+        for _ in range(args.steps):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        graph_ms = g0.elapsed_time(g1) / args.steps
+    ms_per_step = graph_ms if graph_ms is not None else eager_ms
     st = int(share.lay["status"].item())
 
     counts = share.lay["counts"].cpu().numpy().astype(np.int64)
@@ -289,6 +318,8 @@ def main(argv=None):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "timing": "hip_graph_replay" if graph_ms is not None else "eager",
+        "ms_per_step_eager": round(eager_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

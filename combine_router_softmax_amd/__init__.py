@@ -180,12 +180,12 @@ def moe_dispatch_layout(topk_idx: torch.Tensor, src_offsets: torch.Tensor, n_exp
     wsb = int(lib().moe_dispatch_layout_workspace(ctypes.byref(d)))
     dev = topk_idx.device
     o = dict(out) if out else {}
-    o.setdefault("counts", torch.empty((n_local, S), dtype=torch.int32, device=dev))
-    o.setdefault("expert_off", torch.empty(n_local + 1, dtype=torch.int32, device=dev))
-    o.setdefault("row_of", torch.empty(N * K, dtype=torch.int32, device=dev))
-    o.setdefault("row_token", torch.empty(max(R, 1), dtype=torch.int32, device=dev))
-    o.setdefault("status", torch.empty(1, dtype=torch.int32, device=dev))
-    o.setdefault("ws", torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev))
+    shapes = {"counts": ((n_local, S), torch.int32), "expert_off": ((n_local + 1,), torch.int32),
+              "row_of": ((N * K,), torch.int32), "row_token": ((max(R, 1),), torch.int32),
+              "status": ((1,), torch.int32), "ws": ((max(wsb, 256),), torch.uint8)}
+    for k, (shape, dt) in shapes.items():
+        if k not in o:   # allocate only what the caller did not bring
+            o[k] = torch.empty(shape, dtype=dt, device=dev)
     for k in ("counts", "expert_off", "row_of", "row_token", "status"):
         _dev(o[k], k, torch.int32)
     _check(lib().moe_dispatch_layout(ctypes.byref(d), _ptr(topk_idx), _ptr(src_offsets), _ptr(o["counts"]),

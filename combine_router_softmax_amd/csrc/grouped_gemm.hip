@@ -30,14 +30,14 @@
 // permuted identically for both operands so every weight load is a 64-byte
 // run.
 //
-// fp8 e4m3 weights: codes are decoded exactly to bf16 in registers
-// (v_cvt_scalef32_pk_bf16_fp8 with unit scale), the chunk is accumulated
-// separately, and the fp32 128x128 block scale is applied to that partial sum
-// (scale blocks align with the 128-deep chunks and the 64/128-row tiles).
+// fp8 e4m3 weights: each code is decoded exactly to fp32, multiplied by its
+// 128x128 block's fp32 scale and rounded once to bf16 in registers, then the
+// bf16 MFMA runs as for bf16 weights (W8A16).
 //
 // fp32 activations + fp32 weights (small parity problems) use a plain SIMT
 // kernel with the same scheduler.
 #include <algorithm>
+#include <type_traits>
 
 #include "moe_common.hpp"
 
@@ -129,6 +129,7 @@ struct Tile {
   int we;       // expert index inside the weight tensor of the tile's problem
   bool shared;
   int nt, r0, nrows;
+  int mtiles;   // row tiles of the tile's group (1: its weights are read once)
 };
 
 __device__ Tile decode_tile(const GemmArgs& p, int bm, const Sched& sh, int t) {
@@ -146,6 +147,7 @@ __device__ Tile decode_tile(const GemmArgs& p, int bm, const Sched& sh, int t) {
   tl.we = tl.g;
   const int local = t - sh.tile_start[lo];
   const int mtiles = (sh.m[lo] + bm - 1) / bm;
+  tl.mtiles = mtiles;
   tl.nt = local / mtiles;
   tl.r0 = (local % mtiles) * bm;
   tl.nrows = min(bm, sh.m[lo] - tl.r0);
@@ -191,18 +193,34 @@ __device__ void build_rowmap(const GemmArgs& p, const Tile& tl, int bm, Sched& s
   __syncthreads();
 }
 
+// 16-byte weight load; with STREAM the non-temporal hint (data used once).
+template <bool STREAM>
+__device__ __forceinline__ uint4 ld_w(const uint4* p) {
+  if constexpr (STREAM) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+  } else {
+    return *p;
+  }
+}
+
 __device__ __forceinline__ float silu_f(float g) { return g / (1.f + __expf(-g)); }
 
-// e4m3fn x 8 (two dwords) -> bf16 x 8, exact.
-__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+// e4m3fn x 8 (two dwords) -> bf16 x 8 of code * scale: exact decode to fp32
+// (v_cvt_pk_f32_fp8), one fp32 multiply by the 128x128 block scale, one RNE
+// rounding to bf16. (v_cvt_scalef32_pk_bf16_fp8 would apply only the
+// power-of-two exponent of a scale, which block scales are not.)
+__device__ __forceinline__ bf16x8_t fp8x8_dequant(uint32_t w0, uint32_t w1, float s) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
-  bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
-  bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
-  bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  const bf16x2_t r0 = __builtin_convertvector(__builtin_amdgcn_cvt_pk_f32_fp8(w0, false) * s, bf16x2_t);
+  const bf16x2_t r1 = __builtin_convertvector(__builtin_amdgcn_cvt_pk_f32_fp8(w0, true) * s, bf16x2_t);
+  const bf16x2_t r2 = __builtin_convertvector(__builtin_amdgcn_cvt_pk_f32_fp8(w1, false) * s, bf16x2_t);
+  const bf16x2_t r3 = __builtin_convertvector(__builtin_amdgcn_cvt_pk_f32_fp8(w1, true) * s, bf16x2_t);
   bf16x8_t r;
-  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
-  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  r[0] = r0[0]; r[1] = r0[1]; r[2] = r1[0]; r[3] = r1[1];
+  r[4] = r2[0]; r[5] = r2[1]; r[6] = r3[0]; r[7] = r3[1];
   return r;
 }
 
@@ -216,6 +234,7 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
 // workspace, and ffn_fixup_kernel adds them in workgroup order and finishes
 // the tile. No workgroup ever waits for another.
 constexpr int kSkGrid = 512;                          // 2 resident workgroups x 256 compute units
+constexpr int kXcds = 8;                              // accelerator complex dies of MI355X
 constexpr int kPartFloats = 4 * kMB * 16 * kWave;     // one workgroup's accumulators (64 KiB)
 
 __host__ __device__ inline int64_t sk_start(int b, int64_t total) { return int64_t(b) * total / kSkGrid; }
@@ -276,10 +295,10 @@ struct TileRun {
 // activations for chunk c+1 before weights for chunk c+2, because vector loads
 // retire in order: staging chunk c+1 then waits only for its own loads while
 // two weight chunks stay in flight.
-template <int KIND, bool FP8, bool PACKED, int NB, int BMT>
+template <int KIND, bool FP8, bool PACKED, int NB, int BMT, bool STREAM>
 __device__ __forceinline__ void run_tile(const GemmArgs& p, const TileRun& tr, const Tile& tl, Sched& sh,
                                          uint16_t (&xs)[2][BMT * kKC], float* __restrict__ parts,
-                                         bool first_tile) {
+                                         int rng, bool first_tile) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
@@ -324,15 +343,20 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const TileRun& tr, c
   const uint4* wpk = static_cast<const uint4*>(tr.W) + tr.wpack + size_t(wv) * WV * kWave + lane;
   const uint8_t* wrm8 = static_cast<const uint8_t*>(tr.W) + tr.wrow_elems + 64 * lh;
   const uint16_t* wrm16 = static_cast<const uint16_t*>(tr.W) + tr.wrow_elems + 32 * lh;
+  // STREAM (the group fits one row tile, so its weights are read once):
+  // non-temporal weight loads, so the stream does not evict the activation rows
+  // that the expert's other N tiles re-read from L2. Otherwise the other row
+  // tiles re-read these weights and plain loads keep them cacheable.
 #define MOE_LOAD_W(W_, C_)                                                                                    \
   if constexpr (PACKED) {                                                                                     \
-    _Pragma("unroll") for (int j = 0; j < WV; ++j) W_[j] = wpk[(size_t(C_) * 4 * WV + j) * kWave];           \
+    _Pragma("unroll") for (int j = 0; j < WV; ++j) W_[j] = ld_w<STREAM>(wpk + (size_t(C_) * 4 * WV + j) * kWave); \
   } else if constexpr (FP8) {                                                                                 \
     _Pragma("unroll") for (int j = 0; j < WV; ++j)                                                            \
-        W_[j] = *reinterpret_cast<const uint4*>(wrm8 + size_t(C_) * kKC + 16 * j);                            \
+        W_[j] = ld_w<STREAM>(reinterpret_cast<const uint4*>(wrm8 + size_t(C_) * kKC + 16 * j));                  \
   } else {                                                                                                    \
     _Pragma("unroll") for (int j = 0; j < WV; ++j)                                                            \
-        W_[j] = *reinterpret_cast<const uint4*>(wrm16 + size_t(C_) * kKC + 64 * (j >> 2) + 8 * (j & 3));      \
+        W_[j] = ld_w<STREAM>(                                                                                 \
+            reinterpret_cast<const uint4*>(wrm16 + size_t(C_) * kKC + 64 * (j >> 2) + 8 * (j & 3)));          \
   }
 
   f32x16_t acc[NB];
@@ -364,29 +388,22 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const TileRun& tr, c
       __syncthreads();  // chunk c staged by every wave; nobody still reads buf ^ 1
       const uint16_t* xb = xs[buf];
       if constexpr (FP8) {
-        f32x16_t part[NB];
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) part[b][v] = 0.f;
+        // this lane's weight row: gate rows use srow0's scale, up rows srow1's
+        const float s0 = tr.sbase[tr.srow0 * tr.nchunks + c];
+        const float s1 = tr.sbase[tr.srow1 * tr.nchunks + c];
+        const float sc = lr < 16 ? s0 : s1;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const uint4 q = w[d][j >> 1];
-          const bf16x8_t a = (j & 1) ? fp8x8_to_bf16(q.z, q.w) : fp8x8_to_bf16(q.x, q.y);
+          const bf16x8_t a = (j & 1) ? fp8x8_dequant(q.z, q.w, sc) : fp8x8_dequant(q.x, q.y, sc);
           const int cl = 8 * lh + j;  // 16-byte column: k = 64*lh + 8*j
 #pragma unroll
           for (int b = 0; b < NB; ++b) {
             const int rr = b * 32 + lr;
             const uint4 bv = *reinterpret_cast<const uint4*>(&xb[rr * kKC + ((cl ^ (rr & 15)) * 8)]);
-            part[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bv), part[b], 0, 0, 0);
+            acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bv), acc[b], 0, 0, 0);
           }
         }
-        const float s0 = tr.sbase[tr.srow0 * tr.nchunks + c];
-        const float s1 = tr.sbase[tr.srow1 * tr.nchunks + c];
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) acc[b][v] = fmaf(v < 8 ? s0 : s1, part[b][v], acc[b][v]);
       } else {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
@@ -411,7 +428,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const TileRun& tr, c
     ffn_epilogue<KIND, NB>(acc, tl, NB, sh, out, p.n_out, wv, lr, lh);
   } else {
     // partial sums of a split tile, in accumulator-register order
-    float* dst = sk_slot(parts, blockIdx.x, first_tile ? 0 : 1);
+    float* dst = sk_slot(parts, rng, first_tile ? 0 : 1);
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -433,7 +450,12 @@ __global__ __launch_bounds__(kGemmThreads, 2) void ffn_mfma_kernel(GemmArgs p, f
   const int n_tiles = build_schedule(p, BMT, sh);
   const int nchunks = p.K / kKC;
   const int64_t total = int64_t(n_tiles) * nchunks;
-  const int64_t i0 = sk_start(blockIdx.x, total), i1 = sk_start(blockIdx.x + 1, total);
+  // XCD-aware range order: workgroups are dispatched round-robin over the 8
+  // XCDs, so range r goes to workgroup (r % 64) * 8 + r / 64; consecutive
+  // ranges (the N tiles of one expert, which share its activation rows) then
+  // run on one XCD and its L2 fetches those rows once.
+  const int rng = int(blockIdx.x % kXcds) * (kSkGrid / kXcds) + int(blockIdx.x / kXcds);
+  const int64_t i0 = sk_start(rng, total), i1 = sk_start(rng + 1, total);
   if (i0 >= i1) return;  // uniform
   const int t_first = int(i0 / nchunks), t_last = int((i1 - 1) / nchunks);
 
@@ -467,18 +489,24 @@ __global__ __launch_bounds__(kGemmThreads, 2) void ffn_mfma_kernel(GemmArgs p, f
       }
       tr.sbase = (tl.shared ? p.sh_s : p.s) + size_t(tl.we) * (p.n_w_rows / 128) * nchunks;
     }
-    const int nb = (tl.nrows + 31) / 32;  // active 32-row blocks (uniform; 3 runs as 4)
+    const int nb = (tl.nrows + 31) / 32;  // active 32-row blocks (uniform)
     const bool first = t == t_first;
-    if constexpr (FP8) {
-      switch (nb) {
-        case 1: run_tile<KIND, FP8, PACKED, 1, BMT>(p, tr, tl, sh, xs, parts, first); break;
-        case 2: run_tile<KIND, FP8, PACKED, 2, BMT>(p, tr, tl, sh, xs, parts, first); break;
-        default: run_tile<KIND, FP8, PACKED, 4, BMT>(p, tr, tl, sh, xs, parts, first); break;
+    auto run = [&](auto stream_tag) __attribute__((always_inline)) {
+      constexpr bool ST = decltype(stream_tag)::value;
+      if constexpr (FP8) {
+        switch (nb) {
+          case 1: run_tile<KIND, FP8, PACKED, 1, BMT, ST>(p, tr, tl, sh, xs, parts, rng, first); break;
+          case 2: run_tile<KIND, FP8, PACKED, 2, BMT, ST>(p, tr, tl, sh, xs, parts, rng, first); break;
+          case 3: run_tile<KIND, FP8, PACKED, 3, BMT, ST>(p, tr, tl, sh, xs, parts, rng, first); break;
+          default: run_tile<KIND, FP8, PACKED, 4, BMT, ST>(p, tr, tl, sh, xs, parts, rng, first); break;
+        }
+      } else {
+        if (nb == 1) run_tile<KIND, FP8, PACKED, 1, BMT, ST>(p, tr, tl, sh, xs, parts, rng, first);
+        else run_tile<KIND, FP8, PACKED, 2, BMT, ST>(p, tr, tl, sh, xs, parts, rng, first);
       }
-    } else {
-      if (nb == 1) run_tile<KIND, FP8, PACKED, 1, BMT>(p, tr, tl, sh, xs, parts, first);
-      else run_tile<KIND, FP8, PACKED, 2, BMT>(p, tr, tl, sh, xs, parts, first);
-    }
+    };
+    if (tl.mtiles == 1) run(std::true_type{});
+    else run(std::false_type{});
     __syncthreads();  // rowmap and staging buffers are rewritten by the next tile
   }
 }
