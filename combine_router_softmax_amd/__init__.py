@@ -24,6 +24,7 @@ __all__ = [
 COMPACT, PADDED = 0, 1
 W_ROWMAJOR, W_PACKED = 0, 1
 GG_FULL, GG_UP, GG_DOWN = 0, 1, 2
+GEMM_AUTO, GEMM_WIDE, GEMM_STREAM_K = 0, 1, 2
 STATUS_OVERFLOW = 1
 _F32, _BF16, _FP8 = 0, 1, 2
 
@@ -55,7 +56,8 @@ class GGemmDesc(ctypes.Structure):
     _fields_ = [("n_groups", ctypes.c_int), ("hidden", ctypes.c_int), ("inter", ctypes.c_int),
                 ("act_dt", ctypes.c_int), ("w_dt", ctypes.c_int), ("layout", ctypes.c_int),
                 ("n_src", ctypes.c_int), ("capacity", ctypes.c_int), ("rows", ctypes.c_int64),
-                ("stage", ctypes.c_int), ("shared", ctypes.POINTER(SharedExpert)), ("w_format", ctypes.c_int)]
+                ("stage", ctypes.c_int), ("shared", ctypes.POINTER(SharedExpert)), ("w_format", ctypes.c_int),
+                ("policy", ctypes.c_int)]
 
 
 _P = ctypes.c_void_p
@@ -216,10 +218,11 @@ _W_CODE = {torch.float32: _F32, torch.bfloat16: _BF16, torch.uint8: _FP8, torch.
 
 
 def gemm_desc(n_groups, hidden, inter, act_dtype, w_dtype, layout, n_src, capacity, rows, stage=GG_FULL,
-              shared: "SharedExpert | None" = None, w_format: int = W_ROWMAJOR):
+              shared: "SharedExpert | None" = None, w_format: int = W_ROWMAJOR, policy: int = 0):
     w_code = _W_CODE[w_dtype]
     d = GGemmDesc(n_groups, hidden, inter, _act_code(act_dtype), w_code, layout, n_src, capacity, rows, stage)
     d.w_format = w_format
+    d.policy = policy
     if shared is not None:
         d.shared = ctypes.pointer(shared)
     return d
@@ -246,7 +249,7 @@ def moe_grouped_gemm(a: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, *, gr
                      s13=None, s2=None, layout: int = COMPACT, n_src: int = 1, capacity: int = 0,
                      stage: int = GG_FULL, y: Optional[torch.Tensor] = None,
                      ws: Optional[torch.Tensor] = None, shared: Optional[dict] = None,
-                     w_format: int = W_ROWMAJOR) -> torch.Tensor:
+                     w_format: int = W_ROWMAJOR, policy: int = 0) -> torch.Tensor:
     """SwiGLU FFN per expert over the rows each expert holds (see moe.h).
 
     ``shared`` = dict(a, w13, w2, y[, s13, s2]) runs the shared expert in the same launches."""
@@ -262,7 +265,7 @@ def moe_grouped_gemm(a: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, *, gr
     if shared is not None:
         se = shared_expert(shared["a"], shared["w13"], shared["w2"], shared.get("y"), shared.get("s13"),
                            shared.get("s2"))
-    desc = gemm_desc(G, H, I, a.dtype, w13.dtype, layout, n_src, capacity, R, stage, se, w_format)
+    desc = gemm_desc(G, H, I, a.dtype, w13.dtype, layout, n_src, capacity, R, stage, se, w_format, policy)
     wsb = moe_grouped_gemm_workspace(desc)
     if wsb == 0:
         raise MoeError("moe_grouped_gemm: invalid descriptor")

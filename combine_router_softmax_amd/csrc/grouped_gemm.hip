@@ -46,6 +46,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kGemmThreads = 256;
 constexpr int kBM = 128;            // rows per tile
@@ -55,6 +56,15 @@ constexpr int kMaxGroups = 512;
 constexpr int kGemmMaxSrc = 512;
 
 enum { kUp = 0, kDown = 1 };
+
+// wide-tile kernel (groups with many rows)
+constexpr int kWN = 256;             // weight rows per wide tile
+constexpr int kWM = 256;             // activation rows per wide tile
+constexpr int kWK = 64;              // reduction depth per LDS stage
+constexpr int kWideGrid = 256;       // one workgroup per compute unit
+constexpr int kWideMinRows = 128;    // a group with at least this many rows may take the wide kernel ...
+constexpr int kWideMinTiles = 128;   // ... if the launch then has at least this many wide tiles
+constexpr int kNoWide = 0x7fffffff;  // wide_min when the wide kernel is not used
 
 struct GemmArgs {
   // routed experts
@@ -75,25 +85,32 @@ struct GemmArgs {
   int n_w_rows;               // 2I (up) or H (down)
   int K;                      // reduction length
   int n_out;                  // I (up) or H (down)
-  int n_tiles_n;              // N tiles per expert
+  int n_tiles_n;              // N tiles per expert (decode-shaped kernels)
   int packed;                 // weights in the packed (load-order) layout
+  int wide_min;               // groups with at least this many rows may go to the wide-tile kernel ...
+  int wide_min_tiles;         // ... if the wide groups make at least this many wide tiles
 };
 
 struct Sched {
   int tile_start[kMaxGroups + 2];
   int m[kMaxGroups + 1];
   int seg[kGemmMaxSrc + 1];
-  int rowmap[kBM];
+  int rowmap[256];
   int tmp[kGemmThreads];
   int cur_seg_group;
+  int wide_tiles;
 };
 
 // Rows per group from the device counts (clamped so every row stays inside
 // [0, rows)), then the exclusive prefix of tiles per group. Schedule order:
 // the shared expert first (its rows are always present, so its tiles start
 // with the first wave of workgroups instead of forming a tail), then the
-// routed experts. Returns the tile count. All threads must call it.
-__device__ int build_schedule(const GemmArgs& p, int bm, Sched& sh) {
+// routed experts. Only groups on the kernel's side get tiles: a group is wide
+// if m >= wide_min and the wide groups together make at least wide_min_tiles
+// wide tiles (fewer would leave most compute units idle; the stream-K kernel
+// then takes them). Both kernels evaluate this identically from the same
+// counts. Returns the tile count. All threads must call it.
+__device__ int build_schedule(const GemmArgs& p, int bm, int ntn, bool wide, Sched& sh) {
   const int tid = threadIdx.x;
   const int nsh = p.sh_rows > 0 ? 1 : 0;
   const int Gt = p.G + nsh;
@@ -111,9 +128,23 @@ __device__ int build_schedule(const GemmArgs& p, int bm, Sched& sh) {
       if (c) atomicAdd(&sh.m[nsh + i / p.S], c);
     }
   }
-  if (tid == 0 && nsh) sh.m[0] = p.sh_rows;
+  if (tid == 0) {
+    if (nsh) sh.m[0] = p.sh_rows;
+    sh.wide_tiles = 0;
+  }
   __syncthreads();
-  for (int g = tid; g < Gt; g += kGemmThreads) sh.tile_start[g] = (sh.m[g] + bm - 1) / bm * p.n_tiles_n;
+  if (p.wide_min != kNoWide) {
+    int wt = 0;
+    for (int g = tid; g < Gt; g += kGemmThreads)
+      if (sh.m[g] >= p.wide_min) wt += (sh.m[g] + kWM - 1) / kWM * (p.n_w_rows / kWN);
+    if (wt) atomicAdd(&sh.wide_tiles, wt);
+    __syncthreads();
+  }
+  const int wide_min = sh.wide_tiles >= p.wide_min_tiles ? p.wide_min : kNoWide;
+  for (int g = tid; g < Gt; g += kGemmThreads) {
+    const int m = sh.m[g];
+    sh.tile_start[g] = ((m >= wide_min) == wide) ? (m + bm - 1) / bm * ntn : 0;
+  }
   __syncthreads();
   const int total = block_scan_lds<false, kGemmThreads>(sh.tile_start, Gt, sh.tmp);
   if (tid == 0) {
@@ -132,7 +163,14 @@ struct Tile {
   int mtiles;   // row tiles of the tile's group (1: its weights are read once)
 };
 
-__device__ Tile decode_tile(const GemmArgs& p, int bm, const Sched& sh, int t) {
+// Tile order inside a group. Default: row tiles fastest (consecutive tiles
+// share a weight block). BLOCKED: the N tiles are cut into blocks of nbw (4
+// when they divide evenly), and inside a block the order is (row tile, N
+// tile); so any 32 consecutive tiles cover a compact rectangle of row tiles x
+// N tiles (8 x 4 when the group has 8 row tiles), i.e. 12 distinct operand
+// slabs instead of 2 + 16 (N fastest) or 32 + 1 (rows fastest).
+template <bool BLOCKED = false>
+__device__ Tile decode_tile(const GemmArgs& p, int bm, int ntn, const Sched& sh, int t) {
   const int nsh = p.sh_rows > 0 ? 1 : 0;
   const int Gt = p.G + nsh;
   int lo = 0, hi = Gt;  // last q with tile_start[q] <= t
@@ -148,8 +186,15 @@ __device__ Tile decode_tile(const GemmArgs& p, int bm, const Sched& sh, int t) {
   const int local = t - sh.tile_start[lo];
   const int mtiles = (sh.m[lo] + bm - 1) / bm;
   tl.mtiles = mtiles;
-  tl.nt = local / mtiles;
-  tl.r0 = (local % mtiles) * bm;
+  if (BLOCKED) {
+    const int nbw = ntn % 4 == 0 ? 4 : (ntn % 2 == 0 ? 2 : 1);
+    const int blk = local / (nbw * mtiles), rem = local % (nbw * mtiles);
+    tl.nt = blk * nbw + rem % nbw;
+    tl.r0 = (rem / nbw) * bm;
+  } else {
+    tl.nt = local / mtiles;
+    tl.r0 = (local % mtiles) * bm;
+  }
   tl.nrows = min(bm, sh.m[lo] - tl.r0);
   return tl;
 }
@@ -447,7 +492,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void ffn_mfma_kernel(GemmArgs p, f
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
   const int lr = lane & 31;
-  const int n_tiles = build_schedule(p, BMT, sh);
+  const int n_tiles = build_schedule(p, BMT, p.n_tiles_n, false, sh);
   const int nchunks = p.K / kKC;
   const int64_t total = int64_t(n_tiles) * nchunks;
   // XCD-aware range order: workgroups are dispatched round-robin over the 8
@@ -460,7 +505,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void ffn_mfma_kernel(GemmArgs p, f
   const int t_first = int(i0 / nchunks), t_last = int((i1 - 1) / nchunks);
 
   for (int t = t_first; t <= t_last; ++t) {
-    const Tile tl = decode_tile(p, BMT, sh, t);
+    const Tile tl = decode_tile(p, BMT, p.n_tiles_n, sh, t);
     build_rowmap(p, tl, BMT, sh);
     TileRun tr;
     tr.c_begin = int(max<int64_t>(i0, int64_t(t) * nchunks) - int64_t(t) * nchunks);
@@ -522,7 +567,7 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_fixup_kernel(GemmArgs p, con
   const int wv = tid / kWave;
   const int lr = lane & 31;
   const int lh = lane >> 5;
-  const int n_tiles = build_schedule(p, BMT, sh);
+  const int n_tiles = build_schedule(p, BMT, p.n_tiles_n, false, sh);
   const int nchunks = p.K / kKC;
   const int64_t total = int64_t(n_tiles) * nchunks;
   const int j = blockIdx.x;
@@ -530,7 +575,7 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_fixup_kernel(GemmArgs p, con
   if (ib <= 0 || ib >= total || ib % nchunks == 0) return;  // not inside a tile
   const int t = int(ib / nchunks);
   if (j > 0 && sk_start(j, total) > int64_t(t) * nchunks) return;  // an earlier boundary owns this tile
-  const Tile tl = decode_tile(p, BMT, sh, t);
+  const Tile tl = decode_tile(p, BMT, p.n_tiles_n, sh, t);
   build_rowmap(p, tl, BMT, sh);
   const int nb = (tl.nrows + 31) / 32;
   const int b_lo = sk_owner(int64_t(t) * nchunks, total);
@@ -553,6 +598,238 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_fixup_kernel(GemmArgs p, con
   }
   uint16_t* out = static_cast<uint16_t*>(tl.shared ? p.sh_out : p.out);
   ffn_epilogue<KIND, kMB>(acc, tl, nb, sh, out, p.n_out, wv, lr, lh);
+}
+
+// ------------------------------------------------------------------ wide-tile kernel
+// Groups with many rows (prefill, and decode with few experts per GPU) are
+// compute-heavy: a weight block is used by hundreds of rows, so it pays to
+// stage it once in LDS and reuse every operand fragment several times from
+// registers. Tile = 256 weight rows x 256 activation rows; each of the 4 waves
+// owns 64 weight rows (up: 32 gate rows and the 32 matching up rows, so the
+// SwiGLU pairs meet in one lane) against all 256 activation rows, i.e. a
+// 64 x 256 accumulator block (2 x 8 MFMA 32x32 tiles, 256 accumulator
+// registers; one wave per SIMD). Per 16-deep step a wave reads 2 weight and
+// up to 8 activation fragments from LDS for up to 16 MFMAs.
+//
+// Pipeline: both operands go global -> registers -> LDS in 64-deep stages,
+// double-buffered; the loads of stage k+1 are issued before the MFMAs of stage
+// k and written to the other buffer after three of its four 16-deep steps. The
+// one barrier per stage sits before the fourth step, whose fragments are
+// already in registers, so the fragment reads of stage k+1 overlap its MFMAs.
+// LDS: 64 banks of 4 bytes, a 128-bit access is served 16 lanes at a time.
+// Rows are 128 bytes (64 bf16) and slot s of row r holds 16-byte column
+// s ^ ((r / 2) % 8): the 16 rows read together by a fragment load (and the two
+// rows written together by 16 lanes) fall on 16 distinct 16-byte bank groups.
+// Activation blocks past the tile's rows are neither loaded nor multiplied (NB).
+// Tiles are ordered (group, row tile, N tile) with N fastest and handed out so
+// that the 32 workgroups of one XCD take consecutive tiles: they share the
+// activation rows and a few weight blocks in that XCD's L2.
+
+template <int KIND, bool PACKED, int NB>
+__device__ __forceinline__ void wide_tile(const GemmArgs& p, const Tile& tl, const Sched& sh,
+                                          uint16_t (&wl)[2][kWN * kWK], uint16_t (&xl)[2][kWM * kWK]) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
+  const int lr = lane & 31;
+  const int lh = lane >> 5;
+  const int nk = p.K / kWK;
+  const int last = nk - 1;
+  const uint16_t* A = static_cast<const uint16_t*>(tl.shared ? p.sh_a : p.a);
+  const uint16_t* W = static_cast<const uint16_t*>(tl.shared ? p.sh_w : p.w);
+
+  // activation staging: thread -> rows sr + 32 i (i < NB), 16-byte column ss
+  const int sr = tid >> 3, ss = tid & 7;
+  const uint16_t* xp[NB];
+  const int phys0 = sh.rowmap[0];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int phys = sh.rowmap[sr + 32 * i];
+    xp[i] = A + size_t(phys >= 0 ? phys : phys0) * p.K + ss * 8;
+  }
+  const int xdst = sr * kWK + ((ss ^ ((sr >> 1) & 7)) * 8);  // + 32 i rows (same swizzle)
+
+  // weight staging. Row-major: thread -> tile rows sr + 32 i, column ss; tile
+  // block i is wave i/2's A block i%2 (up: gate rows, then the matching up rows).
+  // Packed: load i is one 4 KiB run of the packed layout (one decode-kernel
+  // wave's 32 rows x 64 deep), piece tid of it.
+  const uint16_t* wp[8];
+  int wdst[8];
+  if constexpr (!PACKED) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      int row;
+      if (KIND == kUp) row = ((i & 1) ? p.n_out : 0) + tl.nt * 128 + 32 * (i >> 1) + sr;
+      else row = tl.nt * 256 + 32 * i + sr;
+      wp[i] = W + (size_t(tl.we) * p.n_w_rows + row) * p.K + ss * 8;
+      wdst[i] = (32 * i + sr) * kWK + ((ss ^ ((sr >> 1) & 7)) * 8);
+    }
+  } else {
+    const int ip = tid >> 6, pl = tid & 63, r = pl & 31, plh = pl >> 5;
+    const int nchunks = p.K / kKC;
+    const int ntp_total = p.n_tiles_n;  // packed N tiles per expert (64 h columns / 128 rows)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int pn = i >> 2, pw = i & 3;
+      int R;
+      if (KIND == kUp) {
+        const int jj = 64 * pn + 16 * pw + (r & 15);
+        R = 64 * (jj >> 5) + 32 * (r >> 4) + (jj & 31);
+      } else {
+        R = 128 * pn + 32 * pw + r;
+      }
+      wdst[i] = R * kWK + (((4 * plh + ip) ^ ((R >> 1) & 7)) * 8);
+      const size_t run = ((size_t(tl.we) * ntp_total + (2 * tl.nt + pn)) * nchunks) * 4 + pw;
+      wp[i] = W + (run * 8 * kWave + size_t(ip) * kWave + pl) * 8;  // chunk 0, first half
+    }
+  }
+
+  // per-stage pointer advance (elements): row-major moves 64 along the row;
+  // packed alternates between the two halves of a 128-deep chunk
+  auto advance = [&](int kt) -> size_t {
+    if constexpr (PACKED) return (kt & 1) ? size_t(4 * 8 - 4) * kWave * 8 : size_t(4) * kWave * 8;
+    else return kWK;
+  };
+  // (native vector types: arrays of uint4 would not be split into registers)
+  u32x4_t xr[NB], wr[8];
+#define MOE_WIDE_LOAD()                                                                                     \
+  {                                                                                                         \
+    _Pragma("unroll") for (int i = 0; i < NB; ++i) xr[i] = *reinterpret_cast<const u32x4_t*>(xp[i]);        \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) wr[i] = *reinterpret_cast<const u32x4_t*>(wp[i]);         \
+  }
+#define MOE_WIDE_ADVANCE(XN_, WN_)                                                                          \
+  {                                                                                                         \
+    _Pragma("unroll") for (int i = 0; i < NB; ++i) xp[i] += (XN_);                                          \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) wp[i] += (WN_);                                           \
+  }
+#define MOE_WIDE_STORE(BUF_)                                                                                \
+  {                                                                                                         \
+    _Pragma("unroll") for (int i = 0; i < NB; ++i) *reinterpret_cast<u32x4_t*>(&xl[BUF_][xdst + 32 * i * kWK]) = xr[i]; \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4_t*>(&wl[BUF_][wdst[i]]) = wr[i];  \
+  }
+
+  f32x16_t acc[2][NB];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
+
+  MOE_WIDE_LOAD()
+  MOE_WIDE_STORE(0)
+  if (last > 0) MOE_WIDE_ADVANCE(size_t(kWK), advance(0))
+  __syncthreads();
+  const int fsw = (lr >> 1) & 7;
+  const int arow0 = (64 * wv + lr) * kWK, arow1 = (64 * wv + 32 + lr) * kWK;
+  // weight fragments of step s+1 are read at the start of step s; activation
+  // fragment b of step s+1 right after its last use in step s
+  bf16x8_t fa[2][2], fb[NB];
+#define MOE_WIDE_FA(SET_, BUFP_, S_)                                                                        \
+  {                                                                                                         \
+    const int col_ = ((2 * (S_) + lh) ^ fsw) * 8;                                                           \
+    fa[SET_][0] = *reinterpret_cast<const bf16x8_t*>((BUFP_) + arow0 + col_);                               \
+    fa[SET_][1] = *reinterpret_cast<const bf16x8_t*>((BUFP_) + arow1 + col_);                               \
+  }
+#define MOE_WIDE_FB(B_, BUFP_, S_)                                                                          \
+  fb[B_] = *reinterpret_cast<const bf16x8_t*>((BUFP_) + (32 * (B_) + lr) * kWK + ((2 * (S_) + lh) ^ fsw) * 8);
+  MOE_WIDE_FA(0, wl[0], 0)
+#pragma unroll
+  for (int b = 0; b < NB; ++b) MOE_WIDE_FB(b, xl[0], 0)
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    // stage kt+1 (at the end a harmless repeat of the last stage)
+    MOE_WIDE_LOAD()
+    // keep the loads here, ahead of the MFMAs (the scheduler would otherwise
+    // sink them next to their LDS stores and expose their latency)
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 2 <= last) MOE_WIDE_ADVANCE(size_t(kWK), advance(kt + 1))
+    const uint16_t* wb = wl[buf];
+    const uint16_t* xb = xl[buf];
+#pragma unroll
+    for (int s = 0; s < kWK / 16 - 1; ++s) {
+      MOE_WIDE_FA((s + 1) & 1, wb, s + 1)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        acc[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][0], fb[b], acc[0][b], 0, 0, 0);
+        acc[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][1], fb[b], acc[1][b], 0, 0, 0);
+        MOE_WIDE_FB(b, xb, s + 1)
+        __builtin_amdgcn_sched_barrier(0);  // keep each refill one step ahead of its use
+      }
+    }
+    MOE_WIDE_STORE(buf ^ 1)
+    __syncthreads();  // stage kt+1 staged by every wave; nobody reads buffer buf any more
+    // last step of stage kt from registers; step 0 of stage kt+1 read meanwhile
+    const uint16_t* wn = wl[buf ^ 1];
+    const uint16_t* xn = xl[buf ^ 1];
+    MOE_WIDE_FA(0, wn, 0)
+    constexpr int sl = kWK / 16 - 1;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      acc[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[sl & 1][0], fb[b], acc[0][b], 0, 0, 0);
+      acc[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[sl & 1][1], fb[b], acc[1][b], 0, 0, 0);
+      MOE_WIDE_FB(b, xn, 0)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#undef MOE_WIDE_FA
+#undef MOE_WIDE_FB
+#undef MOE_WIDE_LOAD
+#undef MOE_WIDE_ADVANCE
+#undef MOE_WIDE_STORE
+
+  uint16_t* out = static_cast<uint16_t*>(tl.shared ? p.sh_out : p.out);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int phys = sh.rowmap[32 * b + lr];
+    if (phys < 0) continue;
+    uint16_t* orow = out + size_t(phys) * p.n_out;
+    if (KIND == kUp) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float h[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) h[r] = silu_f(acc[0][b][4 * q + r]) * acc[1][b][4 * q + r];
+        const int col = tl.nt * 128 + 32 * wv + 8 * q + 4 * lh;
+        *reinterpret_cast<uint2*>(orow + col) = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+      }
+    } else {
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = tl.nt * 256 + 64 * wv + 32 * a + 8 * q + 4 * lh;
+          *reinterpret_cast<uint2*>(orow + col) = make_uint2(pack_bf16x2(acc[a][b][4 * q], acc[a][b][4 * q + 1]),
+                                                             pack_bf16x2(acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]));
+        }
+    }
+  }
+}
+
+template <int KIND, bool PACKED>
+__global__ __launch_bounds__(kGemmThreads, 1) void ffn_wide_kernel(GemmArgs p) {
+  __shared__ Sched sh;
+  __shared__ __attribute__((aligned(16))) uint16_t wl[2][kWN * kWK];
+  __shared__ __attribute__((aligned(16))) uint16_t xl[2][kWM * kWK];
+  const int ntn = KIND == kUp ? p.n_out / 128 : p.n_out / 256;
+  const int n_tiles = build_schedule(p, kWM, ntn, true, sh);
+  const int per_xcd = int(gridDim.x) / kXcds;
+  const int first = int(blockIdx.x % kXcds) * per_xcd + int(blockIdx.x / kXcds);
+  for (int t = first; t < n_tiles; t += gridDim.x) {
+    const Tile tl = decode_tile<true>(p, kWM, ntn, sh, t);
+    build_rowmap(p, tl, kWM, sh);
+    switch ((tl.nrows + 31) / 32) {
+      case 1: wide_tile<KIND, PACKED, 1>(p, tl, sh, wl, xl); break;
+      case 2: wide_tile<KIND, PACKED, 2>(p, tl, sh, wl, xl); break;
+      case 3: wide_tile<KIND, PACKED, 3>(p, tl, sh, wl, xl); break;
+      case 4: wide_tile<KIND, PACKED, 4>(p, tl, sh, wl, xl); break;
+      case 5: wide_tile<KIND, PACKED, 5>(p, tl, sh, wl, xl); break;
+      case 6: wide_tile<KIND, PACKED, 6>(p, tl, sh, wl, xl); break;
+      case 7: wide_tile<KIND, PACKED, 7>(p, tl, sh, wl, xl); break;
+      default: wide_tile<KIND, PACKED, 8>(p, tl, sh, wl, xl); break;
+    }
+    __syncthreads();  // rowmap and stage buffers are rewritten by the next tile
+  }
 }
 
 // ------------------------------------------------------------------ weight packing
@@ -605,13 +882,13 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_f32_kernel(GemmArgs p) {
   __shared__ float xs[kFBM][kFKC + 1];
   __shared__ float ws[2 * kFBN][kFKC + 1];
   const int tid = threadIdx.x;
-  const int n_tiles = build_schedule(p, kFBM, sh);
+  const int n_tiles = build_schedule(p, kFBM, p.n_tiles_n, false, sh);
   const int nwr = KIND == kUp ? 2 * kFBN : kFBN;  // weight rows staged per tile
   const int row = tid / 8;                         // 0..31
   const int cg = (tid % 8) * 4;                    // 4 output columns
 
   for (int t = blockIdx.x; t < n_tiles; t += gridDim.x) {
-    const Tile tl = decode_tile(p, kFBM, sh, t);
+    const Tile tl = decode_tile(p, kFBM, p.n_tiles_n, sh, t);
     build_rowmap(p, tl, kFBM, sh);
     const float* A = static_cast<const float*>(tl.shared ? p.sh_a : p.a);
     const float* W = static_cast<const float*>(tl.shared ? p.sh_w : p.w);
@@ -668,6 +945,7 @@ static bool ggemm_desc_ok(const moe_ggemm_desc_t* d) {
   }
   if (d->shared && d->shared->rows < 0) return false;
   if (d->w_format != MOE_W_ROWMAJOR && d->w_format != MOE_W_PACKED) return false;
+  if (d->policy != MOE_GEMM_AUTO && d->policy != MOE_GEMM_WIDE && d->policy != MOE_GEMM_STREAM_K) return false;
   return true;
 }
 
@@ -722,6 +1000,14 @@ static moe_status_t launch_stage(const GemmArgs& p, bool f32, bool fp8, int kind
     if (kind == kUp) hipLaunchKernelGGL(ffn_f32_kernel<kUp>, grid, block, 0, stream, p);
     else hipLaunchKernelGGL(ffn_f32_kernel<kDown>, grid, block, 0, stream, p);
     return launch_status();
+  }
+  if (p.wide_min != kNoWide) {
+    const dim3 wgrid(kWideGrid);
+#define MOE_WIDE(K, P) hipLaunchKernelGGL((ffn_wide_kernel<K, P>), wgrid, block, 0, stream, p)
+    if (kind == kUp) { if (p.packed) MOE_WIDE(kUp, true); else MOE_WIDE(kUp, false); }
+    else { if (p.packed) MOE_WIDE(kDown, true); else MOE_WIDE(kDown, false); }
+#undef MOE_WIDE
+    if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
   }
   const dim3 grid(kSkGrid), fix_grid(kSkGrid - 1);
 #define MOE_FFN(K, F, P) hipLaunchKernelGGL((ffn_mfma_kernel<K, F, P>), grid, block, 0, stream, p, parts)
@@ -783,6 +1069,12 @@ MOE_API moe_status_t moe_grouped_gemm(const moe_ggemm_desc_t* d, const void* a, 
   p.layout = d->layout;
   p.sh_rows = se ? se->rows : 0;
   p.packed = d->w_format == MOE_W_PACKED;
+  // the wide-tile kernel: bf16 weights, 256-row output blocks of W2 and 128-column blocks of h
+  const bool wide_ok = !f32 && !fp8 && d->hidden % 256 == 0 && d->inter % 128 == 0 &&
+                       d->policy != MOE_GEMM_STREAM_K;
+  const bool force = d->policy == MOE_GEMM_WIDE;
+  p.wide_min = wide_ok ? (force ? 1 : kWideMinRows) : kNoWide;
+  p.wide_min_tiles = force ? 0 : kWideMinTiles;
   moe_status_t st = MOE_OK;
   if (up) {
     p.a = a;

@@ -166,6 +166,18 @@ typedef enum {
   MOE_W_PACKED = 1    /* the same bytes permuted by moe_pack_weights (bf16 and fp8 only) */
 } moe_weight_format_t;
 
+/* Which kernel takes which expert group. Both compute the same products in
+ * fp32 (the sum order differs, so results may differ in the last bits).
+ * AUTO: groups of at least 128 rows take the 256 x 256 wide-tile kernel when
+ * the launch then has at least 128 wide tiles (bf16 weights, hidden % 256 == 0),
+ * all others the stream-K kernel. WIDE: every group takes the wide-tile kernel
+ * where its shape and dtype allow. STREAM_K: never the wide-tile kernel. */
+typedef enum {
+  MOE_GEMM_AUTO = 0,
+  MOE_GEMM_WIDE = 1,
+  MOE_GEMM_STREAM_K = 2
+} moe_gemm_policy_t;
+
 typedef enum {
   MOE_GG_FULL = 0, /* both products */
   MOE_GG_UP = 1,   /* h = silu(a W_gate^T) * (a W_up^T) into the workspace only */
@@ -200,6 +212,7 @@ typedef struct {
   moe_gg_stage_t stage;
   const moe_shared_expert_t* shared; /* host pointer, or NULL for none */
   moe_weight_format_t w_format;      /* layout of w13/w2 (and of the shared expert's) */
+  moe_gemm_policy_t policy;          /* kernel choice per group; MOE_GEMM_AUTO unless tuning or testing */
 } moe_ggemm_desc_t;
 
 /* Bytes of scratch moe_grouped_gemm needs (the intermediates h [R, I] and, with

@@ -160,6 +160,9 @@ def test_pack_weights_and_format_validation(lib):
     bad = _gd()
     bad.w_format = 7
     assert lib.moe_grouped_gemm_workspace(ctypes.byref(bad)) == 0
+    badp = _gd()
+    badp.policy = 3
+    assert lib.moe_grouped_gemm_workspace(ctypes.byref(badp)) == 0
     f32p = _gd(act_dt=0, w_dt=0)
     f32p.w_format = 1
     ws = lib.moe_grouped_gemm_workspace(ctypes.byref(f32p))

@@ -45,7 +45,7 @@ def _dev_weights(wd):
 
 
 # --------------------------------------------------------------------------- grouped GEMM
-def _gemm_case(cfg, m_per_group, layout, seed=0, S=3, C=None):
+def _gemm_case(cfg, m_per_group, layout, seed=0, S=3, C=None, policy=moe.GEMM_AUTO):
     """Random rows grouped as given; returns GPU y and oracle y on occupied rows."""
     rng = np.random.default_rng(seed)
     G = len(m_per_group)
@@ -69,7 +69,7 @@ def _gemm_case(cfg, m_per_group, layout, seed=0, S=3, C=None):
     act = torch.float32 if cfg.act == "f32" else torch.bfloat16
     a = torch.from_numpy(rng.standard_normal((R, H)).astype(np.float32)).to(act)
     y = torch.full((R, H), 3.0, dtype=act, device="cuda")
-    kw = dict(layout=layout, y=y)
+    kw = dict(layout=layout, y=y, policy=policy)
     if layout == COMPACT:
         kw["group_off"] = torch.from_numpy(lay["expert_off"].astype(np.int32)).cuda()
     else:
@@ -100,6 +100,31 @@ def test_gemm_bf16_ragged(layout, ms):
     got, ref, _ = _gemm_case(cfg, ms, layout, seed=len(ms))
     if len(ref):
         assert rel_l2(got, ref) <= TOL["bf16"]
+
+
+# The 256 x 256 wide-tile kernel (bf16 weights, hidden % 256 == 0): forced for
+# every group, and in AUTO mode beside the stream-K kernel. Sizes span ragged
+# wide tiles (1..8 active 32-row blocks), several row tiles per group, and
+# groups below the AUTO row threshold.
+@pytest.mark.parametrize("layout", [COMPACT, PADDED])
+@pytest.mark.parametrize("ms", [[127, 128, 255, 256, 257, 0, 31, 700], [1000], [129, 2, 160, 224, 96, 520]])
+def test_gemm_wide_tiles(layout, ms):
+    cfg = get_config("dsv3_prefill_ep8", hidden=1024, inter=512)
+    got, ref, (a, dw, kw) = _gemm_case(cfg, ms, layout, seed=sum(ms) % 97, policy=moe.GEMM_WIDE)
+    # bf16 operands are exact, sums are fp32; h and y are each rounded once to
+    # bf16 (relative error <= 2^-9 each), far inside the bf16 bound
+    assert rel_l2(got, ref) <= 8e-3
+    # packed weights give the same bits as row-major ones
+    y_wide = kw["y"].clone()
+    p13, p2 = moe.moe_pack_weights(dw["w13"], dw["w2"], 1024, 512)
+    kw["y"].fill_(3.0)
+    moe.moe_grouped_gemm(a.cuda(), p13, p2, w_format=moe.W_PACKED, **kw)
+    assert torch.equal(kw["y"].view(torch.int16), y_wide.view(torch.int16))
+    # the stream-K kernel computes the same products (fp32 sums in another order)
+    kw["y"].fill_(3.0)
+    kw["policy"] = moe.GEMM_STREAM_K
+    moe.moe_grouped_gemm(a.cuda(), dw["w13"], dw["w2"], **kw)
+    assert rel_l2(f64(kw["y"]), f64(y_wide)) <= 4e-3
 
 
 @pytest.mark.parametrize("layout", [COMPACT, PADDED])
