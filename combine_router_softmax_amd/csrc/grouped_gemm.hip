@@ -60,7 +60,7 @@ enum { kUp = 0, kDown = 1 };
 // wide-tile kernel (groups with many rows)
 constexpr int kWN = 256;             // weight rows per wide tile
 constexpr int kWM = 256;             // activation rows per wide tile
-constexpr int kWK = 64;              // reduction depth per LDS stage
+constexpr int kWK = 32;              // reduction depth per LDS stage (32 or 64)
 constexpr int kWideGrid = 256;       // one workgroup per compute unit
 constexpr int kWideMinRows = 128;    // a group with at least this many rows may take the wide kernel ...
 constexpr int kWideMinTiles = 128;   // ... if the launch then has at least this many wide tiles
@@ -611,23 +611,48 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_fixup_kernel(GemmArgs p, con
 // registers; one wave per SIMD). Per 16-deep step a wave reads 2 weight and
 // up to 8 activation fragments from LDS for up to 16 MFMAs.
 //
-// Pipeline: both operands go global -> registers -> LDS in 64-deep stages,
-// double-buffered; the loads of stage k+1 are issued before the MFMAs of stage
-// k and written to the other buffer after three of its four 16-deep steps. The
-// one barrier per stage sits before the fourth step, whose fragments are
-// already in registers, so the fragment reads of stage k+1 overlap its MFMAs.
+// Data path: global -> LDS directly (global_load_lds, 16 bytes per lane; lane
+// l of a load writes bytes [16 l, 16 l + 16) of the 1 KiB the wave's load
+// covers), in kWK-deep stages through a ring of kWStages LDS buffers (128 KiB
+// in all), so all but one stage are in flight while one is multiplied, and no
+// registers hold data in transit. Each wave waits for its own loads of a stage
+// (vmcnt) before the barrier that publishes it; the barrier sits before the
+// last 16-deep step of each stage, whose fragments are already in registers,
+// so the fragment reads of the next stage overlap its MFMAs.
 // LDS: 64 banks of 4 bytes, a 128-bit access is served 16 lanes at a time.
-// Rows are 128 bytes (64 bf16) and slot s of row r holds 16-byte column
-// s ^ ((r / 2) % 8): the 16 rows read together by a fragment load (and the two
-// rows written together by 16 lanes) fall on 16 distinct 16-byte bank groups.
-// Activation blocks past the tile's rows are neither loaded nor multiplied (NB).
-// Tiles are ordered (group, row tile, N tile) with N fastest and handed out so
-// that the 32 workgroups of one XCD take consecutive tiles: they share the
-// activation rows and a few weight blocks in that XCD's L2.
+// A row holds one stage of one operand row (kWK bf16, kWSlots 16-byte slots)
+// and slot s of row r holds column s ^ ((r / (16 / kWSlots)) % kWSlots): the 16
+// rows a fragment load reads together fall on 16 distinct 16-byte bank
+// groups. The swizzle is applied on the global side (each lane fetches the
+// column its LDS slot holds).
+// Activation blocks past the tile's rows are not multiplied (NB), and their
+// loads are limited to what keeps every wave's load count equal.
+// Tiles are ordered (group, blocked row/N tiles) and handed out so that the 32
+// workgroups of one XCD take consecutive tiles, which share operand slabs in
+// that XCD's L2.
+constexpr int kWStages = 128 / kWK;     // LDS ring depth (the ring holds 128 KiB)
+constexpr int kWSlots = kWK / 8;        // 16-byte slots per LDS row
+constexpr int kWRowsPerLoad = 64 / kWSlots;  // rows one 1 KiB wave load covers
+constexpr int kWStage = kWN * kWK;      // elements of one operand per stage
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// s_waitcnt immediate: wait until at most n vector-memory ops are outstanding
+// and no LDS op is (gfx9 encoding: vmcnt[3:0], expcnt[6:4] (7 = no wait),
+// lgkmcnt[11:8], vmcnt[5:4] in bits [15:14]).
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 14); }
+
+// The ring buffers are separate LDS objects, and the stage loop is unrolled by
+// the ring depth so every load and fragment read names its buffer statically:
+// the compiler can then see that a read does not touch the buffers still being
+// filled and does not wait for those loads.
+struct WideLds {
+  uint16_t* w[4];
+  uint16_t* x[4];
+};
 
 template <int KIND, bool PACKED, int NB>
-__device__ __forceinline__ void wide_tile(const GemmArgs& p, const Tile& tl, const Sched& sh,
-                                          uint16_t (&wl)[2][kWN * kWK], uint16_t (&xl)[2][kWM * kWK]) {
+__device__ __forceinline__ void wide_tile(const GemmArgs& p, const Tile& tl, const Sched& sh, const WideLds& L) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
@@ -638,74 +663,73 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& p, const Tile& tl, con
   const uint16_t* A = static_cast<const uint16_t*>(tl.shared ? p.sh_a : p.a);
   const uint16_t* W = static_cast<const uint16_t*>(tl.shared ? p.sh_w : p.w);
 
-  // activation staging: thread -> rows sr + 32 i (i < NB), 16-byte column ss
-  const int sr = tid >> 3, ss = tid & 7;
-  const uint16_t* xp[NB];
+  // Load q of wave wv covers tile rows kWRowsPerLoad (4 q + wv) + lane /
+  // kWSlots, LDS slot lane % kWSlots, i.e. global column
+  // cg = (lane % kWSlots) ^ swizzle(row). WL loads per wave per stage for the
+  // weights; XL for the activations, enough for NB blocks (rows past the
+  // tile's rows re-read row 0 of the tile into rows nobody multiplies).
+  constexpr int WL = kWN / kWRowsPerLoad / 4;
+  constexpr int XL = (NB * 32 / kWRowsPerLoad + 3) / 4;
+  constexpr int P = WL + XL;  // loads per wave per stage
+  const int lrow = lane / kWSlots;
+  auto col_of = [&](int row) { return (lane % kWSlots) ^ ((row / (16 / kWSlots)) % kWSlots); };
+  const uint16_t* xg[XL];
   const int phys0 = sh.rowmap[0];
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const int phys = sh.rowmap[sr + 32 * i];
-    xp[i] = A + size_t(phys >= 0 ? phys : phys0) * p.K + ss * 8;
+  for (int q = 0; q < XL; ++q) {
+    const int row = kWRowsPerLoad * (4 * q + wv) + lrow;
+    const int phys = row < NB * 32 ? sh.rowmap[row] : -1;
+    xg[q] = A + size_t(phys >= 0 ? phys : phys0) * p.K + col_of(row) * 8;
   }
-  const int xdst = sr * kWK + ((ss ^ ((sr >> 1) & 7)) * 8);  // + 32 i rows (same swizzle)
-
-  // weight staging. Row-major: thread -> tile rows sr + 32 i, column ss; tile
-  // block i is wave i/2's A block i%2 (up: gate rows, then the matching up rows).
-  // Packed: load i is one 4 KiB run of the packed layout (one decode-kernel
-  // wave's 32 rows x 64 deep), piece tid of it.
-  const uint16_t* wp[8];
-  int wdst[8];
-  if constexpr (!PACKED) {
+  const uint16_t* wg[WL];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+  for (int q = 0; q < WL; ++q) {
+    const int R = kWRowsPerLoad * (4 * q + wv) + lrow;  // tile weight row
+    const int cg = col_of(R);
+    if constexpr (!PACKED) {
       int row;
-      if (KIND == kUp) row = ((i & 1) ? p.n_out : 0) + tl.nt * 128 + 32 * (i >> 1) + sr;
-      else row = tl.nt * 256 + 32 * i + sr;
-      wp[i] = W + (size_t(tl.we) * p.n_w_rows + row) * p.K + ss * 8;
-      wdst[i] = (32 * i + sr) * kWK + ((ss ^ ((sr >> 1) & 7)) * 8);
-    }
-  } else {
-    const int ip = tid >> 6, pl = tid & 63, r = pl & 31, plh = pl >> 5;
-    const int nchunks = p.K / kKC;
-    const int ntp_total = p.n_tiles_n;  // packed N tiles per expert (64 h columns / 128 rows)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int pn = i >> 2, pw = i & 3;
-      int R;
+      if (KIND == kUp) row = ((R >> 5) & 1 ? p.n_out : 0) + tl.nt * 128 + 32 * (R >> 6) + (R & 31);
+      else row = tl.nt * 256 + R;
+      wg[q] = W + (size_t(tl.we) * p.n_w_rows + row) * p.K + cg * 8;
+    } else {
+      // the 16-byte piece of the packed layout [g][ntp][c][w][i][lane] that holds
+      // this row's columns [8 cg, 8 cg + 8) of stage 0 (k = 128 c + 64 (i / 4) +
+      // 32 (lane / 32) + 8 (i % 4))
+      int ntp, wdec, lrp;
       if (KIND == kUp) {
-        const int jj = 64 * pn + 16 * pw + (r & 15);
-        R = 64 * (jj >> 5) + 32 * (r >> 4) + (jj & 31);
+        const int j = tl.nt * 128 + 32 * (R >> 6) + (R & 31);  // h column
+        ntp = j >> 6;
+        wdec = (j & 63) >> 4;
+        lrp = ((R >> 5) & 1) * 16 + (j & 15);
       } else {
-        R = 128 * pn + 32 * pw + r;
+        const int row = tl.nt * 256 + R;
+        ntp = row >> 7;
+        wdec = (row & 127) >> 5;
+        lrp = row & 31;
       }
-      wdst[i] = R * kWK + (((4 * plh + ip) ^ ((R >> 1) & 7)) * 8);
-      const size_t run = ((size_t(tl.we) * ntp_total + (2 * tl.nt + pn)) * nchunks) * 4 + pw;
-      wp[i] = W + (run * 8 * kWave + size_t(ip) * kWave + pl) * 8;  // chunk 0, first half
+      const int nchunks = p.K / kKC;
+      const size_t piece = ((size_t(tl.we) * p.n_tiles_n + ntp) * nchunks * 4 + wdec) * 8 * kWave +
+                           (cg & 3) * kWave + ((cg >> 2) & 1) * 32 + lrp;
+      wg[q] = W + piece * 8;
     }
   }
-
-  // per-stage pointer advance (elements): row-major moves 64 along the row;
-  // packed alternates between the two halves of a 128-deep chunk
-  auto advance = [&](int kt) -> size_t {
-    if constexpr (PACKED) return (kt & 1) ? size_t(4 * 8 - 4) * kWave * 8 : size_t(4) * kWave * 8;
-    else return kWK;
+  // element offset of stage kt relative to stage 0 (packed: the stage's first
+  // column kb = kWK kt sets the chunk, the load's upper half and the lane half)
+  auto woff = [&](int kt) -> size_t {
+    if constexpr (PACKED) {
+      const int kb = kWK * kt;
+      return (size_t(kb >> 7) * 4 * 8 * kWave + size_t((kb >> 6) & 1) * 4 * kWave + size_t((kb >> 5) & 1) * 32) * 8;
+    } else {
+      return size_t(kt) * kWK;
+    }
   };
-  // (native vector types: arrays of uint4 would not be split into registers)
-  u32x4_t xr[NB], wr[8];
-#define MOE_WIDE_LOAD()                                                                                     \
+#define MOE_WIDE_ISSUE(KT_, SLOT_)                                                                          \
   {                                                                                                         \
-    _Pragma("unroll") for (int i = 0; i < NB; ++i) xr[i] = *reinterpret_cast<const u32x4_t*>(xp[i]);        \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i) wr[i] = *reinterpret_cast<const u32x4_t*>(wp[i]);         \
-  }
-#define MOE_WIDE_ADVANCE(XN_, WN_)                                                                          \
-  {                                                                                                         \
-    _Pragma("unroll") for (int i = 0; i < NB; ++i) xp[i] += (XN_);                                          \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i) wp[i] += (WN_);                                           \
-  }
-#define MOE_WIDE_STORE(BUF_)                                                                                \
-  {                                                                                                         \
-    _Pragma("unroll") for (int i = 0; i < NB; ++i) *reinterpret_cast<u32x4_t*>(&xl[BUF_][xdst + 32 * i * kWK]) = xr[i]; \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4_t*>(&wl[BUF_][wdst[i]]) = wr[i];  \
+    const size_t wo_ = woff(KT_), xo_ = size_t(KT_) * kWK;                                                  \
+    _Pragma("unroll") for (int q = 0; q < WL; ++q)                                                          \
+      __builtin_amdgcn_global_load_lds(wg[q] + wo_, (lds_ptr_t)(L.w[SLOT_] + (4 * q + wv) * 512), 16, 0, 0);  \
+    _Pragma("unroll") for (int q = 0; q < XL; ++q)                                                          \
+      __builtin_amdgcn_global_load_lds(xg[q] + xo_, (lds_ptr_t)(L.x[SLOT_] + (4 * q + wv) * 512), 16, 0, 0);  \
   }
 
   f32x16_t acc[2][NB];
@@ -716,67 +740,85 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& p, const Tile& tl, con
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
 
-  MOE_WIDE_LOAD()
-  MOE_WIDE_STORE(0)
-  if (last > 0) MOE_WIDE_ADVANCE(size_t(kWK), advance(0))
-  __syncthreads();
-  const int fsw = (lr >> 1) & 7;
+  const int fsw = (lr / (16 / kWSlots)) % kWSlots;
   const int arow0 = (64 * wv + lr) * kWK, arow1 = (64 * wv + 32 + lr) * kWK;
-  // weight fragments of step s+1 are read at the start of step s; activation
-  // fragment b of step s+1 right after its last use in step s
-  bf16x8_t fa[2][2], fb[NB];
-#define MOE_WIDE_FA(SET_, BUFP_, S_)                                                                        \
+  // two fragment sets: all ten reads of step s+1 are issued at the start of
+  // step s, so they have the whole step to land
+  bf16x8_t fa[2][2], fb[2][NB];
+#define MOE_WIDE_FRAGS(SET_, WBUF_, XBUF_, S_)                                                              \
   {                                                                                                         \
     const int col_ = ((2 * (S_) + lh) ^ fsw) * 8;                                                           \
-    fa[SET_][0] = *reinterpret_cast<const bf16x8_t*>((BUFP_) + arow0 + col_);                               \
-    fa[SET_][1] = *reinterpret_cast<const bf16x8_t*>((BUFP_) + arow1 + col_);                               \
+    fa[SET_][0] = *reinterpret_cast<const bf16x8_t*>((WBUF_) + arow0 + col_);                               \
+    fa[SET_][1] = *reinterpret_cast<const bf16x8_t*>((WBUF_) + arow1 + col_);                               \
+    _Pragma("unroll") for (int b = 0; b < NB; ++b)                                                          \
+        fb[SET_][b] = *reinterpret_cast<const bf16x8_t*>((XBUF_) + (32 * b + lr) * kWK + col_);             \
   }
-#define MOE_WIDE_FB(B_, BUFP_, S_)                                                                          \
-  fb[B_] = *reinterpret_cast<const bf16x8_t*>((BUFP_) + (32 * (B_) + lr) * kWK + ((2 * (S_) + lh) ^ fsw) * 8);
-  MOE_WIDE_FA(0, wl[0], 0)
+#define MOE_WIDE_MFMAS(SET_)                                                                                \
+  _Pragma("unroll") for (int b = 0; b < NB; ++b) {                                                          \
+    acc[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[SET_][0], fb[SET_][b], acc[0][b], 0, 0, 0);      \
+    acc[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[SET_][1], fb[SET_][b], acc[1][b], 0, 0, 0);      \
+  }
+
+  // prologue: stages 0 .. kWStages-2 in flight, wait for stage 0
+  constexpr int NS = kWK / 16;  // 16-deep MFMA steps per stage
 #pragma unroll
-  for (int b = 0; b < NB; ++b) MOE_WIDE_FB(b, xl[0], 0)
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    // stage kt+1 (at the end a harmless repeat of the last stage)
-    MOE_WIDE_LOAD()
-    // keep the loads here, ahead of the MFMAs (the scheduler would otherwise
-    // sink them next to their LDS stores and expose their latency)
-    __builtin_amdgcn_sched_barrier(0);
-    if (kt + 2 <= last) MOE_WIDE_ADVANCE(size_t(kWK), advance(kt + 1))
-    const uint16_t* wb = wl[buf];
-    const uint16_t* xb = xl[buf];
-#pragma unroll
-    for (int s = 0; s < kWK / 16 - 1; ++s) {
-      MOE_WIDE_FA((s + 1) & 1, wb, s + 1)
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        acc[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][0], fb[b], acc[0][b], 0, 0, 0);
-        acc[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][1], fb[b], acc[1][b], 0, 0, 0);
-        MOE_WIDE_FB(b, xb, s + 1)
-        __builtin_amdgcn_sched_barrier(0);  // keep each refill one step ahead of its use
-      }
-    }
-    MOE_WIDE_STORE(buf ^ 1)
-    __syncthreads();  // stage kt+1 staged by every wave; nobody reads buffer buf any more
-    // last step of stage kt from registers; step 0 of stage kt+1 read meanwhile
-    const uint16_t* wn = wl[buf ^ 1];
-    const uint16_t* xn = xl[buf ^ 1];
-    MOE_WIDE_FA(0, wn, 0)
-    constexpr int sl = kWK / 16 - 1;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      acc[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[sl & 1][0], fb[b], acc[0][b], 0, 0, 0);
-      acc[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[sl & 1][1], fb[b], acc[1][b], 0, 0, 0);
-      MOE_WIDE_FB(b, xn, 0)
-      __builtin_amdgcn_sched_barrier(0);
+  for (int st = 0; st < kWStages - 1; ++st) MOE_WIDE_ISSUE(min(st, last), st)
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((kWStages - 2) * P));
+  __builtin_amdgcn_s_barrier();
+  MOE_WIDE_FRAGS(0, L.w[0], L.x[0], 0)
+
+  // One stage (two 16-deep steps); J = stage % kWStages is a literal in each
+  // expansion. While LDS-DMA loads are outstanding the compiler waits for all
+  // LDS reads (lgkmcnt(0)) before using any fragment, so the reads are placed
+  // where that wait finds them done: the step-1 fragments are read in the
+  // middle of step 0's MFMAs, the next stage's step-0 fragments right after
+  // the barrier, ahead of step 1's MFMAs.
+#define MOE_WIDE_MFMA_RANGE(SET_, B0_, B1_)                                                                 \
+  _Pragma("unroll") for (int b = (B0_); b < (B1_); ++b) {                                                   \
+    acc[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[SET_][0], fb[SET_][b], acc[0][b], 0, 0, 0);      \
+    acc[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[SET_][1], fb[SET_][b], acc[1][b], 0, 0, 0);      \
+  }
+#define MOE_WIDE_STAGE(J_, KT_)                                                                             \
+  {                                                                                                         \
+    MOE_WIDE_MFMA_RANGE(0, 0, (NB + 1) / 2)                                                                 \
+    __builtin_amdgcn_sched_barrier(0);                                                                      \
+    MOE_WIDE_FRAGS(1, L.w[J_], L.x[J_], 1)                                                                  \
+    __builtin_amdgcn_sched_barrier(0);                                                                      \
+    MOE_WIDE_MFMA_RANGE(0, (NB + 1) / 2, NB)                                                                \
+    __builtin_amdgcn_sched_barrier(0);                                                                      \
+    /* the stage kWStages-1 ahead goes into the buffer the previous stage used  \
+       (everyone finished reading it before the previous barrier); past the    \
+       end a harmless repeat */                                                                             \
+    MOE_WIDE_ISSUE(min((KT_) + kWStages - 1, last), ((J_) + kWStages - 1) % kWStages)                       \
+    __builtin_amdgcn_sched_barrier(0);                                                                      \
+    /* this wave's loads of the next stage are done (later stages may still be \
+       in flight); the barrier makes every wave's part visible */                                          \
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((kWStages - 2) * P));                                       \
+    __builtin_amdgcn_s_barrier();                                                                           \
+    __builtin_amdgcn_sched_barrier(0);                                                                      \
+    MOE_WIDE_FRAGS(0, L.w[((J_) + 1) % kWStages], L.x[((J_) + 1) % kWStages], 0)                            \
+    __builtin_amdgcn_sched_barrier(0);                                                                      \
+    MOE_WIDE_MFMA_RANGE(1, 0, NB)                                                                           \
+    __builtin_amdgcn_sched_barrier(0);                                                                      \
+  }
+  static_assert(NS == 2, "the stage body is written for two 16-deep steps");
+  // the stage count is a multiple of kWStages (K is a multiple of 128)
+  for (int kt = 0; kt < nk; kt += kWStages) {
+    MOE_WIDE_STAGE(0, kt)
+    MOE_WIDE_STAGE(1, kt + 1)
+    if constexpr (kWStages == 4) {
+      MOE_WIDE_STAGE(2, kt + 2)
+      MOE_WIDE_STAGE(3, kt + 3)
     }
   }
-#undef MOE_WIDE_FA
-#undef MOE_WIDE_FB
-#undef MOE_WIDE_LOAD
-#undef MOE_WIDE_ADVANCE
-#undef MOE_WIDE_STORE
+#undef MOE_WIDE_STAGE
+#undef MOE_WIDE_ISSUE
+#undef MOE_WIDE_FRAGS
+#undef MOE_WIDE_MFMAS
+#undef MOE_WIDE_MFMA_RANGE
+  // no load may still be writing LDS when the next tile reuses the buffers
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+  __builtin_amdgcn_s_barrier();
 
   uint16_t* out = static_cast<uint16_t*>(tl.shared ? p.sh_out : p.out);
 #pragma unroll
@@ -809,8 +851,10 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& p, const Tile& tl, con
 template <int KIND, bool PACKED>
 __global__ __launch_bounds__(kGemmThreads, 1) void ffn_wide_kernel(GemmArgs p) {
   __shared__ Sched sh;
-  __shared__ __attribute__((aligned(16))) uint16_t wl[2][kWN * kWK];
-  __shared__ __attribute__((aligned(16))) uint16_t xl[2][kWM * kWK];
+  constexpr int kExtra = kWStages == 4 ? kWStage : 8;  // buffers 2 and 3 exist with a 4-deep ring only
+  __shared__ __attribute__((aligned(1024))) uint16_t w0[kWStage], w1[kWStage], w2[kExtra], w3[kExtra];
+  __shared__ __attribute__((aligned(1024))) uint16_t x0[kWStage], x1[kWStage], x2[kExtra], x3[kExtra];
+  const WideLds L = {{w0, w1, w2, w3}, {x0, x1, x2, x3}};
   const int ntn = KIND == kUp ? p.n_out / 128 : p.n_out / 256;
   const int n_tiles = build_schedule(p, kWM, ntn, true, sh);
   const int per_xcd = int(gridDim.x) / kXcds;
@@ -819,16 +863,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_wide_kernel(GemmArgs p) {
     const Tile tl = decode_tile<true>(p, kWM, ntn, sh, t);
     build_rowmap(p, tl, kWM, sh);
     switch ((tl.nrows + 31) / 32) {
-      case 1: wide_tile<KIND, PACKED, 1>(p, tl, sh, wl, xl); break;
-      case 2: wide_tile<KIND, PACKED, 2>(p, tl, sh, wl, xl); break;
-      case 3: wide_tile<KIND, PACKED, 3>(p, tl, sh, wl, xl); break;
-      case 4: wide_tile<KIND, PACKED, 4>(p, tl, sh, wl, xl); break;
-      case 5: wide_tile<KIND, PACKED, 5>(p, tl, sh, wl, xl); break;
-      case 6: wide_tile<KIND, PACKED, 6>(p, tl, sh, wl, xl); break;
-      case 7: wide_tile<KIND, PACKED, 7>(p, tl, sh, wl, xl); break;
-      default: wide_tile<KIND, PACKED, 8>(p, tl, sh, wl, xl); break;
+      case 1: wide_tile<KIND, PACKED, 1>(p, tl, sh, L); break;
+      case 2: wide_tile<KIND, PACKED, 2>(p, tl, sh, L); break;
+      case 3: wide_tile<KIND, PACKED, 3>(p, tl, sh, L); break;
+      case 4: wide_tile<KIND, PACKED, 4>(p, tl, sh, L); break;
+      case 5: wide_tile<KIND, PACKED, 5>(p, tl, sh, L); break;
+      case 6: wide_tile<KIND, PACKED, 6>(p, tl, sh, L); break;
+      case 7: wide_tile<KIND, PACKED, 7>(p, tl, sh, L); break;
+      default: wide_tile<KIND, PACKED, 8>(p, tl, sh, L); break;
     }
-    __syncthreads();  // rowmap and stage buffers are rewritten by the next tile
+    __syncthreads();  // rowmap is rewritten by the next tile
   }
 }
 
