@@ -25,6 +25,7 @@ COMPACT, PADDED = 0, 1
 W_ROWMAJOR, W_PACKED = 0, 1
 GG_FULL, GG_UP, GG_DOWN = 0, 1, 2
 GEMM_AUTO, GEMM_WIDE, GEMM_STREAM_K = 0, 1, 2
+ACT_ROWS, ACT_BLOCKED16 = 0, 1
 STATUS_OVERFLOW = 1
 _F32, _BF16, _FP8 = 0, 1, 2
 
@@ -57,7 +58,7 @@ class GGemmDesc(ctypes.Structure):
                 ("act_dt", ctypes.c_int), ("w_dt", ctypes.c_int), ("layout", ctypes.c_int),
                 ("n_src", ctypes.c_int), ("capacity", ctypes.c_int), ("rows", ctypes.c_int64),
                 ("stage", ctypes.c_int), ("shared", ctypes.POINTER(SharedExpert)), ("w_format", ctypes.c_int),
-                ("policy", ctypes.c_int)]
+                ("policy", ctypes.c_int), ("a_layout", ctypes.c_int)]
 
 
 _P = ctypes.c_void_p
@@ -73,6 +74,7 @@ _SIGNATURES = {
     "moe_dispatch_layout_workspace": (_SZ, [ctypes.POINTER(LayoutDesc)]),
     "moe_dispatch_layout": (_I, [ctypes.POINTER(LayoutDesc), _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_dispatch": (_I, [_P, _I, _I, _I, _I, _P, _I64, _P, _P]),
+    "moe_dispatch_blocked": (_I, [_P, _I, _I, _I, _P, _I64, _P, _P, _P]),
     "moe_grouped_gemm_workspace": (_SZ, [ctypes.POINTER(GGemmDesc)]),
     "moe_grouped_gemm": (_I, [ctypes.POINTER(GGemmDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_combine": (_I, [_P, _I, _I64, _P, _P, _I, _I, _I, _P, _I, _I, _P, _P]),
@@ -213,16 +215,43 @@ def moe_dispatch(x: torch.Tensor, row_of: torch.Tensor, top_k: int, n_rows: int,
     return xe
 
 
+def blocked_rows(n_rows: int) -> int:
+    """Rows a 16-row blocked buffer of n_rows rows holds."""
+    return (n_rows + 15) // 16 * 16
+
+
+def moe_dispatch_blocked(x: torch.Tensor, row_token: torch.Tensor, n_rows: int, n_used: Optional[torch.Tensor] = None,
+                         xe: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Copy token rows into the expert-grouped buffer in the 16-row blocked layout
+    (xe [blocked_rows(n_rows), H]; holes untouched). ``n_used`` is a device int32
+    row count (e.g. expert_off[n_local:]) or None for all rows."""
+    _dev(x, "x", torch.bfloat16)
+    _dev(row_token, "row_token", torch.int32)
+    N, H = x.shape
+    if xe is None:
+        xe = torch.empty((blocked_rows(n_rows), H), dtype=x.dtype, device=x.device)
+    _dev(xe, "xe", x.dtype)
+    if xe.shape[0] < blocked_rows(n_rows):
+        raise ValueError("xe must hold blocked_rows(n_rows) rows")
+    if n_used is not None:
+        _dev(n_used, "n_used", torch.int32)
+    _check(lib().moe_dispatch_blocked(_ptr(x), _act_code(x.dtype), N, H, _ptr(row_token), n_rows, _ptr(n_used),
+                                      _ptr(xe), _stream()), "moe_dispatch_blocked")
+    return xe
+
+
 # --------------------------------------------------------------------------- grouped GEMM
 _W_CODE = {torch.float32: _F32, torch.bfloat16: _BF16, torch.uint8: _FP8, torch.float8_e4m3fn: _FP8}
 
 
 def gemm_desc(n_groups, hidden, inter, act_dtype, w_dtype, layout, n_src, capacity, rows, stage=GG_FULL,
-              shared: "SharedExpert | None" = None, w_format: int = W_ROWMAJOR, policy: int = 0):
+              shared: "SharedExpert | None" = None, w_format: int = W_ROWMAJOR, policy: int = 0,
+              a_layout: int = ACT_ROWS):
     w_code = _W_CODE[w_dtype]
     d = GGemmDesc(n_groups, hidden, inter, _act_code(act_dtype), w_code, layout, n_src, capacity, rows, stage)
     d.w_format = w_format
     d.policy = policy
+    d.a_layout = a_layout
     if shared is not None:
         d.shared = ctypes.pointer(shared)
     return d
@@ -249,7 +278,8 @@ def moe_grouped_gemm(a: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, *, gr
                      s13=None, s2=None, layout: int = COMPACT, n_src: int = 1, capacity: int = 0,
                      stage: int = GG_FULL, y: Optional[torch.Tensor] = None,
                      ws: Optional[torch.Tensor] = None, shared: Optional[dict] = None,
-                     w_format: int = W_ROWMAJOR, policy: int = 0) -> torch.Tensor:
+                     w_format: int = W_ROWMAJOR, policy: int = 0, a_layout: int = ACT_ROWS,
+                     rows: Optional[int] = None) -> torch.Tensor:
     """SwiGLU FFN per expert over the rows each expert holds (see moe.h).
 
     ``shared`` = dict(a, w13, w2, y[, s13, s2]) runs the shared expert in the same launches."""
@@ -265,7 +295,11 @@ def moe_grouped_gemm(a: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, *, gr
     if shared is not None:
         se = shared_expert(shared["a"], shared["w13"], shared["w2"], shared.get("y"), shared.get("s13"),
                            shared.get("s2"))
-    desc = gemm_desc(G, H, I, a.dtype, w13.dtype, layout, n_src, capacity, R, stage, se, w_format, policy)
+    if a_layout == ACT_BLOCKED16:
+        R = a.shape[0] // 16 * 16 if rows is None else rows
+    elif rows is not None:
+        R = rows
+    desc = gemm_desc(G, H, I, a.dtype, w13.dtype, layout, n_src, capacity, R, stage, se, w_format, policy, a_layout)
     wsb = moe_grouped_gemm_workspace(desc)
     if wsb == 0:
         raise MoeError("moe_grouped_gemm: invalid descriptor")

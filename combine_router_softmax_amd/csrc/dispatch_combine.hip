@@ -45,6 +45,40 @@ __global__ __launch_bounds__(kVecThreads) void dispatch_kernel(const uint4* __re
     if (r[k] >= 0) xe[size_t(r[k]) * row_vecs + c] = v;
 }
 
+// Row-wise dispatch into the 16-row blocked layout: a unit of work is one
+// group of 16 output rows x 128 columns (four 1 KiB blocks, contiguous in xe).
+// Wave w reads rows 4w..4w+3 of the group, 256 contiguous bytes each, and
+// every lane stores its 16 bytes at their blocked position, so the workgroup
+// writes 4 KiB of contiguous memory. Persistent workgroups walk the units up
+// to the device-side row count.
+constexpr int kBlkCols = 128;  // columns per unit
+__global__ __launch_bounds__(kVecThreads) void dispatch_blocked_kernel(const uint4* __restrict__ x, int hidden,
+                                                                        int n_tokens,
+                                                                        const int32_t* __restrict__ row_token,
+                                                                        int64_t n_rows,
+                                                                        const int32_t* __restrict__ n_used,
+                                                                        uint16_t* __restrict__ xe) {
+  const int64_t rows = n_used ? min<int64_t>(max(n_used[0], 0), n_rows) : n_rows;
+  const int ncu = (hidden + kBlkCols - 1) / kBlkCols;  // column units per row group
+  const int64_t units = (rows + 15) / 16 * ncu;
+  const int tid = threadIdx.x;
+  const int ri = tid >> 4;         // row inside the group (wave w: rows 4w..4w+3)
+  const int piece = tid & 15;      // 16-byte piece inside the unit's 256 bytes of the row
+  const int row_vecs = hidden / 8;
+  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+    const int64_t g = u / ncu;
+    const int cu = int(u - g * ncu);
+    const int64_t r = g * 16 + ri;
+    const int col = cu * kBlkCols + piece * 8;
+    if (r >= rows || col >= hidden) continue;
+    const int t = row_token[r];
+    if (t < 0 || t >= n_tokens) continue;  // a hole (or an invalid entry): not written
+    const uint4 v = x[size_t(t) * row_vecs + col / 8];
+    const size_t off = (size_t(g) * (hidden >> 5) + (col >> 5)) * 512 + size_t(ri) * 32 + (col & 31);
+    *reinterpret_cast<uint4*>(xe + off) = v;
+  }
+}
+
 // 16-byte piece <-> floats
 template <typename T>
 struct Vec;
@@ -158,6 +192,22 @@ MOE_API moe_status_t moe_dispatch(const void* x, moe_dtype_t dt, int n_tokens, i
     case 8: hipLaunchKernelGGL(dispatch_kernel<8>, grid, block, 0, stream, xv, row_vecs, n_chunks, top_k, row_of, n_rows, ov); break;
     default: hipLaunchKernelGGL(dispatch_kernel<16>, grid, block, 0, stream, xv, row_vecs, n_chunks, top_k, row_of, n_rows, ov); break;
   }
+  return launch_status();
+}
+
+MOE_API moe_status_t moe_dispatch_blocked(const void* x, moe_dtype_t dt, int n_tokens, int hidden,
+                                          const int32_t* row_token, int64_t n_rows, const int32_t* n_used, void* xe,
+                                          hipStream_t stream) {
+  if (n_tokens < 0 || hidden < 1 || n_rows < 0) return MOE_ERR_INVALID_ARG;
+  if (dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (hidden % 32) return MOE_ERR_INVALID_ARG;
+  if (n_tokens == 0 || n_rows == 0) return MOE_OK;
+  if (!x || !row_token || !xe || !aligned16(x) || !aligned16(xe)) return MOE_ERR_INVALID_ARG;
+  const int64_t units = (n_rows + 15) / 16 * ((hidden + kBlkCols - 1) / kBlkCols);
+  const int64_t cap = int64_t(device_cu_count()) * 8;  // 8 workgroups per compute unit
+  const dim3 grid(unsigned(units < cap ? units : cap)), block(kVecThreads);
+  hipLaunchKernelGGL(dispatch_blocked_kernel, grid, block, 0, stream, static_cast<const uint4*>(x), hidden, n_tokens,
+                     row_token, n_rows, n_used, static_cast<uint16_t*>(xe));
   return launch_status();
 }
 

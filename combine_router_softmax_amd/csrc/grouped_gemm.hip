@@ -89,7 +89,21 @@ struct GemmArgs {
   int packed;                 // weights in the packed (load-order) layout
   int wide_min;               // groups with at least this many rows may go to the wide-tile kernel ...
   int wide_min_tiles;         // ... if the wide groups make at least this many wide tiles
+  int a_blk, sh_a_blk;        // routed / shared activations in the 16-row blocked layout
+  int out_blk;                // outputs (routed and shared) in the 16-row blocked layout
 };
+
+// 16-row blocked activation layout: element (r, c) of an [R, K] matrix sits
+// at ((r / 16) * (K / 32) + c / 32) * 512 + (r % 16) * 32 + c % 32, i.e.
+// blocks of 16 rows x 32 columns (1 KiB of bf16) stored contiguously, the
+// blocks of one 16-row group in column order. A wave load of 16 rows x 32
+// columns is then one contiguous KiB instead of 16 separate 64-byte pieces.
+__device__ __forceinline__ size_t blk_row_base(int64_t r, int K) {
+  return size_t(r >> 4) * size_t(K >> 5) * 512 + size_t(r & 15) * 32;
+}
+__device__ __forceinline__ size_t act_off(int64_t r, int c, int K, bool blk) {
+  return blk ? blk_row_base(r, K) + size_t(c >> 5) * 512 + (c & 31) : size_t(r) * K + c;
+}
 
 struct Sched {
   int tile_start[kMaxGroups + 2];
@@ -294,15 +308,16 @@ __device__ inline float* sk_slot(float* parts, int b, int slot) {
   return parts + (size_t(b) * 2 + slot) * kPartFloats;
 }
 
+// (four consecutive output columns never straddle a 32-column block)
 template <int KIND, int NBMAX>
 __device__ __forceinline__ void ffn_epilogue(const f32x16_t (&acc)[NBMAX], const Tile& tl, int nb, const Sched& sh,
-                                             uint16_t* out, int n_out, int wv, int lr, int lh) {
+                                             uint16_t* out, int n_out, int wv, int lr, int lh, bool oblk) {
 #pragma unroll
   for (int b = 0; b < NBMAX; ++b) {
     if (b >= nb) continue;
     const int phys = sh.rowmap[b * 32 + lr];
     if (phys < 0) continue;
-    uint16_t* orow = out + size_t(phys) * n_out;
+    uint16_t* orow = out + act_off(phys, 0, n_out, oblk);
     if (KIND == kUp) {
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
@@ -310,13 +325,14 @@ __device__ __forceinline__ void ffn_epilogue(const f32x16_t (&acc)[NBMAX], const
 #pragma unroll
         for (int r = 0; r < 4; ++r) h[r] = silu_f(acc[b][4 * q + r]) * acc[b][4 * (q + 2) + r];
         const int col = tl.nt * 64 + 16 * wv + 8 * q + 4 * lh;
-        *reinterpret_cast<uint2*>(orow + col) = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+        *reinterpret_cast<uint2*>(orow + (oblk ? size_t(col >> 5) * 512 + (col & 31) : size_t(col))) =
+            make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
       }
     } else {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int col = tl.nt * 128 + 32 * wv + 8 * q + 4 * lh;
-        *reinterpret_cast<uint2*>(orow + col) =
+        *reinterpret_cast<uint2*>(orow + (oblk ? size_t(col >> 5) * 512 + (col & 31) : size_t(col))) =
             make_uint2(pack_bf16x2(acc[b][4 * q], acc[b][4 * q + 1]), pack_bf16x2(acc[b][4 * q + 2], acc[b][4 * q + 3]));
       }
     }
@@ -368,6 +384,11 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const TileRun& tr, c
     const int phys = sh.rowmap[xr + 16 * i];
     xrow[i] = phys >= 0 ? phys : phys0;
   }
+  // address of this thread's 16 bytes of row `row`, chunk C: row-major, or
+  // in the blocked layout (a chunk of 128 columns spans four 32-column blocks)
+  const bool ablk = tl.shared ? p.sh_a_blk : p.a_blk;
+  const size_t xcstep = ablk ? size_t(4) * 512 : size_t(kKC);
+  const size_t xcofs = ablk ? size_t((tid & 15) >> 2) * 512 + ((tid & 15) & 3) * 8 : size_t(tid & 15) * 8;
   // (plain unrolled loops over register arrays, no closures: the arrays must
   // stay in registers)
   // staged activations live in one vector value (XV x 16 bytes)
@@ -375,7 +396,8 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const TileRun& tr, c
 #define MOE_LOAD_X(XV_, C_)                                                                                   \
   _Pragma("unroll") for (int i = 0; i < XV; ++i) {                                                            \
     const uint4 t_ =                                                                                          \
-        *reinterpret_cast<const uint4*>(tr.A + size_t(xrow[i]) * p.K + size_t(C_) * kKC + (tid & 15) * 8);    \
+        *reinterpret_cast<const uint4*>(tr.A + (ablk ? blk_row_base(xrow[i], p.K) : size_t(xrow[i]) * p.K) +     \
+                                        size_t(C_) * xcstep + xcofs);                                         \
     XV_[4 * i] = t_.x;                                                                                        \
     XV_[4 * i + 1] = t_.y;                                                                                    \
     XV_[4 * i + 2] = t_.z;                                                                                    \
@@ -470,7 +492,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const TileRun& tr, c
 #undef MOE_LOAD_W
   if (tr.c_begin == 0 && tr.c_end == tr.nchunks) {
     uint16_t* out = static_cast<uint16_t*>(tl.shared ? p.sh_out : p.out);
-    ffn_epilogue<KIND, NB>(acc, tl, NB, sh, out, p.n_out, wv, lr, lh);
+    ffn_epilogue<KIND, NB>(acc, tl, NB, sh, out, p.n_out, wv, lr, lh, p.out_blk);
   } else {
     // partial sums of a split tile, in accumulator-register order
     float* dst = sk_slot(parts, rng, first_tile ? 0 : 1);
@@ -597,7 +619,7 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_fixup_kernel(GemmArgs p, con
     }
   }
   uint16_t* out = static_cast<uint16_t*>(tl.shared ? p.sh_out : p.out);
-  ffn_epilogue<KIND, kMB>(acc, tl, nb, sh, out, p.n_out, wv, lr, lh);
+  ffn_epilogue<KIND, kMB>(acc, tl, nb, sh, out, p.n_out, wv, lr, lh, p.out_blk);
 }
 
 // ------------------------------------------------------------------ wide-tile kernel
@@ -673,13 +695,17 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& p, const Tile& tl, con
   constexpr int P = WL + XL;  // loads per wave per stage
   const int lrow = lane / kWSlots;
   auto col_of = [&](int row) { return (lane % kWSlots) ^ ((row / (16 / kWSlots)) % kWSlots); };
+  const bool ablk = tl.shared ? p.sh_a_blk : p.a_blk;
+  const size_t xstep = ablk ? 512 : kWK;  // elements from one stage of a row to the next
   const uint16_t* xg[XL];
   const int phys0 = sh.rowmap[0];
 #pragma unroll
   for (int q = 0; q < XL; ++q) {
     const int row = kWRowsPerLoad * (4 * q + wv) + lrow;
     const int phys = row < NB * 32 ? sh.rowmap[row] : -1;
-    xg[q] = A + size_t(phys >= 0 ? phys : phys0) * p.K + col_of(row) * 8;
+    const int pr = phys >= 0 ? phys : phys0;
+    // (columns 8 cg .. 8 cg + 7 of stage 0 lie inside the first 32-column block)
+    xg[q] = A + (ablk ? blk_row_base(pr, p.K) : size_t(pr) * p.K) + col_of(row) * 8;
   }
   const uint16_t* wg[WL];
 #pragma unroll
@@ -725,7 +751,7 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& p, const Tile& tl, con
   };
 #define MOE_WIDE_ISSUE(KT_, SLOT_)                                                                          \
   {                                                                                                         \
-    const size_t wo_ = woff(KT_), xo_ = size_t(KT_) * kWK;                                                  \
+    const size_t wo_ = woff(KT_), xo_ = size_t(KT_) * xstep;                                                \
     _Pragma("unroll") for (int q = 0; q < WL; ++q)                                                          \
       __builtin_amdgcn_global_load_lds(wg[q] + wo_, (lds_ptr_t)(L.w[SLOT_] + (4 * q + wv) * 512), 16, 0, 0);  \
     _Pragma("unroll") for (int q = 0; q < XL; ++q)                                                          \
@@ -821,11 +847,12 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& p, const Tile& tl, con
   __builtin_amdgcn_s_barrier();
 
   uint16_t* out = static_cast<uint16_t*>(tl.shared ? p.sh_out : p.out);
+  const bool oblk = p.out_blk;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const int phys = sh.rowmap[32 * b + lr];
     if (phys < 0) continue;
-    uint16_t* orow = out + size_t(phys) * p.n_out;
+    uint16_t* orow = out + act_off(phys, 0, p.n_out, oblk);
     if (KIND == kUp) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -833,7 +860,8 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& p, const Tile& tl, con
 #pragma unroll
         for (int r = 0; r < 4; ++r) h[r] = silu_f(acc[0][b][4 * q + r]) * acc[1][b][4 * q + r];
         const int col = tl.nt * 128 + 32 * wv + 8 * q + 4 * lh;
-        *reinterpret_cast<uint2*>(orow + col) = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+        *reinterpret_cast<uint2*>(orow + (oblk ? size_t(col >> 5) * 512 + (col & 31) : size_t(col))) =
+            make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
       }
     } else {
 #pragma unroll
@@ -841,7 +869,7 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& p, const Tile& tl, con
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int col = tl.nt * 256 + 64 * wv + 32 * a + 8 * q + 4 * lh;
-          *reinterpret_cast<uint2*>(orow + col) = make_uint2(pack_bf16x2(acc[a][b][4 * q], acc[a][b][4 * q + 1]),
+          *reinterpret_cast<uint2*>(orow + (oblk ? size_t(col >> 5) * 512 + (col & 31) : size_t(col))) = make_uint2(pack_bf16x2(acc[a][b][4 * q], acc[a][b][4 * q + 1]),
                                                              pack_bf16x2(acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]));
         }
     }
@@ -990,6 +1018,7 @@ static bool ggemm_desc_ok(const moe_ggemm_desc_t* d) {
   if (d->shared && d->shared->rows < 0) return false;
   if (d->w_format != MOE_W_ROWMAJOR && d->w_format != MOE_W_PACKED) return false;
   if (d->policy != MOE_GEMM_AUTO && d->policy != MOE_GEMM_WIDE && d->policy != MOE_GEMM_STREAM_K) return false;
+  if (d->a_layout != MOE_ACT_ROWS && d->a_layout != MOE_ACT_BLOCKED16) return false;
   return true;
 }
 
@@ -1003,11 +1032,15 @@ static bool ggemm_desc_supported(const moe_ggemm_desc_t* d) {
   if (d->rows >= (int64_t(1) << 31)) return false;
   if (d->shared && d->shared->rows >= (1 << 30)) return false;
   if (f32 && d->w_format == MOE_W_PACKED) return false;
+  if (f32 && d->a_layout != MOE_ACT_ROWS) return false;
   return true;
 }
 
+// h [rows, I]: fp32 row-major, or bf16 in the 16-row blocked layout (rows
+// rounded up to 16)
 static size_t h_bytes(const moe_ggemm_desc_t* d, int64_t rows) {
   const size_t el = d->act_dt == MOE_F32 ? 4 : 2;
+  if (d->act_dt != MOE_F32) rows = (rows + 15) / 16 * 16;
   return align_up(size_t(rows) * size_t(d->inter) * el, 256);
 }
 
@@ -1119,6 +1152,7 @@ MOE_API moe_status_t moe_grouped_gemm(const moe_ggemm_desc_t* d, const void* a, 
   const bool force = d->policy == MOE_GEMM_WIDE;
   p.wide_min = wide_ok ? (force ? 1 : kWideMinRows) : kNoWide;
   p.wide_min_tiles = force ? 0 : kWideMinTiles;
+  p.sh_a_blk = 0;
   moe_status_t st = MOE_OK;
   if (up) {
     p.a = a;
@@ -1133,6 +1167,9 @@ MOE_API moe_status_t moe_grouped_gemm(const moe_ggemm_desc_t* d, const void* a, 
     p.K = d->hidden;
     p.n_out = d->inter;
     p.n_tiles_n = f32 ? d->inter / kFBN : d->inter / 64;
+    p.a_blk = d->a_layout == MOE_ACT_BLOCKED16;
+    p.sh_a_blk = 0;       // the shared expert reads its rows of x in place
+    p.out_blk = !f32;     // h (internal) is blocked for bf16
     st = launch_stage(p, f32, fp8, kUp, parts, stream);
     if (st != MOE_OK) return st;
   }
@@ -1149,6 +1186,8 @@ MOE_API moe_status_t moe_grouped_gemm(const moe_ggemm_desc_t* d, const void* a, 
     p.K = d->inter;
     p.n_out = d->hidden;
     p.n_tiles_n = f32 ? d->hidden / kFBN : d->hidden / 128;
+    p.a_blk = p.sh_a_blk = !f32;  // h
+    p.out_blk = 0;                // y rows are read by the combine
     st = launch_stage(p, f32, fp8, kDown, parts, stream);
   }
   return st;

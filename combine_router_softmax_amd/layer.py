@@ -13,9 +13,9 @@ from typing import Optional
 
 import torch
 
-from . import (COMPACT, GG_DOWN, GG_FULL, GG_UP, PADDED, W_PACKED, W_ROWMAJOR, SharedExpert, gemm_desc, moe_combine, moe_dispatch, moe_dispatch_layout,
-               moe_grouped_gemm, moe_grouped_gemm_workspace, moe_layout_rows, moe_pack_weights,
-               moe_route_topk)
+from . import (ACT_BLOCKED16, ACT_ROWS, COMPACT, GG_DOWN, GG_FULL, GG_UP, PADDED, W_PACKED, W_ROWMAJOR, SharedExpert,
+               blocked_rows, gemm_desc, moe_combine, moe_dispatch, moe_dispatch_blocked, moe_dispatch_layout,
+               moe_grouped_gemm, moe_grouped_gemm_workspace, moe_layout_rows, moe_pack_weights, moe_route_topk)
 
 
 class MoEShare:
@@ -23,7 +23,8 @@ class MoEShare:
 
     def __init__(self, *, n_tokens: int, hidden: int, inter: int, n_experts: int, top_k: int, n_src: int,
                  expert_lo: int, n_local: int, act_dtype: torch.dtype, layout: int = COMPACT,
-                 capacity: Optional[int] = None, self_range=(0, 0), device="cuda"):
+                 capacity: Optional[int] = None, self_range=(0, 0), device="cuda",
+                 blocked: Optional[bool] = None):
         self.N, self.H, self.I, self.E, self.K = n_tokens, hidden, inter, n_experts, top_k
         self.S, self.lo, self.L = n_src, expert_lo, n_local
         self.layout = layout
@@ -36,11 +37,18 @@ class MoEShare:
         self.act_dtype = act_dtype
         self.dev = torch.device(device)
         self.R = moe_layout_rows(n_tokens, top_k, n_experts, n_src, expert_lo, n_local, layout, capacity)
+        # expert rows in the 16-row blocked layout when experts are expected to
+        # hold enough rows for the wide-tile GEMM (the layout speeds up its loads)
+        if blocked is None:
+            blocked = n_tokens * top_k >= 128 * n_experts
+        self.blocked = bool(blocked) and act_dtype == torch.bfloat16 and hidden % 32 == 0
+        self.a_layout = ACT_BLOCKED16 if self.blocked else ACT_ROWS
         d = self.dev
         self.topk_idx = torch.empty((n_tokens, top_k), dtype=torch.int32, device=d)
         self.topk_w = torch.empty((n_tokens, top_k), dtype=torch.float32, device=d)
         self.lay = None
-        self.xe = torch.empty((max(self.R, 1), hidden), dtype=act_dtype, device=d)
+        self.xe = torch.empty((max(blocked_rows(self.R) if self.blocked else self.R, 1), hidden), dtype=act_dtype,
+                              device=d)
         self.ye = torch.empty((max(self.R, 1), hidden), dtype=act_dtype, device=d)
         B0 = self.self_hi - self.self_lo
         self.ys = torch.empty((max(B0, 1), hidden), dtype=act_dtype, device=d)
@@ -69,7 +77,7 @@ class MoEShare:
         B0 = self.self_hi - self.self_lo
         se = SharedExpert(rows=B0 if self.sw is not None else 0)
         desc = gemm_desc(self.L, self.H, self.I, self.act_dtype, wdt, self.layout, self.S, self.capacity, self.R,
-                         shared=se, w_format=self.w_format)
+                         shared=se, w_format=self.w_format, a_layout=self.a_layout)
         self.ws = torch.zeros(moe_grouped_gemm_workspace(desc), dtype=torch.uint8, device=self.dev)
         if self.sw is not None:
             sdesc = gemm_desc(1, self.H, self.I, self.act_dtype, self.sw["w13"].dtype, COMPACT, 1, 0, max(B0, 1),
@@ -92,15 +100,21 @@ class MoEShare:
                                        self.capacity, out=self.lay)
 
     def dispatch(self, x):
-        moe_dispatch(x, self.lay["row_of"], self.K, self.R, self.xe)
+        if self.blocked:
+            n_used = self.lay["expert_off"][self.L:] if self.layout == COMPACT else None
+            moe_dispatch_blocked(x, self.lay["row_token"], self.R, n_used, self.xe)
+        else:
+            moe_dispatch(x, self.lay["row_of"], self.K, self.R, self.xe)
 
     def gemm(self, stage=GG_FULL, x=None):
         """Routed experts; with ``x`` the shared expert runs in the same launches."""
         w = self.w
-        moe_grouped_gemm(self.xe[: self.R], w["w13"], w["w2"], group_off=self.lay["expert_off"],
+        a = self.xe if self.blocked else self.xe[: self.R]
+        moe_grouped_gemm(a, w["w13"], w["w2"], group_off=self.lay["expert_off"],
                          counts=self.lay["counts"], s13=w.get("s13"), s2=w.get("s2"), layout=self.layout,
                          n_src=self.S, capacity=self.capacity, stage=stage, y=self.ye[: self.R], ws=self.ws,
-                         shared=None if x is None else self._shared_arg(x), w_format=self.w_format)
+                         shared=None if x is None else self._shared_arg(x), w_format=self.w_format,
+                         a_layout=self.a_layout, rows=self.R)
 
     def shared_gemm(self, x, stage=GG_FULL):
         if self.sw is None or self.self_hi <= self.self_lo:

@@ -74,6 +74,18 @@ typedef enum {
   MOE_LAYOUT_PADDED = 1
 } moe_layout_t;
 
+/* Storage of an activation matrix [R, K] (bf16, K % 32 == 0).
+ * ROWS: row-major. BLOCKED16: blocks of 16 rows x 32 columns (1 KiB) stored
+ * contiguously, the blocks of one 16-row group in column order: element
+ * (r, c) sits at ((r / 16) * (K / 32) + c / 32) * 512 + (r % 16) * 32 + c % 32.
+ * A blocked matrix holds ceil(R / 16) * 16 rows. The grouped GEMM loads
+ * 16 rows x 32 columns per wave instruction; blocked, that is one contiguous
+ * KiB instead of 16 separate 64-byte pieces. */
+typedef enum {
+  MOE_ACT_ROWS = 0,
+  MOE_ACT_BLOCKED16 = 1
+} moe_act_layout_t;
+
 /* Bit of the device status word written by moe_dispatch_layout. */
 #define MOE_STATUS_OVERFLOW 1
 
@@ -160,6 +172,19 @@ moe_status_t moe_dispatch_layout(const moe_layout_desc_t* d, const int32_t* topk
 moe_status_t moe_dispatch(const void* x, moe_dtype_t dt, int n_tokens, int hidden, int top_k,
                           const int32_t* row_of, int64_t n_rows, void* xe, hipStream_t stream);
 
+/* The same copy into an expert-grouped buffer in the MOE_ACT_BLOCKED16 layout,
+ * row by row: xe row r = x[row_token[r]] for row_token[r] in [0, n_tokens);
+ * other rows (holes) are not written. Only rows [0, *n_used) are visited
+ * (n_used: device int32, e.g. expert_off + n_local for the COMPACT layout, or
+ * NULL for all n_rows). A token row is read once per slot.
+ *
+ * x [n_tokens, hidden] bf16 row-major, hidden % 32 == 0; xe holds
+ * ceil(n_rows / 16) * 16 rows of hidden bf16.
+ */
+moe_status_t moe_dispatch_blocked(const void* x, moe_dtype_t dt, int n_tokens, int hidden,
+                                  const int32_t* row_token, int64_t n_rows, const int32_t* n_used, void* xe,
+                                  hipStream_t stream);
+
 /* ------------------------------------------------------------------ grouped GEMM */
 typedef enum {
   MOE_W_ROWMAJOR = 0, /* w13 [G, 2I, H] and w2 [G, H, I] row-major */
@@ -213,6 +238,7 @@ typedef struct {
   const moe_shared_expert_t* shared; /* host pointer, or NULL for none */
   moe_weight_format_t w_format;      /* layout of w13/w2 (and of the shared expert's) */
   moe_gemm_policy_t policy;          /* kernel choice per group; MOE_GEMM_AUTO unless tuning or testing */
+  moe_act_layout_t a_layout;         /* storage of the routed rows a (bf16 only for BLOCKED16) */
 } moe_ggemm_desc_t;
 
 /* Bytes of scratch moe_grouped_gemm needs (the intermediates h [R, I] and, with
@@ -230,7 +256,9 @@ size_t moe_grouped_gemm_workspace(const moe_ggemm_desc_t* d);
  * rounded to the activation dtype. Unoccupied rows are not written. Empty
  * groups cost nothing.
  *
- * a          [R, H] activations (act_dt).
+ * a          [R, H] activations (act_dt), stored as desc->a_layout says (the
+ *            shared expert's rows are always row-major). The intermediate h
+ *            lives in the workspace (bf16: blocked layout).
  * counts     [G, S] int32 (PADDED: group g's rows are, for each s,
  *            (g*S+s)*capacity + [0, min(counts[g*S+s], capacity)) ); may be NULL
  *            for COMPACT.

@@ -91,6 +91,12 @@ def test_dispatch_and_combine_argument_errors(lib):
     assert lib.moe_dispatch(FAKE, 1, 10, 64, 17, FAKE, 100, FAKE, None) == UNSUPPORTED
     assert lib.moe_dispatch(ctypes.c_void_p(0x100008), 1, 10, 64, 2, FAKE, 100, FAKE, None) == INVALID  # misaligned
     assert lib.moe_dispatch(None, 1, 0, 64, 2, None, 100, None, None) == OK
+    b = lib.moe_dispatch_blocked
+    assert b(FAKE, 0, 10, 64, FAKE, 100, None, FAKE, None) == UNSUPPORTED  # f32 rows
+    assert b(FAKE, 1, 10, 48, FAKE, 100, None, FAKE, None) == INVALID      # hidden % 32
+    assert b(FAKE, 1, -1, 64, FAKE, 100, None, FAKE, None) == INVALID
+    assert b(FAKE, 1, 10, 64, None, 100, None, FAKE, None) == INVALID      # no row_token
+    assert b(None, 1, 0, 64, None, 100, None, None, None) == OK
     c = lib.moe_combine
     assert c(FAKE, 1, 100, FAKE, FAKE, 10, 2, 12, None, 0, 0, FAKE, None) == INVALID  # 24-byte rows
     assert c(FAKE, 1, 100, FAKE, FAKE, 10, 2, 64, FAKE, 5, 20, FAKE, None) == INVALID  # self range past N
@@ -163,6 +169,13 @@ def test_pack_weights_and_format_validation(lib):
     badp = _gd()
     badp.policy = 3
     assert lib.moe_grouped_gemm_workspace(ctypes.byref(badp)) == 0
+    bada = _gd()
+    bada.a_layout = 2
+    assert lib.moe_grouped_gemm_workspace(ctypes.byref(bada)) == 0
+    f32b = _gd(act_dt=0, w_dt=0)
+    f32b.a_layout = 1
+    ws = lib.moe_grouped_gemm_workspace(ctypes.byref(f32b))
+    assert lib.moe_grouped_gemm(ctypes.byref(f32b), *([FAKE] * 8), FAKE, ws, None) == UNSUPPORTED
     f32p = _gd(act_dt=0, w_dt=0)
     f32p.w_format = 1
     ws = lib.moe_grouped_gemm_workspace(ctypes.byref(f32p))
@@ -177,3 +190,18 @@ def test_product_never_imports_the_oracle():
                 text = open(os.path.join(dirpath, fn)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", text, flags=re.M), fn
                 assert "oracle/" not in text, fn
+
+
+def test_blocked_layout_helper_matches_the_documented_formula():
+    # element (r, c) at ((r / 16) * (K / 32) + c / 32) * 512 + (r % 16) * 32 + c % 32
+    import numpy as np
+    from util import unblock16
+    R, K = 37, 96
+    a = np.arange(R * K).reshape(R, K)
+    R16 = (R + 15) // 16 * 16
+    flat = np.full(R16 * K, -1)
+    for r in range(R):
+        for c in range(K):
+            flat[((r // 16) * (K // 32) + c // 32) * 512 + (r % 16) * 32 + c % 32] = a[r, c]
+    np.testing.assert_array_equal(unblock16(flat.reshape(R16, K), R), a)
+    assert moe.blocked_rows(37) == 48 and moe.blocked_rows(48) == 48 and moe.blocked_rows(0) == 0

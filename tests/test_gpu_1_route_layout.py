@@ -10,7 +10,7 @@ import torch
 import combine_router_softmax_amd as moe
 from oracle import COMPACT, PADDED, dispatch, dispatch_layout, route_topk, worst_case_rows
 from synth import get_config, make_routing_inputs, make_x, tiny_config
-from util import f64, flush, i64, rel_l2
+from util import f64, flush, i64, rel_l2, unblock16
 
 pytestmark = pytest.mark.gpu
 
@@ -180,3 +180,47 @@ def test_dispatch_full_size(name):
     tok = torch.from_numpy(ref["row_token"][:M]).cuda()
     # every occupied row is a bit copy of its token's row
     assert torch.equal(xe[:M].view(torch.int16), x[tok].view(torch.int16))
+
+
+# the 16-row blocked layout (rows x 32-column blocks of 1 KiB)
+@pytest.mark.parametrize("layout", [COMPACT, PADDED])
+@pytest.mark.parametrize("seed", range(4))
+def test_dispatch_blocked_tiny_bit_exact(seed, layout):
+    cfg = get_config("tiny", act="bf16")
+    d = make_routing_inputs(cfg, seed)
+    x = make_x(cfg, seed, d["src_offsets"]).cuda()
+    idx, _ = route_topk(d["logits"], cfg.top_k)
+    N = len(idx)
+    cap = worst_case_rows(N, 2, 2) if layout == COMPACT else int(np.diff(d["src_offsets"]).max())
+    ref = dispatch_layout(idx, d["src_offsets"], 0, 2, layout, cap)
+    R = ref["rows"]
+    row_token = torch.from_numpy(ref["row_token"].astype(np.int32)).cuda()
+    n_used = torch.tensor([int(ref["expert_off"][-1]) if layout == COMPACT else R], dtype=torch.int32, device="cuda")
+    xe = torch.full((moe.blocked_rows(R), cfg.hidden), 7.5, dtype=torch.bfloat16, device="cuda")
+    moe.moe_dispatch_blocked(x, row_token, R, n_used, xe)
+    rows = unblock16(xe, R)
+    occ = torch.from_numpy(ref["row_token"] >= 0).cuda()
+    tok = torch.from_numpy(np.maximum(ref["row_token"], 0)).cuda()
+    assert torch.equal(rows[occ].view(torch.int16), x[tok][occ].view(torch.int16))
+    assert torch.all(rows[~occ] == 7.5)   # holes and rows past n_used untouched
+    # without a device row count every row is visited; the result is the same
+    xe2 = torch.full_like(xe, 7.5)
+    moe.moe_dispatch_blocked(x, row_token, R, None, xe2)
+    assert torch.equal(xe.view(torch.int16), xe2.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["dsv3_prefill_ep8", "dsv3_decode_ep128"])
+def test_dispatch_blocked_full_size(name):
+    cfg = get_config(name)
+    flush(f"dispatch blocked {name}")
+    d = make_routing_inputs(cfg, 0)
+    idx, _ = route_topk(d["logits"], cfg.top_k)
+    N = len(idx)
+    ref = dispatch_layout(idx, d["src_offsets"], 0, cfg.n_local, COMPACT, worst_case_rows(N, 8, cfg.n_local))
+    x = make_x(cfg, 0, d["src_offsets"]).cuda()
+    M = int(ref["expert_off"][-1])
+    row_token = torch.from_numpy(ref["row_token"].astype(np.int32)).cuda()
+    n_used = torch.tensor([M], dtype=torch.int32, device="cuda")
+    xe = moe.moe_dispatch_blocked(x, row_token, ref["rows"], n_used)
+    tok = torch.from_numpy(ref["row_token"][:M]).cuda()
+    assert torch.equal(unblock16(xe, M).view(torch.int16), x[tok].view(torch.int16))

@@ -14,7 +14,7 @@ from combine_router_softmax_amd.layer import MoEShare
 from oracle import (COMPACT, PADDED, combine, dispatch, dispatch_layout, group_rows, grouped_ffn, moe_layer,
                     route_topk, swiglu_ffn, worst_case_rows)
 from synth import get_config, make_expert_weights, make_inputs, make_routing_inputs, tiny_config
-from util import f64, flush, i64, rel_l2, weights_f64
+from util import f64, flush, i64, rel_l2, unblock16, weights_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -125,6 +125,27 @@ def test_gemm_wide_tiles(layout, ms):
     kw["policy"] = moe.GEMM_STREAM_K
     moe.moe_grouped_gemm(a.cuda(), dw["w13"], dw["w2"], **kw)
     assert rel_l2(f64(kw["y"]), f64(y_wide)) <= 4e-3
+
+
+# Routed rows in the 16-row blocked layout give the same bits as row-major
+# rows, through both kernels (the layout only changes addresses).
+@pytest.mark.parametrize("policy", [moe.GEMM_WIDE, moe.GEMM_STREAM_K])
+@pytest.mark.parametrize("layout", [COMPACT, PADDED])
+def test_gemm_blocked_rows_match_row_major(layout, policy):
+    cfg = get_config("dsv3_prefill_ep8", hidden=1024, inter=512)
+    ms = [129, 0, 300, 17, 260]
+    got, ref, (a, dw, kw) = _gemm_case(cfg, ms, layout, seed=11, policy=policy)
+    y_rm = kw["y"].clone()
+    R = a.shape[0]
+    R16 = moe.blocked_rows(R)
+    ab = torch.zeros((R16, 1024), dtype=torch.bfloat16)
+    ab[:R] = a
+    blk = ab.reshape(R16 // 16, 16, 1024 // 32, 32).permute(0, 2, 1, 3).contiguous().reshape(R16, 1024)
+    assert torch.equal(unblock16(blk, R), a)
+    kw["y"].fill_(3.0)
+    moe.moe_grouped_gemm(blk.cuda(), dw["w13"], dw["w2"], a_layout=moe.ACT_BLOCKED16, rows=R, **kw)
+    assert torch.equal(kw["y"].view(torch.int16), y_rm.view(torch.int16))
+    assert rel_l2(got, ref) <= 8e-3
 
 
 @pytest.mark.parametrize("layout", [COMPACT, PADDED])

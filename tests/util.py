@@ -32,3 +32,14 @@ def weights_f64(wd: dict, g: int):
 
 def flush(msg: str):
     print(msg, flush=True)
+
+
+def unblock16(t, rows: int):
+    """Row-major [rows, K] view of a matrix in the 16-row blocked layout (blocks
+    of 16 rows x 32 columns stored contiguously, a row group's blocks in column
+    order); works on torch tensors and NumPy arrays."""
+    r16 = (rows + 15) // 16 * 16
+    K = t.shape[1]
+    b = t[:r16].reshape(r16 // 16, K // 32, 16, 32)
+    b = b.permute(0, 2, 1, 3) if hasattr(b, "permute") else b.transpose(0, 2, 1, 3)
+    return b.reshape(r16, K)[:rows]
