@@ -13,7 +13,7 @@ from typing import Optional
 
 import torch
 
-from . import (ACT_BLOCKED16, ACT_ROWS, COMPACT, GG_DOWN, GG_FULL, GG_UP, PADDED, W_PACKED, W_ROWMAJOR, SharedExpert,
+from . import (ACT_BLOCKED16, ACT_ROWS, COMPACT, GEMM_AUTO, GEMM_STREAM_K, GG_DOWN, GG_FULL, GG_UP, PADDED, W_PACKED, W_ROWMAJOR, SharedExpert,
                blocked_rows, gemm_desc, moe_combine, moe_dispatch, moe_dispatch_blocked, moe_dispatch_layout,
                moe_grouped_gemm, moe_grouped_gemm_workspace, moe_layout_rows, moe_pack_weights, moe_route_topk)
 
@@ -43,6 +43,8 @@ class MoEShare:
             blocked = n_tokens * top_k >= 128 * n_experts
         self.blocked = bool(blocked) and act_dtype == torch.bfloat16 and hidden % 32 == 0
         self.a_layout = ACT_BLOCKED16 if self.blocked else ACT_ROWS
+        # decode-sized batches never make enough wide tiles: skip that launch
+        self.policy = GEMM_AUTO if self.blocked else GEMM_STREAM_K
         d = self.dev
         self.topk_idx = torch.empty((n_tokens, top_k), dtype=torch.int32, device=d)
         self.topk_w = torch.empty((n_tokens, top_k), dtype=torch.float32, device=d)
@@ -77,7 +79,7 @@ class MoEShare:
         B0 = self.self_hi - self.self_lo
         se = SharedExpert(rows=B0 if self.sw is not None else 0)
         desc = gemm_desc(self.L, self.H, self.I, self.act_dtype, wdt, self.layout, self.S, self.capacity, self.R,
-                         shared=se, w_format=self.w_format, a_layout=self.a_layout)
+                         shared=se, w_format=self.w_format, a_layout=self.a_layout, policy=self.policy)
         self.ws = torch.zeros(moe_grouped_gemm_workspace(desc), dtype=torch.uint8, device=self.dev)
         if self.sw is not None:
             sdesc = gemm_desc(1, self.H, self.I, self.act_dtype, self.sw["w13"].dtype, COMPACT, 1, 0, max(B0, 1),
@@ -114,7 +116,7 @@ class MoEShare:
                          counts=self.lay["counts"], s13=w.get("s13"), s2=w.get("s2"), layout=self.layout,
                          n_src=self.S, capacity=self.capacity, stage=stage, y=self.ye[: self.R], ws=self.ws,
                          shared=None if x is None else self._shared_arg(x), w_format=self.w_format,
-                         a_layout=self.a_layout, rows=self.R)
+                         a_layout=self.a_layout, rows=self.R, policy=self.policy)
 
     def shared_gemm(self, x, stage=GG_FULL):
         if self.sw is None or self.self_hi <= self.self_lo:
