@@ -63,7 +63,7 @@ constexpr int kWM = 256;             // activation rows per wide tile
 constexpr int kWK = 32;              // reduction depth per LDS stage (32 or 64)
 constexpr int kWideGrid = 256;       // one workgroup per compute unit
 constexpr int kWideMinRows = 128;    // a group with at least this many rows may take the wide kernel ...
-constexpr int kWideMinTiles = 128;   // ... if the launch then has at least this many wide tiles
+constexpr int kWideMinTiles = 16;    // ... if the launch then has at least this many wide tiles
 constexpr int kNoWide = 0x7fffffff;  // wide_min when the wide kernel is not used
 
 struct GemmArgs {
@@ -119,11 +119,11 @@ struct Sched {
 // [0, rows)), then the exclusive prefix of tiles per group. Schedule order:
 // the shared expert first (its rows are always present, so its tiles start
 // with the first wave of workgroups instead of forming a tail), then the
-// routed experts. Only groups on the kernel's side get tiles: a group is wide
-// if m >= wide_min and the wide groups together make at least wide_min_tiles
-// wide tiles (fewer would leave most compute units idle; the stream-K kernel
-// then takes them). Both kernels evaluate this identically from the same
-// counts. Returns the tile count. All threads must call it.
+// routed experts. Only groups on the kernel's side get tiles: the launch goes
+// wide if the groups with m >= wide_min make at least wide_min_tiles wide
+// tiles, and then every group is wide; otherwise the stream-K kernel takes
+// them all. Both kernels evaluate this identically from the same counts.
+// Returns the tile count. All threads must call it.
 __device__ int build_schedule(const GemmArgs& p, int bm, int ntn, bool wide, Sched& sh) {
   const int tid = threadIdx.x;
   const int nsh = p.sh_rows > 0 ? 1 : 0;
@@ -154,7 +154,9 @@ __device__ int build_schedule(const GemmArgs& p, int bm, int ntn, bool wide, Sch
     if (wt) atomicAdd(&sh.wide_tiles, wt);
     __syncthreads();
   }
-  const int wide_min = sh.wide_tiles >= p.wide_min_tiles ? p.wide_min : kNoWide;
+  // once the launch qualifies, every group takes the wide kernel (one launch
+  // does all the work; small groups are cheap ragged tiles there)
+  const int wide_min = sh.wide_tiles >= p.wide_min_tiles ? 1 : kNoWide;
   for (int g = tid; g < Gt; g += kGemmThreads) {
     const int m = sh.m[g];
     sh.tile_start[g] = ((m >= wide_min) == wide) ? (m + bm - 1) / bm * ntn : 0;
@@ -291,16 +293,25 @@ __device__ __forceinline__ bf16x8_t fp8x8_dequant(uint32_t w0, uint32_t w1, floa
 // covered by one workgroup is finished in place; a tile cut by a range
 // boundary leaves fp32 partial sums (in accumulator-register order) in the
 // workspace, and ffn_fixup_kernel adds them in workgroup order and finishes
-// the tile. No workgroup ever waits for another.
+// the tile. No workgroup ever waits for another. When the launch has little
+// work, fewer ranges are used (at least kSkMinChunks chunks each), so the
+// partial sums stay small next to the weights streamed.
 constexpr int kSkGrid = 512;                          // 2 resident workgroups x 256 compute units
 constexpr int kXcds = 8;                              // accelerator complex dies of MI355X
 constexpr int kPartFloats = 4 * kMB * 16 * kWave;     // one workgroup's accumulators (64 KiB)
+constexpr int kSkMinChunks = 8;
 
-__host__ __device__ inline int64_t sk_start(int b, int64_t total) { return int64_t(b) * total / kSkGrid; }
+// Ranges used for a launch of `total` iterations: a multiple of the XCD count.
+__device__ inline int sk_grid(int64_t total) {
+  const int64_t g = total / kSkMinChunks / kXcds * kXcds;
+  return int(max<int64_t>(kXcds, min<int64_t>(kSkGrid, g)));
+}
 
-// Workgroup whose range holds iteration i (the last one, if several start there).
-__device__ inline int sk_owner(int64_t i, int64_t total) {
-  return int(((i + 1) * kSkGrid + total - 1) / total) - 1;
+__host__ __device__ inline int64_t sk_start(int b, int64_t total, int G) { return int64_t(b) * total / G; }
+
+// Range whose span holds iteration i (the last one, if several start there).
+__device__ inline int sk_owner(int64_t i, int64_t total, int G) {
+  return int(((i + 1) * G + total - 1) / total) - 1;
 }
 
 // Partial slot of workgroup b: 0 for its first tile, 1 for its last.
@@ -499,7 +510,9 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const TileRun& tr, c
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) dst[((wv * kMB + b) * 16 + v) * kWave + lane] = acc[b][v];
+      for (int v = 0; v < 16; v += 4)  // [wave][block][quad][lane][4]: 1 KiB contiguous per store
+        *reinterpret_cast<float4*>(dst + (((wv * kMB + b) * 4 + v / 4) * kWave + lane) * 4) =
+            make_float4(acc[b][v], acc[b][v + 1], acc[b][v + 2], acc[b][v + 3]);
   }
 }
 
@@ -521,8 +534,10 @@ __global__ __launch_bounds__(kGemmThreads, 2) void ffn_mfma_kernel(GemmArgs p, f
   // XCDs, so range r goes to workgroup (r % 64) * 8 + r / 64; consecutive
   // ranges (the N tiles of one expert, which share its activation rows) then
   // run on one XCD and its L2 fetches those rows once.
-  const int rng = int(blockIdx.x % kXcds) * (kSkGrid / kXcds) + int(blockIdx.x / kXcds);
-  const int64_t i0 = sk_start(rng, total), i1 = sk_start(rng + 1, total);
+  const int G = sk_grid(total);
+  if (int(blockIdx.x) >= G) return;  // uniform
+  const int rng = int(blockIdx.x % kXcds) * (G / kXcds) + int(blockIdx.x / kXcds);
+  const int64_t i0 = sk_start(rng, total, G), i1 = sk_start(rng + 1, total, G);
   if (i0 >= i1) return;  // uniform
   const int t_first = int(i0 / nchunks), t_last = int((i1 - 1) / nchunks);
 
@@ -593,30 +608,43 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_fixup_kernel(GemmArgs p, con
   const int nchunks = p.K / kKC;
   const int64_t total = int64_t(n_tiles) * nchunks;
   const int j = blockIdx.x;
-  const int64_t ib = sk_start(j + 1, total);
+  const int G = sk_grid(total);
+  if (j + 1 >= G) return;  // uniform: boundaries lie between ranges 0 .. G-1
+  const int64_t ib = sk_start(j + 1, total, G);
   if (ib <= 0 || ib >= total || ib % nchunks == 0) return;  // not inside a tile
   const int t = int(ib / nchunks);
-  if (j > 0 && sk_start(j, total) > int64_t(t) * nchunks) return;  // an earlier boundary owns this tile
+  if (j > 0 && sk_start(j, total, G) > int64_t(t) * nchunks) return;  // an earlier boundary owns this tile
   const Tile tl = decode_tile(p, BMT, p.n_tiles_n, sh, t);
   build_rowmap(p, tl, BMT, sh);
   const int nb = (tl.nrows + 31) / 32;
-  const int b_lo = sk_owner(int64_t(t) * nchunks, total);
-  const int b_hi = sk_owner(int64_t(t + 1) * nchunks - 1, total);
+  const int b_lo = sk_owner(int64_t(t) * nchunks, total, G);
+  const int b_hi = sk_owner(int64_t(t + 1) * nchunks - 1, total, G);
   f32x16_t acc[kMB];
 #pragma unroll
   for (int b = 0; b < kMB; ++b)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
   for (int w = b_lo; w <= b_hi; ++w) {
-    const int64_t s0 = sk_start(w, total), s1 = sk_start(w + 1, total);
+    const int64_t s0 = sk_start(w, total, G), s1 = sk_start(w + 1, total, G);
     if (s0 >= s1) continue;  // empty range
     const float* src = sk_slot(const_cast<float*>(parts), w, int(s0 / nchunks) == t ? 0 : 1);
+    // all of this partial's loads first (16 bytes per lane, 1 KiB per wave), then the adds
+    float4 ld[kMB][4];
 #pragma unroll
-    for (int b = 0; b < kMB; ++b) {
-      if (b >= nb) continue;
+    for (int b = 0; b < kMB; ++b)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[b][v] += src[((wv * kMB + b) * 16 + v) * kWave + lane];
-    }
+      for (int i = 0; i < 4; ++i)
+        ld[b][i] = b < nb ? *reinterpret_cast<const float4*>(src + (((wv * kMB + b) * 4 + i) * kWave + lane) * 4)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int b = 0; b < kMB; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[b][4 * i] += ld[b][i].x;
+        acc[b][4 * i + 1] += ld[b][i].y;
+        acc[b][4 * i + 2] += ld[b][i].z;
+        acc[b][4 * i + 3] += ld[b][i].w;
+      }
   }
   uint16_t* out = static_cast<uint16_t*>(tl.shared ? p.sh_out : p.out);
   ffn_epilogue<KIND, kMB>(acc, tl, nb, sh, out, p.n_out, wv, lr, lh, p.out_blk);
@@ -673,15 +701,62 @@ struct WideLds {
   uint16_t* x[4];
 };
 
+// One wide tile's accumulators: 4 waves x (gate/up or two output halves) x 8
+// activation blocks x 16 registers x 64 lanes.
+constexpr int kWidePart = 4 * 2 * 8 * 16 * kWave;
+// [wave][a][block][quad q][lane][4 floats]: registers 4q..4q+3 of one
+// accumulator tile, 16 bytes per lane, 1 KiB contiguous per wave access
+__device__ __forceinline__ int wide_part_idx(int wv, int a, int b, int q, int lane) {
+  return ((((wv * 2 + a) * 8 + b) * 4 + q) * kWave + lane) * 4;
+}
+
+// Epilogue of one 32-row activation block b of a wide tile from its two
+// accumulator tiles (up: gate and up rows of the same h columns; down: the two
+// 32-row halves of the wave's 64 output columns).
+template <int KIND>
+__device__ __forceinline__ void wide_epilogue_block(const GemmArgs& p, const Tile& tl, const Sched& sh, int b,
+                                                    const f32x16_t& a0, const f32x16_t& a1, int wv, int lr, int lh) {
+  const int phys = sh.rowmap[32 * b + lr];
+  if (phys < 0) return;
+  uint16_t* out = static_cast<uint16_t*>(tl.shared ? p.sh_out : p.out);
+  const bool oblk = p.out_blk;
+  uint16_t* orow = out + act_off(phys, 0, p.n_out, oblk);
+  if (KIND == kUp) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float h[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) h[r] = silu_f(a0[4 * q + r]) * a1[4 * q + r];
+      const int col = tl.nt * 128 + 32 * wv + 8 * q + 4 * lh;
+      *reinterpret_cast<uint2*>(orow + (oblk ? size_t(col >> 5) * 512 + (col & 31) : size_t(col))) =
+          make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+    }
+  } else {
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const f32x16_t& ac = a ? a1 : a0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = tl.nt * 256 + 64 * wv + 32 * a + 8 * q + 4 * lh;
+        *reinterpret_cast<uint2*>(orow + (oblk ? size_t(col >> 5) * 512 + (col & 31) : size_t(col))) =
+            make_uint2(pack_bf16x2(ac[4 * q], ac[4 * q + 1]), pack_bf16x2(ac[4 * q + 2], ac[4 * q + 3]));
+      }
+    }
+  }
+}
+
+// Stages [s_begin, s_end) of one wide tile (a multiple of the ring depth).
+// part == nullptr: the range is the whole tile, run the epilogue; else leave
+// the fp32 accumulators in part for ffn_wide_fixup_kernel.
 template <int KIND, bool PACKED, int NB>
-__device__ __forceinline__ void wide_tile(const GemmArgs& p, const Tile& tl, const Sched& sh, const WideLds& L) {
+__device__ __forceinline__ void wide_tile(const GemmArgs& p, const Tile& tl, const Sched& sh, const WideLds& L,
+                                          int s_begin, int s_end, float* __restrict__ part) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
   const int lr = lane & 31;
   const int lh = lane >> 5;
-  const int nk = p.K / kWK;
-  const int last = nk - 1;
+  const int last = s_end - 1;
   const uint16_t* A = static_cast<const uint16_t*>(tl.shared ? p.sh_a : p.a);
   const uint16_t* W = static_cast<const uint16_t*>(tl.shared ? p.sh_w : p.w);
 
@@ -788,7 +863,7 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& p, const Tile& tl, con
   // prologue: stages 0 .. kWStages-2 in flight, wait for stage 0
   constexpr int NS = kWK / 16;  // 16-deep MFMA steps per stage
 #pragma unroll
-  for (int st = 0; st < kWStages - 1; ++st) MOE_WIDE_ISSUE(min(st, last), st)
+  for (int st = 0; st < kWStages - 1; ++st) MOE_WIDE_ISSUE(min(s_begin + st, last), st)
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((kWStages - 2) * P));
   __builtin_amdgcn_s_barrier();
   MOE_WIDE_FRAGS(0, L.w[0], L.x[0], 0)
@@ -828,8 +903,8 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& p, const Tile& tl, con
     __builtin_amdgcn_sched_barrier(0);                                                                      \
   }
   static_assert(NS == 2, "the stage body is written for two 16-deep steps");
-  // the stage count is a multiple of kWStages (K is a multiple of 128)
-  for (int kt = 0; kt < nk; kt += kWStages) {
+  // the stage count is a multiple of kWStages (ranges are whole 128-deep chunks)
+  for (int kt = s_begin; kt < s_end; kt += kWStages) {
     MOE_WIDE_STAGE(0, kt)
     MOE_WIDE_STAGE(1, kt + 1)
     if constexpr (kWStages == 4) {
@@ -846,38 +921,48 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& p, const Tile& tl, con
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
   __builtin_amdgcn_s_barrier();
 
-  uint16_t* out = static_cast<uint16_t*>(tl.shared ? p.sh_out : p.out);
-  const bool oblk = p.out_blk;
+  if (part == nullptr) {
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int phys = sh.rowmap[32 * b + lr];
-    if (phys < 0) continue;
-    uint16_t* orow = out + act_off(phys, 0, p.n_out, oblk);
-    if (KIND == kUp) {
+    for (int b = 0; b < NB; ++b) wide_epilogue_block<KIND>(p, tl, sh, b, acc[0][b], acc[1][b], wv, lr, lh);
+  } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float h[4];
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) h[r] = silu_f(acc[0][b][4 * q + r]) * acc[1][b][4 * q + r];
-        const int col = tl.nt * 128 + 32 * wv + 8 * q + 4 * lh;
-        *reinterpret_cast<uint2*>(orow + (oblk ? size_t(col >> 5) * 512 + (col & 31) : size_t(col))) =
-            make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
-      }
-    } else {
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = tl.nt * 256 + 64 * wv + 32 * a + 8 * q + 4 * lh;
-          *reinterpret_cast<uint2*>(orow + (oblk ? size_t(col >> 5) * 512 + (col & 31) : size_t(col))) = make_uint2(pack_bf16x2(acc[a][b][4 * q], acc[a][b][4 * q + 1]),
-                                                             pack_bf16x2(acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]));
-        }
-    }
+        for (int v = 0; v < 16; v += 4)
+          *reinterpret_cast<float4*>(part + wide_part_idx(wv, a, b, v / 4, lane)) =
+              make_float4(acc[a][b][v], acc[a][b][v + 1], acc[a][b][v + 2], acc[a][b][v + 3]);
   }
 }
 
+// Work split of the wide kernel (kWideGrid workgroups, one per compute unit):
+// whole tiles in full rounds, tile r * kWideGrid + (XCD-blocked slot of the
+// workgroup), so the 32 workgroups of an XCD work on 32 consecutive tiles of
+// the blocked order; then the last n_tiles % kWideGrid tiles are split along
+// K into S equal chunk ranges each (S as large as the idle workgroups allow,
+// at least kWideMinChunks chunks per range), so a launch with few tiles (a
+// decode batch with few experts per GPU) still keeps the compute units busy.
+// A split leaves fp32 partials (one slot per workgroup); ffn_wide_fixup_kernel
+// adds the S partials of a tile in split order and runs the epilogue.
+constexpr int kWideMinChunks = 4;
+
+struct WideSplit {
+  int full;   // tiles done whole, in full rounds
+  int rem;    // tiles split along K
+  int S;      // ranges per split tile
+};
+
+__device__ inline WideSplit wide_split(int n_tiles, int nch) {
+  WideSplit w;
+  w.full = n_tiles / kWideGrid * kWideGrid;
+  w.rem = n_tiles - w.full;
+  w.S = w.rem ? max(1, min(kWideGrid / w.rem, nch / kWideMinChunks)) : 1;
+  return w;
+}
+
 template <int KIND, bool PACKED>
-__global__ __launch_bounds__(kGemmThreads, 1) void ffn_wide_kernel(GemmArgs p) {
+__global__ __launch_bounds__(kGemmThreads, 1) void ffn_wide_kernel(GemmArgs p, float* __restrict__ parts) {
   __shared__ Sched sh;
   constexpr int kExtra = kWStages == 4 ? kWStage : 8;  // buffers 2 and 3 exist with a 4-deep ring only
   __shared__ __attribute__((aligned(1024))) uint16_t w0[kWStage], w1[kWStage], w2[kExtra], w3[kExtra];
@@ -885,23 +970,89 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_wide_kernel(GemmArgs p) {
   const WideLds L = {{w0, w1, w2, w3}, {x0, x1, x2, x3}};
   const int ntn = KIND == kUp ? p.n_out / 128 : p.n_out / 256;
   const int n_tiles = build_schedule(p, kWM, ntn, true, sh);
-  const int per_xcd = int(gridDim.x) / kXcds;
-  const int first = int(blockIdx.x % kXcds) * per_xcd + int(blockIdx.x / kXcds);
-  for (int t = first; t < n_tiles; t += gridDim.x) {
+  const int nch = p.K / kKC;  // 128-deep chunks per tile
+  constexpr int SPC = kKC / kWK;  // stages per chunk
+  const WideSplit ws = wide_split(n_tiles, nch);
+  const int slot = int(blockIdx.x % kXcds) * (kWideGrid / kXcds) + int(blockIdx.x / kXcds);
+  auto run = [&](int t, int c_begin, int c_end, float* part) __attribute__((always_inline)) {
     const Tile tl = decode_tile<true>(p, kWM, ntn, sh, t);
     build_rowmap(p, tl, kWM, sh);
+    const int sb = c_begin * SPC, se = c_end * SPC;
     switch ((tl.nrows + 31) / 32) {
-      case 1: wide_tile<KIND, PACKED, 1>(p, tl, sh, L); break;
-      case 2: wide_tile<KIND, PACKED, 2>(p, tl, sh, L); break;
-      case 3: wide_tile<KIND, PACKED, 3>(p, tl, sh, L); break;
-      case 4: wide_tile<KIND, PACKED, 4>(p, tl, sh, L); break;
-      case 5: wide_tile<KIND, PACKED, 5>(p, tl, sh, L); break;
-      case 6: wide_tile<KIND, PACKED, 6>(p, tl, sh, L); break;
-      case 7: wide_tile<KIND, PACKED, 7>(p, tl, sh, L); break;
-      default: wide_tile<KIND, PACKED, 8>(p, tl, sh, L); break;
+      case 1: wide_tile<KIND, PACKED, 1>(p, tl, sh, L, sb, se, part); break;
+      case 2: wide_tile<KIND, PACKED, 2>(p, tl, sh, L, sb, se, part); break;
+      case 3: wide_tile<KIND, PACKED, 3>(p, tl, sh, L, sb, se, part); break;
+      case 4: wide_tile<KIND, PACKED, 4>(p, tl, sh, L, sb, se, part); break;
+      case 5: wide_tile<KIND, PACKED, 5>(p, tl, sh, L, sb, se, part); break;
+      case 6: wide_tile<KIND, PACKED, 6>(p, tl, sh, L, sb, se, part); break;
+      case 7: wide_tile<KIND, PACKED, 7>(p, tl, sh, L, sb, se, part); break;
+      default: wide_tile<KIND, PACKED, 8>(p, tl, sh, L, sb, se, part); break;
     }
     __syncthreads();  // rowmap is rewritten by the next tile
+  };
+  for (int t = slot; t < ws.full; t += kWideGrid) run(t, 0, nch, nullptr);
+  const int u = int(blockIdx.x);  // split unit: tile full + u / S, range u % S
+  if (ws.rem && u < ws.rem * ws.S) {
+    const int t = ws.full + u / ws.S, k = u % ws.S;
+    if (ws.S == 1) {
+      run(t, 0, nch, nullptr);
+    } else {
+      run(t, k * nch / ws.S, (k + 1) * nch / ws.S, parts + size_t(u) * kWidePart);
+    }
   }
+}
+
+// Finishes the split wide tiles: block (i, b) sums the S partials of split
+// tile i for activation block b in split order and runs its epilogue.
+template <int KIND>
+__global__ __launch_bounds__(kGemmThreads) void ffn_wide_fixup_kernel(GemmArgs p, const float* __restrict__ parts) {
+  __shared__ Sched sh;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
+  const int lr = lane & 31;
+  const int lh = lane >> 5;
+  const int ntn = KIND == kUp ? p.n_out / 128 : p.n_out / 256;
+  const int n_tiles = build_schedule(p, kWM, ntn, true, sh);
+  const int nch = p.K / kKC;
+  const WideSplit ws = wide_split(n_tiles, nch);
+  const int i = blockIdx.x, b = blockIdx.y;
+  if (i >= ws.rem || ws.S == 1) return;  // uniform
+  const int t = ws.full + i;
+  const Tile tl = decode_tile<true>(p, kWM, ntn, sh, t);
+  if (b * 32 >= tl.nrows) return;  // uniform: no rows in this block
+  build_rowmap(p, tl, kWM, sh);
+  f32x16_t a0, a1;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) a0[v] = a1[v] = 0.f;
+  // two partials' loads in flight at a time (16 bytes per lane), then the adds
+  for (int k = 0; k < ws.S; k += 2) {
+    float4 ld[2][2][4];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const float* src = parts + size_t(i * ws.S + min(k + kk, ws.S - 1)) * kWidePart;
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) ld[kk][a][q] = *reinterpret_cast<const float4*>(src + wide_part_idx(wv, a, b, q, lane));
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      if (k + kk >= ws.S) break;  // uniform
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        a0[4 * q] += ld[kk][0][q].x;
+        a0[4 * q + 1] += ld[kk][0][q].y;
+        a0[4 * q + 2] += ld[kk][0][q].z;
+        a0[4 * q + 3] += ld[kk][0][q].w;
+        a1[4 * q] += ld[kk][1][q].x;
+        a1[4 * q + 1] += ld[kk][1][q].y;
+        a1[4 * q + 2] += ld[kk][1][q].z;
+        a1[4 * q + 3] += ld[kk][1][q].w;
+      }
+    }
+  }
+  wide_epilogue_block<KIND>(p, tl, sh, b, a0, a1, wv, lr, lh);
 }
 
 // ------------------------------------------------------------------ weight packing
@@ -1045,7 +1196,9 @@ static size_t h_bytes(const moe_ggemm_desc_t* d, int64_t rows) {
 }
 
 static size_t parts_bytes(const moe_ggemm_desc_t* d) {
-  return d->act_dt == MOE_F32 ? 0 : size_t(2) * kSkGrid * kPartFloats * sizeof(float);
+  // shared by the wide and the stream-K kernels, which run one after the other
+  const size_t sk = size_t(2) * kSkGrid * kPartFloats, wide = size_t(kWideGrid) * kWidePart;
+  return d->act_dt == MOE_F32 ? 0 : std::max(sk, wide) * sizeof(float);
 }
 
 MOE_API size_t moe_grouped_gemm_workspace(const moe_ggemm_desc_t* d) {
@@ -1080,10 +1233,15 @@ static moe_status_t launch_stage(const GemmArgs& p, bool f32, bool fp8, int kind
   }
   if (p.wide_min != kNoWide) {
     const dim3 wgrid(kWideGrid);
-#define MOE_WIDE(K, P) hipLaunchKernelGGL((ffn_wide_kernel<K, P>), wgrid, block, 0, stream, p)
+#define MOE_WIDE(K, P) hipLaunchKernelGGL((ffn_wide_kernel<K, P>), wgrid, block, 0, stream, p, parts)
     if (kind == kUp) { if (p.packed) MOE_WIDE(kUp, true); else MOE_WIDE(kUp, false); }
     else { if (p.packed) MOE_WIDE(kDown, true); else MOE_WIDE(kDown, false); }
 #undef MOE_WIDE
+    if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
+    // the partials are finished before the stream-K kernel reuses the buffer
+    const dim3 wfix(kWideGrid, 8);
+    if (kind == kUp) hipLaunchKernelGGL((ffn_wide_fixup_kernel<kUp>), wfix, block, 0, stream, p, parts);
+    else hipLaunchKernelGGL((ffn_wide_fixup_kernel<kDown>), wfix, block, 0, stream, p, parts);
     if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
   }
   const dim3 grid(kSkGrid), fix_grid(kSkGrid - 1);

@@ -193,10 +193,11 @@ typedef enum {
 
 /* Which kernel takes which expert group. Both compute the same products in
  * fp32 (the sum order differs, so results may differ in the last bits).
- * AUTO: groups of at least 128 rows take the 256 x 256 wide-tile kernel when
- * the launch then has at least 128 wide tiles (bf16 weights, hidden % 256 == 0),
- * all others the stream-K kernel. WIDE: every group takes the wide-tile kernel
- * where its shape and dtype allow. STREAM_K: never the wide-tile kernel. */
+ * AUTO: if the groups of at least 128 rows make at least 16 tiles of the
+ * 256 x 256 wide-tile kernel (bf16 weights, hidden % 256 == 0), every group
+ * of the launch takes that kernel, else every group takes the stream-K
+ * kernel (decided on the device from the counts). WIDE: every group takes the
+ * wide-tile kernel where its shape and dtype allow. STREAM_K: never. */
 typedef enum {
   MOE_GEMM_AUTO = 0,
   MOE_GEMM_WIDE = 1,
