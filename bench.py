@@ -178,6 +178,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="dsv3_decode_ep8")
     ap.add_argument("--layout", choices=["compact", "padded"], default="compact")
+    ap.add_argument("--xe-layout", choices=["auto", "rows", "blocked"], default="auto",
+                    help="storage of the expert rows (auto: the layer's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of replays of a HIP graph of one step")
@@ -220,7 +222,8 @@ def main(argv=None):
     act = torch.float32 if cfg.act == "f32" else torch.bfloat16
     share = MoEShare(n_tokens=N, hidden=cfg.hidden, inter=cfg.inter, n_experts=cfg.n_experts, top_k=cfg.top_k,
                      n_src=cfg.n_src, expert_lo=cfg.expert_lo, n_local=cfg.n_local, act_dtype=act, layout=layout,
-                     capacity=cap, self_range=(0, B0))
+                     capacity=cap, self_range=(0, B0),
+                     blocked=None if args.xe_layout == "auto" else args.xe_layout == "blocked")
     share.set_weights(d["routed"], d["shared"])
     logits = torch.from_numpy(d["logits"]).cuda()
     offs = torch.from_numpy(off).cuda()
@@ -325,7 +328,8 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "bf16" if cfg.act == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "layout": args.layout, "global_batch": N, "tokens_per_gpu": B0,
+        "config": {"workload": cfg.name, "layout": args.layout,
+                   "xe_layout": "blocked" if share.blocked else "rows", "global_batch": N, "tokens_per_gpu": B0,
                    "source_ranks": cfg.n_src, "hidden": cfg.hidden, "n_experts": cfg.n_experts,
                    "top_k": cfg.top_k, "local_experts": cfg.n_local, "shared_expert": cfg.shared,
                    "inter": cfg.inter, "weights": cfg.weight, "parallelism": f"ep{cfg.n_experts // cfg.n_local}"},

@@ -74,7 +74,7 @@ _SIGNATURES = {
     "moe_dispatch_layout_workspace": (_SZ, [ctypes.POINTER(LayoutDesc)]),
     "moe_dispatch_layout": (_I, [ctypes.POINTER(LayoutDesc), _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_dispatch": (_I, [_P, _I, _I, _I, _I, _P, _I64, _P, _P]),
-    "moe_dispatch_blocked": (_I, [_P, _I, _I, _I, _P, _I64, _P, _P, _P]),
+    "moe_dispatch_blocked": (_I, [_P, _I, _I, _I, _I, _P, _I64, _P, _P]),
     "moe_grouped_gemm_workspace": (_SZ, [ctypes.POINTER(GGemmDesc)]),
     "moe_grouped_gemm": (_I, [ctypes.POINTER(GGemmDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_combine": (_I, [_P, _I, _I64, _P, _P, _I, _I, _I, _P, _I, _I, _P, _P]),
@@ -220,23 +220,20 @@ def blocked_rows(n_rows: int) -> int:
     return (n_rows + 15) // 16 * 16
 
 
-def moe_dispatch_blocked(x: torch.Tensor, row_token: torch.Tensor, n_rows: int, n_used: Optional[torch.Tensor] = None,
+def moe_dispatch_blocked(x: torch.Tensor, row_of: torch.Tensor, top_k: int, n_rows: int,
                          xe: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Copy token rows into the expert-grouped buffer in the 16-row blocked layout
-    (xe [blocked_rows(n_rows), H]; holes untouched). ``n_used`` is a device int32
-    row count (e.g. expert_off[n_local:]) or None for all rows."""
+    """Copy token rows into their expert-grouped slots in the 16-row blocked
+    layout (xe [blocked_rows(n_rows), H]; unused rows untouched)."""
     _dev(x, "x", torch.bfloat16)
-    _dev(row_token, "row_token", torch.int32)
+    _dev(row_of, "row_of", torch.int32)
     N, H = x.shape
     if xe is None:
         xe = torch.empty((blocked_rows(n_rows), H), dtype=x.dtype, device=x.device)
     _dev(xe, "xe", x.dtype)
     if xe.shape[0] < blocked_rows(n_rows):
         raise ValueError("xe must hold blocked_rows(n_rows) rows")
-    if n_used is not None:
-        _dev(n_used, "n_used", torch.int32)
-    _check(lib().moe_dispatch_blocked(_ptr(x), _act_code(x.dtype), N, H, _ptr(row_token), n_rows, _ptr(n_used),
-                                      _ptr(xe), _stream()), "moe_dispatch_blocked")
+    _check(lib().moe_dispatch_blocked(_ptr(x), _act_code(x.dtype), N, H, top_k, _ptr(row_of), n_rows, _ptr(xe),
+                                      _stream()), "moe_dispatch_blocked")
     return xe
 
 

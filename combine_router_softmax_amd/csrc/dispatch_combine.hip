@@ -20,15 +20,23 @@ namespace {
 constexpr int kVecThreads = 256;  // one 16-byte piece per thread, 4 KiB of a row per workgroup
 constexpr int kMaxK = 16;
 
-// Workgroup b handles 16-byte pieces [chunk * 256, chunk * 256 + 256) of token
-// t = b / n_chunks: the token's slots are uniform per workgroup (scalar loads),
-// every thread loads one piece and stores it to each slot.
-template <int KMAX>
+// Workgroup b handles PPT * 256 consecutive 16-byte pieces of token
+// t = b / n_chunks (thread i: pieces i, i + 256, ...): the token's slots are
+// uniform per workgroup (scalar loads); every thread has PPT loads in flight
+// and stores each piece to each slot.
+// BLOCKED: xe in the 16-row blocked layout (blocks of 16 rows x 32 columns,
+// 1 KiB each): piece c of row r (8 columns) goes to block (r / 16, c / 4),
+// row r % 16, 16-byte slot c % 4; four neighbouring lanes still write 64
+// contiguous bytes.
+constexpr int kDispatchPpt = 4;
+template <int KMAX, bool BLOCKED>
 __global__ __launch_bounds__(kVecThreads) void dispatch_kernel(const uint4* __restrict__ x, int row_vecs, int n_chunks,
-                                                                int top_k, const int32_t* __restrict__ row_of,
-                                                                int64_t n_rows, uint4* __restrict__ xe) {
+                                                                int n_tokens, int top_k,
+                                                                const int32_t* __restrict__ row_of, int64_t n_rows,
+                                                                uint4* __restrict__ xe) {
+  (void)n_tokens;
   const int t = blockIdx.x / n_chunks;
-  const int c = (blockIdx.x - t * n_chunks) * kVecThreads + threadIdx.x;
+  const int c0 = (blockIdx.x - t * n_chunks) * kVecThreads * kDispatchPpt + threadIdx.x;
   const int32_t* ro = row_of + size_t(t) * top_k;
   int r[KMAX];
   bool any = false;
@@ -38,45 +46,30 @@ __global__ __launch_bounds__(kVecThreads) void dispatch_kernel(const uint4* __re
     if (r[k] >= n_rows) r[k] = -1;
     any |= r[k] >= 0;
   }
-  if (!any || c >= row_vecs) return;
-  const uint4 v = x[size_t(t) * row_vecs + c];
+  if (!any || c0 >= row_vecs) return;
+  uint4 v[kDispatchPpt];
+#pragma unroll
+  for (int i = 0; i < kDispatchPpt; ++i)  // unconditional loads (a tail piece repeats a valid one)
+    v[i] = x[size_t(t) * row_vecs + min(c0 + i * kVecThreads, row_vecs - 1)];
+  // keep the pieces in registers: without this the compiler reloads each one
+  // from memory before every slot's store
+#pragma unroll
+  for (int i = 0; i < kDispatchPpt; ++i) asm volatile("" : "+v"(v[i].x), "+v"(v[i].y), "+v"(v[i].z), "+v"(v[i].w));
 #pragma unroll
   for (int k = 0; k < KMAX; ++k)
-    if (r[k] >= 0) xe[size_t(r[k]) * row_vecs + c] = v;
-}
-
-// Row-wise dispatch into the 16-row blocked layout: a unit of work is one
-// group of 16 output rows x 128 columns (four 1 KiB blocks, contiguous in xe).
-// Wave w reads rows 4w..4w+3 of the group, 256 contiguous bytes each, and
-// every lane stores its 16 bytes at their blocked position, so the workgroup
-// writes 4 KiB of contiguous memory. Persistent workgroups walk the units up
-// to the device-side row count.
-constexpr int kBlkCols = 128;  // columns per unit
-__global__ __launch_bounds__(kVecThreads) void dispatch_blocked_kernel(const uint4* __restrict__ x, int hidden,
-                                                                        int n_tokens,
-                                                                        const int32_t* __restrict__ row_token,
-                                                                        int64_t n_rows,
-                                                                        const int32_t* __restrict__ n_used,
-                                                                        uint16_t* __restrict__ xe) {
-  const int64_t rows = n_used ? min<int64_t>(max(n_used[0], 0), n_rows) : n_rows;
-  const int ncu = (hidden + kBlkCols - 1) / kBlkCols;  // column units per row group
-  const int64_t units = (rows + 15) / 16 * ncu;
-  const int tid = threadIdx.x;
-  const int ri = tid >> 4;         // row inside the group (wave w: rows 4w..4w+3)
-  const int piece = tid & 15;      // 16-byte piece inside the unit's 256 bytes of the row
-  const int row_vecs = hidden / 8;
-  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
-    const int64_t g = u / ncu;
-    const int cu = int(u - g * ncu);
-    const int64_t r = g * 16 + ri;
-    const int col = cu * kBlkCols + piece * 8;
-    if (r >= rows || col >= hidden) continue;
-    const int t = row_token[r];
-    if (t < 0 || t >= n_tokens) continue;  // a hole (or an invalid entry): not written
-    const uint4 v = x[size_t(t) * row_vecs + col / 8];
-    const size_t off = (size_t(g) * (hidden >> 5) + (col >> 5)) * 512 + size_t(ri) * 32 + (col & 31);
-    *reinterpret_cast<uint4*>(xe + off) = v;
-  }
+    if (r[k] >= 0) {
+#pragma unroll
+      for (int i = 0; i < kDispatchPpt; ++i) {
+        const int c = c0 + i * kVecThreads;
+        if (c >= row_vecs) continue;
+        if (BLOCKED) {
+          const size_t blk = size_t(r[k] >> 4) * size_t(row_vecs >> 2) + size_t(c >> 2);
+          xe[blk * 64 + size_t(r[k] & 15) * 4 + (c & 3)] = v[i];
+        } else {
+          xe[size_t(r[k]) * row_vecs + c] = v[i];
+        }
+      }
+    }
 }
 
 // 16-byte piece <-> floats
@@ -115,14 +108,16 @@ struct Vec<uint16_t> {
 // Same decomposition as dispatch: each thread owns one 16-byte piece of the
 // output row and sums the token's kept expert rows in k order (all K loads in
 // flight at once), plus the shared-expert row for the GPU's own tokens.
-template <typename T, int KMAX>
+// PPT pieces per thread (stride 256), all their loads in flight at once.
+template <typename T, int KMAX, int PPT>
 __global__ __launch_bounds__(kVecThreads) void combine_kernel(
     const uint4* __restrict__ ye, int64_t n_rows, const int32_t* __restrict__ row_of, const float* __restrict__ topk_w,
-    int top_k, int row_vecs, int n_chunks, const uint4* __restrict__ shared_y, int self_lo, int self_hi,
+    int n_tokens, int top_k, int row_vecs, int n_chunks, const uint4* __restrict__ shared_y, int self_lo, int self_hi,
     uint4* __restrict__ out) {
   constexpr int EPV = Vec<T>::N;
+  (void)n_tokens;
   const int t = blockIdx.x / n_chunks;
-  const int c = (blockIdx.x - t * n_chunks) * kVecThreads + threadIdx.x;
+  const int c0 = (blockIdx.x - t * n_chunks) * kVecThreads * PPT + threadIdx.x;
   const int32_t* ro = row_of + size_t(t) * top_k;
   const float* wo = topk_w + size_t(t) * top_k;
   int r[KMAX];
@@ -136,30 +131,38 @@ __global__ __launch_bounds__(kVecThreads) void combine_kernel(
     any |= r[k] >= 0;
   }
   const bool in_self = shared_y != nullptr && t >= self_lo && t < self_hi;
-  if ((!any && !in_self) || c >= row_vecs) return;
-  uint4 v[KMAX];
+  if ((!any && !in_self) || c0 >= row_vecs) return;
+  uint4 v[PPT][KMAX], vs[PPT];
 #pragma unroll
-  for (int k = 0; k < KMAX; ++k) v[k] = r[k] >= 0 ? ye[size_t(r[k]) * row_vecs + c] : make_uint4(0, 0, 0, 0);
-  const uint4 vs = in_self ? shared_y[size_t(t - self_lo) * row_vecs + c] : make_uint4(0, 0, 0, 0);
-  float acc[EPV];
+  for (int i = 0; i < PPT; ++i) {
+    const int c = min(c0 + i * kVecThreads, row_vecs - 1);  // a tail piece repeats a valid one
 #pragma unroll
-  for (int e = 0; e < EPV; ++e) acc[e] = 0.f;
+    for (int k = 0; k < KMAX; ++k) v[i][k] = r[k] >= 0 ? ye[size_t(r[k]) * row_vecs + c] : make_uint4(0, 0, 0, 0);
+    vs[i] = in_self ? shared_y[size_t(t - self_lo) * row_vecs + c] : make_uint4(0, 0, 0, 0);
+  }
 #pragma unroll
-  for (int k = 0; k < KMAX; ++k) {
-    if (r[k] >= 0) {
-      float f[EPV];
-      Vec<T>::load(v[k], f);
+  for (int i = 0; i < PPT; ++i) {
+    const int c = c0 + i * kVecThreads;
+    float acc[EPV];
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) acc[e] = fmaf(w[k], f[e], acc[e]);
+    for (int e = 0; e < EPV; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      if (r[k] >= 0) {
+        float f[EPV];
+        Vec<T>::load(v[i][k], f);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) acc[e] = fmaf(w[k], f[e], acc[e]);
+      }
     }
-  }
-  if (in_self) {
-    float f[EPV];
-    Vec<T>::load(vs, f);
+    if (in_self) {
+      float f[EPV];
+      Vec<T>::load(vs[i], f);
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) acc[e] += f[e];
+      for (int e = 0; e < EPV; ++e) acc[e] += f[e];
+    }
+    if (c < row_vecs) out[size_t(t) * row_vecs + c] = Vec<T>::store(acc);
   }
-  out[size_t(t) * row_vecs + c] = Vec<T>::store(acc);
 }
 
 }  // namespace
@@ -171,6 +174,9 @@ static bool row_dtype_ok(moe_dtype_t dt) { return dt == MOE_F32 || dt == MOE_BF1
 
 static int kmax_of(int top_k) { return top_k <= 2 ? 2 : top_k <= 4 ? 4 : top_k <= 8 ? 8 : 16; }
 
+// One workgroup per (token, chunk) unit.
+static unsigned vec_grid(int64_t units) { return unsigned(units > 0 ? units : 1); }
+
 MOE_API moe_status_t moe_dispatch(const void* x, moe_dtype_t dt, int n_tokens, int hidden, int top_k,
                                   const int32_t* row_of, int64_t n_rows, void* xe, hipStream_t stream) {
   if (n_tokens < 0 || hidden < 1 || top_k < 1 || n_rows < 0) return MOE_ERR_INVALID_ARG;
@@ -181,42 +187,53 @@ MOE_API moe_status_t moe_dispatch(const void* x, moe_dtype_t dt, int n_tokens, i
   if (n_tokens == 0 || n_rows == 0) return MOE_OK;
   if (!x || !row_of || !xe || !aligned16(x) || !aligned16(xe)) return MOE_ERR_INVALID_ARG;
   const int row_vecs = int(row_bytes / 16);
-  const int n_chunks = (row_vecs + kVecThreads - 1) / kVecThreads;
+  const int n_chunks = (row_vecs + kVecThreads * kDispatchPpt - 1) / (kVecThreads * kDispatchPpt);
   if (int64_t(n_chunks) * n_tokens >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
-  const dim3 grid(unsigned(n_chunks * n_tokens)), block(kVecThreads);
+  const dim3 grid(vec_grid(int64_t(n_chunks) * n_tokens)), block(kVecThreads);
   const uint4* xv = static_cast<const uint4*>(x);
   uint4* ov = static_cast<uint4*>(xe);
   switch (kmax_of(top_k)) {
-    case 2: hipLaunchKernelGGL(dispatch_kernel<2>, grid, block, 0, stream, xv, row_vecs, n_chunks, top_k, row_of, n_rows, ov); break;
-    case 4: hipLaunchKernelGGL(dispatch_kernel<4>, grid, block, 0, stream, xv, row_vecs, n_chunks, top_k, row_of, n_rows, ov); break;
-    case 8: hipLaunchKernelGGL(dispatch_kernel<8>, grid, block, 0, stream, xv, row_vecs, n_chunks, top_k, row_of, n_rows, ov); break;
-    default: hipLaunchKernelGGL(dispatch_kernel<16>, grid, block, 0, stream, xv, row_vecs, n_chunks, top_k, row_of, n_rows, ov); break;
+    case 2: hipLaunchKernelGGL((dispatch_kernel<2, false>), grid, block, 0, stream, xv, row_vecs, n_chunks, n_tokens, top_k, row_of, n_rows, ov); break;
+    case 4: hipLaunchKernelGGL((dispatch_kernel<4, false>), grid, block, 0, stream, xv, row_vecs, n_chunks, n_tokens, top_k, row_of, n_rows, ov); break;
+    case 8: hipLaunchKernelGGL((dispatch_kernel<8, false>), grid, block, 0, stream, xv, row_vecs, n_chunks, n_tokens, top_k, row_of, n_rows, ov); break;
+    default: hipLaunchKernelGGL((dispatch_kernel<16, false>), grid, block, 0, stream, xv, row_vecs, n_chunks, n_tokens, top_k, row_of, n_rows, ov); break;
   }
   return launch_status();
 }
 
-MOE_API moe_status_t moe_dispatch_blocked(const void* x, moe_dtype_t dt, int n_tokens, int hidden,
-                                          const int32_t* row_token, int64_t n_rows, const int32_t* n_used, void* xe,
-                                          hipStream_t stream) {
-  if (n_tokens < 0 || hidden < 1 || n_rows < 0) return MOE_ERR_INVALID_ARG;
+MOE_API moe_status_t moe_dispatch_blocked(const void* x, moe_dtype_t dt, int n_tokens, int hidden, int top_k,
+                                          const int32_t* row_of, int64_t n_rows, void* xe, hipStream_t stream) {
+  if (n_tokens < 0 || hidden < 1 || top_k < 1 || n_rows < 0) return MOE_ERR_INVALID_ARG;
   if (dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (top_k > kMaxK) return MOE_ERR_UNSUPPORTED;
   if (hidden % 32) return MOE_ERR_INVALID_ARG;
   if (n_tokens == 0 || n_rows == 0) return MOE_OK;
-  if (!x || !row_token || !xe || !aligned16(x) || !aligned16(xe)) return MOE_ERR_INVALID_ARG;
-  const int64_t units = (n_rows + 15) / 16 * ((hidden + kBlkCols - 1) / kBlkCols);
-  const int64_t cap = int64_t(device_cu_count()) * 8;  // 8 workgroups per compute unit
-  const dim3 grid(unsigned(units < cap ? units : cap)), block(kVecThreads);
-  hipLaunchKernelGGL(dispatch_blocked_kernel, grid, block, 0, stream, static_cast<const uint4*>(x), hidden, n_tokens,
-                     row_token, n_rows, n_used, static_cast<uint16_t*>(xe));
+  if (!x || !row_of || !xe || !aligned16(x) || !aligned16(xe)) return MOE_ERR_INVALID_ARG;
+  const int row_vecs = hidden / 8;
+  const int n_chunks = (row_vecs + kVecThreads * kDispatchPpt - 1) / (kVecThreads * kDispatchPpt);
+  if (int64_t(n_chunks) * n_tokens >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  const dim3 grid(vec_grid(int64_t(n_chunks) * n_tokens)), block(kVecThreads);
+  const uint4* xv = static_cast<const uint4*>(x);
+  uint4* ov = static_cast<uint4*>(xe);
+  switch (kmax_of(top_k)) {
+    case 2: hipLaunchKernelGGL((dispatch_kernel<2, true>), grid, block, 0, stream, xv, row_vecs, n_chunks, n_tokens, top_k, row_of, n_rows, ov); break;
+    case 4: hipLaunchKernelGGL((dispatch_kernel<4, true>), grid, block, 0, stream, xv, row_vecs, n_chunks, n_tokens, top_k, row_of, n_rows, ov); break;
+    case 8: hipLaunchKernelGGL((dispatch_kernel<8, true>), grid, block, 0, stream, xv, row_vecs, n_chunks, n_tokens, top_k, row_of, n_rows, ov); break;
+    default: hipLaunchKernelGGL((dispatch_kernel<16, true>), grid, block, 0, stream, xv, row_vecs, n_chunks, n_tokens, top_k, row_of, n_rows, ov); break;
+  }
   return launch_status();
 }
 
+// pieces per combine thread: 2 keeps up to 2 x 16 loads in flight within the
+// register budget
+constexpr int kCombinePpt = 2;
+
 template <typename T, int KMAX>
 static void launch_combine(dim3 grid, hipStream_t stream, const void* ye, int64_t n_rows, const int32_t* row_of,
-                           const float* topk_w, int top_k, int row_vecs, int n_chunks, const void* shared_y,
+                           const float* topk_w, int n_tokens, int top_k, int row_vecs, int n_chunks, const void* shared_y,
                            int self_lo, int self_hi, void* out) {
-  hipLaunchKernelGGL((combine_kernel<T, KMAX>), grid, dim3(kVecThreads), 0, stream, static_cast<const uint4*>(ye),
-                     n_rows, row_of, topk_w, top_k, row_vecs, n_chunks, static_cast<const uint4*>(shared_y), self_lo,
+  hipLaunchKernelGGL((combine_kernel<T, KMAX, kCombinePpt>), grid, dim3(kVecThreads), 0, stream, static_cast<const uint4*>(ye),
+                     n_rows, row_of, topk_w, n_tokens, top_k, row_vecs, n_chunks, static_cast<const uint4*>(shared_y), self_lo,
                      self_hi, static_cast<uint4*>(out));
 }
 
@@ -234,11 +251,11 @@ MOE_API moe_status_t moe_combine(const void* ye, moe_dtype_t dt, int64_t n_rows,
   if (n_rows > 0 && (!ye || !aligned16(ye))) return MOE_ERR_INVALID_ARG;
   if (shared_y && !aligned16(shared_y)) return MOE_ERR_INVALID_ARG;
   const int row_vecs = int(row_bytes / 16);
-  const int n_chunks = (row_vecs + kVecThreads - 1) / kVecThreads;
+  const int n_chunks = (row_vecs + kVecThreads * kCombinePpt - 1) / (kVecThreads * kCombinePpt);
   if (int64_t(n_chunks) * n_tokens >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
-  const dim3 grid(unsigned(n_chunks * n_tokens));
+  const dim3 grid(vec_grid(int64_t(n_chunks) * n_tokens));
 #define MOE_COMBINE(T, KM) \
-  launch_combine<T, KM>(grid, stream, ye, n_rows, row_of, topk_w, top_k, row_vecs, n_chunks, shared_y, self_lo, self_hi, out)
+  launch_combine<T, KM>(grid, stream, ye, n_rows, row_of, topk_w, n_tokens, top_k, row_vecs, n_chunks, shared_y, self_lo, self_hi, out)
   const int kmax = kmax_of(top_k);
   if (dt == MOE_F32) {
     if (kmax == 2) MOE_COMBINE(float, 2);

@@ -39,12 +39,16 @@ class MoEShare:
         self.R = moe_layout_rows(n_tokens, top_k, n_experts, n_src, expert_lo, n_local, layout, capacity)
         # expert rows in the 16-row blocked layout when experts are expected to
         # hold enough rows for the wide-tile GEMM (the layout speeds up its loads)
+        many_rows = n_tokens * top_k >= 128 * n_experts
+        # expert rows row-major by default: the token-major dispatch into them
+        # moves the fewest bytes; blocked rows speed the wide GEMM's loads but
+        # cost the dispatch more than that saves on the prefill share
         if blocked is None:
-            blocked = n_tokens * top_k >= 128 * n_experts
+            blocked = False
         self.blocked = bool(blocked) and act_dtype == torch.bfloat16 and hidden % 32 == 0
         self.a_layout = ACT_BLOCKED16 if self.blocked else ACT_ROWS
         # decode-sized batches never make enough wide tiles: skip that launch
-        self.policy = GEMM_AUTO if self.blocked else GEMM_STREAM_K
+        self.policy = GEMM_AUTO if many_rows else GEMM_STREAM_K
         d = self.dev
         self.topk_idx = torch.empty((n_tokens, top_k), dtype=torch.int32, device=d)
         self.topk_w = torch.empty((n_tokens, top_k), dtype=torch.float32, device=d)
@@ -103,8 +107,7 @@ class MoEShare:
 
     def dispatch(self, x):
         if self.blocked:
-            n_used = self.lay["expert_off"][self.L:] if self.layout == COMPACT else None
-            moe_dispatch_blocked(x, self.lay["row_token"], self.R, n_used, self.xe)
+            moe_dispatch_blocked(x, self.lay["row_of"], self.K, self.R, self.xe)
         else:
             moe_dispatch(x, self.lay["row_of"], self.K, self.R, self.xe)
 

@@ -172,18 +172,15 @@ moe_status_t moe_dispatch_layout(const moe_layout_desc_t* d, const int32_t* topk
 moe_status_t moe_dispatch(const void* x, moe_dtype_t dt, int n_tokens, int hidden, int top_k,
                           const int32_t* row_of, int64_t n_rows, void* xe, hipStream_t stream);
 
-/* The same copy into an expert-grouped buffer in the MOE_ACT_BLOCKED16 layout,
- * row by row: xe row r = x[row_token[r]] for row_token[r] in [0, n_tokens);
- * other rows (holes) are not written. Only rows [0, *n_used) are visited
- * (n_used: device int32, e.g. expert_off + n_local for the COMPACT layout, or
- * NULL for all n_rows). A token row is read once per slot.
+/* The same copy into an expert-grouped buffer in the MOE_ACT_BLOCKED16 layout
+ * (same arguments as moe_dispatch): each token row is read once and written to
+ * each of its slots' blocks; unused rows are not written.
  *
  * x [n_tokens, hidden] bf16 row-major, hidden % 32 == 0; xe holds
  * ceil(n_rows / 16) * 16 rows of hidden bf16.
  */
-moe_status_t moe_dispatch_blocked(const void* x, moe_dtype_t dt, int n_tokens, int hidden,
-                                  const int32_t* row_token, int64_t n_rows, const int32_t* n_used, void* xe,
-                                  hipStream_t stream);
+moe_status_t moe_dispatch_blocked(const void* x, moe_dtype_t dt, int n_tokens, int hidden, int top_k,
+                                  const int32_t* row_of, int64_t n_rows, void* xe, hipStream_t stream);
 
 /* ------------------------------------------------------------------ grouped GEMM */
 typedef enum {

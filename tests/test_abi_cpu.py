@@ -92,11 +92,12 @@ def test_dispatch_and_combine_argument_errors(lib):
     assert lib.moe_dispatch(ctypes.c_void_p(0x100008), 1, 10, 64, 2, FAKE, 100, FAKE, None) == INVALID  # misaligned
     assert lib.moe_dispatch(None, 1, 0, 64, 2, None, 100, None, None) == OK
     b = lib.moe_dispatch_blocked
-    assert b(FAKE, 0, 10, 64, FAKE, 100, None, FAKE, None) == UNSUPPORTED  # f32 rows
-    assert b(FAKE, 1, 10, 48, FAKE, 100, None, FAKE, None) == INVALID      # hidden % 32
-    assert b(FAKE, 1, -1, 64, FAKE, 100, None, FAKE, None) == INVALID
-    assert b(FAKE, 1, 10, 64, None, 100, None, FAKE, None) == INVALID      # no row_token
-    assert b(None, 1, 0, 64, None, 100, None, None, None) == OK
+    assert b(FAKE, 0, 10, 64, 2, FAKE, 100, FAKE, None) == UNSUPPORTED  # f32 rows
+    assert b(FAKE, 1, 10, 48, 2, FAKE, 100, FAKE, None) == INVALID      # hidden % 32
+    assert b(FAKE, 1, -1, 64, 2, FAKE, 100, FAKE, None) == INVALID
+    assert b(FAKE, 1, 10, 64, 17, FAKE, 100, FAKE, None) == UNSUPPORTED  # K > 16
+    assert b(FAKE, 1, 10, 64, 2, None, 100, FAKE, None) == INVALID      # no row_of
+    assert b(None, 1, 0, 64, 2, None, 100, None, None) == OK
     c = lib.moe_combine
     assert c(FAKE, 1, 100, FAKE, FAKE, 10, 2, 12, None, 0, 0, FAKE, None) == INVALID  # 24-byte rows
     assert c(FAKE, 1, 100, FAKE, FAKE, 10, 2, 64, FAKE, 5, 20, FAKE, None) == INVALID  # self range past N

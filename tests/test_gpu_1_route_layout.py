@@ -194,19 +194,17 @@ def test_dispatch_blocked_tiny_bit_exact(seed, layout):
     cap = worst_case_rows(N, 2, 2) if layout == COMPACT else int(np.diff(d["src_offsets"]).max())
     ref = dispatch_layout(idx, d["src_offsets"], 0, 2, layout, cap)
     R = ref["rows"]
-    row_token = torch.from_numpy(ref["row_token"].astype(np.int32)).cuda()
-    n_used = torch.tensor([int(ref["expert_off"][-1]) if layout == COMPACT else R], dtype=torch.int32, device="cuda")
+    row_of = torch.from_numpy(ref["row_of"].astype(np.int32)).cuda()
     xe = torch.full((moe.blocked_rows(R), cfg.hidden), 7.5, dtype=torch.bfloat16, device="cuda")
-    moe.moe_dispatch_blocked(x, row_token, R, n_used, xe)
+    moe.moe_dispatch_blocked(x, row_of, 2, R, xe)
     rows = unblock16(xe, R)
     occ = torch.from_numpy(ref["row_token"] >= 0).cuda()
     tok = torch.from_numpy(np.maximum(ref["row_token"], 0)).cuda()
     assert torch.equal(rows[occ].view(torch.int16), x[tok][occ].view(torch.int16))
-    assert torch.all(rows[~occ] == 7.5)   # holes and rows past n_used untouched
-    # without a device row count every row is visited; the result is the same
-    xe2 = torch.full_like(xe, 7.5)
-    moe.moe_dispatch_blocked(x, row_token, R, None, xe2)
-    assert torch.equal(xe.view(torch.int16), xe2.view(torch.int16))
+    assert torch.all(rows[~occ] == 7.5)   # unused rows untouched
+    # the row-major dispatch holds the same rows
+    xr = moe.moe_dispatch(x, row_of, 2, R, torch.full((R, cfg.hidden), 7.5, dtype=torch.bfloat16, device="cuda"))
+    assert torch.equal(rows.view(torch.int16), xr.view(torch.int16))
 
 
 @pytest.mark.parametrize("name", ["dsv3_prefill_ep8", "dsv3_decode_ep128"])
@@ -219,8 +217,7 @@ def test_dispatch_blocked_full_size(name):
     ref = dispatch_layout(idx, d["src_offsets"], 0, cfg.n_local, COMPACT, worst_case_rows(N, 8, cfg.n_local))
     x = make_x(cfg, 0, d["src_offsets"]).cuda()
     M = int(ref["expert_off"][-1])
-    row_token = torch.from_numpy(ref["row_token"].astype(np.int32)).cuda()
-    n_used = torch.tensor([M], dtype=torch.int32, device="cuda")
-    xe = moe.moe_dispatch_blocked(x, row_token, ref["rows"], n_used)
+    row_of = torch.from_numpy(ref["row_of"].astype(np.int32)).cuda()
+    xe = moe.moe_dispatch_blocked(x, row_of, cfg.top_k, ref["rows"])
     tok = torch.from_numpy(ref["row_token"][:M]).cuda()
     assert torch.equal(unblock16(xe, M).view(torch.int16), x[tok].view(torch.int16))
