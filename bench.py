@@ -38,6 +38,8 @@ STEP_NAMES = ("route", "layout", "dispatch", "gemm_up", "gemm_down", "combine")
 KERNEL_OF_STEP = {"gemm_up": "ffn_wide_kernel<up> + ffn_mfma_kernel<up> + ffn_fixup_kernel<up>",
                   "gemm_down": "ffn_wide_kernel<down> + ffn_mfma_kernel<down> + ffn_fixup_kernel<down>",
                   "dispatch": "dispatch_kernel", "combine": "combine_kernel", "route": "route_topk_kernel"}
+KERNEL_OF_STEP_FP8 = {"gemm_up": "ffn_fp8_kernel<up> + ffn_fp8_fixup_kernel<up>",
+                      "gemm_down": "ffn_fp8_kernel<down> + ffn_fp8_fixup_kernel<down>"}
 
 
 # --------------------------------------------------------------------------- perf model
@@ -303,7 +305,8 @@ def main(argv=None):
         roof = {"bound": "hbm", "achieved": round(byts / dom_us / 1e3, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = _traffic(cfg.name, dom)
-    roof["kernel"] = KERNEL_OF_STEP.get(dom, dom)
+    names = dict(KERNEL_OF_STEP, **(KERNEL_OF_STEP_FP8 if cfg.weight == "fp8_e4m3" else {}))
+    roof["kernel"] = names.get(dom, dom)
     roof["algorithmic_bytes_per_launch"] = int(byts)
     roof["flops_per_launch"] = int(flops)
     roof["avg_launch_us"] = round(dom_us, 2)

@@ -15,8 +15,8 @@
 // weight block run side by side and the weight block is fetched from HBM
 // once. Empty experts produce no tiles.
 //
-// Tile (4 waves): up = 128 rows x 64 h columns, i.e. 64 gate + 64 up weight
-// rows; down = 128 rows x 128 output columns. Each wave owns 32 weight rows
+// Tile (4 waves): up = 64 rows x 64 h columns, i.e. 64 gate + 64 up weight
+// rows; down = 64 rows x 128 output columns. Each wave owns 32 weight rows
 // (up: 16 gate + the 16 matching up rows, so SwiGLU pairs land in one lane)
 // and all row blocks. MFMA v_mfma_f32_32x32x16_bf16 with the weights as the
 // A operand (32 weight rows) and the activations as the B operand (32 rows);
@@ -24,15 +24,15 @@
 // costs one MFMA column block while the weights stream once.
 //
 // Data path per 128-deep K chunk: each lane loads 64 contiguous bytes of its
-// weight row straight from HBM into registers (one chunk ahead), and the
-// workgroup stages the activation chunk [128 rows x 128] in LDS (double
+// weight row straight from HBM into registers (chunks ahead), and the
+// workgroup stages the activation chunk [64 rows x 128] in LDS (double
 // buffer, one barrier per chunk). The reduction order inside a chunk is
 // permuted identically for both operands so every weight load is a 64-byte
-// run.
+// run. Groups with many rows take the wide-tile kernel instead.
 //
-// fp8 e4m3 weights: each code is decoded exactly to fp32, multiplied by its
-// 128x128 block's fp32 scale and rounded once to bf16 in registers, then the
-// bf16 MFMA runs as for bf16 weights (W8A16).
+// fp8 e4m3 weights (ffn_fp8_kernel): each code is decoded exactly to fp32,
+// multiplied by its 128x128 block's fp32 scale and rounded once to bf16 in
+// registers, then the bf16 MFMA runs as for bf16 weights (W8A16).
 //
 // fp32 activations + fp32 weights (small parity problems) use a plain SIMT
 // kernel with the same scheduler.
@@ -354,10 +354,8 @@ __device__ __forceinline__ void ffn_epilogue(const f32x16_t (&acc)[NBMAX], const
 struct TileRun {
   const uint16_t* A;   // activation rows of the tile's problem
   const void* W;       // weights of the tile's problem
-  const float* sbase;  // fp8: block scales of the tile's expert
   size_t wrow_elems;   // row-major weights: first element of this lane's weight row
   size_t wpack;        // packed weights: first 16-byte piece of this workgroup's (expert, N block)
-  int srow0, srow1;    // fp8: scale rows of the gate/up (or output) rows
   int c_begin, c_end, nchunks;
 };
 
@@ -367,7 +365,7 @@ struct TileRun {
 // activations for chunk c+1 before weights for chunk c+2, because vector loads
 // retire in order: staging chunk c+1 then waits only for its own loads while
 // two weight chunks stay in flight.
-template <int KIND, bool FP8, bool PACKED, int NB, int BMT, bool STREAM>
+template <int KIND, bool PACKED, int NB, int BMT, bool STREAM>
 __device__ __forceinline__ void run_tile(const GemmArgs& p, const TileRun& tr, const Tile& tl, Sched& sh,
                                          uint16_t (&xs)[2][BMT * kKC], float* __restrict__ parts,
                                          int rng, bool first_tile) {
@@ -376,7 +374,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const TileRun& tr, c
   const int wv = tid / kWave;
   const int lr = lane & 31;
   const int lh = lane >> 5;
-  constexpr int WV = FP8 ? 4 : 8;  // 16-byte weight loads per lane per chunk
+  constexpr int WV = 8;       // 16-byte weight loads per lane per chunk
   constexpr int XV = NB * 2;       // 16-row passes of activation staging
   const int last = tr.c_end - 1;
 
@@ -419,7 +417,6 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const TileRun& tr, c
       *reinterpret_cast<uint4*>(&xs[BUF_][(xr + 16 * i) * kKC + xslot]) =                                     \
           make_uint4(XV_[4 * i], XV_[4 * i + 1], XV_[4 * i + 2], XV_[4 * i + 3]);
   const uint4* wpk = static_cast<const uint4*>(tr.W) + tr.wpack + size_t(wv) * WV * kWave + lane;
-  const uint8_t* wrm8 = static_cast<const uint8_t*>(tr.W) + tr.wrow_elems + 64 * lh;
   const uint16_t* wrm16 = static_cast<const uint16_t*>(tr.W) + tr.wrow_elems + 32 * lh;
   // STREAM (the group fits one row tile, so its weights are read once):
   // non-temporal weight loads, so the stream does not evict the activation rows
@@ -428,9 +425,6 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const TileRun& tr, c
 #define MOE_LOAD_W(W_, C_)                                                                                    \
   if constexpr (PACKED) {                                                                                     \
     _Pragma("unroll") for (int j = 0; j < WV; ++j) W_[j] = ld_w<STREAM>(wpk + (size_t(C_) * 4 * WV + j) * kWave); \
-  } else if constexpr (FP8) {                                                                                 \
-    _Pragma("unroll") for (int j = 0; j < WV; ++j)                                                            \
-        W_[j] = ld_w<STREAM>(reinterpret_cast<const uint4*>(wrm8 + size_t(C_) * kKC + 16 * j));                  \
   } else {                                                                                                    \
     _Pragma("unroll") for (int j = 0; j < WV; ++j)                                                            \
         W_[j] = ld_w<STREAM>(                                                                                 \
@@ -448,7 +442,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const TileRun& tr, c
   // loaded before the weights of chunk c+DEPTH-1: vector loads retire in order,
   // so staging chunk c+1 waits only for its own loads while the weight
   // prefetch stays in flight.
-  constexpr int DEPTH = (NB == 1 || (FP8 && NB <= 2)) ? 3 : 2;
+  constexpr int DEPTH = NB == 1 ? 3 : 2;
   uint4 w[DEPTH][WV];
   xvec_t xv;
   MOE_LOAD_X(xv, tr.c_begin)
@@ -465,34 +459,15 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const TileRun& tr, c
       MOE_LOAD_W(w[(d + DEPTH - 1) % DEPTH], min(c + DEPTH - 1, last))
       __syncthreads();  // chunk c staged by every wave; nobody still reads buf ^ 1
       const uint16_t* xb = xs[buf];
-      if constexpr (FP8) {
-        // this lane's weight row: gate rows use srow0's scale, up rows srow1's
-        const float s0 = tr.sbase[tr.srow0 * tr.nchunks + c];
-        const float s1 = tr.sbase[tr.srow1 * tr.nchunks + c];
-        const float sc = lr < 16 ? s0 : s1;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const uint4 q = w[d][j >> 1];
-          const bf16x8_t a = (j & 1) ? fp8x8_dequant(q.z, q.w, sc) : fp8x8_dequant(q.x, q.y, sc);
-          const int cl = 8 * lh + j;  // 16-byte column: k = 64*lh + 8*j
-#pragma unroll
-          for (int b = 0; b < NB; ++b) {
-            const int rr = b * 32 + lr;
-            const uint4 bv = *reinterpret_cast<const uint4*>(&xb[rr * kKC + ((cl ^ (rr & 15)) * 8)]);
-            acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bv), acc[b], 0, 0, 0);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int cl = 8 * (j >> 2) + 4 * lh + (j & 3);  // k = 64*(j/4) + 32*lh + 8*(j%4)
-            const int rr = b * 32 + lr;
-            const uint4 bv = *reinterpret_cast<const uint4*>(&xb[rr * kKC + ((cl ^ (rr & 15)) * 8)]);
-            acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w[d][j]),
-                                                              __builtin_bit_cast(bf16x8_t, bv), acc[b], 0, 0, 0);
-          }
+          const int cl = 8 * (j >> 2) + 4 * lh + (j & 3);  // k = 64*(j/4) + 32*lh + 8*(j%4)
+          const int rr = b * 32 + lr;
+          const uint4 bv = *reinterpret_cast<const uint4*>(&xb[rr * kKC + ((cl ^ (rr & 15)) * 8)]);
+          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w[d][j]),
+                                                            __builtin_bit_cast(bf16x8_t, bv), acc[b], 0, 0, 0);
         }
       }
       MOE_STORE_X(xv, buf ^ 1)  // chunk c+1 (a harmless repeat of the last chunk at the end)
@@ -516,10 +491,9 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const TileRun& tr, c
   }
 }
 
-template <int KIND, bool FP8, bool PACKED>
+template <int KIND, bool PACKED>
 __global__ __launch_bounds__(kGemmThreads, 2) void ffn_mfma_kernel(GemmArgs p, float* __restrict__ parts) {
-  // rows per tile: 64 for bf16 weights (registers), 128 for fp8 weights
-  constexpr int BMT = FP8 ? kBM : kBM / 2;
+  constexpr int BMT = kBM / 2;  // rows per tile
   __shared__ Sched sh;
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][BMT * kKC];
 
@@ -558,34 +532,13 @@ __global__ __launch_bounds__(kGemmThreads, 2) void ffn_mfma_kernel(GemmArgs p, f
       wrow = tl.nt * 128 + 32 * wv + lr;
     }
     tr.wrow_elems = (size_t(tl.we) * p.n_w_rows + wrow) * p.K;
-    constexpr int WV = FP8 ? 4 : 8;
-    tr.wpack = (size_t(tl.we) * p.n_tiles_n + tl.nt) * nchunks * 4 * WV * kWave;
-    tr.srow0 = tr.srow1 = 0;
-    tr.sbase = nullptr;
-    if (FP8) {
-      if (KIND == kUp) {
-        tr.srow0 = (tl.nt * 64) / 128;
-        tr.srow1 = (p.n_out + tl.nt * 64) / 128;
-      } else {
-        tr.srow0 = tr.srow1 = tl.nt;
-      }
-      tr.sbase = (tl.shared ? p.sh_s : p.s) + size_t(tl.we) * (p.n_w_rows / 128) * nchunks;
-    }
+    tr.wpack = (size_t(tl.we) * p.n_tiles_n + tl.nt) * nchunks * 4 * 8 * kWave;
     const int nb = (tl.nrows + 31) / 32;  // active 32-row blocks (uniform)
     const bool first = t == t_first;
     auto run = [&](auto stream_tag) __attribute__((always_inline)) {
       constexpr bool ST = decltype(stream_tag)::value;
-      if constexpr (FP8) {
-        switch (nb) {
-          case 1: run_tile<KIND, FP8, PACKED, 1, BMT, ST>(p, tr, tl, sh, xs, parts, rng, first); break;
-          case 2: run_tile<KIND, FP8, PACKED, 2, BMT, ST>(p, tr, tl, sh, xs, parts, rng, first); break;
-          case 3: run_tile<KIND, FP8, PACKED, 3, BMT, ST>(p, tr, tl, sh, xs, parts, rng, first); break;
-          default: run_tile<KIND, FP8, PACKED, 4, BMT, ST>(p, tr, tl, sh, xs, parts, rng, first); break;
-        }
-      } else {
-        if (nb == 1) run_tile<KIND, FP8, PACKED, 1, BMT, ST>(p, tr, tl, sh, xs, parts, rng, first);
-        else run_tile<KIND, FP8, PACKED, 2, BMT, ST>(p, tr, tl, sh, xs, parts, rng, first);
-      }
+      if (nb == 1) run_tile<KIND, PACKED, 1, BMT, ST>(p, tr, tl, sh, xs, parts, rng, first);
+      else run_tile<KIND, PACKED, 2, BMT, ST>(p, tr, tl, sh, xs, parts, rng, first);
     };
     if (tl.mtiles == 1) run(std::true_type{});
     else run(std::false_type{});
@@ -1055,6 +1008,308 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_wide_fixup_kernel(GemmArgs p
   wide_epilogue_block<KIND>(p, tl, sh, b, a0, a1, wv, lr, lh);
 }
 
+// ------------------------------------------------------------------ fp8 kernel
+// fp8 e4m3 weights, decode-shaped groups (W8A16). A tile is 96 activation
+// rows x two adjacent N blocks (up: 2 x 64 h columns; down: 2 x 128 output
+// columns), i.e. 256 weight rows: each wave owns its 32 rows of both N blocks
+// (sub-blocks a = 0, 1), so every activation chunk staged in LDS feeds 256
+// weight rows and the activation rows are re-read half as often as with one N
+// block per tile (at ~100 rows per expert they would otherwise outweigh the
+// fp8 weight bytes). 96 rows (3 MFMA blocks) keep the accumulators (96
+// registers) and a two-deep weight ring (64) inside one wave's registers at
+// two workgroups per compute unit.
+// Weights stream from HBM straight into the register ring (each lane 64
+// contiguous bytes of each of its two rows per chunk, as in the packed layout).
+// Activations go global -> LDS by LDS DMA (16 bytes per lane, 1 KiB = 4 staged
+// rows per wave load; the lane's global column is chosen so that slot s of
+// staged row r holds column piece s ^ (r % 16)), so they take no registers.
+// All loads of chunk c+1 are issued at the top of chunk c, right after the
+// barrier, and are first needed at its last step.
+// Dequantisation as fp8x8_dequant (exact decode, one fp32 multiply by the
+// 128 x 128 block scale, one rounding to bf16).
+constexpr int kF8BM = 96;                                   // activation rows per tile
+constexpr int kF8MB = kF8BM / 32;                           // MFMA row blocks per tile
+constexpr int kF8PartFloats = 4 * 2 * kF8MB * 16 * kWave;  // one workgroup's accumulators (96 KiB)
+
+__device__ __forceinline__ float* f8_slot(float* parts, int b, int slot) {
+  return parts + (size_t(b) * 2 + slot) * kF8PartFloats;
+}
+// [wave][a][block][quad q][lane][4 floats]: 1 KiB contiguous per wave access
+__device__ __forceinline__ int f8_part_idx(int wv, int a, int b, int q, int lane) {
+  return ((((wv * 2 + a) * kF8MB + b) * 4 + q) * kWave + lane) * 4;
+}
+
+template <int KIND, bool PACKED, int NB, bool STREAM>
+__device__ __forceinline__ void f8_tile(const GemmArgs& p, const Tile& tl, const Sched& sh, uint16_t* __restrict__ x0,
+                                        uint16_t* __restrict__ x1, int c_begin, int c_end, float* __restrict__ part) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
+  const int lr = lane & 31;
+  const int lh = lane >> 5;
+  const int nchunks = p.K / kKC;
+  const int last = c_end - 1;
+  const int nt0 = 2 * tl.nt;
+  const bool has1 = nt0 + 1 < p.n_tiles_n;  // uniform: an odd N-block count leaves the last tile one block
+  const int ntb[2] = {nt0, has1 ? nt0 + 1 : nt0};
+
+  // weights: this lane's row in each sub-block, its first chunk, and its block-scale row
+  const uint8_t* W = static_cast<const uint8_t*>(tl.shared ? p.sh_w : p.w);
+  const float* sbase = (tl.shared ? p.sh_s : p.s) + size_t(tl.we) * (p.n_w_rows / 128) * nchunks;
+  const uint4* wsrc[2];
+  const float* ssrc[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int nt = ntb[a];
+    int wrow;
+    if (KIND == kUp) {
+      const int j = nt * 64 + 16 * wv + (lr & 15);
+      wrow = lr < 16 ? j : p.n_out + j;
+    } else {
+      wrow = nt * 128 + 32 * wv + lr;
+    }
+    if constexpr (PACKED)
+      wsrc[a] = reinterpret_cast<const uint4*>(W) + (size_t(tl.we) * p.n_tiles_n + nt) * nchunks * 4 * 4 * kWave +
+                size_t(wv) * 4 * kWave + lane;
+    else
+      wsrc[a] = reinterpret_cast<const uint4*>(W + (size_t(tl.we) * p.n_w_rows + wrow) * p.K + 64 * lh);
+    ssrc[a] = sbase + size_t(wrow / 128) * nchunks;
+  }
+  // chunk C of sub-block a, 16-byte piece j (of 4)
+  auto wpiece = [&](int a, int C, int j) -> const uint4* {
+    if constexpr (PACKED) return wsrc[a] + (size_t(C) * 4 * 4 + j) * kWave;
+    else return wsrc[a] + size_t(C) * (kKC / 16) + j;
+  };
+
+  // activations: load q of this wave stages tile rows 4 (4 q + wv) .. + 3
+  constexpr int XL = (NB * 8 + 3) / 4;  // 1 KiB loads per wave per chunk
+  const uint16_t* A = static_cast<const uint16_t*>(tl.shared ? p.sh_a : p.a);
+  const bool ablk = tl.shared ? p.sh_a_blk : p.a_blk;
+  const size_t xstep = ablk ? size_t(4) * 512 : size_t(kKC);  // elements from one chunk of a row to the next
+  const uint16_t* xg[XL];
+  const int phys0 = sh.rowmap[0];
+#pragma unroll
+  for (int q = 0; q < XL; ++q) {
+    const int r = 4 * (4 * q + wv) + (lane >> 4);
+    const int c = (lane & 15) ^ (r & 15);  // column piece this lane's LDS slot holds
+    const int phys = r < NB * 32 ? sh.rowmap[r] : -1;
+    const int pr = phys >= 0 ? phys : phys0;  // rows past the tile feed only discarded columns
+    xg[q] = A + (ablk ? blk_row_base(pr, p.K) + size_t(c >> 2) * 512 + (c & 3) * 8 : size_t(pr) * p.K + c * 8);
+  }
+
+  f32x16_t acc[2][NB];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
+
+  // Two-deep ring (even / odd chunks of the range). Per chunk the vector-memory
+  // ops go out in the order: activation DMA of the next chunk, its two scales,
+  // its 8 weight pieces. (With LDS-DMA and register loads both outstanding the
+  // compiler waits for all of them before the first use of any, so every load
+  // of a chunk is issued one chunk ahead, before the first use.)
+  // Software pipeline, one 16-deep step at a time (fenced, so the compiler
+  // cannot hoist a whole chunk of fragment reads): step j reads its activation
+  // fragments, dequantises the weights of step j + 1 (step 0 of the next chunk
+  // after step 7) and issues its MFMAs with the fragments dequantised before.
+  uint4 w0[2][4], w1[2][4];  // [sub-block][piece]
+  float s0[2], s1[2];        // block scales
+  bf16x8_t fa[2];            // weight fragments of the current step
+#define MOE_F8_LOADS(C_, XBUF_, WR_, SR_)                                                                     \
+  {                                                                                                         \
+    const size_t xo_ = size_t(C_) * xstep;                                                                  \
+    _Pragma("unroll") for (int q = 0; q < XL; ++q)                                                          \
+      __builtin_amdgcn_global_load_lds(xg[q] + xo_, (lds_ptr_t)((XBUF_) + (4 * q + wv) * 512), 16, 0, 0);     \
+    _Pragma("unroll") for (int a = 0; a < 2; ++a) SR_[a] = ssrc[a][C_];                                     \
+    _Pragma("unroll") for (int a = 0; a < 2; ++a)                                                           \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j) WR_[a][j] = ld_w<STREAM>(wpiece(a, C_, j));             \
+  }
+  // all of this wave's loads of the chunk have landed; after the barrier every
+  // wave's staged rows are visible and nobody still reads the other buffer
+#define MOE_F8_SYNC()                                                                                       \
+  __builtin_amdgcn_sched_barrier(0);                                                                        \
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));                                                          \
+  __builtin_amdgcn_s_barrier();                                                                             \
+  __builtin_amdgcn_sched_barrier(0);
+#define MOE_F8_DEQ(DST_, WR_, J_, SR_)                                                                      \
+  _Pragma("unroll") for (int a = 0; a < 2; ++a) DST_[a] =                                                   \
+      ((J_) & 1) ? fp8x8_dequant(WR_[a][(J_) >> 1].z, WR_[a][(J_) >> 1].w, SR_[a])                          \
+                 : fp8x8_dequant(WR_[a][(J_) >> 1].x, WR_[a][(J_) >> 1].y, SR_[a]);
+  // chunk in (XBUF_, WR_, SR_); the next chunk's weights are in (WN_, SN_)
+#define MOE_F8_CHUNK(XBUF_, WR_, SR_, WN_, SN_)                                                             \
+  _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                                           \
+    const int cl_ = 8 * lh + j; /* 16-byte column: k = 64 lh + 8 j */                                       \
+    bf16x8_t fb_[NB];                                                                                       \
+    _Pragma("unroll") for (int b = 0; b < NB; ++b) {                                                        \
+      const int rr_ = b * 32 + lr;                                                                          \
+      fb_[b] = *reinterpret_cast<const bf16x8_t*>((XBUF_) + rr_ * kKC + ((cl_ ^ (rr_ & 15)) * 8));           \
+    }                                                                                                       \
+    bf16x8_t na_[2];                                                                                        \
+    if (j < 7) {                                                                                            \
+      MOE_F8_DEQ(na_, WR_, j + 1, SR_)                                                                      \
+    } else {                                                                                                \
+      MOE_F8_DEQ(na_, WN_, 0, SN_)                                                                          \
+    }                                                                                                       \
+    _Pragma("unroll") for (int b = 0; b < NB; ++b) {                                                        \
+      acc[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0], fb_[b], acc[0][b], 0, 0, 0);               \
+      acc[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1], fb_[b], acc[1][b], 0, 0, 0);               \
+    }                                                                                                       \
+    fa[0] = na_[0];                                                                                         \
+    fa[1] = na_[1];                                                                                         \
+    __builtin_amdgcn_sched_barrier(0);                                                                      \
+  }
+  // even chunk: activations in x0, weights in (w0, s0); loads chunk CN_
+#define MOE_F8_EVEN(CN_)                                                                                    \
+  {                                                                                                         \
+    MOE_F8_SYNC()                                                                                           \
+    MOE_F8_LOADS(CN_, x1, w1, s1)                                                                           \
+    MOE_F8_CHUNK(x0, w0, s0, w1, s1)                                                                        \
+  }
+
+  MOE_F8_LOADS(c_begin, x0, w0, s0)
+  MOE_F8_DEQ(fa, w0, 0, s0)
+  // (no exit in the middle of the two-chunk body: the accumulators would
+  // need a second copy at the exit)
+  int c = c_begin;
+  for (; c + 1 < c_end; c += 2) {
+    MOE_F8_EVEN(c + 1)
+    {
+      const int cn = min(c + 2, last);  // past the end a harmless repeat
+      MOE_F8_SYNC()
+      MOE_F8_LOADS(cn, x0, w0, s0)
+      MOE_F8_CHUNK(x1, w1, s1, w0, s0)
+    }
+  }
+  if (c < c_end) MOE_F8_EVEN(last)  // odd count: the last chunk, then a harmless repeat
+#undef MOE_F8_EVEN
+#undef MOE_F8_LOADS
+#undef MOE_F8_SYNC
+#undef MOE_F8_DEQ
+#undef MOE_F8_CHUNK
+  // no load may still be writing LDS when the next tile reuses the buffers
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+  __builtin_amdgcn_s_barrier();
+
+  if (part == nullptr) {
+    uint16_t* out = static_cast<uint16_t*>(tl.shared ? p.sh_out : p.out);
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      if (a == 1 && !has1) break;
+      Tile ta = tl;
+      ta.nt = ntb[a];
+      ffn_epilogue<KIND, NB>(acc[a], ta, NB, sh, out, p.n_out, wv, lr, lh, p.out_blk);
+    }
+  } else {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; v += 4)
+          *reinterpret_cast<float4*>(part + f8_part_idx(wv, a, b, v / 4, lane)) =
+              make_float4(acc[a][b][v], acc[a][b][v + 1], acc[a][b][v + 2], acc[a][b][v + 3]);
+  }
+}
+
+// Stream-K over (tile, chunk) iterations exactly as ffn_mfma_kernel, with
+// tiles of 96 rows x two N blocks.
+template <int KIND, bool PACKED>
+__global__ __launch_bounds__(kGemmThreads, 2) void ffn_fp8_kernel(GemmArgs p, float* __restrict__ parts) {
+  __shared__ Sched sh;
+  __shared__ __attribute__((aligned(1024))) uint16_t x0[kF8BM * kKC], x1[kF8BM * kKC];
+  const int ntn2 = (p.n_tiles_n + 1) / 2;
+  const int n_tiles = build_schedule(p, kF8BM, ntn2, false, sh);
+  const int nchunks = p.K / kKC;
+  const int64_t total = int64_t(n_tiles) * nchunks;
+  const int G = sk_grid(total);
+  if (int(blockIdx.x) >= G) return;  // uniform
+  const int rng = int(blockIdx.x % kXcds) * (G / kXcds) + int(blockIdx.x / kXcds);
+  const int64_t i0 = sk_start(rng, total, G), i1 = sk_start(rng + 1, total, G);
+  if (i0 >= i1) return;  // uniform
+  const int t_first = int(i0 / nchunks), t_last = int((i1 - 1) / nchunks);
+  for (int t = t_first; t <= t_last; ++t) {
+    const Tile tl = decode_tile(p, kF8BM, ntn2, sh, t);
+    build_rowmap(p, tl, kF8BM, sh);
+    const int cb = int(max<int64_t>(i0, int64_t(t) * nchunks) - int64_t(t) * nchunks);
+    const int ce = int(min<int64_t>(i1, int64_t(t + 1) * nchunks) - int64_t(t) * nchunks);
+    float* part = (cb == 0 && ce == nchunks) ? nullptr : f8_slot(parts, rng, t == t_first ? 0 : 1);
+    auto run = [&](auto stream_tag) __attribute__((always_inline)) {
+      constexpr bool ST = decltype(stream_tag)::value;
+      switch ((tl.nrows + 31) / 32) {
+        case 1: f8_tile<KIND, PACKED, 1, ST>(p, tl, sh, x0, x1, cb, ce, part); break;
+        case 2: f8_tile<KIND, PACKED, 2, ST>(p, tl, sh, x0, x1, cb, ce, part); break;
+        default: f8_tile<KIND, PACKED, 3, ST>(p, tl, sh, x0, x1, cb, ce, part); break;
+      }
+    };
+    if (tl.mtiles == 1) run(std::true_type{});
+    else run(std::false_type{});
+    __syncthreads();  // rowmap is rewritten by the next tile
+  }
+}
+
+// Finishes the fp8 tiles cut by a range boundary (as ffn_fixup_kernel), one
+// sub-block at a time.
+template <int KIND>
+__global__ __launch_bounds__(kGemmThreads) void ffn_fp8_fixup_kernel(GemmArgs p, const float* __restrict__ parts) {
+  __shared__ Sched sh;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
+  const int lr = lane & 31;
+  const int lh = lane >> 5;
+  const int ntn2 = (p.n_tiles_n + 1) / 2;
+  const int n_tiles = build_schedule(p, kF8BM, ntn2, false, sh);
+  const int nchunks = p.K / kKC;
+  const int64_t total = int64_t(n_tiles) * nchunks;
+  const int j = blockIdx.x;
+  const int G = sk_grid(total);
+  if (j + 1 >= G) return;  // uniform: boundaries lie between ranges 0 .. G-1
+  const int64_t ib = sk_start(j + 1, total, G);
+  if (ib <= 0 || ib >= total || ib % nchunks == 0) return;  // not inside a tile
+  const int t = int(ib / nchunks);
+  if (j > 0 && sk_start(j, total, G) > int64_t(t) * nchunks) return;  // an earlier boundary owns this tile
+  const Tile tl = decode_tile(p, kF8BM, ntn2, sh, t);
+  build_rowmap(p, tl, kF8BM, sh);
+  const int nb = (tl.nrows + 31) / 32;
+  const int b_lo = sk_owner(int64_t(t) * nchunks, total, G);
+  const int b_hi = sk_owner(int64_t(t + 1) * nchunks - 1, total, G);
+  uint16_t* out = static_cast<uint16_t*>(tl.shared ? p.sh_out : p.out);
+  for (int a = 0; a < 2; ++a) {
+    Tile ta = tl;
+    ta.nt = 2 * tl.nt + a;
+    if (ta.nt >= p.n_tiles_n) break;  // uniform
+    f32x16_t acc[kF8MB];
+#pragma unroll
+    for (int b = 0; b < kF8MB; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
+    for (int w = b_lo; w <= b_hi; ++w) {
+      const int64_t s0 = sk_start(w, total, G), s1 = sk_start(w + 1, total, G);
+      if (s0 >= s1) continue;  // empty range
+      const float* src = f8_slot(const_cast<float*>(parts), w, int(s0 / nchunks) == t ? 0 : 1);
+      float4 ld[kF8MB][4];
+#pragma unroll
+      for (int b = 0; b < kF8MB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          ld[b][i] = b < nb ? *reinterpret_cast<const float4*>(src + f8_part_idx(wv, a, b, i, lane))
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int b = 0; b < kF8MB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[b][4 * i] += ld[b][i].x;
+          acc[b][4 * i + 1] += ld[b][i].y;
+          acc[b][4 * i + 2] += ld[b][i].z;
+          acc[b][4 * i + 3] += ld[b][i].w;
+        }
+    }
+    ffn_epilogue<KIND, kF8MB>(acc, ta, nb, sh, out, p.n_out, wv, lr, lh, p.out_blk);
+  }
+}
+
 // ------------------------------------------------------------------ weight packing
 // Packed layout: for expert g, N block nt (64 h columns = 128 rows of W13, or
 // 128 rows of W2) and 128-deep K chunk c, the 32 rows x 128 k of each of the 4
@@ -1197,7 +1452,8 @@ static size_t h_bytes(const moe_ggemm_desc_t* d, int64_t rows) {
 
 static size_t parts_bytes(const moe_ggemm_desc_t* d) {
   // shared by the wide and the stream-K kernels, which run one after the other
-  const size_t sk = size_t(2) * kSkGrid * kPartFloats, wide = size_t(kWideGrid) * kWidePart;
+  const size_t sk = size_t(2) * kSkGrid * (d->w_dt == MOE_FP8_E4M3 ? kF8PartFloats : kPartFloats);
+  const size_t wide = size_t(kWideGrid) * kWidePart;
   return d->act_dt == MOE_F32 ? 0 : std::max(sk, wide) * sizeof(float);
 }
 
@@ -1245,24 +1501,24 @@ static moe_status_t launch_stage(const GemmArgs& p, bool f32, bool fp8, int kind
     if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
   }
   const dim3 grid(kSkGrid), fix_grid(kSkGrid - 1);
-#define MOE_FFN(K, F, P) hipLaunchKernelGGL((ffn_mfma_kernel<K, F, P>), grid, block, 0, stream, p, parts)
   if (fp8) {
-    if (kind == kUp) { if (p.packed) MOE_FFN(kUp, true, true); else MOE_FFN(kUp, true, false); }
-    else { if (p.packed) MOE_FFN(kDown, true, true); else MOE_FFN(kDown, true, false); }
-  } else {
-    if (kind == kUp) { if (p.packed) MOE_FFN(kUp, false, true); else MOE_FFN(kUp, false, false); }
-    else { if (p.packed) MOE_FFN(kDown, false, true); else MOE_FFN(kDown, false, false); }
+#define MOE_F8(K, P) hipLaunchKernelGGL((ffn_fp8_kernel<K, P>), grid, block, 0, stream, p, parts)
+    if (kind == kUp) { if (p.packed) MOE_F8(kUp, true); else MOE_F8(kUp, false); }
+    else { if (p.packed) MOE_F8(kDown, true); else MOE_F8(kDown, false); }
+#undef MOE_F8
+    if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
+    if (kind == kUp) hipLaunchKernelGGL((ffn_fp8_fixup_kernel<kUp>), fix_grid, block, 0, stream, p, parts);
+    else hipLaunchKernelGGL((ffn_fp8_fixup_kernel<kDown>), fix_grid, block, 0, stream, p, parts);
+    return launch_status();
   }
+#define MOE_FFN(K, P) hipLaunchKernelGGL((ffn_mfma_kernel<K, P>), grid, block, 0, stream, p, parts)
+  if (kind == kUp) { if (p.packed) MOE_FFN(kUp, true); else MOE_FFN(kUp, false); }
+  else { if (p.packed) MOE_FFN(kDown, true); else MOE_FFN(kDown, false); }
 #undef MOE_FFN
   if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
-  const int bmt = fp8 ? kBM : kBM / 2;  // must match ffn_mfma_kernel
-  if (kind == kUp) {
-    if (bmt == kBM) hipLaunchKernelGGL((ffn_fixup_kernel<kUp, kBM>), fix_grid, block, 0, stream, p, parts);
-    else hipLaunchKernelGGL((ffn_fixup_kernel<kUp, kBM / 2>), fix_grid, block, 0, stream, p, parts);
-  } else {
-    if (bmt == kBM) hipLaunchKernelGGL((ffn_fixup_kernel<kDown, kBM>), fix_grid, block, 0, stream, p, parts);
-    else hipLaunchKernelGGL((ffn_fixup_kernel<kDown, kBM / 2>), fix_grid, block, 0, stream, p, parts);
-  }
+  // (the tile height must match ffn_mfma_kernel)
+  if (kind == kUp) hipLaunchKernelGGL((ffn_fixup_kernel<kUp, kBM / 2>), fix_grid, block, 0, stream, p, parts);
+  else hipLaunchKernelGGL((ffn_fixup_kernel<kDown, kBM / 2>), fix_grid, block, 0, stream, p, parts);
   return launch_status();
 }
 

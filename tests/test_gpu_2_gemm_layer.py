@@ -148,13 +148,35 @@ def test_gemm_blocked_rows_match_row_major(layout, policy):
     assert rel_l2(got, ref) <= 8e-3
 
 
+# fp8 tiles are 96 rows x two N blocks: the sizes span 1..3 active row blocks,
+# groups of two row tiles (129 = 96 + 33), and (hidden 384) an odd number of
+# down-projection N blocks, whose last tile holds one block.
 @pytest.mark.parametrize("layout", [COMPACT, PADDED])
-def test_gemm_fp8_ragged(layout):
-    cfg = get_config("kimi_k2_ep8", hidden=512, inter=384)
-    got, ref, _ = _gemm_case(cfg, [3, 0, 64, 129, 40], layout, seed=9)
+@pytest.mark.parametrize("hidden,inter", [(512, 384), (384, 256)])
+def test_gemm_fp8_ragged(layout, hidden, inter):
+    cfg = get_config("kimi_k2_ep8", hidden=hidden, inter=inter)
+    got, ref, _ = _gemm_case(cfg, [3, 0, 64, 129, 40, 96, 97], layout, seed=9)
     assert rel_l2(got, ref) <= TOL["fp8_e4m3"]
     # the fp8 path must be far better than the bound: it decodes codes exactly
     assert rel_l2(got, ref) <= 1e-2
+
+
+# Blocked activation rows through the fp8 kernel give the same bits as row-major rows.
+@pytest.mark.parametrize("layout", [COMPACT, PADDED])
+def test_gemm_fp8_blocked_rows_match_row_major(layout):
+    cfg = get_config("kimi_k2_ep8", hidden=1024, inter=256)
+    got, ref, (a, dw, kw) = _gemm_case(cfg, [70, 0, 200, 5, 96], layout, seed=12)
+    assert rel_l2(got, ref) <= 1e-2
+    y_rm = kw["y"].clone()
+    R = a.shape[0]
+    R16 = moe.blocked_rows(R)
+    ab = torch.zeros((R16, 1024), dtype=torch.bfloat16)
+    ab[:R] = a
+    blk = ab.reshape(R16 // 16, 16, 1024 // 32, 32).permute(0, 2, 1, 3).contiguous().reshape(R16, 1024)
+    kw["y"].fill_(3.0)
+    moe.moe_grouped_gemm(blk.cuda(), dw["w13"], dw["w2"], s13=dw["s13"], s2=dw["s2"], a_layout=moe.ACT_BLOCKED16,
+                         rows=R, **kw)
+    assert torch.equal(kw["y"].view(torch.int16), y_rm.view(torch.int16))
 
 
 def test_gemm_stages_match_full_and_are_deterministic():
