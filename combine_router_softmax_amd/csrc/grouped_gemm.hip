@@ -319,33 +319,76 @@ __device__ inline float* sk_slot(float* parts, int b, int slot) {
   return parts + (size_t(b) * 2 + slot) * kPartFloats;
 }
 
-// (four consecutive output columns never straddle a 32-column block)
+// Epilogue of 32-row block b of a tile (four consecutive output columns never
+// straddle a 32-column block).
+template <int KIND>
+__device__ __forceinline__ void ffn_epilogue_block(const f32x16_t& acc, const Tile& tl, int b, const Sched& sh,
+                                                   uint16_t* out, int n_out, int wv, int lr, int lh, bool oblk) {
+  const int phys = sh.rowmap[b * 32 + lr];
+  if (phys < 0) return;
+  uint16_t* orow = out + act_off(phys, 0, n_out, oblk);
+  if (KIND == kUp) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      float h[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) h[r] = silu_f(acc[4 * q + r]) * acc[4 * (q + 2) + r];
+      const int col = tl.nt * 64 + 16 * wv + 8 * q + 4 * lh;
+      *reinterpret_cast<uint2*>(orow + (oblk ? size_t(col >> 5) * 512 + (col & 31) : size_t(col))) =
+          make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int col = tl.nt * 128 + 32 * wv + 8 * q + 4 * lh;
+      *reinterpret_cast<uint2*>(orow + (oblk ? size_t(col >> 5) * 512 + (col & 31) : size_t(col))) =
+          make_uint2(pack_bf16x2(acc[4 * q], acc[4 * q + 1]), pack_bf16x2(acc[4 * q + 2], acc[4 * q + 3]));
+    }
+  }
+}
+
 template <int KIND, int NBMAX>
 __device__ __forceinline__ void ffn_epilogue(const f32x16_t (&acc)[NBMAX], const Tile& tl, int nb, const Sched& sh,
                                              uint16_t* out, int n_out, int wv, int lr, int lh, bool oblk) {
 #pragma unroll
-  for (int b = 0; b < NBMAX; ++b) {
-    if (b >= nb) continue;
-    const int phys = sh.rowmap[b * 32 + lr];
-    if (phys < 0) continue;
-    uint16_t* orow = out + act_off(phys, 0, n_out, oblk);
-    if (KIND == kUp) {
+  for (int b = 0; b < NBMAX; ++b)
+    if (b < nb) ffn_epilogue_block<KIND>(acc[b], tl, b, sh, out, n_out, wv, lr, lh, oblk);
+}
+
+// NA accumulator tiles (16 floats per lane each) summed over the partials of
+// ranges w_lo .. w_hi in range order; src(w) is the partial of range w
+// (nullptr: an empty range, nothing to add) and idx(a, q) the offset of quad q
+// of tile a in it. The loads of four ranges are in flight at a time.
+template <int NA, class Src, class Idx>
+__device__ __forceinline__ void sum_partials(f32x16_t (&acc)[NA], int w_lo, int w_hi, Src src, Idx idx) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        float h[4];
+  for (int a = 0; a < NA; ++a)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) h[r] = silu_f(acc[b][4 * q + r]) * acc[b][4 * (q + 2) + r];
-        const int col = tl.nt * 64 + 16 * wv + 8 * q + 4 * lh;
-        *reinterpret_cast<uint2*>(orow + (oblk ? size_t(col >> 5) * 512 + (col & 31) : size_t(col))) =
-            make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
-      }
-    } else {
+    for (int v = 0; v < 16; ++v) acc[a][v] = 0.f;
+  for (int w0 = w_lo; w0 <= w_hi; w0 += 4) {
+    float4 ld[4][NA][4];
+    const float* ps[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = tl.nt * 128 + 32 * wv + 8 * q + 4 * lh;
-        *reinterpret_cast<uint2*>(orow + (oblk ? size_t(col >> 5) * 512 + (col & 31) : size_t(col))) =
-            make_uint2(pack_bf16x2(acc[b][4 * q], acc[b][4 * q + 1]), pack_bf16x2(acc[b][4 * q + 2], acc[b][4 * q + 3]));
-      }
+    for (int k = 0; k < 4; ++k) {
+      ps[k] = w0 + k <= w_hi ? src(w0 + k) : nullptr;
+#pragma unroll
+      for (int a = 0; a < NA; ++a)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          ld[k][a][q] = ps[k] ? *reinterpret_cast<const float4*>(ps[k] + idx(a, q)) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (!ps[k]) continue;  // uniform
+#pragma unroll
+      for (int a = 0; a < NA; ++a)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[a][4 * q] += ld[k][a][q].x;
+          acc[a][4 * q + 1] += ld[k][a][q].y;
+          acc[a][4 * q + 2] += ld[k][a][q].z;
+          acc[a][4 * q + 3] += ld[k][a][q].w;
+        }
     }
   }
 }
@@ -546,9 +589,10 @@ __global__ __launch_bounds__(kGemmThreads, 2) void ffn_mfma_kernel(GemmArgs p, f
   }
 }
 
-// Finishes the tiles cut by a stream-K range boundary: block j looks at the
-// boundary between workgroups j and j+1; the first boundary inside a tile
-// sums that tile's partials in workgroup order and runs the epilogue.
+// Finishes the tiles cut by a stream-K range boundary: block (j, b) looks at
+// the boundary between workgroups j and j+1; the first boundary inside a tile
+// sums that tile's partials of 32-row block b in workgroup order and runs its
+// epilogue.
 template <int KIND, int BMT>
 __global__ __launch_bounds__(kGemmThreads) void ffn_fixup_kernel(GemmArgs p, const float* __restrict__ parts) {
   __shared__ Sched sh;
@@ -560,7 +604,7 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_fixup_kernel(GemmArgs p, con
   const int n_tiles = build_schedule(p, BMT, p.n_tiles_n, false, sh);
   const int nchunks = p.K / kKC;
   const int64_t total = int64_t(n_tiles) * nchunks;
-  const int j = blockIdx.x;
+  const int j = blockIdx.x, b = blockIdx.y;
   const int G = sk_grid(total);
   if (j + 1 >= G) return;  // uniform: boundaries lie between ranges 0 .. G-1
   const int64_t ib = sk_start(j + 1, total, G);
@@ -568,39 +612,20 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_fixup_kernel(GemmArgs p, con
   const int t = int(ib / nchunks);
   if (j > 0 && sk_start(j, total, G) > int64_t(t) * nchunks) return;  // an earlier boundary owns this tile
   const Tile tl = decode_tile(p, BMT, p.n_tiles_n, sh, t);
+  if (b * 32 >= tl.nrows) return;  // uniform: no rows in this block
   build_rowmap(p, tl, BMT, sh);
-  const int nb = (tl.nrows + 31) / 32;
   const int b_lo = sk_owner(int64_t(t) * nchunks, total, G);
   const int b_hi = sk_owner(int64_t(t + 1) * nchunks - 1, total, G);
-  f32x16_t acc[kMB];
-#pragma unroll
-  for (int b = 0; b < kMB; ++b)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
-  for (int w = b_lo; w <= b_hi; ++w) {
-    const int64_t s0 = sk_start(w, total, G), s1 = sk_start(w + 1, total, G);
-    if (s0 >= s1) continue;  // empty range
-    const float* src = sk_slot(const_cast<float*>(parts), w, int(s0 / nchunks) == t ? 0 : 1);
-    // all of this partial's loads first (16 bytes per lane, 1 KiB per wave), then the adds
-    float4 ld[kMB][4];
-#pragma unroll
-    for (int b = 0; b < kMB; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        ld[b][i] = b < nb ? *reinterpret_cast<const float4*>(src + (((wv * kMB + b) * 4 + i) * kWave + lane) * 4)
-                          : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int b = 0; b < kMB; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[b][4 * i] += ld[b][i].x;
-        acc[b][4 * i + 1] += ld[b][i].y;
-        acc[b][4 * i + 2] += ld[b][i].z;
-        acc[b][4 * i + 3] += ld[b][i].w;
-      }
-  }
+  f32x16_t acc[1];
+  sum_partials(
+      acc, b_lo, b_hi,
+      [&](int w) -> const float* {
+        const int64_t s0 = sk_start(w, total, G), s1 = sk_start(w + 1, total, G);
+        return s0 < s1 ? sk_slot(const_cast<float*>(parts), w, int(s0 / nchunks) == t ? 0 : 1) : nullptr;
+      },
+      [&](int, int q) { return (((wv * kMB + b) * 4 + q) * kWave + lane) * 4; });
   uint16_t* out = static_cast<uint16_t*>(tl.shared ? p.sh_out : p.out);
-  ffn_epilogue<KIND, kMB>(acc, tl, nb, sh, out, p.n_out, wv, lr, lh, p.out_blk);
+  ffn_epilogue_block<KIND>(acc[0], tl, b, sh, out, p.n_out, wv, lr, lh, p.out_blk);
 }
 
 // ------------------------------------------------------------------ wide-tile kernel
@@ -975,37 +1000,12 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_wide_fixup_kernel(GemmArgs p
   const Tile tl = decode_tile<true>(p, kWM, ntn, sh, t);
   if (b * 32 >= tl.nrows) return;  // uniform: no rows in this block
   build_rowmap(p, tl, kWM, sh);
-  f32x16_t a0, a1;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) a0[v] = a1[v] = 0.f;
-  // two partials' loads in flight at a time (16 bytes per lane), then the adds
-  for (int k = 0; k < ws.S; k += 2) {
-    float4 ld[2][2][4];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const float* src = parts + size_t(i * ws.S + min(k + kk, ws.S - 1)) * kWidePart;
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) ld[kk][a][q] = *reinterpret_cast<const float4*>(src + wide_part_idx(wv, a, b, q, lane));
-    }
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      if (k + kk >= ws.S) break;  // uniform
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        a0[4 * q] += ld[kk][0][q].x;
-        a0[4 * q + 1] += ld[kk][0][q].y;
-        a0[4 * q + 2] += ld[kk][0][q].z;
-        a0[4 * q + 3] += ld[kk][0][q].w;
-        a1[4 * q] += ld[kk][1][q].x;
-        a1[4 * q + 1] += ld[kk][1][q].y;
-        a1[4 * q + 2] += ld[kk][1][q].z;
-        a1[4 * q + 3] += ld[kk][1][q].w;
-      }
-    }
-  }
-  wide_epilogue_block<KIND>(p, tl, sh, b, a0, a1, wv, lr, lh);
+  // the S partials of each accumulator tile in split order, four in flight at a time
+  f32x16_t acc[2];
+  sum_partials(
+      acc, 0, ws.S - 1, [&](int k) -> const float* { return parts + size_t(i * ws.S + k) * kWidePart; },
+      [&](int a, int q) { return wide_part_idx(wv, a, b, q, lane); });
+  wide_epilogue_block<KIND>(p, tl, sh, b, acc[0], acc[1], wv, lr, lh);
 }
 
 // ------------------------------------------------------------------ fp8 kernel
@@ -1249,8 +1249,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void ffn_fp8_kernel(GemmArgs p, fl
   }
 }
 
-// Finishes the fp8 tiles cut by a range boundary (as ffn_fixup_kernel), one
-// sub-block at a time.
+// Finishes the fp8 tiles cut by a range boundary (as ffn_fixup_kernel); block
+// (j, a * kF8MB + b) takes sub-block a, 32-row block b.
 template <int KIND>
 __global__ __launch_bounds__(kGemmThreads) void ffn_fp8_fixup_kernel(GemmArgs p, const float* __restrict__ parts) {
   __shared__ Sched sh;
@@ -1263,51 +1263,29 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_fp8_fixup_kernel(GemmArgs p,
   const int n_tiles = build_schedule(p, kF8BM, ntn2, false, sh);
   const int nchunks = p.K / kKC;
   const int64_t total = int64_t(n_tiles) * nchunks;
-  const int j = blockIdx.x;
+  const int j = blockIdx.x, a = blockIdx.y / kF8MB, b = blockIdx.y % kF8MB;
   const int G = sk_grid(total);
   if (j + 1 >= G) return;  // uniform: boundaries lie between ranges 0 .. G-1
   const int64_t ib = sk_start(j + 1, total, G);
   if (ib <= 0 || ib >= total || ib % nchunks == 0) return;  // not inside a tile
   const int t = int(ib / nchunks);
   if (j > 0 && sk_start(j, total, G) > int64_t(t) * nchunks) return;  // an earlier boundary owns this tile
-  const Tile tl = decode_tile(p, kF8BM, ntn2, sh, t);
+  Tile tl = decode_tile(p, kF8BM, ntn2, sh, t);
+  if (b * 32 >= tl.nrows || 2 * tl.nt + a >= p.n_tiles_n) return;  // uniform: no rows / no such N block
   build_rowmap(p, tl, kF8BM, sh);
-  const int nb = (tl.nrows + 31) / 32;
   const int b_lo = sk_owner(int64_t(t) * nchunks, total, G);
   const int b_hi = sk_owner(int64_t(t + 1) * nchunks - 1, total, G);
+  f32x16_t acc[1];
+  sum_partials(
+      acc, b_lo, b_hi,
+      [&](int w) -> const float* {
+        const int64_t s0 = sk_start(w, total, G), s1 = sk_start(w + 1, total, G);
+        return s0 < s1 ? f8_slot(const_cast<float*>(parts), w, int(s0 / nchunks) == t ? 0 : 1) : nullptr;
+      },
+      [&](int, int q) { return f8_part_idx(wv, a, b, q, lane); });
+  tl.nt = 2 * tl.nt + a;
   uint16_t* out = static_cast<uint16_t*>(tl.shared ? p.sh_out : p.out);
-  for (int a = 0; a < 2; ++a) {
-    Tile ta = tl;
-    ta.nt = 2 * tl.nt + a;
-    if (ta.nt >= p.n_tiles_n) break;  // uniform
-    f32x16_t acc[kF8MB];
-#pragma unroll
-    for (int b = 0; b < kF8MB; ++b)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
-    for (int w = b_lo; w <= b_hi; ++w) {
-      const int64_t s0 = sk_start(w, total, G), s1 = sk_start(w + 1, total, G);
-      if (s0 >= s1) continue;  // empty range
-      const float* src = f8_slot(const_cast<float*>(parts), w, int(s0 / nchunks) == t ? 0 : 1);
-      float4 ld[kF8MB][4];
-#pragma unroll
-      for (int b = 0; b < kF8MB; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          ld[b][i] = b < nb ? *reinterpret_cast<const float4*>(src + f8_part_idx(wv, a, b, i, lane))
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-      for (int b = 0; b < kF8MB; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[b][4 * i] += ld[b][i].x;
-          acc[b][4 * i + 1] += ld[b][i].y;
-          acc[b][4 * i + 2] += ld[b][i].z;
-          acc[b][4 * i + 3] += ld[b][i].w;
-        }
-    }
-    ffn_epilogue<KIND, kF8MB>(acc, ta, nb, sh, out, p.n_out, wv, lr, lh, p.out_blk);
-  }
+  ffn_epilogue_block<KIND>(acc[0], tl, b, sh, out, p.n_out, wv, lr, lh, p.out_blk);
 }
 
 // ------------------------------------------------------------------ weight packing
@@ -1476,7 +1454,8 @@ int device_cu_count() {
 }
 }  // namespace moe
 
-static moe_status_t launch_stage(const GemmArgs& p, bool f32, bool fp8, int kind, float* parts,
+// sk: launch the stream-K kernel (false only when the wide kernel takes every group)
+static moe_status_t launch_stage(const GemmArgs& p, bool f32, bool fp8, int kind, bool sk, float* parts,
                                  hipStream_t stream) {
   const dim3 block(kGemmThreads);
   if (f32) {
@@ -1499,14 +1478,16 @@ static moe_status_t launch_stage(const GemmArgs& p, bool f32, bool fp8, int kind
     if (kind == kUp) hipLaunchKernelGGL((ffn_wide_fixup_kernel<kUp>), wfix, block, 0, stream, p, parts);
     else hipLaunchKernelGGL((ffn_wide_fixup_kernel<kDown>), wfix, block, 0, stream, p, parts);
     if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
+    if (!sk) return launch_status();
   }
-  const dim3 grid(kSkGrid), fix_grid(kSkGrid - 1);
+  const dim3 grid(kSkGrid);
   if (fp8) {
 #define MOE_F8(K, P) hipLaunchKernelGGL((ffn_fp8_kernel<K, P>), grid, block, 0, stream, p, parts)
     if (kind == kUp) { if (p.packed) MOE_F8(kUp, true); else MOE_F8(kUp, false); }
     else { if (p.packed) MOE_F8(kDown, true); else MOE_F8(kDown, false); }
 #undef MOE_F8
     if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
+    const dim3 fix_grid(kSkGrid - 1, 2 * kF8MB);
     if (kind == kUp) hipLaunchKernelGGL((ffn_fp8_fixup_kernel<kUp>), fix_grid, block, 0, stream, p, parts);
     else hipLaunchKernelGGL((ffn_fp8_fixup_kernel<kDown>), fix_grid, block, 0, stream, p, parts);
     return launch_status();
@@ -1517,6 +1498,7 @@ static moe_status_t launch_stage(const GemmArgs& p, bool f32, bool fp8, int kind
 #undef MOE_FFN
   if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
   // (the tile height must match ffn_mfma_kernel)
+  const dim3 fix_grid(kSkGrid - 1, kBM / 2 / 32);
   if (kind == kUp) hipLaunchKernelGGL((ffn_fixup_kernel<kUp, kBM / 2>), fix_grid, block, 0, stream, p, parts);
   else hipLaunchKernelGGL((ffn_fixup_kernel<kDown, kBM / 2>), fix_grid, block, 0, stream, p, parts);
   return launch_status();
@@ -1565,6 +1547,7 @@ MOE_API moe_status_t moe_grouped_gemm(const moe_ggemm_desc_t* d, const void* a, 
                        d->policy != MOE_GEMM_STREAM_K;
   const bool force = d->policy == MOE_GEMM_WIDE;
   p.wide_min = wide_ok ? (force ? 1 : kWideMinRows) : kNoWide;
+  const bool sk = !(wide_ok && force);  // forced wide leaves the stream-K kernel nothing
   p.wide_min_tiles = force ? 0 : kWideMinTiles;
   p.sh_a_blk = 0;
   moe_status_t st = MOE_OK;
@@ -1584,7 +1567,7 @@ MOE_API moe_status_t moe_grouped_gemm(const moe_ggemm_desc_t* d, const void* a, 
     p.a_blk = d->a_layout == MOE_ACT_BLOCKED16;
     p.sh_a_blk = 0;       // the shared expert reads its rows of x in place
     p.out_blk = !f32;     // h (internal) is blocked for bf16
-    st = launch_stage(p, f32, fp8, kUp, parts, stream);
+    st = launch_stage(p, f32, fp8, kUp, sk, parts, stream);
     if (st != MOE_OK) return st;
   }
   if (down) {
@@ -1602,7 +1585,7 @@ MOE_API moe_status_t moe_grouped_gemm(const moe_ggemm_desc_t* d, const void* a, 
     p.n_tiles_n = f32 ? d->hidden / kFBN : d->hidden / 128;
     p.a_blk = p.sh_a_blk = !f32;  // h
     p.out_blk = 0;                // y rows are read by the combine
-    st = launch_stage(p, f32, fp8, kDown, parts, stream);
+    st = launch_stage(p, f32, fp8, kDown, sk, parts, stream);
   }
   return st;
 }

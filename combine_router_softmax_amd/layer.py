@@ -13,7 +13,7 @@ from typing import Optional
 
 import torch
 
-from . import (ACT_BLOCKED16, ACT_ROWS, COMPACT, GEMM_AUTO, GEMM_STREAM_K, GG_DOWN, GG_FULL, GG_UP, PADDED, W_PACKED, W_ROWMAJOR, SharedExpert,
+from . import (ACT_BLOCKED16, ACT_ROWS, COMPACT, GEMM_STREAM_K, GEMM_WIDE, GG_DOWN, GG_FULL, GG_UP, PADDED, W_PACKED, W_ROWMAJOR, SharedExpert,
                blocked_rows, gemm_desc, moe_combine, moe_dispatch, moe_dispatch_blocked, moe_dispatch_layout,
                moe_grouped_gemm, moe_grouped_gemm_workspace, moe_layout_rows, moe_pack_weights, moe_route_topk)
 
@@ -47,8 +47,11 @@ class MoEShare:
             blocked = False
         self.blocked = bool(blocked) and act_dtype == torch.bfloat16 and hidden % 32 == 0
         self.a_layout = ACT_BLOCKED16 if self.blocked else ACT_ROWS
-        # decode-sized batches never make enough wide tiles: skip that launch
-        self.policy = GEMM_AUTO if many_rows else GEMM_STREAM_K
+        # one kernel per product: batches whose experts are expected to hold
+        # enough rows take the wide-tile kernel for every group (what the AUTO
+        # rule picks for them) without an empty stream-K launch; decode-sized
+        # batches take the stream-K kernel without an empty wide launch
+        self.policy = GEMM_WIDE if many_rows else GEMM_STREAM_K
         d = self.dev
         self.topk_idx = torch.empty((n_tokens, top_k), dtype=torch.int32, device=d)
         self.topk_w = torch.empty((n_tokens, top_k), dtype=torch.float32, device=d)

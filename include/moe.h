@@ -194,7 +194,8 @@ typedef enum {
  * 256 x 256 wide-tile kernel (bf16 weights, hidden % 256 == 0), every group
  * of the launch takes that kernel, else every group takes the stream-K
  * kernel (decided on the device from the counts). WIDE: every group takes the
- * wide-tile kernel where its shape and dtype allow. STREAM_K: never. */
+ * wide-tile kernel where its shape and dtype allow (then the stream-K kernel
+ * is not launched). STREAM_K: never (then the wide kernel is not launched). */
 typedef enum {
   MOE_GEMM_AUTO = 0,
   MOE_GEMM_WIDE = 1,
