@@ -35,8 +35,8 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
 # the shared expert runs inside the gemm_up / gemm_down launches
 STEP_NAMES = ("route", "layout", "dispatch", "gemm_up", "gemm_down", "combine")
-KERNEL_OF_STEP = {"gemm_up": "ffn_wide_kernel<up> + ffn_mfma_kernel<up> + ffn_fixup_kernel<up>",
-                  "gemm_down": "ffn_wide_kernel<down> + ffn_mfma_kernel<down> + ffn_fixup_kernel<down>",
+KERNEL_OF_STEP = {"gemm_up": "ffn_wide_kernel<up> + ffn_bf16_kernel<up> + ffn_fixup_kernel<up>",
+                  "gemm_down": "ffn_wide_kernel<down> + ffn_bf16_kernel<down> + ffn_fixup_kernel<down>",
                   "dispatch": "dispatch_kernel", "combine": "combine_kernel", "route": "route_topk_kernel"}
 KERNEL_OF_STEP_FP8 = {"gemm_up": "ffn_fp8_kernel<up> + ffn_fp8_fixup_kernel<up>",
                       "gemm_down": "ffn_fp8_kernel<down> + ffn_fp8_fixup_kernel<down>"}

@@ -15,20 +15,21 @@
 // weight block run side by side and the weight block is fetched from HBM
 // once. Empty experts produce no tiles.
 //
-// Tile (4 waves): up = 64 rows x 64 h columns, i.e. 64 gate + 64 up weight
-// rows; down = 64 rows x 128 output columns. Each wave owns 32 weight rows
-// (up: 16 gate + the 16 matching up rows, so SwiGLU pairs land in one lane)
-// and all row blocks. MFMA v_mfma_f32_32x32x16_bf16 with the weights as the
-// A operand (32 weight rows) and the activations as the B operand (32 rows);
-// 32-row blocks with no rows are skipped, so a decode expert with ~32 rows
-// costs one MFMA column block while the weights stream once.
+// Decode tile (4 waves, ffn_bf16_kernel): up = 64 rows x 64 h columns, i.e.
+// 64 gate + 64 up weight rows; down = 64 rows x 128 output columns. Each wave
+// owns 32 weight rows (up: 16 gate + the 16 matching up rows, so SwiGLU pairs
+// land in one lane) and all row blocks. MFMA v_mfma_f32_32x32x16_bf16 with the
+// weights as the A operand (32 weight rows) and the activations as the B
+// operand (32 rows); 32-row blocks with no rows are skipped, so a decode
+// expert with ~32 rows costs one MFMA column block while the weights stream
+// once.
 //
-// Data path per 128-deep K chunk: each lane loads 64 contiguous bytes of its
-// weight row straight from HBM into registers (chunks ahead), and the
-// workgroup stages the activation chunk [64 rows x 128] in LDS (double
-// buffer, one barrier per chunk). The reduction order inside a chunk is
-// permuted identically for both operands so every weight load is a 64-byte
-// run. Groups with many rows take the wide-tile kernel instead.
+// Data path per 128-deep K chunk: each lane loads its weight row's pieces
+// straight from HBM into registers (chunks ahead), and the workgroup stages
+// the activation chunk [64 rows x 128] in LDS by LDS DMA (one barrier per
+// chunk). The reduction order inside a chunk is permuted identically for both
+// operands so every weight load is a 64-byte run. Groups with many rows take
+// the wide-tile kernel instead.
 //
 // fp8 e4m3 weights (ffn_fp8_kernel): each code is decoded exactly to fp32,
 // multiplied by its 128x128 block's fp32 scale and rounded once to bf16 in
@@ -254,16 +255,35 @@ __device__ void build_rowmap(const GemmArgs& p, const Tile& tl, int bm, Sched& s
   __syncthreads();
 }
 
+// A pointer every lane of the wave holds, moved into scalar registers (values
+// read from LDS are not known to be uniform): loads can then take it as their
+// scalar base with a 32-bit per-lane offset, so no per-lane 64-bit address
+// register is computed (and freed) per load.
+// (The result is a global-address-space pointer: rebuilt from integers, a
+// generic pointer would be accessed with flat instructions.)
+template <class T>
+using gptr = const T __attribute__((address_space(1)))*;
+template <class T>
+__device__ __forceinline__ gptr<T> uniform_ptr(const T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+  return (gptr<T>)((uint64_t(hi) << 32) | lo);
+}
+
+// base (scalar registers) + uniform byte offset + the lane's 32-bit byte offset
+template <class T>
+__device__ __forceinline__ gptr<T> at(gptr<char> base, uint64_t uniform_bytes, uint32_t lane_bytes) {
+  return (gptr<T>)(base + uniform_bytes + lane_bytes);
+}
+
 // 16-byte weight load; with STREAM the non-temporal hint (data used once).
 template <bool STREAM>
-__device__ __forceinline__ uint4 ld_w(const uint4* p) {
-  if constexpr (STREAM) {
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-    return make_uint4(v[0], v[1], v[2], v[3]);
-  } else {
-    return *p;
-  }
+__device__ __forceinline__ uint4 ld_w(gptr<uint4> p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const gptr<u32x4> q = (gptr<u32x4>)p;
+  const u32x4 v = STREAM ? __builtin_nontemporal_load(q) : *q;
+  return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.f + __expf(-g)); }
@@ -390,202 +410,6 @@ __device__ __forceinline__ void sum_partials(f32x16_t (&acc)[NA], int w_lo, int 
           acc[a][4 * q + 3] += ld[k][a][q].w;
         }
     }
-  }
-}
-
-// Everything one workgroup does for the K chunks [c_begin, c_end) of one tile.
-struct TileRun {
-  const uint16_t* A;   // activation rows of the tile's problem
-  const void* W;       // weights of the tile's problem
-  size_t wrow_elems;   // row-major weights: first element of this lane's weight row
-  size_t wpack;        // packed weights: first 16-byte piece of this workgroup's (expert, N block)
-  int c_begin, c_end, nchunks;
-};
-
-// NB = active 32-row blocks, a compile-time constant so the K loop has no
-// branches. Loads are issued unconditionally (chunk indices clamped to the
-// range; rows past the tile read a valid row and are zeroed before staging),
-// activations for chunk c+1 before weights for chunk c+2, because vector loads
-// retire in order: staging chunk c+1 then waits only for its own loads while
-// two weight chunks stay in flight.
-template <int KIND, bool PACKED, int NB, int BMT, bool STREAM>
-__device__ __forceinline__ void run_tile(const GemmArgs& p, const TileRun& tr, const Tile& tl, Sched& sh,
-                                         uint16_t (&xs)[2][BMT * kKC], float* __restrict__ parts,
-                                         int rng, bool first_tile) {
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wv = tid / kWave;
-  const int lr = lane & 31;
-  const int lh = lane >> 5;
-  constexpr int WV = 8;       // 16-byte weight loads per lane per chunk
-  constexpr int XV = NB * 2;       // 16-row passes of activation staging
-  const int last = tr.c_end - 1;
-
-  // Activation staging through registers into LDS: thread -> (row = tid/16 +
-  // 16*i, 16-byte column tid%16). Slot s of staged row r holds 16-byte column
-  // s ^ (r % 16) (XOR swizzle instead of padding: a column read by 16
-  // consecutive rows hits 16 different bank groups). Rows past the tile load a
-  // valid row: a token row only feeds its own MFMA output column, which the
-  // epilogue discards.
-  const int xr = tid >> 4;
-  const int xslot = ((tid & 15) ^ (xr & 15)) * 8;  // (xr + 16 i) % 16 == xr % 16
-  int xrow[XV];
-  const int phys0 = sh.rowmap[0];
-#pragma unroll
-  for (int i = 0; i < XV; ++i) {
-    const int phys = sh.rowmap[xr + 16 * i];
-    xrow[i] = phys >= 0 ? phys : phys0;
-  }
-  // address of this thread's 16 bytes of row `row`, chunk C: row-major, or
-  // in the blocked layout (a chunk of 128 columns spans four 32-column blocks)
-  const bool ablk = tl.shared ? p.sh_a_blk : p.a_blk;
-  const size_t xcstep = ablk ? size_t(4) * 512 : size_t(kKC);
-  const size_t xcofs = ablk ? size_t((tid & 15) >> 2) * 512 + ((tid & 15) & 3) * 8 : size_t(tid & 15) * 8;
-  // (plain unrolled loops over register arrays, no closures: the arrays must
-  // stay in registers)
-  // staged activations live in one vector value (XV x 16 bytes)
-  typedef uint32_t xvec_t __attribute__((ext_vector_type(4 * XV)));
-#define MOE_LOAD_X(XV_, C_)                                                                                   \
-  _Pragma("unroll") for (int i = 0; i < XV; ++i) {                                                            \
-    const uint4 t_ =                                                                                          \
-        *reinterpret_cast<const uint4*>(tr.A + (ablk ? blk_row_base(xrow[i], p.K) : size_t(xrow[i]) * p.K) +     \
-                                        size_t(C_) * xcstep + xcofs);                                         \
-    XV_[4 * i] = t_.x;                                                                                        \
-    XV_[4 * i + 1] = t_.y;                                                                                    \
-    XV_[4 * i + 2] = t_.z;                                                                                    \
-    XV_[4 * i + 3] = t_.w;                                                                                    \
-  }
-#define MOE_STORE_X(XV_, BUF_)                                                                                \
-  _Pragma("unroll") for (int i = 0; i < XV; ++i)                                                              \
-      *reinterpret_cast<uint4*>(&xs[BUF_][(xr + 16 * i) * kKC + xslot]) =                                     \
-          make_uint4(XV_[4 * i], XV_[4 * i + 1], XV_[4 * i + 2], XV_[4 * i + 3]);
-  const uint4* wpk = static_cast<const uint4*>(tr.W) + tr.wpack + size_t(wv) * WV * kWave + lane;
-  const uint16_t* wrm16 = static_cast<const uint16_t*>(tr.W) + tr.wrow_elems + 32 * lh;
-  // STREAM (the group fits one row tile, so its weights are read once):
-  // non-temporal weight loads, so the stream does not evict the activation rows
-  // that the expert's other N tiles re-read from L2. Otherwise the other row
-  // tiles re-read these weights and plain loads keep them cacheable.
-#define MOE_LOAD_W(W_, C_)                                                                                    \
-  if constexpr (PACKED) {                                                                                     \
-    _Pragma("unroll") for (int j = 0; j < WV; ++j) W_[j] = ld_w<STREAM>(wpk + (size_t(C_) * 4 * WV + j) * kWave); \
-  } else {                                                                                                    \
-    _Pragma("unroll") for (int j = 0; j < WV; ++j)                                                            \
-        W_[j] = ld_w<STREAM>(                                                                                 \
-            reinterpret_cast<const uint4*>(wrm16 + size_t(C_) * kKC + 64 * (j >> 2) + 8 * (j & 3)));          \
-  }
-
-  f32x16_t acc[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
-
-  // weight register ring: DEPTH-1 chunks in flight while one is used (3 deep
-  // where the registers allow it). Per chunk, the activations of chunk c+1 are
-  // loaded before the weights of chunk c+DEPTH-1: vector loads retire in order,
-  // so staging chunk c+1 waits only for its own loads while the weight
-  // prefetch stays in flight.
-  constexpr int DEPTH = NB == 1 ? 3 : 2;
-  uint4 w[DEPTH][WV];
-  xvec_t xv;
-  MOE_LOAD_X(xv, tr.c_begin)
-#pragma unroll
-  for (int d = 0; d + 1 < DEPTH; ++d) { MOE_LOAD_W(w[d], min(tr.c_begin + d, last)) }
-  MOE_STORE_X(xv, 0)
-  for (int c0 = tr.c_begin; c0 < tr.c_end; c0 += DEPTH) {
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-      const int c = c0 + d;
-      if (c >= tr.c_end) break;
-      const int buf = (c - tr.c_begin) & 1;
-      MOE_LOAD_X(xv, min(c + 1, last))
-      MOE_LOAD_W(w[(d + DEPTH - 1) % DEPTH], min(c + DEPTH - 1, last))
-      __syncthreads();  // chunk c staged by every wave; nobody still reads buf ^ 1
-      const uint16_t* xb = xs[buf];
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int cl = 8 * (j >> 2) + 4 * lh + (j & 3);  // k = 64*(j/4) + 32*lh + 8*(j%4)
-          const int rr = b * 32 + lr;
-          const uint4 bv = *reinterpret_cast<const uint4*>(&xb[rr * kKC + ((cl ^ (rr & 15)) * 8)]);
-          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w[d][j]),
-                                                            __builtin_bit_cast(bf16x8_t, bv), acc[b], 0, 0, 0);
-        }
-      }
-      MOE_STORE_X(xv, buf ^ 1)  // chunk c+1 (a harmless repeat of the last chunk at the end)
-    }
-  }
-#undef MOE_LOAD_X
-#undef MOE_STORE_X
-#undef MOE_LOAD_W
-  if (tr.c_begin == 0 && tr.c_end == tr.nchunks) {
-    uint16_t* out = static_cast<uint16_t*>(tl.shared ? p.sh_out : p.out);
-    ffn_epilogue<KIND, NB>(acc, tl, NB, sh, out, p.n_out, wv, lr, lh, p.out_blk);
-  } else {
-    // partial sums of a split tile, in accumulator-register order
-    float* dst = sk_slot(parts, rng, first_tile ? 0 : 1);
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int v = 0; v < 16; v += 4)  // [wave][block][quad][lane][4]: 1 KiB contiguous per store
-        *reinterpret_cast<float4*>(dst + (((wv * kMB + b) * 4 + v / 4) * kWave + lane) * 4) =
-            make_float4(acc[b][v], acc[b][v + 1], acc[b][v + 2], acc[b][v + 3]);
-  }
-}
-
-template <int KIND, bool PACKED>
-__global__ __launch_bounds__(kGemmThreads, 2) void ffn_mfma_kernel(GemmArgs p, float* __restrict__ parts) {
-  constexpr int BMT = kBM / 2;  // rows per tile
-  __shared__ Sched sh;
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][BMT * kKC];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wv = tid / kWave;
-  const int lr = lane & 31;
-  const int n_tiles = build_schedule(p, BMT, p.n_tiles_n, false, sh);
-  const int nchunks = p.K / kKC;
-  const int64_t total = int64_t(n_tiles) * nchunks;
-  // XCD-aware range order: workgroups are dispatched round-robin over the 8
-  // XCDs, so range r goes to workgroup (r % 64) * 8 + r / 64; consecutive
-  // ranges (the N tiles of one expert, which share its activation rows) then
-  // run on one XCD and its L2 fetches those rows once.
-  const int G = sk_grid(total);
-  if (int(blockIdx.x) >= G) return;  // uniform
-  const int rng = int(blockIdx.x % kXcds) * (G / kXcds) + int(blockIdx.x / kXcds);
-  const int64_t i0 = sk_start(rng, total, G), i1 = sk_start(rng + 1, total, G);
-  if (i0 >= i1) return;  // uniform
-  const int t_first = int(i0 / nchunks), t_last = int((i1 - 1) / nchunks);
-
-  for (int t = t_first; t <= t_last; ++t) {
-    const Tile tl = decode_tile(p, BMT, p.n_tiles_n, sh, t);
-    build_rowmap(p, tl, BMT, sh);
-    TileRun tr;
-    tr.c_begin = int(max<int64_t>(i0, int64_t(t) * nchunks) - int64_t(t) * nchunks);
-    tr.c_end = int(min<int64_t>(i1, int64_t(t + 1) * nchunks) - int64_t(t) * nchunks);
-    tr.nchunks = nchunks;
-    tr.A = static_cast<const uint16_t*>(tl.shared ? p.sh_a : p.a);
-    tr.W = tl.shared ? p.sh_w : p.w;
-    int wrow;  // weight row of this lane (row-major weights)
-    if (KIND == kUp) {
-      const int j = tl.nt * 64 + 16 * wv + (lr & 15);
-      wrow = lr < 16 ? j : p.n_out + j;
-    } else {
-      wrow = tl.nt * 128 + 32 * wv + lr;
-    }
-    tr.wrow_elems = (size_t(tl.we) * p.n_w_rows + wrow) * p.K;
-    tr.wpack = (size_t(tl.we) * p.n_tiles_n + tl.nt) * nchunks * 4 * 8 * kWave;
-    const int nb = (tl.nrows + 31) / 32;  // active 32-row blocks (uniform)
-    const bool first = t == t_first;
-    auto run = [&](auto stream_tag) __attribute__((always_inline)) {
-      constexpr bool ST = decltype(stream_tag)::value;
-      if (nb == 1) run_tile<KIND, PACKED, 1, BMT, ST>(p, tr, tl, sh, xs, parts, rng, first);
-      else run_tile<KIND, PACKED, 2, BMT, ST>(p, tr, tl, sh, xs, parts, rng, first);
-    };
-    if (tl.mtiles == 1) run(std::true_type{});
-    else run(std::false_type{});
-    __syncthreads();  // rowmap and staging buffers are rewritten by the next tile
   }
 }
 
@@ -1008,6 +832,232 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_wide_fixup_kernel(GemmArgs p
   wide_epilogue_block<KIND>(p, tl, sh, b, acc[0], acc[1], wv, lr, lh);
 }
 
+// ------------------------------------------------------------------ bf16 decode kernel
+// bf16 weights, decode-shaped groups: stream-K ranges over tiles of 64
+// activation rows x one N block (128 weight rows; each wave 32 weight rows,
+// up: 16 gate rows and the 16 matching up rows), the activations staged by
+// LDS DMA and the weights
+// loaded straight into registers (each lane 8 16-byte pieces of its weight row
+// per chunk). Three chunks are in flight per workgroup (three LDS activation
+// buffers, a three-deep weight register ring): all loads of chunk c+2 are
+// issued at the top of chunk c, right after the barrier, and the wait at the
+// top of a chunk leaves the next chunk's loads outstanding.
+// A group with one row tile has its N tiles next to each other in the
+// schedule, and they read the same activation rows: a workgroup streams such a
+// run of tiles as one sequence of chunks, so the loads run ahead across tile
+// boundaries instead of draining at every tile (with K = 2048 a tile is only
+// 16 chunks); each tile's epilogue is issued as soon as its last chunk is
+// multiplied.
+constexpr int kBfBM = kBM / 2;  // activation rows per tile
+
+// Tiles tl.nt .. tl.nt + n - 1 of one group and row tile, iterations
+// [it_begin, it_end) of the run (iteration k * nchunks + c is chunk c of its
+// tile k). The first / last tile leave fp32 partials in part_first /
+// part_last when split (else nullptr: their epilogue runs here).
+template <int KIND, bool PACKED, int NB, bool STREAM>
+__device__ __forceinline__ void bf_run(const GemmArgs& p, const Tile& tl, int n, const Sched& sh,
+                                       uint16_t* __restrict__ x0, uint16_t* __restrict__ x1,
+                                       uint16_t* __restrict__ x2, int it_begin, int it_end,
+                                       float* __restrict__ part_first, float* __restrict__ part_last) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
+  const int lr = lane & 31;
+  const int lh = lane >> 5;
+  const int nchunks = p.K / kKC;
+  const int last = it_end - 1;
+
+  // weights: this lane's row of the run's first tile; piece j of chunk C covers
+  // k = 128 C + 64 (j / 4) + 32 lh + 8 (j % 4)
+  const uint16_t* W = static_cast<const uint16_t*>(tl.shared ? p.sh_w : p.w);
+  int wrow;
+  if (KIND == kUp) {
+    const int j = tl.nt * 64 + 16 * wv + (lr & 15);
+    wrow = lr < 16 ? j : p.n_out + j;
+  } else {
+    wrow = tl.nt * 128 + 32 * wv + lr;
+  }
+  // uniform base (the expert's block) + the lane's loop-invariant byte offset
+  // (an expert's weights span less than 4 GiB)
+  gptr<char> wbase;
+  uint32_t woff;
+  if constexpr (PACKED) {
+    wbase = uniform_ptr(reinterpret_cast<const char*>(W) +
+                        (size_t(tl.we) * p.n_tiles_n + tl.nt) * nchunks * 4 * 8 * kWave * 16);
+    woff = uint32_t(wv * 8 * kWave + lane) * 16u;
+  } else {
+    wbase = uniform_ptr(reinterpret_cast<const char*>(W + size_t(tl.we) * p.n_w_rows * p.K));
+    woff = uint32_t(wrow * p.K + 32 * lh) * 2u;
+  }
+  // iteration I, piece j: packed, the N tiles of a group follow each other, so
+  // the address is linear in I; row-major, tile k's rows are 64 (gate and up)
+  // or 128 rows below the first tile's
+  const uint64_t tstep = uint64_t(KIND == kUp ? 64 : 128) * p.K * 2;
+  auto wpiece = [&](int I, int j) -> gptr<uint4> {
+    if constexpr (PACKED) {
+      return at<uint4>(wbase, (uint64_t(I) * 4 * 8 + j) * kWave * 16, woff);
+    } else {
+      const int k = I / nchunks, C = I - k * nchunks;
+      return at<uint4>(wbase, k * tstep + uint64_t(C) * kKC * 2 + (j >> 2) * 128 + (j & 3) * 16, woff);
+    }
+  };
+
+  // activations: load q of this wave stages tile rows 4 (4 q + wv) .. + 3
+  constexpr int XL = 2 * NB;  // 1 KiB loads per wave per chunk
+  const uint16_t* A = static_cast<const uint16_t*>(tl.shared ? p.sh_a : p.a);
+  const bool ablk = tl.shared ? p.sh_a_blk : p.a_blk;
+  const size_t xstep = ablk ? size_t(4) * 512 : size_t(kKC);  // elements from one chunk of a row to the next
+  // per-lane byte offsets from the tile's first row (a tile's rows lie in one
+  // expert's region, which the host keeps below 2^31 elements)
+  const int phys0 = sh.rowmap[0];
+  const size_t xbase = ablk ? blk_row_base(phys0, p.K) : size_t(phys0) * p.K;
+  const gptr<char> xb = uniform_ptr(reinterpret_cast<const char*>(A + xbase));
+  uint32_t xoff[XL];
+#pragma unroll
+  for (int q = 0; q < XL; ++q) {
+    const int r = 4 * (4 * q + wv) + (lane >> 4);
+    const int c = (lane & 15) ^ (r & 15);  // column piece this lane's LDS slot holds
+    const int phys = sh.rowmap[r];
+    const int pr = phys >= 0 ? phys : phys0;  // rows past the tile feed only discarded columns
+    xoff[q] = uint32_t((ablk ? blk_row_base(pr, p.K) + size_t(c >> 2) * 512 + (c & 3) * 8 : size_t(pr) * p.K + c * 8) -
+                       xbase) * 2u;
+  }
+
+  f32x16_t acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
+  uint16_t* out = static_cast<uint16_t*>(tl.shared ? p.sh_out : p.out);
+
+  uint4 w0[8], w1[8], w2[8];  // weight ring
+#define MOE_BF_LOADS(I_, XBUF_, WR_)                                                                          \
+  {                                                                                                         \
+    const int c_ = (I_) % nchunks;                                                                          \
+    const size_t xo_ = size_t(c_) * xstep;                                                                  \
+    _Pragma("unroll") for (int q = 0; q < XL; ++q)                                                          \
+      __builtin_amdgcn_global_load_lds(at<void>(xb, xo_ * 2, xoff[q]), (lds_ptr_t)((XBUF_) + (4 * q + wv) * 512), 16, 0, 0); \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j) WR_[j] = ld_w<STREAM>(wpiece(I_, j));                     \
+  }
+  // this wave's loads of the chunk have landed (only the next chunk's, XL + 8
+  // ops, and epilogue stores issued after them may be outstanding: loads
+  // retire in order, so at most over-waiting); after the barrier every wave's
+  // staged rows are visible and nobody still reads the buffer the next loads
+  // overwrite
+#define MOE_BF_SYNC()                                                                                       \
+  __builtin_amdgcn_sched_barrier(0);                                                                        \
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(XL + 8));                                                     \
+  __builtin_amdgcn_s_barrier();                                                                             \
+  __builtin_amdgcn_sched_barrier(0);
+#define MOE_BF_CHUNK(XBUF_, WR_)                                                                            \
+  _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                                           \
+    const int cl_ = 8 * (j >> 2) + 4 * lh + (j & 3);                                                        \
+    _Pragma("unroll") for (int b = 0; b < NB; ++b) {                                                        \
+      const int rr_ = b * 32 + lr;                                                                          \
+      const bf16x8_t bv_ = *reinterpret_cast<const bf16x8_t*>((XBUF_) + rr_ * kKC + ((cl_ ^ (rr_ & 15)) * 8)); \
+      acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, WR_[j]), bv_, acc[b], 0, 0, 0); \
+    }                                                                                                       \
+  }
+  // after iteration I_: if it ends its tile, the tile's epilogue (or partial
+  // sums) and fresh accumulators
+#define MOE_BF_FINISH(I_)                                                                                   \
+  {                                                                                                         \
+    const int k_ = (I_) / nchunks;                                                                          \
+    if ((I_) - k_ * nchunks == nchunks - 1 || (I_) == last) { /* uniform */                                 \
+      float* part_ = k_ == 0 ? part_first : (k_ == n - 1 ? part_last : nullptr);                            \
+      if (part_ == nullptr) {                                                                               \
+        Tile tk_ = tl;                                                                                      \
+        tk_.nt = tl.nt + k_;                                                                                \
+        ffn_epilogue<KIND, NB>(acc, tk_, NB, sh, out, p.n_out, wv, lr, lh, p.out_blk);                      \
+      } else {                                                                                              \
+        _Pragma("unroll") for (int b = 0; b < NB; ++b)                                                      \
+          _Pragma("unroll") for (int v = 0; v < 16; v += 4)                                                 \
+            *reinterpret_cast<float4*>(part_ + (((wv * kMB + b) * 4 + v / 4) * kWave + lane) * 4) =         \
+                make_float4(acc[b][v], acc[b][v + 1], acc[b][v + 2], acc[b][v + 3]);                        \
+      }                                                                                                     \
+      _Pragma("unroll") for (int b = 0; b < NB; ++b)                                                        \
+        _Pragma("unroll") for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;                                     \
+    }                                                                                                       \
+  }
+  // iteration I_ in slot (XA_, WA_); loads iteration I_ + 2 into the slot two ahead (XN_, WN_)
+#define MOE_BF_STEP(I_, XA_, WA_, XN_, WN_)                                                                 \
+  {                                                                                                         \
+    MOE_BF_SYNC()                                                                                           \
+    MOE_BF_LOADS(min((I_) + 2, last), XN_, WN_) /* past the end a harmless repeat */                        \
+    MOE_BF_CHUNK(XA_, WA_)                                                                                  \
+    MOE_BF_FINISH(I_)                                                                                       \
+  }
+
+  MOE_BF_LOADS(it_begin, x0, w0)
+  MOE_BF_LOADS(min(it_begin + 1, last), x1, w1)
+  // (no exit in the middle of the three-chunk body: the accumulators would
+  // need a second copy at the exit)
+  int it = it_begin;
+  for (; it + 3 <= it_end; it += 3) {
+    MOE_BF_STEP(it, x0, w0, x2, w2)
+    MOE_BF_STEP(it + 1, x1, w1, x0, w0)
+    MOE_BF_STEP(it + 2, x2, w2, x1, w1)
+  }
+  if (it + 1 == it_end) {
+    MOE_BF_STEP(it, x0, w0, x2, w2)
+  } else if (it + 2 == it_end) {
+    MOE_BF_STEP(it, x0, w0, x2, w2)
+    MOE_BF_STEP(it + 1, x1, w1, x0, w0)
+  }
+#undef MOE_BF_STEP
+#undef MOE_BF_FINISH
+#undef MOE_BF_LOADS
+#undef MOE_BF_SYNC
+#undef MOE_BF_CHUNK
+  // no load may still be writing LDS when the next run reuses the buffers
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+  __builtin_amdgcn_s_barrier();
+}
+
+// Stream-K over (tile, chunk) iterations; ffn_fixup_kernel finishes the split
+// tiles. XCD-aware range order: workgroups are dispatched round-robin over
+// the 8 XCDs, so range r goes to workgroup (r % 64) * 8 + r / 64; consecutive
+// ranges (the N tiles of one expert, which share its activation rows) then run
+// on one XCD and its L2 fetches those rows once.
+template <int KIND, bool PACKED>
+__global__ __launch_bounds__(kGemmThreads, 2) void ffn_bf16_kernel(GemmArgs p, float* __restrict__ parts) {
+  __shared__ Sched sh;
+  __shared__ __attribute__((aligned(1024))) uint16_t x0[kBfBM * kKC], x1[kBfBM * kKC], x2[kBfBM * kKC];
+  const int n_tiles = build_schedule(p, kBfBM, p.n_tiles_n, false, sh);
+  const int nchunks = p.K / kKC;
+  const int64_t total = int64_t(n_tiles) * nchunks;
+  const int G = sk_grid(total);
+  if (int(blockIdx.x) >= G) return;  // uniform
+  const int rng = int(blockIdx.x % kXcds) * (G / kXcds) + int(blockIdx.x / kXcds);
+  const int64_t i0 = sk_start(rng, total, G), i1 = sk_start(rng + 1, total, G);
+  if (i0 >= i1) return;  // uniform
+  const int t_first = int(i0 / nchunks), t_last = int((i1 - 1) / nchunks);
+  for (int t = t_first; t <= t_last;) {
+    const Tile tl = decode_tile(p, kBfBM, p.n_tiles_n, sh, t);
+    build_rowmap(p, tl, kBfBM, sh);
+    // a run: with one row tile the group's next tiles are its next N tiles
+    // (same activation rows)
+    const int n = tl.mtiles == 1 ? min(t_last - t + 1, p.n_tiles_n - tl.nt) : 1;
+    const int64_t t0 = int64_t(t) * nchunks;
+    const int it_begin = int(max<int64_t>(i0 - t0, 0));
+    const int it_end = int(min<int64_t>(i1 - t0, int64_t(n) * nchunks));
+    // a split tile leaves partials in the workgroup's slot (0 for its first tile, 1 for its last)
+    const bool split_first = it_begin > 0 || (n == 1 && it_end < nchunks);
+    const bool split_last = it_end < n * nchunks;
+    float* part_first = split_first ? sk_slot(parts, rng, t == t_first ? 0 : 1) : nullptr;
+    float* part_last = n == 1 ? part_first : (split_last ? sk_slot(parts, rng, 1) : nullptr);
+    auto run = [&](auto stream_tag) __attribute__((always_inline)) {
+      constexpr bool ST = decltype(stream_tag)::value;
+      if (tl.nrows <= 32) bf_run<KIND, PACKED, 1, ST>(p, tl, n, sh, x0, x1, x2, it_begin, it_end, part_first, part_last);
+      else bf_run<KIND, PACKED, 2, ST>(p, tl, n, sh, x0, x1, x2, it_begin, it_end, part_first, part_last);
+    };
+    if (tl.mtiles == 1) run(std::true_type{});
+    else run(std::false_type{});
+    __syncthreads();  // rowmap is rewritten by the next run
+    t += n;
+  }
+}
+
 // ------------------------------------------------------------------ fp8 kernel
 // fp8 e4m3 weights, decode-shaped groups (W8A16). A tile is 96 activation
 // rows x two adjacent N blocks (up: 2 x 64 h columns; down: 2 x 128 output
@@ -1039,46 +1089,57 @@ __device__ __forceinline__ int f8_part_idx(int wv, int a, int b, int q, int lane
   return ((((wv * 2 + a) * kF8MB + b) * 4 + q) * kWave + lane) * 4;
 }
 
+// Tiles (pairs of N blocks) tl.nt .. tl.nt + n - 1 of one group and row tile,
+// iterations [it_begin, it_end) of the run (as bf_run: with one row tile the
+// group's next tiles read the same activation rows, so the loads run ahead
+// across tile boundaries).
 template <int KIND, bool PACKED, int NB, bool STREAM>
-__device__ __forceinline__ void f8_tile(const GemmArgs& p, const Tile& tl, const Sched& sh, uint16_t* __restrict__ x0,
-                                        uint16_t* __restrict__ x1, int c_begin, int c_end, float* __restrict__ part) {
+__device__ __forceinline__ void f8_run(const GemmArgs& p, const Tile& tl, int n, const Sched& sh,
+                                       uint16_t* __restrict__ x0, uint16_t* __restrict__ x1, int it_begin, int it_end,
+                                       float* __restrict__ part_first, float* __restrict__ part_last) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
   const int lr = lane & 31;
   const int lh = lane >> 5;
   const int nchunks = p.K / kKC;
-  const int last = c_end - 1;
-  const int nt0 = 2 * tl.nt;
-  const bool has1 = nt0 + 1 < p.n_tiles_n;  // uniform: an odd N-block count leaves the last tile one block
-  const int ntb[2] = {nt0, has1 ? nt0 + 1 : nt0};
+  const int last = it_end - 1;
+  // N block of sub-block a of the run's tile k (an odd N-block count leaves a
+  // group's last tile one block: its second sub-block repeats the first)
+  auto ntof = [&](int k, int a) { return min(2 * (tl.nt + k) + a, p.n_tiles_n - 1); };
 
-  // weights: this lane's row in each sub-block, its first chunk, and its block-scale row
+  // weights: uniform base (the expert's block) + the lane's loop-invariant byte
+  // offset (its row in N block 0; an expert's weights span less than 4 GiB)
   const uint8_t* W = static_cast<const uint8_t*>(tl.shared ? p.sh_w : p.w);
-  const float* sbase = (tl.shared ? p.sh_s : p.s) + size_t(tl.we) * (p.n_w_rows / 128) * nchunks;
-  const uint4* wsrc[2];
-  const float* ssrc[2];
-#pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    const int nt = ntb[a];
-    int wrow;
-    if (KIND == kUp) {
-      const int j = nt * 64 + 16 * wv + (lr & 15);
-      wrow = lr < 16 ? j : p.n_out + j;
-    } else {
-      wrow = nt * 128 + 32 * wv + lr;
-    }
-    if constexpr (PACKED)
-      wsrc[a] = reinterpret_cast<const uint4*>(W) + (size_t(tl.we) * p.n_tiles_n + nt) * nchunks * 4 * 4 * kWave +
-                size_t(wv) * 4 * kWave + lane;
-    else
-      wsrc[a] = reinterpret_cast<const uint4*>(W + (size_t(tl.we) * p.n_w_rows + wrow) * p.K + 64 * lh);
-    ssrc[a] = sbase + size_t(wrow / 128) * nchunks;
+  int wrow0;  // this lane's weight row in N block 0
+  if (KIND == kUp) {
+    const int j = 16 * wv + (lr & 15);
+    wrow0 = lr < 16 ? j : p.n_out + j;
+  } else {
+    wrow0 = 32 * wv + lr;
   }
-  // chunk C of sub-block a, 16-byte piece j (of 4)
-  auto wpiece = [&](int a, int C, int j) -> const uint4* {
-    if constexpr (PACKED) return wsrc[a] + (size_t(C) * 4 * 4 + j) * kWave;
-    else return wsrc[a] + size_t(C) * (kKC / 16) + j;
+  gptr<char> wbase;
+  uint32_t woff;
+  if constexpr (PACKED) {
+    wbase = uniform_ptr(reinterpret_cast<const char*>(W) + size_t(tl.we) * p.n_tiles_n * nchunks * 4 * 4 * kWave * 16);
+    woff = uint32_t(wv * 4 * kWave + lane) * 16u;
+  } else {
+    wbase = uniform_ptr(reinterpret_cast<const char*>(W + size_t(tl.we) * p.n_w_rows * p.K));
+    woff = uint32_t(wrow0 * p.K + 64 * lh);
+  }
+  // iteration I = k * nchunks + C: piece j of sub-block a
+  auto wpiece = [&](int k, int C, int a, int j) -> gptr<uint4> {
+    const int nt = ntof(k, a);
+    if constexpr (PACKED) return at<uint4>(wbase, ((uint64_t(nt) * nchunks + C) * 4 * 4 + j) * kWave * 16, woff);
+    else return at<uint4>(wbase, uint64_t(nt) * (KIND == kUp ? 64 : 128) * p.K + uint64_t(C) * kKC + j * 16, woff);
+  };
+  // block scales: 128-row blocks; up: gate rows of N block nt lie in block
+  // nt / 2, its up rows in block I / 128 + nt / 2; down: block nt
+  const float* sl = (tl.shared ? p.sh_s : p.s) + size_t(tl.we) * (p.n_w_rows / 128) * nchunks +
+                    size_t(KIND == kUp && lr >= 16 ? p.n_out / 128 : 0) * nchunks;
+  auto scale = [&](int k, int C, int a) {
+    const int nt = ntof(k, a);
+    return sl[(KIND == kUp ? nt >> 1 : nt) * nchunks + C];
   };
 
   // activations: load q of this wave stages tile rows 4 (4 q + wv) .. + 3
@@ -1086,15 +1147,20 @@ __device__ __forceinline__ void f8_tile(const GemmArgs& p, const Tile& tl, const
   const uint16_t* A = static_cast<const uint16_t*>(tl.shared ? p.sh_a : p.a);
   const bool ablk = tl.shared ? p.sh_a_blk : p.a_blk;
   const size_t xstep = ablk ? size_t(4) * 512 : size_t(kKC);  // elements from one chunk of a row to the next
-  const uint16_t* xg[XL];
+  // per-lane byte offsets from the tile's first row (a tile's rows lie in one
+  // expert's region, which the host keeps below 2^31 elements)
   const int phys0 = sh.rowmap[0];
+  const size_t xbase = ablk ? blk_row_base(phys0, p.K) : size_t(phys0) * p.K;
+  const gptr<char> xb = uniform_ptr(reinterpret_cast<const char*>(A + xbase));
+  uint32_t xoff[XL];
 #pragma unroll
   for (int q = 0; q < XL; ++q) {
     const int r = 4 * (4 * q + wv) + (lane >> 4);
     const int c = (lane & 15) ^ (r & 15);  // column piece this lane's LDS slot holds
     const int phys = r < NB * 32 ? sh.rowmap[r] : -1;
     const int pr = phys >= 0 ? phys : phys0;  // rows past the tile feed only discarded columns
-    xg[q] = A + (ablk ? blk_row_base(pr, p.K) + size_t(c >> 2) * 512 + (c & 3) * 8 : size_t(pr) * p.K + c * 8);
+    xoff[q] = uint32_t((ablk ? blk_row_base(pr, p.K) + size_t(c >> 2) * 512 + (c & 3) * 8 : size_t(pr) * p.K + c * 8) -
+                       xbase) * 2u;
   }
 
   f32x16_t acc[2][NB];
@@ -1104,30 +1170,34 @@ __device__ __forceinline__ void f8_tile(const GemmArgs& p, const Tile& tl, const
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
+  uint16_t* out = static_cast<uint16_t*>(tl.shared ? p.sh_out : p.out);
 
-  // Two-deep ring (even / odd chunks of the range). Per chunk the vector-memory
-  // ops go out in the order: activation DMA of the next chunk, its two scales,
-  // its 8 weight pieces. (With LDS-DMA and register loads both outstanding the
-  // compiler waits for all of them before the first use of any, so every load
-  // of a chunk is issued one chunk ahead, before the first use.)
+  // Two-deep ring (even / odd iterations of the run). Per iteration the
+  // vector-memory ops go out in the order: activation DMA of the next
+  // iteration, its two scales, its 8 weight pieces. (With LDS-DMA and register
+  // loads both outstanding the compiler waits for all of them before the first
+  // use of any, so every load of an iteration is issued one iteration ahead,
+  // before the first use.)
   // Software pipeline, one 16-deep step at a time (fenced, so the compiler
   // cannot hoist a whole chunk of fragment reads): step j reads its activation
-  // fragments, dequantises the weights of step j + 1 (step 0 of the next chunk
-  // after step 7) and issues its MFMAs with the fragments dequantised before.
+  // fragments, dequantises the weights of step j + 1 (step 0 of the next
+  // iteration after step 7) and issues its MFMAs with the fragments
+  // dequantised before.
   uint4 w0[2][4], w1[2][4];  // [sub-block][piece]
   float s0[2], s1[2];        // block scales
   bf16x8_t fa[2];            // weight fragments of the current step
-#define MOE_F8_LOADS(C_, XBUF_, WR_, SR_)                                                                     \
+#define MOE_F8_LOADS(I_, XBUF_, WR_, SR_)                                                                     \
   {                                                                                                         \
-    const size_t xo_ = size_t(C_) * xstep;                                                                  \
+    const int k_ = (I_) / nchunks, c_ = (I_) - k_ * nchunks;                                                \
+    const size_t xo_ = size_t(c_) * xstep;                                                                  \
     _Pragma("unroll") for (int q = 0; q < XL; ++q)                                                          \
-      __builtin_amdgcn_global_load_lds(xg[q] + xo_, (lds_ptr_t)((XBUF_) + (4 * q + wv) * 512), 16, 0, 0);     \
-    _Pragma("unroll") for (int a = 0; a < 2; ++a) SR_[a] = ssrc[a][C_];                                     \
+      __builtin_amdgcn_global_load_lds(at<void>(xb, xo_ * 2, xoff[q]), (lds_ptr_t)((XBUF_) + (4 * q + wv) * 512), 16, 0, 0); \
+    _Pragma("unroll") for (int a = 0; a < 2; ++a) SR_[a] = scale(k_, c_, a);                                \
     _Pragma("unroll") for (int a = 0; a < 2; ++a)                                                           \
-      _Pragma("unroll") for (int j = 0; j < 4; ++j) WR_[a][j] = ld_w<STREAM>(wpiece(a, C_, j));             \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j) WR_[a][j] = ld_w<STREAM>(wpiece(k_, c_, a, j));         \
   }
-  // all of this wave's loads of the chunk have landed; after the barrier every
-  // wave's staged rows are visible and nobody still reads the other buffer
+  // all of this wave's loads of the iteration have landed; after the barrier
+  // every wave's staged rows are visible and nobody still reads the other buffer
 #define MOE_F8_SYNC()                                                                                       \
   __builtin_amdgcn_sched_barrier(0);                                                                        \
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));                                                          \
@@ -1137,7 +1207,7 @@ __device__ __forceinline__ void f8_tile(const GemmArgs& p, const Tile& tl, const
   _Pragma("unroll") for (int a = 0; a < 2; ++a) DST_[a] =                                                   \
       ((J_) & 1) ? fp8x8_dequant(WR_[a][(J_) >> 1].z, WR_[a][(J_) >> 1].w, SR_[a])                          \
                  : fp8x8_dequant(WR_[a][(J_) >> 1].x, WR_[a][(J_) >> 1].y, SR_[a]);
-  // chunk in (XBUF_, WR_, SR_); the next chunk's weights are in (WN_, SN_)
+  // iteration in (XBUF_, WR_, SR_); the next iteration's weights are in (WN_, SN_)
 #define MOE_F8_CHUNK(XBUF_, WR_, SR_, WN_, SN_)                                                             \
   _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                                           \
     const int cl_ = 8 * lh + j; /* 16-byte column: k = 64 lh + 8 j */                                       \
@@ -1160,61 +1230,69 @@ __device__ __forceinline__ void f8_tile(const GemmArgs& p, const Tile& tl, const
     fa[1] = na_[1];                                                                                         \
     __builtin_amdgcn_sched_barrier(0);                                                                      \
   }
-  // even chunk: activations in x0, weights in (w0, s0); loads chunk CN_
-#define MOE_F8_EVEN(CN_)                                                                                    \
+  // after iteration I_: if it ends its tile, the tile's epilogue (or partial
+  // sums) and fresh accumulators
+#define MOE_F8_FINISH(I_)                                                                                   \
+  {                                                                                                         \
+    const int k_ = (I_) / nchunks;                                                                          \
+    if ((I_) - k_ * nchunks == nchunks - 1 || (I_) == last) { /* uniform */                                 \
+      float* part_ = k_ == 0 ? part_first : (k_ == n - 1 ? part_last : nullptr);                            \
+      if (part_ == nullptr) {                                                                               \
+        _Pragma("unroll") for (int a = 0; a < 2; ++a) {                                                     \
+          Tile ta_ = tl;                                                                                    \
+          ta_.nt = 2 * (tl.nt + k_) + a;                                                                    \
+          if (ta_.nt < p.n_tiles_n) ffn_epilogue<KIND, NB>(acc[a], ta_, NB, sh, out, p.n_out, wv, lr, lh, p.out_blk); \
+        }                                                                                                   \
+      } else {                                                                                              \
+        _Pragma("unroll") for (int a = 0; a < 2; ++a)                                                       \
+          _Pragma("unroll") for (int b = 0; b < NB; ++b)                                                    \
+            _Pragma("unroll") for (int v = 0; v < 16; v += 4)                                               \
+              *reinterpret_cast<float4*>(part_ + f8_part_idx(wv, a, b, v / 4, lane)) =                      \
+                  make_float4(acc[a][b][v], acc[a][b][v + 1], acc[a][b][v + 2], acc[a][b][v + 3]);          \
+      }                                                                                                     \
+      _Pragma("unroll") for (int a = 0; a < 2; ++a)                                                         \
+        _Pragma("unroll") for (int b = 0; b < NB; ++b)                                                      \
+          _Pragma("unroll") for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;                                \
+    }                                                                                                       \
+  }
+  // even iteration I_: activations in x0, weights in (w0, s0); loads iteration IN_
+#define MOE_F8_EVEN(I_, IN_)                                                                                \
   {                                                                                                         \
     MOE_F8_SYNC()                                                                                           \
-    MOE_F8_LOADS(CN_, x1, w1, s1)                                                                           \
+    MOE_F8_LOADS(IN_, x1, w1, s1)                                                                           \
     MOE_F8_CHUNK(x0, w0, s0, w1, s1)                                                                        \
+    MOE_F8_FINISH(I_)                                                                                       \
   }
 
-  MOE_F8_LOADS(c_begin, x0, w0, s0)
+  MOE_F8_LOADS(it_begin, x0, w0, s0)
   MOE_F8_DEQ(fa, w0, 0, s0)
-  // (no exit in the middle of the two-chunk body: the accumulators would
+  // (no exit in the middle of the two-iteration body: the accumulators would
   // need a second copy at the exit)
-  int c = c_begin;
-  for (; c + 1 < c_end; c += 2) {
-    MOE_F8_EVEN(c + 1)
+  int it = it_begin;
+  for (; it + 1 < it_end; it += 2) {
+    MOE_F8_EVEN(it, it + 1)
     {
-      const int cn = min(c + 2, last);  // past the end a harmless repeat
+      const int in = min(it + 2, last);  // past the end a harmless repeat
       MOE_F8_SYNC()
-      MOE_F8_LOADS(cn, x0, w0, s0)
+      MOE_F8_LOADS(in, x0, w0, s0)
       MOE_F8_CHUNK(x1, w1, s1, w0, s0)
+      MOE_F8_FINISH(it + 1)
     }
   }
-  if (c < c_end) MOE_F8_EVEN(last)  // odd count: the last chunk, then a harmless repeat
+  if (it < it_end) MOE_F8_EVEN(it, last)  // odd count: the last iteration, then a harmless repeat
 #undef MOE_F8_EVEN
+#undef MOE_F8_FINISH
 #undef MOE_F8_LOADS
 #undef MOE_F8_SYNC
 #undef MOE_F8_DEQ
 #undef MOE_F8_CHUNK
-  // no load may still be writing LDS when the next tile reuses the buffers
+  // no load may still be writing LDS when the next run reuses the buffers
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
   __builtin_amdgcn_s_barrier();
-
-  if (part == nullptr) {
-    uint16_t* out = static_cast<uint16_t*>(tl.shared ? p.sh_out : p.out);
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      if (a == 1 && !has1) break;
-      Tile ta = tl;
-      ta.nt = ntb[a];
-      ffn_epilogue<KIND, NB>(acc[a], ta, NB, sh, out, p.n_out, wv, lr, lh, p.out_blk);
-    }
-  } else {
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int v = 0; v < 16; v += 4)
-          *reinterpret_cast<float4*>(part + f8_part_idx(wv, a, b, v / 4, lane)) =
-              make_float4(acc[a][b][v], acc[a][b][v + 1], acc[a][b][v + 2], acc[a][b][v + 3]);
-  }
 }
 
-// Stream-K over (tile, chunk) iterations exactly as ffn_mfma_kernel, with
-// tiles of 96 rows x two N blocks.
+// Stream-K over (tile, chunk) iterations as ffn_bf16_kernel, with tiles of 96
+// rows x two N blocks, streamed in runs as there.
 template <int KIND, bool PACKED>
 __global__ __launch_bounds__(kGemmThreads, 2) void ffn_fp8_kernel(GemmArgs p, float* __restrict__ parts) {
   __shared__ Sched sh;
@@ -1229,23 +1307,29 @@ __global__ __launch_bounds__(kGemmThreads, 2) void ffn_fp8_kernel(GemmArgs p, fl
   const int64_t i0 = sk_start(rng, total, G), i1 = sk_start(rng + 1, total, G);
   if (i0 >= i1) return;  // uniform
   const int t_first = int(i0 / nchunks), t_last = int((i1 - 1) / nchunks);
-  for (int t = t_first; t <= t_last; ++t) {
+  for (int t = t_first; t <= t_last;) {
     const Tile tl = decode_tile(p, kF8BM, ntn2, sh, t);
     build_rowmap(p, tl, kF8BM, sh);
-    const int cb = int(max<int64_t>(i0, int64_t(t) * nchunks) - int64_t(t) * nchunks);
-    const int ce = int(min<int64_t>(i1, int64_t(t + 1) * nchunks) - int64_t(t) * nchunks);
-    float* part = (cb == 0 && ce == nchunks) ? nullptr : f8_slot(parts, rng, t == t_first ? 0 : 1);
+    const int n = tl.mtiles == 1 ? min(t_last - t + 1, ntn2 - tl.nt) : 1;
+    const int64_t t0 = int64_t(t) * nchunks;
+    const int it_begin = int(max<int64_t>(i0 - t0, 0));
+    const int it_end = int(min<int64_t>(i1 - t0, int64_t(n) * nchunks));
+    const bool split_first = it_begin > 0 || (n == 1 && it_end < nchunks);
+    const bool split_last = it_end < n * nchunks;
+    float* part_first = split_first ? f8_slot(parts, rng, t == t_first ? 0 : 1) : nullptr;
+    float* part_last = n == 1 ? part_first : (split_last ? f8_slot(parts, rng, 1) : nullptr);
     auto run = [&](auto stream_tag) __attribute__((always_inline)) {
       constexpr bool ST = decltype(stream_tag)::value;
       switch ((tl.nrows + 31) / 32) {
-        case 1: f8_tile<KIND, PACKED, 1, ST>(p, tl, sh, x0, x1, cb, ce, part); break;
-        case 2: f8_tile<KIND, PACKED, 2, ST>(p, tl, sh, x0, x1, cb, ce, part); break;
-        default: f8_tile<KIND, PACKED, 3, ST>(p, tl, sh, x0, x1, cb, ce, part); break;
+        case 1: f8_run<KIND, PACKED, 1, ST>(p, tl, n, sh, x0, x1, it_begin, it_end, part_first, part_last); break;
+        case 2: f8_run<KIND, PACKED, 2, ST>(p, tl, n, sh, x0, x1, it_begin, it_end, part_first, part_last); break;
+        default: f8_run<KIND, PACKED, 3, ST>(p, tl, n, sh, x0, x1, it_begin, it_end, part_first, part_last); break;
       }
     };
     if (tl.mtiles == 1) run(std::true_type{});
     else run(std::false_type{});
-    __syncthreads();  // rowmap is rewritten by the next tile
+    __syncthreads();  // rowmap is rewritten by the next run
+    t += n;
   }
 }
 
@@ -1291,7 +1375,7 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_fp8_fixup_kernel(GemmArgs p,
 // ------------------------------------------------------------------ weight packing
 // Packed layout: for expert g, N block nt (64 h columns = 128 rows of W13, or
 // 128 rows of W2) and 128-deep K chunk c, the 32 rows x 128 k of each of the 4
-// waves, in the order the lanes of ffn_mfma_kernel load them:
+// waves, in the order the lanes of the decode kernels load them:
 // [g][nt][c][wave][load i][lane][16 bytes]. One load instruction of a wave then
 // reads 1 KiB of contiguous memory and a workgroup streams one sequential
 // region, instead of 128 rows in 256-byte pieces. It is a permutation of the
@@ -1492,12 +1576,12 @@ static moe_status_t launch_stage(const GemmArgs& p, bool f32, bool fp8, int kind
     else hipLaunchKernelGGL((ffn_fp8_fixup_kernel<kDown>), fix_grid, block, 0, stream, p, parts);
     return launch_status();
   }
-#define MOE_FFN(K, P) hipLaunchKernelGGL((ffn_mfma_kernel<K, P>), grid, block, 0, stream, p, parts)
+#define MOE_FFN(K, P) hipLaunchKernelGGL((ffn_bf16_kernel<K, P>), grid, block, 0, stream, p, parts)
   if (kind == kUp) { if (p.packed) MOE_FFN(kUp, true); else MOE_FFN(kUp, false); }
   else { if (p.packed) MOE_FFN(kDown, true); else MOE_FFN(kDown, false); }
 #undef MOE_FFN
   if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
-  // (the tile height must match ffn_mfma_kernel)
+  // (the tile height must match ffn_bf16_kernel)
   const dim3 fix_grid(kSkGrid - 1, kBM / 2 / 32);
   if (kind == kUp) hipLaunchKernelGGL((ffn_fixup_kernel<kUp, kBM / 2>), fix_grid, block, 0, stream, p, parts);
   else hipLaunchKernelGGL((ffn_fixup_kernel<kDown, kBM / 2>), fix_grid, block, 0, stream, p, parts);
@@ -1528,6 +1612,11 @@ MOE_API moe_status_t moe_grouped_gemm(const moe_ggemm_desc_t* d, const void* a, 
     if (fp8 && ((up && !se->s13) || (down && !se->s2))) return MOE_ERR_INVALID_ARG;
   }
   if (!ws || !aligned16(ws) || ws_bytes < moe_grouped_gemm_workspace(d)) return MOE_ERR_WORKSPACE;
+  // the decode kernels address a tile's activation rows relative to its first
+  // row: one expert's padded region must span fewer than 2^31 elements
+  if (!f32 && d->layout == MOE_LAYOUT_PADDED &&
+      (int64_t(d->n_src) * d->capacity + 16) * std::max(d->hidden, d->inter) >= (int64_t(1) << 31))
+    return MOE_ERR_UNSUPPORTED;
 
   void* h = ws;
   void* sh_h = static_cast<char*>(ws) + h_bytes(d, d->rows);

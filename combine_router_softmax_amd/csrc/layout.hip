@@ -17,8 +17,9 @@
 //   pass 2 (scan):  one workgroup per local expert: exclusive scan of its tile
 //                   counts, per-source counts, expert totals.
 //   pass 3 (rank):  one workgroup per tile: stable rank of each entry inside
-//                   its tile (ballot + popcount over the lanes holding the same
-//                   expert, then across the 4 waves), row = tile base + rank;
+//                   its tile (popcount over the lower lanes holding the same
+//                   expert, found with one ballot per bit of the expert index,
+//                   then across the 4 waves), row = tile base + rank;
 //                   every workgroup also marks unused rows with -1.
 //
 // Tiles never straddle a source rank, so the fixed-rectangle rank inside a
@@ -33,6 +34,7 @@ constexpr int kLayoutThreads = 256;
 constexpr int kTileTokens = 256;
 constexpr int kMaxSrc = 4096;
 constexpr int kMaxLocal = 1024;
+constexpr int kBatch = 8;  // entries per thread whose index loads are in flight together
 
 struct LayoutWs {
   int32_t* prefix;  // [L][tcap]: pass 1 tile counts, pass 2 turns them into exclusive prefixes
@@ -115,9 +117,17 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_hist_kernel(LayoutArgs 
   const int t1 = min(t0 + kTileTokens, off[s + 1]);
   const int n_ent = (t1 - t0) * p.top_k;
   const int32_t* idx = p.topk_idx + size_t(t0) * p.top_k;
-  for (int i = threadIdx.x; i < n_ent; i += kLayoutThreads) {
-    const unsigned le = unsigned(idx[i]) - unsigned(p.expert_lo);
-    if (le < unsigned(p.n_local)) atomicAdd(&hist[le], 1);
+  // kBatch entries per thread loaded before their atomics
+  for (int i0 = 0; i0 < n_ent; i0 += kBatch * kLayoutThreads) {
+    unsigned le[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = i0 + u * kLayoutThreads + threadIdx.x;
+      le[u] = i < n_ent ? unsigned(idx[i]) - unsigned(p.expert_lo) : ~0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (le[u] < unsigned(p.n_local)) atomicAdd(&hist[le[u]], 1);
   }
   __syncthreads();
   for (int le = threadIdx.x; le < p.n_local; le += kLayoutThreads)
@@ -237,22 +247,38 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(LayoutArgs 
   const int w = tid / kWave;
   const uint64_t lt_mask = (uint64_t(1) << lane) - 1;
   const size_t ent0 = size_t(t0) * K;
+  int nbits = 0;  // bits of a local expert index
+  while ((1 << nbits) < L) ++nbits;
+  int lev[kBatch];
 
   for (int r0 = 0; r0 < n_ent; r0 += kLayoutThreads) {
+    // the indices of kBatch rounds are loaded together
+    const int u = (r0 / kLayoutThreads) % kBatch;
+    if (u == 0) {
+#pragma unroll
+      for (int v = 0; v < kBatch; ++v) {
+        const int iv = r0 + v * kLayoutThreads + tid;
+        lev[v] = iv < n_ent ? int(unsigned(p.topk_idx[ent0 + iv]) - unsigned(p.expert_lo)) : -1;
+      }
+    }
+    int le = lev[0];
+#pragma unroll
+    for (int v = 1; v < kBatch; ++v)
+      if (u == v) le = lev[v];
     const int i = r0 + tid;
     const bool valid = i < n_ent;
-    const int le = valid ? int(unsigned(p.topk_idx[ent0 + i]) - unsigned(p.expert_lo)) : -1;
     const bool local = valid && unsigned(le) < unsigned(L);
-    uint64_t pending = __ballot(local);
-    int in_rank = 0;
-    while (pending) {
-      const int leader = __ffsll((unsigned long long)pending) - 1;
-      const int lle = __shfl(le, leader, kWave);
-      const uint64_t m = __ballot(local && le == lle);
-      if (local && le == lle) in_rank = __popcll(m & lt_mask);
-      if (lane == leader) wtot[w][lle] = __popcll(m);
-      pending &= ~m;
+    // lanes holding the same local expert: one ballot per bit of the expert
+    // index (a lane keeps the lanes that agree with it on every bit), so the
+    // cost does not grow with the number of distinct experts in the wave
+    uint64_t same = __ballot(local);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool set = local && ((le >> bit) & 1);
+      const uint64_t m = __ballot(set);
+      same &= set ? m : ~m;
     }
+    const int in_rank = __popcll(same & lt_mask);
+    if (local && in_rank == 0) wtot[w][le] = __popcll(same);  // the expert's first lane
     __syncthreads();
     if (valid) {
       int row = -1;

@@ -145,6 +145,19 @@ def test_layout_arbitrary_indices():
         _layout_check(idx, off, 12, 3, 6, layout, cap)
 
 
+@pytest.mark.parametrize("L", [1, 3, 64, 100, 256, 1024])
+def test_layout_local_expert_counts(L):
+    # one local expert (no index bits), non-powers of two, every expert local
+    rng = np.random.default_rng(L)
+    E = max(L + 7, 16)
+    N, K = 900, 6
+    idx = rng.integers(0, E, size=(N, K)).astype(np.int32)
+    off = np.array([0, 100, 356, 357, 900])
+    lo = E - L - 3
+    for layout, cap in [(COMPACT, N * K), (PADDED, 300)]:
+        _layout_check(idx, off, E, lo, L, layout, cap)
+
+
 # --------------------------------------------------------------------------- dispatch
 @pytest.mark.parametrize("layout", [COMPACT, PADDED])
 @pytest.mark.parametrize("seed", range(8))
