@@ -180,6 +180,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="dsv3_decode_ep8")
     ap.add_argument("--layout", choices=["compact", "padded"], default="compact")
+    ap.add_argument("--gemm-policy", choices=["layer", "auto", "wide", "stream_k"], default="layer",
+                    help="grouped-GEMM kernel choice (default: the layer's own, from its shape)")
     ap.add_argument("--xe-layout", choices=["auto", "rows", "blocked"], default="auto",
                     help="storage of the expert rows (auto: the layer's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -209,6 +211,7 @@ def main(argv=None):
         print(json.dumps({"copy_calib_bytes": 1 << 30, "launches": 3}))
         return 0
 
+    import combine_router_softmax_amd as moe
     from combine_router_softmax_amd import COMPACT, PADDED
     from combine_router_softmax_amd.layer import MoEShare
     from synth import get_config, make_inputs
@@ -225,7 +228,9 @@ def main(argv=None):
     share = MoEShare(n_tokens=N, hidden=cfg.hidden, inter=cfg.inter, n_experts=cfg.n_experts, top_k=cfg.top_k,
                      n_src=cfg.n_src, expert_lo=cfg.expert_lo, n_local=cfg.n_local, act_dtype=act, layout=layout,
                      capacity=cap, self_range=(0, B0),
-                     blocked=None if args.xe_layout == "auto" else args.xe_layout == "blocked")
+                     blocked=None if args.xe_layout == "auto" else args.xe_layout == "blocked",
+                     policy={"layer": None, "auto": moe.GEMM_AUTO, "wide": moe.GEMM_WIDE,
+                             "stream_k": moe.GEMM_STREAM_K}[args.gemm_policy])
     share.set_weights(d["routed"], d["shared"])
     logits = torch.from_numpy(d["logits"]).cuda()
     offs = torch.from_numpy(off).cuda()

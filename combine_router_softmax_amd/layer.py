@@ -24,7 +24,7 @@ class MoEShare:
     def __init__(self, *, n_tokens: int, hidden: int, inter: int, n_experts: int, top_k: int, n_src: int,
                  expert_lo: int, n_local: int, act_dtype: torch.dtype, layout: int = COMPACT,
                  capacity: Optional[int] = None, self_range=(0, 0), device="cuda",
-                 blocked: Optional[bool] = None):
+                 blocked: Optional[bool] = None, policy: Optional[int] = None):
         self.N, self.H, self.I, self.E, self.K = n_tokens, hidden, inter, n_experts, top_k
         self.S, self.lo, self.L = n_src, expert_lo, n_local
         self.layout = layout
@@ -51,7 +51,7 @@ class MoEShare:
         # enough rows take the wide-tile kernel for every group (what the AUTO
         # rule picks for them) without an empty stream-K launch; decode-sized
         # batches take the stream-K kernel without an empty wide launch
-        self.policy = GEMM_WIDE if many_rows else GEMM_STREAM_K
+        self.policy = (GEMM_WIDE if many_rows else GEMM_STREAM_K) if policy is None else policy
         d = self.dev
         self.topk_idx = torch.empty((n_tokens, top_k), dtype=torch.int32, device=d)
         self.topk_w = torch.empty((n_tokens, top_k), dtype=torch.float32, device=d)
