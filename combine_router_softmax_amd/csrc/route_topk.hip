@@ -2,13 +2,14 @@
 // weights (Perplexity, "Lower latency and higher throughput with multi-node
 // DeepSeek deployment", section MoE Router).
 //
-// One wavefront per token. Each lane holds ceil(E/64) logits as 64-bit keys
-// (order-preserving integer image of the fp32 logit in the high word, the
-// complement of the expert index in the low word), so one unsigned max picks
-// the highest logit and, among equal logits, the lowest index. K rounds of a
-// wave-wide max (xor butterfly) select the experts in order; the selection is
-// exact integer comparison, no exp involved. Weights use the fp32 exp of
-// (logit - max).
+// One wavefront per token. Each lane holds ceil(E/64) logits as 32-bit
+// order-preserving integer keys (expert j * 64 + lane), so an unsigned max is
+// the highest logit. K rounds select the experts in order: each lane takes its
+// best live key (the lowest index among equal keys), a wave-wide max over the
+// lanes (DPP row shifts and broadcasts, then a lane read) gives the round's
+// key, a ballot finds the lanes holding it, and among several (equal logits)
+// the lowest expert index wins. The selection is exact integer comparison, no
+// exp involved. Weights use the fp32 exp of (logit - max).
 #include "moe_common.hpp"
 
 namespace moe {
@@ -27,11 +28,27 @@ __device__ __forceinline__ float key_value(uint32_t k) {
   return __uint_as_float(u);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+// max over the wave's 64 lanes: within each row of 16 lanes by right shifts of
+// 1, 2, 3, 4 and 8 (lane 15 of a row then holds the row's max), across rows by
+// the row-15 and row-31 broadcasts (lane 63 then holds the wave's max); lanes
+// a shift reads from outside the row get 0, the identity of an unsigned max
+__device__ __forceinline__ uint32_t dpp_max(uint32_t v, uint32_t o) { return o > v ? o : v; }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = dpp_max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x111, 0xf, 0xf, false)));  // row_shr:1
+  v = dpp_max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x112, 0xf, 0xf, false)));  // row_shr:2
+  v = dpp_max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x113, 0xf, 0xf, false)));  // row_shr:3
+  v = dpp_max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x114, 0xf, 0xe, false)));  // row_shr:4
+  v = dpp_max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x118, 0xf, 0xc, false)));  // row_shr:8
+  v = dpp_max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x142, 0xa, 0xf, false)));  // row_bcast:15
+  v = dpp_max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x143, 0xc, 0xf, false)));  // row_bcast:31
+  return uint32_t(__builtin_amdgcn_readlane(int(v), 63));
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
-    const uint64_t o = __shfl_xor((unsigned long long)v, off, kWave);
-    v = o > v ? o : v;
+    const uint32_t o = uint32_t(__shfl_xor(int(v), off, kWave));
+    v = o < v ? o : v;
   }
   return v;
 }
@@ -52,34 +69,47 @@ __global__ __launch_bounds__(kWave * kRouteTokensPerBlock) void route_topk_kerne
   const float* row = logits + size_t(t) * n_experts;
 
   float val[VPL];
-  uint64_t cand[VPL];
+  uint32_t key[VPL];  // 0: no expert here, or already selected (no real logit maps to 0 but -NaN)
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
     const int e = j * kWave + lane;
-    if (e < n_experts) {
-      val[j] = row[e];
-      cand[j] = (uint64_t(order_key(val[j])) << 32) | uint64_t(0xFFFFFFFFu - uint32_t(e));
-    } else {
-      val[j] = 0.f;
-      cand[j] = 0;  // below every real key (a real key's low word is > 0)
+    val[j] = e < n_experts ? row[e] : 0.f;
+    key[j] = e < n_experts ? order_key(val[j]) : 0u;
+  }
+
+  uint32_t mine_key = 0;  // lane k keeps the k-th winner
+  int mine_idx = 0;
+  for (int k = 0; k < top_k; ++k) {
+    // this lane's best live key; the lowest j among equal keys
+    uint32_t lb = 0;
+    int lj = 0;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j)
+      if (key[j] > lb) {
+        lb = key[j];
+        lj = j;
+      }
+    const uint32_t m = wave_max_u32(lb);
+    const bool holder = lb == m && m != 0;
+    const uint64_t h = __ballot(holder);
+    int e;
+    if (__popcll(h) == 1) {  // uniform: one lane holds the round's key
+      const int hl = __ffsll((unsigned long long)h) - 1;
+      e = __builtin_amdgcn_readlane(lj * kWave + lane, hl);
+    } else {  // equal logits on several lanes: the lowest expert index
+      e = int(wave_min_u32(holder ? uint32_t(lj * kWave + lane) : 0xFFFFFFFFu));
+    }
+#pragma unroll
+    for (int j = 0; j < VPL; ++j)
+      if (j * kWave + lane == e) key[j] = 0;
+    if (lane == k) {
+      mine_key = m;
+      mine_idx = e;
     }
   }
 
-  uint64_t mine = 0;  // lane k keeps the k-th winner
-  for (int k = 0; k < top_k; ++k) {
-    uint64_t best = cand[0];
-#pragma unroll
-    for (int j = 1; j < VPL; ++j) best = cand[j] > best ? cand[j] : best;
-    best = wave_max_u64(best);
-    const int e = int(0xFFFFFFFFu - uint32_t(best));
-#pragma unroll
-    for (int j = 0; j < VPL; ++j)
-      if (j * kWave + lane == e) cand[j] = 0;
-    if (lane == k) mine = best;
-  }
-
-  const float vmax = key_value(uint32_t((unsigned long long)__shfl((unsigned long long)mine, 0, kWave) >> 32));
-  const float v = key_value(uint32_t(mine >> 32));
+  const float vmax = key_value(uint32_t(__builtin_amdgcn_readlane(int(mine_key), 0)));
+  const float v = key_value(mine_key);
   const float ex = lane < top_k ? expf(v - vmax) : 0.f;
   float denom;
   if (renorm) {
@@ -92,7 +122,7 @@ __global__ __launch_bounds__(kWave * kRouteTokensPerBlock) void route_topk_kerne
     denom = wave_sum_f32(part);
   }
   if (lane < top_k) {
-    topk_idx[size_t(t) * top_k + lane] = int32_t(0xFFFFFFFFu - uint32_t(mine));
+    topk_idx[size_t(t) * top_k + lane] = int32_t(mine_idx);
     topk_w[size_t(t) * top_k + lane] = ex / denom;
   }
 }
