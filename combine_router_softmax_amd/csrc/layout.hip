@@ -11,7 +11,7 @@
 // be the token order and bit-reproducible, so ranks come from wavefront
 // ballots instead of atomics, and the work is spread over many workgroups:
 //
-//   pass 1 (hist):  one workgroup per tile of <= 256 tokens of one source;
+//   pass 1 (hist):  one workgroup per tile of <= 64 tokens of one source;
 //                   per-tile counts per local expert (LDS integer atomics:
 //                   order-free, deterministic totals).
 //   pass 2 (scan):  one workgroup per local expert: exclusive scan of its tile
@@ -31,7 +31,7 @@ namespace moe {
 namespace {
 
 constexpr int kLayoutThreads = 256;
-constexpr int kTileTokens = 256;
+constexpr int kTileTokens = 64;
 constexpr int kMaxSrc = 4096;
 constexpr int kMaxLocal = 1024;
 constexpr int kBatch = 8;  // entries per thread whose index loads are in flight together
