@@ -16,6 +16,8 @@
 //                   order-free, deterministic totals).
 //   pass 2 (scan):  one workgroup per local expert: exclusive scan of its tile
 //                   counts, per-source counts, expert totals.
+//   (small layouts fold pass 2 into pass 3: each workgroup scans the tile
+//   counts in LDS itself; see layout_rank_kernel)
 //   pass 3 (rank):  one workgroup per tile: stable rank of each entry inside
 //                   its tile (popcount over the lower lanes holding the same
 //                   expert, found with one ballot per bit of the expert index,
@@ -177,6 +179,13 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_scan_kernel(LayoutArgs 
   }
 }
 
+// FUSED (small layouts, L * (tcap + 1) <= kFusedPrefix): pass 2 is folded in.
+// Every workgroup scans all experts' tile counts in LDS itself (pre[le][b] =
+// the expert's count in tiles before b), and workgroup 0 writes the
+// per-source counts and the status; one launch fewer.
+constexpr int kFusedPrefix = 8192;
+
+template <bool FUSED>
 __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(LayoutArgs p) {
   __shared__ int off[kMaxSrc + 1];
   __shared__ int ts[kMaxSrc + 1];
@@ -185,12 +194,38 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(LayoutArgs 
   __shared__ int base[kMaxLocal];
   __shared__ int running[kMaxLocal];
   __shared__ int wtot[kLayoutThreads / kWave][kMaxLocal];
+  extern __shared__ int pre[];  // FUSED: [L][tcap + 1]
   const int tid = threadIdx.x;
   const int L = p.n_local;
   const int n_tiles = build_tile_map(p.src_offsets, p.n_src, p.n_tokens, off, ts, tmp);
+  const int PW = p.tcap + 1;  // FUSED: row pitch of pre
+  if (FUSED) {
+    for (int i = tid; i < L * n_tiles; i += kLayoutThreads) {
+      const int le = i / n_tiles, b = i - le * n_tiles;
+      pre[le * PW + b] = p.ws.prefix[size_t(le) * p.tcap + b];
+    }
+    __syncthreads();
+    for (int le = tid; le < L; le += kLayoutThreads) {
+      int acc = 0;
+      for (int b = 0; b < n_tiles; ++b) {
+        const int v = pre[le * PW + b];
+        pre[le * PW + b] = acc;
+        acc += v;
+      }
+      pre[le * PW + n_tiles] = acc;
+    }
+    __syncthreads();
+  }
+  // (le, s) entries before tile b of expert le; the count of (le, s)
+  auto prefix_at = [&](int le, int b) -> int {
+    return FUSED ? pre[le * PW + b] : p.ws.prefix[size_t(le) * p.tcap + b];
+  };
+  auto count_of = [&](int le, int s) -> int {
+    return FUSED ? pre[le * PW + ts[s + 1]] - pre[le * PW + ts[s]] : p.counts[size_t(le) * p.n_src + s];
+  };
 
   // expert start rows (compact): exclusive scan of the totals
-  for (int le = tid; le < L; le += kLayoutThreads) start[le] = p.ws.total[le];
+  for (int le = tid; le < L; le += kLayoutThreads) start[le] = FUSED ? pre[le * PW + n_tiles] : p.ws.total[le];
   __syncthreads();
   const int m_total = block_scan_lds<false, kLayoutThreads>(start, L, tmp);
   if (tid == 0) start[L] = m_total;
@@ -203,7 +238,16 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(LayoutArgs 
     for (int le = tid; le <= L; le += kLayoutThreads)
       p.expert_off[le] = compact ? min(start[le], C) : le * p.n_src * C;
     int ovf = 0;
-    for (int le = tid; le < L; le += kLayoutThreads) ovf |= p.ws.ovf[le];
+    if (FUSED) {
+      for (int i = tid; i < L * p.n_src; i += kLayoutThreads) {
+        const int le = i / p.n_src, s = i - le * p.n_src;
+        const int c = count_of(le, s);
+        p.counts[i] = c;
+        ovf |= c > p.capacity;
+      }
+    } else {
+      for (int le = tid; le < L; le += kLayoutThreads) ovf |= p.ws.ovf[le];
+    }
     ovf = __syncthreads_or(ovf);
     if (tid == 0) p.status[0] = (compact ? (m_total > C) : (ovf != 0)) ? MOE_STATUS_OVERFLOW : 0;
   }
@@ -217,7 +261,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(LayoutArgs 
     } else {
       const int64_t region = r / C;  // = le * S + s
       const int j = int(r - region * C);
-      const int cnt = p.counts[region];
+      const int cnt = count_of(int(region / p.n_src), int(region % p.n_src));
       hole = j >= cnt;
     }
     if (hole) p.row_token[r] = -1;
@@ -227,11 +271,11 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(LayoutArgs 
   if (b >= n_tiles) return;  // uniform per block
   const int s = tile_source(ts, p.n_src, b);
   for (int le = tid; le < L; le += kLayoutThreads) {
-    const int pb = p.ws.prefix[size_t(le) * p.tcap + b];
+    const int pb = prefix_at(le, b);
     if (compact) {
       base[le] = start[le] + pb;  // row of the tile's first entry of expert le
     } else {
-      const int ps = p.ws.prefix[size_t(le) * p.tcap + ts[s]];
+      const int ps = prefix_at(le, ts[s]);
       base[le] = pb - ps;  // rank inside the (le, s) region of that entry
     }
     running[le] = 0;
@@ -376,8 +420,13 @@ MOE_API moe_status_t moe_dispatch_layout(const moe_layout_desc_t* d, const int32
   const dim3 block(kLayoutThreads);
   hipLaunchKernelGGL(layout_hist_kernel, dim3(p.tcap), block, 0, stream, p);
   if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
+  const int64_t pre_ints = int64_t(d->n_local) * (p.tcap + 1);
+  if (pre_ints <= kFusedPrefix) {
+    hipLaunchKernelGGL(layout_rank_kernel<true>, dim3(p.tcap), block, size_t(pre_ints) * sizeof(int), stream, p);
+    return launch_status();
+  }
   hipLaunchKernelGGL(layout_scan_kernel, dim3(d->n_local), block, 0, stream, p);
   if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
-  hipLaunchKernelGGL(layout_rank_kernel, dim3(p.tcap), block, 0, stream, p);
+  hipLaunchKernelGGL(layout_rank_kernel<false>, dim3(p.tcap), block, 0, stream, p);
   return launch_status();
 }
