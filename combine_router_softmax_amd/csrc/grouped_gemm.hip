@@ -1637,6 +1637,10 @@ MOE_API moe_status_t moe_grouped_gemm(const moe_ggemm_desc_t* d, const void* a, 
   const bool force = d->policy == MOE_GEMM_WIDE;
   p.wide_min = wide_ok ? (force ? 1 : kWideMinRows) : kNoWide;
   const bool sk = !(wide_ok && force);  // forced wide leaves the stream-K kernel nothing
+  // h (internal) in the 16-row blocked layout where the wide kernel may run
+  // (its loads take 16 rows x 32 columns); row-major for the decode kernels,
+  // whose loads take 4 rows x 128 columns
+  const bool h_blk = wide_ok;
   p.wide_min_tiles = force ? 0 : kWideMinTiles;
   p.sh_a_blk = 0;
   moe_status_t st = MOE_OK;
@@ -1655,7 +1659,7 @@ MOE_API moe_status_t moe_grouped_gemm(const moe_ggemm_desc_t* d, const void* a, 
     p.n_tiles_n = f32 ? d->inter / kFBN : d->inter / 64;
     p.a_blk = d->a_layout == MOE_ACT_BLOCKED16;
     p.sh_a_blk = 0;       // the shared expert reads its rows of x in place
-    p.out_blk = !f32;     // h (internal) is blocked for bf16
+    p.out_blk = h_blk;
     st = launch_stage(p, f32, fp8, kUp, sk, parts, stream);
     if (st != MOE_OK) return st;
   }
@@ -1672,7 +1676,7 @@ MOE_API moe_status_t moe_grouped_gemm(const moe_ggemm_desc_t* d, const void* a, 
     p.K = d->inter;
     p.n_out = d->hidden;
     p.n_tiles_n = f32 ? d->hidden / kFBN : d->hidden / 128;
-    p.a_blk = p.sh_a_blk = !f32;  // h
+    p.a_blk = p.sh_a_blk = h_blk;  // h
     p.out_blk = 0;                // y rows are read by the combine
     st = launch_stage(p, f32, fp8, kDown, sk, parts, stream);
   }
