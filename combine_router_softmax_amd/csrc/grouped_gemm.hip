@@ -110,8 +110,10 @@ struct Sched {
   int tile_start[kMaxGroups + 2];
   int m[kMaxGroups + 1];
   int seg[kGemmMaxSrc + 1];
-  int rowmap[256];
-  int tmp[kGemmThreads];
+  union {
+    int rowmap[256];
+    int tmp[kGemmThreads];  // scan scratch: every scan ends before a rowmap is written
+  };
   int cur_seg_group;
   int wide_tiles;
 };
@@ -125,7 +127,7 @@ struct Sched {
 // tiles, and then every group is wide; otherwise the stream-K kernel takes
 // them all. Both kernels evaluate this identically from the same counts.
 // Returns the tile count. All threads must call it.
-__device__ int build_schedule(const GemmArgs& p, int bm, int ntn, bool wide, Sched& sh) {
+__device__ __forceinline__ int build_schedule(const GemmArgs& p, int bm, int ntn, bool wide, Sched& sh) {
   const int tid = threadIdx.x;
   const int nsh = p.sh_rows > 0 ? 1 : 0;
   const int Gt = p.G + nsh;
@@ -169,7 +171,18 @@ __device__ int build_schedule(const GemmArgs& p, int bm, int ntn, bool wide, Sch
     sh.cur_seg_group = -1;
   }
   __syncthreads();
-  return total;
+  // uniform (every thread read the same LDS word): scalar registers, so the
+  // work split derived from it stays scalar
+  return __builtin_amdgcn_readfirstlane(total);
+}
+
+// c ? a : b on values: the operands are read before the choice. (On the two
+// fields themselves the conditional is an lvalue, which the compiler may
+// lower to a load from a chosen field address; that keeps the whole kernel
+// argument block in scratch memory.)
+template <class T>
+__device__ __forceinline__ T pick(bool c, T a, T b) {
+  return c ? a : b;
 }
 
 struct Tile {
@@ -187,7 +200,7 @@ struct Tile {
 // N tiles (8 x 4 when the group has 8 row tiles), i.e. 12 distinct operand
 // slabs instead of 2 + 16 (N fastest) or 32 + 1 (rows fastest).
 template <bool BLOCKED = false>
-__device__ Tile decode_tile(const GemmArgs& p, int bm, int ntn, const Sched& sh, int t) {
+__device__ __forceinline__ Tile decode_tile(const GemmArgs& p, int bm, int ntn, const Sched& sh, int t) {
   const int nsh = p.sh_rows > 0 ? 1 : 0;
   const int Gt = p.G + nsh;
   int lo = 0, hi = Gt;  // last q with tile_start[q] <= t
@@ -213,11 +226,21 @@ __device__ Tile decode_tile(const GemmArgs& p, int bm, int ntn, const Sched& sh,
     tl.r0 = (local % mtiles) * bm;
   }
   tl.nrows = min(bm, sh.m[lo] - tl.r0);
+  // every caller passes a workgroup-uniform t, so the fields are uniform; the
+  // compiler cannot see that through the LDS reads: scalar registers (loop
+  // bounds and weight addresses derived from them then stay scalar)
+  tl.g = __builtin_amdgcn_readfirstlane(tl.g);
+  tl.we = __builtin_amdgcn_readfirstlane(tl.we);
+  tl.shared = __builtin_amdgcn_readfirstlane(int(tl.shared)) != 0;
+  tl.nt = __builtin_amdgcn_readfirstlane(tl.nt);
+  tl.r0 = __builtin_amdgcn_readfirstlane(tl.r0);
+  tl.nrows = __builtin_amdgcn_readfirstlane(tl.nrows);
+  tl.mtiles = __builtin_amdgcn_readfirstlane(tl.mtiles);
   return tl;
 }
 
 // Physical row of each of the tile's rows (-1 past the group's rows).
-__device__ void build_rowmap(const GemmArgs& p, const Tile& tl, int bm, Sched& sh) {
+__device__ __forceinline__ void build_rowmap(const GemmArgs& p, const Tile& tl, int bm, Sched& sh) {
   const int tid = threadIdx.x;
   if (tl.shared || p.layout == MOE_LAYOUT_COMPACT) {
     if (tid < bm) {
@@ -448,7 +471,7 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_fixup_kernel(GemmArgs p, con
         return s0 < s1 ? sk_slot(const_cast<float*>(parts), w, int(s0 / nchunks) == t ? 0 : 1) : nullptr;
       },
       [&](int, int q) { return (((wv * kMB + b) * 4 + q) * kWave + lane) * 4; });
-  uint16_t* out = static_cast<uint16_t*>(tl.shared ? p.sh_out : p.out);
+  uint16_t* out = static_cast<uint16_t*>(pick(tl.shared, p.sh_out, p.out));
   ffn_epilogue_block<KIND>(acc[0], tl, b, sh, out, p.n_out, wv, lr, lh, p.out_blk);
 }
 
@@ -489,10 +512,39 @@ constexpr int kWStage = kWN * kWK;      // elements of one operand per stage
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// Global -> LDS copy of 16 bytes per lane (lane l writes bytes [16 l, 16 l +
+// 16) of the wave's KiB at lds), from scalar base + the lane's 32-bit offset:
+// global_load_lds as inline assembly, so that the compiler's wait-count
+// analysis does not see it. (With an LDS-writing global load outstanding that
+// analysis waits for every vector-memory op before the next use of any loaded
+// register, which would cap the prefetch at one stage.) The caller's own
+// counted waits must cover it; ops the analysis does not know of only make
+// its waits longer, since the count retires in order.
+__device__ __forceinline__ void lds_dma16_untracked(gptr<char> base, uint32_t lane_off, const void* lds) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_ptr_t)lds);
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(lane_off), "s"(base), "{m0}"(l) : "memory");
+}
+
+// Raw buffer resource over the 4 GiB from a wave-uniform base (scalar
+// registers): a buffer load addresses base + scalar offset + the lane's 32-bit
+// offset + an immediate, so no per-lane 64-bit address is held in registers.
+// (num_records is the maximum: the offsets are our own and stay in range.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base) {
+  const uint64_t v = reinterpret_cast<uint64_t>(base);
+  // (readfirstlane returns a signed int: each half goes through uint32_t, or
+  // widening would sign-extend the low half over the high one)
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+  const uint64_t u = (uint64_t(hi) << 32) | lo;
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(u), short(0), -1, 0x00020000);
+}
+
 // s_waitcnt immediate: wait until at most n vector-memory ops are outstanding
 // and no LDS op is (gfx9 encoding: vmcnt[3:0], expcnt[6:4] (7 = no wait),
 // lgkmcnt[11:8], vmcnt[5:4] in bits [15:14]).
 constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 14); }
+// s_waitcnt operand: at most n vector-memory ops outstanding, LDS/scalar count not waited for
+constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
 // The ring buffers are separate LDS objects, and the stage loop is unrolled by
 // the ring depth so every load and fragment read names its buffer statically:
@@ -520,7 +572,7 @@ __device__ __forceinline__ void wide_epilogue_block(const GemmArgs& p, const Til
                                                     const f32x16_t& a0, const f32x16_t& a1, int wv, int lr, int lh) {
   const int phys = sh.rowmap[32 * b + lr];
   if (phys < 0) return;
-  uint16_t* out = static_cast<uint16_t*>(tl.shared ? p.sh_out : p.out);
+  uint16_t* out = static_cast<uint16_t*>(pick(tl.shared, p.sh_out, p.out));
   const bool oblk = p.out_blk;
   uint16_t* orow = out + act_off(phys, 0, p.n_out, oblk);
   if (KIND == kUp) {
@@ -559,8 +611,8 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& p, const Tile& tl, con
   const int lr = lane & 31;
   const int lh = lane >> 5;
   const int last = s_end - 1;
-  const uint16_t* A = static_cast<const uint16_t*>(tl.shared ? p.sh_a : p.a);
-  const uint16_t* W = static_cast<const uint16_t*>(tl.shared ? p.sh_w : p.w);
+  const uint16_t* A = static_cast<const uint16_t*>(pick(tl.shared, p.sh_a, p.a));
+  const uint16_t* W = static_cast<const uint16_t*>(pick(tl.shared, p.sh_w, p.w));
 
   // Load q of wave wv covers tile rows kWRowsPerLoad (4 q + wv) + lane /
   // kWSlots, LDS slot lane % kWSlots, i.e. global column
@@ -572,7 +624,7 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& p, const Tile& tl, con
   constexpr int P = WL + XL;  // loads per wave per stage
   const int lrow = lane / kWSlots;
   auto col_of = [&](int row) { return (lane % kWSlots) ^ ((row / (16 / kWSlots)) % kWSlots); };
-  const bool ablk = tl.shared ? p.sh_a_blk : p.a_blk;
+  const bool ablk = pick(tl.shared, p.sh_a_blk, p.a_blk);
   const size_t xstep = ablk ? 512 : kWK;  // elements from one stage of a row to the next
   const uint16_t* xg[XL];
   const int phys0 = sh.rowmap[0];
@@ -869,7 +921,7 @@ __device__ __forceinline__ void bf_run(const GemmArgs& p, const Tile& tl, int n,
 
   // weights: this lane's row of the run's first tile; piece j of chunk C covers
   // k = 128 C + 64 (j / 4) + 32 lh + 8 (j % 4)
-  const uint16_t* W = static_cast<const uint16_t*>(tl.shared ? p.sh_w : p.w);
+  const uint16_t* W = static_cast<const uint16_t*>(pick(tl.shared, p.sh_w, p.w));
   int wrow;
   if (KIND == kUp) {
     const int j = tl.nt * 64 + 16 * wv + (lr & 15);
@@ -904,8 +956,8 @@ __device__ __forceinline__ void bf_run(const GemmArgs& p, const Tile& tl, int n,
 
   // activations: load q of this wave stages tile rows 4 (4 q + wv) .. + 3
   constexpr int XL = 2 * NB;  // 1 KiB loads per wave per chunk
-  const uint16_t* A = static_cast<const uint16_t*>(tl.shared ? p.sh_a : p.a);
-  const bool ablk = tl.shared ? p.sh_a_blk : p.a_blk;
+  const uint16_t* A = static_cast<const uint16_t*>(pick(tl.shared, p.sh_a, p.a));
+  const bool ablk = pick(tl.shared, p.sh_a_blk, p.a_blk);
   const size_t xstep = ablk ? size_t(4) * 512 : size_t(kKC);  // elements from one chunk of a row to the next
   // per-lane byte offsets from the tile's first row (a tile's rows lie in one
   // expert's region, which the host keeps below 2^31 elements)
@@ -928,7 +980,7 @@ __device__ __forceinline__ void bf_run(const GemmArgs& p, const Tile& tl, int n,
   for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
-  uint16_t* out = static_cast<uint16_t*>(tl.shared ? p.sh_out : p.out);
+  uint16_t* out = static_cast<uint16_t*>(pick(tl.shared, p.sh_out, p.out));
 
   uint4 w0[8], w1[8], w2[8];  // weight ring
 #define MOE_BF_LOADS(I_, XBUF_, WR_)                                                                          \
@@ -1095,22 +1147,29 @@ __device__ __forceinline__ int f8_part_idx(int wv, int a, int b, int q, int lane
 // across tile boundaries).
 template <int KIND, bool PACKED, int NB, bool STREAM>
 __device__ __forceinline__ void f8_run(const GemmArgs& p, const Tile& tl, int n, const Sched& sh,
-                                       uint16_t* __restrict__ x0, uint16_t* __restrict__ x1, int it_begin, int it_end,
+                                       uint16_t* __restrict__ x0, uint16_t* __restrict__ x1,
+                                       uint16_t* __restrict__ x2, int it_begin, int it_end,
                                        float* __restrict__ part_first, float* __restrict__ part_last) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wv = tid / kWave;
+  const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform: scalar
   const int lr = lane & 31;
   const int lh = lane >> 5;
-  const int nchunks = p.K / kKC;
+  const int nchunks = __builtin_amdgcn_readfirstlane(p.K / kKC);
+  it_begin = __builtin_amdgcn_readfirstlane(it_begin);
+  it_end = __builtin_amdgcn_readfirstlane(it_end);
+  n = __builtin_amdgcn_readfirstlane(n);
   const int last = it_end - 1;
   // N block of sub-block a of the run's tile k (an odd N-block count leaves a
   // group's last tile one block: its second sub-block repeats the first)
-  auto ntof = [&](int k, int a) { return min(2 * (tl.nt + k) + a, p.n_tiles_n - 1); };
+  // (operands in scalar registers, so the arithmetic on them stays scalar)
+  const int nt0 = __builtin_amdgcn_readfirstlane(2 * tl.nt);
+  const int nt_max = __builtin_amdgcn_readfirstlane(p.n_tiles_n - 1);
+  auto ntof = [&](int k, int a) { return min(nt0 + 2 * k + a, nt_max); };
 
   // weights: uniform base (the expert's block) + the lane's loop-invariant byte
   // offset (its row in N block 0; an expert's weights span less than 4 GiB)
-  const uint8_t* W = static_cast<const uint8_t*>(tl.shared ? p.sh_w : p.w);
+  const uint8_t* W = static_cast<const uint8_t*>(pick(tl.shared, p.sh_w, p.w));
   int wrow0;  // this lane's weight row in N block 0
   if (KIND == kUp) {
     const int j = 16 * wv + (lr & 15);
@@ -1118,34 +1177,49 @@ __device__ __forceinline__ void f8_run(const GemmArgs& p, const Tile& tl, int n,
   } else {
     wrow0 = 32 * wv + lr;
   }
-  gptr<char> wbase;
+  // Weights and scales come by buffer loads (see buf_rsrc) from a resource at
+  // the expert's base, with a scalar offset per (N block, chunk) and a
+  // loop-invariant lane offset. (The activations go to LDS by global_load_lds
+  // (lds_dma16_untracked): the buffer form of the LDS copy is not used, its
+  // LDS addressing on this chip - scalar offset, destinations above 64 KiB -
+  // not being established.)
+  __amdgpu_buffer_rsrc_t rw;
   uint32_t woff;
   if constexpr (PACKED) {
-    wbase = uniform_ptr(reinterpret_cast<const char*>(W) + size_t(tl.we) * p.n_tiles_n * nchunks * 4 * 4 * kWave * 16);
+    rw = buf_rsrc(W + size_t(tl.we) * p.n_tiles_n * nchunks * 4 * 4 * kWave * 16);
     woff = uint32_t(wv * 4 * kWave + lane) * 16u;
   } else {
-    wbase = uniform_ptr(reinterpret_cast<const char*>(W + size_t(tl.we) * p.n_w_rows * p.K));
+    rw = buf_rsrc(W + size_t(tl.we) * p.n_w_rows * p.K);
     woff = uint32_t(wrow0 * p.K + 64 * lh);
   }
-  // iteration I = k * nchunks + C: piece j of sub-block a
-  auto wpiece = [&](int k, int C, int a, int j) -> gptr<uint4> {
+  // iteration I = k * nchunks + C, sub-block a: scalar offset of its piece 0
+  // (piece j lies j KiB (packed) or 16 j bytes (row-major) further)
+  auto wsoff = [&](int k, int C, int a) -> int {
     const int nt = ntof(k, a);
-    if constexpr (PACKED) return at<uint4>(wbase, ((uint64_t(nt) * nchunks + C) * 4 * 4 + j) * kWave * 16, woff);
-    else return at<uint4>(wbase, uint64_t(nt) * (KIND == kUp ? 64 : 128) * p.K + uint64_t(C) * kKC + j * 16, woff);
+    if constexpr (PACKED) return (nt * nchunks + C) * 4 * 4 * kWave * 16;
+    else return nt * (KIND == kUp ? 64 : 128) * p.K + C * kKC;
+  };
+  auto wpiece = [&](int k, int C, int a, int j) -> uint4 {
+    constexpr int aux = STREAM ? 2 : 0;  // non-temporal: the weights are read once
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
+        rw, woff, __builtin_amdgcn_readfirstlane(wsoff(k, C, a) + (PACKED ? j * kWave * 16 : j * 16)), aux);
+    return make_uint4(v[0], v[1], v[2], v[3]);
   };
   // block scales: 128-row blocks; up: gate rows of N block nt lie in block
   // nt / 2, its up rows in block I / 128 + nt / 2; down: block nt
-  const float* sl = (tl.shared ? p.sh_s : p.s) + size_t(tl.we) * (p.n_w_rows / 128) * nchunks +
-                    size_t(KIND == kUp && lr >= 16 ? p.n_out / 128 : 0) * nchunks;
+  const __amdgpu_buffer_rsrc_t rs = buf_rsrc(pick(tl.shared, p.sh_s, p.s) + size_t(tl.we) * (p.n_w_rows / 128) * nchunks);
+  const uint32_t s_lane = KIND == kUp && lr >= 16 ? uint32_t(p.n_out / 128) * nchunks * 4u : 0u;
   auto scale = [&](int k, int C, int a) {
     const int nt = ntof(k, a);
-    return sl[(KIND == kUp ? nt >> 1 : nt) * nchunks + C];
+    const int so = ((KIND == kUp ? nt >> 1 : nt) * nchunks + C) * 4;
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, s_lane, __builtin_amdgcn_readfirstlane(so), 0));
   };
 
   // activations: load q of this wave stages tile rows 4 (4 q + wv) .. + 3
   constexpr int XL = (NB * 8 + 3) / 4;  // 1 KiB loads per wave per chunk
-  const uint16_t* A = static_cast<const uint16_t*>(tl.shared ? p.sh_a : p.a);
-  const bool ablk = tl.shared ? p.sh_a_blk : p.a_blk;
+  const uint16_t* A = static_cast<const uint16_t*>(pick(tl.shared, p.sh_a, p.a));
+  const bool ablk = pick(tl.shared, p.sh_a_blk, p.a_blk);
   const size_t xstep = ablk ? size_t(4) * 512 : size_t(kKC);  // elements from one chunk of a row to the next
   // per-lane byte offsets from the tile's first row (a tile's rows lie in one
   // expert's region, which the host keeps below 2^31 elements)
@@ -1170,72 +1244,108 @@ __device__ __forceinline__ void f8_run(const GemmArgs& p, const Tile& tl, int n,
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
-  uint16_t* out = static_cast<uint16_t*>(tl.shared ? p.sh_out : p.out);
+  uint16_t* out = static_cast<uint16_t*>(pick(tl.shared, p.sh_out, p.out));
 
-  // Two-deep ring (even / odd iterations of the run). Per iteration the
-  // vector-memory ops go out in the order: activation DMA of the next
-  // iteration, its two scales, its 8 weight pieces. (With LDS-DMA and register
-  // loads both outstanding the compiler waits for all of them before the first
-  // use of any, so every load of an iteration is issued one iteration ahead,
-  // before the first use.)
-  // Software pipeline, one 16-deep step at a time (fenced, so the compiler
-  // cannot hoist a whole chunk of fragment reads): step j reads its activation
-  // fragments, dequantises the weights of step j + 1 (step 0 of the next
-  // iteration after step 7) and issues its MFMAs with the fragments
-  // dequantised before.
-  uint4 w0[2][4], w1[2][4];  // [sub-block][piece]
-  float s0[2], s1[2];        // block scales
-  bf16x8_t fa[2];            // weight fragments of the current step
-#define MOE_F8_LOADS(I_, XBUF_, WR_, SR_)                                                                     \
+  // Ring. Iteration I of the run (counted from it_begin) takes activation
+  // buffer and scale pair (I - it_begin) % 3 and weight set (I - it_begin) % 2.
+  // At the top of iteration I (after the barrier: every wave has left I - 1,
+  // the last reader of that buffer) go out the activation DMA and the scales
+  // of I + 2; piece j of the weights of I + 2 replaces piece j of I's set as
+  // soon as the dequantisation of I has read it for the last time (steps 0,
+  // 2, 4, 6). Every operand is so requested about two iterations before its
+  // use, with the registers of two. A wave's vector-memory ops per iteration,
+  // in issue order: XL activation DMAs, 2 scale loads, 2 weight loads at each
+  // of steps 0, 2, 4 and 6 (XL + 10); they retire in order (epilogue stores
+  // in between only make a count wait longer), so
+  //  - at the top of I, the activations, scales and piece 0 of I are followed
+  //    by pieces 1-3 of I (6 ops) and all of I + 1: vmcnt(XL + 16);
+  //  - piece j = 1, 2, 3 of I, first read in step 2j - 1, is followed by the
+  //    2 (3 - j) later pieces of I, all of I + 1 and, of I + 2, the top loads
+  //    and pieces 0 .. j - 1: vmcnt(2 XL + 18) in each case.
+  // (Past the run's end the loads repeat its last iteration, so the counts
+  // hold.) Inside an iteration, one 16-deep step at a time (fenced, so the
+  // compiler cannot hoist a whole iteration of fragment reads): step j reads
+  // its activation fragments, dequantises the weights of step j + 1 and
+  // issues its MFMAs with the fragments dequantised before.
+  // LDS fragment of row block b in step j: row 32 b + lr, 16-byte column
+  // (8 lh + j) ^ (lr % 16) = (8 lh ^ (lr & 8)) + (j ^ (lr & 7)); the lane's
+  // part is rebuilt from an opaque copy each iteration, so the compiler does
+  // not hold the eight step addresses in registers for the whole loop
+  const int fr_base = lr * kKC + ((8 * lh) ^ (lr & 8)) * 8;
+  const int fr_x = lr & 7;
+  uint4 w0[2][4], w1[2][4];   // weight sets [sub-block][piece]
+  float s0[2], s1[2], s2[2];  // block scales per sub-block
+  bf16x8_t fa[2];             // weight fragments of the current step
+  // (tile k of the run, chunk c) of the iteration being computed and of the
+  // one being loaded, kept as counters (an integer division per iteration
+  // would be done by the vector ALU)
+  int k_cur = __builtin_amdgcn_readfirstlane(it_begin / nchunks);
+  int c_cur = __builtin_amdgcn_readfirstlane(it_begin - k_cur * nchunks);
+  int i_ld = it_begin, k_ld = k_cur, c_ld = c_cur;
+  // (readfirstlane: the counters are uniform; it keeps the compiler from
+  // moving them and the address arithmetic on them to vector registers)
+  auto adv_ld = [&]() __attribute__((always_inline)) {  // to the next iteration, but not past the last
+    if (i_ld < last) {
+      ++i_ld;
+      if (++c_ld == nchunks) {
+        c_ld = 0;
+        ++k_ld;
+      }
+    }
+    i_ld = __builtin_amdgcn_readfirstlane(i_ld);
+    c_ld = __builtin_amdgcn_readfirstlane(c_ld);
+    k_ld = __builtin_amdgcn_readfirstlane(k_ld);
+  };
+#define MOE_F8_TOP(XBUF_, SR_)                                                                              \
   {                                                                                                         \
-    const int k_ = (I_) / nchunks, c_ = (I_) - k_ * nchunks;                                                \
-    const size_t xo_ = size_t(c_) * xstep;                                                                  \
+    const int k_ = k_ld, c_ = c_ld;                                                                         \
+    const gptr<char> xc_ = xb + uint64_t(c_) * xstep * 2; /* the chunk's base: scalar */                   \
     _Pragma("unroll") for (int q = 0; q < XL; ++q)                                                          \
-      __builtin_amdgcn_global_load_lds(at<void>(xb, xo_ * 2, xoff[q]), (lds_ptr_t)((XBUF_) + (4 * q + wv) * 512), 16, 0, 0); \
+      lds_dma16_untracked(xc_, xoff[q], (XBUF_) + (4 * q + wv) * 512);                                      \
     _Pragma("unroll") for (int a = 0; a < 2; ++a) SR_[a] = scale(k_, c_, a);                                \
-    _Pragma("unroll") for (int a = 0; a < 2; ++a)                                                           \
-      _Pragma("unroll") for (int j = 0; j < 4; ++j) WR_[a][j] = ld_w<STREAM>(wpiece(k_, c_, a, j));         \
   }
-  // all of this wave's loads of the iteration have landed; after the barrier
-  // every wave's staged rows are visible and nobody still reads the other buffer
-#define MOE_F8_SYNC()                                                                                       \
-  __builtin_amdgcn_sched_barrier(0);                                                                        \
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));                                                          \
-  __builtin_amdgcn_s_barrier();                                                                             \
-  __builtin_amdgcn_sched_barrier(0);
+#define MOE_F8_PIECE(WR_, J_)                                                                               \
+  _Pragma("unroll") for (int a = 0; a < 2; ++a) WR_[a][J_] = wpiece(k_ld, c_ld, a, J_);
 #define MOE_F8_DEQ(DST_, WR_, J_, SR_)                                                                      \
   _Pragma("unroll") for (int a = 0; a < 2; ++a) DST_[a] =                                                   \
       ((J_) & 1) ? fp8x8_dequant(WR_[a][(J_) >> 1].z, WR_[a][(J_) >> 1].w, SR_[a])                          \
                  : fp8x8_dequant(WR_[a][(J_) >> 1].x, WR_[a][(J_) >> 1].y, SR_[a]);
-  // iteration in (XBUF_, WR_, SR_); the next iteration's weights are in (WN_, SN_)
-#define MOE_F8_CHUNK(XBUF_, WR_, SR_, WN_, SN_)                                                             \
+  // the 8 steps of an iteration (activations XBUF_, weights WR_, scales SR_);
+  // refills WR_ with the pieces of the iteration being loaded
+#define MOE_F8_STEPS(XBUF_, WR_, SR_)                                                                       \
+  int fx_ = fr_x;                                                                                           \
+  asm volatile("" : "+v"(fx_));                                                                             \
   _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                                           \
-    const int cl_ = 8 * lh + j; /* 16-byte column: k = 64 lh + 8 j */                                       \
+    const int fo_ = fr_base + ((j ^ fx_) * 8); /* 16-byte column: k = 64 lh + 8 j */                        \
     bf16x8_t fb_[NB];                                                                                       \
-    _Pragma("unroll") for (int b = 0; b < NB; ++b) {                                                        \
-      const int rr_ = b * 32 + lr;                                                                          \
-      fb_[b] = *reinterpret_cast<const bf16x8_t*>((XBUF_) + rr_ * kKC + ((cl_ ^ (rr_ & 15)) * 8));           \
-    }                                                                                                       \
+    _Pragma("unroll") for (int b = 0; b < NB; ++b)                                                          \
+      fb_[b] = *reinterpret_cast<const bf16x8_t*>((XBUF_) + b * 32 * kKC + fo_);                             \
     bf16x8_t na_[2];                                                                                        \
     if (j < 7) {                                                                                            \
+      if (j & 1) {                                                                                          \
+        __builtin_amdgcn_sched_barrier(0);                                                                  \
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * XL + 18));                                                \
+        __builtin_amdgcn_sched_barrier(0);                                                                  \
+      }                                                                                                     \
       MOE_F8_DEQ(na_, WR_, j + 1, SR_)                                                                      \
-    } else {                                                                                                \
-      MOE_F8_DEQ(na_, WN_, 0, SN_)                                                                          \
+      if (!(j & 1)) { MOE_F8_PIECE(WR_, j >> 1) }                                                           \
     }                                                                                                       \
     _Pragma("unroll") for (int b = 0; b < NB; ++b) {                                                        \
       acc[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0], fb_[b], acc[0][b], 0, 0, 0);               \
       acc[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1], fb_[b], acc[1][b], 0, 0, 0);               \
     }                                                                                                       \
-    fa[0] = na_[0];                                                                                         \
-    fa[1] = na_[1];                                                                                         \
+    if (j < 7) {                                                                                            \
+      fa[0] = na_[0];                                                                                       \
+      fa[1] = na_[1];                                                                                       \
+    }                                                                                                       \
     __builtin_amdgcn_sched_barrier(0);                                                                      \
   }
   // after iteration I_: if it ends its tile, the tile's epilogue (or partial
   // sums) and fresh accumulators
 #define MOE_F8_FINISH(I_)                                                                                   \
   {                                                                                                         \
-    const int k_ = (I_) / nchunks;                                                                          \
-    if ((I_) - k_ * nchunks == nchunks - 1 || (I_) == last) { /* uniform */                                 \
+    const int k_ = k_cur;                                                                                   \
+    if (c_cur == nchunks - 1 || (I_) == last) { /* uniform */                                               \
       float* part_ = k_ == 0 ? part_first : (k_ == n - 1 ? part_last : nullptr);                            \
       if (part_ == nullptr) {                                                                               \
         _Pragma("unroll") for (int a = 0; a < 2; ++a) {                                                     \
@@ -1254,38 +1364,70 @@ __device__ __forceinline__ void f8_run(const GemmArgs& p, const Tile& tl, int n,
         _Pragma("unroll") for (int b = 0; b < NB; ++b)                                                      \
           _Pragma("unroll") for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;                                \
     }                                                                                                       \
+    if (++c_cur == nchunks) {                                                                               \
+      c_cur = 0;                                                                                            \
+      ++k_cur;                                                                                              \
+    }                                                                                                       \
+    c_cur = __builtin_amdgcn_readfirstlane(c_cur);                                                          \
+    k_cur = __builtin_amdgcn_readfirstlane(k_cur);                                                          \
   }
-  // even iteration I_: activations in x0, weights in (w0, s0); loads iteration IN_
-#define MOE_F8_EVEN(I_, IN_)                                                                                \
+  // iteration I_ in (XBUF_, WR_, SR_); the activations and scales of I_ + 2 go to (XN_, SN_)
+#define MOE_F8_ITER(I_, XBUF_, WR_, SR_, XN_, SN_)                                                          \
   {                                                                                                         \
-    MOE_F8_SYNC()                                                                                           \
-    MOE_F8_LOADS(IN_, x1, w1, s1)                                                                           \
-    MOE_F8_CHUNK(x0, w0, s0, w1, s1)                                                                        \
+    __builtin_amdgcn_sched_barrier(0);                                                                      \
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(XL + 16));                                                  \
+    __builtin_amdgcn_s_barrier();                                                                           \
+    __builtin_amdgcn_sched_barrier(0);                                                                      \
+    adv_ld(); /* to min(I_ + 2, last): past the end a harmless repeat */                                    \
+    MOE_F8_TOP(XN_, SN_)                                                                                    \
+    MOE_F8_DEQ(fa, WR_, 0, SR_)                                                                             \
+    MOE_F8_STEPS(XBUF_, WR_, SR_)                                                                           \
     MOE_F8_FINISH(I_)                                                                                       \
   }
 
-  MOE_F8_LOADS(it_begin, x0, w0, s0)
-  MOE_F8_DEQ(fa, w0, 0, s0)
-  // (no exit in the middle of the two-iteration body: the accumulators would
-  // need a second copy at the exit)
+  MOE_F8_TOP(x0, s0)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    MOE_F8_PIECE(w0, j)
+  }
+  adv_ld();
+  MOE_F8_TOP(x1, s1)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    MOE_F8_PIECE(w1, j)
+  }
+  // six iterations per trip (the ring periods are 3 and 2), then up to five
+  // in a tail with the same slots. (No exit in the middle of a trip: the
+  // accumulators would need a second copy at the exit, and the wait counts of
+  // the loop head would have to cover the shorter trips.)
   int it = it_begin;
-  for (; it + 1 < it_end; it += 2) {
-    MOE_F8_EVEN(it, it + 1)
-    {
-      const int in = min(it + 2, last);  // past the end a harmless repeat
-      MOE_F8_SYNC()
-      MOE_F8_LOADS(in, x0, w0, s0)
-      MOE_F8_CHUNK(x1, w1, s1, w0, s0)
-      MOE_F8_FINISH(it + 1)
+  for (; it + 6 <= it_end; it += 6) {
+    MOE_F8_ITER(it, x0, w0, s0, x2, s2)
+    MOE_F8_ITER(it + 1, x1, w1, s1, x0, s0)
+    MOE_F8_ITER(it + 2, x2, w0, s2, x1, s1)
+    MOE_F8_ITER(it + 3, x0, w1, s0, x2, s2)
+    MOE_F8_ITER(it + 4, x1, w0, s1, x0, s0)
+    MOE_F8_ITER(it + 5, x2, w1, s2, x1, s1)
+  }
+  if (it < it_end) {
+    MOE_F8_ITER(it, x0, w0, s0, x2, s2)
+    if (it + 1 < it_end) {
+      MOE_F8_ITER(it + 1, x1, w1, s1, x0, s0)
+      if (it + 2 < it_end) {
+        MOE_F8_ITER(it + 2, x2, w0, s2, x1, s1)
+        if (it + 3 < it_end) {
+          MOE_F8_ITER(it + 3, x0, w1, s0, x2, s2)
+          if (it + 4 < it_end) MOE_F8_ITER(it + 4, x1, w0, s1, x0, s0)
+        }
+      }
     }
   }
-  if (it < it_end) MOE_F8_EVEN(it, last)  // odd count: the last iteration, then a harmless repeat
-#undef MOE_F8_EVEN
+#undef MOE_F8_ITER
 #undef MOE_F8_FINISH
-#undef MOE_F8_LOADS
-#undef MOE_F8_SYNC
+#undef MOE_F8_STEPS
 #undef MOE_F8_DEQ
-#undef MOE_F8_CHUNK
+#undef MOE_F8_PIECE
+#undef MOE_F8_TOP
   // no load may still be writing LDS when the next run reuses the buffers
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
   __builtin_amdgcn_s_barrier();
@@ -1296,7 +1438,7 @@ __device__ __forceinline__ void f8_run(const GemmArgs& p, const Tile& tl, int n,
 template <int KIND, bool PACKED>
 __global__ __launch_bounds__(kGemmThreads, 2) void ffn_fp8_kernel(GemmArgs p, float* __restrict__ parts) {
   __shared__ Sched sh;
-  __shared__ __attribute__((aligned(1024))) uint16_t x0[kF8BM * kKC], x1[kF8BM * kKC];
+  __shared__ __attribute__((aligned(1024))) uint16_t x0[kF8BM * kKC], x1[kF8BM * kKC], x2[kF8BM * kKC];
   const int ntn2 = (p.n_tiles_n + 1) / 2;
   const int n_tiles = build_schedule(p, kF8BM, ntn2, false, sh);
   const int nchunks = p.K / kKC;
@@ -1321,9 +1463,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void ffn_fp8_kernel(GemmArgs p, fl
     auto run = [&](auto stream_tag) __attribute__((always_inline)) {
       constexpr bool ST = decltype(stream_tag)::value;
       switch ((tl.nrows + 31) / 32) {
-        case 1: f8_run<KIND, PACKED, 1, ST>(p, tl, n, sh, x0, x1, it_begin, it_end, part_first, part_last); break;
-        case 2: f8_run<KIND, PACKED, 2, ST>(p, tl, n, sh, x0, x1, it_begin, it_end, part_first, part_last); break;
-        default: f8_run<KIND, PACKED, 3, ST>(p, tl, n, sh, x0, x1, it_begin, it_end, part_first, part_last); break;
+        case 1: f8_run<KIND, PACKED, 1, ST>(p, tl, n, sh, x0, x1, x2, it_begin, it_end, part_first, part_last); break;
+        case 2: f8_run<KIND, PACKED, 2, ST>(p, tl, n, sh, x0, x1, x2, it_begin, it_end, part_first, part_last); break;
+        default: f8_run<KIND, PACKED, 3, ST>(p, tl, n, sh, x0, x1, x2, it_begin, it_end, part_first, part_last); break;
       }
     };
     if (tl.mtiles == 1) run(std::true_type{});
@@ -1368,7 +1510,7 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_fp8_fixup_kernel(GemmArgs p,
       },
       [&](int, int q) { return f8_part_idx(wv, a, b, q, lane); });
   tl.nt = 2 * tl.nt + a;
-  uint16_t* out = static_cast<uint16_t*>(tl.shared ? p.sh_out : p.out);
+  uint16_t* out = static_cast<uint16_t*>(pick(tl.shared, p.sh_out, p.out));
   ffn_epilogue_block<KIND>(acc[0], tl, b, sh, out, p.n_out, wv, lr, lh, p.out_blk);
 }
 
@@ -1430,9 +1572,9 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_f32_kernel(GemmArgs p) {
   for (int t = blockIdx.x; t < n_tiles; t += gridDim.x) {
     const Tile tl = decode_tile(p, kFBM, p.n_tiles_n, sh, t);
     build_rowmap(p, tl, kFBM, sh);
-    const float* A = static_cast<const float*>(tl.shared ? p.sh_a : p.a);
-    const float* W = static_cast<const float*>(tl.shared ? p.sh_w : p.w);
-    float* out = static_cast<float*>(tl.shared ? p.sh_out : p.out);
+    const float* A = static_cast<const float*>(pick(tl.shared, p.sh_a, p.a));
+    const float* W = static_cast<const float*>(pick(tl.shared, p.sh_w, p.w));
+    float* out = static_cast<float*>(pick(tl.shared, p.sh_out, p.out));
     float g[4] = {0.f, 0.f, 0.f, 0.f}, u[4] = {0.f, 0.f, 0.f, 0.f};
     for (int k0 = 0; k0 < p.K; k0 += kFKC) {
       for (int i = tid; i < kFBM * kFKC; i += kGemmThreads) {
