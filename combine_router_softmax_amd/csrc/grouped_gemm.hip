@@ -50,6 +50,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kGemmThreads = 256;
+constexpr int kMaxGemmThreads = 512;  // the fp8 decode kernel's workgroup
 constexpr int kBM = 128;            // rows per tile
 constexpr int kMB = kBM / 32;       // 32-row MFMA blocks per tile
 constexpr int kKC = 128;            // reduction chunk
@@ -112,7 +113,7 @@ struct Sched {
   int seg[kGemmMaxSrc + 1];
   union {
     int rowmap[256];
-    int tmp[kGemmThreads];  // scan scratch: every scan ends before a rowmap is written
+    int tmp[kMaxGemmThreads];  // scan scratch: every scan ends before a rowmap is written
   };
   int cur_seg_group;
   int wide_tiles;
@@ -127,20 +128,21 @@ struct Sched {
 // tiles, and then every group is wide; otherwise the stream-K kernel takes
 // them all. Both kernels evaluate this identically from the same counts.
 // Returns the tile count. All threads must call it.
+template <int NT = kGemmThreads>
 __device__ __forceinline__ int build_schedule(const GemmArgs& p, int bm, int ntn, bool wide, Sched& sh) {
   const int tid = threadIdx.x;
   const int nsh = p.sh_rows > 0 ? 1 : 0;
   const int Gt = p.G + nsh;
   if (p.layout == MOE_LAYOUT_COMPACT) {
-    for (int g = tid; g < p.G; g += kGemmThreads) {
+    for (int g = tid; g < p.G; g += NT) {
       const int64_t lo = min<int64_t>(max<int64_t>(p.group_off[g], 0), p.rows);
       const int64_t hi = min<int64_t>(max<int64_t>(p.group_off[g + 1], lo), p.rows);
       sh.m[nsh + g] = int(hi - lo);
     }
   } else {
-    for (int g = tid; g < p.G; g += kGemmThreads) sh.m[nsh + g] = 0;
+    for (int g = tid; g < p.G; g += NT) sh.m[nsh + g] = 0;
     __syncthreads();
-    for (int i = tid; i < p.G * p.S; i += kGemmThreads) {
+    for (int i = tid; i < p.G * p.S; i += NT) {
       const int c = min(max(p.counts[i], 0), p.C);
       if (c) atomicAdd(&sh.m[nsh + i / p.S], c);
     }
@@ -152,7 +154,7 @@ __device__ __forceinline__ int build_schedule(const GemmArgs& p, int bm, int ntn
   __syncthreads();
   if (p.wide_min != kNoWide) {
     int wt = 0;
-    for (int g = tid; g < Gt; g += kGemmThreads)
+    for (int g = tid; g < Gt; g += NT)
       if (sh.m[g] >= p.wide_min) wt += (sh.m[g] + kWM - 1) / kWM * (p.n_w_rows / kWN);
     if (wt) atomicAdd(&sh.wide_tiles, wt);
     __syncthreads();
@@ -160,12 +162,12 @@ __device__ __forceinline__ int build_schedule(const GemmArgs& p, int bm, int ntn
   // once the launch qualifies, every group takes the wide kernel (one launch
   // does all the work; small groups are cheap ragged tiles there)
   const int wide_min = sh.wide_tiles >= p.wide_min_tiles ? 1 : kNoWide;
-  for (int g = tid; g < Gt; g += kGemmThreads) {
+  for (int g = tid; g < Gt; g += NT) {
     const int m = sh.m[g];
     sh.tile_start[g] = ((m >= wide_min) == wide) ? (m + bm - 1) / bm * ntn : 0;
   }
   __syncthreads();
-  const int total = block_scan_lds<false, kGemmThreads>(sh.tile_start, Gt, sh.tmp);
+  const int total = block_scan_lds<false, NT>(sh.tile_start, Gt, sh.tmp);
   if (tid == 0) {
     sh.tile_start[Gt] = total;
     sh.cur_seg_group = -1;
@@ -240,6 +242,7 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& p, int bm, int ntn, 
 }
 
 // Physical row of each of the tile's rows (-1 past the group's rows).
+template <int NT = kGemmThreads>
 __device__ __forceinline__ void build_rowmap(const GemmArgs& p, const Tile& tl, int bm, Sched& sh) {
   const int tid = threadIdx.x;
   if (tl.shared || p.layout == MOE_LAYOUT_COMPACT) {
@@ -252,9 +255,9 @@ __device__ __forceinline__ void build_rowmap(const GemmArgs& p, const Tile& tl, 
   }
   if (sh.cur_seg_group != tl.g) {  // uniform: every thread reads the same LDS word
     __syncthreads();
-    for (int s = tid; s < p.S; s += kGemmThreads) sh.seg[s] = min(max(p.counts[tl.g * p.S + s], 0), p.C);
+    for (int s = tid; s < p.S; s += NT) sh.seg[s] = min(max(p.counts[tl.g * p.S + s], 0), p.C);
     __syncthreads();
-    const int tot = block_scan_lds<false, kGemmThreads>(sh.seg, p.S, sh.tmp);
+    const int tot = block_scan_lds<false, NT>(sh.seg, p.S, sh.tmp);
     if (tid == 0) {
       sh.seg[p.S] = tot;
       sh.cur_seg_group = tl.g;
@@ -345,9 +348,9 @@ constexpr int kPartFloats = 4 * kMB * 16 * kWave;     // one workgroup's accumul
 constexpr int kSkMinChunks = 8;
 
 // Ranges used for a launch of `total` iterations: a multiple of the XCD count.
-__device__ inline int sk_grid(int64_t total) {
+__device__ inline int sk_grid(int64_t total, int max_grid = kSkGrid) {
   const int64_t g = total / kSkMinChunks / kXcds * kXcds;
-  return int(max<int64_t>(kXcds, min<int64_t>(kSkGrid, g)));
+  return int(max<int64_t>(kXcds, min<int64_t>(max_grid, g)));
 }
 
 __host__ __device__ inline int64_t sk_start(int b, int64_t total, int G) { return int64_t(b) * total / G; }
@@ -1112,26 +1115,29 @@ __global__ __launch_bounds__(kGemmThreads, 2) void ffn_bf16_kernel(GemmArgs p, f
 
 // ------------------------------------------------------------------ fp8 kernel
 // fp8 e4m3 weights, decode-shaped groups (W8A16). A tile is 96 activation
-// rows x two adjacent N blocks (up: 2 x 64 h columns; down: 2 x 128 output
-// columns), i.e. 256 weight rows: each wave owns its 32 rows of both N blocks
-// (sub-blocks a = 0, 1), so every activation chunk staged in LDS feeds 256
-// weight rows and the activation rows are re-read half as often as with one N
-// block per tile (at ~100 rows per expert they would otherwise outweigh the
-// fp8 weight bytes). 96 rows (3 MFMA blocks) keep the accumulators (96
-// registers) and a two-deep weight ring (64) inside one wave's registers at
-// two workgroups per compute unit.
+// rows x four adjacent N blocks (up: 4 x 64 h columns; down: 4 x 128 output
+// columns), i.e. 512 weight rows, for a workgroup of 8 waves (one per compute
+// unit, two waves per SIMD): wave w owns rows 32 (w % 4) .. + 31 of N blocks
+// 2 (w / 4) + a (sub-blocks a = 0, 1). Every activation chunk staged in LDS so
+// feeds 512 weight rows: at ~100 rows per expert the activation re-reads,
+// which would otherwise rival the fp8 weight bytes, are three eighths of them.
+// 96 rows (3 MFMA blocks) keep the accumulators (96 registers) and a two-deep
+// weight ring (64) inside one wave's registers at two waves per SIMD.
 // Weights stream from HBM straight into the register ring (each lane 64
 // contiguous bytes of each of its two rows per chunk, as in the packed layout).
 // Activations go global -> LDS by LDS DMA (16 bytes per lane, 1 KiB = 4 staged
 // rows per wave load; the lane's global column is chosen so that slot s of
 // staged row r holds column piece s ^ (r % 16)), so they take no registers.
-// All loads of chunk c+1 are issued at the top of chunk c, right after the
-// barrier, and are first needed at its last step.
 // Dequantisation as fp8x8_dequant (exact decode, one fp32 multiply by the
 // 128 x 128 block scale, one rounding to bf16).
-constexpr int kF8BM = 96;                                   // activation rows per tile
-constexpr int kF8MB = kF8BM / 32;                           // MFMA row blocks per tile
-constexpr int kF8PartFloats = 4 * 2 * kF8MB * 16 * kWave;  // one workgroup's accumulators (96 KiB)
+constexpr int kF8BM = 96;                                           // activation rows per tile
+constexpr int kF8MB = kF8BM / 32;                                   // MFMA row blocks per tile
+constexpr int kF8Waves = 8;                                         // waves per workgroup
+constexpr int kF8Threads = kF8Waves * kWave;
+constexpr int kF8NB = kF8Waves / 2;                                 // N blocks per tile
+constexpr int kF8Grid = 256;                                        // 1 resident workgroup x 256 CUs
+constexpr int kF8PartFloats = kF8Waves * 2 * kF8MB * 16 * kWave;   // one workgroup's accumulators (192 KiB)
+static_assert(kF8Threads <= kMaxGemmThreads, "schedule scratch holds one entry per thread");
 
 __device__ __forceinline__ float* f8_slot(float* parts, int b, int slot) {
   return parts + (size_t(b) * 2 + slot) * kF8PartFloats;
@@ -1141,7 +1147,7 @@ __device__ __forceinline__ int f8_part_idx(int wv, int a, int b, int q, int lane
   return ((((wv * 2 + a) * kF8MB + b) * 4 + q) * kWave + lane) * 4;
 }
 
-// Tiles (pairs of N blocks) tl.nt .. tl.nt + n - 1 of one group and row tile,
+// Tiles (of four N blocks) tl.nt .. tl.nt + n - 1 of one group and row tile,
 // iterations [it_begin, it_end) of the run (as bf_run: with one row tile the
 // group's next tiles read the same activation rows, so the loads run ahead
 // across tile boundaries).
@@ -1153,6 +1159,8 @@ __device__ __forceinline__ void f8_run(const GemmArgs& p, const Tile& tl, int n,
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform: scalar
+  const int wq = wv & 3;   // the wave's 32 rows of each N block
+  const int wg = wv >> 2;  // the wave's pair of N blocks in the tile
   const int lr = lane & 31;
   const int lh = lane >> 5;
   const int nchunks = __builtin_amdgcn_readfirstlane(p.K / kKC);
@@ -1160,22 +1168,22 @@ __device__ __forceinline__ void f8_run(const GemmArgs& p, const Tile& tl, int n,
   it_end = __builtin_amdgcn_readfirstlane(it_end);
   n = __builtin_amdgcn_readfirstlane(n);
   const int last = it_end - 1;
-  // N block of sub-block a of the run's tile k (an odd N-block count leaves a
-  // group's last tile one block: its second sub-block repeats the first)
+  // N block of sub-block a of the run's tile k (past the group's last block a
+  // sub-block repeats it; its results are discarded)
   // (operands in scalar registers, so the arithmetic on them stays scalar)
-  const int nt0 = __builtin_amdgcn_readfirstlane(2 * tl.nt);
+  const int nt0 = __builtin_amdgcn_readfirstlane(kF8NB * tl.nt + 2 * wg);
   const int nt_max = __builtin_amdgcn_readfirstlane(p.n_tiles_n - 1);
-  auto ntof = [&](int k, int a) { return min(nt0 + 2 * k + a, nt_max); };
+  auto ntof = [&](int k, int a) { return min(nt0 + kF8NB * k + a, nt_max); };
 
   // weights: uniform base (the expert's block) + the lane's loop-invariant byte
   // offset (its row in N block 0; an expert's weights span less than 4 GiB)
   const uint8_t* W = static_cast<const uint8_t*>(pick(tl.shared, p.sh_w, p.w));
   int wrow0;  // this lane's weight row in N block 0
   if (KIND == kUp) {
-    const int j = 16 * wv + (lr & 15);
+    const int j = 16 * wq + (lr & 15);
     wrow0 = lr < 16 ? j : p.n_out + j;
   } else {
-    wrow0 = 32 * wv + lr;
+    wrow0 = 32 * wq + lr;
   }
   // Weights and scales come by buffer loads (see buf_rsrc) from a resource at
   // the expert's base, with a scalar offset per (N block, chunk) and a
@@ -1187,7 +1195,7 @@ __device__ __forceinline__ void f8_run(const GemmArgs& p, const Tile& tl, int n,
   uint32_t woff;
   if constexpr (PACKED) {
     rw = buf_rsrc(W + size_t(tl.we) * p.n_tiles_n * nchunks * 4 * 4 * kWave * 16);
-    woff = uint32_t(wv * 4 * kWave + lane) * 16u;
+    woff = uint32_t(wq * 4 * kWave + lane) * 16u;
   } else {
     rw = buf_rsrc(W + size_t(tl.we) * p.n_w_rows * p.K);
     woff = uint32_t(wrow0 * p.K + 64 * lh);
@@ -1216,8 +1224,8 @@ __device__ __forceinline__ void f8_run(const GemmArgs& p, const Tile& tl, int n,
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, s_lane, __builtin_amdgcn_readfirstlane(so), 0));
   };
 
-  // activations: load q of this wave stages tile rows 4 (4 q + wv) .. + 3
-  constexpr int XL = (NB * 8 + 3) / 4;  // 1 KiB loads per wave per chunk
+  // activations: load q of this wave stages tile rows 4 (8 q + wv) .. + 3
+  constexpr int XL = NB * 8 / kF8Waves;  // 1 KiB loads per wave per chunk
   const uint16_t* A = static_cast<const uint16_t*>(pick(tl.shared, p.sh_a, p.a));
   const bool ablk = pick(tl.shared, p.sh_a_blk, p.a_blk);
   const size_t xstep = ablk ? size_t(4) * 512 : size_t(kKC);  // elements from one chunk of a row to the next
@@ -1229,7 +1237,7 @@ __device__ __forceinline__ void f8_run(const GemmArgs& p, const Tile& tl, int n,
   uint32_t xoff[XL];
 #pragma unroll
   for (int q = 0; q < XL; ++q) {
-    const int r = 4 * (4 * q + wv) + (lane >> 4);
+    const int r = 4 * (kF8Waves * q + wv) + (lane >> 4);
     const int c = (lane & 15) ^ (r & 15);  // column piece this lane's LDS slot holds
     const int phys = r < NB * 32 ? sh.rowmap[r] : -1;
     const int pr = phys >= 0 ? phys : phys0;  // rows past the tile feed only discarded columns
@@ -1301,7 +1309,7 @@ __device__ __forceinline__ void f8_run(const GemmArgs& p, const Tile& tl, int n,
     const int k_ = k_ld, c_ = c_ld;                                                                         \
     const gptr<char> xc_ = xb + uint64_t(c_) * xstep * 2; /* the chunk's base: scalar */                   \
     _Pragma("unroll") for (int q = 0; q < XL; ++q)                                                          \
-      lds_dma16_untracked(xc_, xoff[q], (XBUF_) + (4 * q + wv) * 512);                                      \
+      lds_dma16_untracked(xc_, xoff[q], (XBUF_) + (kF8Waves * q + wv) * 512);                               \
     _Pragma("unroll") for (int a = 0; a < 2; ++a) SR_[a] = scale(k_, c_, a);                                \
   }
 #define MOE_F8_PIECE(WR_, J_)                                                                               \
@@ -1350,8 +1358,8 @@ __device__ __forceinline__ void f8_run(const GemmArgs& p, const Tile& tl, int n,
       if (part_ == nullptr) {                                                                               \
         _Pragma("unroll") for (int a = 0; a < 2; ++a) {                                                     \
           Tile ta_ = tl;                                                                                    \
-          ta_.nt = 2 * (tl.nt + k_) + a;                                                                    \
-          if (ta_.nt < p.n_tiles_n) ffn_epilogue<KIND, NB>(acc[a], ta_, NB, sh, out, p.n_out, wv, lr, lh, p.out_blk); \
+          ta_.nt = kF8NB * (tl.nt + k_) + 2 * wg + a;                                                       \
+          if (ta_.nt < p.n_tiles_n) ffn_epilogue<KIND, NB>(acc[a], ta_, NB, sh, out, p.n_out, wq, lr, lh, p.out_blk); \
         }                                                                                                   \
       } else {                                                                                              \
         _Pragma("unroll") for (int a = 0; a < 2; ++a)                                                       \
@@ -1434,25 +1442,25 @@ __device__ __forceinline__ void f8_run(const GemmArgs& p, const Tile& tl, int n,
 }
 
 // Stream-K over (tile, chunk) iterations as ffn_bf16_kernel, with tiles of 96
-// rows x two N blocks, streamed in runs as there.
+// rows x four N blocks over at most kF8Grid ranges, streamed in runs as there.
 template <int KIND, bool PACKED>
-__global__ __launch_bounds__(kGemmThreads, 2) void ffn_fp8_kernel(GemmArgs p, float* __restrict__ parts) {
+__global__ __launch_bounds__(kF8Threads, 1) void ffn_fp8_kernel(GemmArgs p, float* __restrict__ parts) {
   __shared__ Sched sh;
   __shared__ __attribute__((aligned(1024))) uint16_t x0[kF8BM * kKC], x1[kF8BM * kKC], x2[kF8BM * kKC];
-  const int ntn2 = (p.n_tiles_n + 1) / 2;
-  const int n_tiles = build_schedule(p, kF8BM, ntn2, false, sh);
+  const int ntn4 = (p.n_tiles_n + kF8NB - 1) / kF8NB;
+  const int n_tiles = build_schedule<kF8Threads>(p, kF8BM, ntn4, false, sh);
   const int nchunks = p.K / kKC;
   const int64_t total = int64_t(n_tiles) * nchunks;
-  const int G = sk_grid(total);
+  const int G = sk_grid(total, kF8Grid);
   if (int(blockIdx.x) >= G) return;  // uniform
   const int rng = int(blockIdx.x % kXcds) * (G / kXcds) + int(blockIdx.x / kXcds);
   const int64_t i0 = sk_start(rng, total, G), i1 = sk_start(rng + 1, total, G);
   if (i0 >= i1) return;  // uniform
   const int t_first = int(i0 / nchunks), t_last = int((i1 - 1) / nchunks);
   for (int t = t_first; t <= t_last;) {
-    const Tile tl = decode_tile(p, kF8BM, ntn2, sh, t);
-    build_rowmap(p, tl, kF8BM, sh);
-    const int n = tl.mtiles == 1 ? min(t_last - t + 1, ntn2 - tl.nt) : 1;
+    const Tile tl = decode_tile(p, kF8BM, ntn4, sh, t);
+    build_rowmap<kF8Threads>(p, tl, kF8BM, sh);
+    const int n = tl.mtiles == 1 ? min(t_last - t + 1, ntn4 - tl.nt) : 1;
     const int64_t t0 = int64_t(t) * nchunks;
     const int it_begin = int(max<int64_t>(i0 - t0, 0));
     const int it_end = int(min<int64_t>(i1 - t0, int64_t(n) * nchunks));
@@ -1476,7 +1484,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void ffn_fp8_kernel(GemmArgs p, fl
 }
 
 // Finishes the fp8 tiles cut by a range boundary (as ffn_fixup_kernel); block
-// (j, a * kF8MB + b) takes sub-block a, 32-row block b.
+// (j, m * kF8MB + b) takes the tile's N block m, 32-row block b, with one wave
+// per 32 rows of the block (the partials of the main kernel's waves m / 2 * 4
+// .. + 3, sub-block m % 2).
 template <int KIND>
 __global__ __launch_bounds__(kGemmThreads) void ffn_fp8_fixup_kernel(GemmArgs p, const float* __restrict__ parts) {
   __shared__ Sched sh;
@@ -1485,19 +1495,19 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_fp8_fixup_kernel(GemmArgs p,
   const int wv = tid / kWave;
   const int lr = lane & 31;
   const int lh = lane >> 5;
-  const int ntn2 = (p.n_tiles_n + 1) / 2;
-  const int n_tiles = build_schedule(p, kF8BM, ntn2, false, sh);
+  const int ntn4 = (p.n_tiles_n + kF8NB - 1) / kF8NB;
+  const int n_tiles = build_schedule(p, kF8BM, ntn4, false, sh);
   const int nchunks = p.K / kKC;
   const int64_t total = int64_t(n_tiles) * nchunks;
-  const int j = blockIdx.x, a = blockIdx.y / kF8MB, b = blockIdx.y % kF8MB;
-  const int G = sk_grid(total);
+  const int j = blockIdx.x, m = blockIdx.y / kF8MB, b = blockIdx.y % kF8MB;
+  const int G = sk_grid(total, kF8Grid);
   if (j + 1 >= G) return;  // uniform: boundaries lie between ranges 0 .. G-1
   const int64_t ib = sk_start(j + 1, total, G);
   if (ib <= 0 || ib >= total || ib % nchunks == 0) return;  // not inside a tile
   const int t = int(ib / nchunks);
   if (j > 0 && sk_start(j, total, G) > int64_t(t) * nchunks) return;  // an earlier boundary owns this tile
-  Tile tl = decode_tile(p, kF8BM, ntn2, sh, t);
-  if (b * 32 >= tl.nrows || 2 * tl.nt + a >= p.n_tiles_n) return;  // uniform: no rows / no such N block
+  Tile tl = decode_tile(p, kF8BM, ntn4, sh, t);
+  if (b * 32 >= tl.nrows || kF8NB * tl.nt + m >= p.n_tiles_n) return;  // uniform: no rows / no such N block
   build_rowmap(p, tl, kF8BM, sh);
   const int b_lo = sk_owner(int64_t(t) * nchunks, total, G);
   const int b_hi = sk_owner(int64_t(t + 1) * nchunks - 1, total, G);
@@ -1508,8 +1518,8 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_fp8_fixup_kernel(GemmArgs p,
         const int64_t s0 = sk_start(w, total, G), s1 = sk_start(w + 1, total, G);
         return s0 < s1 ? f8_slot(const_cast<float*>(parts), w, int(s0 / nchunks) == t ? 0 : 1) : nullptr;
       },
-      [&](int, int q) { return f8_part_idx(wv, a, b, q, lane); });
-  tl.nt = 2 * tl.nt + a;
+      [&](int, int q) { return f8_part_idx(m / 2 * 4 + wv, m % 2, b, q, lane); });
+  tl.nt = kF8NB * tl.nt + m;
   uint16_t* out = static_cast<uint16_t*>(pick(tl.shared, p.sh_out, p.out));
   ffn_epilogue_block<KIND>(acc[0], tl, b, sh, out, p.n_out, wv, lr, lh, p.out_blk);
 }
@@ -1656,7 +1666,7 @@ static size_t h_bytes(const moe_ggemm_desc_t* d, int64_t rows) {
 
 static size_t parts_bytes(const moe_ggemm_desc_t* d) {
   // shared by the wide and the stream-K kernels, which run one after the other
-  const size_t sk = size_t(2) * kSkGrid * (d->w_dt == MOE_FP8_E4M3 ? kF8PartFloats : kPartFloats);
+  const size_t sk = d->w_dt == MOE_FP8_E4M3 ? size_t(2) * kF8Grid * kF8PartFloats : size_t(2) * kSkGrid * kPartFloats;
   const size_t wide = size_t(kWideGrid) * kWidePart;
   return d->act_dt == MOE_F32 ? 0 : std::max(sk, wide) * sizeof(float);
 }
@@ -1708,12 +1718,13 @@ static moe_status_t launch_stage(const GemmArgs& p, bool f32, bool fp8, int kind
   }
   const dim3 grid(kSkGrid);
   if (fp8) {
-#define MOE_F8(K, P) hipLaunchKernelGGL((ffn_fp8_kernel<K, P>), grid, block, 0, stream, p, parts)
+    const dim3 f8_grid(kF8Grid), f8_block(kF8Threads);
+#define MOE_F8(K, P) hipLaunchKernelGGL((ffn_fp8_kernel<K, P>), f8_grid, f8_block, 0, stream, p, parts)
     if (kind == kUp) { if (p.packed) MOE_F8(kUp, true); else MOE_F8(kUp, false); }
     else { if (p.packed) MOE_F8(kDown, true); else MOE_F8(kDown, false); }
 #undef MOE_F8
     if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
-    const dim3 fix_grid(kSkGrid - 1, 2 * kF8MB);
+    const dim3 fix_grid(kF8Grid - 1, kF8NB * kF8MB);
     if (kind == kUp) hipLaunchKernelGGL((ffn_fp8_fixup_kernel<kUp>), fix_grid, block, 0, stream, p, parts);
     else hipLaunchKernelGGL((ffn_fp8_fixup_kernel<kDown>), fix_grid, block, 0, stream, p, parts);
     return launch_status();
