@@ -105,11 +105,14 @@ struct Vec<uint16_t> {
   }
 };
 
-// Same decomposition as dispatch: each thread owns one 16-byte piece of the
-// output row and sums the token's kept expert rows in k order (all K loads in
-// flight at once), plus the shared-expert row for the GPU's own tokens.
-// PPT pieces per thread (stride 256), all their loads in flight at once.
-template <typename T, int KMAX, int PPT>
+// Same decomposition as dispatch: workgroup b handles PPT * 256 16-byte pieces
+// of token t = b / n_chunks. The token's kept entries (uniform per workgroup:
+// scalar) are taken in ascending k, KG at a time: the pieces of those KG rows
+// (and, with the first group, of the shared-expert row) are all in flight
+// together, then accumulated in k order; a token with at most KG rows on this
+// GPU - the usual case - costs one round trip. The registers held are PPT x KG
+// pieces, not PPT x K.
+template <typename T, int KMAX, int PPT, int KG>
 __global__ __launch_bounds__(kVecThreads) void combine_kernel(
     const uint4* __restrict__ ye, int64_t n_rows, const int32_t* __restrict__ row_of, const float* __restrict__ topk_w,
     int n_tokens, int top_k, int row_vecs, int n_chunks, const uint4* __restrict__ shared_y, int self_lo, int self_hi,
@@ -122,46 +125,82 @@ __global__ __launch_bounds__(kVecThreads) void combine_kernel(
   const float* wo = topk_w + size_t(t) * top_k;
   int r[KMAX];
   float w[KMAX];
-  bool any = false;
+  uint32_t kept = 0;  // bit k: entry k is a row of this GPU
 #pragma unroll
   for (int k = 0; k < KMAX; ++k) {
     r[k] = k < top_k ? ro[k] : -1;
     if (r[k] >= n_rows) r[k] = -1;
     w[k] = r[k] >= 0 ? wo[k] : 0.f;
-    any |= r[k] >= 0;
+    kept |= r[k] >= 0 ? 1u << k : 0u;
   }
   const bool in_self = shared_y != nullptr && t >= self_lo && t < self_hi;
-  if ((!any && !in_self) || c0 >= row_vecs) return;
-  uint4 v[PPT][KMAX], vs[PPT];
+  if ((kept == 0 && !in_self) || c0 >= row_vecs) return;
+  int cs[PPT];  // piece indices (a tail piece repeats a valid one; its result is not stored)
 #pragma unroll
-  for (int i = 0; i < PPT; ++i) {
-    const int c = min(c0 + i * kVecThreads, row_vecs - 1);  // a tail piece repeats a valid one
+  for (int i = 0; i < PPT; ++i) cs[i] = min(c0 + i * kVecThreads, row_vecs - 1);
+  uint4 vs[PPT];
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k) v[i][k] = r[k] >= 0 ? ye[size_t(r[k]) * row_vecs + c] : make_uint4(0, 0, 0, 0);
-    vs[i] = in_self ? shared_y[size_t(t - self_lo) * row_vecs + c] : make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < PPT; ++i)
+    vs[i] = in_self ? shared_y[size_t(t - self_lo) * row_vecs + cs[i]] : make_uint4(0, 0, 0, 0);
+  float acc[PPT][EPV];
+#pragma unroll
+  for (int i = 0; i < PPT; ++i)
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) acc[i][e] = 0.f;
+  // entry k's rank among the kept ones (scalar); round j takes ranks
+  // j KG .. j KG + KG - 1. (Slots are chosen by comparing ranks, every array
+  // index static: a select on a computed index would be turned back into an
+  // indexed array, which the compiler keeps in memory.)
+  int rank[KMAX];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) rank[k] = (kept >> k & 1u) ? __builtin_popcount(kept & ((1u << k) - 1u)) : -1;
+  const int n_kept = __builtin_popcount(kept);
+  for (int j0 = 0; j0 < n_kept; j0 += KG) {  // uniform
+    int rg[KG];
+    float wg[KG];
+#pragma unroll
+    for (int g = 0; g < KG; ++g) {
+      if constexpr (KG >= KMAX) {  // one round: every entry in its own slot
+        rg[g] = r[g];
+        wg[g] = w[g];
+      } else {
+        rg[g] = -1;
+        wg[g] = 0.f;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+          const bool hit = rank[k] == j0 + g;
+          rg[g] = hit ? r[k] : rg[g];
+          wg[g] = hit ? w[k] : wg[g];
+        }
+      }
+    }
+    uint4 v[PPT][KG];
+#pragma unroll
+    for (int i = 0; i < PPT; ++i)
+#pragma unroll
+      for (int g = 0; g < KG; ++g)
+        v[i][g] = rg[g] >= 0 ? ye[size_t(rg[g]) * row_vecs + cs[i]] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < PPT; ++i)
+#pragma unroll
+      for (int g = 0; g < KG; ++g)
+        if (rg[g] >= 0) {
+          float f[EPV];
+          Vec<T>::load(v[i][g], f);
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) acc[i][e] = fmaf(wg[g], f[e], acc[i][e]);
+        }
   }
 #pragma unroll
   for (int i = 0; i < PPT; ++i) {
     const int c = c0 + i * kVecThreads;
-    float acc[EPV];
-#pragma unroll
-    for (int e = 0; e < EPV; ++e) acc[e] = 0.f;
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-      if (r[k] >= 0) {
-        float f[EPV];
-        Vec<T>::load(v[i][k], f);
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) acc[e] = fmaf(w[k], f[e], acc[e]);
-      }
-    }
     if (in_self) {
       float f[EPV];
       Vec<T>::load(vs[i], f);
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) acc[e] += f[e];
+      for (int e = 0; e < EPV; ++e) acc[i][e] += f[e];
     }
-    if (c < row_vecs) out[size_t(t) * row_vecs + c] = Vec<T>::store(acc);
+    if (c < row_vecs) out[size_t(t) * row_vecs + c] = Vec<T>::store(acc[i]);
   }
 }
 
@@ -224,17 +263,34 @@ MOE_API moe_status_t moe_dispatch_blocked(const void* x, moe_dtype_t dt, int n_t
   return launch_status();
 }
 
-// pieces per combine thread: 2 keeps up to 2 x 16 loads in flight within the
-// register budget
-constexpr int kCombinePpt = 2;
+// Two shapes. From about a thousand tokens: 4 pieces per thread (a 7168-wide
+// bf16 row is one workgroup) and 2 kept rows per round trip, the most bytes
+// in flight per register (measured best from 1024 tokens of a 7168-wide
+// layer up). Smaller batches: 2 pieces per thread (twice the workgroups) and
+// all K rows in one round trip, so no token costs more than one.
+constexpr int kCombineManyTokens = 1024;
+
+template <typename T, int KMAX, int PPT, int KG>
+static void launch_combine(hipStream_t stream, const void* ye, int64_t n_rows, const int32_t* row_of,
+                           const float* topk_w, int n_tokens, int top_k, int row_vecs, const void* shared_y,
+                           int self_lo, int self_hi, void* out) {
+  const int n_chunks = (row_vecs + kVecThreads * PPT - 1) / (kVecThreads * PPT);
+  const dim3 grid(vec_grid(int64_t(n_chunks) * n_tokens));
+  hipLaunchKernelGGL((combine_kernel<T, KMAX, PPT, KG>), grid, dim3(kVecThreads), 0, stream,
+                     static_cast<const uint4*>(ye), n_rows, row_of, topk_w, n_tokens, top_k, row_vecs, n_chunks,
+                     static_cast<const uint4*>(shared_y), self_lo, self_hi, static_cast<uint4*>(out));
+}
 
 template <typename T, int KMAX>
-static void launch_combine(dim3 grid, hipStream_t stream, const void* ye, int64_t n_rows, const int32_t* row_of,
-                           const float* topk_w, int n_tokens, int top_k, int row_vecs, int n_chunks, const void* shared_y,
+static void launch_combine(hipStream_t stream, const void* ye, int64_t n_rows, const int32_t* row_of,
+                           const float* topk_w, int n_tokens, int top_k, int row_vecs, const void* shared_y,
                            int self_lo, int self_hi, void* out) {
-  hipLaunchKernelGGL((combine_kernel<T, KMAX, kCombinePpt>), grid, dim3(kVecThreads), 0, stream, static_cast<const uint4*>(ye),
-                     n_rows, row_of, topk_w, n_tokens, top_k, row_vecs, n_chunks, static_cast<const uint4*>(shared_y), self_lo,
-                     self_hi, static_cast<uint4*>(out));
+  if (n_tokens >= kCombineManyTokens)
+    launch_combine<T, KMAX, 4, 2>(stream, ye, n_rows, row_of, topk_w, n_tokens, top_k, row_vecs, shared_y, self_lo,
+                                  self_hi, out);
+  else
+    launch_combine<T, KMAX, 2, KMAX>(stream, ye, n_rows, row_of, topk_w, n_tokens, top_k, row_vecs, shared_y, self_lo,
+                                     self_hi, out);
 }
 
 MOE_API moe_status_t moe_combine(const void* ye, moe_dtype_t dt, int64_t n_rows, const int32_t* row_of,
@@ -251,11 +307,10 @@ MOE_API moe_status_t moe_combine(const void* ye, moe_dtype_t dt, int64_t n_rows,
   if (n_rows > 0 && (!ye || !aligned16(ye))) return MOE_ERR_INVALID_ARG;
   if (shared_y && !aligned16(shared_y)) return MOE_ERR_INVALID_ARG;
   const int row_vecs = int(row_bytes / 16);
-  const int n_chunks = (row_vecs + kVecThreads * kCombinePpt - 1) / (kVecThreads * kCombinePpt);
+  const int n_chunks = (row_vecs + kVecThreads * 2 - 1) / (kVecThreads * 2);  // the smaller pieces' count
   if (int64_t(n_chunks) * n_tokens >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
-  const dim3 grid(vec_grid(int64_t(n_chunks) * n_tokens));
 #define MOE_COMBINE(T, KM) \
-  launch_combine<T, KM>(grid, stream, ye, n_rows, row_of, topk_w, n_tokens, top_k, row_vecs, n_chunks, shared_y, self_lo, self_hi, out)
+  launch_combine<T, KM>(stream, ye, n_rows, row_of, topk_w, n_tokens, top_k, row_vecs, shared_y, self_lo, self_hi, out)
   const int kmax = kmax_of(top_k);
   if (dt == MOE_F32) {
     if (kmax == 2) MOE_COMBINE(float, 2);

@@ -263,6 +263,31 @@ def test_layer_identity_property_bf16():
     assert rel_l2(f64(out), ref) <= 4e-3  # one bf16 rounding of each output
 
 
+# Many tokens take the combine's throughput shape (four pieces per thread, two
+# kept rows per round trip): tokens keeping 0..8 local rows exercise every
+# number of round trips, plus the shared rows of the self range; rows with
+# nothing to add keep their previous contents.
+def test_combine_many_tokens_all_kept_counts():
+    rng = np.random.default_rng(31)
+    N, K, H = 20000, 8, 264  # 33 pieces per row: a ragged last piece group
+    R = N * K
+    keep = rng.random((N, K)) < rng.random((N, 1))  # per-token keep rate: kept counts spread over 0..8
+    row_of = np.where(keep, rng.permutation(R).reshape(N, K), -1).astype(np.int32)
+    w = rng.random((N, K)).astype(np.float32)
+    ye = torch.randn(R, H).to(torch.bfloat16)
+    lo, hi = 1000, 3000
+    sy = torch.randn(hi - lo, H).to(torch.bfloat16)
+    out = torch.full((N, H), 7.0, dtype=torch.bfloat16, device="cuda")
+    moe.moe_combine(ye.cuda(), torch.from_numpy(row_of).cuda(), torch.from_numpy(w).cuda(), out, sy.cuda(), lo, hi)
+    sample = np.sort(rng.choice(N, 3000, replace=False))
+    ref = combine(f64(ye), row_of.reshape(-1), w, K, np.full((N, H), 7.0), f64(sy), lo, hi, tokens=sample)
+    got = f64(out)
+    assert rel_l2(got[sample], ref[sample]) <= 4e-3  # one bf16 rounding of each output
+    untouched = np.array([t for t in sample if not keep[t].any() and not lo <= t < hi])
+    assert len(untouched) > 0 and (got[untouched] == 7.0).all()
+    assert {int(c) for c in keep[sample].sum(axis=1)} >= set(range(K + 1))
+
+
 # --------------------------------------------------------------------------- whole layer (full size)
 FULL = ["dsv3_decode_ep8", "dsv3_decode_ep128", "kimi_k2_ep8", "dsv3_prefill_ep8"]
 
