@@ -188,6 +188,9 @@ def main(argv=None):
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of replays of a HIP graph of one step")
     ap.add_argument("--cpu-max-tokens", type=int, default=1024)
+    ap.add_argument("--flush-mb", type=int, default=512,
+                    help="read a buffer of this size between timed steps (outside the timed events), so the 256 MB "
+                         "Infinity Cache and L2 cannot carry data from one step to the next; 0: off")
     ap.add_argument("--copy-calib", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
     args = ap.parse_args(argv)
@@ -242,19 +245,34 @@ def main(argv=None):
         share.step(logits, offs, x, out)
     torch.cuda.synchronize()
 
+    # between timed steps (never inside the events): a read of a buffer twice
+    # the Infinity Cache, so no step finds the previous one's weights or
+    # activations in a cache. (A read, not a write: written flush data would
+    # sit dirty in the cache and be written back during the next step.) The
+    # previous step's own dirty lines are written back during the flush.
+    flush_buf = torch.ones((args.flush_mb << 20) // 8, dtype=torch.int64, device="cuda") if args.flush_mb > 0 else None
+    flush_sink = torch.zeros((), dtype=torch.int64, device="cuda")
+
+    def flush():
+        if flush_buf is not None:
+            torch.sum(flush_buf, dim=0, out=flush_sink)
+
+    def step_events(n):
+        return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
     # per-call timing: eager steps with events around each call
-    ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)] for n in STEP_NAMES}
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = {n: step_events(args.steps) for n in STEP_NAMES}
+    est = step_events(args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    e0.record()
     for i in range(args.steps):
+        flush()
+        est[i][0].record()
         share.step(logits, offs, x, out, events={n: ev[n][i] for n in STEP_NAMES})
-    e1.record()
+        est[i][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    eager_ms = e0.elapsed_time(e1) / args.steps
+    eager_ms = float(np.mean([a.elapsed_time(b) for a, b in est]))
     per_call_us = {n: 1e3 * float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n in STEP_NAMES}
 
     # the step as one HIP graph (one graph per batch shape, as the pages do with
@@ -273,15 +291,16 @@ def main(argv=None):
         for _ in range(max(1, args.warmup)):
             graph.replay()
         torch.cuda.synchronize()
-        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gst = step_events(args.steps)
         t0 = time.perf_counter()
-        g0.record()
-        for _ in range(args.steps):
+        for i in range(args.steps):
+            flush()
+            gst[i][0].record()
             graph.replay()
-        g1.record()
+            gst[i][1].record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        graph_ms = g0.elapsed_time(g1) / args.steps
+        graph_ms = float(np.mean([a.elapsed_time(b) for a, b in gst]))
     ms_per_step = graph_ms if graph_ms is not None else eager_ms
     st = int(share.lay["status"].item())
 
@@ -330,6 +349,7 @@ def main(argv=None):
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
         "timing": "hip_graph_replay" if graph_ms is not None else "eager",
+        "cache_flush_mb": args.flush_mb,
         "ms_per_step_eager": round(eager_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
