@@ -333,8 +333,9 @@ __device__ __forceinline__ bf16x8_t fp8x8_dequant(uint32_t w0, uint32_t w1, floa
 
 // ------------------------------------------------------------------ MFMA kernel
 // Stream-K split of the work: the iterations (tile, 128-deep K chunk) of the
-// whole launch are cut into kSkGrid equal contiguous ranges, one per
-// workgroup, so every workgroup streams the same number of weight bytes no
+// whole launch are cut into equal contiguous ranges, one per workgroup (at
+// most kBfGrid for bf16 weights, kF8Grid for fp8: one resident workgroup per
+// compute unit), so every workgroup streams the same number of weight bytes no
 // matter how the tile count compares with the number of workgroups. A tile
 // covered by one workgroup is finished in place; a tile cut by a range
 // boundary leaves fp32 partial sums (in accumulator-register order) in the
@@ -342,13 +343,27 @@ __device__ __forceinline__ bf16x8_t fp8x8_dequant(uint32_t w0, uint32_t w1, floa
 // the tile. No workgroup ever waits for another. When the launch has little
 // work, fewer ranges are used (at least kSkMinChunks chunks each), so the
 // partial sums stay small next to the weights streamed.
-constexpr int kSkGrid = 512;                          // 2 resident workgroups x 256 compute units
 constexpr int kXcds = 8;                              // accelerator complex dies of MI355X
-constexpr int kPartFloats = 4 * kMB * 16 * kWave;     // one workgroup's accumulators (64 KiB)
+constexpr int kPartFloats = 4 * kMB * 16 * kWave;     // a bf16 workgroup's accumulators (64 KiB)
 constexpr int kSkMinChunks = 8;
 
+// bf16 decode kernel (ffn_bf16_kernel): tiles of 64 activation rows x two N
+// blocks for a workgroup of 8 waves, one workgroup per compute unit
+constexpr int kBfBM = kBM / 2;                 // activation rows per tile
+constexpr int kBfMB = kBfBM / 32;              // 32-row MFMA blocks per tile
+constexpr int kBfWaves = 8;                    // waves per workgroup (one workgroup per CU)
+constexpr int kBfThreads = kBfWaves * kWave;
+constexpr int kBfNB = kBfWaves / 4;            // N blocks per tile
+constexpr int kBfGrid = 256;                   // 1 resident workgroup x 256 CUs
+static_assert(kBfThreads <= kMaxGemmThreads, "schedule scratch holds one entry per thread");
+static_assert(kBfWaves * kBfMB * 16 * kWave <= kPartFloats, "a workgroup's accumulators fit a partial slot");
+// [wave][block][quad q][lane][4 floats]: 1 KiB contiguous per wave access
+__device__ __forceinline__ int bf_part_idx(int wv, int b, int q, int lane) {
+  return (((wv * kBfMB + b) * 4 + q) * kWave + lane) * 4;
+}
+
 // Ranges used for a launch of `total` iterations: a multiple of the XCD count.
-__device__ inline int sk_grid(int64_t total, int max_grid = kSkGrid) {
+__device__ inline int sk_grid(int64_t total, int max_grid) {
   const int64_t g = total / kSkMinChunks / kXcds * kXcds;
   return int(max<int64_t>(kXcds, min<int64_t>(max_grid, g)));
 }
@@ -439,11 +454,13 @@ __device__ __forceinline__ void sum_partials(f32x16_t (&acc)[NA], int w_lo, int 
   }
 }
 
-// Finishes the tiles cut by a stream-K range boundary: block (j, b) looks at
-// the boundary between workgroups j and j+1; the first boundary inside a tile
-// sums that tile's partials of 32-row block b in workgroup order and runs its
+// Finishes the tiles of ffn_bf16_kernel cut by a stream-K range boundary:
+// block (j, m * kBfMB + b) looks at the boundary between workgroups j and
+// j+1; the first boundary inside a tile sums, for the tile's N block m and
+// 32-row block b, its partials in workgroup order (one wave per 32 rows of the
+// block: the main kernel's waves 4 m .. 4 m + 3) and runs that block's
 // epilogue.
-template <int KIND, int BMT>
+template <int KIND>
 __global__ __launch_bounds__(kGemmThreads) void ffn_fixup_kernel(GemmArgs p, const float* __restrict__ parts) {
   __shared__ Sched sh;
   const int tid = threadIdx.x;
@@ -451,19 +468,20 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_fixup_kernel(GemmArgs p, con
   const int wv = tid / kWave;
   const int lr = lane & 31;
   const int lh = lane >> 5;
-  const int n_tiles = build_schedule(p, BMT, p.n_tiles_n, false, sh);
+  const int ntn2 = (p.n_tiles_n + kBfNB - 1) / kBfNB;
+  const int n_tiles = build_schedule(p, kBfBM, ntn2, false, sh);
   const int nchunks = p.K / kKC;
   const int64_t total = int64_t(n_tiles) * nchunks;
-  const int j = blockIdx.x, b = blockIdx.y;
-  const int G = sk_grid(total);
+  const int j = blockIdx.x, m = blockIdx.y / kBfMB, b = blockIdx.y % kBfMB;
+  const int G = sk_grid(total, kBfGrid);
   if (j + 1 >= G) return;  // uniform: boundaries lie between ranges 0 .. G-1
   const int64_t ib = sk_start(j + 1, total, G);
   if (ib <= 0 || ib >= total || ib % nchunks == 0) return;  // not inside a tile
   const int t = int(ib / nchunks);
   if (j > 0 && sk_start(j, total, G) > int64_t(t) * nchunks) return;  // an earlier boundary owns this tile
-  const Tile tl = decode_tile(p, BMT, p.n_tiles_n, sh, t);
-  if (b * 32 >= tl.nrows) return;  // uniform: no rows in this block
-  build_rowmap(p, tl, BMT, sh);
+  Tile tl = decode_tile(p, kBfBM, ntn2, sh, t);
+  if (b * 32 >= tl.nrows || kBfNB * tl.nt + m >= p.n_tiles_n) return;  // uniform: no rows / no such N block
+  build_rowmap(p, tl, kBfBM, sh);
   const int b_lo = sk_owner(int64_t(t) * nchunks, total, G);
   const int b_hi = sk_owner(int64_t(t + 1) * nchunks - 1, total, G);
   f32x16_t acc[1];
@@ -473,7 +491,8 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_fixup_kernel(GemmArgs p, con
         const int64_t s0 = sk_start(w, total, G), s1 = sk_start(w + 1, total, G);
         return s0 < s1 ? sk_slot(const_cast<float*>(parts), w, int(s0 / nchunks) == t ? 0 : 1) : nullptr;
       },
-      [&](int, int q) { return (((wv * kMB + b) * 4 + q) * kWave + lane) * 4; });
+      [&](int, int q) { return bf_part_idx(4 * m + wv, b, q, lane); });
+  tl.nt = kBfNB * tl.nt + m;
   uint16_t* out = static_cast<uint16_t*>(pick(tl.shared, p.sh_out, p.out));
   ffn_epilogue_block<KIND>(acc[0], tl, b, sh, out, p.n_out, wv, lr, lh, p.out_blk);
 }
@@ -889,8 +908,9 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_wide_fixup_kernel(GemmArgs p
 
 // ------------------------------------------------------------------ bf16 decode kernel
 // bf16 weights, decode-shaped groups: stream-K ranges over tiles of 64
-// activation rows x one N block (128 weight rows; each wave 32 weight rows,
-// up: 16 gate rows and the 16 matching up rows), the activations staged by
+// activation rows x two adjacent N blocks (256 weight rows) for a workgroup of
+// 8 waves, one per compute unit (each wave 32 weight rows of one block; up: 16
+// gate rows and the 16 matching up rows), the activations staged by
 // LDS DMA and the weights
 // loaded straight into registers (each lane 8 16-byte pieces of its weight row
 // per chunk). Three chunks are in flight per workgroup (three LDS activation
@@ -903,11 +923,13 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_wide_fixup_kernel(GemmArgs p
 // boundaries instead of draining at every tile (with K = 2048 a tile is only
 // 16 chunks); each tile's epilogue is issued as soon as its last chunk is
 // multiplied.
-constexpr int kBfBM = kBM / 2;  // activation rows per tile
 
 // Tiles tl.nt .. tl.nt + n - 1 of one group and row tile, iterations
 // [it_begin, it_end) of the run (iteration k * nchunks + c is chunk c of its
-// tile k). The first / last tile leave fp32 partials in part_first /
+// tile k). A tile is 64 rows x two N blocks; wave w owns rows 32 (w % 4) ..
+// of N block 2 tile + w / 4 (past the group's last block a wave repeats it and
+// its results are discarded), so each staged activation chunk feeds 256
+// weight rows. The first / last tile leave fp32 partials in part_first /
 // part_last when split (else nullptr: their epilogue runs here).
 template <int KIND, bool PACKED, int NB, bool STREAM>
 __device__ __forceinline__ void bf_run(const GemmArgs& p, const Tile& tl, int n, const Sched& sh,
@@ -916,49 +938,54 @@ __device__ __forceinline__ void bf_run(const GemmArgs& p, const Tile& tl, int n,
                                        float* __restrict__ part_first, float* __restrict__ part_last) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wv = tid / kWave;
+  const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform: scalar
+  const int wq = wv & 3;   // the wave's 32 rows of its N block
+  const int wg = wv >> 2;  // the wave's N block in the tile
   const int lr = lane & 31;
   const int lh = lane >> 5;
   const int nchunks = p.K / kKC;
   const int last = it_end - 1;
+  // N block of the run's tile k for this wave
+  const int nb0 = __builtin_amdgcn_readfirstlane(kBfNB * tl.nt + wg);
+  const int nb_max = __builtin_amdgcn_readfirstlane(p.n_tiles_n - 1);
+  auto nbof = [&](int k) { return min(nb0 + kBfNB * k, nb_max); };
 
-  // weights: this lane's row of the run's first tile; piece j of chunk C covers
+  // weights: this lane's row of N block 0; piece j of chunk C covers
   // k = 128 C + 64 (j / 4) + 32 lh + 8 (j % 4)
   const uint16_t* W = static_cast<const uint16_t*>(pick(tl.shared, p.sh_w, p.w));
   int wrow;
   if (KIND == kUp) {
-    const int j = tl.nt * 64 + 16 * wv + (lr & 15);
+    const int j = 16 * wq + (lr & 15);
     wrow = lr < 16 ? j : p.n_out + j;
   } else {
-    wrow = tl.nt * 128 + 32 * wv + lr;
+    wrow = 32 * wq + lr;
   }
   // uniform base (the expert's block) + the lane's loop-invariant byte offset
   // (an expert's weights span less than 4 GiB)
   gptr<char> wbase;
   uint32_t woff;
   if constexpr (PACKED) {
-    wbase = uniform_ptr(reinterpret_cast<const char*>(W) +
-                        (size_t(tl.we) * p.n_tiles_n + tl.nt) * nchunks * 4 * 8 * kWave * 16);
-    woff = uint32_t(wv * 8 * kWave + lane) * 16u;
+    wbase = uniform_ptr(reinterpret_cast<const char*>(W) + size_t(tl.we) * p.n_tiles_n * nchunks * 4 * 8 * kWave * 16);
+    woff = uint32_t(wq * 8 * kWave + lane) * 16u;
   } else {
     wbase = uniform_ptr(reinterpret_cast<const char*>(W + size_t(tl.we) * p.n_w_rows * p.K));
     woff = uint32_t(wrow * p.K + 32 * lh) * 2u;
   }
-  // iteration I, piece j: packed, the N tiles of a group follow each other, so
-  // the address is linear in I; row-major, tile k's rows are 64 (gate and up)
-  // or 128 rows below the first tile's
+  // iteration (tile k, chunk C), piece j: packed, block nb's chunks follow each
+  // other; row-major, block nb's rows are 64 (gate and up) or 128 rows below
+  // block 0's
   const uint64_t tstep = uint64_t(KIND == kUp ? 64 : 128) * p.K * 2;
-  auto wpiece = [&](int I, int j) -> gptr<uint4> {
+  auto wpiece = [&](int k, int C, int j) -> gptr<uint4> {
+    const int nb = nbof(k);
     if constexpr (PACKED) {
-      return at<uint4>(wbase, (uint64_t(I) * 4 * 8 + j) * kWave * 16, woff);
+      return at<uint4>(wbase, ((uint64_t(nb) * nchunks + C) * 4 * 8 + j) * kWave * 16, woff);
     } else {
-      const int k = I / nchunks, C = I - k * nchunks;
-      return at<uint4>(wbase, k * tstep + uint64_t(C) * kKC * 2 + (j >> 2) * 128 + (j & 3) * 16, woff);
+      return at<uint4>(wbase, nb * tstep + uint64_t(C) * kKC * 2 + (j >> 2) * 128 + (j & 3) * 16, woff);
     }
   };
 
-  // activations: load q of this wave stages tile rows 4 (4 q + wv) .. + 3
-  constexpr int XL = 2 * NB;  // 1 KiB loads per wave per chunk
+  // activations: load q of this wave stages tile rows 4 (8 q + wv) .. + 3
+  constexpr int XL = NB * 8 / kBfWaves;  // 1 KiB loads per wave per chunk
   const uint16_t* A = static_cast<const uint16_t*>(pick(tl.shared, p.sh_a, p.a));
   const bool ablk = pick(tl.shared, p.sh_a_blk, p.a_blk);
   const size_t xstep = ablk ? size_t(4) * 512 : size_t(kKC);  // elements from one chunk of a row to the next
@@ -970,7 +997,7 @@ __device__ __forceinline__ void bf_run(const GemmArgs& p, const Tile& tl, int n,
   uint32_t xoff[XL];
 #pragma unroll
   for (int q = 0; q < XL; ++q) {
-    const int r = 4 * (4 * q + wv) + (lane >> 4);
+    const int r = 4 * (kBfWaves * q + wv) + (lane >> 4);
     const int c = (lane & 15) ^ (r & 15);  // column piece this lane's LDS slot holds
     const int phys = sh.rowmap[r];
     const int pr = phys >= 0 ? phys : phys0;  // rows past the tile feed only discarded columns
@@ -988,11 +1015,11 @@ __device__ __forceinline__ void bf_run(const GemmArgs& p, const Tile& tl, int n,
   uint4 w0[8], w1[8], w2[8];  // weight ring
 #define MOE_BF_LOADS(I_, XBUF_, WR_)                                                                          \
   {                                                                                                         \
-    const int c_ = (I_) % nchunks;                                                                          \
+    const int k_ = (I_) / nchunks, c_ = (I_) - k_ * nchunks;                                                \
     const size_t xo_ = size_t(c_) * xstep;                                                                  \
     _Pragma("unroll") for (int q = 0; q < XL; ++q)                                                          \
-      __builtin_amdgcn_global_load_lds(at<void>(xb, xo_ * 2, xoff[q]), (lds_ptr_t)((XBUF_) + (4 * q + wv) * 512), 16, 0, 0); \
-    _Pragma("unroll") for (int j = 0; j < 8; ++j) WR_[j] = ld_w<STREAM>(wpiece(I_, j));                     \
+      __builtin_amdgcn_global_load_lds(at<void>(xb, xo_ * 2, xoff[q]), (lds_ptr_t)((XBUF_) + (kBfWaves * q + wv) * 512), 16, 0, 0); \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j) WR_[j] = ld_w<STREAM>(wpiece(k_, c_, j));                 \
   }
   // this wave's loads of the chunk have landed (only the next chunk's, XL + 8
   // ops, and epilogue stores issued after them may be outstanding: loads
@@ -1022,12 +1049,12 @@ __device__ __forceinline__ void bf_run(const GemmArgs& p, const Tile& tl, int n,
       float* part_ = k_ == 0 ? part_first : (k_ == n - 1 ? part_last : nullptr);                            \
       if (part_ == nullptr) {                                                                               \
         Tile tk_ = tl;                                                                                      \
-        tk_.nt = tl.nt + k_;                                                                                \
-        ffn_epilogue<KIND, NB>(acc, tk_, NB, sh, out, p.n_out, wv, lr, lh, p.out_blk);                      \
+        tk_.nt = kBfNB * (tl.nt + k_) + wg;                                                                 \
+        if (tk_.nt < p.n_tiles_n) ffn_epilogue<KIND, NB>(acc, tk_, NB, sh, out, p.n_out, wq, lr, lh, p.out_blk); \
       } else {                                                                                              \
         _Pragma("unroll") for (int b = 0; b < NB; ++b)                                                      \
           _Pragma("unroll") for (int v = 0; v < 16; v += 4)                                                 \
-            *reinterpret_cast<float4*>(part_ + (((wv * kMB + b) * 4 + v / 4) * kWave + lane) * 4) =         \
+            *reinterpret_cast<float4*>(part_ + bf_part_idx(wv, b, v / 4, lane)) =                           \
                 make_float4(acc[b][v], acc[b][v + 1], acc[b][v + 2], acc[b][v + 3]);                        \
       }                                                                                                     \
       _Pragma("unroll") for (int b = 0; b < NB; ++b)                                                        \
@@ -1071,28 +1098,30 @@ __device__ __forceinline__ void bf_run(const GemmArgs& p, const Tile& tl, int n,
 
 // Stream-K over (tile, chunk) iterations; ffn_fixup_kernel finishes the split
 // tiles. XCD-aware range order: workgroups are dispatched round-robin over
-// the 8 XCDs, so range r goes to workgroup (r % 64) * 8 + r / 64; consecutive
+// the 8 XCDs, so of G ranges, range r goes to workgroup (r % (G / 8)) * 8 +
+// r / (G / 8); consecutive
 // ranges (the N tiles of one expert, which share its activation rows) then run
 // on one XCD and its L2 fetches those rows once.
 template <int KIND, bool PACKED>
-__global__ __launch_bounds__(kGemmThreads, 2) void ffn_bf16_kernel(GemmArgs p, float* __restrict__ parts) {
+__global__ __launch_bounds__(kBfThreads, 1) void ffn_bf16_kernel(GemmArgs p, float* __restrict__ parts) {
   __shared__ Sched sh;
   __shared__ __attribute__((aligned(1024))) uint16_t x0[kBfBM * kKC], x1[kBfBM * kKC], x2[kBfBM * kKC];
-  const int n_tiles = build_schedule(p, kBfBM, p.n_tiles_n, false, sh);
+  const int ntn2 = (p.n_tiles_n + kBfNB - 1) / kBfNB;
+  const int n_tiles = build_schedule<kBfThreads>(p, kBfBM, ntn2, false, sh);
   const int nchunks = p.K / kKC;
   const int64_t total = int64_t(n_tiles) * nchunks;
-  const int G = sk_grid(total);
+  const int G = sk_grid(total, kBfGrid);
   if (int(blockIdx.x) >= G) return;  // uniform
   const int rng = int(blockIdx.x % kXcds) * (G / kXcds) + int(blockIdx.x / kXcds);
   const int64_t i0 = sk_start(rng, total, G), i1 = sk_start(rng + 1, total, G);
   if (i0 >= i1) return;  // uniform
   const int t_first = int(i0 / nchunks), t_last = int((i1 - 1) / nchunks);
   for (int t = t_first; t <= t_last;) {
-    const Tile tl = decode_tile(p, kBfBM, p.n_tiles_n, sh, t);
-    build_rowmap(p, tl, kBfBM, sh);
+    const Tile tl = decode_tile(p, kBfBM, ntn2, sh, t);
+    build_rowmap<kBfThreads>(p, tl, kBfBM, sh);
     // a run: with one row tile the group's next tiles are its next N tiles
     // (same activation rows)
-    const int n = tl.mtiles == 1 ? min(t_last - t + 1, p.n_tiles_n - tl.nt) : 1;
+    const int n = tl.mtiles == 1 ? min(t_last - t + 1, ntn2 - tl.nt) : 1;
     const int64_t t0 = int64_t(t) * nchunks;
     const int it_begin = int(max<int64_t>(i0 - t0, 0));
     const int it_end = int(min<int64_t>(i1 - t0, int64_t(n) * nchunks));
@@ -1666,7 +1695,7 @@ static size_t h_bytes(const moe_ggemm_desc_t* d, int64_t rows) {
 
 static size_t parts_bytes(const moe_ggemm_desc_t* d) {
   // shared by the wide and the stream-K kernels, which run one after the other
-  const size_t sk = d->w_dt == MOE_FP8_E4M3 ? size_t(2) * kF8Grid * kF8PartFloats : size_t(2) * kSkGrid * kPartFloats;
+  const size_t sk = d->w_dt == MOE_FP8_E4M3 ? size_t(2) * kF8Grid * kF8PartFloats : size_t(2) * kBfGrid * kPartFloats;
   const size_t wide = size_t(kWideGrid) * kWidePart;
   return d->act_dt == MOE_F32 ? 0 : std::max(sk, wide) * sizeof(float);
 }
@@ -1716,7 +1745,6 @@ static moe_status_t launch_stage(const GemmArgs& p, bool f32, bool fp8, int kind
     if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
     if (!sk) return launch_status();
   }
-  const dim3 grid(kSkGrid);
   if (fp8) {
     const dim3 f8_grid(kF8Grid), f8_block(kF8Threads);
 #define MOE_F8(K, P) hipLaunchKernelGGL((ffn_fp8_kernel<K, P>), f8_grid, f8_block, 0, stream, p, parts)
@@ -1729,15 +1757,15 @@ static moe_status_t launch_stage(const GemmArgs& p, bool f32, bool fp8, int kind
     else hipLaunchKernelGGL((ffn_fp8_fixup_kernel<kDown>), fix_grid, block, 0, stream, p, parts);
     return launch_status();
   }
-#define MOE_FFN(K, P) hipLaunchKernelGGL((ffn_bf16_kernel<K, P>), grid, block, 0, stream, p, parts)
+  const dim3 bf_grid(kBfGrid), bf_block(kBfThreads);
+#define MOE_FFN(K, P) hipLaunchKernelGGL((ffn_bf16_kernel<K, P>), bf_grid, bf_block, 0, stream, p, parts)
   if (kind == kUp) { if (p.packed) MOE_FFN(kUp, true); else MOE_FFN(kUp, false); }
   else { if (p.packed) MOE_FFN(kDown, true); else MOE_FFN(kDown, false); }
 #undef MOE_FFN
   if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
-  // (the tile height must match ffn_bf16_kernel)
-  const dim3 fix_grid(kSkGrid - 1, kBM / 2 / 32);
-  if (kind == kUp) hipLaunchKernelGGL((ffn_fixup_kernel<kUp, kBM / 2>), fix_grid, block, 0, stream, p, parts);
-  else hipLaunchKernelGGL((ffn_fixup_kernel<kDown, kBM / 2>), fix_grid, block, 0, stream, p, parts);
+  const dim3 fix_grid(kBfGrid - 1, kBfNB * kBfMB);
+  if (kind == kUp) hipLaunchKernelGGL((ffn_fixup_kernel<kUp>), fix_grid, block, 0, stream, p, parts);
+  else hipLaunchKernelGGL((ffn_fixup_kernel<kDown>), fix_grid, block, 0, stream, p, parts);
   return launch_status();
 }
 

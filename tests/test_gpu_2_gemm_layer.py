@@ -93,10 +93,13 @@ def test_gemm_f32_tiny_shapes(layout):
     assert rel_l2(got, ref) <= TOL["f32"]
 
 
+# bf16 stream-K tiles are 64 rows x two N blocks; hidden 384 gives an odd
+# number (3) of down-projection N blocks, whose last tile holds one block.
 @pytest.mark.parametrize("layout", [COMPACT, PADDED])
 @pytest.mark.parametrize("ms", [[0, 1, 31, 32, 33, 127, 128, 129, 300], [5], [0, 0, 7]])
-def test_gemm_bf16_ragged(layout, ms):
-    cfg = get_config("dsv3_decode_ep8", hidden=512, inter=256)
+@pytest.mark.parametrize("hidden", [512, 384])
+def test_gemm_bf16_ragged(layout, ms, hidden):
+    cfg = get_config("dsv3_decode_ep8", hidden=hidden, inter=256)
     got, ref, _ = _gemm_case(cfg, ms, layout, seed=len(ms))
     if len(ref):
         assert rel_l2(got, ref) <= TOL["bf16"]
@@ -390,8 +393,9 @@ def test_shared_expert_only_call():
 
 
 @pytest.mark.parametrize("wname", ["bf16", "fp8"])
-def test_pack_weights_is_a_permutation_and_gemm_matches(wname):
-    cfg = get_config("dsv3_decode_ep8" if wname == "bf16" else "kimi_k2_ep8", hidden=1024, inter=512)
+@pytest.mark.parametrize("hidden", [1024, 640])  # 640: an odd number of down-projection N blocks
+def test_pack_weights_is_a_permutation_and_gemm_matches(wname, hidden):
+    cfg = get_config("dsv3_decode_ep8" if wname == "bf16" else "kimi_k2_ep8", hidden=hidden, inter=512)
     G = 5
     wd = make_expert_weights(cfg, 1, experts=range(G))
     w13, w2 = wd["w13"].cuda(), wd["w2"].cuda()
