@@ -189,6 +189,8 @@ def main(argv=None):
     ap.add_argument("--layout", choices=["compact", "padded"], default="compact")
     ap.add_argument("--gemm-policy", choices=["layer", "auto", "wide", "stream_k"], default="layer",
                     help="grouped-GEMM kernel choice (default: the layer's own, from its shape)")
+    ap.add_argument("--gather", choices=["auto", "on", "off"], default="auto",
+                    help="up projection reads its rows from the tokens (no dispatch copy); auto: decode batches")
     ap.add_argument("--xe-layout", choices=["auto", "rows", "blocked"], default="auto",
                     help="storage of the expert rows (auto: the layer's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -239,6 +241,7 @@ def main(argv=None):
                      n_src=cfg.n_src, expert_lo=cfg.expert_lo, n_local=cfg.n_local, act_dtype=act, layout=layout,
                      capacity=cap, self_range=(0, B0),
                      blocked=None if args.xe_layout == "auto" else args.xe_layout == "blocked",
+                     gather=None if args.gather == "auto" else args.gather == "on",
                      policy={"layer": None, "auto": moe.GEMM_AUTO, "wide": moe.GEMM_WIDE,
                              "stream_k": moe.GEMM_STREAM_K}[args.gemm_policy])
     share.set_weights(d["routed"], d["shared"])
@@ -314,6 +317,11 @@ def main(argv=None):
     counts = share.lay["counts"].cpu().numpy().astype(np.int64)
     row_of = share.lay["row_of"].cpu().numpy().astype(np.int64)
     model = algorithmic_model(cfg, counts, row_of, B0)
+    if share.gather:
+        # the up projection reads its rows from the tokens: no dispatch copy
+        # (its events enclosed no work)
+        model["bytes"]["dispatch"] = 0
+        per_call_us["dispatch"] = 0.0
     breakdown = {}
     for n in STEP_NAMES:
         us = per_call_us[n]
@@ -321,6 +329,8 @@ def main(argv=None):
         f = model["flops"].get(n, 0)
         breakdown[n] = {"us": round(us, 2), "GB/s": round(b / us / 1e3, 1) if us > 0 else None,
                         "TFLOP/s": round(f / us / 1e6, 1) if f and us > 0 else None}
+    if share.gather:
+        breakdown["dispatch"]["fused_into"] = "gemm_up"
     dc_bytes = model["bytes"]["dispatch"] + model["bytes"]["combine"]
     dc_us = per_call_us["dispatch"] + per_call_us["combine"]
 
@@ -364,7 +374,8 @@ def main(argv=None):
         "dtype": "bf16" if cfg.act == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": cfg.name, "layout": args.layout,
-                   "xe_layout": "blocked" if share.blocked else "rows", "global_batch": N, "tokens_per_gpu": B0,
+                   "xe_layout": "gathered" if share.gather else "blocked" if share.blocked else "rows",
+                   "global_batch": N, "tokens_per_gpu": B0,
                    "source_ranks": cfg.n_src, "hidden": cfg.hidden, "n_experts": cfg.n_experts,
                    "top_k": cfg.top_k, "local_experts": cfg.n_local, "shared_expert": cfg.shared,
                    "inter": cfg.inter, "weights": cfg.weight, "parallelism": f"ep{cfg.n_experts // cfg.n_local}"},

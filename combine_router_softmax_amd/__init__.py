@@ -58,7 +58,8 @@ class GGemmDesc(ctypes.Structure):
                 ("act_dt", ctypes.c_int), ("w_dt", ctypes.c_int), ("layout", ctypes.c_int),
                 ("n_src", ctypes.c_int), ("capacity", ctypes.c_int), ("rows", ctypes.c_int64),
                 ("stage", ctypes.c_int), ("shared", ctypes.POINTER(SharedExpert)), ("w_format", ctypes.c_int),
-                ("policy", ctypes.c_int), ("a_layout", ctypes.c_int)]
+                ("policy", ctypes.c_int), ("a_layout", ctypes.c_int), ("a_rows", ctypes.c_void_p),
+                ("a_nrows", ctypes.c_int64)]
 
 
 _P = ctypes.c_void_p
@@ -276,10 +277,12 @@ def moe_grouped_gemm(a: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, *, gr
                      stage: int = GG_FULL, y: Optional[torch.Tensor] = None,
                      ws: Optional[torch.Tensor] = None, shared: Optional[dict] = None,
                      w_format: int = W_ROWMAJOR, policy: int = 0, a_layout: int = ACT_ROWS,
-                     rows: Optional[int] = None) -> torch.Tensor:
+                     rows: Optional[int] = None, a_rows: Optional[torch.Tensor] = None) -> torch.Tensor:
     """SwiGLU FFN per expert over the rows each expert holds (see moe.h).
 
-    ``shared`` = dict(a, w13, w2, y[, s13, s2]) runs the shared expert in the same launches."""
+    ``shared`` = dict(a, w13, w2, y[, s13, s2]) runs the shared expert in the same launches.
+    ``a_rows`` (int32 [rows], e.g. the layout's row_token) gathers routed row r
+    of the up projection from row a_rows[r] of ``a``; ``rows`` is then required."""
     _dev(a, "a", (torch.float32, torch.bfloat16))
     _dev(w13, "w13")
     _dev(w2, "w2")
@@ -292,11 +295,19 @@ def moe_grouped_gemm(a: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, *, gr
     if shared is not None:
         se = shared_expert(shared["a"], shared["w13"], shared["w2"], shared.get("y"), shared.get("s13"),
                            shared.get("s2"))
-    if a_layout == ACT_BLOCKED16:
+    if a_rows is not None:
+        if rows is None:
+            raise ValueError("a gathered input needs rows (the routed row count)")
+        _dev(a_rows, "a_rows", torch.int32)
+        R = rows
+    elif a_layout == ACT_BLOCKED16:
         R = a.shape[0] // 16 * 16 if rows is None else rows
     elif rows is not None:
         R = rows
     desc = gemm_desc(G, H, I, a.dtype, w13.dtype, layout, n_src, capacity, R, stage, se, w_format, policy, a_layout)
+    if a_rows is not None:
+        desc.a_rows = a_rows.data_ptr()
+        desc.a_nrows = a.shape[0]
     wsb = moe_grouped_gemm_workspace(desc)
     if wsb == 0:
         raise MoeError("moe_grouped_gemm: invalid descriptor")

@@ -93,6 +93,8 @@ struct GemmArgs {
   int wide_min_tiles;         // ... if the wide groups make at least this many wide tiles
   int a_blk, sh_a_blk;        // routed / shared activations in the 16-row blocked layout
   int out_blk;                // outputs (routed and shared) in the 16-row blocked layout
+  const int32_t* a_rows;      // routed input row r is row a_rows[r] of a (nullptr: row r)
+  int a_nrows;                // rows of a when gathering
 };
 
 // 16-row blocked activation layout: element (r, c) of an [R, K] matrix sits
@@ -107,6 +109,8 @@ __device__ __forceinline__ size_t act_off(int64_t r, int c, int K, bool blk) {
   return blk ? blk_row_base(r, K) + size_t(c >> 5) * 512 + (c & 31) : size_t(r) * K + c;
 }
 
+constexpr int kGatherRows = 128;  // tile rows of the kernels that gather (bf16 64, fp8 96)
+
 struct Sched {
   int tile_start[kMaxGroups + 2];
   int m[kMaxGroups + 1];
@@ -115,6 +119,7 @@ struct Sched {
     int rowmap[256];
     int tmp[kMaxGemmThreads];  // scan scratch: every scan ends before a rowmap is written
   };
+  int arow[kGatherRows];       // gathering: the input row of each tile row (decode-shaped kernels)
   int cur_seg_group;
   int wide_tiles;
 };
@@ -243,12 +248,20 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& p, int bm, int ntn, 
 
 // Physical row of each of the tile's rows (-1 past the group's rows).
 template <int NT = kGemmThreads>
-__device__ __forceinline__ void build_rowmap(const GemmArgs& p, const Tile& tl, int bm, Sched& sh) {
+__device__ __forceinline__ void build_rowmap(const GemmArgs& p, const Tile& tl, int bm, Sched& sh,
+                                             bool input_rows = false) {
   const int tid = threadIdx.x;
+  // gathering (kernels that read their input through sh.arow): the input row
+  // of each present row, clamped into a's rows
+  const bool gat = input_rows && p.a_rows != nullptr && !tl.shared && bm <= kGatherRows;
+  auto put = [&](int phys) {
+    sh.rowmap[tid] = phys;
+    if (gat) sh.arow[tid] = phys >= 0 ? min(max(p.a_rows[phys], 0), p.a_nrows - 1) : -1;
+  };
   if (tl.shared || p.layout == MOE_LAYOUT_COMPACT) {
     if (tid < bm) {
       const int64_t base = tl.shared ? 0 : min<int64_t>(max<int64_t>(p.group_off[tl.g], 0), p.rows);
-      sh.rowmap[tid] = tid < tl.nrows ? int(base + tl.r0 + tid) : -1;
+      put(tid < tl.nrows ? int(base + tl.r0 + tid) : -1);
     }
     __syncthreads();
     return;
@@ -276,7 +289,7 @@ __device__ __forceinline__ void build_rowmap(const GemmArgs& p, const Tile& tl, 
       }
       phys = (tl.g * p.S + lo) * p.C + (li - sh.seg[lo]);
     }
-    sh.rowmap[tid] = phys;
+    put(phys);
   }
   __syncthreads();
 }
@@ -990,16 +1003,19 @@ __device__ __forceinline__ void bf_run(const GemmArgs& p, const Tile& tl, int n,
   const bool ablk = pick(tl.shared, p.sh_a_blk, p.a_blk);
   const size_t xstep = ablk ? size_t(4) * 512 : size_t(kKC);  // elements from one chunk of a row to the next
   // per-lane byte offsets from the tile's first row (a tile's rows lie in one
-  // expert's region, which the host keeps below 2^31 elements)
-  const int phys0 = sh.rowmap[0];
-  const size_t xbase = ablk ? blk_row_base(phys0, p.K) : size_t(phys0) * p.K;
+  // expert's region, which the host keeps below 2^31 elements); gathered rows
+  // from a's start (the host keeps a below 2^32 bytes)
+  const bool gat = p.a_rows != nullptr && !tl.shared;
+  const int* amap = gat ? sh.arow : sh.rowmap;
+  const int phys0 = amap[0];
+  const size_t xbase = gat ? 0 : ablk ? blk_row_base(phys0, p.K) : size_t(phys0) * p.K;
   const gptr<char> xb = uniform_ptr(reinterpret_cast<const char*>(A + xbase));
   uint32_t xoff[XL];
 #pragma unroll
   for (int q = 0; q < XL; ++q) {
     const int r = 4 * (kBfWaves * q + wv) + (lane >> 4);
     const int c = (lane & 15) ^ (r & 15);  // column piece this lane's LDS slot holds
-    const int phys = sh.rowmap[r];
+    const int phys = amap[r];
     const int pr = phys >= 0 ? phys : phys0;  // rows past the tile feed only discarded columns
     xoff[q] = uint32_t((ablk ? blk_row_base(pr, p.K) + size_t(c >> 2) * 512 + (c & 3) * 8 : size_t(pr) * p.K + c * 8) -
                        xbase) * 2u;
@@ -1118,7 +1134,7 @@ __global__ __launch_bounds__(kBfThreads, 1) void ffn_bf16_kernel(GemmArgs p, flo
   const int t_first = int(i0 / nchunks), t_last = int((i1 - 1) / nchunks);
   for (int t = t_first; t <= t_last;) {
     const Tile tl = decode_tile(p, kBfBM, ntn2, sh, t);
-    build_rowmap<kBfThreads>(p, tl, kBfBM, sh);
+    build_rowmap<kBfThreads>(p, tl, kBfBM, sh, true);
     // a run: with one row tile the group's next tiles are its next N tiles
     // (same activation rows)
     const int n = tl.mtiles == 1 ? min(t_last - t + 1, ntn2 - tl.nt) : 1;
@@ -1259,16 +1275,19 @@ __device__ __forceinline__ void f8_run(const GemmArgs& p, const Tile& tl, int n,
   const bool ablk = pick(tl.shared, p.sh_a_blk, p.a_blk);
   const size_t xstep = ablk ? size_t(4) * 512 : size_t(kKC);  // elements from one chunk of a row to the next
   // per-lane byte offsets from the tile's first row (a tile's rows lie in one
-  // expert's region, which the host keeps below 2^31 elements)
-  const int phys0 = sh.rowmap[0];
-  const size_t xbase = ablk ? blk_row_base(phys0, p.K) : size_t(phys0) * p.K;
+  // expert's region, which the host keeps below 2^31 elements); gathered rows
+  // from a's start (the host keeps a below 2^32 bytes)
+  const bool gat = p.a_rows != nullptr && !tl.shared;
+  const int* amap = gat ? sh.arow : sh.rowmap;
+  const int phys0 = amap[0];
+  const size_t xbase = gat ? 0 : ablk ? blk_row_base(phys0, p.K) : size_t(phys0) * p.K;
   const gptr<char> xb = uniform_ptr(reinterpret_cast<const char*>(A + xbase));
   uint32_t xoff[XL];
 #pragma unroll
   for (int q = 0; q < XL; ++q) {
     const int r = 4 * (kF8Waves * q + wv) + (lane >> 4);
     const int c = (lane & 15) ^ (r & 15);  // column piece this lane's LDS slot holds
-    const int phys = r < NB * 32 ? sh.rowmap[r] : -1;
+    const int phys = r < NB * 32 ? amap[r] : -1;
     const int pr = phys >= 0 ? phys : phys0;  // rows past the tile feed only discarded columns
     xoff[q] = uint32_t((ablk ? blk_row_base(pr, p.K) + size_t(c >> 2) * 512 + (c & 3) * 8 : size_t(pr) * p.K + c * 8) -
                        xbase) * 2u;
@@ -1488,7 +1507,7 @@ __global__ __launch_bounds__(kF8Threads, 1) void ffn_fp8_kernel(GemmArgs p, floa
   const int t_first = int(i0 / nchunks), t_last = int((i1 - 1) / nchunks);
   for (int t = t_first; t <= t_last;) {
     const Tile tl = decode_tile(p, kF8BM, ntn4, sh, t);
-    build_rowmap<kF8Threads>(p, tl, kF8BM, sh);
+    build_rowmap<kF8Threads>(p, tl, kF8BM, sh, true);
     const int n = tl.mtiles == 1 ? min(t_last - t + 1, ntn4 - tl.nt) : 1;
     const int64_t t0 = int64_t(t) * nchunks;
     const int it_begin = int(max<int64_t>(i0 - t0, 0));
@@ -1668,6 +1687,7 @@ static bool ggemm_desc_ok(const moe_ggemm_desc_t* d) {
   if (d->w_format != MOE_W_ROWMAJOR && d->w_format != MOE_W_PACKED) return false;
   if (d->policy != MOE_GEMM_AUTO && d->policy != MOE_GEMM_WIDE && d->policy != MOE_GEMM_STREAM_K) return false;
   if (d->a_layout != MOE_ACT_ROWS && d->a_layout != MOE_ACT_BLOCKED16) return false;
+  if (d->a_rows && d->a_nrows < 1) return false;
   return true;
 }
 
@@ -1682,6 +1702,10 @@ static bool ggemm_desc_supported(const moe_ggemm_desc_t* d) {
   if (d->shared && d->shared->rows >= (1 << 30)) return false;
   if (f32 && d->w_format == MOE_W_PACKED) return false;
   if (f32 && d->a_layout != MOE_ACT_ROWS) return false;
+  // gathering: the decode-shaped kernels, row-major bf16 rows, 32-bit byte offsets
+  if (d->a_rows && (f32 || d->a_layout != MOE_ACT_ROWS || d->policy == MOE_GEMM_WIDE ||
+                    d->a_nrows > (int64_t(1) << 32) / (int64_t(d->hidden) * 2)))
+    return false;
   return true;
 }
 
@@ -1814,7 +1838,7 @@ MOE_API moe_status_t moe_grouped_gemm(const moe_ggemm_desc_t* d, const void* a, 
   p.packed = d->w_format == MOE_W_PACKED;
   // the wide-tile kernel: bf16 weights, 256-row output blocks of W2 and 128-column blocks of h
   const bool wide_ok = !f32 && !fp8 && d->hidden % 256 == 0 && d->inter % 128 == 0 &&
-                       d->policy != MOE_GEMM_STREAM_K;
+                       d->policy != MOE_GEMM_STREAM_K && !d->a_rows;
   const bool force = d->policy == MOE_GEMM_WIDE;
   p.wide_min = wide_ok ? (force ? 1 : kWideMinRows) : kNoWide;
   const bool sk = !(wide_ok && force);  // forced wide leaves the stream-K kernel nothing
@@ -1824,9 +1848,13 @@ MOE_API moe_status_t moe_grouped_gemm(const moe_ggemm_desc_t* d, const void* a, 
   const bool h_blk = wide_ok;
   p.wide_min_tiles = force ? 0 : kWideMinTiles;
   p.sh_a_blk = 0;
+  p.a_rows = nullptr;
+  p.a_nrows = 0;
   moe_status_t st = MOE_OK;
   if (up) {
     p.a = a;
+    p.a_rows = d->a_rows;
+    p.a_nrows = d->a_rows ? int(d->a_nrows) : 0;
     p.w = w13;
     p.s = s13;
     p.out = h;
@@ -1846,6 +1874,7 @@ MOE_API moe_status_t moe_grouped_gemm(const moe_ggemm_desc_t* d, const void* a, 
   }
   if (down) {
     p.a = h;
+    p.a_rows = nullptr;
     p.w = w2;
     p.s = s2;
     p.out = y;

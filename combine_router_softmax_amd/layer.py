@@ -24,7 +24,7 @@ class MoEShare:
     def __init__(self, *, n_tokens: int, hidden: int, inter: int, n_experts: int, top_k: int, n_src: int,
                  expert_lo: int, n_local: int, act_dtype: torch.dtype, layout: int = COMPACT,
                  capacity: Optional[int] = None, self_range=(0, 0), device="cuda",
-                 blocked: Optional[bool] = None, policy: Optional[int] = None):
+                 blocked: Optional[bool] = None, policy: Optional[int] = None, gather: Optional[bool] = None):
         self.N, self.H, self.I, self.E, self.K = n_tokens, hidden, inter, n_experts, top_k
         self.S, self.lo, self.L = n_src, expert_lo, n_local
         self.layout = layout
@@ -52,6 +52,13 @@ class MoEShare:
         # rule picks for them) without an empty stream-K launch; decode-sized
         # batches take the stream-K kernel without an empty wide launch
         self.policy = (GEMM_WIDE if many_rows else GEMM_STREAM_K) if policy is None else policy
+        # the decode-shaped kernels can read the routed rows straight from the
+        # tokens (row_token of the layout), which leaves out the dispatch copy;
+        # on by default where they run every group
+        can_gather = act_dtype == torch.bfloat16 and not self.blocked and self.policy != GEMM_WIDE
+        self.gather = (can_gather and self.policy == GEMM_STREAM_K) if gather is None else bool(gather)
+        if self.gather and not can_gather:
+            raise ValueError("gathered rows need bf16 activations, row-major rows and a non-wide policy")
         d = self.dev
         self.topk_idx = torch.empty((n_tokens, top_k), dtype=torch.int32, device=d)
         self.topk_w = torch.empty((n_tokens, top_k), dtype=torch.float32, device=d)
@@ -114,15 +121,22 @@ class MoEShare:
         else:
             moe_dispatch(x, self.lay["row_of"], self.K, self.R, self.xe)
 
-    def gemm(self, stage=GG_FULL, x=None):
-        """Routed experts; with ``x`` the shared expert runs in the same launches."""
+    def gemm(self, stage=GG_FULL, x=None, src=None):
+        """Routed experts; with ``x`` the shared expert runs in the same launches.
+        Gathering, the up projection reads its rows from ``src`` (the tokens)."""
         w = self.w
-        a = self.xe if self.blocked else self.xe[: self.R]
+        extra = {}
+        if self.gather:
+            if src is None:
+                raise ValueError("gathered rows need the tokens (src)")
+            a, extra["a_rows"] = src, self.lay["row_token"]
+        else:
+            a = self.xe if self.blocked else self.xe[: self.R]
         moe_grouped_gemm(a, w["w13"], w["w2"], group_off=self.lay["expert_off"],
                          counts=self.lay["counts"], s13=w.get("s13"), s2=w.get("s2"), layout=self.layout,
                          n_src=self.S, capacity=self.capacity, stage=stage, y=self.ye[: self.R], ws=self.ws,
                          shared=None if x is None else self._shared_arg(x), w_format=self.w_format,
-                         a_layout=self.a_layout, rows=self.R, policy=self.policy)
+                         a_layout=self.a_layout, rows=self.R, policy=self.policy, **extra)
 
     def shared_gemm(self, x, stage=GG_FULL):
         if self.sw is None or self.self_hi <= self.self_lo:
@@ -141,7 +155,8 @@ class MoEShare:
         """One full pass. ``events`` maps step names to (start, end) CUDA events
         recorded around each call on the current stream. With ``fused_shared``
         the shared expert runs inside the routed grouped-GEMM launches; otherwise
-        as calls of its own."""
+        as calls of its own. Gathering, the dispatch copy is left out (its
+        events, if any, enclose no work)."""
         def run(name, fn):
             if events is not None and name in events:
                 events[name][0].record()
@@ -152,10 +167,10 @@ class MoEShare:
 
         run("route", lambda: self.route(logits))
         run("layout", lambda: self.layout_step(src_offsets))
-        run("dispatch", lambda: self.dispatch(x))
+        run("dispatch", (lambda: None) if self.gather else (lambda: self.dispatch(x)))
         xs = x if fused_shared else None
-        run("gemm_up", lambda: self.gemm(GG_UP, xs))
-        run("gemm_down", lambda: self.gemm(GG_DOWN, xs))
+        run("gemm_up", lambda: self.gemm(GG_UP, xs, src=x))
+        run("gemm_down", lambda: self.gemm(GG_DOWN, xs, src=x))
         if not fused_shared:
             run("shared_up", lambda: self.shared_gemm(x, GG_UP))
             run("shared_down", lambda: self.shared_gemm(x, GG_DOWN))

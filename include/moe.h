@@ -238,6 +238,15 @@ typedef struct {
   moe_weight_format_t w_format;      /* layout of w13/w2 (and of the shared expert's) */
   moe_gemm_policy_t policy;          /* kernel choice per group; MOE_GEMM_AUTO unless tuning or testing */
   moe_act_layout_t a_layout;         /* storage of the routed rows a (bf16 only for BLOCKED16) */
+  /* Gather (NULL = off): routed row r of the up projection's input is row
+   * a_rows[r] of a, an [a_nrows, H] row-major bf16 matrix (e.g. the tokens x,
+   * with a_rows = row_token from moe_dispatch_layout), so no dispatched copy is
+   * needed. Indices are clamped into [0, a_nrows). Needs bf16 activations,
+   * MOE_ACT_ROWS, a policy other than MOE_GEMM_WIDE (the decode-shaped kernels
+   * run every group) and a_nrows * H * 2 < 2^32. The shared expert, h and y
+   * keep their own rows. */
+  const int32_t* a_rows;             /* device [rows], or NULL */
+  int64_t a_nrows;
 } moe_ggemm_desc_t;
 
 /* Bytes of scratch moe_grouped_gemm needs (the intermediates h [R, I] and, with

@@ -139,6 +139,20 @@ def test_grouped_gemm_workspace_and_errors(lib):
     assert f(ctypes.byref(_gd(rows=0)), *ptrs, FAKE, ws, None) == OK   # nothing to do
 
 
+def test_grouped_gemm_gather_validation(lib):
+    f = lib.moe_grouped_gemm
+    ws = lib.moe_grouped_gemm_workspace(ctypes.byref(_gd()))
+    ptrs = [FAKE] * 8
+    assert f(ctypes.byref(_gd(a_rows=FAKE.value, a_nrows=0)), *ptrs, FAKE, ws, None) == INVALID   # no input rows
+    wsf = lib.moe_grouped_gemm_workspace(ctypes.byref(_gd(act_dt=0, w_dt=0)))
+    assert f(ctypes.byref(_gd(act_dt=0, w_dt=0, a_rows=FAKE.value, a_nrows=10)), *ptrs, FAKE, wsf,
+             None) == UNSUPPORTED                                                                   # f32
+    assert f(ctypes.byref(_gd(a_rows=FAKE.value, a_nrows=10, policy=1)), *ptrs, FAKE, ws, None) == UNSUPPORTED
+    assert f(ctypes.byref(_gd(a_rows=FAKE.value, a_nrows=10, a_layout=1)), *ptrs, FAKE, ws, None) == UNSUPPORTED
+    assert f(ctypes.byref(_gd(a_rows=FAKE.value, a_nrows=(1 << 23) + 1)), *ptrs, FAKE, ws, None) == UNSUPPORTED  # > 4 GiB
+    assert f(ctypes.byref(_gd(rows=0, a_rows=FAKE.value, a_nrows=10)), *ptrs, FAKE, ws, None) == OK
+
+
 def test_grouped_gemm_shared_expert_validation(lib):
     from combine_router_softmax_amd import SharedExpert
     f = lib.moe_grouped_gemm

@@ -246,6 +246,51 @@ def test_layer_tiny(seed, layout, shared):
     assert rel_l2(got[touched], ref["out"][touched]) <= TOL["f32"]
 
 
+# The up projection reads its rows straight from the tokens (a_rows = the
+# layout's row_token) instead of a dispatched copy: the same arithmetic, so the
+# same bits as through moe_dispatch, for the bf16 and fp8 kernels, both layouts,
+# groups of several row tiles, an empty source, a shared expert in the launch,
+# and AUTO (gathering runs every group on the decode-shaped kernels).
+@pytest.mark.parametrize("wname", ["bf16", "fp8"])
+@pytest.mark.parametrize("layout", [COMPACT, PADDED])
+def test_gemm_gather_matches_dispatched(wname, layout):
+    cfg = get_config("dsv3_decode_ep8" if wname == "bf16" else "kimi_k2_ep8", hidden=384, inter=256)
+    rng = np.random.default_rng(21)
+    E, L, K = 32, 12, 4
+    off = np.array([0, 60, 60, 200, 300], dtype=np.int32)  # source 1 is empty
+    S, N, H = len(off) - 1, int(off[-1]), cfg.hidden
+    idx = np.stack([rng.choice(E, K, replace=False) for _ in range(N)]).astype(np.int32)
+    hot = np.arange(N) < 150  # expert 0 holds 150 rows: several row tiles
+    idx[hot] = np.stack([np.concatenate([[0], 1 + rng.choice(E - 1, K - 1, replace=False)]) for _ in range(150)])
+    cap = N * K if layout == COMPACT else int(np.diff(off).max())
+    lay = moe.moe_dispatch_layout(torch.from_numpy(idx).cuda(), torch.from_numpy(off).cuda(), E, 0, L, layout, cap)
+    R = lay["rows"]
+    x = torch.from_numpy(rng.standard_normal((N, H)).astype(np.float32)).to(torch.bfloat16).cuda()
+    xe = moe.moe_dispatch(x, lay["row_of"], K, R)
+    wd = make_expert_weights(cfg, 5, experts=range(L))
+    dw = _dev_weights(wd)
+    sw = _dev_weights(make_expert_weights(cfg, 6, shared=True))
+    kw = dict(group_off=lay["expert_off"], counts=lay["counts"], s13=dw.get("s13"), s2=dw.get("s2"), layout=layout,
+              n_src=S, capacity=cap, rows=R)
+    outs = []
+    for a, extra in ((xe, dict(policy=moe.GEMM_STREAM_K)), (x, dict(policy=moe.GEMM_AUTO, a_rows=lay["row_token"]))):
+        y = torch.full((R, H), 3.0, dtype=torch.bfloat16, device="cuda")
+        ys = torch.zeros((60, H), dtype=torch.bfloat16, device="cuda")
+        shared = {"a": x[:60], "w13": sw["w13"], "w2": sw["w2"], "y": ys, "s13": sw.get("s13"), "s2": sw.get("s2")}
+        moe.moe_grouped_gemm(a, dw["w13"], dw["w2"], y=y, shared=shared, **kw, **extra)
+        outs.append((y, ys))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
+    assert torch.equal(outs[0][1].view(torch.int16), outs[1][1].view(torch.int16))
+    # the oracle's own layout and dispatch (the GPU layout is the same: it is exact)
+    lo = dispatch_layout(idx, off, 0, L, layout, cap)
+    np.testing.assert_array_equal(lay["row_of"].cpu().numpy().reshape(-1), np.asarray(lo["row_of"]).reshape(-1))
+    rows = np.concatenate([group_rows(lo, g) for g in range(L)])
+    assert len(rows) == int(np.sum(lo["counts"])) and int(np.sum(lo["counts"][0])) >= 150
+    ref = grouped_ffn(dispatch(f64(x), lo["row_of"], K, lo["rows"]), lo, *_oracle_weights(wd))
+    assert rel_l2(f64(outs[1][0])[rows], ref[rows]) <= (1e-2 if wname == "fp8" else TOL["bf16"])
+
+
 def test_layer_identity_property_bf16():
     # combine(dispatch(x)) with identity experts: out = (sum of local weights) * x.
     cfg = get_config("dsv3_decode_ep8")
