@@ -109,7 +109,7 @@ __device__ __forceinline__ size_t act_off(int64_t r, int c, int K, bool blk) {
   return blk ? blk_row_base(r, K) + size_t(c >> 5) * 512 + (c & 31) : size_t(r) * K + c;
 }
 
-constexpr int kGatherRows = 128;  // tile rows of the kernels that gather (bf16 64, fp8 96)
+constexpr int kGatherRows = 256;  // tile rows of the kernels that gather (bf16 64, fp8 96, wide 256)
 
 struct Sched {
   int tile_start[kMaxGroups + 2];
@@ -119,7 +119,7 @@ struct Sched {
     int rowmap[256];
     int tmp[kMaxGemmThreads];  // scan scratch: every scan ends before a rowmap is written
   };
-  int arow[kGatherRows];       // gathering: the input row of each tile row (decode-shaped kernels)
+  int arow[kGatherRows];       // gathering: the input row of each tile row
   int cur_seg_group;
   int wide_tiles;
 };
@@ -662,11 +662,13 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& p, const Tile& tl, con
   const bool ablk = pick(tl.shared, p.sh_a_blk, p.a_blk);
   const size_t xstep = ablk ? 512 : kWK;  // elements from one stage of a row to the next
   const uint16_t* xg[XL];
-  const int phys0 = sh.rowmap[0];
+  const bool gat = p.a_rows != nullptr && !tl.shared;  // input rows gathered from a
+  const int* amap = gat ? sh.arow : sh.rowmap;
+  const int phys0 = amap[0];
 #pragma unroll
   for (int q = 0; q < XL; ++q) {
     const int row = kWRowsPerLoad * (4 * q + wv) + lrow;
-    const int phys = row < NB * 32 ? sh.rowmap[row] : -1;
+    const int phys = row < NB * 32 ? amap[row] : -1;
     const int pr = phys >= 0 ? phys : phys0;
     // (columns 8 cg .. 8 cg + 7 of stage 0 lie inside the first 32-column block)
     xg[q] = A + (ablk ? blk_row_base(pr, p.K) : size_t(pr) * p.K) + col_of(row) * 8;
@@ -865,7 +867,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_wide_kernel(GemmArgs p, f
   const int slot = int(blockIdx.x % kXcds) * (kWideGrid / kXcds) + int(blockIdx.x / kXcds);
   auto run = [&](int t, int c_begin, int c_end, float* part) __attribute__((always_inline)) {
     const Tile tl = decode_tile<true>(p, kWM, ntn, sh, t);
-    build_rowmap(p, tl, kWM, sh);
+    build_rowmap(p, tl, kWM, sh, true);
     const int sb = c_begin * SPC, se = c_end * SPC;
     switch ((tl.nrows + 31) / 32) {
       case 1: wide_tile<KIND, PACKED, 1>(p, tl, sh, L, sb, se, part); break;
@@ -1702,8 +1704,8 @@ static bool ggemm_desc_supported(const moe_ggemm_desc_t* d) {
   if (d->shared && d->shared->rows >= (1 << 30)) return false;
   if (f32 && d->w_format == MOE_W_PACKED) return false;
   if (f32 && d->a_layout != MOE_ACT_ROWS) return false;
-  // gathering: the decode-shaped kernels, row-major bf16 rows, 32-bit byte offsets
-  if (d->a_rows && (f32 || d->a_layout != MOE_ACT_ROWS || d->policy == MOE_GEMM_WIDE ||
+  // gathering: row-major bf16 rows, 32-bit byte offsets (decode-shaped kernels)
+  if (d->a_rows && (f32 || d->a_layout != MOE_ACT_ROWS ||
                     d->a_nrows > (int64_t(1) << 32) / (int64_t(d->hidden) * 2)))
     return false;
   return true;
@@ -1838,7 +1840,7 @@ MOE_API moe_status_t moe_grouped_gemm(const moe_ggemm_desc_t* d, const void* a, 
   p.packed = d->w_format == MOE_W_PACKED;
   // the wide-tile kernel: bf16 weights, 256-row output blocks of W2 and 128-column blocks of h
   const bool wide_ok = !f32 && !fp8 && d->hidden % 256 == 0 && d->inter % 128 == 0 &&
-                       d->policy != MOE_GEMM_STREAM_K && !d->a_rows;
+                       d->policy != MOE_GEMM_STREAM_K;
   const bool force = d->policy == MOE_GEMM_WIDE;
   p.wide_min = wide_ok ? (force ? 1 : kWideMinRows) : kNoWide;
   const bool sk = !(wide_ok && force);  // forced wide leaves the stream-K kernel nothing

@@ -52,13 +52,12 @@ class MoEShare:
         # rule picks for them) without an empty stream-K launch; decode-sized
         # batches take the stream-K kernel without an empty wide launch
         self.policy = (GEMM_WIDE if many_rows else GEMM_STREAM_K) if policy is None else policy
-        # the decode-shaped kernels can read the routed rows straight from the
-        # tokens (row_token of the layout), which leaves out the dispatch copy;
-        # on by default where they run every group
-        can_gather = act_dtype == torch.bfloat16 and not self.blocked and self.policy != GEMM_WIDE
-        self.gather = (can_gather and self.policy == GEMM_STREAM_K) if gather is None else bool(gather)
+        # the bf16 GEMM kernels can read the routed rows straight from the
+        # tokens (row_token of the layout), which leaves out the dispatch copy
+        can_gather = act_dtype == torch.bfloat16 and not self.blocked and n_tokens * hidden * 2 <= 1 << 32
+        self.gather = can_gather if gather is None else bool(gather)
         if self.gather and not can_gather:
-            raise ValueError("gathered rows need bf16 activations, row-major rows and a non-wide policy")
+            raise ValueError("gathered rows need bf16 activations, row-major rows and tokens below 4 GiB")
         d = self.dev
         self.topk_idx = torch.empty((n_tokens, top_k), dtype=torch.int32, device=d)
         self.topk_w = torch.empty((n_tokens, top_k), dtype=torch.float32, device=d)

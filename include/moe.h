@@ -242,9 +242,8 @@ typedef struct {
    * a_rows[r] of a, an [a_nrows, H] row-major bf16 matrix (e.g. the tokens x,
    * with a_rows = row_token from moe_dispatch_layout), so no dispatched copy is
    * needed. Indices are clamped into [0, a_nrows). Needs bf16 activations,
-   * MOE_ACT_ROWS, a policy other than MOE_GEMM_WIDE (the decode-shaped kernels
-   * run every group) and a_nrows * H * 2 < 2^32. The shared expert, h and y
-   * keep their own rows. */
+   * MOE_ACT_ROWS and a_nrows * H * 2 <= 2^32. The shared expert, h and y keep
+   * their own rows. */
   const int32_t* a_rows;             /* device [rows], or NULL */
   int64_t a_nrows;
 } moe_ggemm_desc_t;

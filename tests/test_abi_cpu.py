@@ -147,7 +147,6 @@ def test_grouped_gemm_gather_validation(lib):
     wsf = lib.moe_grouped_gemm_workspace(ctypes.byref(_gd(act_dt=0, w_dt=0)))
     assert f(ctypes.byref(_gd(act_dt=0, w_dt=0, a_rows=FAKE.value, a_nrows=10)), *ptrs, FAKE, wsf,
              None) == UNSUPPORTED                                                                   # f32
-    assert f(ctypes.byref(_gd(a_rows=FAKE.value, a_nrows=10, policy=1)), *ptrs, FAKE, ws, None) == UNSUPPORTED
     assert f(ctypes.byref(_gd(a_rows=FAKE.value, a_nrows=10, a_layout=1)), *ptrs, FAKE, ws, None) == UNSUPPORTED
     assert f(ctypes.byref(_gd(a_rows=FAKE.value, a_nrows=(1 << 23) + 1)), *ptrs, FAKE, ws, None) == UNSUPPORTED  # > 4 GiB
     assert f(ctypes.byref(_gd(rows=0, a_rows=FAKE.value, a_nrows=10)), *ptrs, FAKE, ws, None) == OK

@@ -248,13 +248,15 @@ def test_layer_tiny(seed, layout, shared):
 
 # The up projection reads its rows straight from the tokens (a_rows = the
 # layout's row_token) instead of a dispatched copy: the same arithmetic, so the
-# same bits as through moe_dispatch, for the bf16 and fp8 kernels, both layouts,
-# groups of several row tiles, an empty source, a shared expert in the launch,
-# and AUTO (gathering runs every group on the decode-shaped kernels).
-@pytest.mark.parametrize("wname", ["bf16", "fp8"])
+# same bits as through moe_dispatch, for the bf16 stream-K, fp8 and wide-tile
+# kernels, both layouts, groups of several row tiles, an empty source and a
+# shared expert in the launch.
+@pytest.mark.parametrize("wname", ["bf16", "fp8", "bf16_wide"])
 @pytest.mark.parametrize("layout", [COMPACT, PADDED])
 def test_gemm_gather_matches_dispatched(wname, layout):
-    cfg = get_config("dsv3_decode_ep8" if wname == "bf16" else "kimi_k2_ep8", hidden=384, inter=256)
+    wide = wname == "bf16_wide"
+    cfg = get_config("kimi_k2_ep8" if wname == "fp8" else "dsv3_decode_ep8", hidden=512 if wide else 384, inter=256)
+    pol = moe.GEMM_WIDE if wide else moe.GEMM_STREAM_K
     rng = np.random.default_rng(21)
     E, L, K = 32, 12, 4
     off = np.array([0, 60, 60, 200, 300], dtype=np.int32)  # source 1 is empty
@@ -273,7 +275,7 @@ def test_gemm_gather_matches_dispatched(wname, layout):
     kw = dict(group_off=lay["expert_off"], counts=lay["counts"], s13=dw.get("s13"), s2=dw.get("s2"), layout=layout,
               n_src=S, capacity=cap, rows=R)
     outs = []
-    for a, extra in ((xe, dict(policy=moe.GEMM_STREAM_K)), (x, dict(policy=moe.GEMM_AUTO, a_rows=lay["row_token"]))):
+    for a, extra in ((xe, dict(policy=pol)), (x, dict(policy=pol, a_rows=lay["row_token"]))):
         y = torch.full((R, H), 3.0, dtype=torch.bfloat16, device="cuda")
         ys = torch.zeros((60, H), dtype=torch.bfloat16, device="cuda")
         shared = {"a": x[:60], "w13": sw["w13"], "w2": sw["w2"], "y": ys, "s13": sw.get("s13"), "s2": sw.get("s2")}
