@@ -299,6 +299,8 @@ def moe_grouped_gemm(a: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, *, gr
         if rows is None:
             raise ValueError("a gathered input needs rows (the routed row count)")
         _dev(a_rows, "a_rows", torch.int32)
+        if a_rows.numel() < rows:
+            raise ValueError(f"a_rows holds {a_rows.numel()} entries, fewer than rows={rows}")
         R = rows
     elif a_layout == ACT_BLOCKED16:
         R = a.shape[0] // 16 * 16 if rows is None else rows

@@ -62,8 +62,8 @@ class MoEShare:
         self.topk_idx = torch.empty((n_tokens, top_k), dtype=torch.int32, device=d)
         self.topk_w = torch.empty((n_tokens, top_k), dtype=torch.float32, device=d)
         self.lay = None
-        self.xe = torch.empty((max(blocked_rows(self.R) if self.blocked else self.R, 1), hidden), dtype=act_dtype,
-                              device=d)
+        # the expert-grouped copy of the rows; gathering layers need none (made on first dispatch)
+        self.xe = None if self.gather else self._new_xe()
         self.ye = torch.empty((max(self.R, 1), hidden), dtype=act_dtype, device=d)
         B0 = self.self_hi - self.self_lo
         self.ys = torch.empty((max(B0, 1), hidden), dtype=act_dtype, device=d)
@@ -73,6 +73,10 @@ class MoEShare:
         self.w_format = W_ROWMAJOR
         self.ws = None
         self.sws = None
+
+    def _new_xe(self):
+        return torch.empty((max(blocked_rows(self.R) if self.blocked else self.R, 1), self.H), dtype=self.act_dtype,
+                           device=self.dev)
 
     # weights: dict with w13 [G,2I,H], w2 [G,H,I], optional s13/s2 (host or device tensors)
     def set_weights(self, routed: dict, shared: Optional[dict] = None, pack: bool = True):
@@ -115,6 +119,8 @@ class MoEShare:
                                        self.capacity, out=self.lay)
 
     def dispatch(self, x):
+        if self.xe is None:
+            self.xe = self._new_xe()
         if self.blocked:
             moe_dispatch_blocked(x, self.lay["row_of"], self.K, self.R, self.xe)
         else:
