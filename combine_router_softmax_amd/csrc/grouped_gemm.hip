@@ -357,7 +357,7 @@ __device__ __forceinline__ bf16x8_t fp8x8_dequant(uint32_t w0, uint32_t w1, floa
 // work, fewer ranges are used (at least kSkMinChunks chunks each), so the
 // partial sums stay small next to the weights streamed.
 constexpr int kXcds = 8;                              // accelerator complex dies of MI355X
-constexpr int kPartFloats = 4 * kMB * 16 * kWave;     // a bf16 workgroup's accumulators (64 KiB)
+constexpr int kPartFloats = 4 * kMB * 16 * kWave;     // a bf16 workgroup's accumulators (64 KiB: 8 waves x 2 blocks)
 constexpr int kSkMinChunks = 8;
 
 // bf16 decode kernel (ffn_bf16_kernel): tiles of 64 activation rows x two N
@@ -470,9 +470,9 @@ __device__ __forceinline__ void sum_partials(f32x16_t (&acc)[NA], int w_lo, int 
 // Finishes the tiles of ffn_bf16_kernel cut by a stream-K range boundary:
 // block (j, m * kBfMB + b) looks at the boundary between workgroups j and
 // j+1; the first boundary inside a tile sums, for the tile's N block m and
-// 32-row block b, its partials in workgroup order (one wave per 32 rows of the
-// block: the main kernel's waves 4 m .. 4 m + 3) and runs that block's
-// epilogue.
+// 32-row block b, its partials in workgroup order (one wave per 32 weight rows
+// of the N block, i.e. the partials of the main kernel's waves 4 m .. 4 m + 3)
+// and runs that block's epilogue.
 template <int KIND>
 __global__ __launch_bounds__(kGemmThreads) void ffn_fixup_kernel(GemmArgs p, const float* __restrict__ parts) {
   __shared__ Sched sh;
@@ -941,10 +941,10 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_wide_fixup_kernel(GemmArgs p
 
 // Tiles tl.nt .. tl.nt + n - 1 of one group and row tile, iterations
 // [it_begin, it_end) of the run (iteration k * nchunks + c is chunk c of its
-// tile k). A tile is 64 rows x two N blocks; wave w owns rows 32 (w % 4) ..
-// of N block 2 tile + w / 4 (past the group's last block a wave repeats it and
-// its results are discarded), so each staged activation chunk feeds 256
-// weight rows. The first / last tile leave fp32 partials in part_first /
+// tile k). A tile is 64 activation rows x two N blocks; wave w owns weight
+// rows 32 (w % 4) .. + 31 of N block 2 tile + w / 4 (past the group's last
+// block a wave repeats it and its results are discarded), so each staged
+// activation chunk feeds 256 weight rows. The first / last tile leave fp32 partials in part_first /
 // part_last when split (else nullptr: their epilogue runs here).
 template <int KIND, bool PACKED, int NB, bool STREAM>
 __device__ __forceinline__ void bf_run(const GemmArgs& p, const Tile& tl, int n, const Sched& sh,
@@ -954,7 +954,7 @@ __device__ __forceinline__ void bf_run(const GemmArgs& p, const Tile& tl, int n,
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform: scalar
-  const int wq = wv & 3;   // the wave's 32 rows of its N block
+  const int wq = wv & 3;   // the wave's 32 weight rows of its N block
   const int wg = wv >> 2;  // the wave's N block in the tile
   const int lr = lane & 31;
   const int lh = lane >> 5;

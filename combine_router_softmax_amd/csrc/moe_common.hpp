@@ -53,12 +53,32 @@ inline moe_status_t launch_status() {
 }
 
 // Block-wide scan of a[0..n) in LDS (kThreads threads). Each thread
-// scans a contiguous run, then the run totals are scanned across the block.
-// kMax: inclusive max-scan; otherwise exclusive sum-scan with the total
-// returned. All threads must call it.
+// scans a contiguous run, then the run totals are scanned across the block;
+// up to one wavefront of values, the first wave scans them alone with lane
+// shuffles (two barriers instead of two per doubling step). kMax: inclusive
+// max-scan; otherwise exclusive sum-scan with the total returned. All threads
+// must call it.
 template <bool kMax, int kThreads>
 __device__ int block_scan_lds(int* a, int n, int* tmp /* [kThreads] */) {
   const int tid = threadIdx.x;
+  if (n <= kWave) {  // uniform
+    if (tid < kWave) {
+      const int id = kMax ? INT_MIN : 0;
+      const int v = tid < n ? a[tid] : id;
+      int incl = v;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int u = __shfl_up(incl, off);
+        if (tid >= off) incl = kMax ? max(incl, u) : incl + u;
+      }
+      if (tid < n) a[tid] = kMax ? incl : incl - v;
+      if (tid == kWave - 1) tmp[0] = incl;
+    }
+    __syncthreads();
+    const int total = tmp[0];
+    __syncthreads();  // every thread has read tmp[0] before a later scan reuses tmp
+    return total;
+  }
   const int per = (n + kThreads - 1) / kThreads;
   const int lo = min(n, tid * per), hi = min(n, lo + per);
   int acc = kMax ? INT_MIN : 0;
