@@ -26,7 +26,8 @@ def _inputs(cfg):
 
 
 @pytest.mark.parametrize("name,layout", [("tiny", PADDED), ("tiny", COMPACT), ("dsv3_decode_ep8", COMPACT),
-                                         ("kimi_k2_ep8", COMPACT), ("dsv3_decode_ep8", PADDED)])
+                                         ("kimi_k2_ep8", COMPACT), ("dsv3_decode_ep8", PADDED),
+                                         ("dsv3_decode_ep128", COMPACT)])  # wide-tile kernel, gathered rows
 def test_graph_replays_match_eager(name, layout):
     cfg = tiny_config(shared=True) if name == "tiny" else get_config(name)
     flush(f"graph {cfg.name} layout={layout}")
