@@ -219,3 +219,22 @@ def test_blocked_layout_helper_matches_the_documented_formula():
             flat[((r // 16) * (K // 32) + c // 32) * 512 + (r % 16) * 32 + c % 32] = a[r, c]
     np.testing.assert_array_equal(unblock16(flat.reshape(R16, K), R), a)
     assert moe.blocked_rows(37) == 48 and moe.blocked_rows(48) == 48 and moe.blocked_rows(0) == 0
+
+
+def test_layer_gather_rule():
+    # bf16 row-major rows: the up projection gathers from the tokens and no
+    # expert-row copy is allocated; blocked rows and fp32 keep the dispatch
+    import torch
+    from combine_router_softmax_amd.layer import MoEShare
+    kw = dict(n_tokens=64, hidden=256, inter=128, n_experts=16, top_k=2, n_src=2, expert_lo=0, n_local=4,
+              device="cpu")
+    s = MoEShare(act_dtype=torch.bfloat16, **kw)
+    assert s.gather and s.xe is None
+    s = MoEShare(act_dtype=torch.bfloat16, blocked=True, **kw)
+    assert not s.gather and s.xe is not None
+    s = MoEShare(act_dtype=torch.bfloat16, gather=False, **kw)
+    assert not s.gather and s.xe is not None
+    s = MoEShare(act_dtype=torch.float32, **kw)
+    assert not s.gather
+    with pytest.raises(ValueError):
+        MoEShare(act_dtype=torch.float32, gather=True, **kw)
