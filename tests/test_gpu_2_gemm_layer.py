@@ -351,18 +351,60 @@ def full_case(request):
     torch.cuda.empty_cache()
 
 
-def _sample_tokens(rng, N, B0, n=12):
-    a = np.sort(rng.choice(B0, size=min(n // 2, B0), replace=False))
-    b = np.sort(rng.choice(np.arange(B0, N), size=min(n - len(a), N - B0), replace=False))
-    return np.concatenate([a, b]).astype(np.int64), len(a)
+def _shared_oracle_weights(sw):
+    fp8 = sw.get("s13") is not None
+    return (_Lazy(sw["w13"], fp8), _Lazy(sw["w2"], fp8), None if not fp8 else sw["s13"].numpy(),
+            None if not fp8 else sw["s2"].numpy())
+
+
+def _assert_rows_close(got, ref, tol, what, row_tol=None):
+    """Relative L2 over all compared rows (<= tol), and over each row on its
+    own (<= row_tol, default tol): a single wrong row must fail even among
+    thousands of right ones."""
+    row_tol = tol if row_tol is None else row_tol
+    err = rel_l2(got, ref)
+    num = np.linalg.norm(got - ref, axis=1)
+    den = np.maximum(np.linalg.norm(ref, axis=1), 1e-30)
+    worst = int(np.argmax(num / den))
+    flush(f"  {what}: {len(ref)} rows, rel-L2 {err:.3e}, worst row {worst} rel {num[worst] / den[worst]:.3e}")
+    assert err <= tol, f"{what}: rel-L2 {err:.3e} > {tol}"
+    assert num[worst] / den[worst] <= row_tol, f"{what}: row {worst} rel {num[worst] / den[worst]:.3e} > {row_tol}"
+
+
+def _split_experts(m, ntn):
+    """Local experts that hold wide tiles split along K: the wide kernel takes
+    whole tiles in rounds of 256 and splits the last (tiles % 256), which are
+    the last tiles of the schedule (the shared expert first, then the routed
+    experts in index order, 256-row tiles, ntn weight tiles per row tile)."""
+    tiles = [(int(mm) + 255) // 256 * ntn for mm in m]
+    total = sum(tiles) + ntn * 16  # + the shared expert's 4096 rows
+    rem = total % 256
+    out, acc = [], 0
+    for g in reversed(range(len(m))):
+        if acc >= rem:
+            break
+        if tiles[g]:
+            out.append(g)
+        acc += tiles[g]
+    return out
 
 
 def test_layer_full_size(full_case):
+    """Whole layer at the full configuration, compact and padded layouts.
+
+    Exact integer results; the two layouts and two runs give the same bits.
+    Decode-sized shares (every touched token affordable on the CPU): every
+    touched output row against the oracle's whole layer. The prefill share
+    (32,768 tokens): every row of the GPU's own 4096 tokens end to end, and
+    every expert-output row of the hottest local expert, of the experts whose
+    wide tiles are split along K, and of the shared expert."""
     cfg, d = full_case
     flush(f"layer {cfg.name}")
     off = d["src_offsets"]
     N, B0 = int(off[-1]), int(off[1])
+    tol = TOL[cfg.weight]
     outs = {}
+    keep = {}
     for layout in (COMPACT, PADDED):
         share = _share_from_inputs(d, layout)
         out = _run(share, d)
@@ -373,7 +415,11 @@ def test_layer_full_size(full_case):
             lay = dispatch_layout(ridx, off, cfg.expert_lo, cfg.n_local, COMPACT, share.capacity)
             np.testing.assert_array_equal(i64(share.lay["row_of"]), lay["row_of"])
             np.testing.assert_array_equal(i64(share.lay["counts"]).reshape(cfg.n_local, -1), lay["counts"])
+            np.testing.assert_array_equal(i64(share.lay["expert_off"]), lay["expert_off"])
             assert int(share.lay["status"].item()) == 0
+            keep["lay"] = lay
+            keep["ye"] = share.ye[: int(lay["expert_off"][-1])].cpu()
+            keep["ys"] = share.ys[:B0].cpu()
         outs[layout] = out
         # determinism: a second step gives the same bits
         out2 = _run(share, d)
@@ -383,20 +429,73 @@ def test_layer_full_size(full_case):
     # the two layouts compute every row the same way
     assert torch.equal(outs[COMPACT].view(torch.int16), outs[PADDED].view(torch.int16))
 
-    # sampled tokens, end to end against the oracle on the same tokens
-    rng = np.random.default_rng(5)
-    tok, n_self = _sample_tokens(rng, N, B0, n=8 if cfg.n_local > 8 else 16)
     w13, w2, s13, s2 = _oracle_weights(d["routed"])
-    sw = d["shared"]
-    sh = (_Lazy(sw["w13"], sw.get("s13") is not None), _Lazy(sw["w2"], sw.get("s2") is not None),
-          None if sw.get("s13") is None else sw["s13"].numpy(), None if sw.get("s2") is None else sw["s2"].numpy())
-    xs = f64(d["x"][torch.from_numpy(tok)])
-    ref = moe_layer(xs, d["logits"][tok], [0, len(tok)], cfg.top_k, cfg.expert_lo, cfg.n_local, w13, w2, s13, s2,
-                    shared=sh, self_range=(0, n_self), out_init=np.full(xs.shape, -9.0))
-    got = f64(outs[COMPACT][torch.from_numpy(tok).cuda()])
+    sh = _shared_oracle_weights(d["shared"])
+    got_all = f64(outs[COMPACT])
+    if N * cfg.n_local <= 4096 * 48:
+        # every token, end to end
+        flush(f"  oracle layer over {N} tokens")
+        ref = moe_layer(f64(d["x"]), d["logits"], off, cfg.top_k, cfg.expert_lo, cfg.n_local, w13, w2, s13, s2,
+                        shared=sh, self_range=(0, B0), out_init=np.full(tuple(d["x"].shape), -9.0))
+        touched = ref["out"][:, 0] != -9.0
+        assert np.all(got_all[~touched] == -9.0)
+        assert touched[:B0].all()
+        _assert_rows_close(got_all[touched], ref["out"][touched], tol, f"{cfg.name} touched rows")
+        return
+
+    # prefill share: the GPU's own tokens end to end ...
+    flush(f"  oracle layer over the {B0} own tokens")
+    ref = moe_layer(f64(d["x"][:B0]), d["logits"][:B0], [0, B0], cfg.top_k, cfg.expert_lo, cfg.n_local, w13, w2,
+                    s13, s2, shared=sh, self_range=(0, B0), out_init=np.full((B0, cfg.hidden), -9.0))
+    _assert_rows_close(got_all[:B0], ref["out"], tol, f"{cfg.name} own tokens")
+    # ... and whole experts' output rows of the routed GEMM
+    lay = keep["lay"]
+    m = lay["counts"].sum(axis=1)
+    ye = f64(keep["ye"])
+    experts = {int(np.argmax(m))} | set(_split_experts(m, 16)) | set(_split_experts(m, 28))
+    for g in sorted(experts):
+        rows = group_rows(lay, g)
+        a13, a2 = weights_f64(d["routed"], g)
+        flush(f"  oracle expert {g}: {len(rows)} rows")
+        ref_g = swiglu_ffn(f64(d["x"])[lay["row_token"][rows]], a13, a2)
+        _assert_rows_close(ye[rows], ref_g, tol, f"{cfg.name} expert {g}")
+    a13, a2 = weights_f64(d["shared"], 0)
+    _assert_rows_close(f64(keep["ys"]), swiglu_ffn(f64(d["x"][:B0]), a13, a2), tol, f"{cfg.name} shared expert")
+
+
+# A mid-sized whole layer through each MFMA kernel (bf16 stream-K, bf16 wide
+# tiles forced, fp8 stream-K), every touched output row against the oracle.
+# Hidden 1024, 8 ranks x 96 tokens, 64 experts (8 local), top-8, intermediate
+# 512: several tiles per expert, stream-K ranges cut inside tiles (fixups),
+# gathered rows, a shared expert in the launch.
+@pytest.mark.parametrize("kernel", ["bf16_stream_k", "bf16_wide", "fp8"])
+@pytest.mark.parametrize("layout", [COMPACT, PADDED])
+def test_layer_mid_size_every_row(kernel, layout):
+    name = "kimi_k2_ep8" if kernel == "fp8" else "dsv3_decode_ep8"
+    cfg = get_config(name, hidden=1024, inter=512, n_experts=64, n_local=8, tokens_per_src=96)
+    d = make_inputs(cfg, 7)
+    off = d["src_offsets"]
+    N, B0 = int(off[-1]), int(off[1])
+    cap = None if layout == COMPACT else int(np.diff(off).max())
+    share = MoEShare(n_tokens=N, hidden=cfg.hidden, inter=cfg.inter, n_experts=cfg.n_experts, top_k=cfg.top_k,
+                     n_src=cfg.n_src, expert_lo=0, n_local=cfg.n_local, act_dtype=torch.bfloat16, layout=layout,
+                     capacity=cap, self_range=(0, B0),
+                     policy=moe.GEMM_WIDE if kernel == "bf16_wide" else moe.GEMM_STREAM_K)
+    share.set_weights(d["routed"], d["shared"])
+    out = _run(share, d)
+    w13, w2, s13, s2 = _oracle_weights(d["routed"])
+    ref = moe_layer(f64(d["x"]), d["logits"], off, cfg.top_k, 0, cfg.n_local, w13, w2, s13, s2,
+                    shared=_shared_oracle_weights(d["shared"]), self_range=(0, B0), layout=layout,
+                    capacity=share.capacity, out_init=np.full(tuple(d["x"].shape), -9.0))
+    np.testing.assert_array_equal(i64(share.lay["row_of"]), ref["layout"]["row_of"])
+    got = f64(out)
     touched = ref["out"][:, 0] != -9.0
     assert np.all(got[~touched] == -9.0)
-    assert rel_l2(got[touched], ref["out"][touched]) <= TOL[cfg.weight]
+    assert touched.sum() > B0
+    # bf16 operands are exact, sums fp32; h and y (and fp8 weights, once) are
+    # rounded to bf16: far inside the benchmark spec's bounds, which hold per row
+    _assert_rows_close(got[touched], ref["out"][touched], 1e-2, f"mid {kernel} layout={layout}",
+                       row_tol=TOL[cfg.weight])
 
 
 @pytest.mark.parametrize("name", ["dsv3_decode_ep8", "kimi_k2_ep8"])

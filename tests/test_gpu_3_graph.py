@@ -7,11 +7,50 @@ import pytest
 import torch
 
 from combine_router_softmax_amd.layer import MoEShare
-from oracle import COMPACT, PADDED
+from oracle import COMPACT, PADDED, moe_layer
 from synth import get_config, make_inputs, make_routing_inputs, make_x, tiny_config
-from util import flush
+from util import f64, flush, rel_l2
 
 pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8_e4m3": 5e-2}
+
+
+def _oracle_weights(d0):
+    r, s = d0["routed"], d0["shared"]
+    fp8 = r.get("s13") is not None
+
+    def w(t):
+        return t.numpy() if fp8 else t.double().numpy()
+    sc = (r["s13"].numpy(), r["s2"].numpy()) if fp8 else (None, None)
+    routed = (w(r["w13"]), w(r["w2"]), *sc)
+    sh = None if s is None else (w(s["w13"]), w(s["w2"]),
+                                 *((s["s13"].numpy(), s["s2"].numpy()) if fp8 else (None, None)))
+    return routed, sh
+
+
+def _oracle_check(cfg, weights, inp, got, layout, capacity):
+    """The eager step (which every replay equals bit for bit) against the
+    oracle: every touched row for batches up to 2048 tokens, else the GPU's
+    own tokens plus 256 others."""
+    lg, of, x = inp
+    of = np.asarray(of, dtype=np.int64)
+    N, B0 = int(of[-1]), int(of[1])
+    routed, sh = weights
+    if N <= 2048:
+        tok = np.arange(N)
+        sub_off = of
+    else:
+        rng = np.random.default_rng(N)
+        tok = np.concatenate([np.arange(B0), np.sort(rng.choice(np.arange(B0, N), 256, replace=False))])
+        sub_off, layout, capacity = [0, len(tok)], COMPACT, None
+    ref = moe_layer(f64(x[torch.from_numpy(tok)]), lg[tok], sub_off, cfg.top_k, cfg.expert_lo, cfg.n_local, *routed,
+                    shared=sh, self_range=(0, B0), layout=layout, capacity=capacity,
+                    out_init=np.full((len(tok), cfg.hidden), -9.0))
+    g = f64(got)[tok]
+    touched = ref["out"][:, 0] != -9.0
+    assert np.all(g[~touched] == -9.0)
+    assert rel_l2(g[touched], ref["out"][touched]) <= TOL[cfg.weight]
 
 
 def _inputs(cfg):
@@ -55,12 +94,14 @@ def test_graph_replays_match_eager(name, layout):
         X.copy_(x)
         out.fill_(-9.0)
 
+    weights = _oracle_weights(d0)
     eager = []
     for i in range(2):
         load(i)
         share.step(L, O, X, out)
         torch.cuda.synchronize()
         eager.append(out.clone())
+        _oracle_check(cfg, weights, ins[i], eager[i], layout, share.capacity)
     assert not torch.equal(eager[0], eager[1])
 
     side = torch.cuda.Stream()
