@@ -13,6 +13,7 @@ import ctypes
 import os
 from typing import Optional
 
+import numpy as np
 import torch
 
 __all__ = [
@@ -119,13 +120,29 @@ def _stream():
 
 
 def _dev(t: torch.Tensor, name: str, dtype=None):
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
+    """Contiguity and dtype (placement is checked by _on_gpu right before the
+    call, after every size check)."""
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
     return t
+
+
+def _on_gpu(**tensors):
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+
+
+def _need(ok: bool, msg: str):
+    """Host-side size check: a short buffer must never reach a kernel."""
+    if not ok:
+        raise ValueError(msg)
+
+
+def _shape_is(t: torch.Tensor, shape, name: str):
+    _need(tuple(t.shape) == tuple(shape), f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
 def _act_code(dt: torch.dtype) -> int:
@@ -152,6 +169,9 @@ def moe_route_topk(logits: torch.Tensor, top_k: int, renormalize: bool = True,
         topk_w = torch.empty((N, top_k), dtype=torch.float32, device=logits.device)
     _dev(topk_idx, "topk_idx", torch.int32)
     _dev(topk_w, "topk_w", torch.float32)
+    _need(logits.dim() == 2, "logits must be [N, E]")
+    _need(topk_idx.numel() == N * top_k and topk_w.numel() == N * top_k, "topk_idx and topk_w must hold N * top_k")
+    _on_gpu(logits=logits, topk_idx=topk_idx, topk_w=topk_w)
     _check(lib().moe_route_topk(_ptr(logits), N, E, top_k, int(bool(renormalize)), _ptr(topk_idx), _ptr(topk_w),
                                 _stream()), "moe_route_topk")
     return topk_idx, topk_w
@@ -193,6 +213,12 @@ def moe_dispatch_layout(topk_idx: torch.Tensor, src_offsets: torch.Tensor, n_exp
             o[k] = torch.empty(shape, dtype=dt, device=dev)
     for k in ("counts", "expert_off", "row_of", "row_token", "status"):
         _dev(o[k], k, torch.int32)
+    _dev(o["ws"], "ws")
+    for k, (shape, _) in shapes.items():
+        need = int(np.prod(shape))
+        _need(o[k].numel() * o[k].element_size() >= need * (1 if k == "ws" else 4),
+              f"{k} holds {o[k].numel()} elements, fewer than the {need} the layout writes")
+    _on_gpu(topk_idx=topk_idx, src_offsets=src_offsets, **{k: o[k] for k in shapes})
     _check(lib().moe_dispatch_layout(ctypes.byref(d), _ptr(topk_idx), _ptr(src_offsets), _ptr(o["counts"]),
                                      _ptr(o["expert_off"]), _ptr(o["row_of"]), _ptr(o["row_token"]),
                                      _ptr(o["status"]), _ptr(o["ws"]), o["ws"].numel(), _stream()),
@@ -211,6 +237,9 @@ def moe_dispatch(x: torch.Tensor, row_of: torch.Tensor, top_k: int, n_rows: int,
     if xe is None:
         xe = torch.empty((n_rows, H), dtype=x.dtype, device=x.device)
     _dev(xe, "xe", x.dtype)
+    _need(xe.dim() == 2 and xe.shape[1] == H and xe.shape[0] >= n_rows, f"xe must be [>= {n_rows}, {H}]")
+    _need(row_of.numel() >= N * top_k, f"row_of must hold N * top_k = {N * top_k} entries")
+    _on_gpu(x=x, row_of=row_of, xe=xe)
     _check(lib().moe_dispatch(_ptr(x), _act_code(x.dtype), N, H, top_k, _ptr(row_of), n_rows, _ptr(xe), _stream()),
            "moe_dispatch")
     return xe
@@ -231,8 +260,10 @@ def moe_dispatch_blocked(x: torch.Tensor, row_of: torch.Tensor, top_k: int, n_ro
     if xe is None:
         xe = torch.empty((blocked_rows(n_rows), H), dtype=x.dtype, device=x.device)
     _dev(xe, "xe", x.dtype)
-    if xe.shape[0] < blocked_rows(n_rows):
-        raise ValueError("xe must hold blocked_rows(n_rows) rows")
+    _need(xe.dim() == 2 and xe.shape[1] == H and xe.shape[0] >= blocked_rows(n_rows),
+          f"xe must be [>= blocked_rows({n_rows}), {H}]")
+    _need(row_of.numel() >= N * top_k, f"row_of must hold N * top_k = {N * top_k} entries")
+    _on_gpu(x=x, row_of=row_of, xe=xe)
     _check(lib().moe_dispatch_blocked(_ptr(x), _act_code(x.dtype), N, H, top_k, _ptr(row_of), n_rows, _ptr(xe),
                                       _stream()), "moe_dispatch_blocked")
     return xe
@@ -261,8 +292,20 @@ def shared_expert(a: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, y: Optio
     _dev(a, "shared a")
     _dev(w13, "shared w13")
     _dev(w2, "shared w2")
+    _need(a.dim() == 2 and w13.dim() == 3 and w13.shape[0] == 1 and w13.shape[2] == a.shape[1],
+          "shared expert: a must be [B, H] and w13 [1, 2I, H]")
+    B, H = a.shape
+    I = w13.shape[1] // 2
+    _shape_is(w2, (1, H, I), "shared w2")
     if y is not None:
         _dev(y, "shared y", a.dtype)
+        _need(y.dim() == 2 and y.shape[1] == H and y.shape[0] >= B, f"shared y must be [>= {B}, {H}]")
+    if s13 is not None or s2 is not None:
+        _need(s13 is not None and s2 is not None, "fp8 shared weights need both scale tensors")
+        _dev(s13, "shared s13", torch.float32)
+        _dev(s2, "shared s2", torch.float32)
+        _shape_is(s13, (1, 2 * I // 128, H // 128), "shared s13")
+        _shape_is(s2, (1, H // 128, I // 128), "shared s2")
     return SharedExpert(a.data_ptr(), a.shape[0], w13.data_ptr(), w2.data_ptr(),
                         None if s13 is None else s13.data_ptr(), None if s2 is None else s2.data_ptr(),
                         None if y is None else y.data_ptr())
@@ -286,11 +329,19 @@ def moe_grouped_gemm(a: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, *, gr
     _dev(a, "a", (torch.float32, torch.bfloat16))
     _dev(w13, "w13")
     _dev(w2, "w2")
+    _need(a.dim() == 2 and w13.dim() == 3, "a must be [rows, H] and w13 [G, 2I, H]")
     R, H = a.shape
     G, I2, H2 = w13.shape
     if H2 != H or I2 % 2:
         raise ValueError("w13 must be [G, 2I, H]")
     I = I2 // 2
+    _shape_is(w2, (G, H, I), "w2")
+    if w13.dtype in (torch.uint8, torch.float8_e4m3fn):
+        _need(s13 is not None and s2 is not None, "fp8 weights need s13 and s2")
+    if s13 is not None or s2 is not None:
+        _need(s13 is not None and s2 is not None, "fp8 weights need both scale tensors")
+        _shape_is(s13, (G, I2 // 128, H // 128), "s13")
+        _shape_is(s2, (G, H // 128, I // 128), "s2")
     se = None
     if shared is not None:
         se = shared_expert(shared["a"], shared["w13"], shared["w2"], shared.get("y"), shared.get("s13"),
@@ -301,11 +352,19 @@ def moe_grouped_gemm(a: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, *, gr
         _dev(a_rows, "a_rows", torch.int32)
         if a_rows.numel() < rows:
             raise ValueError(f"a_rows holds {a_rows.numel()} entries, fewer than rows={rows}")
+        _need(a.shape[0] >= 1, "a gathered input needs at least one row to gather from")
         R = rows
     elif a_layout == ACT_BLOCKED16:
         R = a.shape[0] // 16 * 16 if rows is None else rows
+        _need(a.shape[0] >= blocked_rows(R), f"blocked a must hold blocked_rows({R}) rows")
     elif rows is not None:
+        _need(a.shape[0] >= rows, f"a holds {a.shape[0]} rows, fewer than rows={rows}")
         R = rows
+    if layout == COMPACT:
+        _need(group_off is not None and group_off.numel() >= G + 1, f"group_off must hold G + 1 = {G + 1} entries")
+    else:
+        _need(counts is not None and counts.numel() >= G * n_src, f"counts must hold G * n_src = {G * n_src}")
+        _need(R >= G * n_src * capacity, f"the padded layout needs {G * n_src * capacity} rows, got {R}")
     desc = gemm_desc(G, H, I, a.dtype, w13.dtype, layout, n_src, capacity, R, stage, se, w_format, policy, a_layout)
     if a_rows is not None:
         desc.a_rows = a_rows.data_ptr()
@@ -315,14 +374,22 @@ def moe_grouped_gemm(a: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, *, gr
         raise MoeError("moe_grouped_gemm: invalid descriptor")
     if ws is None:
         ws = torch.zeros(wsb, dtype=torch.uint8, device=a.device)
+    _dev(ws, "ws")
+    _need(ws.numel() * ws.element_size() >= wsb, f"ws holds {ws.numel() * ws.element_size()} bytes, needs {wsb}")
     if y is None and stage != GG_UP:
         y = torch.empty((R, H), dtype=a.dtype, device=a.device)
+    if y is not None:
+        _dev(y, "y", a.dtype)
+        _need(y.dim() == 2 and y.shape[1] == H and y.shape[0] >= R, f"y must be [>= {R}, {H}]")
     for name, t in (("group_off", group_off), ("counts", counts)):
         if t is not None:
             _dev(t, name, torch.int32)
     for name, t in (("s13", s13), ("s2", s2)):
         if t is not None:
             _dev(t, name, torch.float32)
+    _on_gpu(a=a, w13=w13, w2=w2, group_off=group_off, counts=counts, s13=s13, s2=s2, y=y, ws=ws, a_rows=a_rows)
+    if shared is not None:
+        _on_gpu(**{f"shared {k}": v for k, v in shared.items() if isinstance(v, torch.Tensor)})
     _check(lib().moe_grouped_gemm(ctypes.byref(desc), _ptr(a), _ptr(counts), _ptr(group_off), _ptr(w13), _ptr(w2),
                                   _ptr(s13), _ptr(s2), _ptr(y), _ptr(ws), ws.numel(), _stream()),
            "moe_grouped_gemm")
@@ -333,8 +400,13 @@ def moe_pack_weights(w13: Optional[torch.Tensor], w2: Optional[torch.Tensor], hi
     """Packed copies of expert weights (w13 [G,2I,H], w2 [G,H,I]; bf16 or fp8 codes)."""
     ref = w13 if w13 is not None else w2
     G = ref.shape[0]
+    if w13 is not None:
+        _shape_is(w13, (G, 2 * inter, hidden), "w13")
+    if w2 is not None:
+        _shape_is(w2, (G, hidden, inter), "w2")
     out13 = None if w13 is None else torch.empty_like(_dev(w13, "w13"))
     out2 = None if w2 is None else torch.empty_like(_dev(w2, "w2"))
+    _on_gpu(w13=w13, w2=w2)
     _check(lib().moe_pack_weights(G, hidden, inter, _W_CODE[ref.dtype], _ptr(w13), _ptr(w2), _ptr(out13), _ptr(out2),
                                   _stream()), "moe_pack_weights")
     return out13, out2
@@ -350,8 +422,14 @@ def moe_combine(ye: torch.Tensor, row_of: torch.Tensor, topk_w: torch.Tensor, ou
     _dev(out, "out", ye.dtype)
     N, H = out.shape
     K = topk_w.shape[-1] if topk_w.dim() == 2 else (topk_w.numel() // N if N else 1)
+    _need(ye.dim() == 2 and ye.shape[1] == H, f"ye must be [rows, {H}]")
+    _need(row_of.numel() >= N * K and topk_w.numel() >= N * K, f"row_of and topk_w must hold N * K = {N * K}")
     if shared_y is not None:
         _dev(shared_y, "shared_y", ye.dtype)
+        _need(0 <= self_lo <= self_hi <= N, "the self range must lie inside [0, N]")
+        _need(shared_y.dim() == 2 and shared_y.shape[1] == H and shared_y.shape[0] >= self_hi - self_lo,
+              f"shared_y must be [>= {self_hi - self_lo}, {H}]")
+    _on_gpu(ye=ye, row_of=row_of, topk_w=topk_w, out=out, shared_y=shared_y)
     _check(lib().moe_combine(_ptr(ye), _act_code(ye.dtype), ye.shape[0], _ptr(row_of), _ptr(topk_w), N, K, H,
                              _ptr(shared_y), self_lo, self_hi, _ptr(out), _stream()), "moe_combine")
     return out

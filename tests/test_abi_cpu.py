@@ -238,3 +238,86 @@ def test_layer_gather_rule():
     assert not s.gather
     with pytest.raises(ValueError):
         MoEShare(act_dtype=torch.float32, gather=True, **kw)
+
+
+# The binding checks every size a kernel relies on before anything reaches the
+# library: a short buffer raises ValueError on the host (these run on CPU
+# tensors; the size checks come before the placement check).
+def _t(*shape, dt=None):
+    import torch
+    return torch.zeros(shape, dtype=dt or torch.bfloat16)
+
+
+def test_binding_rejects_short_buffers(lib):
+    import torch
+    i32, f32 = torch.int32, torch.float32
+    with pytest.raises(ValueError, match="topk_idx and topk_w"):
+        moe.moe_route_topk(_t(10, 16, dt=f32), 2, topk_idx=_t(9, 2, dt=i32), topk_w=_t(10, 2, dt=f32))
+    # dispatch: xe rows / width, row_of length
+    with pytest.raises(ValueError, match="xe must be"):
+        moe.moe_dispatch(_t(4, 64), _t(8, dt=i32), 2, 10, xe=_t(9, 64))
+    with pytest.raises(ValueError, match="xe must be"):
+        moe.moe_dispatch(_t(4, 64), _t(8, dt=i32), 2, 10, xe=_t(10, 32))
+    with pytest.raises(ValueError, match="row_of must hold"):
+        moe.moe_dispatch(_t(4, 64), _t(7, dt=i32), 2, 10, xe=_t(10, 64))
+    with pytest.raises(ValueError, match="blocked_rows"):
+        moe.moe_dispatch_blocked(_t(4, 64), _t(8, dt=i32), 2, 17, xe=_t(17, 64))
+    # layout outputs passed in by the caller
+    out = {"row_of": _t(199, dt=i32)}
+    with pytest.raises(ValueError, match="row_of holds"):
+        moe.moe_dispatch_layout(_t(100, 2, dt=i32), _t(5, dt=i32), 16, 0, 2, moe.COMPACT, 200, out=out)
+    with pytest.raises(ValueError, match="counts holds"):
+        moe.moe_dispatch_layout(_t(100, 2, dt=i32), _t(5, dt=i32), 16, 0, 2, moe.COMPACT, 200,
+                                out={"counts": _t(7, dt=i32)})
+    with pytest.raises(ValueError, match="row_token holds"):
+        moe.moe_dispatch_layout(_t(100, 2, dt=i32), _t(5, dt=i32), 16, 0, 2, moe.COMPACT, 200,
+                                out={"row_token": _t(150, dt=i32)})
+    # combine: ye width, shared rows, routing lengths
+    with pytest.raises(ValueError, match="ye must be"):
+        moe.moe_combine(_t(10, 32), _t(8, dt=i32), _t(4, 2, dt=f32), _t(4, 64))
+    with pytest.raises(ValueError, match="shared_y must be"):
+        moe.moe_combine(_t(10, 64), _t(8, dt=i32), _t(4, 2, dt=f32), _t(4, 64), _t(1, 64), 0, 2)
+    with pytest.raises(ValueError, match="self range"):
+        moe.moe_combine(_t(10, 64), _t(8, dt=i32), _t(4, 2, dt=f32), _t(4, 64), _t(9, 64), 0, 9)
+    with pytest.raises(ValueError, match="row_of and topk_w"):
+        moe.moe_combine(_t(10, 64), _t(7, dt=i32), _t(4, 2, dt=f32), _t(4, 64))
+
+
+def test_binding_rejects_bad_gemm_shapes(lib):
+    import torch
+    i32, f32 = torch.int32, torch.float32
+    G, H, I = 3, 256, 128
+    a, w13, w2 = _t(40, H), _t(G, 2 * I, H), _t(G, H, I)
+    off = _t(G + 1, dt=i32)
+    with pytest.raises(ValueError, match="w2 has shape"):
+        moe.moe_grouped_gemm(a, w13, _t(G, I, H), group_off=off)
+    with pytest.raises(ValueError, match="group_off must hold"):
+        moe.moe_grouped_gemm(a, w13, w2, group_off=_t(G, dt=i32))
+    with pytest.raises(ValueError, match="counts must hold"):
+        moe.moe_grouped_gemm(_t(3 * 2 * 4, H), w13, w2, counts=_t(5, dt=i32), layout=moe.PADDED, n_src=2,
+                             capacity=4)
+    with pytest.raises(ValueError, match="padded layout needs"):
+        moe.moe_grouped_gemm(_t(20, H), w13, w2, counts=_t(6, dt=i32), layout=moe.PADDED, n_src=2, capacity=4)
+    with pytest.raises(ValueError, match="a holds"):
+        moe.moe_grouped_gemm(a, w13, w2, group_off=off, rows=41)
+    with pytest.raises(ValueError, match="y must be"):
+        moe.moe_grouped_gemm(a, w13, w2, group_off=off, y=_t(39, H))
+    with pytest.raises(ValueError, match="ws holds"):
+        moe.moe_grouped_gemm(a, w13, w2, group_off=off, ws=_t(16, dt=torch.uint8))
+    u8 = torch.uint8
+    with pytest.raises(ValueError, match="fp8 weights need"):
+        moe.moe_grouped_gemm(a, _t(G, 2 * I, H, dt=u8), _t(G, H, I, dt=u8), group_off=off)
+    with pytest.raises(ValueError, match="s13 has shape"):
+        moe.moe_grouped_gemm(a, _t(G, 2 * I, H, dt=u8), _t(G, H, I, dt=u8), group_off=off,
+                             s13=_t(G, 2, 1, dt=f32), s2=_t(G, 2, 1, dt=f32))
+    with pytest.raises(ValueError, match="shared y must be"):
+        moe.moe_grouped_gemm(a, w13, w2, group_off=off,
+                             shared={"a": _t(9, H), "w13": w13[:1], "w2": w2[:1], "y": _t(8, H)})
+    with pytest.raises(ValueError, match="shared w2 has shape"):
+        moe.moe_grouped_gemm(a, w13, w2, group_off=off,
+                             shared={"a": _t(9, H), "w13": w13[:1], "w2": _t(1, I, H), "y": _t(9, H)})
+    with pytest.raises(ValueError, match="w13 has shape"):
+        moe.moe_pack_weights(_t(G, I, H), None, H, I)
+    # right sizes on host tensors: the placement check is the one that fails
+    with pytest.raises(ValueError, match="must be a device tensor"):
+        moe.moe_grouped_gemm(a, w13, w2, group_off=off)
