@@ -17,10 +17,15 @@ namespace {
 
 constexpr int kRouteTokensPerBlock = 4;
 
+// Key 0 marks "no expert here / already taken"; every present expert gets a
+// key of at least 1, so the K rounds always find K distinct, in-range experts.
+// (Only a NaN with a negative sign and an all-ones payload maps to 0 before
+// the clamp; NaNs carry no order, so where they land is unspecified.)
 __device__ __forceinline__ uint32_t order_key(float v) {
   uint32_t u = __float_as_uint(v);
   if (u == 0x80000000u) u = 0u;  // -0 and +0 compare equal
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return k > 1u ? k : 1u;
 }
 
 __device__ __forceinline__ float key_value(uint32_t k) {
@@ -69,7 +74,7 @@ __global__ __launch_bounds__(kWave * kRouteTokensPerBlock) void route_topk_kerne
   const float* row = logits + size_t(t) * n_experts;
 
   float val[VPL];
-  uint32_t key[VPL];  // 0: no expert here, or already selected (no real logit maps to 0 but -NaN)
+  uint32_t key[VPL];  // 0: no expert here, or already selected (present experts have keys >= 1)
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
     const int e = j * kWave + lane;

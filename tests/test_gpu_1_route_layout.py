@@ -52,6 +52,29 @@ def test_route_shapes_and_ties(E, K):
     _route_check(z, K, renorm=False)
 
 
+def test_route_nan_logits_give_in_range_distinct_indices():
+    # NaN logits are outside the contract (no order), but the indices must stay
+    # in range and distinct: 0xFFFFFFFF (memory filled with 0xFF) and other NaNs,
+    # whole rows of them and mixed with finite logits
+    E, K = 96, 8
+    z = np.random.default_rng(3).standard_normal((6, E)).astype(np.float32)
+    bits = z.view(np.uint32)
+    bits[0] = 0xFFFFFFFF
+    bits[1] = 0x7FC00000
+    bits[2, ::3] = 0xFFFFFFFF
+    bits[3, :90] = 0xFFFFFFFE
+    bits[4] = 0xFFFFFFFF
+    bits[4, 50] = np.float32(1.0).view(np.uint32)
+    idx, _ = moe.moe_route_topk(torch.from_numpy(z).cuda(), K)
+    idx = i64(idx)
+    assert ((idx >= 0) & (idx < E)).all()
+    assert all(len(set(r)) == K for r in idx)
+    # rows with finite logits among NaNs still pick a finite maximum first
+    assert idx[4, 0] == 50
+    # a finite row is unaffected
+    np.testing.assert_array_equal(idx[5], route_topk(z[5:6], K)[0][0])
+
+
 def test_route_large_magnitude_and_empty():
     z = np.array([[1e30, -1e30, 3.0e38, -3.0e38, 1.0, 88.0, -88.0, 0.0]], dtype=np.float32)
     _route_check(np.repeat(z, 70, 0), 4)
