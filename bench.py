@@ -2,19 +2,26 @@
 """Throughput of one GPU's share of an expert-parallel MoE layer on MI355X.
 
 One step = route top-K -> dispatch layout -> dispatch -> grouped SwiGLU GEMM
-(routed experts) -> shared expert -> combine, over one batch of seeded
-synthetic input already resident in HBM. Default workload: DeepSeek-V3-shaped
-decode, single-node EP8 share (8 source ranks x 128 tokens, hidden 7168, 256
-experts, top-8, local experts 0-31 + 1 shared, SwiGLU intermediate 2048, bf16).
+(routed experts, shared expert in the same launches) -> combine, over one
+batch of seeded synthetic input already resident in HBM. Default workload (the
+largest single-GPU configuration): DeepSeek-V3-shaped prefill, EP8 share
+(8 source ranks x 4096 tokens, hidden 7168, 256 experts with Zipf-skewed
+routing, top-8, local experts 0-31 + 1 shared, SwiGLU intermediate 2048, bf16,
+count-first compact layout).
 
 Prints one JSON line. ``value`` is MoE-layer tokens per second for this GPU
-(its own 128 tokens per step divided by the step time). ``roofline`` reports
-the dominant kernel against MI355X's published peak, from HIP events around
-each launch on the launching stream. ``cpu_baseline`` times the CPU oracle on
-the host (rank 0, one GPU only) on the bounded sample it names.
+(its own tokens per step divided by the step time). ``roofline`` reports the
+dominant kernel against MI355X's published peak, from HIP events around each
+launch on the launching stream. ``cpu_baseline`` times the CPU oracle on the
+host (rank 0, one GPU only) on the bounded sample it names, with all cores and
+single-threaded. ``extras`` holds the other configurations (decode shares, the
+fixed-rectangle layout of the prefill share), ``overlap`` the shared expert on
+a second stream against the fused launch, and ``microbatch`` the cost of
+running the grouped GEMM as two half batches.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--layout compact|padded] [--no-cpu-baseline] [--copy-calib]
+                       [--layout compact|padded] [--extras LIST|none]
+                       [--no-cpu-baseline] [--copy-calib]
 """
 from __future__ import annotations
 
@@ -35,11 +42,14 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
 # the shared expert runs inside the gemm_up / gemm_down launches
 STEP_NAMES = ("route", "layout", "dispatch", "gemm_up", "gemm_down", "combine")
-KERNEL_OF_STEP = {"gemm_up": "ffn_wide_kernel<up> + ffn_bf16_kernel<up> + ffn_fixup_kernel<up>",
-                  "gemm_down": "ffn_wide_kernel<down> + ffn_bf16_kernel<down> + ffn_fixup_kernel<down>",
+KERNEL_OF_STEP = {"gemm_up": "ffn_wide_kernel<up> + ffn_wide_fixup_kernel<up> (or ffn_bf16_kernel<up> + "
+                             "ffn_fixup_kernel<up> for decode batches)",
+                  "gemm_down": "ffn_wide_kernel<down> + ffn_wide_fixup_kernel<down> (or ffn_bf16_kernel<down> + "
+                               "ffn_fixup_kernel<down>)",
                   "dispatch": "dispatch_kernel", "combine": "combine_kernel", "route": "route_topk_kernel"}
 KERNEL_OF_STEP_FP8 = {"gemm_up": "ffn_fp8_kernel<up> + ffn_fp8_fixup_kernel<up>",
                       "gemm_down": "ffn_fp8_kernel<down> + ffn_fp8_fixup_kernel<down>"}
+DEFAULT_EXTRAS = "dsv3_decode_ep8,dsv3_decode_ep128,kimi_k2_ep8,dsv3_prefill_ep8:padded"
 
 
 # --------------------------------------------------------------------------- perf model
@@ -83,7 +93,7 @@ def algorithmic_model(cfg, counts, row_of, B0):
     B0s = B0 if cfg.shared else 0
     MS = M + B0s  # rows through the expert FFN: routed plus the shared expert's
     model = {
-        "M": M, "U": U, "active_experts": active, "max_rows_per_expert": int(m.max(initial=0)),
+        "M": M, "U": U, "touched": UT, "active_experts": active, "max_rows_per_expert": int(m.max(initial=0)),
         "bytes": {
             "route": N * cfg.n_experts * 4 + N * K * 8,
             "layout": 3 * N * K * 4 + M * 4,
@@ -119,65 +129,315 @@ def _traffic(workload, kernel_step):
     return t.get("hbm_bytes_per_launch")
 
 
-def _cpu_baseline(cfg, d, B0, max_tokens, min_seconds=10.0):
-    """Time the CPU oracle (as it stands) on the host for one step of the same
-    workload, or a token-prefix sample of it, and scale to tokens/s."""
-    import oracle
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        blas_threads = None
-    off = d["src_offsets"]
-    N = int(off[-1])
-    n = min(N, max_tokens)
-    # keep whole sources so the sample has the same shape: a prefix of source ranks
-    s_cnt = int(np.searchsorted(off, n, side="right") - 1)
-    s_cnt = max(s_cnt, 1)
-    n = int(off[s_cnt])
-    sub_off = off[: s_cnt + 1]
+        return None
 
-    class Lazy:
-        def __init__(self, t, codes):
-            self.t, self.codes = t, codes
 
-        def __getitem__(self, g):
-            v = self.t[g]
-            return v.numpy() if self.codes else v.double().numpy()
-
+def _oracle_weights(cfg, d):
+    """The oracle's weight inputs: float64 arrays for bf16/f32 checkpoints
+    (converted once, outside any timing), e4m3fn codes + scales for fp8 (the
+    oracle decodes them itself)."""
     fp8 = cfg.weight == "fp8_e4m3"
-    rw, sw = d["routed"], d["shared"]
-    w13, w2 = Lazy(rw["w13"], fp8), Lazy(rw["w2"], fp8)
-    s13 = rw["s13"].numpy() if fp8 else None
-    s2 = rw["s2"].numpy() if fp8 else None
-    sh = None
-    if sw is not None:
-        sh = (Lazy(sw["w13"], fp8), Lazy(sw["w2"], fp8), sw["s13"].numpy() if fp8 else None,
-              sw["s2"].numpy() if fp8 else None)
+
+    def conv(wd):
+        if wd is None:
+            return None
+        if fp8:
+            return (wd["w13"].numpy(), wd["w2"].numpy(), wd["s13"].numpy(), wd["s2"].numpy())
+        return (wd["w13"].double().numpy(), wd["w2"].double().numpy(), None, None)
+
+    return conv(d["routed"]), conv(d["shared"])
+
+
+def _cpu_time(cfg, d, weights, n, sub_off, B0_sample, min_seconds):
+    import oracle
+    (w13, w2, s13, s2), sh = weights
     x = d["x"][:n].double().numpy()
-    # the sample is repeated until about min_seconds of CPU work (a bounded
-    # sample of 10-30 s), then timed per pass
     reps = 0
     t0 = time.perf_counter()
     while True:
         oracle.moe_layer(x, d["logits"][:n], sub_off, cfg.top_k, cfg.expert_lo, cfg.n_local, w13, w2, s13, s2,
-                         shared=sh, self_range=(0, int(off[1])))
+                         shared=sh, self_range=(0, B0_sample))
         reps += 1
         dt = time.perf_counter() - t0
         if dt >= min_seconds or dt / reps * (reps + 1) > 3 * min_seconds:
-            break
-    full_time = dt / reps * (N / n)
+            return dt, reps
+
+
+def _cpu_baseline(cfg, d, B0, max_tokens, min_seconds=10.0):
+    """Time the CPU oracle (as it stands) on the host for one step of the same
+    workload, on a bounded sample of it, and scale to tokens/s. Once with every
+    BLAS thread, once single-threaded (a smaller sample)."""
+    off = d["src_offsets"]
+    N = int(off[-1])
     try:
-        cores = len(os.sched_getaffinity(0))
+        host_cores = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        cores = os.cpu_count()
-    return {
-        "value": B0 / full_time, "unit": "tokens/s", "cores": blas_threads or cores,
-        "host_cores": cores, "kind": "oracle", "seconds": dt, "passes": reps,
+        host_cores = os.cpu_count()
+    weights = _oracle_weights(cfg, d)
+
+    # all cores: whole source ranks (a prefix), so the sample has the layer's shape
+    n = min(N, max_tokens)
+    s_cnt = max(int(np.searchsorted(off, n, side="right") - 1), 1)
+    n = int(off[s_cnt])
+    dt, reps = _cpu_time(cfg, d, weights, n, off[: s_cnt + 1], int(off[1]), min_seconds)
+    full_time = dt / reps * (N / n)
+    res = {
+        "value": B0 / full_time, "unit": "tokens/s", "cores": _blas_threads() or host_cores,
+        "host_cores": host_cores, "kind": "oracle", "seconds": round(dt, 2), "passes": reps,
         "sample": (f"float64 NumPy oracle, one whole layer step over the first {s_cnt} of {len(off) - 1} source "
                    f"ranks ({n} of {N} tokens, all their local experts, shared expert on the GPU's own "
                    f"{int(off[1])} tokens), repeated {reps} times ({dt:.1f} s); time per pass scaled by {N}/{n}"),
     }
+    # one thread: the first n1 tokens of source 0 (also the shared expert's rows)
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        return res
+    n1 = min(int(off[1]), 256)
+    with threadpool_limits(limits=1):
+        dt1, reps1 = _cpu_time(cfg, d, weights, n1, np.array([0, n1], dtype=np.int32), n1, min_seconds)
+    t1 = dt1 / reps1 * (N / n1)
+    res["single_thread"] = {
+        "value": B0 / t1, "unit": "tokens/s", "cores": 1, "kind": "oracle", "seconds": round(dt1, 2),
+        "passes": reps1,
+        "sample": (f"the same oracle with one BLAS thread over the first {n1} tokens of source rank 0 (their local "
+                   f"experts and the shared expert), repeated {reps1} times ({dt1:.1f} s); time per pass scaled "
+                   f"by {N}/{n1}"),
+    }
+    return res
+
+
+# --------------------------------------------------------------------------- GPU timing
+class Bench:
+    def __init__(self, torch, flush_mb):
+        self.torch = torch
+        self.flush_buf = (torch.ones((flush_mb << 20) // 8, dtype=torch.int64, device="cuda")
+                          if flush_mb > 0 else None)
+        self.flush_sink = torch.zeros((), dtype=torch.int64, device="cuda")
+
+    def flush(self):
+        # between timed steps (never inside the events): a read of a buffer
+        # twice the Infinity Cache, so no step finds the previous one's weights
+        # or activations in a cache. (A read, not a write: written flush data
+        # would sit dirty in the cache and be written back during the next
+        # step.) The previous step's own dirty lines are written back here.
+        if self.flush_buf is not None:
+            self.torch.sum(self.flush_buf, dim=0, out=self.flush_sink)
+
+    def events(self, n):
+        E = self.torch.cuda.Event
+        return [(E(enable_timing=True), E(enable_timing=True)) for _ in range(n)]
+
+    def time_step(self, share, logits, offs, x, out, steps, warmup, graph=True, shared_mode="fused"):
+        """Eager steps with events around every call, then (graph) replays of
+        one captured step; mean times."""
+        torch = self.torch
+        run = lambda ev=None: share.step(logits, offs, x, out, events=ev, shared_mode=shared_mode)
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        names = STEP_NAMES + (("shared",) if shared_mode == "stream" else ())
+        ev = {n: self.events(steps) for n in names}
+        est = self.events(steps)
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.flush()
+            est[i][0].record()
+            run({n: ev[n][i] for n in names})
+            est[i][1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        eager_ms = float(np.mean([a.elapsed_time(b) for a, b in est]))
+        per_call_us = {n: 1e3 * float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n in names}
+        graph_ms = None
+        if graph:
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                run()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run()
+            for _ in range(max(1, warmup)):
+                g.replay()
+            torch.cuda.synchronize()
+            gst = self.events(steps)
+            t0 = time.perf_counter()
+            for i in range(steps):
+                self.flush()
+                gst[i][0].record()
+                g.replay()
+                gst[i][1].record()
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+            graph_ms = float(np.mean([a.elapsed_time(b) for a, b in gst]))
+            del g
+        return {"ms": graph_ms if graph_ms is not None else eager_ms, "ms_eager": eager_ms,
+                "timing": "hip_graph_replay" if graph_ms is not None else "eager", "per_call_us": per_call_us,
+                "wall": wall}
+
+
+def _make_share(cfg, d, layout, *, policy=None, gather=None, blocked=None, weights_from=None, self_range=None):
+    import torch
+    from combine_router_softmax_amd import COMPACT
+    from combine_router_softmax_amd.layer import MoEShare
+    off = d["src_offsets"]
+    N, B0 = int(off[-1]), int(off[1])
+    cap = None if layout == COMPACT else int(np.diff(off).max())
+    act = torch.float32 if cfg.act == "f32" else torch.bfloat16
+    share = MoEShare(n_tokens=N, hidden=cfg.hidden, inter=cfg.inter, n_experts=cfg.n_experts, top_k=cfg.top_k,
+                     n_src=cfg.n_src, expert_lo=cfg.expert_lo, n_local=cfg.n_local, act_dtype=act, layout=layout,
+                     capacity=cap, self_range=self_range or (0, B0), blocked=blocked, gather=gather, policy=policy)
+    if weights_from is not None:
+        share.share_weights_from(weights_from)
+    else:
+        share.set_weights(d["routed"], d["shared"])
+    return share
+
+
+def _dev_inputs(d):
+    import torch
+    return (torch.from_numpy(d["logits"]).cuda(), torch.from_numpy(d["src_offsets"]).cuda(), d["x"].cuda())
+
+
+def _summarize(cfg, share, res, B0):
+    """Algorithmic model of the step's actual routing, per-call rates and the
+    dominant kernel's roofline."""
+    counts = share.lay["counts"].cpu().numpy().astype(np.int64)
+    row_of = share.lay["row_of"].cpu().numpy().astype(np.int64)
+    model = algorithmic_model(cfg, counts, row_of, B0)
+    per_call_us = dict(res["per_call_us"])
+    if share.gather:
+        # the up projection reads its rows from the tokens: no dispatch copy
+        # (its events enclosed no work)
+        model["bytes"]["dispatch"] = 0
+        per_call_us["dispatch"] = 0.0
+    breakdown = {}
+    for n in STEP_NAMES:
+        us = per_call_us[n]
+        b = model["bytes"].get(n, 0)
+        f = model["flops"].get(n, 0)
+        breakdown[n] = {"us": round(us, 2), "GB/s": round(b / us / 1e3, 1) if us > 0 and b else None,
+                        "TFLOP/s": round(f / us / 1e6, 1) if f and us > 0 else None}
+    if share.gather:
+        breakdown["dispatch"]["fused_into"] = "gemm_up"
+    dom = max(("gemm_up", "gemm_down", "dispatch", "combine"), key=lambda n: per_call_us[n])
+    dom_us = per_call_us[dom]
+    flops = model["flops"].get(dom, 0)
+    byts = model["bytes"][dom]
+    mfma_bound = flops > 0 and flops / byts > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if mfma_bound:
+        roof = {"bound": "mfma", "achieved": round(flops / dom_us / 1e6, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(byts / dom_us / 1e3, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = _traffic(cfg.name, dom) if share.layout == 0 else None
+    names = dict(KERNEL_OF_STEP, **(KERNEL_OF_STEP_FP8 if cfg.weight == "fp8_e4m3" else {}))
+    roof["kernel"] = names.get(dom, dom)
+    roof["step"] = dom
+    roof["algorithmic_bytes_per_launch"] = int(byts)
+    roof["flops_per_launch"] = int(flops)
+    roof["avg_launch_us"] = round(dom_us, 2)
+    # the GEMM's other bound, for context (decode GEMMs are graded on HBM, prefill on MFMA)
+    gemm_us = per_call_us["gemm_up"] + per_call_us["gemm_down"]
+    gb = model["bytes"]["gemm_up"] + model["bytes"]["gemm_down"]
+    gf = model["flops"]["gemm_up"] + model["flops"]["gemm_down"]
+    gemm = {"us": round(gemm_us, 2), "frac_hbm": round(gb / gemm_us / 1e3 / HBM_PEAK_GBS, 4),
+            "frac_mfma_bf16": round(gf / gemm_us / 1e6 / BF16_PEAK_TFLOPS, 4)}
+    mv = {"combine": {"GB/s": breakdown["combine"]["GB/s"],
+                      "frac_hbm": round(model["bytes"]["combine"] / per_call_us["combine"] / 1e3 / HBM_PEAK_GBS, 4)}}
+    if not share.gather:
+        dc_bytes = model["bytes"]["dispatch"] + model["bytes"]["combine"]
+        dc_us = per_call_us["dispatch"] + per_call_us["combine"]
+        mv["dispatch_combine"] = {"GB/s": round(dc_bytes / dc_us / 1e3, 1),
+                                  "frac_hbm": round(dc_bytes / dc_us / 1e3 / HBM_PEAK_GBS, 4)}
+    routing = {k: model[k] for k in ("M", "U", "touched", "active_experts", "max_rows_per_expert")}
+    return model, breakdown, roof, gemm, mv, routing
+
+
+def _measure_extra(bench, name, steps, warmup, headline=None):
+    """One more configuration: step time, per-call times, the dominant
+    kernel's roofline, the expert-buffer footprint."""
+    import torch
+    from combine_router_softmax_amd import COMPACT, PADDED
+    from synth import get_config, make_inputs
+    wl, _, lay = name.partition(":")
+    layout = PADDED if lay == "padded" else COMPACT
+    cfg = get_config(wl)
+    if headline is not None and headline[0].name == wl:
+        d = headline[1]
+    else:
+        d = make_inputs(cfg, 0)
+    off = d["src_offsets"]
+    B0 = int(off[1])
+    share = _make_share(cfg, d, layout,
+                        weights_from=headline[2] if headline is not None and headline[0].name == wl else None)
+    logits, offs, x = _dev_inputs(d)
+    out = torch.zeros_like(x)
+    res = bench.time_step(share, logits, offs, x, out, steps, warmup)
+    model, breakdown, roof, gemm, mv, routing = _summarize(cfg, share, res, B0)
+    ent = {"workload": wl, "layout": "padded" if layout == PADDED else "compact", "ms_per_step": round(res["ms"], 4),
+           "tokens_per_s": round(B0 / (res["ms"] / 1e3), 1), "ms_per_step_eager": round(res["ms_eager"], 4),
+           "roofline": {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "kernel", "avg_launch_us")},
+           "gemm": gemm, **mv, "breakdown": {k: v["us"] for k, v in breakdown.items()}, "routing": routing,
+           "expert_buffer_bytes": share.footprint_bytes(), "status_word": int(share.lay["status"].item())}
+    return cfg, d, share, ent
+
+
+def _overlap(bench, cfg, d, share, steps, warmup):
+    """The shared expert fused into the routed launches, against its own calls
+    on the same stream, and on a second stream beside the routed path."""
+    import torch
+    logits, offs, x = _dev_inputs(d)
+    out = torch.zeros_like(x)
+    r = {}
+    for mode in ("fused", "serial", "stream"):
+        res = bench.time_step(share, logits, offs, x, out, steps, warmup, shared_mode=mode)
+        r[mode] = {"ms_per_step": round(res["ms"], 4), "ms_per_step_eager": round(res["ms_eager"], 4)}
+    return r
+
+
+def _microbatch(bench, cfg, d, share, steps, warmup):
+    """The step as two microbatches, each holding half of every source rank's
+    tokens (the pages' two-microbatch overlap), against one step over the whole
+    batch: the grouped GEMM streams the weights once per microbatch."""
+    import torch
+    from combine_router_softmax_amd import COMPACT
+    off = np.asarray(d["src_offsets"], dtype=np.int64)
+    halves = []
+    for h in range(2):
+        idx = np.concatenate([np.arange(off[s] + (off[s + 1] - off[s]) // 2 * h,
+                                        off[s] + ((off[s + 1] - off[s]) // 2 if h == 0 else off[s + 1] - off[s]))
+                              for s in range(len(off) - 1)])
+        b = np.array([((off[s + 1] - off[s]) // 2 if h == 0 else (off[s + 1] - off[s]) - (off[s + 1] - off[s]) // 2)
+                      for s in range(len(off) - 1)])
+        sub = {"logits": np.ascontiguousarray(d["logits"][idx]), "x": d["x"][torch.from_numpy(idx)],
+               "src_offsets": np.concatenate([[0], np.cumsum(b)]).astype(np.int32), "routed": None, "shared": None}
+        halves.append(sub)
+    full = bench.time_step(share, *_dev_inputs(d), torch.zeros_like(d["x"]).cuda(), steps, warmup)
+    r = {"full": {"ms_per_step": round(full["ms"], 4),
+                  "gemm_us": round(full["per_call_us"]["gemm_up"] + full["per_call_us"]["gemm_down"], 2)}}
+    tot_ms = tot_gemm = 0.0
+    for h, sub in enumerate(halves):
+        s = _make_share(cfg, sub, COMPACT, weights_from=share)
+        res = bench.time_step(s, *_dev_inputs(sub), torch.zeros_like(sub["x"]).cuda(), steps, warmup)
+        g = res["per_call_us"]["gemm_up"] + res["per_call_us"]["gemm_down"]
+        r[f"half{h}"] = {"tokens": int(sub["src_offsets"][-1]), "ms_per_step": round(res["ms"], 4),
+                         "gemm_us": round(g, 2)}
+        tot_ms += res["ms"]
+        tot_gemm += g
+        del s
+    r["two_halves_ms"] = round(tot_ms, 4)
+    r["gemm_penalty"] = round(tot_gemm / (r["full"]["gemm_us"]) - 1.0, 4)
+    return r
 
 
 def main(argv=None):
@@ -185,14 +445,20 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="dsv3_decode_ep8")
+    ap.add_argument("--workload", default="dsv3_prefill_ep8")
     ap.add_argument("--layout", choices=["compact", "padded"], default="compact")
     ap.add_argument("--gemm-policy", choices=["layer", "auto", "wide", "stream_k"], default="layer",
                     help="grouped-GEMM kernel choice (default: the layer's own, from its shape)")
     ap.add_argument("--gather", choices=["auto", "on", "off"], default="auto",
-                    help="up projection reads its rows from the tokens (no dispatch copy); auto: decode batches")
+                    help="up projection reads its rows from the tokens (no dispatch copy); auto: the layer's choice")
     ap.add_argument("--xe-layout", choices=["auto", "rows", "blocked"], default="auto",
                     help="storage of the expert rows (auto: the layer's choice)")
+    ap.add_argument("--shared-mode", choices=["fused", "serial", "stream"], default="fused",
+                    help="shared expert inside the routed launches, after them, or on a second stream")
+    ap.add_argument("--extras", default=DEFAULT_EXTRAS,
+                    help="comma-separated workloads[:padded] measured after the headline, or 'none'")
+    ap.add_argument("--extra-steps", type=int, default=20)
+    ap.add_argument("--no-overlap", action="store_true", help="skip the shared-expert stream and microbatch study")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of replays of a HIP graph of one step")
@@ -225,9 +491,9 @@ def main(argv=None):
 
     import combine_router_softmax_amd as moe
     from combine_router_softmax_amd import COMPACT, PADDED
-    from combine_router_softmax_amd.layer import MoEShare
     from synth import get_config, make_inputs
 
+    moe.lib()  # raises if the HIP library is missing: there is no other path
     cfg = get_config(args.workload)
     t_gen = time.perf_counter()
     d = make_inputs(cfg, 0)
@@ -235,122 +501,39 @@ def main(argv=None):
     off = d["src_offsets"]
     N, B0 = int(off[-1]), int(off[1])
     layout = COMPACT if args.layout == "compact" else PADDED
-    cap = None if layout == COMPACT else int(np.diff(off).max())
-    act = torch.float32 if cfg.act == "f32" else torch.bfloat16
-    share = MoEShare(n_tokens=N, hidden=cfg.hidden, inter=cfg.inter, n_experts=cfg.n_experts, top_k=cfg.top_k,
-                     n_src=cfg.n_src, expert_lo=cfg.expert_lo, n_local=cfg.n_local, act_dtype=act, layout=layout,
-                     capacity=cap, self_range=(0, B0),
-                     blocked=None if args.xe_layout == "auto" else args.xe_layout == "blocked",
-                     gather=None if args.gather == "auto" else args.gather == "on",
-                     policy={"layer": None, "auto": moe.GEMM_AUTO, "wide": moe.GEMM_WIDE,
-                             "stream_k": moe.GEMM_STREAM_K}[args.gemm_policy])
-    share.set_weights(d["routed"], d["shared"])
-    logits = torch.from_numpy(d["logits"]).cuda()
-    offs = torch.from_numpy(off).cuda()
-    x = d["x"].cuda()
+    share = _make_share(cfg, d, layout,
+                        blocked=None if args.xe_layout == "auto" else args.xe_layout == "blocked",
+                        gather=None if args.gather == "auto" else args.gather == "on",
+                        policy={"layer": None, "auto": moe.GEMM_AUTO, "wide": moe.GEMM_WIDE,
+                                "stream_k": moe.GEMM_STREAM_K}[args.gemm_policy])
+    logits, offs, x = _dev_inputs(d)
     out = torch.zeros_like(x)
     torch.cuda.synchronize()
-
-    for _ in range(args.warmup):
-        share.step(logits, offs, x, out)
-    torch.cuda.synchronize()
-
-    # between timed steps (never inside the events): a read of a buffer twice
-    # the Infinity Cache, so no step finds the previous one's weights or
-    # activations in a cache. (A read, not a write: written flush data would
-    # sit dirty in the cache and be written back during the next step.) The
-    # previous step's own dirty lines are written back during the flush.
-    flush_buf = torch.ones((args.flush_mb << 20) // 8, dtype=torch.int64, device="cuda") if args.flush_mb > 0 else None
-    flush_sink = torch.zeros((), dtype=torch.int64, device="cuda")
-
-    def flush():
-        if flush_buf is not None:
-            torch.sum(flush_buf, dim=0, out=flush_sink)
-
-    def step_events(n):
-        return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-
-    # per-call timing: eager steps with events around each call
-    ev = {n: step_events(args.steps) for n in STEP_NAMES}
-    est = step_events(args.steps)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        flush()
-        est[i][0].record()
-        share.step(logits, offs, x, out, events={n: ev[n][i] for n in STEP_NAMES})
-        est[i][1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    eager_ms = float(np.mean([a.elapsed_time(b) for a, b in est]))
-    per_call_us = {n: 1e3 * float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n in STEP_NAMES}
-
-    # the step as one HIP graph (one graph per batch shape, as the pages do with
-    # CUDA graphs): same kernels, no host launch gaps
-    graph_ms = None
-    if not args.eager:
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            share.step(logits, offs, x, out)
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            share.step(logits, offs, x, out)
-        for _ in range(max(1, args.warmup)):
-            graph.replay()
-        torch.cuda.synchronize()
-        gst = step_events(args.steps)
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            flush()
-            gst[i][0].record()
-            graph.replay()
-            gst[i][1].record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        graph_ms = float(np.mean([a.elapsed_time(b) for a, b in gst]))
-    ms_per_step = graph_ms if graph_ms is not None else eager_ms
+    bench = Bench(torch, args.flush_mb)
+    res = bench.time_step(share, logits, offs, x, out, args.steps, args.warmup, graph=not args.eager,
+                          shared_mode=args.shared_mode)
+    print(f"# headline {cfg.name}: {res['ms']:.4f} ms/step", file=sys.stderr, flush=True)
+    ms_per_step = res["ms"]
     st = int(share.lay["status"].item())
+    model, breakdown, roof, gemm, mv, routing = _summarize(cfg, share, res, B0)
 
-    counts = share.lay["counts"].cpu().numpy().astype(np.int64)
-    row_of = share.lay["row_of"].cpu().numpy().astype(np.int64)
-    model = algorithmic_model(cfg, counts, row_of, B0)
-    if share.gather:
-        # the up projection reads its rows from the tokens: no dispatch copy
-        # (its events enclosed no work)
-        model["bytes"]["dispatch"] = 0
-        per_call_us["dispatch"] = 0.0
-    breakdown = {}
-    for n in STEP_NAMES:
-        us = per_call_us[n]
-        b = model["bytes"].get(n, 0)
-        f = model["flops"].get(n, 0)
-        breakdown[n] = {"us": round(us, 2), "GB/s": round(b / us / 1e3, 1) if us > 0 else None,
-                        "TFLOP/s": round(f / us / 1e6, 1) if f and us > 0 else None}
-    if share.gather:
-        breakdown["dispatch"]["fused_into"] = "gemm_up"
-    dc_bytes = model["bytes"]["dispatch"] + model["bytes"]["combine"]
-    dc_us = per_call_us["dispatch"] + per_call_us["combine"]
-
-    dom = max(("gemm_up", "gemm_down", "dispatch", "combine"), key=lambda n: per_call_us[n])
-    dom_us = per_call_us[dom]
-    flops = model["flops"].get(dom, 0)
-    byts = model["bytes"][dom]
-    mfma_bound = flops > 0 and flops / byts > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    if mfma_bound:
-        roof = {"bound": "mfma", "achieved": round(flops / dom_us / 1e6, 2), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": round(byts / dom_us / 1e3, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = _traffic(cfg.name, dom)
-    names = dict(KERNEL_OF_STEP, **(KERNEL_OF_STEP_FP8 if cfg.weight == "fp8_e4m3" else {}))
-    roof["kernel"] = names.get(dom, dom)
-    roof["algorithmic_bytes_per_launch"] = int(byts)
-    roof["flops_per_launch"] = int(flops)
-    roof["avg_launch_us"] = round(dom_us, 2)
+    extras = {}
+    headline = (cfg, d, share)
+    if args.extras and args.extras != "none":
+        for name in args.extras.split(","):
+            t0 = time.perf_counter()
+            e_cfg, e_d, e_share, ent = _measure_extra(bench, name, args.extra_steps, 3, headline)
+            ent["wall_s"] = round(time.perf_counter() - t0, 1)
+            extras[name] = ent
+            print(f"# extra {name}: {ent['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
+            if not args.no_overlap and name in ("dsv3_decode_ep8", "kimi_k2_ep8"):
+                ent["overlap"] = _overlap(bench, e_cfg, e_d, e_share, args.extra_steps, 3)
+                ent["microbatch"] = _microbatch(bench, e_cfg, e_d, e_share, args.extra_steps, 3)
+                print(f"# overlap and microbatch {name} done", file=sys.stderr, flush=True)
+            del e_share
+            if e_d is not d:
+                del e_d
+            torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -365,9 +548,9 @@ def main(argv=None):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
-        "timing": "hip_graph_replay" if graph_ms is not None else "eager",
+        "timing": res["timing"],
         "cache_flush_mb": args.flush_mb,
-        "ms_per_step_eager": round(eager_ms, 4),
+        "ms_per_step_eager": round(res["ms_eager"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -375,18 +558,22 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": cfg.name, "layout": args.layout,
                    "xe_layout": "gathered" if share.gather else "blocked" if share.blocked else "rows",
+                   "shared_mode": args.shared_mode,
                    "global_batch": N, "tokens_per_gpu": B0,
                    "source_ranks": cfg.n_src, "hidden": cfg.hidden, "n_experts": cfg.n_experts,
                    "top_k": cfg.top_k, "local_experts": cfg.n_local, "shared_expert": cfg.shared,
-                   "inter": cfg.inter, "weights": cfg.weight, "parallelism": f"ep{cfg.n_experts // cfg.n_local}"},
+                   "inter": cfg.inter, "weights": cfg.weight, "zipf": cfg.zipf,
+                   "parallelism": f"ep{cfg.n_experts // cfg.n_local}"},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "dispatch_combine": {"GB/s": round(dc_bytes / dc_us / 1e3, 1), "frac_hbm": round(dc_bytes / dc_us / 1e3 /
-                                                                                        HBM_PEAK_GBS, 4)},
+        "gemm": gemm,
+        **mv,
         "breakdown": breakdown,
-        "routing": {k: model[k] for k in ("M", "U", "active_experts", "max_rows_per_expert")},
+        "routing": routing,
+        "expert_buffer_bytes": share.footprint_bytes(),
         "status_word": st,
-        "wall_s": round(wall, 3),
+        "extras": extras,
+        "wall_s": round(res["wall"], 3),
         "input_gen_s": round(t_gen, 2),
     }
     print(json.dumps(line), flush=True)

@@ -143,6 +143,29 @@ class MoEShare:
                          shared=None if x is None else self._shared_arg(x), w_format=self.w_format,
                          a_layout=self.a_layout, rows=self.R, policy=self.policy, **extra)
 
+    def share_weights_from(self, other: "MoEShare"):
+        """Use another share's (already uploaded and packed) weights: a second
+        share over a different batch of the same layer, e.g. a microbatch."""
+        self.w_format, self.w, self.sw = other.w_format, other.w, other.sw
+        wdt = self.w["w13"].dtype
+        B0 = self.self_hi - self.self_lo
+        se = SharedExpert(rows=B0 if self.sw is not None else 0)
+        desc = gemm_desc(self.L, self.H, self.I, self.act_dtype, wdt, self.layout, self.S, self.capacity, self.R,
+                         shared=se, w_format=self.w_format, a_layout=self.a_layout, policy=self.policy)
+        self.ws = torch.zeros(moe_grouped_gemm_workspace(desc), dtype=torch.uint8, device=self.dev)
+        if self.sw is not None:
+            sdesc = gemm_desc(1, self.H, self.I, self.act_dtype, self.sw["w13"].dtype, COMPACT, 1, 0, max(B0, 1),
+                              w_format=self.w_format)
+            self.sws = torch.zeros(moe_grouped_gemm_workspace(sdesc), dtype=torch.uint8, device=self.dev)
+
+    def footprint_bytes(self) -> int:
+        """Device bytes of the per-step expert buffers (xe, ye and the GEMM
+        workspace with h and the partial sums): what the layout choice costs."""
+        n = self.ye.numel() * self.ye.element_size() + self.ws.numel()
+        if self.xe is not None:
+            n += self.xe.numel() * self.xe.element_size()
+        return int(n)
+
     def shared_gemm(self, x, stage=GG_FULL):
         if self.sw is None or self.self_hi <= self.self_lo:
             return
@@ -156,12 +179,20 @@ class MoEShare:
         moe_combine(self.ye[: max(self.R, 1)] if self.R else self.ye[:0], self.lay["row_of"], self.topk_w, out, sy,
                     self.self_lo, self.self_hi)
 
-    def step(self, logits, src_offsets, x, out, events: Optional[dict] = None, fused_shared: bool = True):
+    def step(self, logits, src_offsets, x, out, events: Optional[dict] = None, fused_shared: bool = True,
+             shared_mode: Optional[str] = None):
         """One full pass. ``events`` maps step names to (start, end) CUDA events
-        recorded around each call on the current stream. With ``fused_shared``
-        the shared expert runs inside the routed grouped-GEMM launches; otherwise
-        as calls of its own. Gathering, the dispatch copy is left out (its
-        events, if any, enclose no work)."""
+        recorded around each call. ``shared_mode`` places the shared expert:
+        "fused" (default) inside the routed grouped-GEMM launches; "serial" as
+        calls of its own on the same stream after the routed GEMM; "stream" as
+        calls of its own on a second stream, concurrent with route, layout and
+        the routed GEMM, joined before the combine (the pages overlap it with
+        the dispatch). ``fused_shared=False`` is "serial". Gathering, the
+        dispatch copy is left out (its events, if any, enclose no work)."""
+        mode = shared_mode or ("fused" if fused_shared else "serial")
+        if mode not in ("fused", "serial", "stream"):
+            raise ValueError(f"unknown shared_mode {mode}")
+
         def run(name, fn):
             if events is not None and name in events:
                 events[name][0].record()
@@ -170,15 +201,25 @@ class MoEShare:
             else:
                 fn()
 
+        cur = side = None
+        if mode == "stream" and self.sw is not None and self.self_hi > self.self_lo:
+            if getattr(self, "_side", None) is None:
+                self._side = torch.cuda.Stream(device=self.dev)  # default priority
+            cur, side = torch.cuda.current_stream(self.dev), self._side
+            side.wait_stream(cur)
+            with torch.cuda.stream(side):
+                run("shared", lambda: self.shared_gemm(x, GG_FULL))
         run("route", lambda: self.route(logits))
         run("layout", lambda: self.layout_step(src_offsets))
         run("dispatch", (lambda: None) if self.gather else (lambda: self.dispatch(x)))
-        xs = x if fused_shared else None
+        xs = x if mode == "fused" else None
         run("gemm_up", lambda: self.gemm(GG_UP, xs, src=x))
         run("gemm_down", lambda: self.gemm(GG_DOWN, xs, src=x))
-        if not fused_shared:
+        if mode == "serial":
             run("shared_up", lambda: self.shared_gemm(x, GG_UP))
             run("shared_down", lambda: self.shared_gemm(x, GG_DOWN))
+        if side is not None:
+            cur.wait_stream(side)
         run("combine", lambda: self.combine(out))
         return out
 
