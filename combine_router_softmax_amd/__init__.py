@@ -75,6 +75,7 @@ _SIGNATURES = {
     "moe_layout_rows": (_I64, [ctypes.POINTER(LayoutDesc)]),
     "moe_dispatch_layout_workspace": (_SZ, [ctypes.POINTER(LayoutDesc)]),
     "moe_dispatch_layout": (_I, [ctypes.POINTER(LayoutDesc), _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_dispatch_layout_noalloc": (_I, [ctypes.POINTER(LayoutDesc), _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_dispatch": (_I, [_P, _I, _I, _I, _I, _P, _I64, _P, _P]),
     "moe_dispatch_blocked": (_I, [_P, _I, _I, _I, _I, _P, _I64, _P, _P]),
     "moe_grouped_gemm_workspace": (_SZ, [ctypes.POINTER(GGemmDesc)]),
@@ -223,6 +224,37 @@ def moe_dispatch_layout(topk_idx: torch.Tensor, src_offsets: torch.Tensor, n_exp
                                      _ptr(o["expert_off"]), _ptr(o["row_of"]), _ptr(o["row_token"]),
                                      _ptr(o["status"]), _ptr(o["ws"]), o["ws"].numel(), _stream()),
            "moe_dispatch_layout")
+    o["rows"] = R
+    return o
+
+
+def moe_dispatch_layout_noalloc(topk_idx: torch.Tensor, src_offsets: torch.Tensor, n_experts: int, expert_lo: int,
+                                n_local: int, layout: int, capacity: int, out: Optional[dict] = None) -> dict:
+    """moe_dispatch_layout without a workspace argument: the library's fixed
+    per-GPU scratch array serves instead (calls that overlap on one GPU race).
+    ``out`` may hold preallocated ``counts, expert_off, row_of, row_token,
+    status``; the C call itself allocates nothing."""
+    _dev(topk_idx, "topk_idx", torch.int32)
+    _dev(src_offsets, "src_offsets", torch.int32)
+    N, K = topk_idx.shape
+    S = src_offsets.numel() - 1
+    d = _layout_desc(N, K, n_experts, S, expert_lo, n_local, layout, capacity)
+    R = int(lib().moe_layout_rows(ctypes.byref(d)))
+    if R < 0:
+        raise MoeError("moe_dispatch_layout_noalloc: invalid descriptor")
+    dev = topk_idx.device
+    o = dict(out) if out else {}
+    shapes = {"counts": (n_local, S), "expert_off": (n_local + 1,), "row_of": (N * K,), "row_token": (max(R, 1),),
+              "status": (1,)}
+    for k, shape in shapes.items():
+        if k not in o:
+            o[k] = torch.empty(shape, dtype=torch.int32, device=dev)
+        _dev(o[k], k, torch.int32)
+        _need(o[k].numel() >= int(np.prod(shape)), f"{k} holds {o[k].numel()} elements, fewer than {np.prod(shape)}")
+    _on_gpu(topk_idx=topk_idx, src_offsets=src_offsets, **{k: o[k] for k in shapes})
+    _check(lib().moe_dispatch_layout_noalloc(ctypes.byref(d), _ptr(topk_idx), _ptr(src_offsets), _ptr(o["counts"]),
+                                             _ptr(o["expert_off"]), _ptr(o["row_of"]), _ptr(o["row_token"]),
+                                             _ptr(o["status"]), _stream()), "moe_dispatch_layout_noalloc")
     o["rows"] = R
     return o
 

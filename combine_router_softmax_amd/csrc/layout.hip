@@ -27,6 +27,8 @@
 // Tiles never straddle a source rank, so the fixed-rectangle rank inside a
 // (expert, source) region is the expert's running count minus its count at
 // the start of the source.
+#include <mutex>
+
 #include "moe_common.hpp"
 
 namespace moe {
@@ -384,6 +386,49 @@ MOE_API size_t moe_dispatch_layout_workspace(const moe_layout_desc_t* d) {
   if (!layout_desc_ok(d)) return 0;
   const size_t tcap = size_t(tile_cap(d->n_tokens, d->n_src));
   return align_up((size_t(d->n_local) * tcap + 2 * size_t(d->n_local)) * sizeof(int32_t), 256);
+}
+
+// Scratch of the allocation-free entry point: the layout's tile-count
+// workspace in a file-scope device array, one copy per GPU, kept until the
+// process ends. The host never passes the array's name to a kernel (in host
+// code it only stands for the symbol): its device address is looked up once
+// per device with hipGetSymbolAddress and cached.
+constexpr size_t kLayoutScratchBytes = size_t(4) << 20;
+__device__ __align__(256) char layout_scratch[kLayoutScratchBytes];
+
+namespace {
+constexpr int kScratchMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[kScratchMaxDevices] = {};
+
+// Device address of the current device's scratch array (nullptr on failure).
+void* layout_scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(layout_scratch)) != hipSuccess || !ptr) return nullptr;
+    scratch_ptr[dev] = ptr;
+  }
+  return scratch_ptr[dev];
+}
+}  // namespace
+
+MOE_API moe_status_t moe_dispatch_layout_noalloc(const moe_layout_desc_t* d, const int32_t* topk_idx,
+                                                 const int32_t* src_offsets, int32_t* counts, int32_t* expert_off,
+                                                 int32_t* row_of, int32_t* row_token, int32_t* status,
+                                                 hipStream_t stream) {
+  if (!layout_desc_ok(d)) return MOE_ERR_INVALID_ARG;
+  if (!layout_desc_supported(d)) return MOE_ERR_UNSUPPORTED;
+  const size_t need = moe_dispatch_layout_workspace(d);
+  if (need > kLayoutScratchBytes) return MOE_ERR_UNSUPPORTED;  // beyond the fixed scratch
+  void* ws = layout_scratch_ptr();
+  if (!ws) return MOE_ERR_HIP;
+  // every word of the scratch a call reads is written earlier in the same
+  // call (tile counts, then their prefixes), so nothing needs clearing
+  return moe_dispatch_layout(d, topk_idx, src_offsets, counts, expert_off, row_of, row_token, status, ws, need,
+                             stream);
 }
 
 MOE_API moe_status_t moe_dispatch_layout(const moe_layout_desc_t* d, const int32_t* topk_idx,

@@ -33,7 +33,9 @@
  *  - Results are deterministic: no floating-point atomics anywhere, and the
  *    integer layout is bit-reproducible.
  *  - No global mutable state apart from a per-device cache of the compute-unit
- *    count; calls from several host threads are safe.
+ *    count and, for moe_dispatch_layout_noalloc only, its per-GPU scratch
+ *    array and the cached address of it; calls from several host threads are
+ *    safe (except overlapping moe_dispatch_layout_noalloc calls on one GPU).
  */
 #ifndef MOE_H
 #define MOE_H
@@ -159,6 +161,22 @@ size_t moe_dispatch_layout_workspace(const moe_layout_desc_t* d);
 moe_status_t moe_dispatch_layout(const moe_layout_desc_t* d, const int32_t* topk_idx, const int32_t* src_offsets,
                                  int32_t* counts, int32_t* expert_off, int32_t* row_of, int32_t* row_token,
                                  int32_t* status, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* moe_dispatch_layout without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments and results as
+ * moe_dispatch_layout; the scratch is a fixed 4 MiB array in the library's
+ * device data, one copy per GPU, held until the process ends. The call itself
+ * allocates and frees nothing. Requests whose workspace
+ * (moe_dispatch_layout_workspace) exceeds 4 MiB return MOE_ERR_UNSUPPORTED
+ * before anything is enqueued. Every call on one GPU shares that GPU's array:
+ * calls that overlap in time on one GPU (several streams, several host
+ * threads) race and give undefined results; calls ordered on one stream are
+ * safe (each call writes every scratch word it reads). Returns MOE_ERR_HIP if
+ * the array's device address cannot be found. */
+moe_status_t moe_dispatch_layout_noalloc(const moe_layout_desc_t* d, const int32_t* topk_idx,
+                                         const int32_t* src_offsets, int32_t* counts, int32_t* expert_off,
+                                         int32_t* row_of, int32_t* row_token, int32_t* status, hipStream_t stream);
 
 /* ------------------------------------------------------------------ dispatch
  * Copy each token row into every slot the layout gave it: xe[row_of[t*K+k]] =
