@@ -1,0 +1,500 @@
+// Grouped-GEMM internals shared by the kernel translation units
+// (gemm_wide.hip, gemm_bf16.hip, gemm_fp8.hip) and the host code in
+// grouped_gemm.hip. Internal header.
+#pragma once
+
+#include <algorithm>
+#include <type_traits>
+
+#include "moe_common.hpp"
+
+namespace moe {
+
+struct GemmArgs {
+  // routed experts
+  const void* a;              // [rows, K] activations (x for up, h for down)
+  int64_t rows;               // R
+  const int32_t* counts;      // [G, S] (padded)
+  const int32_t* group_off;   // [G + 1] (compact)
+  int G, S, C, layout;
+  const void* w;              // [G, n_w_rows, K]
+  const float* s;             // fp8: [G, n_w_rows/128, K/128]
+  void* out;                  // [rows, n_out]
+  // optional shared expert: one more group (index G) over rows [0, sh_rows) of its own buffers
+  const void* sh_a;
+  const void* sh_w;
+  const float* sh_s;
+  void* sh_out;
+  int sh_rows;                // 0 = none
+  int n_w_rows;               // 2I (up) or H (down)
+  int K;                      // reduction length
+  int n_out;                  // I (up) or H (down)
+  int n_tiles_n;              // N tiles per expert (decode-shaped kernels)
+  int packed;                 // weights in the packed (load-order) layout
+  int wide_min;               // groups with at least this many rows may go to the wide-tile kernel ...
+  int wide_min_tiles;         // ... if the wide groups make at least this many wide tiles
+  int a_blk, sh_a_blk;        // routed / shared activations in the 16-row blocked layout
+  int out_blk;                // outputs (routed and shared) in the 16-row blocked layout
+  const int32_t* a_rows;      // routed input row r is row a_rows[r] of a (nullptr: row r)
+  int a_nrows;                // rows of a when gathering
+};
+
+// Launchers of the three MFMA kernel families (each in its own translation
+// unit): the main kernel of the stage and its fix-up kernel on `stream`.
+moe_status_t launch_wide(const GemmArgs& p, int kind, float* parts, hipStream_t stream);
+moe_status_t launch_bf16(const GemmArgs& p, int kind, float* parts, hipStream_t stream);
+moe_status_t launch_fp8(const GemmArgs& p, int kind, float* parts, hipStream_t stream);
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kGemmThreads = 256;
+constexpr int kMaxGemmThreads = 512;  // the fp8 decode kernel's workgroup
+constexpr int kBM = 128;            // rows per tile
+constexpr int kMB = kBM / 32;       // 32-row MFMA blocks per tile
+constexpr int kKC = 128;            // reduction chunk
+constexpr int kMaxGroups = 512;
+constexpr int kGemmMaxSrc = 512;
+
+enum { kUp = 0, kDown = 1 };
+
+// wide-tile kernel (groups with many rows)
+constexpr int kWN = 256;             // weight rows per wide tile
+constexpr int kWM = 256;             // activation rows per wide tile
+constexpr int kWK = 32;              // reduction depth per LDS stage (32 or 64)
+constexpr int kWideGrid = 256;       // one workgroup per compute unit
+constexpr int kWideMinRows = 128;    // a group with at least this many rows may take the wide kernel ...
+constexpr int kWideMinTiles = 16;    // ... if the launch then has at least this many wide tiles
+constexpr int kNoWide = 0x7fffffff;  // wide_min when the wide kernel is not used
+
+
+// 16-row blocked activation layout: element (r, c) of an [R, K] matrix sits
+// at ((r / 16) * (K / 32) + c / 32) * 512 + (r % 16) * 32 + c % 32, i.e.
+// blocks of 16 rows x 32 columns (1 KiB of bf16) stored contiguously, the
+// blocks of one 16-row group in column order. A wave load of 16 rows x 32
+// columns is then one contiguous KiB instead of 16 separate 64-byte pieces.
+__device__ __forceinline__ size_t blk_row_base(int64_t r, int K) {
+  return size_t(r >> 4) * size_t(K >> 5) * 512 + size_t(r & 15) * 32;
+}
+__device__ __forceinline__ size_t act_off(int64_t r, int c, int K, bool blk) {
+  return blk ? blk_row_base(r, K) + size_t(c >> 5) * 512 + (c & 31) : size_t(r) * K + c;
+}
+
+constexpr int kGatherRows = 256;  // tile rows of the kernels that gather (bf16 64, fp8 96, wide 256)
+
+struct Sched {
+  int tile_start[kMaxGroups + 2];
+  int m[kMaxGroups + 1];
+  int seg[kGemmMaxSrc + 1];
+  union {
+    int rowmap[256];
+    int tmp[kMaxGemmThreads];  // scan scratch: every scan ends before a rowmap is written
+  };
+  int arow[kGatherRows];       // gathering: the input row of each tile row
+  int cur_seg_group;
+  int wide_tiles;
+};
+
+// Rows per group from the device counts (clamped so every row stays inside
+// [0, rows)), then the exclusive prefix of tiles per group. Schedule order:
+// the shared expert first (its rows are always present, so its tiles start
+// with the first wave of workgroups instead of forming a tail), then the
+// routed experts. Only groups on the kernel's side get tiles: the launch goes
+// wide if the groups with m >= wide_min make at least wide_min_tiles wide
+// tiles, and then every group is wide; otherwise the stream-K kernel takes
+// them all. Both kernels evaluate this identically from the same counts.
+// Returns the tile count. All threads must call it.
+template <int NT = kGemmThreads>
+__device__ __forceinline__ int build_schedule(const GemmArgs& p, int bm, int ntn, bool wide, Sched& sh) {
+  const int tid = threadIdx.x;
+  const int nsh = p.sh_rows > 0 ? 1 : 0;
+  const int Gt = p.G + nsh;
+  if (p.layout == MOE_LAYOUT_COMPACT) {
+    for (int g = tid; g < p.G; g += NT) {
+      const int64_t lo = min<int64_t>(max<int64_t>(p.group_off[g], 0), p.rows);
+      const int64_t hi = min<int64_t>(max<int64_t>(p.group_off[g + 1], lo), p.rows);
+      sh.m[nsh + g] = int(hi - lo);
+    }
+  } else {
+    for (int g = tid; g < p.G; g += NT) sh.m[nsh + g] = 0;
+    __syncthreads();
+    for (int i = tid; i < p.G * p.S; i += NT) {
+      const int c = min(max(p.counts[i], 0), p.C);
+      if (c) atomicAdd(&sh.m[nsh + i / p.S], c);
+    }
+  }
+  if (tid == 0) {
+    if (nsh) sh.m[0] = p.sh_rows;
+    sh.wide_tiles = 0;
+  }
+  __syncthreads();
+  if (p.wide_min != kNoWide) {
+    int wt = 0;
+    for (int g = tid; g < Gt; g += NT)
+      if (sh.m[g] >= p.wide_min) wt += (sh.m[g] + kWM - 1) / kWM * (p.n_w_rows / kWN);
+    if (wt) atomicAdd(&sh.wide_tiles, wt);
+    __syncthreads();
+  }
+  // once the launch qualifies, every group takes the wide kernel (one launch
+  // does all the work; small groups are cheap ragged tiles there)
+  const int wide_min = sh.wide_tiles >= p.wide_min_tiles ? 1 : kNoWide;
+  for (int g = tid; g < Gt; g += NT) {
+    const int m = sh.m[g];
+    sh.tile_start[g] = ((m >= wide_min) == wide) ? (m + bm - 1) / bm * ntn : 0;
+  }
+  __syncthreads();
+  const int total = block_scan_lds<false, NT>(sh.tile_start, Gt, sh.tmp);
+  if (tid == 0) {
+    sh.tile_start[Gt] = total;
+    sh.cur_seg_group = -1;
+  }
+  __syncthreads();
+  // uniform (every thread read the same LDS word): scalar registers, so the
+  // work split derived from it stays scalar
+  return __builtin_amdgcn_readfirstlane(total);
+}
+
+// c ? a : b on values: the operands are read before the choice. (On the two
+// fields themselves the conditional is an lvalue, which the compiler may
+// lower to a load from a chosen field address; that keeps the whole kernel
+// argument block in scratch memory.)
+template <class T>
+__device__ __forceinline__ T pick(bool c, T a, T b) {
+  return c ? a : b;
+}
+
+struct Tile {
+  int g;        // routed expert index (unused for the shared expert)
+  int we;       // expert index inside the weight tensor of the tile's problem
+  bool shared;
+  int nt, r0, nrows;
+  int mtiles;   // row tiles of the tile's group (1: its weights are read once)
+};
+
+// Tile order inside a group. Default: row tiles fastest (consecutive tiles
+// share a weight block). BLOCKED: the N tiles are cut into blocks of nbw (4
+// when they divide evenly), and inside a block the order is (row tile, N
+// tile); so any 32 consecutive tiles cover a compact rectangle of row tiles x
+// N tiles (8 x 4 when the group has 8 row tiles), i.e. 12 distinct operand
+// slabs instead of 2 + 16 (N fastest) or 32 + 1 (rows fastest).
+template <bool BLOCKED = false>
+__device__ __forceinline__ Tile decode_tile(const GemmArgs& p, int bm, int ntn, const Sched& sh, int t) {
+  const int nsh = p.sh_rows > 0 ? 1 : 0;
+  const int Gt = p.G + nsh;
+  int lo = 0, hi = Gt;  // last q with tile_start[q] <= t
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (sh.tile_start[mid] <= t) lo = mid;
+    else hi = mid;
+  }
+  Tile tl;
+  tl.shared = lo < nsh;
+  tl.g = tl.shared ? 0 : lo - nsh;
+  tl.we = tl.g;
+  const int local = t - sh.tile_start[lo];
+  const int mtiles = (sh.m[lo] + bm - 1) / bm;
+  tl.mtiles = mtiles;
+  if (BLOCKED) {
+    const int nbw = ntn % 4 == 0 ? 4 : (ntn % 2 == 0 ? 2 : 1);
+    const int blk = local / (nbw * mtiles), rem = local % (nbw * mtiles);
+    tl.nt = blk * nbw + rem % nbw;
+    tl.r0 = (rem / nbw) * bm;
+  } else {
+    tl.nt = local / mtiles;
+    tl.r0 = (local % mtiles) * bm;
+  }
+  tl.nrows = min(bm, sh.m[lo] - tl.r0);
+  // every caller passes a workgroup-uniform t, so the fields are uniform; the
+  // compiler cannot see that through the LDS reads: scalar registers (loop
+  // bounds and weight addresses derived from them then stay scalar)
+  tl.g = __builtin_amdgcn_readfirstlane(tl.g);
+  tl.we = __builtin_amdgcn_readfirstlane(tl.we);
+  tl.shared = __builtin_amdgcn_readfirstlane(int(tl.shared)) != 0;
+  tl.nt = __builtin_amdgcn_readfirstlane(tl.nt);
+  tl.r0 = __builtin_amdgcn_readfirstlane(tl.r0);
+  tl.nrows = __builtin_amdgcn_readfirstlane(tl.nrows);
+  tl.mtiles = __builtin_amdgcn_readfirstlane(tl.mtiles);
+  return tl;
+}
+
+// Physical row of each of the tile's rows (-1 past the group's rows).
+template <int NT = kGemmThreads>
+__device__ __forceinline__ void build_rowmap(const GemmArgs& p, const Tile& tl, int bm, Sched& sh,
+                                             bool input_rows = false) {
+  const int tid = threadIdx.x;
+  // gathering (kernels that read their input through sh.arow): the input row
+  // of each present row, clamped into a's rows
+  const bool gat = input_rows && p.a_rows != nullptr && !tl.shared && bm <= kGatherRows;
+  auto put = [&](int phys) {
+    sh.rowmap[tid] = phys;
+    if (gat) sh.arow[tid] = phys >= 0 ? min(max(p.a_rows[phys], 0), p.a_nrows - 1) : -1;
+  };
+  if (tl.shared || p.layout == MOE_LAYOUT_COMPACT) {
+    if (tid < bm) {
+      const int64_t base = tl.shared ? 0 : min<int64_t>(max<int64_t>(p.group_off[tl.g], 0), p.rows);
+      put(tid < tl.nrows ? int(base + tl.r0 + tid) : -1);
+    }
+    __syncthreads();
+    return;
+  }
+  if (sh.cur_seg_group != tl.g) {  // uniform: every thread reads the same LDS word
+    __syncthreads();
+    for (int s = tid; s < p.S; s += NT) sh.seg[s] = min(max(p.counts[tl.g * p.S + s], 0), p.C);
+    __syncthreads();
+    const int tot = block_scan_lds<false, NT>(sh.seg, p.S, sh.tmp);
+    if (tid == 0) {
+      sh.seg[p.S] = tot;
+      sh.cur_seg_group = tl.g;
+    }
+    __syncthreads();
+  }
+  if (tid < bm) {
+    int phys = -1;
+    if (tid < tl.nrows) {
+      const int li = tl.r0 + tid;
+      int lo = 0, hi = p.S;  // last s with seg[s] <= li
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (sh.seg[mid] <= li) lo = mid;
+        else hi = mid;
+      }
+      phys = (tl.g * p.S + lo) * p.C + (li - sh.seg[lo]);
+    }
+    put(phys);
+  }
+  __syncthreads();
+}
+
+// A pointer every lane of the wave holds, moved into scalar registers (values
+// read from LDS are not known to be uniform): loads can then take it as their
+// scalar base with a 32-bit per-lane offset, so no per-lane 64-bit address
+// register is computed (and freed) per load.
+// (The result is a global-address-space pointer: rebuilt from integers, a
+// generic pointer would be accessed with flat instructions.)
+template <class T>
+using gptr = const T __attribute__((address_space(1)))*;
+template <class T>
+__device__ __forceinline__ gptr<T> uniform_ptr(const T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+  return (gptr<T>)((uint64_t(hi) << 32) | lo);
+}
+
+// base (scalar registers) + uniform byte offset + the lane's 32-bit byte offset
+template <class T>
+__device__ __forceinline__ gptr<T> at(gptr<char> base, uint64_t uniform_bytes, uint32_t lane_bytes) {
+  return (gptr<T>)(base + uniform_bytes + lane_bytes);
+}
+
+// 16-byte weight load; with STREAM the non-temporal hint (data used once).
+template <bool STREAM>
+__device__ __forceinline__ uint4 ld_w(gptr<uint4> p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const gptr<u32x4> q = (gptr<u32x4>)p;
+  const u32x4 v = STREAM ? __builtin_nontemporal_load(q) : *q;
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ float silu_f(float g) { return g / (1.f + __expf(-g)); }
+
+// e4m3fn x 8 (two dwords) -> bf16 x 8 of code * scale: exact decode to fp32
+// (v_cvt_pk_f32_fp8), one fp32 multiply by the 128x128 block scale, one RNE
+// rounding to bf16. (v_cvt_scalef32_pk_bf16_fp8 would apply only the
+// power-of-two exponent of a scale, which block scales are not.)
+__device__ __forceinline__ bf16x8_t fp8x8_dequant(uint32_t w0, uint32_t w1, float s) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t r0 = __builtin_convertvector(__builtin_amdgcn_cvt_pk_f32_fp8(w0, false) * s, bf16x2_t);
+  const bf16x2_t r1 = __builtin_convertvector(__builtin_amdgcn_cvt_pk_f32_fp8(w0, true) * s, bf16x2_t);
+  const bf16x2_t r2 = __builtin_convertvector(__builtin_amdgcn_cvt_pk_f32_fp8(w1, false) * s, bf16x2_t);
+  const bf16x2_t r3 = __builtin_convertvector(__builtin_amdgcn_cvt_pk_f32_fp8(w1, true) * s, bf16x2_t);
+  bf16x8_t r;
+  r[0] = r0[0]; r[1] = r0[1]; r[2] = r1[0]; r[3] = r1[1];
+  r[4] = r2[0]; r[5] = r2[1]; r[6] = r3[0]; r[7] = r3[1];
+  return r;
+}
+
+// ------------------------------------------------------------------ MFMA kernel
+// Stream-K split of the work: the iterations (tile, 128-deep K chunk) of the
+// whole launch are cut into equal contiguous ranges, one per workgroup (at
+// most kBfGrid for bf16 weights, kF8Grid for fp8: one resident workgroup per
+// compute unit), so every workgroup streams the same number of weight bytes no
+// matter how the tile count compares with the number of workgroups. A tile
+// covered by one workgroup is finished in place; a tile cut by a range
+// boundary leaves fp32 partial sums (in accumulator-register order) in the
+// workspace, and ffn_fixup_kernel adds them in workgroup order and finishes
+// the tile. No workgroup ever waits for another. When the launch has little
+// work, fewer ranges are used (at least kSkMinChunks chunks each), so the
+// partial sums stay small next to the weights streamed.
+constexpr int kXcds = 8;                              // accelerator complex dies of MI355X
+constexpr int kPartFloats = 4 * kMB * 16 * kWave;     // a bf16 workgroup's accumulators (64 KiB: 8 waves x 2 blocks)
+constexpr int kSkMinChunks = 8;
+
+// bf16 decode kernel (ffn_bf16_kernel): tiles of 64 activation rows x two N
+// blocks for a workgroup of 8 waves, one workgroup per compute unit
+constexpr int kBfBM = kBM / 2;                 // activation rows per tile
+constexpr int kBfMB = kBfBM / 32;              // 32-row MFMA blocks per tile
+constexpr int kBfWaves = 8;                    // waves per workgroup (one workgroup per CU)
+constexpr int kBfThreads = kBfWaves * kWave;
+constexpr int kBfNB = kBfWaves / 4;            // N blocks per tile
+constexpr int kBfGrid = 256;                   // 1 resident workgroup x 256 CUs
+static_assert(kBfThreads <= kMaxGemmThreads, "schedule scratch holds one entry per thread");
+static_assert(kBfWaves * kBfMB * 16 * kWave <= kPartFloats, "a workgroup's accumulators fit a partial slot");
+// [wave][block][quad q][lane][4 floats]: 1 KiB contiguous per wave access
+__device__ __forceinline__ int bf_part_idx(int wv, int b, int q, int lane) {
+  return (((wv * kBfMB + b) * 4 + q) * kWave + lane) * 4;
+}
+
+// Ranges used for a launch of `total` iterations: a multiple of the XCD count.
+__device__ inline int sk_grid(int64_t total, int max_grid) {
+  const int64_t g = total / kSkMinChunks / kXcds * kXcds;
+  return int(max<int64_t>(kXcds, min<int64_t>(max_grid, g)));
+}
+
+__host__ __device__ inline int64_t sk_start(int b, int64_t total, int G) { return int64_t(b) * total / G; }
+
+// Range whose span holds iteration i (the last one, if several start there).
+__device__ inline int sk_owner(int64_t i, int64_t total, int G) {
+  return int(((i + 1) * G + total - 1) / total) - 1;
+}
+
+// Partial slot of workgroup b: 0 for its first tile, 1 for its last.
+__device__ inline float* sk_slot(float* parts, int b, int slot) {
+  return parts + (size_t(b) * 2 + slot) * kPartFloats;
+}
+
+// Epilogue of 32-row block b of a tile (four consecutive output columns never
+// straddle a 32-column block).
+template <int KIND>
+__device__ __forceinline__ void ffn_epilogue_block(const f32x16_t& acc, const Tile& tl, int b, const Sched& sh,
+                                                   uint16_t* out, int n_out, int wv, int lr, int lh, bool oblk) {
+  const int phys = sh.rowmap[b * 32 + lr];
+  if (phys < 0) return;
+  uint16_t* orow = out + act_off(phys, 0, n_out, oblk);
+  if (KIND == kUp) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      float h[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) h[r] = silu_f(acc[4 * q + r]) * acc[4 * (q + 2) + r];
+      const int col = tl.nt * 64 + 16 * wv + 8 * q + 4 * lh;
+      *reinterpret_cast<uint2*>(orow + (oblk ? size_t(col >> 5) * 512 + (col & 31) : size_t(col))) =
+          make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int col = tl.nt * 128 + 32 * wv + 8 * q + 4 * lh;
+      *reinterpret_cast<uint2*>(orow + (oblk ? size_t(col >> 5) * 512 + (col & 31) : size_t(col))) =
+          make_uint2(pack_bf16x2(acc[4 * q], acc[4 * q + 1]), pack_bf16x2(acc[4 * q + 2], acc[4 * q + 3]));
+    }
+  }
+}
+
+template <int KIND, int NBMAX>
+__device__ __forceinline__ void ffn_epilogue(const f32x16_t (&acc)[NBMAX], const Tile& tl, int nb, const Sched& sh,
+                                             uint16_t* out, int n_out, int wv, int lr, int lh, bool oblk) {
+#pragma unroll
+  for (int b = 0; b < NBMAX; ++b)
+    if (b < nb) ffn_epilogue_block<KIND>(acc[b], tl, b, sh, out, n_out, wv, lr, lh, oblk);
+}
+
+// NA accumulator tiles (16 floats per lane each) summed over the partials of
+// ranges w_lo .. w_hi in range order; src(w) is the partial of range w
+// (nullptr: an empty range, nothing to add) and idx(a, q) the offset of quad q
+// of tile a in it. The loads of four ranges are in flight at a time.
+template <int NA, class Src, class Idx>
+__device__ __forceinline__ void sum_partials(f32x16_t (&acc)[NA], int w_lo, int w_hi, Src src, Idx idx) {
+#pragma unroll
+  for (int a = 0; a < NA; ++a)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[a][v] = 0.f;
+  for (int w0 = w_lo; w0 <= w_hi; w0 += 4) {
+    float4 ld[4][NA][4];
+    const float* ps[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      ps[k] = w0 + k <= w_hi ? src(w0 + k) : nullptr;
+#pragma unroll
+      for (int a = 0; a < NA; ++a)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          ld[k][a][q] = ps[k] ? *reinterpret_cast<const float4*>(ps[k] + idx(a, q)) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (!ps[k]) continue;  // uniform
+#pragma unroll
+      for (int a = 0; a < NA; ++a)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[a][4 * q] += ld[k][a][q].x;
+          acc[a][4 * q + 1] += ld[k][a][q].y;
+          acc[a][4 * q + 2] += ld[k][a][q].z;
+          acc[a][4 * q + 3] += ld[k][a][q].w;
+        }
+    }
+  }
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Global -> LDS copy of 16 bytes per lane (lane l writes bytes [16 l, 16 l +
+// 16) of the wave's KiB at lds), from scalar base + the lane's 32-bit offset:
+// global_load_lds as inline assembly, so that the compiler's wait-count
+// analysis does not see it. (With an LDS-writing global load outstanding that
+// analysis waits for every vector-memory op before the next use of any loaded
+// register, which would cap the prefetch at one stage.) The caller's own
+// counted waits must cover it; ops the analysis does not know of only make
+// its waits longer, since the count retires in order.
+__device__ __forceinline__ void lds_dma16_untracked(gptr<char> base, uint32_t lane_off, const void* lds) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_ptr_t)lds);
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(lane_off), "s"(base), "{m0}"(l) : "memory");
+}
+
+// Raw buffer resource over the 4 GiB from a wave-uniform base (scalar
+// registers): a buffer load addresses base + scalar offset + the lane's 32-bit
+// offset + an immediate, so no per-lane 64-bit address is held in registers.
+// (num_records is the maximum: the offsets are our own and stay in range.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base) {
+  const uint64_t v = reinterpret_cast<uint64_t>(base);
+  // (readfirstlane returns a signed int: each half goes through uint32_t, or
+  // widening would sign-extend the low half over the high one)
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+  const uint64_t u = (uint64_t(hi) << 32) | lo;
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(u), short(0), -1, 0x00020000);
+}
+
+// s_waitcnt immediate: wait until at most n vector-memory ops are outstanding
+// and no LDS op is (gfx9 encoding: vmcnt[3:0], expcnt[6:4] (7 = no wait),
+// lgkmcnt[11:8], vmcnt[5:4] in bits [15:14]).
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 14); }
+// s_waitcnt operand: at most n vector-memory ops outstanding, LDS/scalar count not waited for
+constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+// One wide tile's accumulators: 4 waves x 2 weight blocks x 8 activation
+// blocks x 16 registers x 64 lanes.
+constexpr int kWidePart = 4 * 2 * 8 * 16 * kWave;
+// [wave][a][block][quad q][lane][4 floats]: registers 4q..4q+3 of one
+// accumulator tile, 16 bytes per lane, 1 KiB contiguous per wave access
+__device__ __forceinline__ int wide_part_idx(int wv, int a, int b, int q, int lane) {
+  return ((((wv * 2 + a) * 8 + b) * 4 + q) * kWave + lane) * 4;
+}
+
+
+constexpr int kF8BM = 96;                                           // activation rows per tile
+constexpr int kF8MB = kF8BM / 32;                                   // MFMA row blocks per tile
+constexpr int kF8Waves = 8;                                         // waves per workgroup
+constexpr int kF8Threads = kF8Waves * kWave;
+constexpr int kF8NB = kF8Waves / 2;                                 // N blocks per tile
+constexpr int kF8Grid = 256;                                        // 1 resident workgroup x 256 CUs
+constexpr int kF8PartFloats = kF8Waves * 2 * kF8MB * 16 * kWave;   // one workgroup's accumulators (192 KiB)
+static_assert(kF8Threads <= kMaxGemmThreads, "schedule scratch holds one entry per thread");
+
+}  // namespace
+}  // namespace moe
