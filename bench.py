@@ -109,9 +109,13 @@ def algorithmic_model(cfg, counts, row_of, B0):
 
 # --------------------------------------------------------------------------- helpers
 def _kernel_source_hash():
+    """Hash of the grouped-GEMM sources (traffic counters are valid for these only)."""
+    import glob
+    csrc = os.path.join(ROOT, "combine_router_softmax_amd", "csrc")
     h = hashlib.sha256()
-    for f in ("grouped_gemm.hip", "moe_common.hpp"):
-        with open(os.path.join(ROOT, "combine_router_softmax_amd", "csrc", f), "rb") as fh:
+    for f in sorted(glob.glob(os.path.join(csrc, "gemm_*"))) + [os.path.join(csrc, "grouped_gemm.hip"),
+                                                                   os.path.join(csrc, "moe_common.hpp")]:
+        with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -233,7 +237,7 @@ class Bench:
         E = self.torch.cuda.Event
         return [(E(enable_timing=True), E(enable_timing=True)) for _ in range(n)]
 
-    def time_step(self, share, logits, offs, x, out, steps, warmup, graph=True, shared_mode="fused"):
+    def time_step(self, share, logits, offs, x, out, steps, warmup, graph=True, shared_mode=None):
         """Eager steps with events around every call, then (graph) replays of
         one captured step; mean times."""
         torch = self.torch
@@ -241,7 +245,7 @@ class Bench:
         for _ in range(warmup):
             run()
         torch.cuda.synchronize()
-        names = STEP_NAMES + (("shared",) if shared_mode == "stream" else ())
+        names = STEP_NAMES + (("shared",) if (shared_mode or share.shared_mode) == "stream" else ())
         ev = {n: self.events(steps) for n in names}
         est = self.events(steps)
         t0 = time.perf_counter()
@@ -384,7 +388,8 @@ def _measure_extra(bench, name, steps, warmup, headline=None):
     out = torch.zeros_like(x)
     res = bench.time_step(share, logits, offs, x, out, steps, warmup)
     model, breakdown, roof, gemm, mv, routing = _summarize(cfg, share, res, B0)
-    ent = {"workload": wl, "layout": "padded" if layout == PADDED else "compact", "ms_per_step": round(res["ms"], 4),
+    ent = {"workload": wl, "layout": "padded" if layout == PADDED else "compact", "shared_mode": share.shared_mode,
+           "ms_per_step": round(res["ms"], 4),
            "tokens_per_s": round(B0 / (res["ms"] / 1e3), 1), "ms_per_step_eager": round(res["ms_eager"], 4),
            "roofline": {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "kernel", "avg_launch_us")},
            "gemm": gemm, **mv, "breakdown": {k: v["us"] for k, v in breakdown.items()}, "routing": routing,
@@ -453,8 +458,9 @@ def main(argv=None):
                     help="up projection reads its rows from the tokens (no dispatch copy); auto: the layer's choice")
     ap.add_argument("--xe-layout", choices=["auto", "rows", "blocked"], default="auto",
                     help="storage of the expert rows (auto: the layer's choice)")
-    ap.add_argument("--shared-mode", choices=["fused", "serial", "stream"], default="fused",
-                    help="shared expert inside the routed launches, after them, or on a second stream")
+    ap.add_argument("--shared-mode", choices=["layer", "fused", "serial", "stream"], default="layer",
+                    help="shared expert inside the routed launches, after them, or on a second stream "
+                         "(default: the layer's choice)")
     ap.add_argument("--extras", default=DEFAULT_EXTRAS,
                     help="comma-separated workloads[:padded] measured after the headline, or 'none'")
     ap.add_argument("--extra-steps", type=int, default=20)
@@ -511,7 +517,7 @@ def main(argv=None):
     torch.cuda.synchronize()
     bench = Bench(torch, args.flush_mb)
     res = bench.time_step(share, logits, offs, x, out, args.steps, args.warmup, graph=not args.eager,
-                          shared_mode=args.shared_mode)
+                          shared_mode=None if args.shared_mode == "layer" else args.shared_mode)
     print(f"# headline {cfg.name}: {res['ms']:.4f} ms/step", file=sys.stderr, flush=True)
     ms_per_step = res["ms"]
     st = int(share.lay["status"].item())
@@ -558,7 +564,7 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": cfg.name, "layout": args.layout,
                    "xe_layout": "gathered" if share.gather else "blocked" if share.blocked else "rows",
-                   "shared_mode": args.shared_mode,
+                   "shared_mode": share.shared_mode if args.shared_mode == "layer" else args.shared_mode,
                    "global_batch": N, "tokens_per_gpu": B0,
                    "source_ranks": cfg.n_src, "hidden": cfg.hidden, "n_experts": cfg.n_experts,
                    "top_k": cfg.top_k, "local_experts": cfg.n_local, "shared_expert": cfg.shared,

@@ -73,6 +73,7 @@ class MoEShare:
         self.w_format = W_ROWMAJOR
         self.ws = None
         self.sws = None
+        self.shared_mode = "fused"
 
     def _new_xe(self):
         return torch.empty((max(blocked_rows(self.R) if self.blocked else self.R, 1), self.H), dtype=self.act_dtype,
@@ -92,6 +93,7 @@ class MoEShare:
         self.w_format = W_PACKED if (pack and routed["w13"].dtype != torch.float32) else W_ROWMAJOR
         self.w = todev(routed)
         self.sw = todev(shared)
+        self._default_shared_mode()
         wdt = self.w["w13"].dtype
         B0 = self.self_hi - self.self_lo
         se = SharedExpert(rows=B0 if self.sw is not None else 0)
@@ -143,10 +145,21 @@ class MoEShare:
                          shared=None if x is None else self._shared_arg(x), w_format=self.w_format,
                          a_layout=self.a_layout, rows=self.R, policy=self.policy, **extra)
 
+    def _default_shared_mode(self):
+        # where the shared expert runs by default (measured on MI355X): beside
+        # route, layout and the routed GEMM on a second stream for bf16 decode
+        # batches, whose streaming GEMM leaves HBM idle during the latency-bound
+        # route and layout (dsv3_decode_ep8: 0.587 -> 0.548 ms); inside the
+        # routed launches otherwise (kimi_k2_ep8, fp8: 0.684 fused against
+        # 0.718 ms on the second stream)
+        bf16_decode = self.w["w13"].dtype == torch.bfloat16 and self.policy == GEMM_STREAM_K
+        self.shared_mode = "stream" if bf16_decode and self.sw is not None else "fused"
+
     def share_weights_from(self, other: "MoEShare"):
         """Use another share's (already uploaded and packed) weights: a second
         share over a different batch of the same layer, e.g. a microbatch."""
         self.w_format, self.w, self.sw = other.w_format, other.w, other.sw
+        self._default_shared_mode()
         wdt = self.w["w13"].dtype
         B0 = self.self_hi - self.self_lo
         se = SharedExpert(rows=B0 if self.sw is not None else 0)
@@ -182,14 +195,15 @@ class MoEShare:
     def step(self, logits, src_offsets, x, out, events: Optional[dict] = None, fused_shared: bool = True,
              shared_mode: Optional[str] = None):
         """One full pass. ``events`` maps step names to (start, end) CUDA events
-        recorded around each call. ``shared_mode`` places the shared expert:
-        "fused" (default) inside the routed grouped-GEMM launches; "serial" as
+        recorded around each call. ``shared_mode`` places the shared expert
+        (default: the share's ``shared_mode``, see _default_shared_mode):
+        "fused" inside the routed grouped-GEMM launches; "serial" as
         calls of its own on the same stream after the routed GEMM; "stream" as
         calls of its own on a second stream, concurrent with route, layout and
         the routed GEMM, joined before the combine (the pages overlap it with
         the dispatch). ``fused_shared=False`` is "serial". Gathering, the
         dispatch copy is left out (its events, if any, enclose no work)."""
-        mode = shared_mode or ("fused" if fused_shared else "serial")
+        mode = shared_mode or (self.shared_mode if fused_shared else "serial")
         if mode not in ("fused", "serial", "stream"):
             raise ValueError(f"unknown shared_mode {mode}")
 

@@ -501,7 +501,8 @@ def test_layer_mid_size_every_row(kernel, layout):
 @pytest.mark.parametrize("name", ["dsv3_decode_ep8", "kimi_k2_ep8"])
 @pytest.mark.parametrize("layout", [COMPACT, PADDED])
 def test_fused_shared_expert_matches_separate_calls(name, layout):
-    # the shared expert inside the routed launches matches a call of its own (up to
+    # the shared expert inside the routed launches matches calls of its own, on
+    # the same or on a second stream (up to
     # the fp32 order of stream-K partial sums, which depends on the launch's tile
     # count) and the oracle
     cfg = get_config(name, hidden=1024, inter=512, n_experts=64, n_local=8, tokens_per_src=96)
@@ -510,14 +511,18 @@ def test_fused_shared_expert_matches_separate_calls(name, layout):
     logits = torch.from_numpy(d["logits"]).cuda()
     off = torch.from_numpy(d["src_offsets"]).cuda()
     x = d["x"].cuda()
-    o1 = torch.full_like(x, -9.0)
-    o2 = torch.full_like(x, -9.0)
-    share.step(logits, off, x, o1, fused_shared=True)
-    ys1 = share.ys.clone()
-    share.step(logits, off, x, o2, fused_shared=False)
-    torch.cuda.synchronize()
-    assert rel_l2(f64(ys1), f64(share.ys)) <= 2e-3
-    assert rel_l2(f64(o1), f64(o2)) <= 2e-3
+    outs = {}
+    for mode in ("fused", "serial", "stream"):  # in the routed launches, own calls, own calls on a second stream
+        o = torch.full_like(x, -9.0)
+        share.step(logits, off, x, o, shared_mode=mode)
+        torch.cuda.synchronize()
+        outs[mode] = (o, share.ys.clone())
+    o1, ys1 = outs["fused"]
+    for mode in ("serial", "stream"):
+        assert rel_l2(f64(ys1), f64(outs[mode][1])) <= 2e-3
+        assert rel_l2(f64(o1), f64(outs[mode][0])) <= 2e-3
+    # the shared expert's own calls give the same bits on either stream
+    assert torch.equal(outs["serial"][0].view(torch.int16), outs["stream"][0].view(torch.int16))
     sw = d["shared"]
     fp8 = sw.get("s13") is not None
     B0 = int(d["src_offsets"][1])
