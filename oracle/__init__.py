@@ -31,3 +31,12 @@ from .moe_oracle import (  # noqa: F401
     moe_layer,
     worst_case_rows,
 )
+from .w8a8 import (  # noqa: F401
+    encode_e4m3fn_rne,
+    quantize_1x128,
+    dequant_1x128,
+    gemm_w8a8,
+    w8a8_ffn,
+    w8a8_ffn_q,
+    moe_layer_w8a8,
+)
