@@ -16,8 +16,10 @@ models on AWS EFA", section Evaluation).
 
 Readings (the pages give neither the scale rule nor the rounding):
   * the scale of a 128-element block is its largest magnitude / 448 (the
-    largest OCP e4m3fn value), computed in fp32; an all-zero block has scale 1
-    (the same rule as the weight tiles);
+    largest OCP e4m3fn value), computed in fp32; where that is 0 (an all-zero
+    block, or a largest magnitude below 224 x 2^-149, whose quotient by
+    448 rounds to 0) the scale is 1 (the same rule as the weight tiles), so every
+    code stays finite;
   * codes are round-to-nearest-even of value / scale, computed in fp32 and
     clamped to +-448 first;
   * values are quantized from their fp32 form: the token rows are bf16 (exact
@@ -67,7 +69,7 @@ def quantize_1x128(a):
     multiple of 128; values taken as fp32).
 
     Returns ``(codes uint8 [R, K], scales float32 [R, K / 128])`` with
-    ``scale = fp32(max |block|) / 448`` (1 for an all-zero block) and
+    ``scale = fp32(max |block|) / 448`` (1 where that is 0) and
     ``code = RNE(clamp(fp32(value) / scale, +-448))``.
     """
     a32 = np.asarray(a, dtype=np.float32)
@@ -75,7 +77,8 @@ def quantize_1x128(a):
     assert K % 128 == 0
     blk = a32.reshape(R, K // 128, 128)
     amax = np.abs(blk).max(axis=2)
-    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    scale = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
     y = (blk / scale[:, :, None]).astype(np.float32)
     y = np.clip(y, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
     codes = encode_e4m3fn_rne(y).reshape(R, K)

@@ -110,6 +110,20 @@ def test_scale_closed_form_and_extremes():
             assert q[r, 128 * b + i] == (0xFE if blk[i] < 0 else 0x7E)
 
 
+def test_scale_underflow_gives_scale_one():
+    # a block whose largest magnitude is a float32 subnormal below 224 * 2**-149: its
+    # quotient by 448 rounds to 0, so the scale is 1 and every code is 0
+    x = np.zeros((1, 128), dtype=np.float32)
+    x[0, 5] = np.float32(2.0 ** -143)
+    x[0, 9] = -np.float32(2.0 ** -145)
+    q, s = quantize_1x128(x)
+    assert s[0, 0] == 1.0 and not q.any()
+    # just above that bound the scale is the smallest subnormal and the codes are finite
+    x[0, 5] = np.float32(2.0 ** -140)
+    q, s = quantize_1x128(x)
+    assert s[0, 0] == np.float32(2.0 ** -149) and q[0, 5] != 0 and np.all(~np.isnan(TAB[q]))
+
+
 def test_quantizer_error_within_half_step():
     rng = np.random.default_rng(1)
     x = (rng.standard_normal((64, 1024)) * 2.0 ** rng.integers(-8, 6, (64, 1))).astype(np.float32)
