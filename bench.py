@@ -40,6 +40,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA, TFLOP/s
 # the shared expert runs inside the gemm_up / gemm_down launches
 STEP_NAMES = ("route", "layout", "dispatch", "gemm_up", "gemm_down", "combine")
 KERNEL_OF_STEP = {"gemm_up": "ffn_wide_kernel<up> + ffn_wide_fixup_kernel<up> (or ffn_bf16_kernel<up> + "
@@ -49,7 +50,13 @@ KERNEL_OF_STEP = {"gemm_up": "ffn_wide_kernel<up> + ffn_wide_fixup_kernel<up> (o
                   "dispatch": "dispatch_kernel", "combine": "combine_kernel", "route": "route_topk_kernel"}
 KERNEL_OF_STEP_FP8 = {"gemm_up": "ffn_fp8_kernel<up> + ffn_fp8_fixup_kernel<up>",
                       "gemm_down": "ffn_fp8_kernel<down> + ffn_fp8_fixup_kernel<down>"}
-DEFAULT_EXTRAS = "dsv3_decode_ep8,dsv3_decode_ep128,kimi_k2_ep8,dsv3_prefill_ep8:padded"
+KERNEL_OF_STEP_W8A8 = {"gemm_up": "ffn_w8a8_kernel<up> + ffn_w8a8_fixup_kernel<up>",
+                       "gemm_down": "ffn_w8a8_kernel<down> + ffn_w8a8_fixup_kernel<down>",
+                       "quantize": "quantize_1x128_kernel"}
+# extra configurations: workload[:option+option], options padded (fixed-rectangle
+# layout) and w8a8 (fp8 activations; bf16 checkpoints quantized to fp8 128 x 128 tiles)
+DEFAULT_EXTRAS = ("dsv3_decode_ep8,dsv3_decode_ep128,kimi_k2_ep8,dsv3_prefill_ep8:padded,kimi_k2_ep8:w8a8,"
+                  "dsv3_prefill_ep8:w8a8")
 
 
 # --------------------------------------------------------------------------- perf model
@@ -68,14 +75,17 @@ def tokens_per_expert(batch, qlen, top_k, ep, n_experts):
     return batch * qlen * top_k * ep / n_experts
 
 
-def algorithmic_model(cfg, counts, row_of, B0):
+def algorithmic_model(cfg, counts, row_of, B0, w8a8=False):
     """Algorithmic bytes and FLOP per call from the actual routing of the step.
 
     counts [L, S] rows per local expert and source; row_of [N*K] (-1 = not local).
+    W8A8: the GEMMs read fp8 rows (1 byte + 4 bytes per 128 columns) and the
+    up projection writes fp8 h; y and the combine stay bf16.
     """
     H, I, K = cfg.hidden, cfg.inter, cfg.top_k
     wb = 1 if cfg.weight == "fp8_e4m3" else (4 if cfg.weight == "f32" else 2)
     ab = 4 if cfg.act == "f32" else 2
+    qb = 1 + 4 / 128  # an fp8 payload element with its share of the scale
     N = len(row_of) // K
     m = counts.sum(axis=1)
     M = int(m.sum())
@@ -104,6 +114,12 @@ def algorithmic_model(cfg, counts, row_of, B0):
         },
         "flops": {"gemm_up": 2 * MS * H * 2 * I, "gemm_down": 2 * MS * I * H},
     }
+    if w8a8:
+        b = model["bytes"]
+        b["quantize"] = int(N * H * (ab + qb))
+        b["dispatch"] = int((U + M) * H * qb + N * K * 4)
+        b["gemm_up"] = int(up_w + sh_up_w + MS * H * qb + MS * I * qb)
+        b["gemm_down"] = int(down_w + sh_down_w + MS * I * qb + MS * H * 2)
     return model
 
 
@@ -245,7 +261,8 @@ class Bench:
         for _ in range(warmup):
             run()
         torch.cuda.synchronize()
-        names = STEP_NAMES + (("shared",) if (shared_mode or share.shared_mode) == "stream" else ())
+        names = STEP_NAMES + (("shared",) if (shared_mode or share.shared_mode) == "stream" else ()) + \
+            (("quantize",) if share.w8a8 else ())
         ev = {n: self.events(steps) for n in names}
         est = self.events(steps)
         t0 = time.perf_counter()
@@ -288,7 +305,8 @@ class Bench:
                 "wall": wall}
 
 
-def _make_share(cfg, d, layout, *, policy=None, gather=None, blocked=None, weights_from=None, self_range=None):
+def _make_share(cfg, d, layout, *, policy=None, gather=None, blocked=None, weights_from=None, self_range=None,
+                w8a8=False):
     import torch
     from combine_router_softmax_amd import COMPACT
     from combine_router_softmax_amd.layer import MoEShare
@@ -298,7 +316,8 @@ def _make_share(cfg, d, layout, *, policy=None, gather=None, blocked=None, weigh
     act = torch.float32 if cfg.act == "f32" else torch.bfloat16
     share = MoEShare(n_tokens=N, hidden=cfg.hidden, inter=cfg.inter, n_experts=cfg.n_experts, top_k=cfg.top_k,
                      n_src=cfg.n_src, expert_lo=cfg.expert_lo, n_local=cfg.n_local, act_dtype=act, layout=layout,
-                     capacity=cap, self_range=self_range or (0, B0), blocked=blocked, gather=gather, policy=policy)
+                     capacity=cap, self_range=self_range or (0, B0), blocked=blocked, gather=gather, policy=policy,
+                     w8a8=w8a8)
     if weights_from is not None:
         share.share_weights_from(weights_from)
     else:
@@ -316,15 +335,16 @@ def _summarize(cfg, share, res, B0):
     dominant kernel's roofline."""
     counts = share.lay["counts"].cpu().numpy().astype(np.int64)
     row_of = share.lay["row_of"].cpu().numpy().astype(np.int64)
-    model = algorithmic_model(cfg, counts, row_of, B0)
+    model = algorithmic_model(cfg, counts, row_of, B0, w8a8=share.w8a8)
     per_call_us = dict(res["per_call_us"])
+    steps = STEP_NAMES + (("quantize",) if share.w8a8 else ())
     if share.gather:
         # the up projection reads its rows from the tokens: no dispatch copy
         # (its events enclosed no work)
         model["bytes"]["dispatch"] = 0
         per_call_us["dispatch"] = 0.0
     breakdown = {}
-    for n in STEP_NAMES:
+    for n in steps:
         us = per_call_us[n]
         b = model["bytes"].get(n, 0)
         f = model["flops"].get(n, 0)
@@ -336,15 +356,18 @@ def _summarize(cfg, share, res, B0):
     dom_us = per_call_us[dom]
     flops = model["flops"].get(dom, 0)
     byts = model["bytes"][dom]
-    mfma_bound = flops > 0 and flops / byts > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    mfma_peak = FP8_PEAK_TFLOPS if share.w8a8 else BF16_PEAK_TFLOPS
+    mfma_bound = flops > 0 and flops / byts > mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
     if mfma_bound:
-        roof = {"bound": "mfma", "achieved": round(flops / dom_us / 1e6, 2), "peak": BF16_PEAK_TFLOPS,
+        roof = {"bound": "mfma", "achieved": round(flops / dom_us / 1e6, 2), "peak": mfma_peak,
                 "unit": "TFLOP/s"}
     else:
         roof = {"bound": "hbm", "achieved": round(byts / dom_us / 1e3, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = _traffic(cfg.name, dom) if share.layout == 0 else None
-    names = dict(KERNEL_OF_STEP, **(KERNEL_OF_STEP_FP8 if cfg.weight == "fp8_e4m3" else {}))
+    roof["traffic"] = _traffic(cfg.name + (":w8a8" if share.w8a8 else ""), dom) if share.layout == 0 else None
+    names = dict(KERNEL_OF_STEP)
+    names.update(KERNEL_OF_STEP_FP8 if cfg.weight == "fp8_e4m3" else {})
+    names.update(KERNEL_OF_STEP_W8A8 if share.w8a8 else {})
     roof["kernel"] = names.get(dom, dom)
     roof["step"] = dom
     roof["algorithmic_bytes_per_launch"] = int(byts)
@@ -356,6 +379,8 @@ def _summarize(cfg, share, res, B0):
     gf = model["flops"]["gemm_up"] + model["flops"]["gemm_down"]
     gemm = {"us": round(gemm_us, 2), "frac_hbm": round(gb / gemm_us / 1e3 / HBM_PEAK_GBS, 4),
             "frac_mfma_bf16": round(gf / gemm_us / 1e6 / BF16_PEAK_TFLOPS, 4)}
+    if share.w8a8:
+        gemm["frac_mfma_fp8"] = round(gf / gemm_us / 1e6 / FP8_PEAK_TFLOPS, 4)
     mv = {"combine": {"GB/s": breakdown["combine"]["GB/s"],
                       "frac_hbm": round(model["bytes"]["combine"] / per_call_us["combine"] / 1e3 / HBM_PEAK_GBS, 4)}}
     if not share.gather:
@@ -373,22 +398,26 @@ def _measure_extra(bench, name, steps, warmup, headline=None):
     import torch
     from combine_router_softmax_amd import COMPACT, PADDED
     from synth import get_config, make_inputs
-    wl, _, lay = name.partition(":")
-    layout = PADDED if lay == "padded" else COMPACT
+    wl, _, opts = name.partition(":")
+    opts = set(opts.split("+")) - {""}
+    if opts - {"padded", "w8a8"}:
+        raise ValueError(f"unknown option in extra {name}")
+    layout = PADDED if "padded" in opts else COMPACT
+    w8a8 = "w8a8" in opts
     cfg = get_config(wl)
-    if headline is not None and headline[0].name == wl:
-        d = headline[1]
-    else:
-        d = make_inputs(cfg, 0)
+    if w8a8 and cfg.weight != "fp8_e4m3":
+        cfg = get_config(wl, weight="fp8_e4m3")   # the checkpoint quantized to fp8 128 x 128 tiles
+    same = headline is not None and headline[0] == cfg
+    d = headline[1] if same else make_inputs(cfg, 0)
     off = d["src_offsets"]
     B0 = int(off[1])
-    share = _make_share(cfg, d, layout,
-                        weights_from=headline[2] if headline is not None and headline[0].name == wl else None)
+    share = _make_share(cfg, d, layout, weights_from=headline[2] if same else None, w8a8=w8a8)
     logits, offs, x = _dev_inputs(d)
     out = torch.zeros_like(x)
     res = bench.time_step(share, logits, offs, x, out, steps, warmup)
     model, breakdown, roof, gemm, mv, routing = _summarize(cfg, share, res, B0)
     ent = {"workload": wl, "layout": "padded" if layout == PADDED else "compact", "shared_mode": share.shared_mode,
+           "w8a8": w8a8, "weights": cfg.weight,
            "ms_per_step": round(res["ms"], 4),
            "tokens_per_s": round(B0 / (res["ms"] / 1e3), 1), "ms_per_step_eager": round(res["ms_eager"], 4),
            "roofline": {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "kernel", "avg_launch_us")},

@@ -20,6 +20,7 @@ __all__ = [
     "COMPACT", "PADDED", "GG_FULL", "GG_UP", "GG_DOWN", "STATUS_OVERFLOW", "MoeError", "MoeLibraryMissing",
     "lib", "lib_path", "moe_route_topk", "moe_dispatch_layout", "moe_layout_rows", "moe_dispatch",
     "moe_grouped_gemm", "moe_combine", "moe_abi_version", "moe_pack_weights", "W_ROWMAJOR", "W_PACKED",
+    "moe_quantize_1x128", "moe_dispatch_fp8",
 ]
 
 COMPACT, PADDED = 0, 1
@@ -28,6 +29,7 @@ GG_FULL, GG_UP, GG_DOWN = 0, 1, 2
 GEMM_AUTO, GEMM_WIDE, GEMM_STREAM_K = 0, 1, 2
 ACT_ROWS, ACT_BLOCKED16 = 0, 1
 STATUS_OVERFLOW = 1
+ABI_VERSION = 2  # struct layouts of moe.h this binding mirrors
 _F32, _BF16, _FP8 = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -51,7 +53,8 @@ class LayoutDesc(ctypes.Structure):
 
 class SharedExpert(ctypes.Structure):
     _fields_ = [("a", ctypes.c_void_p), ("rows", ctypes.c_int), ("w13", ctypes.c_void_p), ("w2", ctypes.c_void_p),
-                ("s13", ctypes.c_void_p), ("s2", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+                ("s13", ctypes.c_void_p), ("s2", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("a_scales", ctypes.c_void_p)]
 
 
 class GGemmDesc(ctypes.Structure):
@@ -60,7 +63,7 @@ class GGemmDesc(ctypes.Structure):
                 ("n_src", ctypes.c_int), ("capacity", ctypes.c_int), ("rows", ctypes.c_int64),
                 ("stage", ctypes.c_int), ("shared", ctypes.POINTER(SharedExpert)), ("w_format", ctypes.c_int),
                 ("policy", ctypes.c_int), ("a_layout", ctypes.c_int), ("a_rows", ctypes.c_void_p),
-                ("a_nrows", ctypes.c_int64)]
+                ("a_nrows", ctypes.c_int64), ("a_scales", ctypes.c_void_p)]
 
 
 _P = ctypes.c_void_p
@@ -78,6 +81,8 @@ _SIGNATURES = {
     "moe_dispatch_layout_noalloc": (_I, [ctypes.POINTER(LayoutDesc), _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_dispatch": (_I, [_P, _I, _I, _I, _I, _P, _I64, _P, _P]),
     "moe_dispatch_blocked": (_I, [_P, _I, _I, _I, _I, _P, _I64, _P, _P]),
+    "moe_quantize_1x128": (_I, [_P, _I, _I64, _I, _P, _P, _P]),
+    "moe_dispatch_fp8": (_I, [_P, _P, _I, _I, _I, _P, _I64, _P, _P, _P]),
     "moe_grouped_gemm_workspace": (_SZ, [ctypes.POINTER(GGemmDesc)]),
     "moe_grouped_gemm": (_I, [ctypes.POINTER(GGemmDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_combine": (_I, [_P, _I, _I64, _P, _P, _I, _I, _I, _P, _I, _I, _P, _P]),
@@ -102,6 +107,9 @@ def lib():
             fn = getattr(l, name)
             fn.restype = res
             fn.argtypes = args
+        v = int(l.moe_abi_version())
+        if v != ABI_VERSION:
+            raise MoeError(f"{_LIB_FILE} has ABI version {v}, this binding expects {ABI_VERSION}; rebuild it")
         _lib = l
     return _lib
 
@@ -277,6 +285,53 @@ def moe_dispatch(x: torch.Tensor, row_of: torch.Tensor, top_k: int, n_rows: int,
     return xe
 
 
+def moe_quantize_1x128(x: torch.Tensor, xq: Optional[torch.Tensor] = None, xs: Optional[torch.Tensor] = None):
+    """fp8 payload of token rows: e4m3fn codes ``xq`` (uint8 [N, H]) and one
+    float32 scale per 128 columns ``xs`` ([N, H / 128])."""
+    _dev(x, "x", (torch.float32, torch.bfloat16))
+    _need(x.dim() == 2, "x must be [N, H]")
+    N, H = x.shape
+    _need(H % 128 == 0, f"hidden {H} must be a multiple of 128")
+    if xq is None:
+        xq = torch.empty((N, H), dtype=torch.uint8, device=x.device)
+    if xs is None:
+        xs = torch.empty((N, H // 128), dtype=torch.float32, device=x.device)
+    _dev(xq, "xq", torch.uint8)
+    _dev(xs, "xs", torch.float32)
+    _need(xq.dim() == 2 and xq.shape[1] == H and xq.shape[0] >= N, f"xq must be [>= {N}, {H}]")
+    _need(xs.dim() == 2 and xs.shape[1] == H // 128 and xs.shape[0] >= N, f"xs must be [>= {N}, {H // 128}]")
+    _on_gpu(x=x, xq=xq, xs=xs)
+    _check(lib().moe_quantize_1x128(_ptr(x), _act_code(x.dtype), N, H, _ptr(xq), _ptr(xs), _stream()),
+           "moe_quantize_1x128")
+    return xq, xs
+
+
+def moe_dispatch_fp8(xq: torch.Tensor, xs: torch.Tensor, row_of: torch.Tensor, top_k: int, n_rows: int,
+                     xeq: Optional[torch.Tensor] = None, xes: Optional[torch.Tensor] = None):
+    """Copy fp8 payload rows (codes and scales) into their expert-grouped slots."""
+    _dev(xq, "xq", torch.uint8)
+    _dev(xs, "xs", torch.float32)
+    _dev(row_of, "row_of", torch.int32)
+    _need(xq.dim() == 2, "xq must be [N, H]")
+    N, H = xq.shape
+    _need(H % 128 == 0, f"hidden {H} must be a multiple of 128")
+    _shape_is(xs, (N, H // 128), "xs")
+    if xeq is None:
+        xeq = torch.empty((n_rows, H), dtype=torch.uint8, device=xq.device)
+    if xes is None:
+        xes = torch.empty((n_rows, H // 128), dtype=torch.float32, device=xq.device)
+    _dev(xeq, "xeq", torch.uint8)
+    _dev(xes, "xes", torch.float32)
+    _need(xeq.dim() == 2 and xeq.shape[1] == H and xeq.shape[0] >= n_rows, f"xeq must be [>= {n_rows}, {H}]")
+    _need(xes.dim() == 2 and xes.shape[1] == H // 128 and xes.shape[0] >= n_rows,
+          f"xes must be [>= {n_rows}, {H // 128}]")
+    _need(row_of.numel() >= N * top_k, f"row_of must hold N * top_k = {N * top_k} entries")
+    _on_gpu(xq=xq, xs=xs, row_of=row_of, xeq=xeq, xes=xes)
+    _check(lib().moe_dispatch_fp8(_ptr(xq), _ptr(xs), N, H, top_k, _ptr(row_of), n_rows, _ptr(xeq), _ptr(xes),
+                                  _stream()), "moe_dispatch_fp8")
+    return xeq, xes
+
+
 def blocked_rows(n_rows: int) -> int:
     """Rows a 16-row blocked buffer of n_rows rows holds."""
     return (n_rows + 15) // 16 * 16
@@ -309,7 +364,8 @@ def gemm_desc(n_groups, hidden, inter, act_dtype, w_dtype, layout, n_src, capaci
               shared: "SharedExpert | None" = None, w_format: int = W_ROWMAJOR, policy: int = 0,
               a_layout: int = ACT_ROWS):
     w_code = _W_CODE[w_dtype]
-    d = GGemmDesc(n_groups, hidden, inter, _act_code(act_dtype), w_code, layout, n_src, capacity, rows, stage)
+    a_code = _FP8 if act_dtype in (torch.uint8, torch.float8_e4m3fn) else _act_code(act_dtype)
+    d = GGemmDesc(n_groups, hidden, inter, a_code, w_code, layout, n_src, capacity, rows, stage)
     d.w_format = w_format
     d.policy = policy
     d.a_layout = a_layout
@@ -319,8 +375,10 @@ def gemm_desc(n_groups, hidden, inter, act_dtype, w_dtype, layout, n_src, capaci
 
 
 def shared_expert(a: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, y: Optional[torch.Tensor],
-                  s13: Optional[torch.Tensor] = None, s2: Optional[torch.Tensor] = None) -> SharedExpert:
-    """Descriptor of the shared expert run inside a moe_grouped_gemm call."""
+                  s13: Optional[torch.Tensor] = None, s2: Optional[torch.Tensor] = None,
+                  a_scales: Optional[torch.Tensor] = None) -> SharedExpert:
+    """Descriptor of the shared expert run inside a moe_grouped_gemm call
+    (W8A8: ``a`` holds e4m3 codes and ``a_scales`` their 1 x 128 scales)."""
     _dev(a, "shared a")
     _dev(w13, "shared w13")
     _dev(w2, "shared w2")
@@ -329,9 +387,15 @@ def shared_expert(a: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, y: Optio
     B, H = a.shape
     I = w13.shape[1] // 2
     _shape_is(w2, (1, H, I), "shared w2")
+    w8a8 = a.dtype == torch.uint8
     if y is not None:
-        _dev(y, "shared y", a.dtype)
+        _dev(y, "shared y", torch.bfloat16 if w8a8 else a.dtype)
         _need(y.dim() == 2 and y.shape[1] == H and y.shape[0] >= B, f"shared y must be [>= {B}, {H}]")
+    if w8a8:
+        _need(a_scales is not None, "W8A8 shared rows need a_scales")
+        _dev(a_scales, "shared a_scales", torch.float32)
+        _need(a_scales.dim() == 2 and a_scales.shape[1] == H // 128 and a_scales.shape[0] >= B,
+              f"shared a_scales must be [>= {B}, {H // 128}]")
     if s13 is not None or s2 is not None:
         _need(s13 is not None and s2 is not None, "fp8 shared weights need both scale tensors")
         _dev(s13, "shared s13", torch.float32)
@@ -340,7 +404,7 @@ def shared_expert(a: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, y: Optio
         _shape_is(s2, (1, H // 128, I // 128), "shared s2")
     return SharedExpert(a.data_ptr(), a.shape[0], w13.data_ptr(), w2.data_ptr(),
                         None if s13 is None else s13.data_ptr(), None if s2 is None else s2.data_ptr(),
-                        None if y is None else y.data_ptr())
+                        None if y is None else y.data_ptr(), None if a_scales is None else a_scales.data_ptr())
 
 
 def moe_grouped_gemm_workspace(desc: GGemmDesc) -> int:
@@ -352,13 +416,18 @@ def moe_grouped_gemm(a: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, *, gr
                      stage: int = GG_FULL, y: Optional[torch.Tensor] = None,
                      ws: Optional[torch.Tensor] = None, shared: Optional[dict] = None,
                      w_format: int = W_ROWMAJOR, policy: int = 0, a_layout: int = ACT_ROWS,
-                     rows: Optional[int] = None, a_rows: Optional[torch.Tensor] = None) -> torch.Tensor:
+                     rows: Optional[int] = None, a_rows: Optional[torch.Tensor] = None,
+                     a_scales: Optional[torch.Tensor] = None) -> torch.Tensor:
     """SwiGLU FFN per expert over the rows each expert holds (see moe.h).
 
-    ``shared`` = dict(a, w13, w2, y[, s13, s2]) runs the shared expert in the same launches.
+    ``shared`` = dict(a, w13, w2, y[, s13, s2, a_scales]) runs the shared expert in the same launches.
     ``a_rows`` (int32 [rows], e.g. the layout's row_token) gathers routed row r
-    of the up projection from row a_rows[r] of ``a``; ``rows`` is then required."""
-    _dev(a, "a", (torch.float32, torch.bfloat16))
+    of the up projection from row a_rows[r] of ``a``; ``rows`` is then required.
+    W8A8: ``a`` is uint8 e4m3 codes with ``a_scales`` [rows of a, H / 128]
+    (moe_quantize_1x128 / moe_dispatch_fp8), the weights fp8 codes with
+    scales; ``y`` is bf16."""
+    _dev(a, "a", (torch.float32, torch.bfloat16, torch.uint8))
+    w8a8 = a.dtype == torch.uint8
     _dev(w13, "w13")
     _dev(w2, "w2")
     _need(a.dim() == 2 and w13.dim() == 3, "a must be [rows, H] and w13 [G, 2I, H]")
@@ -374,10 +443,19 @@ def moe_grouped_gemm(a: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, *, gr
         _need(s13 is not None and s2 is not None, "fp8 weights need both scale tensors")
         _shape_is(s13, (G, I2 // 128, H // 128), "s13")
         _shape_is(s2, (G, H // 128, I // 128), "s2")
+    if w8a8:
+        _need(w13.dtype in (torch.uint8, torch.float8_e4m3fn) and s13 is not None,
+              "W8A8 needs fp8 weights with their scales")
+        _need(a_scales is not None, "W8A8 rows need a_scales")
+        _dev(a_scales, "a_scales", torch.float32)
+        _need(a_scales.dim() == 2 and a_scales.shape[1] == H // 128 and a_scales.shape[0] >= a.shape[0],
+              f"a_scales must be [>= {a.shape[0]}, {H // 128}]")
+    else:
+        _need(a_scales is None, "a_scales belong to fp8 (uint8) activations")
     se = None
     if shared is not None:
         se = shared_expert(shared["a"], shared["w13"], shared["w2"], shared.get("y"), shared.get("s13"),
-                           shared.get("s2"))
+                           shared.get("s2"), shared.get("a_scales"))
     if a_rows is not None:
         if rows is None:
             raise ValueError("a gathered input needs rows (the routed row count)")
@@ -401,6 +479,8 @@ def moe_grouped_gemm(a: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, *, gr
     if a_rows is not None:
         desc.a_rows = a_rows.data_ptr()
         desc.a_nrows = a.shape[0]
+    if w8a8:
+        desc.a_scales = a_scales.data_ptr()
     wsb = moe_grouped_gemm_workspace(desc)
     if wsb == 0:
         raise MoeError("moe_grouped_gemm: invalid descriptor")
@@ -408,10 +488,11 @@ def moe_grouped_gemm(a: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, *, gr
         ws = torch.zeros(wsb, dtype=torch.uint8, device=a.device)
     _dev(ws, "ws")
     _need(ws.numel() * ws.element_size() >= wsb, f"ws holds {ws.numel() * ws.element_size()} bytes, needs {wsb}")
+    y_dtype = torch.bfloat16 if w8a8 else a.dtype
     if y is None and stage != GG_UP:
-        y = torch.empty((R, H), dtype=a.dtype, device=a.device)
+        y = torch.empty((R, H), dtype=y_dtype, device=a.device)
     if y is not None:
-        _dev(y, "y", a.dtype)
+        _dev(y, "y", y_dtype)
         _need(y.dim() == 2 and y.shape[1] == H and y.shape[0] >= R, f"y must be [>= {R}, {H}]")
     for name, t in (("group_off", group_off), ("counts", counts)):
         if t is not None:
@@ -419,7 +500,8 @@ def moe_grouped_gemm(a: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, *, gr
     for name, t in (("s13", s13), ("s2", s2)):
         if t is not None:
             _dev(t, name, torch.float32)
-    _on_gpu(a=a, w13=w13, w2=w2, group_off=group_off, counts=counts, s13=s13, s2=s2, y=y, ws=ws, a_rows=a_rows)
+    _on_gpu(a=a, w13=w13, w2=w2, group_off=group_off, counts=counts, s13=s13, s2=s2, y=y, ws=ws, a_rows=a_rows,
+            a_scales=a_scales)
     if shared is not None:
         _on_gpu(**{f"shared {k}": v for k, v in shared.items() if isinstance(v, torch.Tensor)})
     _check(lib().moe_grouped_gemm(ctypes.byref(desc), _ptr(a), _ptr(counts), _ptr(group_off), _ptr(w13), _ptr(w2),

@@ -72,6 +72,19 @@ __global__ __launch_bounds__(kVecThreads) void dispatch_kernel(const uint4* __re
     }
 }
 
+// The scales of fp8 payload rows: xes[row_of[t*K+k]][j] = xs[t][j] (one
+// workgroup of one wave per token; a row holds hidden / 128 scales).
+__global__ __launch_bounds__(kWave) void dispatch_scales_kernel(const float* __restrict__ xs, int per_row,
+                                                                int top_k, const int32_t* __restrict__ row_of,
+                                                                int64_t n_rows, float* __restrict__ xes) {
+  const int t = blockIdx.x;
+  for (int k = 0; k < top_k; ++k) {
+    const int r = row_of[size_t(t) * top_k + k];
+    if (r < 0 || r >= n_rows) continue;  // uniform
+    for (int j = threadIdx.x; j < per_row; j += kWave) xes[size_t(r) * per_row + j] = xs[size_t(t) * per_row + j];
+  }
+}
+
 // 16-byte piece <-> floats
 template <typename T>
 struct Vec;
@@ -237,6 +250,23 @@ MOE_API moe_status_t moe_dispatch(const void* x, moe_dtype_t dt, int n_tokens, i
     case 8: hipLaunchKernelGGL((dispatch_kernel<8, false>), grid, block, 0, stream, xv, row_vecs, n_chunks, n_tokens, top_k, row_of, n_rows, ov); break;
     default: hipLaunchKernelGGL((dispatch_kernel<16, false>), grid, block, 0, stream, xv, row_vecs, n_chunks, n_tokens, top_k, row_of, n_rows, ov); break;
   }
+  return launch_status();
+}
+
+MOE_API moe_status_t moe_dispatch_fp8(const uint8_t* xq, const float* xs, int n_tokens, int hidden, int top_k,
+                                      const int32_t* row_of, int64_t n_rows, uint8_t* xeq, float* xes,
+                                      hipStream_t stream) {
+  if (n_tokens < 0 || hidden < 1 || top_k < 1 || n_rows < 0) return MOE_ERR_INVALID_ARG;
+  if (hidden % 128) return MOE_ERR_UNSUPPORTED;
+  if (top_k > kMaxK) return MOE_ERR_UNSUPPORTED;
+  if (n_tokens == 0 || n_rows == 0) return MOE_OK;
+  if (!xs || !xes || (reinterpret_cast<uintptr_t>(xs) & 3u) || (reinterpret_cast<uintptr_t>(xes) & 3u))
+    return MOE_ERR_INVALID_ARG;
+  // the codes are rows of hidden bytes: the bf16/f32 row copy moves them bit for bit
+  const moe_status_t st = moe_dispatch(xq, MOE_BF16, n_tokens, hidden / 2, top_k, row_of, n_rows, xeq, stream);
+  if (st != MOE_OK) return st;
+  hipLaunchKernelGGL(dispatch_scales_kernel, dim3(unsigned(n_tokens)), dim3(kWave), 0, stream, xs, hidden / 128,
+                     top_k, row_of, n_rows, xes);
   return launch_status();
 }
 

@@ -1,5 +1,5 @@
 // Grouped-GEMM internals shared by the kernel translation units
-// (gemm_wide.hip, gemm_bf16.hip, gemm_fp8.hip) and the host code in
+// (gemm_wide.hip, gemm_bf16.hip, gemm_fp8.hip, gemm_w8a8.hip) and the host code in
 // grouped_gemm.hip. Internal header.
 #pragma once
 
@@ -37,13 +37,21 @@ struct GemmArgs {
   int out_blk;                // outputs (routed and shared) in the 16-row blocked layout
   const int32_t* a_rows;      // routed input row r is row a_rows[r] of a (nullptr: row r)
   int a_nrows;                // rows of a when gathering
+  // W8A8: a (and sh_a) are e4m3 codes with one fp32 scale per row and 128
+  // columns in as / sh_as; the up projection writes h as codes (out, sh_out)
+  // and scales (out_s, sh_out_s); the down projection writes bf16
+  const float* as;
+  const float* sh_as;
+  float* out_s;
+  float* sh_out_s;
 };
 
-// Launchers of the three MFMA kernel families (each in its own translation
+// Launchers of the four MFMA kernel families (each in its own translation
 // unit): the main kernel of the stage and its fix-up kernel on `stream`.
 moe_status_t launch_wide(const GemmArgs& p, int kind, float* parts, hipStream_t stream);
 moe_status_t launch_bf16(const GemmArgs& p, int kind, float* parts, hipStream_t stream);
 moe_status_t launch_fp8(const GemmArgs& p, int kind, float* parts, hipStream_t stream);
+moe_status_t launch_w8a8(const GemmArgs& p, int kind, float* parts, hipStream_t stream);
 
 namespace {
 
@@ -139,8 +147,9 @@ __device__ __forceinline__ int build_schedule(const GemmArgs& p, int bm, int ntn
     __syncthreads();
   }
   // once the launch qualifies, every group takes the wide kernel (one launch
-  // does all the work; small groups are cheap ragged tiles there)
-  const int wide_min = sh.wide_tiles >= p.wide_min_tiles ? 1 : kNoWide;
+  // does all the work; small groups are cheap ragged tiles there); a launch
+  // without the wide kernel (wide_min == kNoWide) never qualifies
+  const int wide_min = p.wide_min != kNoWide && sh.wide_tiles >= p.wide_min_tiles ? 1 : kNoWide;
   for (int g = tid; g < Gt; g += NT) {
     const int m = sh.m[g];
     sh.tile_start[g] = ((m >= wide_min) == wide) ? (m + bm - 1) / bm * ntn : 0;

@@ -161,10 +161,20 @@ static bool ggemm_desc_ok(const moe_ggemm_desc_t* d) {
   return true;
 }
 
+static bool is_w8a8(const moe_ggemm_desc_t* d) { return d->act_dt == MOE_FP8_E4M3 && d->w_dt == MOE_FP8_E4M3; }
+
 static bool ggemm_desc_supported(const moe_ggemm_desc_t* d) {
   const bool f32 = d->act_dt == MOE_F32 && d->w_dt == MOE_F32;
   const bool bf16 = d->act_dt == MOE_BF16 && (d->w_dt == MOE_BF16 || d->w_dt == MOE_FP8_E4M3);
-  if (!f32 && !bf16) return false;
+  const bool w8a8 = is_w8a8(d);
+  if (!f32 && !bf16 && !w8a8) return false;
+  if (w8a8) {
+    if (d->a_layout != MOE_ACT_ROWS) return false;
+    // scale offsets are 32-bit byte offsets: rows * (K / 128) * 4 < 2^32
+    const int64_t kmax = std::max(d->hidden, d->inter) / 128;
+    const int64_t srows = std::max<int64_t>(d->rows, d->a_rows ? d->a_nrows : 0);
+    if (srows * kmax * 4 >= (int64_t(1) << 32)) return false;
+  }
   if (d->hidden % 128 || d->inter % 128) return false;
   if (d->n_groups > kMaxGroups) return false;
   if (d->layout == MOE_LAYOUT_PADDED && d->n_src > kGemmMaxSrc) return false;
@@ -172,16 +182,22 @@ static bool ggemm_desc_supported(const moe_ggemm_desc_t* d) {
   if (d->shared && d->shared->rows >= (1 << 30)) return false;
   if (f32 && d->w_format == MOE_W_PACKED) return false;
   if (f32 && d->a_layout != MOE_ACT_ROWS) return false;
-  // gathering: row-major bf16 rows, 32-bit byte offsets (decode-shaped kernels)
+  // gathering: row-major rows, 32-bit byte offsets (decode-shaped kernels)
   if (d->a_rows && (f32 || d->a_layout != MOE_ACT_ROWS ||
-                    d->a_nrows > (int64_t(1) << 32) / (int64_t(d->hidden) * 2)))
+                    d->a_nrows > (int64_t(1) << 32) / (int64_t(d->hidden) * (w8a8 ? 1 : 2))))
     return false;
   return true;
 }
 
+// h codes of W8A8: [rows, I] bytes, then the scales [rows, I / 128]
+static size_t h_codes_bytes(const moe_ggemm_desc_t* d, int64_t rows) {
+  return align_up(size_t(rows) * size_t(d->inter), 256);
+}
+
 // h [rows, I]: fp32 row-major, or bf16 in the 16-row blocked layout (rows
-// rounded up to 16)
+// rounded up to 16), or W8A8 codes and scales
 static size_t h_bytes(const moe_ggemm_desc_t* d, int64_t rows) {
+  if (is_w8a8(d)) return h_codes_bytes(d, rows) + align_up(size_t(rows) * size_t(d->inter / 128) * 4, 256);
   const size_t el = d->act_dt == MOE_F32 ? 4 : 2;
   if (d->act_dt != MOE_F32) rows = (rows + 15) / 16 * 16;
   return align_up(size_t(rows) * size_t(d->inter) * el, 256);
@@ -214,8 +230,9 @@ int device_cu_count() {
 }  // namespace moe
 
 // sk: launch the stream-K kernel (false only when the wide kernel takes every group)
-static moe_status_t launch_stage(const GemmArgs& p, bool f32, bool fp8, int kind, bool sk, float* parts,
+static moe_status_t launch_stage(const GemmArgs& p, bool f32, bool fp8, bool w8a8, int kind, bool sk, float* parts,
                                  hipStream_t stream) {
+  if (w8a8) return launch_w8a8(p, kind, parts, stream);
   const dim3 block(kGemmThreads);
   if (f32) {
     const int64_t upper = int64_t(p.n_tiles_n) * ((p.rows + kFBM - 1) / kFBM + p.G + (p.sh_rows + kFBM - 1) / kFBM + 1);
@@ -244,18 +261,22 @@ MOE_API moe_status_t moe_grouped_gemm(const moe_ggemm_desc_t* d, const void* a, 
   if (!routed && !se) return MOE_OK;
   const bool f32 = d->act_dt == MOE_F32;
   const bool fp8 = d->w_dt == MOE_FP8_E4M3;
+  const bool w8a8 = is_w8a8(d);
   const bool up = d->stage != MOE_GG_DOWN, down = d->stage != MOE_GG_UP;
+  auto aligned4 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 3u) == 0; };
   if (routed) {
     if (d->layout == MOE_LAYOUT_COMPACT && !group_off) return MOE_ERR_INVALID_ARG;
     if (d->layout == MOE_LAYOUT_PADDED && !counts) return MOE_ERR_INVALID_ARG;
     if (up && (!a || !w13 || !aligned16(a) || !aligned16(w13))) return MOE_ERR_INVALID_ARG;
     if (down && (!y || !w2 || !aligned16(y) || !aligned16(w2))) return MOE_ERR_INVALID_ARG;
     if (fp8 && ((up && !s13) || (down && !s2))) return MOE_ERR_INVALID_ARG;
+    if (w8a8 && up && (!d->a_scales || !aligned4(d->a_scales))) return MOE_ERR_INVALID_ARG;
   }
   if (se) {
     if (up && (!se->a || !se->w13 || !aligned16(se->a) || !aligned16(se->w13))) return MOE_ERR_INVALID_ARG;
     if (down && (!se->y || !se->w2 || !aligned16(se->y) || !aligned16(se->w2))) return MOE_ERR_INVALID_ARG;
     if (fp8 && ((up && !se->s13) || (down && !se->s2))) return MOE_ERR_INVALID_ARG;
+    if (w8a8 && up && (!se->a_scales || !aligned4(se->a_scales))) return MOE_ERR_INVALID_ARG;
   }
   if (!ws || !aligned16(ws) || ws_bytes < moe_grouped_gemm_workspace(d)) return MOE_ERR_WORKSPACE;
   // the decode kernels address a tile's activation rows relative to its first
@@ -266,8 +287,14 @@ MOE_API moe_status_t moe_grouped_gemm(const moe_ggemm_desc_t* d, const void* a, 
 
   void* h = ws;
   void* sh_h = static_cast<char*>(ws) + h_bytes(d, d->rows);
-  float* parts = reinterpret_cast<float*>(static_cast<char*>(sh_h) + h_bytes(d, d->shared ? d->shared->rows : 0));
+  const int64_t sh_rows_ws = d->shared ? d->shared->rows : 0;
+  float* parts = reinterpret_cast<float*>(static_cast<char*>(sh_h) + h_bytes(d, sh_rows_ws));
+  // W8A8: the scales of h follow its codes
+  float* h_s = w8a8 ? reinterpret_cast<float*>(static_cast<char*>(h) + h_codes_bytes(d, d->rows)) : nullptr;
+  float* sh_h_s = w8a8 ? reinterpret_cast<float*>(static_cast<char*>(sh_h) + h_codes_bytes(d, sh_rows_ws)) : nullptr;
   GemmArgs p;
+  p.as = p.sh_as = nullptr;
+  p.out_s = p.sh_out_s = nullptr;
   p.rows = routed ? d->rows : 0;
   p.counts = counts;
   p.group_off = group_off;
@@ -278,7 +305,7 @@ MOE_API moe_status_t moe_grouped_gemm(const moe_ggemm_desc_t* d, const void* a, 
   p.sh_rows = se ? se->rows : 0;
   p.packed = d->w_format == MOE_W_PACKED;
   // the wide-tile kernel: bf16 weights, 256-row output blocks of W2 and 128-column blocks of h
-  const bool wide_ok = !f32 && !fp8 && d->hidden % 256 == 0 && d->inter % 128 == 0 &&
+  const bool wide_ok = !f32 && !fp8 && !w8a8 && d->hidden % 256 == 0 && d->inter % 128 == 0 &&
                        d->policy != MOE_GEMM_STREAM_K;
   const bool force = d->policy == MOE_GEMM_WIDE;
   p.wide_min = wide_ok ? (force ? 1 : kWideMinRows) : kNoWide;
@@ -303,6 +330,10 @@ MOE_API moe_status_t moe_grouped_gemm(const moe_ggemm_desc_t* d, const void* a, 
     p.sh_w = se ? se->w13 : nullptr;
     p.sh_s = se ? se->s13 : nullptr;
     p.sh_out = sh_h;
+    p.as = d->a_scales;
+    p.sh_as = se ? se->a_scales : nullptr;
+    p.out_s = h_s;
+    p.sh_out_s = sh_h_s;
     p.n_w_rows = 2 * d->inter;
     p.K = d->hidden;
     p.n_out = d->inter;
@@ -310,7 +341,7 @@ MOE_API moe_status_t moe_grouped_gemm(const moe_ggemm_desc_t* d, const void* a, 
     p.a_blk = d->a_layout == MOE_ACT_BLOCKED16;
     p.sh_a_blk = 0;       // the shared expert reads its rows of x in place
     p.out_blk = h_blk;
-    st = launch_stage(p, f32, fp8, kUp, sk, parts, stream);
+    st = launch_stage(p, f32, fp8, w8a8, kUp, sk, parts, stream);
     if (st != MOE_OK) return st;
   }
   if (down) {
@@ -323,13 +354,16 @@ MOE_API moe_status_t moe_grouped_gemm(const moe_ggemm_desc_t* d, const void* a, 
     p.sh_w = se ? se->w2 : nullptr;
     p.sh_s = se ? se->s2 : nullptr;
     p.sh_out = se ? se->y : nullptr;
+    p.as = h_s;
+    p.sh_as = sh_h_s;
+    p.out_s = p.sh_out_s = nullptr;
     p.n_w_rows = d->hidden;
     p.K = d->inter;
     p.n_out = d->hidden;
     p.n_tiles_n = f32 ? d->hidden / kFBN : d->hidden / 128;
     p.a_blk = p.sh_a_blk = h_blk;  // h
     p.out_blk = 0;                // y rows are read by the combine
-    st = launch_stage(p, f32, fp8, kDown, sk, parts, stream);
+    st = launch_stage(p, f32, fp8, w8a8, kDown, sk, parts, stream);
   }
   return st;
 }

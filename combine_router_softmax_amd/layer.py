@@ -6,6 +6,11 @@ then shared expert) -> combine on the current stream. No host synchronisation
 inside a step: the expert buffer is sized for the worst case (compact) or for
 the fixed rectangle (padded), and the kernels read the real counts on the
 device.
+
+W8A8 (fp8 weights, ``w8a8=True``): the token rows are quantized 1 x 128 once
+(moe_quantize_1x128, the fp8 payload), the dispatch moves codes and scales
+(or the GEMM gathers them), the grouped GEMM runs fp8 x fp8 and returns bf16
+rows, and the combine sums bf16 as before.
 """
 from __future__ import annotations
 
@@ -13,9 +18,10 @@ from typing import Optional
 
 import torch
 
-from . import (ACT_BLOCKED16, ACT_ROWS, COMPACT, GEMM_STREAM_K, GEMM_WIDE, GG_DOWN, GG_FULL, GG_UP, PADDED, W_PACKED, W_ROWMAJOR, SharedExpert,
-               blocked_rows, gemm_desc, moe_combine, moe_dispatch, moe_dispatch_blocked, moe_dispatch_layout,
-               moe_grouped_gemm, moe_grouped_gemm_workspace, moe_layout_rows, moe_pack_weights, moe_route_topk)
+from . import (ACT_BLOCKED16, ACT_ROWS, COMPACT, GEMM_STREAM_K, GEMM_WIDE, GG_DOWN, GG_FULL, GG_UP, PADDED, W_PACKED,
+               W_ROWMAJOR, SharedExpert, blocked_rows, gemm_desc, moe_combine, moe_dispatch, moe_dispatch_blocked,
+               moe_dispatch_fp8, moe_dispatch_layout, moe_grouped_gemm, moe_grouped_gemm_workspace, moe_layout_rows,
+               moe_pack_weights, moe_quantize_1x128, moe_route_topk)
 
 
 class MoEShare:
@@ -24,7 +30,8 @@ class MoEShare:
     def __init__(self, *, n_tokens: int, hidden: int, inter: int, n_experts: int, top_k: int, n_src: int,
                  expert_lo: int, n_local: int, act_dtype: torch.dtype, layout: int = COMPACT,
                  capacity: Optional[int] = None, self_range=(0, 0), device="cuda",
-                 blocked: Optional[bool] = None, policy: Optional[int] = None, gather: Optional[bool] = None):
+                 blocked: Optional[bool] = None, policy: Optional[int] = None, gather: Optional[bool] = None,
+                 w8a8: bool = False):
         self.N, self.H, self.I, self.E, self.K = n_tokens, hidden, inter, n_experts, top_k
         self.S, self.lo, self.L = n_src, expert_lo, n_local
         self.layout = layout
@@ -45,7 +52,10 @@ class MoEShare:
         # cost the dispatch more than that saves on the prefill share
         if blocked is None:
             blocked = False
-        self.blocked = bool(blocked) and act_dtype == torch.bfloat16 and hidden % 32 == 0
+        self.w8a8 = bool(w8a8)
+        if self.w8a8 and act_dtype != torch.bfloat16:
+            raise ValueError("the W8A8 path takes bf16 token rows")
+        self.blocked = bool(blocked) and act_dtype == torch.bfloat16 and hidden % 32 == 0 and not self.w8a8
         self.a_layout = ACT_BLOCKED16 if self.blocked else ACT_ROWS
         # one kernel per product: batches whose experts are expected to hold
         # enough rows take the wide-tile kernel for every group (what the AUTO
@@ -54,7 +64,8 @@ class MoEShare:
         self.policy = (GEMM_WIDE if many_rows else GEMM_STREAM_K) if policy is None else policy
         # the bf16 GEMM kernels can read the routed rows straight from the
         # tokens (row_token of the layout), which leaves out the dispatch copy
-        can_gather = act_dtype == torch.bfloat16 and not self.blocked and n_tokens * hidden * 2 <= 1 << 32
+        can_gather = (act_dtype == torch.bfloat16 and not self.blocked and
+                      n_tokens * hidden * (1 if self.w8a8 else 2) <= 1 << 32)
         self.gather = can_gather if gather is None else bool(gather)
         if self.gather and not can_gather:
             raise ValueError("gathered rows need bf16 activations, row-major rows and tokens below 4 GiB")
@@ -62,6 +73,10 @@ class MoEShare:
         self.topk_idx = torch.empty((n_tokens, top_k), dtype=torch.int32, device=d)
         self.topk_w = torch.empty((n_tokens, top_k), dtype=torch.float32, device=d)
         self.lay = None
+        # W8A8: the quantized token rows (codes, one scale per 128 columns)
+        self.xq = torch.empty((n_tokens, hidden), dtype=torch.uint8, device=d) if self.w8a8 else None
+        self.xs = torch.empty((n_tokens, hidden // 128), dtype=torch.float32, device=d) if self.w8a8 else None
+        self.xes = None
         # the expert-grouped copy of the rows; gathering layers need none (made on first dispatch)
         self.xe = None if self.gather else self._new_xe()
         self.ye = torch.empty((max(self.R, 1), hidden), dtype=act_dtype, device=d)
@@ -76,8 +91,15 @@ class MoEShare:
         self.shared_mode = "fused"
 
     def _new_xe(self):
+        if self.w8a8:
+            self.xes = torch.empty((max(self.R, 1), self.H // 128), dtype=torch.float32, device=self.dev)
+            return torch.empty((max(self.R, 1), self.H), dtype=torch.uint8, device=self.dev)
         return torch.empty((max(blocked_rows(self.R) if self.blocked else self.R, 1), self.H), dtype=self.act_dtype,
                            device=self.dev)
+
+    @property
+    def gemm_act_dtype(self):
+        return torch.uint8 if self.w8a8 else self.act_dtype
 
     # weights: dict with w13 [G,2I,H], w2 [G,H,I], optional s13/s2 (host or device tensors)
     def set_weights(self, routed: dict, shared: Optional[dict] = None, pack: bool = True):
@@ -93,16 +115,18 @@ class MoEShare:
         self.w_format = W_PACKED if (pack and routed["w13"].dtype != torch.float32) else W_ROWMAJOR
         self.w = todev(routed)
         self.sw = todev(shared)
+        if self.w8a8 and self.w.get("s13") is None:
+            raise ValueError("the W8A8 path needs fp8 weights with their 128 x 128 scales")
         self._default_shared_mode()
         wdt = self.w["w13"].dtype
         B0 = self.self_hi - self.self_lo
         se = SharedExpert(rows=B0 if self.sw is not None else 0)
-        desc = gemm_desc(self.L, self.H, self.I, self.act_dtype, wdt, self.layout, self.S, self.capacity, self.R,
-                         shared=se, w_format=self.w_format, a_layout=self.a_layout, policy=self.policy)
+        desc = gemm_desc(self.L, self.H, self.I, self.gemm_act_dtype, wdt, self.layout, self.S, self.capacity,
+                         self.R, shared=se, w_format=self.w_format, a_layout=self.a_layout, policy=self.policy)
         self.ws = torch.zeros(moe_grouped_gemm_workspace(desc), dtype=torch.uint8, device=self.dev)
         if self.sw is not None:
-            sdesc = gemm_desc(1, self.H, self.I, self.act_dtype, self.sw["w13"].dtype, COMPACT, 1, 0, max(B0, 1),
-                              w_format=self.w_format)
+            sdesc = gemm_desc(1, self.H, self.I, self.gemm_act_dtype, self.sw["w13"].dtype, COMPACT, 1, 0,
+                              max(B0, 1), w_format=self.w_format)
             self.sws = torch.zeros(moe_grouped_gemm_workspace(sdesc), dtype=torch.uint8, device=self.dev)
 
     def _shared_arg(self, x):
@@ -110,8 +134,15 @@ class MoEShare:
             return None
         sw = self.sw
         a = x[self.self_lo: self.self_hi]
-        return {"a": a, "w13": sw["w13"], "w2": sw["w2"], "s13": sw.get("s13"), "s2": sw.get("s2"),
-                "y": self.ys[: a.shape[0]]}
+        d = {"a": a, "w13": sw["w13"], "w2": sw["w2"], "s13": sw.get("s13"), "s2": sw.get("s2"),
+             "y": self.ys[: a.shape[0]]}
+        if self.w8a8:
+            d["a"], d["a_scales"] = self.xq[self.self_lo: self.self_hi], self.xs[self.self_lo: self.self_hi]
+        return d
+
+    def quantize(self, x):
+        """W8A8: the fp8 payload of the token rows."""
+        moe_quantize_1x128(x, self.xq, self.xs)
 
     def route(self, logits):
         moe_route_topk(logits, self.K, True, self.topk_idx, self.topk_w)
@@ -123,7 +154,9 @@ class MoEShare:
     def dispatch(self, x):
         if self.xe is None:
             self.xe = self._new_xe()
-        if self.blocked:
+        if self.w8a8:
+            moe_dispatch_fp8(self.xq, self.xs, self.lay["row_of"], self.K, self.R, self.xe, self.xes)
+        elif self.blocked:
             moe_dispatch_blocked(x, self.lay["row_of"], self.K, self.R, self.xe)
         else:
             moe_dispatch(x, self.lay["row_of"], self.K, self.R, self.xe)
@@ -137,8 +170,12 @@ class MoEShare:
             if src is None:
                 raise ValueError("gathered rows need the tokens (src)")
             a, extra["a_rows"] = src, self.lay["row_token"]
+            if self.w8a8:
+                a, extra["a_scales"] = self.xq, self.xs
         else:
             a = self.xe if self.blocked else self.xe[: self.R]
+            if self.w8a8:
+                extra["a_scales"] = self.xes[: self.R]
         moe_grouped_gemm(a, w["w13"], w["w2"], group_off=self.lay["expert_off"],
                          counts=self.lay["counts"], s13=w.get("s13"), s2=w.get("s2"), layout=self.layout,
                          n_src=self.S, capacity=self.capacity, stage=stage, y=self.ye[: self.R], ws=self.ws,
@@ -163,20 +200,21 @@ class MoEShare:
         wdt = self.w["w13"].dtype
         B0 = self.self_hi - self.self_lo
         se = SharedExpert(rows=B0 if self.sw is not None else 0)
-        desc = gemm_desc(self.L, self.H, self.I, self.act_dtype, wdt, self.layout, self.S, self.capacity, self.R,
-                         shared=se, w_format=self.w_format, a_layout=self.a_layout, policy=self.policy)
+        desc = gemm_desc(self.L, self.H, self.I, self.gemm_act_dtype, wdt, self.layout, self.S, self.capacity,
+                         self.R, shared=se, w_format=self.w_format, a_layout=self.a_layout, policy=self.policy)
         self.ws = torch.zeros(moe_grouped_gemm_workspace(desc), dtype=torch.uint8, device=self.dev)
         if self.sw is not None:
-            sdesc = gemm_desc(1, self.H, self.I, self.act_dtype, self.sw["w13"].dtype, COMPACT, 1, 0, max(B0, 1),
-                              w_format=self.w_format)
+            sdesc = gemm_desc(1, self.H, self.I, self.gemm_act_dtype, self.sw["w13"].dtype, COMPACT, 1, 0,
+                              max(B0, 1), w_format=self.w_format)
             self.sws = torch.zeros(moe_grouped_gemm_workspace(sdesc), dtype=torch.uint8, device=self.dev)
 
     def footprint_bytes(self) -> int:
         """Device bytes of the per-step expert buffers (xe, ye and the GEMM
         workspace with h and the partial sums): what the layout choice costs."""
         n = self.ye.numel() * self.ye.element_size() + self.ws.numel()
-        if self.xe is not None:
-            n += self.xe.numel() * self.xe.element_size()
+        for t in (self.xe, self.xes, self.xq, self.xs):
+            if t is not None:
+                n += t.numel() * t.element_size()
         return int(n)
 
     def shared_gemm(self, x, stage=GG_FULL):
@@ -184,8 +222,12 @@ class MoEShare:
             return
         sw = self.sw
         a = x[self.self_lo: self.self_hi]
+        extra = {}
+        if self.w8a8:
+            a, extra["a_scales"] = self.xq[self.self_lo: self.self_hi], self.xs[self.self_lo: self.self_hi]
         moe_grouped_gemm(a, sw["w13"], sw["w2"], group_off=self.shared_off, s13=sw.get("s13"), s2=sw.get("s2"),
-                         layout=COMPACT, stage=stage, y=self.ys[: a.shape[0]], ws=self.sws, w_format=self.w_format)
+                         layout=COMPACT, stage=stage, y=self.ys[: a.shape[0]], ws=self.sws, w_format=self.w_format,
+                         **extra)
 
     def combine(self, out):
         sy = self.ys if (self.sw is not None and self.self_hi > self.self_lo) else None
@@ -215,6 +257,8 @@ class MoEShare:
             else:
                 fn()
 
+        if self.w8a8:
+            run("quantize", lambda: self.quantize(x))
         cur = side = None
         if mode == "stream" and self.sw is not None and self.self_hi > self.self_lo:
             if getattr(self, "_side", None) is None:

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum {
   MOE_OK = 0,
@@ -190,6 +190,35 @@ moe_status_t moe_dispatch_layout_noalloc(const moe_layout_desc_t* d, const int32
 moe_status_t moe_dispatch(const void* x, moe_dtype_t dt, int n_tokens, int hidden, int top_k,
                           const int32_t* row_of, int64_t n_rows, void* xe, hipStream_t stream);
 
+/* ------------------------------------------------------------------ fp8 payload
+ * On-the-fly 1 x 128 quantization of token rows (Perplexity DeepSeek page,
+ * section Quantization: activations take one scale per 128-element vector;
+ * the dispatch payload is fp8 with its scales, lehuy.net page, section
+ * Latency: send without asking, AWS EFA page, section Evaluation). For each
+ * row and each block of 128 columns:
+ *   s = fp32(max |x|) / 448, and s = 1 where that is 0;
+ *   xq = RNE(clamp(fp32(x) / s, -448, 448)) as OCP e4m3fn codes (0x00 for a
+ *   zero result), with correctly rounded fp32 division.
+ *
+ * x  [n_rows, hidden] of dtype dt (MOE_BF16 or MOE_F32), 16-byte aligned.
+ * xq [n_rows, hidden] uint8 out (8-byte aligned), xs [n_rows, hidden / 128]
+ * float32 out. hidden % 128 == 0 (else MOE_ERR_UNSUPPORTED). NaN inputs give
+ * unspecified finite codes.
+ */
+moe_status_t moe_quantize_1x128(const void* x, moe_dtype_t dt, int64_t n_rows, int hidden, uint8_t* xq, float* xs,
+                                hipStream_t stream);
+
+/* moe_dispatch for the fp8 payload: codes and scales of each token row go to
+ * every slot the layout gave it (xeq[row_of[t*K+k]] = xq[t], xes[...] =
+ * xs[t]); bit-exact; unused rows are not written.
+ *
+ * xq [n_tokens, hidden] uint8, xs [n_tokens, hidden / 128] float32 (as
+ * moe_quantize_1x128 wrote them); xeq [n_rows, hidden], xes [n_rows, hidden /
+ * 128]. hidden % 128 == 0; xq and xeq 16-byte aligned.
+ */
+moe_status_t moe_dispatch_fp8(const uint8_t* xq, const float* xs, int n_tokens, int hidden, int top_k,
+                              const int32_t* row_of, int64_t n_rows, uint8_t* xeq, float* xes, hipStream_t stream);
+
 /* The same copy into an expert-grouped buffer in the MOE_ACT_BLOCKED16 layout
  * (same arguments as moe_dispatch): each token row is read once and written to
  * each of its slots' blocks; unused rows are not written.
@@ -238,15 +267,17 @@ typedef struct {
   const void* w2;    /* [1, H, I] */
   const float* s13;  /* fp8 only: [1, 2I/128, H/128] */
   const float* s2;   /* fp8 only: [1, H/128, I/128] */
-  void* y;           /* [rows, H] out (act_dt) */
+  void* y;           /* [rows, H] out (act_dt; bf16 for W8A8) */
+  const float* a_scales; /* W8A8 only: [rows, H/128] scales of the codes in a; else NULL */
 } moe_shared_expert_t;
 
 typedef struct {
   int n_groups;        /* G routed experts in this call (may be 0 with a shared expert) */
   int hidden;          /* H, multiple of 128 */
   int inter;           /* I, multiple of 128 */
-  moe_dtype_t act_dt;  /* a, y, workspace h: MOE_F32 or MOE_BF16 */
-  moe_dtype_t w_dt;    /* weights: MOE_F32 with f32 activations; MOE_BF16 or MOE_FP8_E4M3 with bf16 */
+  moe_dtype_t act_dt;  /* a, y, workspace h: MOE_F32 or MOE_BF16; MOE_FP8_E4M3 = W8A8 (see below) */
+  moe_dtype_t w_dt;    /* weights: MOE_F32 with f32 activations; MOE_BF16 or MOE_FP8_E4M3 with bf16;
+                          MOE_FP8_E4M3 with fp8 activations */
   moe_layout_t layout; /* how rows of a/y are grouped (as moe_dispatch_layout wrote them) */
   int n_src;           /* PADDED: S */
   int capacity;        /* PADDED: rows per (group, source) region */
@@ -264,11 +295,17 @@ typedef struct {
    * their own rows. */
   const int32_t* a_rows;             /* device [rows], or NULL */
   int64_t a_nrows;
+  /* W8A8 (act_dt = w_dt = MOE_FP8_E4M3): a holds e4m3fn codes [R, H] (or
+   * [a_nrows, H] when gathering) and a_scales one float32 scale per row and
+   * 128 columns ([R, H/128], or [a_nrows, H/128]), as moe_quantize_1x128 and
+   * moe_dispatch_fp8 write them; NULL otherwise. */
+  const float* a_scales;
 } moe_ggemm_desc_t;
 
 /* Bytes of scratch moe_grouped_gemm needs (the intermediates h [R, I] and, with
- * a shared expert, [B, I], in the activation dtype, 256-byte aligned); 0 for an
- * invalid descriptor. */
+ * a shared expert, [B, I], in the activation dtype (W8A8: codes plus one
+ * float32 scale per 128 columns), 256-byte aligned); 0 for an invalid
+ * descriptor. */
 size_t moe_grouped_gemm_workspace(const moe_ggemm_desc_t* d);
 
 /* Per-expert SwiGLU FFN over the rows each expert holds (Perplexity DeepSeek
@@ -296,6 +333,16 @@ size_t moe_grouped_gemm_workspace(const moe_ggemm_desc_t* d);
  * The shared expert is either desc->shared (same launches) or a call of its own
  * with n_groups = 1, COMPACT, group_off = {0, B} and a pointing at its rows.
  * MOE_GG_UP then MOE_GG_DOWN with the same workspace equals MOE_GG_FULL.
+ *
+ * W8A8 (act_dt = w_dt = MOE_FP8_E4M3; Perplexity DeepSeek page, section
+ * Quantization): activations and weights both fp8 with block scales, so for
+ * each output element and 128-deep block kb of the reduction
+ *   out += sa[row, kb] * sw[n / 128, kb] * sum_{k in kb} a_code[row, k] w_code[n, k],
+ * accumulated in fp32; h = silu(g) * u is quantized 1 x 128 in the up
+ * projection's epilogue (the moe_quantize_1x128 rule on the fp32 h) and the
+ * down projection reads those codes; y (and the shared expert's y) is bf16.
+ * Needs MOE_ACT_ROWS, a_scales (and shared->a_scales) and 16-byte aligned
+ * code rows; 4-byte aligned scales.
  */
 moe_status_t moe_grouped_gemm(const moe_ggemm_desc_t* d, const void* a, const int32_t* counts,
                               const int32_t* group_off, const void* w13, const void* w2, const float* s13,

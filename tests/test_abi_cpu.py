@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
     assert {"moe_route_topk", "moe_dispatch_layout", "moe_dispatch", "moe_grouped_gemm", "moe_combine"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert moe.moe_abi_version() == 1
+    assert moe.moe_abi_version() == 2
     for s, txt in [(0, b"ok"), (1, b"invalid argument"), (3, b"workspace missing or too small")]:
         assert lib.moe_status_string(s) == txt
 

@@ -164,6 +164,21 @@ def test_gemm_fp8_ragged(layout, hidden, inter):
     assert rel_l2(got, ref) <= 1e-2
 
 
+# A policy that asks for the wide-tile kernel where it cannot run (fp8
+# weights) leaves every group to the stream-K kernel: the same bits as AUTO.
+# (Regression: the schedule once gave such groups to the absent wide kernel,
+# and nothing was computed.)
+@pytest.mark.parametrize("layout", [COMPACT, PADDED])
+def test_gemm_fp8_policy_wide_runs_stream_k(layout):
+    cfg = get_config("kimi_k2_ep8", hidden=512, inter=256)
+    got, ref, (a, dw, kw) = _gemm_case(cfg, [300, 0, 129, 1000], layout, seed=21, policy=moe.GEMM_WIDE)
+    assert rel_l2(got, ref) <= 1e-2
+    y_wide = kw["y"].clone()
+    kw["y"].fill_(3.0)
+    moe.moe_grouped_gemm(a.cuda(), dw["w13"], dw["w2"], s13=dw["s13"], s2=dw["s2"], **dict(kw, policy=moe.GEMM_AUTO))
+    assert torch.equal(kw["y"].view(torch.int16), y_wide.view(torch.int16))
+
+
 # Blocked activation rows through the fp8 kernel give the same bits as row-major rows.
 @pytest.mark.parametrize("layout", [COMPACT, PADDED])
 def test_gemm_fp8_blocked_rows_match_row_major(layout):
