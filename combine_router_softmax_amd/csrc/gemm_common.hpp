@@ -452,19 +452,6 @@ __device__ __forceinline__ void sum_partials(f32x16_t (&acc)[NA], int w_lo, int 
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// Global -> LDS copy of 16 bytes per lane (lane l writes bytes [16 l, 16 l +
-// 16) of the wave's KiB at lds), from scalar base + the lane's 32-bit offset:
-// global_load_lds as inline assembly, so that the compiler's wait-count
-// analysis does not see it. (With an LDS-writing global load outstanding that
-// analysis waits for every vector-memory op before the next use of any loaded
-// register, which would cap the prefetch at one stage.) The caller's own
-// counted waits must cover it; ops the analysis does not know of only make
-// its waits longer, since the count retires in order.
-__device__ __forceinline__ void lds_dma16_untracked(gptr<char> base, uint32_t lane_off, const void* lds) {
-  const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_ptr_t)lds);
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(lane_off), "s"(base), "{m0}"(l) : "memory");
-}
-
 // Raw buffer resource over the 4 GiB from a wave-uniform base (scalar
 // registers): a buffer load addresses base + scalar offset + the lane's 32-bit
 // offset + an immediate, so no per-lane 64-bit address is held in registers.

@@ -70,9 +70,13 @@ __device__ __forceinline__ void f8_run(const GemmArgs& p, const Tile& tl, int n,
   // Weights and scales come by buffer loads (see buf_rsrc) from a resource at
   // the expert's base, with a scalar offset per (N block, chunk) and a
   // loop-invariant lane offset. (The activations go to LDS by global_load_lds
-  // (lds_dma16_untracked): the buffer form of the LDS copy is not used, its
-  // LDS addressing on this chip - scalar offset, destinations above 64 KiB -
-  // not being established.)
+  // through the compiler's builtin, so its wait analysis sees the copies and
+  // waits for them before the LDS reads: the completion of an LDS copy is not
+  // ordered with the loads into registers, so the counted waits below alone
+  // do not guarantee it - with them alone the W8A8 kernel read stale rows now
+  // and then. The buffer form of the LDS copy is not used, its LDS addressing
+  // on this chip - scalar offset, destinations above 64 KiB - not being
+  // established.)
   __amdgpu_buffer_rsrc_t rw;
   uint32_t woff;
   if constexpr (PACKED) {
@@ -194,7 +198,8 @@ __device__ __forceinline__ void f8_run(const GemmArgs& p, const Tile& tl, int n,
     const int k_ = k_ld, c_ = c_ld;                                                                         \
     const gptr<char> xc_ = xb + uint64_t(c_) * xstep * 2; /* the chunk's base: scalar */                   \
     _Pragma("unroll") for (int q = 0; q < XL; ++q)                                                          \
-      lds_dma16_untracked(xc_, xoff[q], (XBUF_) + (kF8Waves * q + wv) * 512);                               \
+      __builtin_amdgcn_global_load_lds(at<void>(xc_, 0, xoff[q]), (lds_ptr_t)((XBUF_) + (kF8Waves * q + wv) * 512), \
+                                       16, 0, 0);                                                           \
     _Pragma("unroll") for (int a = 0; a < 2; ++a) SR_[a] = scale(k_, c_, a);                                \
   }
 #define MOE_F8_PIECE(WR_, J_)                                                                               \
