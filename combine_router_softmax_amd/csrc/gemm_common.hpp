@@ -315,7 +315,6 @@ __device__ __forceinline__ float silu_f(float g) { return g / (1.f + __expf(-g))
 // rounding to bf16. (v_cvt_scalef32_pk_bf16_fp8 would apply only the
 // power-of-two exponent of a scale, which block scales are not.)
 __device__ __forceinline__ bf16x8_t fp8x8_dequant(uint32_t w0, uint32_t w1, float s) {
-  typedef float f32x2_t __attribute__((ext_vector_type(2)));
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   const bf16x2_t r0 = __builtin_convertvector(__builtin_amdgcn_cvt_pk_f32_fp8(w0, false) * s, bf16x2_t);
   const bf16x2_t r1 = __builtin_convertvector(__builtin_amdgcn_cvt_pk_f32_fp8(w0, true) * s, bf16x2_t);

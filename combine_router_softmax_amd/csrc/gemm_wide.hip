@@ -44,7 +44,7 @@ namespace {
 // its share of the loads in between; one barrier per stage (in the middle of
 // its last step) publishes the next stage's activations.
 constexpr int kAK = 64;                 // reduction depth of one stage
-constexpr int kARing = 2;               // LDS ring depth (stages)
+// (the LDS ring holds two stages: X[0], X[1])
 constexpr int kAStage = kWM * kAK;      // elements of one activation stage (32 KiB)
 // s_waitcnt operand: this wave's LDS operations done, vector memory not waited for
 constexpr int kWaitLgkm0 = waitcnt_vm(63) & ~(15 << 8);

@@ -10,33 +10,30 @@
 // Work decomposition (routing-aware, persistent; the page's point that kernels
 // must read the per-expert counts on the device rather than size the work from
 // the buffer bound): a fixed grid of workgroups walks a tile list built in
-// every workgroup from the device counts. A tile is (expert, 128-row block,
-// N block); row blocks are the fastest index, so workgroups that share a
-// weight block run side by side and the weight block is fetched from HBM
-// once. Empty experts produce no tiles.
-//
-// Decode tile (4 waves, ffn_bf16_kernel): up = 64 rows x 64 h columns, i.e.
-// 64 gate + 64 up weight rows; down = 64 rows x 128 output columns. Each wave
-// owns 32 weight rows (up: 16 gate + the 16 matching up rows, so SwiGLU pairs
-// land in one lane) and all row blocks. MFMA v_mfma_f32_32x32x16_bf16 with the
-// weights as the A operand (32 weight rows) and the activations as the B
-// operand (32 rows); 32-row blocks with no rows are skipped, so a decode
-// expert with ~32 rows costs one MFMA column block while the weights stream
-// once.
-//
-// Data path per 128-deep K chunk: each lane loads its weight row's pieces
-// straight from HBM into registers (chunks ahead), and the workgroup stages
-// the activation chunk [64 rows x 128] in LDS by LDS DMA (one barrier per
-// chunk). The reduction order inside a chunk is permuted identically for both
-// operands so every weight load is a 64-byte run. Groups with many rows take
-// the wide-tile kernel instead.
-//
-// fp8 e4m3 weights (ffn_fp8_kernel): each code is decoded exactly to fp32,
-// multiplied by its 128x128 block's fp32 scale and rounded once to bf16 in
-// registers, then the bf16 MFMA runs as for bf16 weights (W8A16).
+// every workgroup from the device counts. A tile is (expert, row block, N
+// block); empty experts produce no tiles. Four kernel families share that
+// scheduler (gemm_common.hpp), each in its own translation unit:
+//  - ffn_bf16_kernel (gemm_bf16.hip): decode-shaped groups, bf16 weights;
+//    tiles of 64 rows x 256 weight rows on 8-wave workgroups, stream-K over
+//    (tile, 128-deep chunk) iterations, weights streamed from HBM into
+//    registers, activations copied into LDS;
+//  - ffn_fp8_kernel (gemm_fp8.hip): fp8 e4m3 weights with 128 x 128 scales and
+//    bf16 activations (W8A16): 96 rows x 512 weight rows on 8 waves, each code
+//    decoded exactly, scaled and rounded once to bf16 in registers;
+//  - ffn_w8a8_kernel (gemm_w8a8.hip): fp8 weights and fp8 activations with
+//    1 x 128 scales: the same tiles on 4 waves, fp8 MFMA with the block scales
+//    applied per 128-deep chunk, h quantized in the up projection's epilogue;
+//  - ffn_wide_kernel (gemm_wide.hip): groups with many rows: 256 x 256 tiles on
+//    4 waves, weights in a register ring, activations staged through registers
+//    into LDS, remainder tiles split along K.
+// Tiles cut by a stream-K or K-split boundary leave fp32 partial sums that a
+// fix-up kernel adds in a fixed order (deterministic) before the epilogue.
+// MFMA with the weights as the A operand (32 weight rows) and the activations
+// as the B operand; each wave owns 32-row weight blocks (up: 16 gate rows and
+// the 16 matching up rows, so the SwiGLU pairs land in one lane).
 //
 // fp32 activations + fp32 weights (small parity problems) use a plain SIMT
-// kernel with the same scheduler.
+// kernel with the same scheduler (below).
 #include "gemm_common.hpp"
 
 namespace moe {
