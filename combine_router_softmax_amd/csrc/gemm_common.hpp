@@ -370,6 +370,31 @@ __device__ inline int sk_owner(int64_t i, int64_t total, int G) {
   return int(((i + 1) * G + total - 1) / total) - 1;
 }
 
+// Data-parallel + stream-K split (the fp8 decode kernels): of the launch's
+// n_tiles tiles (nc chunks each) over G workgroups, workgroup range r first
+// takes `whole` = n_tiles / G consecutive whole tiles, [r whole nc, (r + 1)
+// whole nc), and then an even share of the remaining tiles' iterations,
+// rem_base + [sk_start(r, rem, G), sk_start(r + 1, rem, G)). Only the second
+// part ever cuts a tile, so partial sums number about 2 G fewer than with
+// stream-K over everything, and during the first part all workgroups are at
+// the same chunk index of their tiles, so the tiles of one expert (which sit
+// in neighbouring ranges on one XCD) read each activation chunk at about the
+// same time and the XCD's L2 serves the repeats.
+struct DpSk {
+  int G;             // ranges (workgroups used)
+  int whole;         // whole tiles per range, taken first
+  int64_t rem_base;  // first iteration of the remainder tiles
+  int64_t rem;       // iterations of the remainder tiles
+};
+__device__ inline DpSk dpsk_split(int n_tiles, int nc, int max_grid) {
+  DpSk d;
+  d.G = sk_grid(int64_t(n_tiles) * nc, max_grid);
+  d.whole = n_tiles / d.G;
+  d.rem_base = int64_t(d.whole) * d.G * nc;
+  d.rem = int64_t(n_tiles) * nc - d.rem_base;
+  return d;
+}
+
 // Partial slot of workgroup b: 0 for its first tile, 1 for its last.
 __device__ inline float* sk_slot(float* parts, int b, int slot) {
   return parts + (size_t(b) * 2 + slot) * kPartFloats;

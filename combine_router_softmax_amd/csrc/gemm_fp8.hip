@@ -340,36 +340,40 @@ __global__ __launch_bounds__(kF8Threads, 1) void ffn_fp8_kernel(GemmArgs p, floa
   const int ntn4 = (p.n_tiles_n + kF8NB - 1) / kF8NB;
   const int n_tiles = build_schedule<kF8Threads>(p, kF8BM, ntn4, false, sh);
   const int nchunks = p.K / kKC;
-  const int64_t total = int64_t(n_tiles) * nchunks;
-  const int G = sk_grid(total, kF8Grid);
-  if (int(blockIdx.x) >= G) return;  // uniform
+  const DpSk sp = dpsk_split(n_tiles, nchunks, kF8Grid);
+  if (int(blockIdx.x) >= sp.G) return;  // uniform
+  const int G = sp.G;
   const int rng = int(blockIdx.x % kXcds) * (G / kXcds) + int(blockIdx.x / kXcds);
-  const int64_t i0 = sk_start(rng, total, G), i1 = sk_start(rng + 1, total, G);
-  if (i0 >= i1) return;  // uniform
-  const int t_first = int(i0 / nchunks), t_last = int((i1 - 1) / nchunks);
-  for (int t = t_first; t <= t_last;) {
-    const Tile tl = decode_tile(p, kF8BM, ntn4, sh, t);
-    build_rowmap<kF8Threads>(p, tl, kF8BM, sh, true);
-    const int n = tl.mtiles == 1 ? min(t_last - t + 1, ntn4 - tl.nt) : 1;
-    const int64_t t0 = int64_t(t) * nchunks;
-    const int it_begin = int(max<int64_t>(i0 - t0, 0));
-    const int it_end = int(min<int64_t>(i1 - t0, int64_t(n) * nchunks));
-    const bool split_first = it_begin > 0 || (n == 1 && it_end < nchunks);
-    const bool split_last = it_end < n * nchunks;
-    float* part_first = split_first ? f8_slot(parts, rng, t == t_first ? 0 : 1) : nullptr;
-    float* part_last = n == 1 ? part_first : (split_last ? f8_slot(parts, rng, 1) : nullptr);
-    auto run = [&](auto stream_tag) __attribute__((always_inline)) {
-      constexpr bool ST = decltype(stream_tag)::value;
-      switch ((tl.nrows + 31) / 32) {
-        case 1: f8_run<KIND, PACKED, 1, ST>(p, tl, n, sh, x0, x1, x2, it_begin, it_end, part_first, part_last); break;
-        case 2: f8_run<KIND, PACKED, 2, ST>(p, tl, n, sh, x0, x1, x2, it_begin, it_end, part_first, part_last); break;
-        default: f8_run<KIND, PACKED, 3, ST>(p, tl, n, sh, x0, x1, x2, it_begin, it_end, part_first, part_last); break;
-      }
-    };
-    if (tl.mtiles == 1) run(std::true_type{});
-    else run(std::false_type{});
-    __syncthreads();  // rowmap is rewritten by the next run
-    t += n;
+  // the range's whole tiles first, then its share of the remainder
+  for (int part = 0; part < 2; ++part) {
+    const int64_t i0 = part == 0 ? int64_t(rng) * sp.whole * nchunks : sp.rem_base + sk_start(rng, sp.rem, G);
+    const int64_t i1 = part == 0 ? int64_t(rng + 1) * sp.whole * nchunks : sp.rem_base + sk_start(rng + 1, sp.rem, G);
+    if (i0 >= i1) continue;  // uniform
+    const int t_first = int(i0 / nchunks), t_last = int((i1 - 1) / nchunks);
+    for (int t = t_first; t <= t_last;) {
+      const Tile tl = decode_tile(p, kF8BM, ntn4, sh, t);
+      build_rowmap<kF8Threads>(p, tl, kF8BM, sh, true);
+      const int n = tl.mtiles == 1 ? min(t_last - t + 1, ntn4 - tl.nt) : 1;
+      const int64_t t0 = int64_t(t) * nchunks;
+      const int it_begin = int(max<int64_t>(i0 - t0, 0));
+      const int it_end = int(min<int64_t>(i1 - t0, int64_t(n) * nchunks));
+      const bool split_first = it_begin > 0 || (n == 1 && it_end < nchunks);
+      const bool split_last = it_end < n * nchunks;
+      float* part_first = split_first ? f8_slot(parts, rng, t == t_first ? 0 : 1) : nullptr;
+      float* part_last = n == 1 ? part_first : (split_last ? f8_slot(parts, rng, 1) : nullptr);
+      auto run = [&](auto stream_tag) __attribute__((always_inline)) {
+        constexpr bool ST = decltype(stream_tag)::value;
+        switch ((tl.nrows + 31) / 32) {
+          case 1: f8_run<KIND, PACKED, 1, ST>(p, tl, n, sh, x0, x1, x2, it_begin, it_end, part_first, part_last); break;
+          case 2: f8_run<KIND, PACKED, 2, ST>(p, tl, n, sh, x0, x1, x2, it_begin, it_end, part_first, part_last); break;
+          default: f8_run<KIND, PACKED, 3, ST>(p, tl, n, sh, x0, x1, x2, it_begin, it_end, part_first, part_last); break;
+        }
+      };
+      if (tl.mtiles == 1) run(std::true_type{});
+      else run(std::false_type{});
+      __syncthreads();  // rowmap is rewritten by the next run
+      t += n;
+    }
   }
 }
 
@@ -388,24 +392,25 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_fp8_fixup_kernel(GemmArgs p,
   const int ntn4 = (p.n_tiles_n + kF8NB - 1) / kF8NB;
   const int n_tiles = build_schedule(p, kF8BM, ntn4, false, sh);
   const int nchunks = p.K / kKC;
-  const int64_t total = int64_t(n_tiles) * nchunks;
+  const DpSk sp = dpsk_split(n_tiles, nchunks, kF8Grid);
   const int j = blockIdx.x, m = blockIdx.y / kF8MB, b = blockIdx.y % kF8MB;
-  const int G = sk_grid(total, kF8Grid);
-  if (j + 1 >= G) return;  // uniform: boundaries lie between ranges 0 .. G-1
-  const int64_t ib = sk_start(j + 1, total, G);
-  if (ib <= 0 || ib >= total || ib % nchunks == 0) return;  // not inside a tile
+  const int G = sp.G;
+  if (j + 1 >= G) return;  // uniform: boundaries lie between the remainder shares of ranges 0 .. G-1
+  // (the whole-tile parts never cut a tile)
+  const int64_t ib = sp.rem_base + sk_start(j + 1, sp.rem, G);
+  if (ib <= sp.rem_base || ib >= sp.rem_base + sp.rem || ib % nchunks == 0) return;  // not inside a tile
   const int t = int(ib / nchunks);
-  if (j > 0 && sk_start(j, total, G) > int64_t(t) * nchunks) return;  // an earlier boundary owns this tile
+  if (j > 0 && sp.rem_base + sk_start(j, sp.rem, G) > int64_t(t) * nchunks) return;  // an earlier boundary owns this tile
   Tile tl = decode_tile(p, kF8BM, ntn4, sh, t);
   if (b * 32 >= tl.nrows || kF8NB * tl.nt + m >= p.n_tiles_n) return;  // uniform: no rows / no such N block
   build_rowmap(p, tl, kF8BM, sh);
-  const int b_lo = sk_owner(int64_t(t) * nchunks, total, G);
-  const int b_hi = sk_owner(int64_t(t + 1) * nchunks - 1, total, G);
+  const int b_lo = sk_owner(int64_t(t) * nchunks - sp.rem_base, sp.rem, G);
+  const int b_hi = sk_owner(int64_t(t + 1) * nchunks - 1 - sp.rem_base, sp.rem, G);
   f32x16_t acc[1];
   sum_partials(
       acc, b_lo, b_hi,
       [&](int w) -> const float* {
-        const int64_t s0 = sk_start(w, total, G), s1 = sk_start(w + 1, total, G);
+        const int64_t s0 = sp.rem_base + sk_start(w, sp.rem, G), s1 = sp.rem_base + sk_start(w + 1, sp.rem, G);
         return s0 < s1 ? f8_slot(const_cast<float*>(parts), w, int(s0 / nchunks) == t ? 0 : 1) : nullptr;
       },
       [&](int, int q) { return f8_part_idx(m / 2 * 4 + wv, m % 2, b, q, lane); });
