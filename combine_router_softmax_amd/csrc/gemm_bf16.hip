@@ -21,24 +21,24 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_fixup_kernel(GemmArgs p, con
   const int ntn2 = (p.n_tiles_n + kBfNB - 1) / kBfNB;
   const int n_tiles = build_schedule(p, kBfBM, ntn2, false, sh);
   const int nchunks = p.K / kKC;
-  const int64_t total = int64_t(n_tiles) * nchunks;
+  const DpSk sp = dpsk_split(n_tiles, nchunks, kBfGrid);
   const int j = blockIdx.x, m = blockIdx.y / kBfMB, b = blockIdx.y % kBfMB;
-  const int G = sk_grid(total, kBfGrid);
-  if (j + 1 >= G) return;  // uniform: boundaries lie between ranges 0 .. G-1
-  const int64_t ib = sk_start(j + 1, total, G);
-  if (ib <= 0 || ib >= total || ib % nchunks == 0) return;  // not inside a tile
+  const int G = sp.G;
+  if (j + 1 >= G) return;  // uniform: boundaries lie between the remainder shares of ranges 0 .. G-1
+  const int64_t ib = sp.rem_base + sk_start(j + 1, sp.rem, G);
+  if (ib <= sp.rem_base || ib >= sp.rem_base + sp.rem || ib % nchunks == 0) return;  // not inside a tile
   const int t = int(ib / nchunks);
-  if (j > 0 && sk_start(j, total, G) > int64_t(t) * nchunks) return;  // an earlier boundary owns this tile
+  if (j > 0 && sp.rem_base + sk_start(j, sp.rem, G) > int64_t(t) * nchunks) return;  // an earlier boundary owns this tile
   Tile tl = decode_tile(p, kBfBM, ntn2, sh, t);
   if (b * 32 >= tl.nrows || kBfNB * tl.nt + m >= p.n_tiles_n) return;  // uniform: no rows / no such N block
   build_rowmap(p, tl, kBfBM, sh);
-  const int b_lo = sk_owner(int64_t(t) * nchunks, total, G);
-  const int b_hi = sk_owner(int64_t(t + 1) * nchunks - 1, total, G);
+  const int b_lo = sk_owner(int64_t(t) * nchunks - sp.rem_base, sp.rem, G);
+  const int b_hi = sk_owner(int64_t(t + 1) * nchunks - 1 - sp.rem_base, sp.rem, G);
   f32x16_t acc[1];
   sum_partials(
       acc, b_lo, b_hi,
       [&](int w) -> const float* {
-        const int64_t s0 = sk_start(w, total, G), s1 = sk_start(w + 1, total, G);
+        const int64_t s0 = sp.rem_base + sk_start(w, sp.rem, G), s1 = sp.rem_base + sk_start(w + 1, sp.rem, G);
         return s0 < s1 ? sk_slot(const_cast<float*>(parts), w, int(s0 / nchunks) == t ? 0 : 1) : nullptr;
       },
       [&](int, int q) { return bf_part_idx(4 * m + wv, b, q, lane); });
@@ -253,36 +253,40 @@ __global__ __launch_bounds__(kBfThreads, 1) void ffn_bf16_kernel(GemmArgs p, flo
   const int ntn2 = (p.n_tiles_n + kBfNB - 1) / kBfNB;
   const int n_tiles = build_schedule<kBfThreads>(p, kBfBM, ntn2, false, sh);
   const int nchunks = p.K / kKC;
-  const int64_t total = int64_t(n_tiles) * nchunks;
-  const int G = sk_grid(total, kBfGrid);
-  if (int(blockIdx.x) >= G) return;  // uniform
+  const DpSk sp = dpsk_split(n_tiles, nchunks, kBfGrid);
+  if (int(blockIdx.x) >= sp.G) return;  // uniform
+  const int G = sp.G;
   const int rng = int(blockIdx.x % kXcds) * (G / kXcds) + int(blockIdx.x / kXcds);
-  const int64_t i0 = sk_start(rng, total, G), i1 = sk_start(rng + 1, total, G);
-  if (i0 >= i1) return;  // uniform
-  const int t_first = int(i0 / nchunks), t_last = int((i1 - 1) / nchunks);
-  for (int t = t_first; t <= t_last;) {
-    const Tile tl = decode_tile(p, kBfBM, ntn2, sh, t);
-    build_rowmap<kBfThreads>(p, tl, kBfBM, sh, true);
-    // a run: with one row tile the group's next tiles are its next N tiles
-    // (same activation rows)
-    const int n = tl.mtiles == 1 ? min(t_last - t + 1, ntn2 - tl.nt) : 1;
-    const int64_t t0 = int64_t(t) * nchunks;
-    const int it_begin = int(max<int64_t>(i0 - t0, 0));
-    const int it_end = int(min<int64_t>(i1 - t0, int64_t(n) * nchunks));
-    // a split tile leaves partials in the workgroup's slot (0 for its first tile, 1 for its last)
-    const bool split_first = it_begin > 0 || (n == 1 && it_end < nchunks);
-    const bool split_last = it_end < n * nchunks;
-    float* part_first = split_first ? sk_slot(parts, rng, t == t_first ? 0 : 1) : nullptr;
-    float* part_last = n == 1 ? part_first : (split_last ? sk_slot(parts, rng, 1) : nullptr);
-    auto run = [&](auto stream_tag) __attribute__((always_inline)) {
-      constexpr bool ST = decltype(stream_tag)::value;
-      if (tl.nrows <= 32) bf_run<KIND, PACKED, 1, ST>(p, tl, n, sh, x0, x1, x2, it_begin, it_end, part_first, part_last);
-      else bf_run<KIND, PACKED, 2, ST>(p, tl, n, sh, x0, x1, x2, it_begin, it_end, part_first, part_last);
-    };
-    if (tl.mtiles == 1) run(std::true_type{});
-    else run(std::false_type{});
-    __syncthreads();  // rowmap is rewritten by the next run
-    t += n;
+  // the range's whole tiles first, then its share of the remainder
+  for (int part = 0; part < 2; ++part) {
+    const int64_t i0 = part == 0 ? int64_t(rng) * sp.whole * nchunks : sp.rem_base + sk_start(rng, sp.rem, G);
+    const int64_t i1 = part == 0 ? int64_t(rng + 1) * sp.whole * nchunks : sp.rem_base + sk_start(rng + 1, sp.rem, G);
+    if (i0 >= i1) continue;  // uniform
+    const int t_first = int(i0 / nchunks), t_last = int((i1 - 1) / nchunks);
+    for (int t = t_first; t <= t_last;) {
+      const Tile tl = decode_tile(p, kBfBM, ntn2, sh, t);
+      build_rowmap<kBfThreads>(p, tl, kBfBM, sh, true);
+      // a run: with one row tile the group's next tiles are its next N tiles
+      // (same activation rows)
+      const int n = tl.mtiles == 1 ? min(t_last - t + 1, ntn2 - tl.nt) : 1;
+      const int64_t t0 = int64_t(t) * nchunks;
+      const int it_begin = int(max<int64_t>(i0 - t0, 0));
+      const int it_end = int(min<int64_t>(i1 - t0, int64_t(n) * nchunks));
+      // a split tile leaves partials in the workgroup's slot (0 for its first tile, 1 for its last)
+      const bool split_first = it_begin > 0 || (n == 1 && it_end < nchunks);
+      const bool split_last = it_end < n * nchunks;
+      float* part_first = split_first ? sk_slot(parts, rng, t == t_first ? 0 : 1) : nullptr;
+      float* part_last = n == 1 ? part_first : (split_last ? sk_slot(parts, rng, 1) : nullptr);
+      auto run = [&](auto stream_tag) __attribute__((always_inline)) {
+        constexpr bool ST = decltype(stream_tag)::value;
+        if (tl.nrows <= 32) bf_run<KIND, PACKED, 1, ST>(p, tl, n, sh, x0, x1, x2, it_begin, it_end, part_first, part_last);
+        else bf_run<KIND, PACKED, 2, ST>(p, tl, n, sh, x0, x1, x2, it_begin, it_end, part_first, part_last);
+      };
+      if (tl.mtiles == 1) run(std::true_type{});
+      else run(std::false_type{});
+      __syncthreads();  // rowmap is rewritten by the next run
+      t += n;
+    }
   }
 }
 

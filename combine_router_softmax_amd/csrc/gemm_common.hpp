@@ -370,7 +370,7 @@ __device__ inline int sk_owner(int64_t i, int64_t total, int G) {
   return int(((i + 1) * G + total - 1) / total) - 1;
 }
 
-// Data-parallel + stream-K split (the fp8 decode kernels): of the launch's
+// Data-parallel + stream-K split (the decode kernels): of the launch's
 // n_tiles tiles (nc chunks each) over G workgroups, workgroup range r first
 // takes `whole` = n_tiles / G consecutive whole tiles, [r whole nc, (r + 1)
 // whole nc), and then an even share of the remaining tiles' iterations,
