@@ -130,7 +130,8 @@ def _kernel_source_hash():
     csrc = os.path.join(ROOT, "combine_router_softmax_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(csrc, "gemm_*"))) + [os.path.join(csrc, "grouped_gemm.hip"),
-                                                                   os.path.join(csrc, "moe_common.hpp")]:
+                                                                   os.path.join(csrc, "moe_common.hpp"),
+                                                                   os.path.join(csrc, "fp8_quant.hpp")]:
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -364,7 +365,7 @@ def _summarize(cfg, share, res, B0):
     else:
         roof = {"bound": "hbm", "achieved": round(byts / dom_us / 1e3, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = _traffic(cfg.name + (":w8a8" if share.w8a8 else ""), dom) if share.layout == 0 else None
+    roof["traffic"] = _traffic(cfg.name + ("_w8a8" if share.w8a8 else ""), dom) if share.layout == 0 else None
     names = dict(KERNEL_OF_STEP)
     names.update(KERNEL_OF_STEP_FP8 if cfg.weight == "fp8_e4m3" else {})
     names.update(KERNEL_OF_STEP_W8A8 if share.w8a8 else {})
@@ -490,6 +491,9 @@ def main(argv=None):
     ap.add_argument("--shared-mode", choices=["layer", "fused", "serial", "stream"], default="layer",
                     help="shared expert inside the routed launches, after them, or on a second stream "
                          "(default: the layer's choice)")
+    ap.add_argument("--w8a8", action="store_true",
+                    help="run the headline workload on the W8A8 path (fp8 activations; a bf16 checkpoint is "
+                         "quantized to fp8 128 x 128 tiles), e.g. to profile the W8A8 kernels")
     ap.add_argument("--extras", default=DEFAULT_EXTRAS,
                     help="comma-separated workloads[:padded] measured after the headline, or 'none'")
     ap.add_argument("--extra-steps", type=int, default=20)
@@ -516,12 +520,22 @@ def main(argv=None):
         return 1
 
     if args.copy_calib:
+        # a plain 1 GiB device copy: the counter calibration for rocprofv3 --pmc,
+        # and (timed) the practical streaming rate (read + write bytes / time)
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_calib_bytes": 1 << 30, "launches": 3}))
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+        for a, b in ev:
+            a.record()
+            dst.copy_(src)
+            b.record()
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        print(json.dumps({"copy_calib_bytes": 1 << 30, "launches": 13, "copy_ms": round(ms, 4),
+                          "copy_GBps_read_plus_write": round(2 * (1 << 30) / ms / 1e6, 1)}))
         return 0
 
     import combine_router_softmax_amd as moe
@@ -530,6 +544,8 @@ def main(argv=None):
 
     moe.lib()  # raises if the HIP library is missing: there is no other path
     cfg = get_config(args.workload)
+    if args.w8a8 and cfg.weight != "fp8_e4m3":
+        cfg = get_config(args.workload, weight="fp8_e4m3")
     t_gen = time.perf_counter()
     d = make_inputs(cfg, 0)
     t_gen = time.perf_counter() - t_gen
@@ -540,7 +556,7 @@ def main(argv=None):
                         blocked=None if args.xe_layout == "auto" else args.xe_layout == "blocked",
                         gather=None if args.gather == "auto" else args.gather == "on",
                         policy={"layer": None, "auto": moe.GEMM_AUTO, "wide": moe.GEMM_WIDE,
-                                "stream_k": moe.GEMM_STREAM_K}[args.gemm_policy])
+                                "stream_k": moe.GEMM_STREAM_K}[args.gemm_policy], w8a8=args.w8a8)
     logits, offs, x = _dev_inputs(d)
     out = torch.zeros_like(x)
     torch.cuda.synchronize()
@@ -589,9 +605,9 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.act == "bf16" else "f32",
+        "dtype": "fp8_e4m3" if args.w8a8 else ("bf16" if cfg.act == "bf16" else "f32"),
         "data": "synthetic",
-        "config": {"workload": cfg.name, "layout": args.layout,
+        "config": {"workload": cfg.name + (":w8a8" if args.w8a8 else ""), "layout": args.layout,
                    "xe_layout": "gathered" if share.gather else "blocked" if share.blocked else "rows",
                    "shared_mode": share.shared_mode if args.shared_mode == "layer" else args.shared_mode,
                    "global_batch": N, "tokens_per_gpu": B0,
