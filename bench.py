@@ -75,12 +75,15 @@ def tokens_per_expert(batch, qlen, top_k, ep, n_experts):
     return batch * qlen * top_k * ep / n_experts
 
 
-def algorithmic_model(cfg, counts, row_of, B0, w8a8=False):
+def algorithmic_model(cfg, counts, row_of, B0, w8a8=False, shared_apart=False):
     """Algorithmic bytes and FLOP per call from the actual routing of the step.
 
     counts [L, S] rows per local expert and source; row_of [N*K] (-1 = not local).
     W8A8: the GEMMs read fp8 rows (1 byte + 4 bytes per 128 columns) and the
     up projection writes fp8 h; y and the combine stay bf16.
+    shared_apart: the shared expert runs as calls of its own (on a second
+    stream), so gemm_up / gemm_down carry the routed rows only and the shared
+    expert's bytes and FLOP go to a "shared" entry.
     """
     H, I, K = cfg.hidden, cfg.inter, cfg.top_k
     wb = 1 if cfg.weight == "fp8_e4m3" else (4 if cfg.weight == "f32" else 2)
@@ -120,6 +123,15 @@ def algorithmic_model(cfg, counts, row_of, B0, w8a8=False):
         b["dispatch"] = int((U + M) * H * qb + N * K * 4)
         b["gemm_up"] = int(up_w + sh_up_w + MS * H * qb + MS * I * qb)
         b["gemm_down"] = int(down_w + sh_down_w + MS * I * qb + MS * H * 2)
+    if shared_apart and cfg.shared:
+        b, f = model["bytes"], model["flops"]
+        rb = qb if w8a8 else ab  # bytes of an fp8 or activation element of x and h
+        sh = {"gemm_up": sh_up_w + B0 * H * rb + B0 * I * rb, "gemm_down": sh_down_w + B0 * I * rb + B0 * H * ab}
+        for n in ("gemm_up", "gemm_down"):
+            b[n] = int(b[n] - sh[n])
+        b["shared"] = int(sh["gemm_up"] + sh["gemm_down"])
+        f["gemm_up"], f["gemm_down"] = 2 * M * H * 2 * I, 2 * M * I * H
+        f["shared"] = 2 * B0 * H * 2 * I + 2 * B0 * I * H
     return model
 
 
@@ -303,7 +315,7 @@ class Bench:
             del g
         return {"ms": graph_ms if graph_ms is not None else eager_ms, "ms_eager": eager_ms,
                 "timing": "hip_graph_replay" if graph_ms is not None else "eager", "per_call_us": per_call_us,
-                "wall": wall}
+                "wall": wall, "shared_mode": shared_mode or share.shared_mode}
 
 
 def _make_share(cfg, d, layout, *, policy=None, gather=None, blocked=None, weights_from=None, self_range=None,
@@ -336,9 +348,10 @@ def _summarize(cfg, share, res, B0):
     dominant kernel's roofline."""
     counts = share.lay["counts"].cpu().numpy().astype(np.int64)
     row_of = share.lay["row_of"].cpu().numpy().astype(np.int64)
-    model = algorithmic_model(cfg, counts, row_of, B0, w8a8=share.w8a8)
+    apart = res.get("shared_mode") == "stream"
+    model = algorithmic_model(cfg, counts, row_of, B0, w8a8=share.w8a8, shared_apart=apart)
     per_call_us = dict(res["per_call_us"])
-    steps = STEP_NAMES + (("quantize",) if share.w8a8 else ())
+    steps = STEP_NAMES + (("quantize",) if share.w8a8 else ()) + (("shared",) if "shared" in per_call_us else ())
     if share.gather:
         # the up projection reads its rows from the tokens: no dispatch copy
         # (its events enclosed no work)

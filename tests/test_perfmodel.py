@@ -42,6 +42,17 @@ def test_algorithmic_model_counts():
     assert m["bytes"]["gemm_up"] == 3 * w_up + (3 + 2) * (H + I) * 2
     assert m["bytes"]["dispatch"] == (3 + 3) * H * 2 + N * K * 4
     assert m["bytes"]["combine"] == (3 + 2 + 3) * H * 2 + N * K * 8
+    # the shared expert as calls of its own: the routed GEMMs keep the routed
+    # rows and weights, the shared entry holds one expert over the B0 rows,
+    # and nothing is lost or counted twice
+    a = bench.algorithmic_model(cfg, counts, row_of, B0=2, shared_apart=True)
+    assert a["bytes"]["gemm_up"] == 2 * w_up + 3 * (H + I) * 2
+    assert a["bytes"]["gemm_down"] == 2 * (H * I * 2) + 3 * (I + H) * 2
+    assert a["bytes"]["shared"] == w_up + H * I * 2 + 2 * 2 * (H + I) * 2
+    assert a["flops"]["shared"] == 6 * 2 * H * I and a["flops"]["gemm_up"] == 2 * 3 * H * 2 * I
+    for d in ("bytes", "flops"):
+        tot = sum(m[d][n] for n in ("gemm_up", "gemm_down"))
+        assert sum(a[d][n] for n in ("gemm_up", "gemm_down", "shared")) == tot
 
 
 def test_bench_refuses_more_than_one_gpu():
