@@ -95,6 +95,7 @@ constexpr int kGatherRows = 256;  // tile rows of the kernels that gather (bf16 
 
 struct Sched {
   int tile_start[kMaxGroups + 2];
+  int full_start[kMaxGroups + 2];  // wide kernel: exclusive prefix of the groups' full-row-tile tiles
   int m[kMaxGroups + 1];
   int seg[kGemmMaxSrc + 1];
   union {
@@ -152,10 +153,16 @@ __device__ __forceinline__ int build_schedule(const GemmArgs& p, int bm, int ntn
   const int wide_min = p.wide_min != kNoWide && sh.wide_tiles >= p.wide_min_tiles ? 1 : kNoWide;
   for (int g = tid; g < Gt; g += NT) {
     const int m = sh.m[g];
-    sh.tile_start[g] = ((m >= wide_min) == wide) ? (m + bm - 1) / bm * ntn : 0;
+    const bool mine = (m >= wide_min) == wide;
+    sh.tile_start[g] = mine ? (m + bm - 1) / bm * ntn : 0;
+    if (wide) sh.full_start[g] = mine ? m / bm * ntn : 0;
   }
   __syncthreads();
   const int total = block_scan_lds<false, NT>(sh.tile_start, Gt, sh.tmp);
+  if (wide) {
+    const int full = block_scan_lds<false, NT>(sh.full_start, Gt, sh.tmp);
+    if (tid == 0) sh.full_start[Gt] = full;
+  }
   if (tid == 0) {
     sh.tile_start[Gt] = total;
     sh.cur_seg_group = -1;
@@ -219,6 +226,55 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& p, int bm, int ntn, 
   // every caller passes a workgroup-uniform t, so the fields are uniform; the
   // compiler cannot see that through the LDS reads: scalar registers (loop
   // bounds and weight addresses derived from them then stay scalar)
+  tl.g = __builtin_amdgcn_readfirstlane(tl.g);
+  tl.we = __builtin_amdgcn_readfirstlane(tl.we);
+  tl.shared = __builtin_amdgcn_readfirstlane(int(tl.shared)) != 0;
+  tl.nt = __builtin_amdgcn_readfirstlane(tl.nt);
+  tl.r0 = __builtin_amdgcn_readfirstlane(tl.r0);
+  tl.nrows = __builtin_amdgcn_readfirstlane(tl.nrows);
+  tl.mtiles = __builtin_amdgcn_readfirstlane(tl.mtiles);
+  return tl;
+}
+
+// Tile order of the wide kernel, in two phases. First every group's full
+// row tiles (bm rows each), the N tiles cut into blocks of nbw as in
+// decode_tile<true>: all these tiles cost the same, so the workgroups of an
+// XCD, which take consecutive tiles, stay in step through a round and keep
+// sharing the operand slabs in their L2. Then the groups' last, partial row
+// tiles (rows m % bm), N tiles fastest. tile_start (all tiles) minus
+// full_start (full-row-tile tiles) is the prefix of the partial tiles.
+__device__ __forceinline__ Tile decode_tile_wide(const GemmArgs& p, int bm, int ntn, const Sched& sh, int t) {
+  const int nsh = p.sh_rows > 0 ? 1 : 0;
+  const int Gt = p.G + nsh;
+  const int A = sh.full_start[Gt];
+  const bool full = t < A;
+  const int u = full ? t : t - A;
+  int lo = 0, hi = Gt;  // last q with start[q] <= u
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    const int st = full ? sh.full_start[mid] : sh.tile_start[mid] - sh.full_start[mid];
+    if (st <= u) lo = mid;
+    else hi = mid;
+  }
+  Tile tl;
+  tl.shared = lo < nsh;
+  tl.g = tl.shared ? 0 : lo - nsh;
+  tl.we = tl.g;
+  const int m = sh.m[lo];
+  const int mf = m / bm;  // full row tiles of the group
+  tl.mtiles = (m + bm - 1) / bm;
+  if (full) {
+    const int local = u - sh.full_start[lo];
+    const int nbw = ntn % 4 == 0 ? 4 : (ntn % 2 == 0 ? 2 : 1);
+    const int blk = local / (nbw * mf), rem = local % (nbw * mf);
+    tl.nt = blk * nbw + rem % nbw;
+    tl.r0 = (rem / nbw) * bm;
+    tl.nrows = bm;
+  } else {
+    tl.nt = u - (sh.tile_start[lo] - sh.full_start[lo]);
+    tl.r0 = mf * bm;
+    tl.nrows = m - tl.r0;
+  }
   tl.g = __builtin_amdgcn_readfirstlane(tl.g);
   tl.we = __builtin_amdgcn_readfirstlane(tl.we);
   tl.shared = __builtin_amdgcn_readfirstlane(int(tl.shared)) != 0;
@@ -379,7 +435,14 @@ __device__ inline int sk_owner(int64_t i, int64_t total, int G) {
 // stream-K over everything, and during the first part all workgroups are at
 // the same chunk index of their tiles, so the tiles of one expert (which sit
 // in neighbouring ranges on one XCD) read each activation chunk at about the
-// same time and the XCD's L2 serves the repeats.
+// same time and the XCD's L2 serves the repeats. With one whole tile per
+// range, the remainder part is over a third of the work, and its ranges,
+// which start at different chunks of their tiles, share no activation reads:
+// then a G down to 3/4 of the grid that gives every range exactly two whole
+// tiles is taken instead, if there is one (kimi_k2_ep8 up projection: 394 ->
+// 373 us). With more whole tiles per range the remainder is kept: it balances
+// tiles of unequal cost (measured: three whole tiles and no remainder made the
+// down projection 12% slower, its compute units idle at the end).
 struct DpSk {
   int G;             // ranges (workgroups used)
   int whole;         // whole tiles per range, taken first
@@ -389,10 +452,19 @@ struct DpSk {
 __device__ inline DpSk dpsk_split(int n_tiles, int nc, int max_grid) {
   DpSk d;
   d.G = sk_grid(int64_t(n_tiles) * nc, max_grid);
+  if (n_tiles / d.G == 1 && n_tiles % 2 == 0 && 4 * (n_tiles / 2) >= 3 * d.G) d.G = n_tiles / 2;
   d.whole = n_tiles / d.G;
   d.rem_base = int64_t(d.whole) * d.G * nc;
   d.rem = int64_t(n_tiles) * nc - d.rem_base;
   return d;
+}
+
+// Range of workgroup b (b < G): the workgroups of an XCD (b % kXcds) take
+// consecutive ranges, G / kXcds of them (one more on the first G % kXcds
+// XCDs), so neighbouring tiles share that XCD's L2.
+__device__ inline int xcd_range(int b, int G) {
+  const int x = b % kXcds, q = G / kXcds, r = G % kXcds;
+  return x * q + min(x, r) + b / kXcds;
 }
 
 // Partial slot of workgroup b: 0 for its first tile, 1 for its last.

@@ -343,7 +343,7 @@ __global__ __launch_bounds__(kF8Threads, 1) void ffn_fp8_kernel(GemmArgs p, floa
   const DpSk sp = dpsk_split(n_tiles, nchunks, kF8Grid);
   if (int(blockIdx.x) >= sp.G) return;  // uniform
   const int G = sp.G;
-  const int rng = int(blockIdx.x % kXcds) * (G / kXcds) + int(blockIdx.x / kXcds);
+  const int rng = xcd_range(int(blockIdx.x), G);
   // the range's whole tiles first, then its share of the remainder
   for (int part = 0; part < 2; ++part) {
     const int64_t i0 = part == 0 ? int64_t(rng) * sp.whole * nchunks : sp.rem_base + sk_start(rng, sp.rem, G);
