@@ -21,7 +21,7 @@ running the grouped GEMM as two half batches.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--layout compact|padded] [--extras LIST|none]
-                       [--no-cpu-baseline] [--copy-calib]
+                       [--no-cpu-baseline] [--copy-calib] [--ceilings]
 """
 from __future__ import annotations
 
@@ -440,6 +440,81 @@ def _measure_extra(bench, name, steps, warmup, headline=None):
     return cfg, d, share, ent
 
 
+def _copy_rate(torch, launches=10):
+    """A plain 1 GiB device copy: mean ms and read + write GB/s."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+    for a, b in ev:
+        a.record()
+        dst.copy_(src)
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    return ms, 2 * (1 << 30) / ms / 1e6
+
+
+def _ceilings(torch):
+    """What the chip delivers in practice, for reading the rooflines: the
+    probe program (matrix-core peak loops, LDS, L2 and HBM streams), a device
+    copy, and the platform's dense GEMMs (torch.matmul, torch._scaled_mm) of
+    the prefill share's two projection shapes, with M = the share's routed
+    plus shared-expert rows under its seeded routing (from this library's
+    route and layout calls)."""
+    import subprocess
+    import combine_router_softmax_amd as moe
+    from synth import get_config, make_routing_inputs
+    probe = os.path.join(ROOT, "combine_router_softmax_amd", "ceilings")
+    if not os.path.exists(probe):
+        print("the ceilings probe is not built (combine_router_softmax_amd/build.py builds it)", file=sys.stderr)
+        return 1
+    r = subprocess.run([probe], capture_output=True, text=True, timeout=300)
+    if r.returncode != 0:
+        print(r.stdout + r.stderr, file=sys.stderr)
+        return r.returncode
+    out = {"probe": json.loads(r.stdout.strip().splitlines()[-1])}
+    ms, gbs = _copy_rate(torch)
+    out["copy_1GiB"] = {"ms": round(ms, 4), "GBps_read_plus_write": round(gbs, 1)}
+    cfg = get_config("dsv3_prefill_ep8")
+    d = make_routing_inputs(cfg, 0)
+    idx, _ = moe.moe_route_topk(torch.from_numpy(d["logits"]).cuda(), cfg.top_k)
+    lay = moe.moe_dispatch_layout(idx, torch.from_numpy(d["src_offsets"]).cuda(), cfg.n_experts, cfg.expert_lo,
+                                  cfg.n_local, moe.COMPACT, 0)
+    M = int(lay["counts"].sum().item()) + int(d["src_offsets"][1])
+    H, I = cfg.hidden, cfg.inter
+    g = {}
+    for name, (m, k, n) in {"up": (M, H, 2 * I), "down": (M, I, H)}.items():
+        a = torch.randn(m, k, device="cuda", dtype=torch.bfloat16)
+        b = torch.randn(n, k, device="cuda", dtype=torch.bfloat16)
+        runs = {"bf16": lambda: torch.matmul(a, b.t())}
+        try:
+            a8, b8 = a.to(torch.float8_e4m3fn), b.to(torch.float8_e4m3fn)
+            one = torch.ones((), device="cuda")
+            torch._scaled_mm(a8, b8.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+            runs["fp8"] = lambda: torch._scaled_mm(a8, b8.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+        except Exception as ex:  # pragma: no cover - depends on the platform build
+            g[f"{name}_fp8"] = {"error": repr(ex)[:200]}
+        for dt, fn in runs.items():
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(20):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / 20 * 1e3
+            g[f"{name}_{dt}"] = {"M": m, "K": k, "N": n, "us": round(us, 1),
+                                 "TFLOPs": round(2 * m * k * n / us / 1e6, 1)}
+    out["dense_gemm_prefill_shapes"] = g
+    print(json.dumps(out))
+    return 0
+
+
 def _overlap(bench, cfg, d, share, steps, warmup):
     """The shared expert fused into the routed launches, against its own calls
     on the same stream, and on a second stream beside the routed path."""
@@ -520,6 +595,9 @@ def main(argv=None):
                          "Infinity Cache and L2 cannot carry data from one step to the next; 0: off")
     ap.add_argument("--copy-calib", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="run only the measured ceilings: matrix-core, LDS, L2 and HBM probes, a device copy, and "
+                         "dense library GEMMs of the prefill share's projection shapes")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -532,23 +610,15 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
 
+    if args.ceilings:
+        return _ceilings(torch)
+
     if args.copy_calib:
         # a plain 1 GiB device copy: the counter calibration for rocprofv3 --pmc,
         # and (timed) the practical streaming rate (read + write bytes / time)
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
-        for a, b in ev:
-            a.record()
-            dst.copy_(src)
-            b.record()
-        torch.cuda.synchronize()
-        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        ms, gbs = _copy_rate(torch)
         print(json.dumps({"copy_calib_bytes": 1 << 30, "launches": 13, "copy_ms": round(ms, 4),
-                          "copy_GBps_read_plus_write": round(2 * (1 << 30) / ms / 1e6, 1)}))
+                          "copy_GBps_read_plus_write": round(gbs, 1)}))
         return 0
 
     import combine_router_softmax_amd as moe

@@ -2,7 +2,9 @@
 
 Usage: ``python combine_router_softmax_amd/build.py`` (or ``build()``).
 Every ``csrc/*.hip`` file is compiled to an object in parallel, then linked
-into ``combine_router_softmax_amd/libmoe.so``.
+into ``combine_router_softmax_amd/libmoe.so``. ``probes/ceilings.hip`` (the
+measured-ceilings program that ``bench.py --ceilings`` runs) is built beside
+it as ``combine_router_softmax_amd/ceilings``.
 """
 from __future__ import annotations
 
@@ -19,6 +21,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
+PROBE_SRC = os.path.join(PKG, "probes", "ceilings.hip")
+PROBE = os.path.join(PKG, "ceilings")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -70,7 +74,17 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
     os.replace(tmp, LIB)
+    _build_probe(hipcc)
     return LIB
+
+
+def _build_probe(hipcc: str) -> None:
+    tmp = PROBE + ".tmp"
+    cmd = [hipcc, *[f for f in HIPCC_FLAGS if f not in ("-fPIC", "-fvisibility=hidden")], PROBE_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {PROBE_SRC}:\n{r.stdout}{r.stderr}")
+    os.replace(tmp, PROBE)
 
 
 if __name__ == "__main__":
