@@ -60,7 +60,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kGemmThreads = 256;
-constexpr int kMaxGemmThreads = 512;  // the fp8 decode kernel's workgroup
+constexpr int kMaxGemmThreads = 512;  // the W8A16 decode and the wide kernels' workgroups
 constexpr int kBM = 128;            // rows per tile
 constexpr int kMB = kBM / 32;       // 32-row MFMA blocks per tile
 constexpr int kKC = 128;            // reduction chunk
@@ -572,8 +572,9 @@ constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >
 // One wide tile's accumulators: 4 waves x 2 weight blocks x 8 activation
 // blocks x 16 registers x 64 lanes.
 constexpr int kWidePart = 4 * 2 * 8 * 16 * kWave;
-// [wave][a][block][quad q][lane][4 floats]: registers 4q..4q+3 of one
-// accumulator tile, 16 bytes per lane, 1 KiB contiguous per wave access
+// [wave pair][wave in pair][block][quad q][lane][4 floats]: registers
+// 4q..4q+3 of one accumulator tile, 16 bytes per lane, 1 KiB contiguous per
+// wave access
 __device__ __forceinline__ int wide_part_idx(int wv, int a, int b, int q, int lane) {
   return ((((wv * 2 + a) * 8 + b) * 4 + q) * kWave + lane) * 4;
 }

@@ -24,8 +24,9 @@
 //    1 x 128 scales: the same tiles on 4 waves, fp8 MFMA with the block scales
 //    applied per 128-deep chunk, h quantized in the up projection's epilogue;
 //  - ffn_wide_kernel (gemm_wide.hip): groups with many rows: 256 x 256 tiles on
-//    4 waves, weights in a register ring, activations staged through registers
-//    into LDS, remainder tiles split along K.
+//    8 waves (two per SIMD), weights in a register ring, activations staged
+//    through registers into LDS, full-row tiles first, remainder tiles split
+//    along K.
 // Tiles cut by a stream-K or K-split boundary leave fp32 partial sums that a
 // fix-up kernel adds in a fixed order (deterministic) before the epilogue.
 // MFMA with the weights as the A operand (32 weight rows) and the activations
