@@ -75,7 +75,7 @@ def tokens_per_expert(batch, qlen, top_k, ep, n_experts):
     return batch * qlen * top_k * ep / n_experts
 
 
-def algorithmic_model(cfg, counts, row_of, B0, w8a8=False, shared_apart=False):
+def algorithmic_model(cfg, counts, row_of, B0, w8a8=False, shared_apart=False, scatter=False):
     """Algorithmic bytes and FLOP per call from the actual routing of the step.
 
     counts [L, S] rows per local expert and source; row_of [N*K] (-1 = not local).
@@ -84,6 +84,10 @@ def algorithmic_model(cfg, counts, row_of, B0, w8a8=False, shared_apart=False):
     shared_apart: the shared expert runs as calls of its own (on a second
     stream), so gemm_up / gemm_down carry the routed rows only and the shared
     expert's bytes and FLOP go to a "shared" entry.
+    scatter: the down projection writes the S1 tokens with exactly one row
+    here and no shared-expert row straight to the output (their rows are
+    written once, to out instead of y, after reading the token's K entries),
+    and the combine neither reads their y rows nor writes their output rows.
     """
     H, I, K = cfg.hidden, cfg.inter, cfg.top_k
     wb = 1 if cfg.weight == "fp8_e4m3" else (4 if cfg.weight == "f32" else 2)
@@ -98,6 +102,11 @@ def algorithmic_model(cfg, counts, row_of, B0, w8a8=False, shared_apart=False):
     touched = local_tok.copy()
     touched[:B0] = True
     UT = int(touched.sum())
+    n_local_entries = (row_of.reshape(N, K) >= 0).sum(axis=1)
+    single = n_local_entries == 1
+    if cfg.shared:
+        single[:B0] = False
+    S1 = int(single.sum()) if scatter else 0
     scale_bytes = (2 * I // 128) * (H // 128) * 4 if wb == 1 else 0
     up_w = active * (2 * I * H * wb + scale_bytes)
     down_w = active * (H * I * wb + (scale_bytes // 2))
@@ -107,13 +116,14 @@ def algorithmic_model(cfg, counts, row_of, B0, w8a8=False, shared_apart=False):
     MS = M + B0s  # rows through the expert FFN: routed plus the shared expert's
     model = {
         "M": M, "U": U, "touched": UT, "active_experts": active, "max_rows_per_expert": int(m.max(initial=0)),
+        "single_row_tokens_scattered": S1,
         "bytes": {
             "route": N * cfg.n_experts * 4 + N * K * 8,
             "layout": 3 * N * K * 4 + M * 4,
             "dispatch": (U + M) * H * ab + N * K * 4,
             "gemm_up": up_w + sh_up_w + MS * H * ab + MS * I * ab,
             "gemm_down": down_w + sh_down_w + MS * I * ab + MS * H * ab,
-            "combine": (M + B0s + UT) * H * ab + N * K * 8,
+            "combine": (M - S1 + B0s + UT - S1) * H * ab + N * K * 8,
         },
         "flops": {"gemm_up": 2 * MS * H * 2 * I, "gemm_down": 2 * MS * I * H},
     }
@@ -319,7 +329,7 @@ class Bench:
 
 
 def _make_share(cfg, d, layout, *, policy=None, gather=None, blocked=None, weights_from=None, self_range=None,
-                w8a8=False):
+                w8a8=False, scatter=None):
     import torch
     from combine_router_softmax_amd import COMPACT
     from combine_router_softmax_amd.layer import MoEShare
@@ -330,7 +340,7 @@ def _make_share(cfg, d, layout, *, policy=None, gather=None, blocked=None, weigh
     share = MoEShare(n_tokens=N, hidden=cfg.hidden, inter=cfg.inter, n_experts=cfg.n_experts, top_k=cfg.top_k,
                      n_src=cfg.n_src, expert_lo=cfg.expert_lo, n_local=cfg.n_local, act_dtype=act, layout=layout,
                      capacity=cap, self_range=self_range or (0, B0), blocked=blocked, gather=gather, policy=policy,
-                     w8a8=w8a8)
+                     w8a8=w8a8, scatter=scatter)
     if weights_from is not None:
         share.share_weights_from(weights_from)
     else:
@@ -349,7 +359,7 @@ def _summarize(cfg, share, res, B0):
     counts = share.lay["counts"].cpu().numpy().astype(np.int64)
     row_of = share.lay["row_of"].cpu().numpy().astype(np.int64)
     apart = res.get("shared_mode") == "stream"
-    model = algorithmic_model(cfg, counts, row_of, B0, w8a8=share.w8a8, shared_apart=apart)
+    model = algorithmic_model(cfg, counts, row_of, B0, w8a8=share.w8a8, shared_apart=apart, scatter=share.scatter)
     per_call_us = dict(res["per_call_us"])
     steps = STEP_NAMES + (("quantize",) if share.w8a8 else ()) + (("shared",) if "shared" in per_call_us else ())
     if share.gather:
@@ -402,7 +412,8 @@ def _summarize(cfg, share, res, B0):
         dc_us = per_call_us["dispatch"] + per_call_us["combine"]
         mv["dispatch_combine"] = {"GB/s": round(dc_bytes / dc_us / 1e3, 1),
                                   "frac_hbm": round(dc_bytes / dc_us / 1e3 / HBM_PEAK_GBS, 4)}
-    routing = {k: model[k] for k in ("M", "U", "touched", "active_experts", "max_rows_per_expert")}
+    routing = {k: model[k] for k in ("M", "U", "touched", "active_experts", "max_rows_per_expert",
+                                     "single_row_tokens_scattered")}
     return model, breakdown, roof, gemm, mv, routing
 
 
@@ -579,6 +590,9 @@ def main(argv=None):
     ap.add_argument("--shared-mode", choices=["layer", "fused", "serial", "stream"], default="layer",
                     help="shared expert inside the routed launches, after them, or on a second stream "
                          "(default: the layer's choice)")
+    ap.add_argument("--scatter", action="store_true",
+                    help="the down projection writes the tokens with one row on this GPU (and no shared-expert "
+                         "row) straight to the output and the combine takes the rest (off by default: slower here)")
     ap.add_argument("--w8a8", action="store_true",
                     help="run the headline workload on the W8A8 path (fp8 activations; a bf16 checkpoint is "
                          "quantized to fp8 128 x 128 tiles), e.g. to profile the W8A8 kernels")
@@ -639,7 +653,8 @@ def main(argv=None):
                         blocked=None if args.xe_layout == "auto" else args.xe_layout == "blocked",
                         gather=None if args.gather == "auto" else args.gather == "on",
                         policy={"layer": None, "auto": moe.GEMM_AUTO, "wide": moe.GEMM_WIDE,
-                                "stream_k": moe.GEMM_STREAM_K}[args.gemm_policy], w8a8=args.w8a8)
+                                "stream_k": moe.GEMM_STREAM_K}[args.gemm_policy], w8a8=args.w8a8,
+                        scatter=True if args.scatter else None)
     logits, offs, x = _dev_inputs(d)
     out = torch.zeros_like(x)
     torch.cuda.synchronize()

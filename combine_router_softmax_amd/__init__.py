@@ -29,7 +29,7 @@ GG_FULL, GG_UP, GG_DOWN = 0, 1, 2
 GEMM_AUTO, GEMM_WIDE, GEMM_STREAM_K = 0, 1, 2
 ACT_ROWS, ACT_BLOCKED16 = 0, 1
 STATUS_OVERFLOW = 1
-ABI_VERSION = 2  # struct layouts of moe.h this binding mirrors
+ABI_VERSION = 3  # struct layouts of moe.h this binding mirrors
 _F32, _BF16, _FP8 = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -57,13 +57,20 @@ class SharedExpert(ctypes.Structure):
                 ("a_scales", ctypes.c_void_p)]
 
 
+class Scatter(ctypes.Structure):
+    _fields_ = [("row_token", ctypes.c_void_p), ("row_of", ctypes.c_void_p), ("topk_w", ctypes.c_void_p),
+                ("n_tokens", ctypes.c_int), ("top_k", ctypes.c_int), ("n_rows", ctypes.c_int64),
+                ("self_lo", ctypes.c_int), ("self_hi", ctypes.c_int), ("out", ctypes.c_void_p)]
+
+
 class GGemmDesc(ctypes.Structure):
     _fields_ = [("n_groups", ctypes.c_int), ("hidden", ctypes.c_int), ("inter", ctypes.c_int),
                 ("act_dt", ctypes.c_int), ("w_dt", ctypes.c_int), ("layout", ctypes.c_int),
                 ("n_src", ctypes.c_int), ("capacity", ctypes.c_int), ("rows", ctypes.c_int64),
                 ("stage", ctypes.c_int), ("shared", ctypes.POINTER(SharedExpert)), ("w_format", ctypes.c_int),
                 ("policy", ctypes.c_int), ("a_layout", ctypes.c_int), ("a_rows", ctypes.c_void_p),
-                ("a_nrows", ctypes.c_int64), ("a_scales", ctypes.c_void_p)]
+                ("a_nrows", ctypes.c_int64), ("a_scales", ctypes.c_void_p),
+                ("scatter", ctypes.POINTER(Scatter))]
 
 
 _P = ctypes.c_void_p
@@ -86,6 +93,7 @@ _SIGNATURES = {
     "moe_grouped_gemm_workspace": (_SZ, [ctypes.POINTER(GGemmDesc)]),
     "moe_grouped_gemm": (_I, [ctypes.POINTER(GGemmDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_combine": (_I, [_P, _I, _I64, _P, _P, _I, _I, _I, _P, _I, _I, _P, _P]),
+    "moe_combine_multi": (_I, [_P, _I, _I64, _P, _P, _I, _I, _I, _P, _I, _I, _P, _P]),
     "moe_pack_weights": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P]),
 }
 
@@ -417,8 +425,13 @@ def moe_grouped_gemm(a: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, *, gr
                      ws: Optional[torch.Tensor] = None, shared: Optional[dict] = None,
                      w_format: int = W_ROWMAJOR, policy: int = 0, a_layout: int = ACT_ROWS,
                      rows: Optional[int] = None, a_rows: Optional[torch.Tensor] = None,
-                     a_scales: Optional[torch.Tensor] = None) -> torch.Tensor:
+                     a_scales: Optional[torch.Tensor] = None, scatter: Optional[dict] = None) -> torch.Tensor:
     """SwiGLU FFN per expert over the rows each expert holds (see moe.h).
+
+    ``scatter`` = dict(row_token, row_of, topk_w, out, n_rows[, self_lo, self_hi]):
+    the down projection writes the rows of tokens with exactly one kept entry
+    and no shared-expert row straight into ``out`` as their combine (y rows of
+    those tokens are then not written; finish with moe_combine_multi).
 
     ``shared`` = dict(a, w13, w2, y[, s13, s2, a_scales]) runs the shared expert in the same launches.
     ``a_rows`` (int32 [rows], e.g. the layout's row_token) gathers routed row r
@@ -481,6 +494,24 @@ def moe_grouped_gemm(a: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, *, gr
         desc.a_nrows = a.shape[0]
     if w8a8:
         desc.a_scales = a_scales.data_ptr()
+    sc = None
+    if scatter is not None:
+        rt, ro, tw, so = scatter["row_token"], scatter["row_of"], scatter["topk_w"], scatter["out"]
+        _dev(rt, "scatter row_token", torch.int32)
+        _dev(ro, "scatter row_of", torch.int32)
+        _dev(tw, "scatter topk_w", torch.float32)
+        _dev(so, "scatter out", torch.bfloat16)
+        _need(so.dim() == 2 and so.shape[1] == H, f"scatter out must be [N, {H}]")
+        Nt = so.shape[0]
+        Kt = tw.shape[-1] if tw.dim() == 2 else 1
+        _need(rt.numel() >= R, f"scatter row_token must hold rows = {R} entries")
+        _need(ro.numel() >= Nt * Kt and tw.numel() >= Nt * Kt, f"scatter row_of and topk_w must hold N * K = {Nt * Kt}")
+        lo, hi = int(scatter.get("self_lo", 0)), int(scatter.get("self_hi", 0))
+        _need(0 <= lo <= hi <= Nt, "the scatter self range must lie inside [0, N]")
+        _on_gpu(**{"scatter row_token": rt, "scatter row_of": ro, "scatter topk_w": tw, "scatter out": so})
+        sc = Scatter(rt.data_ptr(), ro.data_ptr(), tw.data_ptr(), Nt, Kt, int(scatter["n_rows"]), lo, hi,
+                     so.data_ptr())
+        desc.scatter = ctypes.pointer(sc)
     wsb = moe_grouped_gemm_workspace(desc)
     if wsb == 0:
         raise MoeError("moe_grouped_gemm: invalid descriptor")
@@ -528,8 +559,11 @@ def moe_pack_weights(w13: Optional[torch.Tensor], w2: Optional[torch.Tensor], hi
 
 # --------------------------------------------------------------------------- combine
 def moe_combine(ye: torch.Tensor, row_of: torch.Tensor, topk_w: torch.Tensor, out: torch.Tensor,
-                shared_y: Optional[torch.Tensor] = None, self_lo: int = 0, self_hi: int = 0) -> torch.Tensor:
-    """Router-weighted sum of each token's expert rows (+ shared expert) into ``out``."""
+                shared_y: Optional[torch.Tensor] = None, self_lo: int = 0, self_hi: int = 0,
+                multi: bool = False) -> torch.Tensor:
+    """Router-weighted sum of each token's expert rows (+ shared expert) into
+    ``out``. ``multi``: only the tokens a down-projection scatter left
+    (moe_combine_multi)."""
     _dev(ye, "ye", (torch.float32, torch.bfloat16))
     _dev(row_of, "row_of", torch.int32)
     _dev(topk_w, "topk_w", torch.float32)
@@ -538,12 +572,14 @@ def moe_combine(ye: torch.Tensor, row_of: torch.Tensor, topk_w: torch.Tensor, ou
     K = topk_w.shape[-1] if topk_w.dim() == 2 else (topk_w.numel() // N if N else 1)
     _need(ye.dim() == 2 and ye.shape[1] == H, f"ye must be [rows, {H}]")
     _need(row_of.numel() >= N * K and topk_w.numel() >= N * K, f"row_of and topk_w must hold N * K = {N * K}")
+    if shared_y is not None or multi:
+        _need(0 <= self_lo <= self_hi <= N, "the self range must lie inside [0, N]")
     if shared_y is not None:
         _dev(shared_y, "shared_y", ye.dtype)
-        _need(0 <= self_lo <= self_hi <= N, "the self range must lie inside [0, N]")
         _need(shared_y.dim() == 2 and shared_y.shape[1] == H and shared_y.shape[0] >= self_hi - self_lo,
               f"shared_y must be [>= {self_hi - self_lo}, {H}]")
     _on_gpu(ye=ye, row_of=row_of, topk_w=topk_w, out=out, shared_y=shared_y)
-    _check(lib().moe_combine(_ptr(ye), _act_code(ye.dtype), ye.shape[0], _ptr(row_of), _ptr(topk_w), N, K, H,
-                             _ptr(shared_y), self_lo, self_hi, _ptr(out), _stream()), "moe_combine")
+    fn = lib().moe_combine_multi if multi else lib().moe_combine
+    _check(fn(_ptr(ye), _act_code(ye.dtype), ye.shape[0], _ptr(row_of), _ptr(topk_w), N, K, H, _ptr(shared_y),
+              self_lo, self_hi, _ptr(out), _stream()), "moe_combine_multi" if multi else "moe_combine")
     return out

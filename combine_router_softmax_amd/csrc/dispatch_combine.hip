@@ -125,7 +125,9 @@ struct Vec<uint16_t> {
 // together, then accumulated in k order; a token with at most KG rows on this
 // GPU - the usual case - costs one round trip. The registers held are PPT x KG
 // pieces, not PPT x K.
-template <typename T, int KMAX, int PPT, int KG>
+// MULTI: leave tokens with exactly one kept entry outside [self_lo, self_hi)
+// (the down projection's scatter wrote them).
+template <typename T, int KMAX, int PPT, int KG, bool MULTI>
 __global__ __launch_bounds__(kVecThreads) void combine_kernel(
     const uint4* __restrict__ ye, int64_t n_rows, const int32_t* __restrict__ row_of, const float* __restrict__ topk_w,
     int n_tokens, int top_k, int row_vecs, int n_chunks, const uint4* __restrict__ shared_y, int self_lo, int self_hi,
@@ -148,6 +150,7 @@ __global__ __launch_bounds__(kVecThreads) void combine_kernel(
   }
   const bool in_self = shared_y != nullptr && t >= self_lo && t < self_hi;
   if ((kept == 0 && !in_self) || c0 >= row_vecs) return;
+  if (MULTI && __builtin_popcount(kept) == 1 && !(t >= self_lo && t < self_hi)) return;
   int cs[PPT];  // piece indices (a tail piece repeats a valid one; its result is not stored)
 #pragma unroll
   for (int i = 0; i < PPT; ++i) cs[i] = min(c0 + i * kVecThreads, row_vecs - 1);
@@ -300,38 +303,39 @@ MOE_API moe_status_t moe_dispatch_blocked(const void* x, moe_dtype_t dt, int n_t
 // all K rows in one round trip, so no token costs more than one.
 constexpr int kCombineManyTokens = 1024;
 
-template <typename T, int KMAX, int PPT, int KG>
+template <typename T, int KMAX, int PPT, int KG, bool MULTI>
 static void launch_combine(hipStream_t stream, const void* ye, int64_t n_rows, const int32_t* row_of,
                            const float* topk_w, int n_tokens, int top_k, int row_vecs, const void* shared_y,
                            int self_lo, int self_hi, void* out) {
   const int n_chunks = (row_vecs + kVecThreads * PPT - 1) / (kVecThreads * PPT);
   const dim3 grid(vec_grid(int64_t(n_chunks) * n_tokens));
-  hipLaunchKernelGGL((combine_kernel<T, KMAX, PPT, KG>), grid, dim3(kVecThreads), 0, stream,
+  hipLaunchKernelGGL((combine_kernel<T, KMAX, PPT, KG, MULTI>), grid, dim3(kVecThreads), 0, stream,
                      static_cast<const uint4*>(ye), n_rows, row_of, topk_w, n_tokens, top_k, row_vecs, n_chunks,
                      static_cast<const uint4*>(shared_y), self_lo, self_hi, static_cast<uint4*>(out));
 }
 
-template <typename T, int KMAX>
+template <typename T, int KMAX, bool MULTI>
 static void launch_combine(hipStream_t stream, const void* ye, int64_t n_rows, const int32_t* row_of,
                            const float* topk_w, int n_tokens, int top_k, int row_vecs, const void* shared_y,
                            int self_lo, int self_hi, void* out) {
   if (n_tokens >= kCombineManyTokens)
-    launch_combine<T, KMAX, 4, 2>(stream, ye, n_rows, row_of, topk_w, n_tokens, top_k, row_vecs, shared_y, self_lo,
-                                  self_hi, out);
+    launch_combine<T, KMAX, 4, 2, MULTI>(stream, ye, n_rows, row_of, topk_w, n_tokens, top_k, row_vecs, shared_y,
+                                         self_lo, self_hi, out);
   else
-    launch_combine<T, KMAX, 2, KMAX>(stream, ye, n_rows, row_of, topk_w, n_tokens, top_k, row_vecs, shared_y, self_lo,
-                                     self_hi, out);
+    launch_combine<T, KMAX, 2, KMAX, MULTI>(stream, ye, n_rows, row_of, topk_w, n_tokens, top_k, row_vecs, shared_y,
+                                            self_lo, self_hi, out);
 }
 
-MOE_API moe_status_t moe_combine(const void* ye, moe_dtype_t dt, int64_t n_rows, const int32_t* row_of,
-                                 const float* topk_w, int n_tokens, int top_k, int hidden, const void* shared_y,
-                                 int self_lo, int self_hi, void* out, hipStream_t stream) {
+template <bool MULTI>
+static moe_status_t combine_entry(const void* ye, moe_dtype_t dt, int64_t n_rows, const int32_t* row_of,
+                                  const float* topk_w, int n_tokens, int top_k, int hidden, const void* shared_y,
+                                  int self_lo, int self_hi, void* out, hipStream_t stream) {
   if (n_tokens < 0 || hidden < 1 || top_k < 1 || n_rows < 0) return MOE_ERR_INVALID_ARG;
   if (!row_dtype_ok(dt)) return MOE_ERR_UNSUPPORTED;
   if (top_k > kMaxK) return MOE_ERR_UNSUPPORTED;
   const size_t row_bytes = size_t(hidden) * dtype_size(dt);
   if (row_bytes % 16) return MOE_ERR_INVALID_ARG;
-  if (shared_y && (self_lo < 0 || self_hi < self_lo || self_hi > n_tokens)) return MOE_ERR_INVALID_ARG;
+  if ((shared_y || MULTI) && (self_lo < 0 || self_hi < self_lo || self_hi > n_tokens)) return MOE_ERR_INVALID_ARG;
   if (n_tokens == 0) return MOE_OK;
   if (!row_of || !topk_w || !out || !aligned16(out)) return MOE_ERR_INVALID_ARG;
   if (n_rows > 0 && (!ye || !aligned16(ye))) return MOE_ERR_INVALID_ARG;
@@ -340,7 +344,8 @@ MOE_API moe_status_t moe_combine(const void* ye, moe_dtype_t dt, int64_t n_rows,
   const int n_chunks = (row_vecs + kVecThreads * 2 - 1) / (kVecThreads * 2);  // the smaller pieces' count
   if (int64_t(n_chunks) * n_tokens >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
 #define MOE_COMBINE(T, KM) \
-  launch_combine<T, KM>(stream, ye, n_rows, row_of, topk_w, n_tokens, top_k, row_vecs, shared_y, self_lo, self_hi, out)
+  launch_combine<T, KM, MULTI>(stream, ye, n_rows, row_of, topk_w, n_tokens, top_k, row_vecs, shared_y, self_lo, \
+                               self_hi, out)
   const int kmax = kmax_of(top_k);
   if (dt == MOE_F32) {
     if (kmax == 2) MOE_COMBINE(float, 2);
@@ -355,4 +360,19 @@ MOE_API moe_status_t moe_combine(const void* ye, moe_dtype_t dt, int64_t n_rows,
   }
 #undef MOE_COMBINE
   return launch_status();
+}
+
+MOE_API moe_status_t moe_combine(const void* ye, moe_dtype_t dt, int64_t n_rows, const int32_t* row_of,
+                                 const float* topk_w, int n_tokens, int top_k, int hidden, const void* shared_y,
+                                 int self_lo, int self_hi, void* out, hipStream_t stream) {
+  return combine_entry<false>(ye, dt, n_rows, row_of, topk_w, n_tokens, top_k, hidden, shared_y, self_lo, self_hi,
+                              out, stream);
+}
+
+MOE_API moe_status_t moe_combine_multi(const void* ye, moe_dtype_t dt, int64_t n_rows, const int32_t* row_of,
+                                       const float* topk_w, int n_tokens, int top_k, int hidden,
+                                       const void* shared_y, int self_lo, int self_hi, void* out,
+                                       hipStream_t stream) {
+  return combine_entry<true>(ye, dt, n_rows, row_of, topk_w, n_tokens, top_k, hidden, shared_y, self_lo, self_hi,
+                             out, stream);
 }

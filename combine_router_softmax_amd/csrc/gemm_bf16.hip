@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_fixup_kernel(GemmArgs p, con
       [&](int, int q) { return bf_part_idx(4 * m + wv, b, q, lane); });
   tl.nt = kBfNB * tl.nt + m;
   uint16_t* out = static_cast<uint16_t*>(pick(tl.shared, p.sh_out, p.out));
-  ffn_epilogue_block<KIND>(acc[0], tl, b, sh, out, p.n_out, wv, lr, lh, p.out_blk);
+  ffn_epilogue_block<KIND>(acc[0], tl, b, sh, out, p.n_out, wv, lr, lh, p.out_blk, p.sc);
 }
 
 // ------------------------------------------------------------------ bf16 decode kernel
@@ -194,7 +194,7 @@ __device__ __forceinline__ void bf_run(const GemmArgs& p, const Tile& tl, int n,
       if (part_ == nullptr) {                                                                               \
         Tile tk_ = tl;                                                                                      \
         tk_.nt = kBfNB * (tl.nt + k_) + wg;                                                                 \
-        if (tk_.nt < p.n_tiles_n) ffn_epilogue<KIND, NB>(acc, tk_, NB, sh, out, p.n_out, wq, lr, lh, p.out_blk); \
+        if (tk_.nt < p.n_tiles_n) ffn_epilogue<KIND, NB>(acc, tk_, NB, sh, out, p.n_out, wq, lr, lh, p.out_blk, p.sc); \
       } else {                                                                                              \
         _Pragma("unroll") for (int b = 0; b < NB; ++b)                                                      \
           _Pragma("unroll") for (int v = 0; v < 16; v += 4)                                                 \

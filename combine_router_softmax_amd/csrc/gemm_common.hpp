@@ -10,6 +10,17 @@
 
 namespace moe {
 
+// Weighted scatter from the down projection (moe_scatter_t): rows whose token
+// has exactly one row of this GPU and no shared-expert row go to out.
+struct ScatterArgs {
+  const int32_t* row_token;   // [rows] token of each routed row
+  const int32_t* row_of;      // [N, K]
+  const float* w;             // [N, K] router weights
+  uint16_t* out;              // [N, H] bf16 (nullptr: no scatter)
+  int64_t n_rows;             // entries in [0, n_rows) are this GPU's rows
+  int K, self_lo, self_hi;
+};
+
 struct GemmArgs {
   // routed experts
   const void* a;              // [rows, K] activations (x for up, h for down)
@@ -44,6 +55,7 @@ struct GemmArgs {
   const float* sh_as;
   float* out_s;
   float* sh_out_s;
+  ScatterArgs sc;             // down projection only
 };
 
 // Launchers of the four MFMA kernel families (each in its own translation
@@ -472,11 +484,49 @@ __device__ inline float* sk_slot(float* parts, int b, int slot) {
   return parts + (size_t(b) * 2 + slot) * kPartFloats;
 }
 
+// The token of routed row phys when its down-projection row is that token's
+// whole combine (exactly one of its K entries is a row of this GPU, and it
+// has no shared-expert row), with that entry's weight in w; else -1. The rule
+// is moe_combine's own (an entry is kept when its row lies in [0, n_rows)).
+__device__ __forceinline__ int scatter_token(const ScatterArgs& sc, int64_t phys, float& w) {
+  const int t = sc.row_token[phys];
+  if (t < 0 || (t >= sc.self_lo && t < sc.self_hi)) return -1;
+  int n = 0;
+  float wk = 0.f;
+  for (int k = 0; k < sc.K; ++k) {
+    const int r = sc.row_of[size_t(t) * sc.K + k];
+    if (r >= 0 && r < sc.n_rows) {
+      ++n;
+      wk = sc.w[size_t(t) * sc.K + k];
+    }
+  }
+  w = wk;
+  return n == 1 ? t : -1;
+}
+
+// Four consecutive down-projection outputs at column col of row `row`: y
+// values rounded to bf16, or (scat: row is the token's output row) as
+// moe_combine writes a token with one kept row, round(w * bf16(y)) with the
+// product formed as fmaf(w, y, 0).
+__device__ __forceinline__ void store_y4(uint16_t* row, bool scat, float sw, int col, float v0, float v1, float v2,
+                                         float v3) {
+  const uint32_t p0 = pack_bf16x2(v0, v1), p1 = pack_bf16x2(v2, v3);
+  if (!scat) {
+    *reinterpret_cast<uint2*>(row + col) = make_uint2(p0, p1);
+    return;
+  }
+  const float y0 = __uint_as_float(p0 << 16), y1 = __uint_as_float(p0 & 0xffff0000u);
+  const float y2 = __uint_as_float(p1 << 16), y3 = __uint_as_float(p1 & 0xffff0000u);
+  *reinterpret_cast<uint2*>(row + col) = make_uint2(pack_bf16x2(fmaf(sw, y0, 0.f), fmaf(sw, y1, 0.f)),
+                                                    pack_bf16x2(fmaf(sw, y2, 0.f), fmaf(sw, y3, 0.f)));
+}
+
 // Epilogue of 32-row block b of a tile (four consecutive output columns never
 // straddle a 32-column block).
 template <int KIND>
 __device__ __forceinline__ void ffn_epilogue_block(const f32x16_t& acc, const Tile& tl, int b, const Sched& sh,
-                                                   uint16_t* out, int n_out, int wv, int lr, int lh, bool oblk) {
+                                                   uint16_t* out, int n_out, int wv, int lr, int lh, bool oblk,
+                                                   const ScatterArgs& sc) {
   const int phys = sh.rowmap[b * 32 + lr];
   if (phys < 0) return;
   uint16_t* orow = out + act_off(phys, 0, n_out, oblk);
@@ -491,21 +541,25 @@ __device__ __forceinline__ void ffn_epilogue_block(const f32x16_t& acc, const Ti
           make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
     }
   } else {
+    // (y rows are row-major)
+    float sw = 0.f;
+    const int st = sc.out != nullptr && !tl.shared ? scatter_token(sc, phys, sw) : -1;
+    uint16_t* yrow = st >= 0 ? sc.out + size_t(st) * n_out : orow;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int col = tl.nt * 128 + 32 * wv + 8 * q + 4 * lh;
-      *reinterpret_cast<uint2*>(orow + (oblk ? size_t(col >> 5) * 512 + (col & 31) : size_t(col))) =
-          make_uint2(pack_bf16x2(acc[4 * q], acc[4 * q + 1]), pack_bf16x2(acc[4 * q + 2], acc[4 * q + 3]));
+      store_y4(yrow, st >= 0, sw, col, acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
     }
   }
 }
 
 template <int KIND, int NBMAX>
 __device__ __forceinline__ void ffn_epilogue(const f32x16_t (&acc)[NBMAX], const Tile& tl, int nb, const Sched& sh,
-                                             uint16_t* out, int n_out, int wv, int lr, int lh, bool oblk) {
+                                             uint16_t* out, int n_out, int wv, int lr, int lh, bool oblk,
+                                             const ScatterArgs& sc) {
 #pragma unroll
   for (int b = 0; b < NBMAX; ++b)
-    if (b < nb) ffn_epilogue_block<KIND>(acc[b], tl, b, sh, out, n_out, wv, lr, lh, oblk);
+    if (b < nb) ffn_epilogue_block<KIND>(acc[b], tl, b, sh, out, n_out, wv, lr, lh, oblk, sc);
 }
 
 // NA accumulator tiles (16 floats per lane each) summed over the partials of

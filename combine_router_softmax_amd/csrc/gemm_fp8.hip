@@ -249,7 +249,7 @@ __device__ __forceinline__ void f8_run(const GemmArgs& p, const Tile& tl, int n,
         _Pragma("unroll") for (int a = 0; a < 2; ++a) {                                                     \
           Tile ta_ = tl;                                                                                    \
           ta_.nt = kF8NB * (tl.nt + k_) + 2 * wg + a;                                                       \
-          if (ta_.nt < p.n_tiles_n) ffn_epilogue<KIND, NB>(acc[a], ta_, NB, sh, out, p.n_out, wq, lr, lh, p.out_blk); \
+          if (ta_.nt < p.n_tiles_n) ffn_epilogue<KIND, NB>(acc[a], ta_, NB, sh, out, p.n_out, wq, lr, lh, p.out_blk, p.sc); \
         }                                                                                                   \
       } else {                                                                                              \
         _Pragma("unroll") for (int a = 0; a < 2; ++a)                                                       \
@@ -416,7 +416,7 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_fp8_fixup_kernel(GemmArgs p,
       [&](int, int q) { return f8_part_idx(m / 2 * 4 + wv, m % 2, b, q, lane); });
   tl.nt = kF8NB * tl.nt + m;
   uint16_t* out = static_cast<uint16_t*>(pick(tl.shared, p.sh_out, p.out));
-  ffn_epilogue_block<KIND>(acc[0], tl, b, sh, out, p.n_out, wv, lr, lh, p.out_blk);
+  ffn_epilogue_block<KIND>(acc[0], tl, b, sh, out, p.n_out, wv, lr, lh, p.out_blk, p.sc);
 }
 
 }  // namespace

@@ -351,7 +351,7 @@ __device__ __forceinline__ void q8_run(const GemmArgs& p, const Tile& tl, int n,
           _Pragma("unroll") for (int a = 0; a < kQ8NA; ++a) {                                               \
             Tile ta_ = tl;                                                                                  \
             ta_.nt = kF8NB * (tl.nt + k_) + a;                                                              \
-            if (ta_.nt < p.n_tiles_n) ffn_epilogue<KIND, NB>(acc[a], ta_, NB, sh, y_, p.n_out, wv, lr, lh, false); \
+            if (ta_.nt < p.n_tiles_n) ffn_epilogue<KIND, NB>(acc[a], ta_, NB, sh, y_, p.n_out, wv, lr, lh, false, p.sc); \
           }                                                                                                 \
         }                                                                                                   \
       } else {                                                                                              \
@@ -519,7 +519,7 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_w8a8_fixup_kernel(GemmArgs p
     for (int a = 0; a < 2; ++a) {
       Tile ta = tl;
       ta.nt = nb0 + a;
-      if (ta.nt < p.n_tiles_n) ffn_epilogue_block<KIND>(acc[a], ta, b, sh, out, p.n_out, wv, lr, lh, false);
+      if (ta.nt < p.n_tiles_n) ffn_epilogue_block<KIND>(acc[a], ta, b, sh, out, p.n_out, wv, lr, lh, false, p.sc);
     }
   }
 }

@@ -79,11 +79,14 @@ __device__ __forceinline__ void wide_epilogue_block(const GemmArgs& p, const Til
           make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
     }
   } else {
+    // (y rows are row-major)
+    float sw = 0.f;
+    const int st = p.sc.out != nullptr && !tl.shared ? scatter_token(p.sc, phys, sw) : -1;
+    uint16_t* yrow = st >= 0 ? p.sc.out + size_t(st) * p.n_out : orow;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int col = ntp * 128 + 32 * pw + 8 * q + 4 * lh;
-      *reinterpret_cast<uint2*>(orow + (oblk ? size_t(col >> 5) * 512 + (col & 31) : size_t(col))) =
-          make_uint2(pack_bf16x2(ac[4 * q], ac[4 * q + 1]), pack_bf16x2(ac[4 * q + 2], ac[4 * q + 3]));
+      store_y4(yrow, st >= 0, sw, col, ac[4 * q], ac[4 * q + 1], ac[4 * q + 2], ac[4 * q + 3]);
     }
   }
 }

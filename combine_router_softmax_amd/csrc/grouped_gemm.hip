@@ -276,6 +276,14 @@ MOE_API moe_status_t moe_grouped_gemm(const moe_ggemm_desc_t* d, const void* a, 
     if (fp8 && ((up && !se->s13) || (down && !se->s2))) return MOE_ERR_INVALID_ARG;
     if (w8a8 && up && (!se->a_scales || !aligned4(se->a_scales))) return MOE_ERR_INVALID_ARG;
   }
+  // weighted scatter from the down projection's epilogue (bf16 y only)
+  const moe_scatter_t* sc = down && routed ? d->scatter : nullptr;
+  if (sc) {
+    if (f32) return MOE_ERR_UNSUPPORTED;
+    if (!sc->row_token || !sc->row_of || !sc->topk_w || !sc->out || !aligned16(sc->out)) return MOE_ERR_INVALID_ARG;
+    if (sc->n_tokens < 0 || sc->top_k < 1 || sc->top_k > 16 || sc->n_rows < 0) return MOE_ERR_INVALID_ARG;
+    if (sc->self_lo < 0 || sc->self_hi < sc->self_lo || sc->self_hi > sc->n_tokens) return MOE_ERR_INVALID_ARG;
+  }
   if (!ws || !aligned16(ws) || ws_bytes < moe_grouped_gemm_workspace(d)) return MOE_ERR_WORKSPACE;
   // the decode kernels address a tile's activation rows relative to its first
   // row: one expert's padded region must span fewer than 2^31 elements
@@ -291,6 +299,7 @@ MOE_API moe_status_t moe_grouped_gemm(const moe_ggemm_desc_t* d, const void* a, 
   float* h_s = w8a8 ? reinterpret_cast<float*>(static_cast<char*>(h) + h_codes_bytes(d, d->rows)) : nullptr;
   float* sh_h_s = w8a8 ? reinterpret_cast<float*>(static_cast<char*>(sh_h) + h_codes_bytes(d, sh_rows_ws)) : nullptr;
   GemmArgs p;
+  p.sc = ScatterArgs{};
   p.as = p.sh_as = nullptr;
   p.out_s = p.sh_out_s = nullptr;
   p.rows = routed ? d->rows : 0;
@@ -361,6 +370,16 @@ MOE_API moe_status_t moe_grouped_gemm(const moe_ggemm_desc_t* d, const void* a, 
     p.n_tiles_n = f32 ? d->hidden / kFBN : d->hidden / 128;
     p.a_blk = p.sh_a_blk = h_blk;  // h
     p.out_blk = 0;                // y rows are read by the combine
+    if (sc) {
+      p.sc.row_token = sc->row_token;
+      p.sc.row_of = sc->row_of;
+      p.sc.w = sc->topk_w;
+      p.sc.out = static_cast<uint16_t*>(sc->out);
+      p.sc.n_rows = sc->n_rows;
+      p.sc.K = sc->top_k;
+      p.sc.self_lo = sc->self_lo;
+      p.sc.self_hi = sc->self_hi;
+    }
     st = launch_stage(p, f32, fp8, w8a8, kDown, sk, parts, stream);
   }
   return st;

@@ -31,7 +31,7 @@ class MoEShare:
                  expert_lo: int, n_local: int, act_dtype: torch.dtype, layout: int = COMPACT,
                  capacity: Optional[int] = None, self_range=(0, 0), device="cuda",
                  blocked: Optional[bool] = None, policy: Optional[int] = None, gather: Optional[bool] = None,
-                 w8a8: bool = False):
+                 w8a8: bool = False, scatter: Optional[bool] = None):
         self.N, self.H, self.I, self.E, self.K = n_tokens, hidden, inter, n_experts, top_k
         self.S, self.lo, self.L = n_src, expert_lo, n_local
         self.layout = layout
@@ -55,6 +55,16 @@ class MoEShare:
         self.w8a8 = bool(w8a8)
         if self.w8a8 and act_dtype != torch.bfloat16:
             raise ValueError("the W8A8 path takes bf16 token rows")
+        # scatter: the down projection writes the tokens with one row here and
+        # no shared-expert row straight into the output (bf16 outputs only) and
+        # the combine takes the other tokens. Off by default: measured on
+        # MI355X it costs the down projection more than it saves the combine
+        # (the epilogue's reads of the token's K entries sit on the tile's
+        # critical path): dsv3_prefill_ep8 3.25 -> 3.48 ms, kimi_k2_ep8
+        # 0.664 -> 0.695 ms, dsv3_decode_ep128 0.189 -> 0.195 ms
+        self.scatter = False if scatter is None else bool(scatter)
+        if self.scatter and act_dtype != torch.bfloat16:
+            raise ValueError("the down projection's scatter writes bf16 outputs")
         self.blocked = bool(blocked) and act_dtype == torch.bfloat16 and hidden % 32 == 0 and not self.w8a8
         self.a_layout = ACT_BLOCKED16 if self.blocked else ACT_ROWS
         # one kernel per product: batches whose experts are expected to hold
@@ -161,11 +171,23 @@ class MoEShare:
         else:
             moe_dispatch(x, self.lay["row_of"], self.K, self.R, self.xe)
 
-    def gemm(self, stage=GG_FULL, x=None, src=None):
+    def _self_range(self):
+        # the tokens with a shared-expert row (the range the scatter and the
+        # combine must agree on)
+        has = self.sw is not None and self.self_hi > self.self_lo
+        return (self.self_lo, self.self_hi) if has else (0, 0)
+
+    def gemm(self, stage=GG_FULL, x=None, src=None, out=None):
         """Routed experts; with ``x`` the shared expert runs in the same launches.
-        Gathering, the up projection reads its rows from ``src`` (the tokens)."""
+        Gathering, the up projection reads its rows from ``src`` (the tokens).
+        With ``out`` and the scatter on, the down projection writes the tokens
+        with one row here (and no shared-expert row) into ``out``."""
         w = self.w
         extra = {}
+        if out is not None and self.scatter and stage != GG_UP and self.R > 0:
+            lo, hi = self._self_range()
+            extra["scatter"] = dict(row_token=self.lay["row_token"], row_of=self.lay["row_of"], topk_w=self.topk_w,
+                                    out=out, n_rows=max(self.R, 1), self_lo=lo, self_hi=hi)
         if self.gather:
             if src is None:
                 raise ValueError("gathered rows need the tokens (src)")
@@ -229,10 +251,13 @@ class MoEShare:
                          layout=COMPACT, stage=stage, y=self.ys[: a.shape[0]], ws=self.sws, w_format=self.w_format,
                          **extra)
 
-    def combine(self, out):
+    def combine(self, out, multi: bool = False):
+        """Weighted sum into ``out``; ``multi``: only the tokens the down
+        projection's scatter left."""
         sy = self.ys if (self.sw is not None and self.self_hi > self.self_lo) else None
+        lo, hi = self._self_range() if multi else (self.self_lo, self.self_hi)
         moe_combine(self.ye[: max(self.R, 1)] if self.R else self.ye[:0], self.lay["row_of"], self.topk_w, out, sy,
-                    self.self_lo, self.self_hi)
+                    lo, hi, multi=multi)
 
     def step(self, logits, src_offsets, x, out, events: Optional[dict] = None, fused_shared: bool = True,
              shared_mode: Optional[str] = None):
@@ -271,14 +296,15 @@ class MoEShare:
         run("layout", lambda: self.layout_step(src_offsets))
         run("dispatch", (lambda: None) if self.gather else (lambda: self.dispatch(x)))
         xs = x if mode == "fused" else None
+        sc = self.scatter and self.R > 0
         run("gemm_up", lambda: self.gemm(GG_UP, xs, src=x))
-        run("gemm_down", lambda: self.gemm(GG_DOWN, xs, src=x))
+        run("gemm_down", lambda: self.gemm(GG_DOWN, xs, src=x, out=out if sc else None))
         if mode == "serial":
             run("shared_up", lambda: self.shared_gemm(x, GG_UP))
             run("shared_down", lambda: self.shared_gemm(x, GG_DOWN))
         if side is not None:
             cur.wait_stream(side)
-        run("combine", lambda: self.combine(out))
+        run("combine", lambda: self.combine(out, multi=sc))
         return out
 
 

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum {
   MOE_OK = 0,
@@ -271,6 +271,29 @@ typedef struct {
   const float* a_scales; /* W8A8 only: [rows, H/128] scales of the codes in a; else NULL */
 } moe_shared_expert_t;
 
+/* Weighted scatter from the down projection (lehuy.net page, section
+ * Combine; Perplexity DeepSeek page, section Quantization: routing-aware
+ * kernels that fuse the grouped GEMM with the data movement around it). A
+ * token with exactly one kept entry (one k with row_of[t*K+k] in
+ * [0, n_rows)) and no shared-expert row (t outside [self_lo, self_hi)) has
+ * that one row as its whole combine; with a scatter, the down projection's
+ * epilogue writes
+ *   out[t] = round(topk_w[t*K+k] * y[row])   (y first rounded to bf16, the
+ *            product formed in fp32 as fmaf(w, y, 0), one rounding)
+ * - bit for bit what moe_combine writes for that token - instead of y[row],
+ * which is then not written. moe_combine_multi combines the other tokens.
+ * bf16 outputs only (bf16 activations or W8A8); device pointers. */
+typedef struct {
+  const int32_t* row_token; /* [rows] token of each routed row (moe_dispatch_layout) */
+  const int32_t* row_of;    /* [n_tokens, top_k] */
+  const float* topk_w;      /* [n_tokens, top_k] */
+  int n_tokens;
+  int top_k;                /* 1..16 */
+  int64_t n_rows;           /* the combine's n_rows */
+  int self_lo, self_hi;     /* shared-expert token range (equal: none) */
+  void* out;                /* [n_tokens, hidden] bf16, 16-byte aligned */
+} moe_scatter_t;
+
 typedef struct {
   int n_groups;        /* G routed experts in this call (may be 0 with a shared expert) */
   int hidden;          /* H, multiple of 128 */
@@ -300,6 +323,9 @@ typedef struct {
    * 128 columns ([R, H/128], or [a_nrows, H/128]), as moe_quantize_1x128 and
    * moe_dispatch_fp8 write them; NULL otherwise. */
   const float* a_scales;
+  /* Weighted scatter of single-row tokens from the down projection (host
+   * pointer, or NULL for none); used with MOE_GG_FULL and MOE_GG_DOWN. */
+  const moe_scatter_t* scatter;
 } moe_ggemm_desc_t;
 
 /* Bytes of scratch moe_grouped_gemm needs (the intermediates h [R, I] and, with
@@ -381,6 +407,15 @@ moe_status_t moe_pack_weights(int n_groups, int hidden, int inter, moe_dtype_t w
 moe_status_t moe_combine(const void* ye, moe_dtype_t dt, int64_t n_rows, const int32_t* row_of,
                          const float* topk_w, int n_tokens, int top_k, int hidden, const void* shared_y,
                          int self_lo, int self_hi, void* out, hipStream_t stream);
+
+/* moe_combine for the tokens the down projection's scatter (moe_scatter_t,
+ * same n_rows, self_lo and self_hi) did not write: those with two or more
+ * kept entries, and those in [self_lo, self_hi) with a shared_y row. Tokens
+ * with exactly one kept entry outside that range are left as they are. Same
+ * arguments and errors as moe_combine. */
+moe_status_t moe_combine_multi(const void* ye, moe_dtype_t dt, int64_t n_rows, const int32_t* row_of,
+                               const float* topk_w, int n_tokens, int top_k, int hidden, const void* shared_y,
+                               int self_lo, int self_hi, void* out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
     assert {"moe_route_topk", "moe_dispatch_layout", "moe_dispatch", "moe_grouped_gemm", "moe_combine"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert moe.moe_abi_version() == 2
+    assert moe.moe_abi_version() == 3
     for s, txt in [(0, b"ok"), (1, b"invalid argument"), (3, b"workspace missing or too small")]:
         assert lib.moe_status_string(s) == txt
 
@@ -103,6 +103,12 @@ def test_dispatch_and_combine_argument_errors(lib):
     assert c(FAKE, 1, 100, FAKE, FAKE, 10, 2, 64, FAKE, 5, 20, FAKE, None) == INVALID  # self range past N
     assert c(FAKE, 1, 100, FAKE, None, 10, 2, 64, None, 0, 0, FAKE, None) == INVALID   # no weights
     assert c(None, 1, 0, None, None, 0, 2, 64, None, 0, 0, None, None) == OK
+    m = lib.moe_combine_multi
+    assert m(FAKE, 1, 100, FAKE, FAKE, 10, 2, 12, None, 0, 0, FAKE, None) == INVALID  # 24-byte rows
+    # the scatter's self range is checked even without shared rows (it decides which tokens are left)
+    assert m(FAKE, 1, 100, FAKE, FAKE, 10, 2, 64, None, 5, 20, FAKE, None) == INVALID
+    assert m(FAKE, 1, 100, FAKE, FAKE, 10, 2, 64, None, 6, 5, FAKE, None) == INVALID
+    assert m(None, 1, 0, None, None, 0, 2, 64, None, 0, 0, None, None) == OK
 
 
 def _gd(**kw):
@@ -167,6 +173,30 @@ def test_grouped_gemm_shared_expert_validation(lib):
     fp8 = SharedExpert(FAKE.value, 32, FAKE.value, FAKE.value, None, None, FAKE.value)
     assert f(ctypes.byref(_gd(w_dt=2, shared=fp8)), *ptrs, FAKE, ws, None) == INVALID  # fp8 without scales
     assert f(ctypes.byref(_gd(n_groups=0, shared=SharedExpert(None, 0))), *ptrs, FAKE, ws, None) == OK
+
+
+def test_grouped_gemm_scatter_validation(lib):
+    from combine_router_softmax_amd import Scatter
+    f = lib.moe_grouped_gemm
+    ws = lib.moe_grouped_gemm_workspace(ctypes.byref(_gd()))
+    ptrs = [FAKE] * 8
+
+    def d(sc, **kw):
+        g = _gd(**kw)
+        g.scatter = ctypes.pointer(sc)
+        return g
+    good = dict(row_token=FAKE.value, row_of=FAKE.value, topk_w=FAKE.value, n_tokens=10, top_k=2, n_rows=64,
+                self_lo=0, self_hi=4, out=FAKE.value)
+    wsf = lib.moe_grouped_gemm_workspace(ctypes.byref(_gd(act_dt=0, w_dt=0)))
+    assert f(ctypes.byref(d(Scatter(**good), act_dt=0, w_dt=0)), *ptrs, FAKE, wsf, None) == UNSUPPORTED  # f32 out
+    for k, v in (("row_token", None), ("row_of", None), ("topk_w", None), ("out", None), ("out", FAKE.value + 8),
+                 ("top_k", 0), ("top_k", 17), ("n_tokens", -1), ("n_rows", -1), ("self_lo", 5), ("self_hi", 11)):
+        bad = dict(good, **{k: v})
+        assert f(ctypes.byref(d(Scatter(**bad))), *ptrs, FAKE, ws, None) == INVALID, (k, v)
+    # checked only where it is used: the up stage ignores it
+    bad = dict(good, out=None)
+    assert f(ctypes.byref(d(Scatter(**bad), stage=1)), *ptrs, FAKE, ws - 1, None) == WORKSPACE
+    assert f(ctypes.byref(d(Scatter(**good), rows=0)), *ptrs, FAKE, ws, None) == OK
 
 
 def test_pack_weights_and_format_validation(lib):

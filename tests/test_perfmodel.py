@@ -53,6 +53,14 @@ def test_algorithmic_model_counts():
     for d in ("bytes", "flops"):
         tot = sum(m[d][n] for n in ("gemm_up", "gemm_down"))
         assert sum(a[d][n] for n in ("gemm_up", "gemm_down", "shared")) == tot
+    # the down projection's scatter: tokens 1 and 3 have one local row each and
+    # lie outside the shared expert's tokens [0, 2): token 3 is scattered
+    # (token 1 is a shared-expert token), so the combine skips one y row read
+    # and one output row write
+    sc = bench.algorithmic_model(cfg, counts, row_of, B0=2, scatter=True)
+    assert sc["single_row_tokens_scattered"] == 1
+    assert sc["bytes"]["combine"] == m["bytes"]["combine"] - 2 * H * 2
+    assert sc["bytes"]["gemm_down"] == m["bytes"]["gemm_down"]
 
 
 def test_bench_refuses_more_than_one_gpu():
