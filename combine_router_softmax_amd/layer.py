@@ -247,9 +247,13 @@ class MoEShare:
         extra = {}
         if self.w8a8:
             a, extra["a_scales"] = self.xq[self.self_lo: self.self_hi], self.xs[self.self_lo: self.self_hi]
+        # a call of its own: with 128 or more rows of bf16 weights the wide
+        # kernel takes it whole (what AUTO picks too), without AUTO's empty
+        # stream-K launch and its fix-up
+        wide = a.shape[0] >= 128 and sw["w13"].dtype == torch.bfloat16 and self.H % 256 == 0
         moe_grouped_gemm(a, sw["w13"], sw["w2"], group_off=self.shared_off, s13=sw.get("s13"), s2=sw.get("s2"),
                          layout=COMPACT, stage=stage, y=self.ys[: a.shape[0]], ws=self.sws, w_format=self.w_format,
-                         **extra)
+                         policy=GEMM_WIDE if wide else 0, **extra)
 
     def combine(self, out, multi: bool = False):
         """Weighted sum into ``out``; ``multi``: only the tokens the down
