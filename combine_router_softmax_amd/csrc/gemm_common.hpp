@@ -632,6 +632,15 @@ constexpr int kWidePart = 4 * 2 * 8 * 16 * kWave;
 __device__ __forceinline__ int wide_part_idx(int wv, int a, int b, int q, int lane) {
   return ((((wv * 2 + a) * 8 + b) * 4 + q) * kWave + lane) * 4;
 }
+// After the wide kernel's kWideGrid partial slots: words its main kernel
+// leaves for the fix-up, so that the fix-up rebuilds no schedule. [0] the
+// number of K-split tiles (0: none), [1] their ranges each; from
+// kWideMetaRecs, one record per split tile: N tile, shared, rows, then the
+// tile's physical rows.
+constexpr int kWideRec = 8 + kWM;
+constexpr int kWideMetaRecs = 16;
+constexpr int kWideMetaInts = kWideMetaRecs + kWideGrid * kWideRec;
+__device__ __forceinline__ int* wide_meta(float* parts) { return reinterpret_cast<int*>(parts + size_t(kWideGrid) * kWidePart); }
 
 
 constexpr int kF8BM = 96;                                           // activation rows per tile

@@ -294,9 +294,23 @@ __global__ __launch_bounds__(kWideThreads, 1) void ffn_wide_kernel(GemmArgs p, f
   constexpr int SPC = kKC / kAK;
   const WideSplit ws = wide_split(n_tiles, nch);
   const int slot = int(blockIdx.x % kXcds) * (kWideGrid / kXcds) + int(blockIdx.x / kXcds);
-  auto run = [&](int t, int c_begin, int c_end, float* part) __attribute__((always_inline)) {
+  int* meta = wide_meta(parts);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {  // for the fix-up
+    meta[0] = ws.S > 1 ? ws.rem : 0;
+    meta[1] = ws.S;
+  }
+  // rec: the fix-up's record of the tile (first range of a split tile), else nullptr
+  auto run = [&](int t, int c_begin, int c_end, float* part, int* rec) __attribute__((always_inline)) {
     const Tile tl = decode_tile_wide(p, kWM, ntn, sh, t);
     build_rowmap<kWideThreads>(p, tl, kWM, sh, true);
+    if (rec != nullptr) {  // uniform
+      if (threadIdx.x == 0) {
+        rec[0] = tl.nt;
+        rec[1] = tl.shared;
+        rec[2] = tl.nrows;
+      }
+      for (int i = threadIdx.x; i < tl.nrows; i += kWideThreads) rec[8 + i] = sh.rowmap[i];
+    }
     const int sb = c_begin * SPC, se = c_end * SPC;
     switch ((tl.nrows + 63) / 64) {
       case 1: wide_tile<KIND, PACKED, 2>(p, tl, sh, X, sb, se, part); break;
@@ -306,20 +320,23 @@ __global__ __launch_bounds__(kWideThreads, 1) void ffn_wide_kernel(GemmArgs p, f
     }
     __syncthreads();
   };
-  for (int t = slot; t < ws.full; t += kWideGrid) run(t, 0, nch, nullptr);
+  for (int t = slot; t < ws.full; t += kWideGrid) run(t, 0, nch, nullptr, nullptr);
   const int u = int(blockIdx.x);
   if (ws.rem && u < ws.rem * ws.S) {
-    const int t = ws.full + u / ws.S, k = u % ws.S;
+    const int i = u / ws.S, k = u % ws.S;
     if (ws.S == 1) {
-      run(t, 0, nch, nullptr);
+      run(ws.full + i, 0, nch, nullptr, nullptr);
     } else {
-      run(t, k * nch / ws.S, (k + 1) * nch / ws.S, parts + size_t(u) * kWidePart);
+      run(ws.full + i, k * nch / ws.S, (k + 1) * nch / ws.S, parts + size_t(u) * kWidePart,
+          k == 0 ? meta + kWideMetaRecs + i * kWideRec : nullptr);
     }
   }
 }
 
 // Finishes the split wide tiles: block (i, b) sums the S partials of split
-// tile i for activation block b in split order and runs its epilogue.
+// tile i for activation block b in split order and runs its epilogue. The
+// tile (its N tile, rows and physical rows) comes from the record its first
+// range left, so a block with nothing to do ends after two loads.
 template <int KIND>
 __global__ __launch_bounds__(kGemmThreads) void ffn_wide_fixup_kernel(GemmArgs p, const float* __restrict__ parts) {
   __shared__ Sched sh;
@@ -328,20 +345,22 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_wide_fixup_kernel(GemmArgs p
   const int wv = tid / kWave;
   const int lr = lane & 31;
   const int lh = lane >> 5;
-  const int ntn = KIND == kUp ? p.n_out / 128 : p.n_out / 256;
-  const int n_tiles = build_schedule(p, kWM, ntn, true, sh);
-  const int nch = p.K / kKC;
-  const WideSplit ws = wide_split(n_tiles, nch);
+  const int* meta = wide_meta(const_cast<float*>(parts));
   const int i = blockIdx.x, b = blockIdx.y;
-  if (i >= ws.rem || ws.S == 1) return;  // uniform
-  const int t = ws.full + i;
-  const Tile tl = decode_tile_wide(p, kWM, ntn, sh, t);
+  if (i >= __builtin_amdgcn_readfirstlane(meta[0])) return;  // uniform: not a split tile
+  const int S = min(max(__builtin_amdgcn_readfirstlane(meta[1]), 1), kWideGrid);
+  const int* rec = meta + kWideMetaRecs + i * kWideRec;
+  Tile tl{};
+  tl.nt = __builtin_amdgcn_readfirstlane(rec[0]);
+  tl.shared = __builtin_amdgcn_readfirstlane(rec[1]) != 0;
+  tl.nrows = min(max(__builtin_amdgcn_readfirstlane(rec[2]), 0), kWM);
   if (b * 32 >= tl.nrows) return;  // uniform: no rows in this block
-  build_rowmap(p, tl, kWM, sh);
+  for (int r = tid; r < kWM; r += kGemmThreads) sh.rowmap[r] = r < tl.nrows ? rec[8 + r] : -1;
+  __syncthreads();
   // the S partials of each accumulator tile in split order, four in flight at a time
   f32x16_t acc[2];
   sum_partials(
-      acc, 0, ws.S - 1, [&](int k) -> const float* { return parts + size_t(i * ws.S + k) * kWidePart; },
+      acc, 0, S - 1, [&](int k) -> const float* { return parts + size_t(i * S + k) * kWidePart; },
       [&](int a, int q) { return wide_part_idx(wv, a, b, q, lane); });
   // the partials of this wave's block a are those of main-kernel wave 2 wv + a
   wide_epilogue_block<KIND>(p, tl, sh, b, acc[0], 2 * wv, lr, lh);
