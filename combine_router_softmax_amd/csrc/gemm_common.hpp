@@ -484,6 +484,94 @@ __device__ inline float* sk_slot(float* parts, int b, int slot) {
   return parts + (size_t(b) * 2 + slot) * kPartFloats;
 }
 
+// Fix-up records of the stream-K decode kernels, so that a fix-up rebuilds no
+// schedule. After the 2 x grid partial slots (slot_floats each): [0] the
+// ranges G, [1..2] rem_base, [3..4] rem (int64 halves), written by
+// workgroup 0; from kSkMetaRecs, one record per range j, written by range j:
+// [0] the tile whose first cut is the boundary after range j (-1: none), [1]
+// its N tile, [2] shared, [3] rows, [4] b_lo, [5] b_hi (the ranges over it),
+// then its physical rows.
+constexpr int kSkRecRows = 96;  // tile rows of the decode kernels (bf16 64, fp8 96)
+constexpr int kSkRecInts = 8 + kSkRecRows;
+constexpr int kSkMetaRecs = 8;
+constexpr int kSkMetaInts = kSkMetaRecs + 256 * kSkRecInts;  // grids of at most 256 ranges
+
+__device__ __forceinline__ int* sk_meta(float* parts, size_t slot_floats, int grid) {
+  return reinterpret_cast<int*>(parts + size_t(2) * grid * slot_floats);
+}
+
+// Main kernel, before its ranges: the header, and no record for range rng
+// until sk_write_rec sets one.
+__device__ __forceinline__ void sk_meta_begin(int* meta, const DpSk& sp, int rng) {
+  if (threadIdx.x == 0) {
+    if (blockIdx.x == 0) {
+      meta[0] = sp.G;
+      meta[1] = int(uint32_t(uint64_t(sp.rem_base)));
+      meta[2] = int(uint32_t(uint64_t(sp.rem_base) >> 32));
+      meta[3] = int(uint32_t(uint64_t(sp.rem)));
+      meta[4] = int(uint32_t(uint64_t(sp.rem) >> 32));
+    }
+    meta[kSkMetaRecs + rng * kSkRecInts] = -1;
+  }
+}
+
+// Whether remainder range [i0, i1) ends inside a tile whose chunk 0 it
+// holds: the boundary after it is that tile's first cut.
+__device__ __forceinline__ bool sk_owns_cut(int64_t i0, int64_t i1, int nchunks) {
+  return i0 < i1 && i1 % nchunks != 0 && i0 <= i1 / nchunks * nchunks;
+}
+
+// Range rng's record of tile t, a tile of the run that starts at tile t_run
+// (tl, whose rows are in sh.rowmap: every tile of a run has the same rows).
+template <int NT>
+__device__ __forceinline__ void sk_write_rec(int* meta, int rng, int t, int t_run, const Tile& tl, const Sched& sh,
+                                             int b_hi) {
+  int* rec = meta + kSkMetaRecs + rng * kSkRecInts;
+  if (threadIdx.x == 0) {
+    rec[0] = t;
+    rec[1] = tl.nt + (t - t_run);
+    rec[2] = tl.shared;
+    rec[3] = tl.nrows;
+    rec[4] = rng;
+    rec[5] = b_hi;
+  }
+  for (int i = threadIdx.x; i < tl.nrows; i += NT) rec[8 + i] = sh.rowmap[i];
+}
+
+// Fix-up side: the record of the boundary after range j (false: none).
+struct SkRec {
+  int t, b_lo, b_hi;
+  Tile tl;
+  DpSk sp;
+};
+__device__ __forceinline__ bool sk_read_rec(const int* meta, int j, int bm, SkRec& r) {
+  r.sp.G = __builtin_amdgcn_readfirstlane(meta[0]);
+  if (j + 1 >= r.sp.G) return false;  // boundaries lie between ranges 0 .. G - 1
+  const int* rec = meta + kSkMetaRecs + j * kSkRecInts;
+  r.t = __builtin_amdgcn_readfirstlane(rec[0]);
+  if (r.t < 0) return false;
+  r.sp.rem_base = int64_t(uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(meta[1]))) |
+                          uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(meta[2]))) << 32);
+  r.sp.rem = int64_t(uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(meta[3]))) |
+                     uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(meta[4]))) << 32);
+  r.sp.whole = 0;
+  r.tl = Tile{};
+  r.tl.nt = __builtin_amdgcn_readfirstlane(rec[1]);
+  r.tl.shared = __builtin_amdgcn_readfirstlane(rec[2]) != 0;
+  r.tl.nrows = min(max(__builtin_amdgcn_readfirstlane(rec[3]), 0), bm);
+  r.b_lo = __builtin_amdgcn_readfirstlane(rec[4]);
+  r.b_hi = min(__builtin_amdgcn_readfirstlane(rec[5]), r.sp.G - 1);
+  return true;
+}
+// The record's physical rows into sh.rowmap (-1 past the tile's rows). All
+// threads must call it.
+template <int NT>
+__device__ __forceinline__ void sk_read_rows(const int* meta, int j, int bm, int nrows, Sched& sh) {
+  const int* rec = meta + kSkMetaRecs + j * kSkRecInts;
+  for (int i = threadIdx.x; i < bm; i += NT) sh.rowmap[i] = i < nrows ? rec[8 + i] : -1;
+  __syncthreads();
+}
+
 // The token of routed row phys when its down-projection row is that token's
 // whole combine (exactly one of its K entries is a row of this GPU, and it
 // has no shared-expert row), with that entry's weight in w; else -1. The rule
@@ -651,6 +739,8 @@ constexpr int kF8NB = kF8Waves / 2;                                 // N blocks 
 constexpr int kF8Grid = 256;                                        // 1 resident workgroup x 256 CUs
 constexpr int kF8PartFloats = kF8Waves * 2 * kF8MB * 16 * kWave;   // one workgroup's accumulators (192 KiB)
 static_assert(kF8Threads <= kMaxGemmThreads, "schedule scratch holds one entry per thread");
+static_assert(kBfGrid <= 256 && kF8Grid <= 256 && kBfBM <= kSkRecRows && kF8BM <= kSkRecRows,
+              "fix-up records: one per range, a tile's rows each");
 
 }  // namespace
 }  // namespace moe

@@ -431,16 +431,22 @@ __global__ __launch_bounds__(kQ8Threads, 1) void ffn_w8a8_kernel(GemmArgs p, flo
   if (int(blockIdx.x) >= sp.G) return;  // uniform
   const int G = sp.G;
   const int rng = xcd_range(int(blockIdx.x), G);
+  int* meta = sk_meta(parts, kF8PartFloats, kF8Grid);
+  sk_meta_begin(meta, sp, rng);
   // the range's whole tiles first, then its share of the remainder
   for (int part = 0; part < 2; ++part) {
     const int64_t i0 = part == 0 ? int64_t(rng) * sp.whole * nchunks : sp.rem_base + sk_start(rng, sp.rem, G);
     const int64_t i1 = part == 0 ? int64_t(rng + 1) * sp.whole * nchunks : sp.rem_base + sk_start(rng + 1, sp.rem, G);
     if (i0 >= i1) continue;  // uniform
     const int t_first = int(i0 / nchunks), t_last = int((i1 - 1) / nchunks);
+    const bool rec_cut = part == 1 && sk_owns_cut(i0, i1, nchunks);  // the fix-up's record of tile t_last
     for (int t = t_first; t <= t_last;) {
       const Tile tl = decode_tile(p, kF8BM, ntn4, sh, t);
       build_rowmap<kQ8Threads>(p, tl, kF8BM, sh, true);
       const int n = tl.mtiles == 1 ? min(t_last - t + 1, ntn4 - tl.nt) : 1;
+      if (rec_cut && t_last < t + n)  // uniform
+        sk_write_rec<kQ8Threads>(meta, rng, t_last, t, tl, sh,
+                         sk_owner(int64_t(t_last + 1) * nchunks - 1 - sp.rem_base, sp.rem, G));
       const int64_t t0 = int64_t(t) * nchunks;
       const int it_begin = int(max<int64_t>(i0 - t0, 0));
       const int it_end = int(min<int64_t>(i1 - t0, int64_t(n) * nchunks));
@@ -478,24 +484,19 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_w8a8_fixup_kernel(GemmArgs p
   const int wv = tid / kWave;
   const int lr = lane & 31;
   const int lh = lane >> 5;
-  const int ntn4 = (p.n_tiles_n + kF8NB - 1) / kF8NB;
-  const int n_tiles = build_schedule(p, kF8BM, ntn4, false, sh);
   const int nchunks = p.K / kKC;
-  const DpSk sp = dpsk_split(n_tiles, nchunks, kF8Grid);
   const int j = blockIdx.x, pr = blockIdx.y / kF8MB, b = blockIdx.y % kF8MB;
-  const int G = sp.G;
-  if (j + 1 >= G) return;  // uniform: boundaries lie between the remainder shares of ranges 0 .. G-1
-  // (the whole-tile parts never cut a tile)
-  const int64_t ib = sp.rem_base + sk_start(j + 1, sp.rem, G);
-  if (ib <= sp.rem_base || ib >= sp.rem_base + sp.rem || ib % nchunks == 0) return;  // not inside a tile
-  const int t = int(ib / nchunks);
-  if (j > 0 && sp.rem_base + sk_start(j, sp.rem, G) > int64_t(t) * nchunks) return;  // an earlier boundary owns this tile
-  const Tile tl = decode_tile(p, kF8BM, ntn4, sh, t);
+  // the tile and its ranges from the record range j left (no schedule rebuilt;
+  // the whole-tile parts never cut a tile)
+  const int* meta = sk_meta(const_cast<float*>(parts), kF8PartFloats, kF8Grid);
+  SkRec r;
+  if (!sk_read_rec(meta, j, kF8BM, r)) return;  // uniform: the boundary after range j is no tile's first cut
+  const DpSk sp = r.sp;
+  const int G = sp.G, t = r.t, b_lo = r.b_lo, b_hi = r.b_hi;
+  const Tile tl = r.tl;
   const int nb0 = kF8NB * tl.nt + 2 * pr;
   if (b * 32 >= tl.nrows || nb0 >= p.n_tiles_n) return;  // uniform: no rows / no such N block
-  build_rowmap(p, tl, kF8BM, sh);
-  const int b_lo = sk_owner(int64_t(t) * nchunks - sp.rem_base, sp.rem, G);
-  const int b_hi = sk_owner(int64_t(t + 1) * nchunks - 1 - sp.rem_base, sp.rem, G);
+  sk_read_rows<kGemmThreads>(meta, j, kF8BM, tl.nrows, sh);
   f32x16_t acc[2];
   sum_partials(
       acc, b_lo, b_hi,

@@ -203,7 +203,8 @@ static size_t h_bytes(const moe_ggemm_desc_t* d, int64_t rows) {
 
 static size_t parts_bytes(const moe_ggemm_desc_t* d) {
   // shared by the wide and the stream-K kernels, which run one after the other
-  const size_t sk = d->w_dt == MOE_FP8_E4M3 ? size_t(2) * kF8Grid * kF8PartFloats : size_t(2) * kBfGrid * kPartFloats;
+  const size_t sk = (d->w_dt == MOE_FP8_E4M3 ? size_t(2) * kF8Grid * kF8PartFloats : size_t(2) * kBfGrid * kPartFloats) +
+                    kSkMetaInts;
   const size_t wide = size_t(kWideGrid) * kWidePart + kWideMetaInts;
   return d->act_dt == MOE_F32 ? 0 : std::max(sk, wide) * sizeof(float);
 }
