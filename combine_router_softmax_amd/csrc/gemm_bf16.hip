@@ -5,11 +5,11 @@ namespace moe {
 namespace {
 
 // Finishes the tiles of ffn_bf16_kernel cut by a stream-K range boundary:
-// block (j, m * kBfMB + b) looks at the boundary between workgroups j and
-// j+1; the first boundary inside a tile sums, for the tile's N block m and
-// 32-row block b, its partials in workgroup order (one wave per 32 weight rows
-// of the N block, i.e. the partials of the main kernel's waves 4 m .. 4 m + 3)
-// and runs that block's epilogue.
+// block (j, m * kBfMB + b) looks at the boundary between ranges j and j+1;
+// where it is a tile's first cut (range j left a record of the tile), it
+// sums, for the tile's N block m and 32-row block b, the partials in range
+// order (one wave per 32 weight rows of the N block, i.e. the partials of the
+// main kernel's waves 4 m .. 4 m + 3) and runs that block's epilogue.
 template <int KIND>
 __global__ __launch_bounds__(kGemmThreads) void ffn_fixup_kernel(GemmArgs p, const float* __restrict__ parts) {
   __shared__ Sched sh;
@@ -257,7 +257,8 @@ __global__ __launch_bounds__(kBfThreads, 1) void ffn_bf16_kernel(GemmArgs p, flo
   // the range's whole tiles first, then its share of the remainder
   for (int part = 0; part < 2; ++part) {
     const int64_t i0 = part == 0 ? int64_t(rng) * sp.whole * nchunks : sp.rem_base + sk_start(rng, sp.rem, G);
-    const int64_t i1 = part == 0 ? int64_t(rng + 1) * sp.whole * nchunks : sp.rem_base + sk_start(rng + 1, sp.rem, G);
+    const int64_t i1 = part == 0 ? min(int64_t(rng + 1) * sp.whole, int64_t(n_tiles)) * nchunks
+                                 : sp.rem_base + sk_start(rng + 1, sp.rem, G);
     if (i0 >= i1) continue;  // uniform
     const int t_first = int(i0 / nchunks), t_last = int((i1 - 1) / nchunks);
     const bool rec_cut = part == 1 && sk_owns_cut(i0, i1, nchunks);  // the fix-up's record of tile t_last

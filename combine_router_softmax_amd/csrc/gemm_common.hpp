@@ -447,14 +447,18 @@ __device__ inline int sk_owner(int64_t i, int64_t total, int G) {
 // stream-K over everything, and during the first part all workgroups are at
 // the same chunk index of their tiles, so the tiles of one expert (which sit
 // in neighbouring ranges on one XCD) read each activation chunk at about the
-// same time and the XCD's L2 serves the repeats. With one whole tile per
-// range, the remainder part is over a third of the work, and its ranges,
-// which start at different chunks of their tiles, share no activation reads:
-// then a G down to 3/4 of the grid that gives every range exactly two whole
-// tiles is taken instead, if there is one (kimi_k2_ep8 up projection: 394 ->
-// 373 us). With more whole tiles per range the remainder is kept: it balances
-// tiles of unequal cost (measured: three whole tiles and no remainder made the
-// down projection 12% slower, its compute units idle at the end).
+// same time and the XCD's L2 serves the repeats. The remainder part costs
+// partial sums and a fix-up, and with one whole tile per range it is over a
+// third of the work, its ranges starting at different chunks of their tiles
+// (no shared activation reads). So when ceil(n_tiles / G) <= 4 whole tiles
+// per range fit on at least 3/4 of the grid, the split takes only whole
+// tiles, on ceil(n_tiles / ceil(n_tiles / G)) ranges (the last takes what is
+// left): no tile is cut (kimi_k2_ep8 up projection, two tiles per range: 394
+// -> 373 us; dsv3_decode_ep8 down projection, four tiles per range on 224
+// workgroups: 187 -> 175 us; kimi_k2_ep8 W8A8 down: 242 -> 231 us). With more
+// whole tiles per range the remainder is kept: it balances tiles of unequal
+// cost (whole tiles only made the W8A8 prefill up projection 5% slower,
+// twelve tiles per range).
 struct DpSk {
   int G;             // ranges (workgroups used)
   int whole;         // whole tiles per range, taken first
@@ -464,7 +468,17 @@ struct DpSk {
 __device__ inline DpSk dpsk_split(int n_tiles, int nc, int max_grid) {
   DpSk d;
   d.G = sk_grid(int64_t(n_tiles) * nc, max_grid);
-  if (n_tiles / d.G == 1 && n_tiles % 2 == 0 && 4 * (n_tiles / 2) >= 3 * d.G) d.G = n_tiles / 2;
+  if (n_tiles % d.G != 0 && n_tiles > d.G) {
+    const int w = (n_tiles + d.G - 1) / d.G;
+    const int g2 = (n_tiles + w - 1) / w;
+    if (w <= 4 && 4 * g2 >= 3 * d.G) {
+      d.G = g2;
+      d.whole = w;
+      d.rem_base = int64_t(n_tiles) * nc;
+      d.rem = 0;
+      return d;
+    }
+  }
   d.whole = n_tiles / d.G;
   d.rem_base = int64_t(d.whole) * d.G * nc;
   d.rem = int64_t(n_tiles) * nc - d.rem_base;

@@ -349,7 +349,8 @@ __global__ __launch_bounds__(kF8Threads, 1) void ffn_fp8_kernel(GemmArgs p, floa
   // the range's whole tiles first, then its share of the remainder
   for (int part = 0; part < 2; ++part) {
     const int64_t i0 = part == 0 ? int64_t(rng) * sp.whole * nchunks : sp.rem_base + sk_start(rng, sp.rem, G);
-    const int64_t i1 = part == 0 ? int64_t(rng + 1) * sp.whole * nchunks : sp.rem_base + sk_start(rng + 1, sp.rem, G);
+    const int64_t i1 = part == 0 ? min(int64_t(rng + 1) * sp.whole, int64_t(n_tiles)) * nchunks
+                                 : sp.rem_base + sk_start(rng + 1, sp.rem, G);
     if (i0 >= i1) continue;  // uniform
     const int t_first = int(i0 / nchunks), t_last = int((i1 - 1) / nchunks);
     const bool rec_cut = part == 1 && sk_owns_cut(i0, i1, nchunks);  // the fix-up's record of tile t_last
