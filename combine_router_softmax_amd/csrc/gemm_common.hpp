@@ -376,7 +376,12 @@ __device__ __forceinline__ uint4 ld_w(gptr<uint4> p) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-__device__ __forceinline__ float silu_f(float g) { return g / (1.f + __expf(-g)); }
+// silu(g) = g / (1 + e^-g), the division as a product with the hardware
+// reciprocal (1 ulp): a correctly rounded division is a ten-instruction
+// sequence, and the result is rounded to bf16 (or compared at fp32 tolerance)
+// right after. g -> -inf: e^-g = inf, rcp(inf) = 0, the product -0 as for the
+// division.
+__device__ __forceinline__ float silu_f(float g) { return g * __builtin_amdgcn_rcpf(1.f + __expf(-g)); }
 
 // e4m3fn x 8 (two dwords) -> bf16 x 8 of code * scale: exact decode to fp32
 // (v_cvt_pk_f32_fp8), one fp32 multiply by the 128x128 block scale, one RNE
