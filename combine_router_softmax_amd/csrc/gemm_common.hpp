@@ -109,6 +109,7 @@ struct Sched {
   int tile_start[kMaxGroups + 2];
   int full_start[kMaxGroups + 2];  // wide kernel: exclusive prefix of the groups' full-row-tile tiles
   int m[kMaxGroups + 1];
+  int goff[kMaxGroups + 1];  // compact layout: each group's first row (the shared expert: 0)
   int seg[kGemmMaxSrc + 1];
   union {
     int rowmap[256];
@@ -138,6 +139,7 @@ __device__ __forceinline__ int build_schedule(const GemmArgs& p, int bm, int ntn
       const int64_t lo = min<int64_t>(max<int64_t>(p.group_off[g], 0), p.rows);
       const int64_t hi = min<int64_t>(max<int64_t>(p.group_off[g + 1], lo), p.rows);
       sh.m[nsh + g] = int(hi - lo);
+      sh.goff[nsh + g] = int(lo);
     }
   } else {
     for (int g = tid; g < p.G; g += NT) sh.m[nsh + g] = 0;
@@ -148,7 +150,10 @@ __device__ __forceinline__ int build_schedule(const GemmArgs& p, int bm, int ntn
     }
   }
   if (tid == 0) {
-    if (nsh) sh.m[0] = p.sh_rows;
+    if (nsh) {
+      sh.m[0] = p.sh_rows;
+      sh.goff[0] = 0;
+    }
     sh.wide_tiles = 0;
   }
   __syncthreads();
@@ -311,7 +316,7 @@ __device__ __forceinline__ void build_rowmap(const GemmArgs& p, const Tile& tl, 
   };
   if (tl.shared || p.layout == MOE_LAYOUT_COMPACT) {
     if (tid < bm) {
-      const int64_t base = tl.shared ? 0 : min<int64_t>(max<int64_t>(p.group_off[tl.g], 0), p.rows);
+      const int64_t base = sh.goff[tl.shared ? 0 : (p.sh_rows > 0 ? 1 : 0) + tl.g];  // (set by build_schedule)
       put(tid < tl.nrows ? int(base + tl.r0 + tid) : -1);
     }
     __syncthreads();
