@@ -353,6 +353,33 @@ def test_combine_many_tokens_all_kept_counts():
     assert {int(c) for c in keep[sample].sum(axis=1)} >= set(range(K + 1))
 
 
+# Rows for at most half the (token, entry) pairs (few local experts, as at
+# the EP128 decode share): the combine takes strided batches of tokens and
+# combines only the touched ones. Every touched token against the oracle,
+# untouched rows keep their contents; rows of 8704 bf16 values take two
+# chunks; K = 2, 8, 16; fewer and more than 1024 tokens (the two piece shapes).
+@pytest.mark.parametrize("N,K,H", [(8192, 8, 7168), (5000, 16, 8704), (3000, 2, 264), (700, 8, 264)])
+def test_combine_few_rows_many_tokens(N, K, H):
+    rng = np.random.default_rng(N + K)
+    R = N * K // 4
+    keep = rng.random((N, K)) < 0.03
+    row_of = np.full((N, K), -1, dtype=np.int32)
+    row_of[keep] = rng.permutation(R)[: int(keep.sum())]
+    w = rng.random((N, K)).astype(np.float32)
+    ye = torch.randn(R, H).to(torch.bfloat16)
+    lo, hi = 40, 200
+    sy = torch.randn(hi - lo, H).to(torch.bfloat16)
+    out = torch.full((N, H), 7.0, dtype=torch.bfloat16, device="cuda")
+    moe.moe_combine(ye.cuda(), torch.from_numpy(row_of).cuda(), torch.from_numpy(w).cuda(), out, sy.cuda(), lo, hi)
+    touched = keep.any(axis=1) | ((np.arange(N) >= lo) & (np.arange(N) < hi))
+    tok = np.nonzero(touched)[0]
+    ref = combine(f64(ye), row_of.reshape(-1), w, K, np.full((N, H), 7.0), f64(sy), lo, hi, tokens=tok)
+    got = f64(out)
+    assert rel_l2(got[tok], ref[tok]) <= 4e-3  # one bf16 rounding of each output
+    assert (got[~touched] == 7.0).all()
+    assert 0 < len(tok) < N // 2
+
+
 # --------------------------------------------------------------------------- whole layer (full size)
 FULL = ["dsv3_decode_ep8", "dsv3_decode_ep128", "kimi_k2_ep8", "dsv3_prefill_ep8"]
 
