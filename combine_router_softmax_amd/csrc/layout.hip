@@ -59,6 +59,53 @@ __host__ __device__ inline LayoutWs layout_ws(void* ws, int n_local, int tcap) {
   return w;
 }
 
+// Block-wide scan of a[0..n) in LDS: each thread folds a contiguous run, the
+// run totals are scanned inside each wavefront by lane shuffles and across the
+// four wavefronts through tmp, then every run is rewritten; two barriers for
+// any n (a Hillis-Steele pass over 256 run totals takes sixteen). kMax:
+// inclusive max-scan, returns the maximum; else exclusive sum-scan, returns
+// the total. All threads must call it.
+template <bool kMax>
+__device__ int layout_scan(int* a, int n, int* tmp) {
+  constexpr int NW = kLayoutThreads / kWave;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  const int id = kMax ? INT_MIN : 0;
+  const int per = (n + kLayoutThreads - 1) / kLayoutThreads;
+  const int lo = min(n, tid * per), hi = min(n, lo + per);
+  int run = id;
+  for (int i = lo; i < hi; ++i) run = kMax ? max(run, a[i]) : run + a[i];
+  int incl = run;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int u = __shfl_up(incl, off);
+    if (lane >= off) incl = kMax ? max(incl, u) : incl + u;
+  }
+  if (lane == kWave - 1) tmp[w] = incl;
+  __syncthreads();
+  int before = id, total = id;
+#pragma unroll
+  for (int w2 = 0; w2 < NW; ++w2) {
+    const int t = tmp[w2];
+    if (w2 < w) before = kMax ? max(before, t) : before + t;
+    total = kMax ? max(total, t) : total + t;
+  }
+  int excl = __shfl_up(incl, 1);
+  if (lane == 0) excl = id;
+  int carry = kMax ? max(before, excl) : before + excl;
+  for (int i = lo; i < hi; ++i) {
+    const int v = a[i];
+    if (kMax) {
+      carry = max(carry, v);
+      a[i] = carry;
+    } else {
+      a[i] = carry;
+      carry += v;
+    }
+  }
+  __syncthreads();  // a[] complete, and tmp free for the next call
+  return total;
+}
+
 // Source offsets repaired into [0 = off[0] <= ... <= off[S] = N], and the
 // exclusive prefix ts[] of tiles per source (ts[S] = tile count). Returns the
 // tile count. All threads must call it.
@@ -72,11 +119,11 @@ __device__ int build_tile_map(const int32_t* __restrict__ src_offsets, int n_src
     off[s] = v;
   }
   __syncthreads();
-  block_scan_lds<true, kLayoutThreads>(off, n_src + 1, tmp);
+  layout_scan<true>(off, n_src + 1, tmp);
   for (int s = threadIdx.x; s < n_src; s += kLayoutThreads)
     ts[s] = (off[s + 1] - off[s] + kTileTokens - 1) / kTileTokens;
   __syncthreads();
-  const int n_tiles = block_scan_lds<false, kLayoutThreads>(ts, n_src, tmp);
+  const int n_tiles = layout_scan<false>(ts, n_src, tmp);
   if (threadIdx.x == 0) ts[n_src] = n_tiles;
   __syncthreads();
   return n_tiles;
@@ -207,14 +254,33 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(LayoutArgs 
       pre[le * PW + b] = p.ws.prefix[size_t(le) * p.tcap + b];
     }
     __syncthreads();
-    for (int le = tid; le < L; le += kLayoutThreads) {
-      int acc = 0;
-      for (int b = 0; b < n_tiles; ++b) {
-        const int v = pre[le * PW + b];
-        pre[le * PW + b] = acc;
-        acc += v;
+    if (n_tiles >= 32) {  // uniform: a wavefront per expert, 64 tiles at a time
+      const int lane = tid & (kWave - 1);
+      for (int le = tid / kWave; le < L; le += kLayoutThreads / kWave) {
+        int carry = 0;
+        for (int b0 = 0; b0 <= n_tiles; b0 += kWave) {
+          const int b = b0 + lane;
+          const int v = b < n_tiles ? pre[le * PW + b] : 0;
+          int incl = v;
+#pragma unroll
+          for (int off = 1; off < kWave; off <<= 1) {
+            const int u = __shfl_up(incl, off);
+            if (lane >= off) incl += u;
+          }
+          if (b <= n_tiles) pre[le * PW + b] = carry + incl - v;  // [n_tiles]: the total
+          carry += __shfl(incl, kWave - 1);
+        }
       }
-      pre[le * PW + n_tiles] = acc;
+    } else {  // a thread per expert
+      for (int le = tid; le < L; le += kLayoutThreads) {
+        int acc = 0;
+        for (int b = 0; b < n_tiles; ++b) {
+          const int v = pre[le * PW + b];
+          pre[le * PW + b] = acc;
+          acc += v;
+        }
+        pre[le * PW + n_tiles] = acc;
+      }
     }
     __syncthreads();
   }
@@ -229,7 +295,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(LayoutArgs 
   // expert start rows (compact): exclusive scan of the totals
   for (int le = tid; le < L; le += kLayoutThreads) start[le] = FUSED ? pre[le * PW + n_tiles] : p.ws.total[le];
   __syncthreads();
-  const int m_total = block_scan_lds<false, kLayoutThreads>(start, L, tmp);
+  const int m_total = layout_scan<false>(start, L, tmp);
   if (tid == 0) start[L] = m_total;
   __syncthreads();
   const bool compact = p.layout == MOE_LAYOUT_COMPACT;
