@@ -380,6 +380,23 @@ def test_combine_few_rows_many_tokens(N, K, H):
     assert 0 < len(tok) < N // 2
 
 
+# No routed rows at all (no token picked a local expert): only the self
+# range's shared rows are written, whichever form the combine takes.
+@pytest.mark.parametrize("N", [700, 4000])
+def test_combine_no_rows_shared_only(N):
+    K, H = 8, 264
+    row_of = np.full((N, K), -1, dtype=np.int32)
+    w = np.random.default_rng(3).random((N, K)).astype(np.float32)
+    lo, hi = 10, 50
+    sy = torch.randn(hi - lo, H).to(torch.bfloat16)
+    out = torch.full((N, H), 7.0, dtype=torch.bfloat16, device="cuda")
+    ye = torch.empty((0, H), dtype=torch.bfloat16, device="cuda")
+    moe.moe_combine(ye, torch.from_numpy(row_of).cuda(), torch.from_numpy(w).cuda(), out, sy.cuda(), lo, hi)
+    got = out.cpu()
+    assert torch.equal(got[lo:hi].view(torch.int16), sy.view(torch.int16))
+    assert (got[:lo] == 7.0).all() and (got[hi:] == 7.0).all()
+
+
 # --------------------------------------------------------------------------- whole layer (full size)
 FULL = ["dsv3_decode_ep8", "dsv3_decode_ep128", "kimi_k2_ep8", "dsv3_prefill_ep8"]
 
