@@ -552,7 +552,7 @@ def test_layer_mid_size_every_row(kernel, layout):
     assert np.all(got[~touched] == -9.0)
     assert touched.sum() > B0
     # bf16 operands are exact, sums fp32; h and y (and fp8 weights, once) are
-    # rounded to bf16: far inside the benchmark spec's bounds, which hold per row
+    # rounded to bf16: far inside the relative-L2 bounds of TOL, which hold per row
     _assert_rows_close(got[touched], ref["out"][touched], 1e-2, f"mid {kernel} layout={layout}",
                        row_tol=TOL[cfg.weight])
 

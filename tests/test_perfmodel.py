@@ -14,7 +14,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def test_tokens_per_expert_worked_example():
     # batch 128, query length 2, top-8, EP128 = DP128 over 256 experts: m = 1024
     assert bench.tokens_per_expert(128, 2, 8, 128, 256) == 1024
-    # at EP8 the same formula gives 64 (the page's figure caption says 128)
+    # at EP8 the same formula gives 64 (the page's figure caption prints 128 for this
+    # case; the formula, not the caption, is taken as the definition)
     assert bench.tokens_per_expert(128, 2, 8, 8, 256) == 64
 
 
