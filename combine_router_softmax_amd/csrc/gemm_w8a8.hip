@@ -122,9 +122,7 @@ __device__ __forceinline__ void q8_store_h(const f32x16_t& g0, const f32x16_t& g
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const f32x16_t& g = a ? g1 : g0;
-      uint32_t w = 0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) w |= e4m3_quant(g[4 * q + r], s) << (8 * r);
+      const uint32_t w = e4m3_quant4(g[4 * q], g[4 * q + 1], g[4 * q + 2], g[4 * q + 3], s);
       const int col = 64 * (nb0 + a) + 16 * wq + 8 * q + 4 * lh;
       *reinterpret_cast<uint32_t*>(row + col) = w;
     }

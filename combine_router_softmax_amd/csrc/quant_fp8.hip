@@ -19,20 +19,20 @@ namespace {
 
 constexpr int kQThreads = 256;
 
-// Code of a bf16 value v (|v| <= the block's largest magnitude) in a block of
-// scale s, with the quotient v / s formed as q0 = v' r corrected once by a
-// fused multiply-add, q = q0 + (v' - q0 s') r, where r = 1 / s' is correctly
+// Clamped quotient of a bf16 value v (|v| <= the block's largest magnitude)
+// by the block's scale s, formed as q0 = v' r corrected once by a fused
+// multiply-add, q = q0 + (v' - q0 s') r, where r = 1 / s' is correctly
 // rounded (one division per thread, not eight) and v' = v k, s' = s k with k
 // = 2^64 for blocks whose scale is below 2^-64 (exact power-of-two scaling,
 // so that the residual stays exact). For every pair of bf16 values this gives
 // the correctly rounded quotient wherever it reaches 2^-10 and the same e4m3
 // code as the correctly rounded division everywhere (tests/fastdiv_check.c
 // runs all 2^30 pairs).
-__device__ __forceinline__ uint32_t e4m3_quant_bf16(float v, float k, float ss, float r) {
+__device__ __forceinline__ float e4m3_quotient_bf16(float v, float k, float ss, float r) {
   const float x = v * k;
   const float q0 = x * r;
   const float q = __builtin_fmaf(__builtin_fmaf(-q0, ss, x), r, q0);
-  return e4m3_encode(fminf(fmaxf(q, -kE4m3Max), kE4m3Max));
+  return fminf(fmaxf(q, -kE4m3Max), kE4m3Max);
 }
 
 template <typename T>
@@ -73,17 +73,14 @@ __global__ __launch_bounds__(kQThreads) void quantize_1x128_kernel(const T* __re
     const float k = s < 0x1p-64f ? 0x1p64f : 1.f;
     const float ss = s * k;
     const float r = 1.f / ss;
+    float q[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lo |= e4m3_quant_bf16(v[i], k, ss, r) << (8 * i);
-      hi |= e4m3_quant_bf16(v[4 + i], k, ss, r) << (8 * i);
-    }
+    for (int i = 0; i < 8; ++i) q[i] = e4m3_quotient_bf16(v[i], k, ss, r);
+    lo = e4m3_encode2(q[0], q[1]) | e4m3_encode2(q[2], q[3]) << 16;
+    hi = e4m3_encode2(q[4], q[5]) | e4m3_encode2(q[6], q[7]) << 16;
   } else {  // float32 inputs: the correctly rounded division of each value
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lo |= e4m3_quant(v[i], s) << (8 * i);
-      hi |= e4m3_quant(v[4 + i], s) << (8 * i);
-    }
+    lo = e4m3_quant4(v[0], v[1], v[2], v[3], s);
+    hi = e4m3_quant4(v[4], v[5], v[6], v[7], s);
   }
   *reinterpret_cast<uint2*>(xq + off) = make_uint2(lo, hi);
   if (part == 0) xs[blk] = s;

@@ -4,9 +4,10 @@
  * For every finite bf16 block maximum amax >= 0 and every finite bf16 x with
  * |x| <= amax: s = amax / 448 (1 when that is 0); k = 2^64 when s < 2^-64,
  * else 1; r = 1 / (s k); q0 = (x k) r; q = fma(fma(-q0, s k, x k), r, q0).
- * Counts the pairs whose e4m3 code (the same encoding rule as the kernel:
- * clamp to +-448, subnormal codes rint(|q| 2^9) below 2^-6, otherwise the
- * mantissa rounded to 3 bits, half to even) differs from that of x / s, and
+ * Counts the pairs whose e4m3 code (clamp to +-448, subnormal codes
+ * rint(|q| 2^9) below 2^-6, otherwise the mantissa rounded to 3 bits, half
+ * to even, zero as 0x00: the rounding of the kernel's conversion
+ * instruction) differs from that of x / s, and
  * the pairs with |x / s| >= 2^-10 whose float32 quotients differ. Prints
  * "tested N code_mismatches A quotient_mismatches B". IEEE float32 with
  * subnormals and exact fmaf are assumed (build without fast-math and with
