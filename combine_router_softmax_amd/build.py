@@ -4,7 +4,9 @@ Usage: ``python combine_router_softmax_amd/build.py`` (or ``build()``).
 Every ``csrc/*.hip`` file is compiled to an object in parallel, then linked
 into ``combine_router_softmax_amd/libmoe.so``. ``probes/ceilings.hip`` (the
 measured-ceilings program that ``bench.py --ceilings`` runs) is built beside
-it as ``combine_router_softmax_amd/ceilings``.
+it as ``combine_router_softmax_amd/ceilings``, and ``probes/fp8_encode.hip``
+(the exhaustive check of the e4m3 encoder that a GPU test runs) as
+``combine_router_softmax_amd/fp8_encode_check``.
 """
 from __future__ import annotations
 
@@ -23,6 +25,8 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 PROBE_SRC = os.path.join(PKG, "probes", "ceilings.hip")
 PROBE = os.path.join(PKG, "ceilings")
+FP8_PROBE_SRC = os.path.join(PKG, "probes", "fp8_encode.hip")
+FP8_PROBE = os.path.join(PKG, "fp8_encode_check")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -74,17 +78,18 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
     os.replace(tmp, LIB)
-    _build_probe(hipcc)
+    _build_probe(hipcc, PROBE_SRC, PROBE)
+    _build_probe(hipcc, FP8_PROBE_SRC, FP8_PROBE)
     return LIB
 
 
-def _build_probe(hipcc: str) -> None:
-    tmp = PROBE + ".tmp"
-    cmd = [hipcc, *[f for f in HIPCC_FLAGS if f not in ("-fPIC", "-fvisibility=hidden")], PROBE_SRC, "-o", tmp]
+def _build_probe(hipcc: str, src: str, exe: str) -> None:
+    tmp = exe + ".tmp"
+    cmd = [hipcc, *[f for f in HIPCC_FLAGS if f not in ("-fPIC", "-fvisibility=hidden")], f"-I{CSRC}", src, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {PROBE_SRC}:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, PROBE)
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}{r.stderr}")
+    os.replace(tmp, exe)
 
 
 if __name__ == "__main__":

@@ -374,3 +374,22 @@ def test_w8a8_layer_full_size_prefill_own_tokens():
     flush(f"  oracle layers over the {B0} own tokens")
     q, u = _oracles(d, COMPACT, None, n=B0)
     _compare_layer(f64(out[:B0]), q, u, "dsv3_prefill_ep8 W8A8 own tokens")
+
+
+def test_e4m3_encoder_on_every_float32():
+    """The encoder behind every fp8 code (the conversion instruction, with
+    magnitudes <= 2^-10 entered as +0) equals a bit-level encoder of the
+    OCP e4m3fn format, round to nearest even, zero as 0x00, on every finite
+    float32 clamped to [-448, 448] (probes/fp8_encode.hip, built by build.py)."""
+    import os
+    import re
+    import subprocess
+    exe = os.path.join(os.path.dirname(moe.__file__), "fp8_encode_check")
+    assert os.path.exists(exe), "fp8_encode_check is built with the library (combine_router_softmax_amd/build.py)"
+    flush("fp8 encoder probe over all float32")
+    out = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stderr
+    m = re.search(r"tested (\d+) mismatches (\d+)", out.stdout)
+    assert m, out.stdout
+    assert int(m.group(1)) == 2 ** 32 - 2 ** 24
+    assert int(m.group(2)) == 0, out.stdout
