@@ -54,6 +54,7 @@ constexpr int kQ8Waves = 4;                  // one per SIMD
 constexpr int kQ8Threads = kQ8Waves * kWave;
 constexpr int kQ8NA = kF8NB;                 // N blocks (sub-blocks) per wave
 constexpr int kQ8Stage = kF8BM * kKC;        // bytes per LDS stage (96 rows)
+constexpr int kQ8Interleave = 6;             // whole tiles per range from which ranges interleave
 constexpr int kQ8WaitLgkm0 = waitcnt_vm(63) & ~(15 << 8);  // LDS ops only
 
 __device__ __forceinline__ float* q8_slot(float* parts, int b, int slot) {
@@ -431,8 +432,28 @@ __global__ __launch_bounds__(kQ8Threads, 1) void ffn_w8a8_kernel(GemmArgs p, flo
   const int rng = xcd_range(int(blockIdx.x), G);
   int* meta = sk_meta(parts, kF8PartFloats, kF8Grid);
   sk_meta_begin(meta, sp, rng);
-  // the range's whole tiles first, then its share of the remainder
-  for (int part = 0; part < 2; ++part) {
+  // Many whole tiles per range (prefill sizes): range r takes whole tiles r,
+  // r + G, r + 2G, ... instead of a contiguous run of them. An (expert, N
+  // tile)'s row tiles are consecutive in the tile order, so the workgroups of
+  // an XCD, which hold consecutive ranges, then stream the same weight slab
+  // together and its L2 serves the repeats; with contiguous runs one
+  // workgroup streamed the slab once per row tile, one after another.
+  if (sp.whole >= kQ8Interleave) {  // uniform
+    for (int j = 0; j < sp.whole; ++j) {
+      const int t = j * G + rng;  // < G * whole <= n_tiles
+      const Tile tl = decode_tile(p, kF8BM, ntn4, sh, t);
+      build_rowmap<kQ8Threads>(p, tl, kF8BM, sh, true);
+      switch ((tl.nrows + 31) / 32) {
+        case 1: q8_run<KIND, PACKED, 1, false>(p, tl, 1, sh, x0, x1, red, 0, nchunks, nullptr, nullptr); break;
+        case 2: q8_run<KIND, PACKED, 2, false>(p, tl, 1, sh, x0, x1, red, 0, nchunks, nullptr, nullptr); break;
+        default: q8_run<KIND, PACKED, 3, false>(p, tl, 1, sh, x0, x1, red, 0, nchunks, nullptr, nullptr); break;
+      }
+      __syncthreads();  // rowmap is rewritten by the next tile
+    }
+  }
+  // the range's whole tiles first (unless taken above), then its share of the
+  // remainder
+  for (int part = sp.whole >= kQ8Interleave ? 1 : 0; part < 2; ++part) {
     const int64_t i0 = part == 0 ? int64_t(rng) * sp.whole * nchunks : sp.rem_base + sk_start(rng, sp.rem, G);
     const int64_t i1 = part == 0 ? min(int64_t(rng + 1) * sp.whole, int64_t(n_tiles)) * nchunks
                                  : sp.rem_base + sk_start(rng + 1, sp.rem, G);
