@@ -44,6 +44,7 @@ struct GemmArgs {
   int packed;                 // weights in the packed (load-order) layout
   int wide_min;               // groups with at least this many rows may go to the wide-tile kernel ...
   int wide_min_tiles;         // ... if the wide groups make at least this many wide tiles
+  int interleave;             // W8A8: ranges of many whole tiles interleave them (prefill-sized launches)
   int a_blk, sh_a_blk;        // routed / shared activations in the 16-row blocked layout
   int out_blk;                // outputs (routed and shared) in the 16-row blocked layout
   const int32_t* a_rows;      // routed input row r is row a_rows[r] of a (nullptr: row r)

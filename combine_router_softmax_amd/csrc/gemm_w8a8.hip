@@ -418,7 +418,9 @@ __device__ __forceinline__ void q8_run(const GemmArgs& p, const Tile& tl, int n,
 }
 
 // Stream-K over (tile, chunk) iterations with the W8A16 kernel's tiles and ranges.
-template <int KIND, bool PACKED>
+// INTERLEAVE: the instantiation for prefill-sized launches (below); decode
+// launches take the other, whose code then holds no trace of it.
+template <int KIND, bool PACKED, bool INTERLEAVE>
 __global__ __launch_bounds__(kQ8Threads, 1) void ffn_w8a8_kernel(GemmArgs p, float* __restrict__ parts) {
   __shared__ Sched sh;
   __shared__ __attribute__((aligned(1024))) uint8_t x0[kQ8Stage], x1[kQ8Stage];
@@ -438,7 +440,8 @@ __global__ __launch_bounds__(kQ8Threads, 1) void ffn_w8a8_kernel(GemmArgs p, flo
   // an XCD, which hold consecutive ranges, then stream the same weight slab
   // together and its L2 serves the repeats; with contiguous runs one
   // workgroup streamed the slab once per row tile, one after another.
-  if (sp.whole >= kQ8Interleave) {  // uniform
+  const bool inter = INTERLEAVE && sp.whole >= kQ8Interleave;
+  if (inter) {  // uniform
     for (int j = 0; j < sp.whole; ++j) {
       const int t = j * G + rng;  // < G * whole <= n_tiles
       const Tile tl = decode_tile(p, kF8BM, ntn4, sh, t);
@@ -453,7 +456,7 @@ __global__ __launch_bounds__(kQ8Threads, 1) void ffn_w8a8_kernel(GemmArgs p, flo
   }
   // the range's whole tiles first (unless taken above), then its share of the
   // remainder
-  for (int part = sp.whole >= kQ8Interleave ? 1 : 0; part < 2; ++part) {
+  for (int part = inter ? 1 : 0; part < 2; ++part) {
     const int64_t i0 = part == 0 ? int64_t(rng) * sp.whole * nchunks : sp.rem_base + sk_start(rng, sp.rem, G);
     const int64_t i1 = part == 0 ? min(int64_t(rng + 1) * sp.whole, int64_t(n_tiles)) * nchunks
                                  : sp.rem_base + sk_start(rng + 1, sp.rem, G);
@@ -549,13 +552,27 @@ __global__ __launch_bounds__(kGemmThreads) void ffn_w8a8_fixup_kernel(GemmArgs p
 
 moe_status_t launch_w8a8(const GemmArgs& p, int kind, float* parts, hipStream_t stream) {
   const dim3 grid(kF8Grid), block(kQ8Threads);
+#define MOE_Q8_LAUNCH(KIND_, PACKED_, INTER_) \
+  hipLaunchKernelGGL((ffn_w8a8_kernel<KIND_, PACKED_, INTER_>), grid, block, 0, stream, p, parts)
+  const bool il = p.interleave != 0;
   if (kind == kUp) {
-    if (p.packed) hipLaunchKernelGGL((ffn_w8a8_kernel<kUp, true>), grid, block, 0, stream, p, parts);
-    else hipLaunchKernelGGL((ffn_w8a8_kernel<kUp, false>), grid, block, 0, stream, p, parts);
+    if (p.packed) {
+      if (il) MOE_Q8_LAUNCH(kUp, true, true);
+      else MOE_Q8_LAUNCH(kUp, true, false);
+    } else {
+      if (il) MOE_Q8_LAUNCH(kUp, false, true);
+      else MOE_Q8_LAUNCH(kUp, false, false);
+    }
   } else {
-    if (p.packed) hipLaunchKernelGGL((ffn_w8a8_kernel<kDown, true>), grid, block, 0, stream, p, parts);
-    else hipLaunchKernelGGL((ffn_w8a8_kernel<kDown, false>), grid, block, 0, stream, p, parts);
+    if (p.packed) {
+      if (il) MOE_Q8_LAUNCH(kDown, true, true);
+      else MOE_Q8_LAUNCH(kDown, true, false);
+    } else {
+      if (il) MOE_Q8_LAUNCH(kDown, false, true);
+      else MOE_Q8_LAUNCH(kDown, false, false);
+    }
   }
+#undef MOE_Q8_LAUNCH
   if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
   const dim3 fix_grid(kF8Grid - 1, 2 * kF8MB);
   if (kind == kUp) hipLaunchKernelGGL((ffn_w8a8_fixup_kernel<kUp>), fix_grid, dim3(kGemmThreads), 0, stream, p, parts);

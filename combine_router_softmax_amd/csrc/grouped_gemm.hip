@@ -323,6 +323,7 @@ MOE_API moe_status_t moe_grouped_gemm(const moe_ggemm_desc_t* d, const void* a, 
   // whose loads take 4 rows x 128 columns
   const bool h_blk = wide_ok;
   p.wide_min_tiles = force ? 0 : kWideMinTiles;
+  p.interleave = d->policy != MOE_GEMM_STREAM_K;
   p.sh_a_blk = 0;
   p.a_rows = nullptr;
   p.a_nrows = 0;

@@ -242,7 +242,12 @@ typedef enum {
  * of the launch takes that kernel, else every group takes the stream-K
  * kernel (decided on the device from the counts). WIDE: every group takes the
  * wide-tile kernel where its shape and dtype allow (then the stream-K kernel
- * is not launched). STREAM_K: never (then the wide kernel is not launched). */
+ * is not launched). STREAM_K: never (then the wide kernel is not launched).
+ * fp8 weights take the W8A16 or W8A8 kernel whatever the policy; for W8A8,
+ * STREAM_K (decode batches) keeps each workgroup's whole tiles contiguous,
+ * while AUTO and WIDE let workgroups holding 6 or more whole tiles take every
+ * G-th tile instead (prefill batches: neighbouring workgroups then share each
+ * weight slab in L2). */
 typedef enum {
   MOE_GEMM_AUTO = 0,
   MOE_GEMM_WIDE = 1,
